@@ -1,0 +1,187 @@
+"""numpy front end of the plain CPU oracle (``ep_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and the CPU-baseline leg of ``bench.py``; the product path never imports it.
+It shares no code with the HIP library.
+
+Parity status: every function is pinned by the CPU tests (see the
+``test_oracle_*`` files): number formats against torch's own converters and
+exhaustive format properties, layout and slots against numpy routines,
+brute force and invariants, combine against exact rational sums.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        path = _build.build(force=False)
+        L = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        i64, i32 = ctypes.c_int64, ctypes.c_int
+        L.orc_layout.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P]
+        L.orc_layout.restype = i32
+        L.orc_slots.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, P, i64]
+        L.orc_slots.restype = i64
+        L.orc_recv_list.argtypes = [P, i32, i32, i32, P]
+        L.orc_recv_list.restype = None
+        L.orc_dispatch.argtypes = [P, i64, i32, P, i32, i32, i32, i64, i64, P, P]
+        L.orc_dispatch.restype = None
+        L.orc_combine.argtypes = [P, P, P, i64, i32, i32, i64, i64, P]
+        L.orc_combine.restype = None
+        for name in ("orc_bf16_from_f32_n", "orc_bf16_from_f64_n", "orc_e4m3fn_from_f32_n",
+                     "orc_f32_from_e4m3fn_n"):
+            getattr(L, name).argtypes = [P, P, i64]
+            getattr(L, name).restype = None
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a
+
+
+# ---- number formats --------------------------------------------------------
+
+def bf16_from_f32(v):
+    v = _c(v, np.float32).ravel()
+    out = np.empty(v.shape, np.uint16)
+    lib().orc_bf16_from_f32_n(_p(v), _p(out), v.size)
+    return out
+
+
+def bf16_from_f64(v):
+    v = _c(v, np.float64).ravel()
+    out = np.empty(v.shape, np.uint16)
+    lib().orc_bf16_from_f64_n(_p(v), _p(out), v.size)
+    return out
+
+
+def f32_from_bf16(b):
+    b = _c(b, np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def e4m3fn_from_f32(v):
+    v = _c(v, np.float32).ravel()
+    out = np.empty(v.shape, np.uint8)
+    lib().orc_e4m3fn_from_f32_n(_p(v), _p(out), v.size)
+    return out
+
+
+def f32_from_e4m3fn(b):
+    b = _c(b, np.uint8).ravel()
+    out = np.empty(b.shape, np.float32)
+    lib().orc_f32_from_e4m3fn_n(_p(b), _p(out), b.size)
+    return out
+
+
+# ---- the four stages -------------------------------------------------------
+
+def layout(topk_idx, num_experts, num_ranks, ranks_per_node=0):
+    """a1. Returns dict(num_tokens_per_rank, num_tokens_per_rdma_rank or None,
+    num_tokens_per_expert, is_token_in_rank[N,R] uint8)."""
+    idx = _c(topk_idx, np.int32)
+    N, K = idx.shape
+    E, R = num_experts, num_ranks
+    per_rank = np.zeros(R, np.int32)
+    per_expert = np.zeros(E, np.int32)
+    in_rank = np.zeros((N, R), np.uint8)
+    nodes = (R + ranks_per_node - 1) // ranks_per_node if ranks_per_node > 0 else 0
+    per_node = np.zeros(max(nodes, 1), np.int32) if nodes else None
+    rc = lib().orc_layout(_p(idx), N, K, E, R, ranks_per_node, _p(per_rank), _p(per_node),
+                          _p(per_expert), _p(in_rank))
+    if rc != 0:
+        raise ValueError("topk_idx holds an id outside [-1, num_experts)")
+    return dict(num_tokens_per_rank=per_rank, num_tokens_per_rdma_rank=per_node,
+                num_tokens_per_expert=per_expert, is_token_in_rank=in_rank)
+
+
+def max_slots(N, K, E, A):
+    """Receive rows needed in the worst case: every pair plus full padding."""
+    return N * K + E * (A - 1)
+
+
+def slots(topk_idx, num_experts, num_ranks, expert_alignment=1):
+    """a2. Returns dict(S, psum_expert, psum_rank, num_unaligned, slot_idx[N,K],
+    src_meta[S,2])."""
+    idx = _c(topk_idx, np.int32)
+    N, K = idx.shape
+    E, R, A = num_experts, num_ranks, expert_alignment
+    cap = max_slots(N, K, E, A)
+    psum_e = np.zeros(E + 1, np.int32)
+    psum_r = np.zeros(R + 1, np.int32)
+    unal = np.zeros(E, np.int32)
+    slot = np.zeros((N, K), np.int32)
+    meta = np.zeros((max(cap, 1), 2), np.int32)
+    S = lib().orc_slots(_p(idx), N, K, E, R, A, _p(psum_e), _p(psum_r), _p(unal), _p(slot),
+                        _p(meta), cap)
+    if S == -1:
+        raise ValueError("topk_idx holds an id outside [-1, num_experts)")
+    if S < 0:
+        raise RuntimeError("receive-row capacity exceeded")
+    return dict(S=int(S), psum_expert=psum_e, psum_rank=psum_r, num_unaligned=unal,
+                slot_idx=slot, src_meta=meta[:S].copy())
+
+
+def recv_list(psum_expert, num_experts, num_ranks, counts_as_prefix):
+    pe = _c(psum_expert, np.int32)
+    out = np.zeros(num_experts, np.int32)
+    lib().orc_recv_list(_p(pe), num_experts, num_ranks, int(bool(counts_as_prefix)), _p(out))
+    return out
+
+
+QUANT_NONE, QUANT_FP8, QUANT_INT8 = 0, 1, 2
+
+
+def dispatch(x_bits, slot_idx, num_rows, quant=QUANT_NONE, group=None, t_begin=0, t_end=None,
+             recv_x=None, recv_scales=None):
+    """a3. x_bits: uint16 [N,H] bf16 bit patterns.  Returns (recv_x, recv_scales)."""
+    x = _c(x_bits, np.uint16)
+    sl = _c(slot_idx, np.int32)
+    N, H = x.shape
+    K = sl.shape[1]
+    t_end = N if t_end is None else t_end
+    if quant == QUANT_NONE:
+        group = H
+        if recv_x is None:
+            recv_x = np.zeros((num_rows, H), np.uint16)
+        G = 1
+    else:
+        group = H if group is None else group
+        G = H // group
+        if recv_x is None:
+            recv_x = np.zeros((num_rows, H), np.uint8 if quant == QUANT_FP8 else np.int8)
+        if recv_scales is None:
+            recv_scales = np.zeros((num_rows, G), np.float32)
+    assert recv_x.flags.c_contiguous
+    lib().orc_dispatch(_p(x), N, H, _p(sl), K, quant, group, t_begin, t_end, _p(recv_x),
+                       _p(recv_scales))
+    return recv_x, recv_scales
+
+
+def combine(y_bits, topk_weights, slot_idx, t_begin=0, t_end=None, out=None):
+    """a4. y_bits uint16 [S,H]; topk_weights fp32 [N,K].  Returns uint16 [N,H]."""
+    y = _c(y_bits, np.uint16)
+    w = _c(topk_weights, np.float32)
+    sl = _c(slot_idx, np.int32)
+    N, K = sl.shape
+    H = y.shape[1]
+    t_end = N if t_end is None else t_end
+    if out is None:
+        out = np.zeros((N, H), np.uint16)
+    assert out.flags.c_contiguous
+    lib().orc_combine(_p(y), _p(w), _p(sl), N, K, H, t_begin, t_end, _p(out))
+    return out

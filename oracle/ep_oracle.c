@@ -1,0 +1,324 @@
+/*
+ * Plain CPU oracle for the MoE token shuffle.  TEST INFRASTRUCTURE ONLY:
+ * used by the tests, the smoke check and the benchmark's CPU-baseline leg,
+ * never by the product path.  Shares nothing with the HIP library.
+ *
+ * Every function is the plain definition, in the order the pages state the
+ * method; no blocking, fusion or reordering.  Sources are cited by page
+ * title and section (see ep_oracle.h for the key [P2], [P3], [P5]).
+ */
+#include "ep_oracle.h"
+
+#include <fenv.h>
+#include <math.h>
+#include <string.h>
+#include <stdlib.h>
+
+/* ------------------------------------------------------------------------ */
+/* Number formats                                                            */
+/* ------------------------------------------------------------------------ */
+
+/* Round v to the nearest number that has p significant bits and an exponent
+ * of at least emin (numbers below 2^emin share the fixed step
+ * 2^(emin - p + 1), i.e. the subnormal range), ties to even.  Dividing by a
+ * power of two is exact in fp64, so the only rounding is nearbyint() in the
+ * default round-to-nearest-even mode. */
+static double round_to_format(double v, int p, int emin)
+{
+    if (v == 0.0 || !isfinite(v)) return v;
+    int e2;
+    frexp(fabs(v), &e2);          /* |v| = m * 2^e2, m in [0.5, 1) */
+    int ex = e2 - 1;              /* 2^ex <= |v| < 2^(ex+1) */
+    if (ex < emin) ex = emin;
+    double step = ldexp(1.0, ex - (p - 1));
+    return nearbyint(v / step) * step;
+}
+
+/* bf16: 8 significant bits, fp32's exponent range (min normal 2^-126). */
+uint16_t orc_bf16_from_f64(double v)
+{
+    double r = round_to_format(v, 8, -126);
+    uint32_t sign = signbit(r) ? 0x8000u : 0u;
+    if (fabs(r) > 3.3895313892515355e38) /* largest finite bf16 */
+        return (uint16_t)(sign | 0x7F80u);      /* rounds to infinity */
+    float f = (float)r;                         /* exact: r has 8 bits */
+    uint32_t bits;
+    memcpy(&bits, &f, 4);
+    return (uint16_t)(bits >> 16);
+}
+
+uint16_t orc_bf16_from_f32(float v) { return orc_bf16_from_f64((double)v); }
+
+float orc_f32_from_bf16(uint16_t b)
+{
+    uint32_t bits = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &bits, 4);
+    return f;
+}
+
+/* OCP 8-bit floating point, E4M3FN variant ([P3] §7.4 names
+ * torch.float8_e4m3fn as the FP8 storage type): 1 sign, 4 exponent bits with
+ * bias 7, 3 mantissa bits, subnormal step 2^-9, largest finite 448, no
+ * infinities, S.1111.111 is NaN. */
+uint8_t orc_e4m3fn_from_f32(float v)
+{
+    double r = round_to_format((double)v, 4, -6);
+    uint8_t sign = signbit(r) ? 0x80 : 0x00;
+    double a = fabs(r);
+    if (a > 448.0) a = 448.0;                   /* saturate (reading) */
+    if (a == 0.0) return sign;
+    if (a < ldexp(1.0, -6)) {                   /* subnormal: a = m * 2^-9 */
+        int m = (int)(a / ldexp(1.0, -9));
+        return (uint8_t)(sign | m);
+    }
+    int e2;
+    frexp(a, &e2);
+    int ex = e2 - 1;                            /* -6 .. 8 */
+    int m = (int)((a / ldexp(1.0, ex) - 1.0) * 8.0);
+    return (uint8_t)(sign | ((ex + 7) << 3) | m);
+}
+
+float orc_f32_from_e4m3fn(uint8_t b)
+{
+    int s = b >> 7, e = (b >> 3) & 0xF, m = b & 7;
+    double a;
+    if (e == 0xF && m == 7) return NAN;
+    if (e == 0) a = ldexp((double)m, -9);
+    else a = ldexp(1.0 + m / 8.0, e - 7);
+    return (float)(s ? -a : a);
+}
+
+/* Array forms for tests. */
+void orc_bf16_from_f32_n(const float* in, uint16_t* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_bf16_from_f32(in[i]);
+}
+void orc_bf16_from_f64_n(const double* in, uint16_t* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_bf16_from_f64(in[i]);
+}
+void orc_e4m3fn_from_f32_n(const float* in, uint8_t* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3fn_from_f32(in[i]);
+}
+void orc_f32_from_e4m3fn_n(const uint8_t* in, float* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_f32_from_e4m3fn(in[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* a1: routing layout                                                        */
+/* ------------------------------------------------------------------------ */
+
+/* Expert e belongs to rank e / num_local_experts, num_local_experts =
+ * num_experts / ep_world_size ([P2] HCCL_BUFFSIZE note).  Reading: each rank
+ * owns a contiguous block of experts. */
+static int rank_of_expert(int e, int num_local_experts) { return e / num_local_experts; }
+
+static int ids_valid(const int32_t* topk_idx, int64_t n, int E)
+{
+    for (int64_t i = 0; i < n; ++i)
+        if (topk_idx[i] < -1 || topk_idx[i] >= E) return 0;
+    return 1;
+}
+
+int orc_layout(const int32_t* topk_idx, int64_t N, int K, int E, int R, int ranks_per_node,
+               int32_t* num_tokens_per_rank, int32_t* num_tokens_per_rdma_rank,
+               int32_t* num_tokens_per_expert, uint8_t* is_token_in_rank)
+{
+    if (!ids_valid(topk_idx, N * K, E)) return -1;
+    int nle = E / R;
+
+    /* num_tokens_per_expert: every (token, k) routed to the expert counts. */
+    for (int e = 0; e < E; ++e) num_tokens_per_expert[e] = 0;
+    for (int64_t t = 0; t < N; ++t)
+        for (int k = 0; k < K; ++k) {
+            int e = topk_idx[t * K + k];
+            if (e >= 0) num_tokens_per_expert[e] += 1;
+        }
+
+    /* is_token_in_rank: the token has at least one expert on the rank. */
+    for (int64_t t = 0; t < N; ++t) {
+        for (int r = 0; r < R; ++r) is_token_in_rank[t * R + r] = 0;
+        for (int k = 0; k < K; ++k) {
+            int e = topk_idx[t * K + k];
+            if (e >= 0) is_token_in_rank[t * R + rank_of_expert(e, nle)] = 1;
+        }
+    }
+
+    /* num_tokens_per_rank: tokens the rank receives (each token once). */
+    for (int r = 0; r < R; ++r) {
+        int32_t c = 0;
+        for (int64_t t = 0; t < N; ++t) c += is_token_in_rank[t * R + r];
+        num_tokens_per_rank[r] = c;
+    }
+
+    /* num_tokens_per_rdma_rank: tokens a node (ranks_per_node consecutive
+     * ranks) receives, each token once. */
+    if (ranks_per_node > 0 && num_tokens_per_rdma_rank) {
+        int nodes = (R + ranks_per_node - 1) / ranks_per_node;
+        for (int n = 0; n < nodes; ++n) {
+            int32_t c = 0;
+            for (int64_t t = 0; t < N; ++t) {
+                int hit = 0;
+                for (int r = n * ranks_per_node; r < (n + 1) * ranks_per_node && r < R; ++r)
+                    if (is_token_in_rank[t * R + r]) hit = 1;
+                c += hit;
+            }
+            num_tokens_per_rdma_rank[n] = c;
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* a2: slot assignment                                                       */
+/* ------------------------------------------------------------------------ */
+
+int64_t orc_slots(const int32_t* topk_idx, int64_t N, int K, int E, int R, int A,
+                  int32_t* psum_expert, int32_t* psum_rank, int32_t* num_unaligned,
+                  int32_t* slot_idx, int32_t* src_meta, int64_t meta_cap)
+{
+    if (!ids_valid(topk_idx, N * K, E)) return -1;
+    int nle = E / R;
+
+    for (int e = 0; e < E; ++e) num_unaligned[e] = 0;
+    for (int64_t i = 0; i < N * K; ++i)
+        if (topk_idx[i] >= 0) num_unaligned[topk_idx[i]] += 1;
+
+    /* Each expert's receive segment is its count rounded up to a multiple of
+     * expert_alignment; psum_num_recv_tokens_per_expert is the prefix of the
+     * aligned sizes ([P3] §3.1: psum vs num_unaligned field pair). */
+    psum_expert[0] = 0;
+    for (int e = 0; e < E; ++e) {
+        int32_t aligned = ((num_unaligned[e] + A - 1) / A) * A;
+        psum_expert[e + 1] = psum_expert[e] + aligned;
+    }
+    for (int r = 0; r <= R; ++r) psum_rank[r] = psum_expert[r * nle];
+
+    int64_t S = psum_expert[E];
+    if (S > meta_cap) return -2;
+    for (int64_t s = 0; s < S; ++s) {
+        src_meta[2 * s] = -1;
+        src_meta[2 * s + 1] = -1;
+    }
+    for (int64_t i = 0; i < N * K; ++i) slot_idx[i] = -1;
+
+    /* Inside an expert's segment the rows follow source token order, then k
+     * (reading of the deterministic order of [P3] §8.4; with a single source
+     * rank this is the stable order).  Padding rows sit at the segment end. */
+    for (int e = 0; e < E; ++e) {
+        int32_t next = psum_expert[e];
+        for (int64_t t = 0; t < N; ++t)
+            for (int k = 0; k < K; ++k)
+                if (topk_idx[t * K + k] == e) {
+                    slot_idx[t * K + k] = next;
+                    src_meta[2 * (int64_t)next] = (int32_t)t;
+                    src_meta[2 * (int64_t)next + 1] = k;
+                    next += 1;
+                }
+    }
+    return S;
+}
+
+void orc_recv_list(const int32_t* psum_expert, int E, int R, int counts_as_prefix, int32_t* list)
+{
+    int nle = E / R;
+    for (int e = 0; e < E; ++e) {
+        int32_t c = psum_expert[e + 1] - psum_expert[e];
+        if (counts_as_prefix && e % nle != 0) c += list[e - 1];
+        list[e] = c;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* a3: dispatch                                                              */
+/* ------------------------------------------------------------------------ */
+
+/* Per-group symmetric quantisation.  Readings (the pages name the modes
+ * -- FP8 with 128-element groups, int8 group 128 or channel = hidden -- but
+ * not the arithmetic): amax = max |x| over the group, floored at 1e-4;
+ * scale = amax / qmax in fp32 with qmax = 448 (E4M3FN) or 127 (int8);
+ * code = x / scale in fp32, rounded to nearest-even into the format
+ * (E4M3FN saturating; int8 clamped to [-127, 127]). */
+static float group_scale(const uint16_t* xg, int len, float qmax)
+{
+    float amax = 0.0f;
+    for (int i = 0; i < len; ++i) {
+        float a = fabsf(orc_f32_from_bf16(xg[i]));
+        if (a > amax) amax = a;
+    }
+    if (amax < 1e-4f) amax = 1e-4f;
+    return amax / qmax;
+}
+
+static int8_t int8_code(float q)
+{
+    double r = nearbyint((double)q);
+    if (r > 127.0) r = 127.0;
+    if (r < -127.0) r = -127.0;
+    return (int8_t)r;
+}
+
+void orc_dispatch(const uint16_t* x, int64_t N, int H, const int32_t* slot_idx, int K,
+                  int quant, int group, int64_t t_begin, int64_t t_end,
+                  void* recv_x, float* recv_scales)
+{
+    (void)N;
+    if (quant == 0) {
+        uint16_t* rx = (uint16_t*)recv_x;
+        for (int64_t t = t_begin; t < t_end; ++t)
+            for (int k = 0; k < K; ++k) {
+                int64_t s = slot_idx[t * K + k];
+                if (s < 0) continue;
+                for (int h = 0; h < H; ++h) rx[s * H + h] = x[t * H + h];
+            }
+        return;
+    }
+
+    int G = H / group;
+    float qmax = (quant == 1) ? 448.0f : 127.0f;
+    uint8_t* codes = (uint8_t*)malloc((size_t)H);
+    float* scales = (float*)malloc(sizeof(float) * (size_t)G);
+    uint8_t* rx = (uint8_t*)recv_x;
+    for (int64_t t = t_begin; t < t_end; ++t) {
+        const uint16_t* xt = x + t * H;
+        for (int g = 0; g < G; ++g) {
+            float scale = group_scale(xt + (int64_t)g * group, group, qmax);
+            scales[g] = scale;
+            for (int i = g * group; i < (g + 1) * group; ++i) {
+                float q = orc_f32_from_bf16(xt[i]) / scale;
+                codes[i] = (quant == 1) ? orc_e4m3fn_from_f32(q) : (uint8_t)int8_code(q);
+            }
+        }
+        for (int k = 0; k < K; ++k) {
+            int64_t s = slot_idx[t * K + k];
+            if (s < 0) continue;
+            for (int h = 0; h < H; ++h) rx[s * H + h] = codes[h];
+            for (int g = 0; g < G; ++g) recv_scales[s * G + g] = scales[g];
+        }
+    }
+    free(codes);
+    free(scales);
+}
+
+/* ------------------------------------------------------------------------ */
+/* a4: combine                                                               */
+/* ------------------------------------------------------------------------ */
+
+void orc_combine(const uint16_t* y, const float* topk_weights, const int32_t* slot_idx,
+                 int64_t N, int K, int H, int64_t t_begin, int64_t t_end, uint16_t* out)
+{
+    (void)N;
+    for (int64_t t = t_begin; t < t_end; ++t)
+        for (int h = 0; h < H; ++h) {
+            double acc = 0.0;
+            for (int k = 0; k < K; ++k) {
+                int64_t s = slot_idx[t * K + k];
+                if (s < 0) continue;
+                acc += (double)topk_weights[t * K + k] * (double)orc_f32_from_bf16(y[s * H + h]);
+            }
+            out[t * H + h] = orc_bf16_from_f64(acc);
+        }
+}

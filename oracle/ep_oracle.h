@@ -1,0 +1,108 @@
+/*
+ * Plain CPU oracle for the MoE expert-parallel token shuffle (routing layout,
+ * slot assignment, dispatch with optional quantisation, weighted combine).
+ *
+ * TEST INFRASTRUCTURE ONLY.  This library exists so that tests, the smoke
+ * check and the CPU-baseline leg of the benchmark can check the HIP library
+ * against an independent, obviously-correct definition.  Nothing in the
+ * product path links, loads or calls it, and it shares no code, header or
+ * constant with the HIP library.
+ *
+ * Sources (web pages), cited by title and section:
+ *   [P3] "DeepEP V1 vs V2 深度对比分析" (backyes.github.io):
+ *        §2.1 (get_dispatch_layout outputs), §2.2 (unified dispatch),
+ *        §3.1 (EPHandle fields), §3.2 (cached dispatch), §7.4 (FP8 storage
+ *        type float8_e4m3fn), §8.4 (deterministic sort).
+ *   [P2] sgl-kernel-npu "A2_DEEPEP.md": API table (dispatch/combine pair),
+ *        the HCCL_BUFFSIZE note (non-layered receive bound,
+ *        num_local_experts = num_experts / ep_world_size), the "Ant moving
+ *        home" long-sequence rounds, the int8 prefill quantisation option and
+ *        the MOE_EXPERT_TOKEN_NUMS_TYPE count/prefix option.
+ *   [P5] Aliyun "DeepEP 通信库使用指南（v2.1）" §1.3.1 (int8 quant_size:
+ *        group mode 128, channel mode = hidden).
+ *
+ * Where the pages are silent the oracle takes one stated reading; every
+ * reading is listed with the function that takes it.
+ *
+ * Floating point: quantisation codes are decided in fp32 (the precision the
+ * kernels decide them in); scales are fp32; the combine sum is formed in
+ * fp64 and rounded once to bf16.
+ *
+ * Parity status: every function here is pinned by the CPU test suite
+ * (closed forms, exhaustive format checks against torch's converters,
+ * numpy library routines, brute force, exact rational sums, invariants).
+ */
+#ifndef EP_ORACLE_H
+#define EP_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- number formats (written from the format definitions) ---- */
+
+/* fp32 -> bf16 bits, round to nearest, ties to even (finite inputs). */
+uint16_t orc_bf16_from_f32(float v);
+/* fp64 -> bf16 bits with a single rounding (nearest, ties to even). */
+uint16_t orc_bf16_from_f64(double v);
+/* bf16 bits -> fp32 (exact). */
+float orc_f32_from_bf16(uint16_t b);
+/* fp32 -> OCP FP8 E4M3FN byte: nearest, ties to even, |v| beyond the
+ * largest finite value (448) saturates to +-448; NaN is never produced. */
+uint8_t orc_e4m3fn_from_f32(float v);
+/* OCP FP8 E4M3FN byte -> fp32 (0x7F/0xFF decode to NaN). */
+float orc_f32_from_e4m3fn(uint8_t b);
+
+/* ---- a1: routing layout ([P3] §2.1) ----
+ * topk_idx: int32 [N,K], entries in [-1, E); -1 = masked.
+ * Outputs: num_tokens_per_expert [E] (pairs), num_tokens_per_rank [R]
+ * (distinct tokens), is_token_in_rank u8 [N,R], and, when ranks_per_node > 0
+ * and num_tokens_per_rdma_rank != NULL, num_tokens_per_rdma_rank
+ * [ceil(R/ranks_per_node)] (distinct tokens per node).
+ * Returns 0, or -1 if an id lies outside [-1, E) (outputs then undefined). */
+int orc_layout(const int32_t* topk_idx, int64_t N, int K, int E, int R, int ranks_per_node,
+               int32_t* num_tokens_per_rank, int32_t* num_tokens_per_rdma_rank,
+               int32_t* num_tokens_per_expert, uint8_t* is_token_in_rank);
+
+/* ---- a2: slot assignment ([P3] §3.1, §8.4) ----
+ * psum_expert [E+1]: exclusive prefix of the A-aligned per-expert counts.
+ * psum_rank [R+1]:   psum_expert at each rank's first expert.
+ * num_unaligned [E]: raw per-expert counts.
+ * slot_idx [N,K]:    receive row of each (t,k), -1 where masked.
+ * src_meta [meta_cap,2]: (t,k) of each receive row, (-1,-1) on padding rows.
+ * Returns S (total receive rows incl. padding), -1 on a bad id, -2 if
+ * S > meta_cap. */
+int64_t orc_slots(const int32_t* topk_idx, int64_t N, int K, int E, int R, int A,
+                  int32_t* psum_expert, int32_t* psum_rank, int32_t* num_unaligned,
+                  int32_t* slot_idx, int32_t* src_meta, int64_t meta_cap);
+
+/* Host list of received tokens per expert ([P2] MOE_EXPERT_TOKEN_NUMS_TYPE):
+ * counts_as_prefix == 0: aligned count of each expert;
+ * counts_as_prefix != 0: inclusive prefix of those counts restarting at each
+ * rank's first local expert. list [E]. */
+void orc_recv_list(const int32_t* psum_expert, int E, int R, int counts_as_prefix, int32_t* list);
+
+/* ---- a3: dispatch ([P3] §2.1/§2.2; quantisation [P5] §1.3.1, [P3] §7.4) ----
+ * x: bf16 bits [N,H]. For every t in [t_begin, t_end) and every k with
+ * slot_idx[t,k] >= 0, receive row slot_idx[t,k] receives token t.
+ * quant 0: recv_x is bf16 [*,H] (bit copy), recv_scales unused.
+ * quant 1: recv_x is E4M3FN bytes [*,H]; quant 2: int8 [*,H].
+ *   For both, group = elements per scale (128 or H), G = H/group, and
+ *   recv_scales is fp32 [*,G]. */
+void orc_dispatch(const uint16_t* x, int64_t N, int H, const int32_t* slot_idx, int K,
+                  int quant, int group, int64_t t_begin, int64_t t_end,
+                  void* recv_x, float* recv_scales);
+
+/* ---- a4: combine ([P2] API table; weighted reduce) ----
+ * out[t,:] = bf16( sum over k with slot_idx[t,k] >= 0 of w[t,k] * y[slot,:] ),
+ * sum formed in fp64, rounded once.  Rows with every k masked are +0. */
+void orc_combine(const uint16_t* y, const float* topk_weights, const int32_t* slot_idx,
+                 int64_t N, int K, int H, int64_t t_begin, int64_t t_end, uint16_t* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

@@ -1,0 +1,191 @@
+"""Pins of the oracle's routing layout and slot assignment.
+
+Against: a hand-worked example (tests/golden), numpy library routines
+(bincount, any-reductions, stable argsort), invariants that hold for every
+input (counts sum to N*K minus masked entries; slots are a bijection onto the
+non-padding rows; segments follow token order; the receive total stays under
+the non-layered buffer bound of 'A2_DEEPEP.md'), and exhaustive enumeration
+of tiny routings.
+"""
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden", "tiny_worked_example.json")
+
+
+def _gold():
+    with open(GOLD) as f:
+        return json.load(f)
+
+
+def test_worked_example_layout_and_slots():
+    g = _gold()
+    idx = np.array(g["topk_idx"], np.int32)
+    E, R, A = g["num_experts"], g["num_ranks"], g["expert_alignment"]
+    lay = oracle.layout(idx, E, R, ranks_per_node=1)
+    assert lay["num_tokens_per_expert"].tolist() == g["num_tokens_per_expert"]
+    assert lay["num_tokens_per_rank"].tolist() == g["num_tokens_per_rank"]
+    assert lay["is_token_in_rank"].tolist() == g["is_token_in_rank"]
+    assert lay["num_tokens_per_rdma_rank"].tolist() == g["num_tokens_per_rdma_rank_ranks_per_node_1"]
+    lay2 = oracle.layout(idx, E, R, ranks_per_node=2)
+    assert lay2["num_tokens_per_rdma_rank"].tolist() == g["num_tokens_per_rdma_rank_ranks_per_node_2"]
+    s = oracle.slots(idx, E, R, A)
+    assert s["S"] == g["S"]
+    assert s["psum_expert"].tolist() == g["psum_expert"]
+    assert s["psum_rank"].tolist() == g["psum_rank"]
+    assert s["num_unaligned"].tolist() == g["num_unaligned"]
+    assert s["slot_idx"].tolist() == g["slot_idx"]
+    assert s["src_meta"].tolist() == g["src_meta"]
+    assert oracle.recv_list(s["psum_expert"], E, R, False).tolist() == g["recv_list_counts"]
+    assert oracle.recv_list(s["psum_expert"], E, R, True).tolist() == g["recv_list_prefix"]
+
+
+def _random_routing(rng, N, K, E, mask_p=0.1, dup_p=0.1):
+    idx = rng.integers(0, E, size=(N, K)).astype(np.int32)
+    # some rows with repeated experts, some masked entries
+    dup = rng.random((N, K)) < dup_p
+    idx[dup] = idx[:, :1].repeat(K, 1)[dup]
+    idx[rng.random((N, K)) < mask_p] = -1
+    return idx
+
+
+def _numpy_layout(idx, E, R, rpn):
+    nle = E // R
+    valid = idx >= 0
+    per_expert = np.bincount(idx[valid], minlength=E)
+    ranks = np.where(valid, idx // nle, -1)
+    in_rank = np.stack([(ranks == r).any(axis=1) for r in range(R)], axis=1)
+    per_rank = in_rank.sum(axis=0)
+    nodes = -(-R // rpn)
+    per_node = np.array([in_rank[:, n * rpn:(n + 1) * rpn].any(axis=1).sum() for n in range(nodes)])
+    return per_expert, per_rank, in_rank.astype(np.uint8), per_node
+
+
+@pytest.mark.parametrize("N,K,E,R,rpn", [(1, 1, 1, 1, 1), (37, 3, 12, 4, 2), (300, 8, 64, 16, 8),
+                                          (513, 6, 64, 8, 3), (1000, 2, 16, 4, 4)])
+def test_layout_matches_numpy(N, K, E, R, rpn):
+    rng = np.random.default_rng(N * 131 + K)
+    idx = _random_routing(rng, N, K, E)
+    lay = oracle.layout(idx, E, R, rpn)
+    pe, pr, ir, pn = _numpy_layout(idx, E, R, rpn)
+    assert np.array_equal(lay["num_tokens_per_expert"], pe)
+    assert np.array_equal(lay["num_tokens_per_rank"], pr)
+    assert np.array_equal(lay["is_token_in_rank"], ir)
+    assert np.array_equal(lay["num_tokens_per_rdma_rank"], pn)
+    # spec invariant: counts sum to N*K minus masked entries
+    assert lay["num_tokens_per_expert"].sum() == N * K - (idx == -1).sum()
+
+
+def _argsort_slots(idx, E, A):
+    """Slot of each pair from numpy's stable sort of the flattened pairs by
+    expert (masked pairs sort last)."""
+    N, K = idx.shape
+    key = np.where(idx >= 0, idx, E).ravel()
+    order = np.argsort(key, kind="stable")
+    cnt = np.bincount(key, minlength=E + 1)[:E]
+    aligned = -(-cnt // A) * A
+    psum = np.concatenate([[0], np.cumsum(aligned)])
+    starts = np.concatenate([[0], np.cumsum(cnt)])
+    slot = np.full(N * K, -1, np.int64)
+    for e in range(E):
+        pairs = order[starts[e]:starts[e] + cnt[e]]
+        slot[pairs] = psum[e] + np.arange(cnt[e])
+    return slot.reshape(N, K), psum
+
+
+def _check_slot_invariants(idx, s, E, R, A):
+    N, K = idx.shape
+    psum, S = s["psum_expert"], s["S"]
+    slot, meta = s["slot_idx"], s["src_meta"]
+    cnt = s["num_unaligned"]
+    V = int((idx >= 0).sum())
+    assert S == psum[-1]
+    assert np.all(psum % A == 0)
+    assert 0 <= S - V <= E * (A - 1)
+    assert np.all(np.diff(psum) >= cnt)
+    assert s["psum_rank"].tolist() == [int(psum[r * (E // R)]) for r in range(R + 1)]
+    # bijection valid pairs <-> non-padding rows, meta is the inverse map
+    valid = idx >= 0
+    assert np.all(slot[~valid] == -1)
+    sv = slot[valid]
+    assert len(np.unique(sv)) == V
+    ts, ks = np.nonzero(valid)
+    assert np.array_equal(meta[sv, 0], ts) and np.array_equal(meta[sv, 1], ks)
+    assert (meta[:, 0] >= 0).sum() == V
+    for e in range(E):
+        seg = meta[psum[e]:psum[e + 1]]
+        real = seg[:cnt[e]]
+        assert np.all(seg[cnt[e]:] == -1)                     # padding at the end
+        assert np.all(idx[real[:, 0], real[:, 1]] == e)       # rows hold expert e
+        key = real[:, 0].astype(np.int64) * K + real[:, 1]
+        assert np.all(np.diff(key) > 0)                       # (t, k) order
+
+
+@pytest.mark.parametrize("N,K,E,R,A", [(1, 1, 1, 1, 1), (50, 4, 8, 2, 1), (200, 8, 32, 4, 4),
+                                        (333, 6, 64, 8, 128), (777, 2, 16, 16, 3)])
+def test_slots_match_stable_argsort(N, K, E, R, A):
+    rng = np.random.default_rng(N + 7 * A)
+    idx = _random_routing(rng, N, K, E)
+    s = oracle.slots(idx, E, R, A)
+    ref_slot, ref_psum = _argsort_slots(idx, E, A)
+    assert np.array_equal(s["slot_idx"], ref_slot)
+    assert np.array_equal(s["psum_expert"], ref_psum)
+    _check_slot_invariants(idx, s, E, R, A)
+
+
+def test_slots_exhaustive_tiny():
+    """Every routing of 3 tokens x 2 choices over {-1,0,1,2,3}, E=4, R=2,
+    with alignment 1 and 3."""
+    E, R = 4, 2
+    for A in (1, 3):
+        for flat in itertools.product(range(-1, E), repeat=6):
+            idx = np.array(flat, np.int32).reshape(3, 2)
+            s = oracle.slots(idx, E, R, A)
+            ref_slot, _ = _argsort_slots(idx, E, A)
+            assert np.array_equal(s["slot_idx"], ref_slot), flat
+            _check_slot_invariants(idx, s, E, R, A)
+
+
+def test_layout_exhaustive_tiny():
+    E, R = 4, 2
+    for flat in itertools.product(range(-1, E), repeat=6):
+        idx = np.array(flat, np.int32).reshape(3, 2)
+        lay = oracle.layout(idx, E, R, 1)
+        pe, pr, ir, pn = _numpy_layout(idx, E, R, 1)
+        assert np.array_equal(lay["num_tokens_per_expert"], pe)
+        assert np.array_equal(lay["num_tokens_per_rank"], pr)
+        assert np.array_equal(lay["is_token_in_rank"], ir)
+        # K=1-like identity: per-rank count >= largest expert count on it
+        for r in range(R):
+            assert lay["num_tokens_per_rank"][r] <= 3
+
+
+def test_invalid_ids_rejected():
+    idx = np.array([[0, 4]], np.int32)
+    with pytest.raises(ValueError):
+        oracle.layout(idx, 4, 2)
+    with pytest.raises(ValueError):
+        oracle.slots(np.array([[-2, 0]], np.int32), 4, 2)
+
+
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+def test_receive_bound_on_workloads(name):
+    """S * hidden * 2B stays within bs * ep_world_size * min(nle, topk) *
+    hidden * 2B, the core term of the non-layered HCCL_BUFFSIZE minimum of
+    'A2_DEEPEP.md' (bs = tokens per rank, here the whole batch)."""
+    w = W.WORKLOADS[name]
+    idx, _ = W.routing(w)
+    s = oracle.slots(idx, w.num_experts, w.num_ranks, w.expert_alignment)
+    nle = w.num_experts // w.num_ranks
+    bound = w.num_tokens * w.num_ranks * min(nle, w.num_topk)
+    assert s["S"] * w.hidden * 2 <= bound * w.hidden * 2
+    lay = oracle.layout(idx, w.num_experts, w.num_ranks)
+    assert lay["num_tokens_per_expert"].sum() == w.num_tokens * w.num_topk - (idx == -1).sum()
+    _check_slot_invariants(idx, s, w.num_experts, w.num_ranks, w.expert_alignment)

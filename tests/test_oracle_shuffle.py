@@ -1,0 +1,218 @@
+"""Pins of the oracle's dispatch (plain and quantised) and combine.
+
+Dispatch: row copies checked by numpy fancy indexing; FP8/int8 scales by
+their closed form in numpy float32; codes by torch's float8_e4m3fn converter
+and numpy's rint applied to the fp32 quotient; dequantisation error bounds.
+Combine: the hand-worked example, exact rational sums (fractions.Fraction)
+rounded to nearest-even bf16, K=1 identity, linearity, and the north-star
+round trip (dispatch, identity experts, combine with weights summing to 1
+returns x bit for bit).  Rounds: per-range calls equal the one-shot result.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden", "tiny_worked_example.json")
+
+
+def _bf16_bits(t):
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def _x(N, H, seed):
+    return _bf16_bits(W.activations(N, H, seed))
+
+
+def _setup(N, K, E, R, A, H, seed, mask_p=0.0):
+    rng = np.random.default_rng(seed)
+    idx = np.argsort(rng.random((N, E)), axis=1)[:, :K].astype(np.int32)
+    idx[rng.random((N, K)) < mask_p] = -1
+    s = oracle.slots(idx, E, R, A)
+    return idx, s, _x(N, H, seed)
+
+
+def test_dispatch_copies_rows():
+    idx, s, x = _setup(300, 6, 32, 4, 8, 96, 5, mask_p=0.1)
+    recv, _ = oracle.dispatch(x, s["slot_idx"], s["S"])
+    meta = s["src_meta"]
+    real = meta[:, 0] >= 0
+    assert np.array_equal(recv[real], x[meta[real, 0]])
+    assert np.all(recv[~real] == 0)      # padding rows untouched
+
+
+@pytest.mark.parametrize("quant,group,H", [(oracle.QUANT_FP8, 128, 512),
+                                          (oracle.QUANT_INT8, 128, 384),
+                                          (oracle.QUANT_INT8, 256, 256)])
+def test_quantised_dispatch_pins(quant, group, H):
+    idx, s, x = _setup(200, 4, 16, 4, 1, H, 9, mask_p=0.05)
+    # include an all-zero group and a tiny group to exercise the floor
+    x[3, :group] = 0
+    x[4, :group] = oracle.bf16_from_f32(np.full(group, 1e-6, np.float32))
+    recv, sc = oracle.dispatch(x, s["slot_idx"], s["S"], quant=quant, group=group)
+    G = H // group
+    xf = oracle.f32_from_bf16(x).reshape(-1, G, group)
+    qmax = np.float32(448.0 if quant == oracle.QUANT_FP8 else 127.0)
+    amax = np.maximum(np.abs(xf).max(axis=2), np.float32(1e-4)).astype(np.float32)
+    scale = (amax / qmax).astype(np.float32)                   # closed form, fp32
+    q = (xf / scale[:, :, None]).astype(np.float32)             # fp32 quotient
+    if quant == oracle.QUANT_FP8:
+        codes = torch.from_numpy(q.reshape(-1, H)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        dq = oracle.f32_from_e4m3fn(codes).reshape(-1, G, group)
+    else:
+        codes = np.clip(np.rint(q), -127, 127).astype(np.int8).reshape(-1, H)
+        dq = codes.astype(np.float32).reshape(-1, G, group)
+    meta = s["src_meta"]
+    real = meta[:, 0] >= 0
+    t_of = meta[real, 0]
+    assert np.array_equal(sc[real].view(np.uint32), scale[t_of].view(np.uint32))
+    assert np.array_equal(recv[real].view(np.uint8), codes[t_of].view(np.uint8))
+    # error bound: |code*scale - x| <= half a step of the format at q, times scale
+    # (fp64 here; the slack 2^-10 covers the fp32 rounding of the quotient)
+    sc64 = scale[:, :, None].astype(np.float64)
+    err = np.abs(dq.astype(np.float64) * sc64 - xf.astype(np.float64))
+    if quant == oracle.QUANT_FP8:
+        step = np.exp2(np.floor(np.log2(np.maximum(np.abs(q), 2.0 ** -6))) - 3)
+        assert np.all(err <= 0.5 * step * sc64 * (1 + 2.0 ** -10))
+    else:
+        assert np.all(err <= 0.5 * sc64 * (1 + 2.0 ** -10))
+    # the group's largest magnitude maps to the top code
+    top = np.abs(dq).max(axis=2)
+    big = np.abs(xf).max(axis=2) > 1e-4
+    assert np.all(top[big] == qmax)
+    # all-zero group: zero codes, scale = 1e-4f / qmax
+    assert np.all(dq[3, 0] == 0) and scale[3, 0] == np.float32(np.float32(1e-4) / qmax)
+
+
+def test_int8_ties_to_even():
+    # x/scale lands exactly on k + 0.5: build a group whose amax is 127 so
+    # scale = 1 and x itself is the quotient
+    H = 128
+    x = np.zeros((1, H), np.float32)
+    x[0, 0] = 127.0
+    x[0, 1:7] = [0.5, 1.5, 2.5, -0.5, -1.5, -2.5]
+    xb = oracle.bf16_from_f32(x).reshape(1, H)
+    slot = np.array([[0]], np.int32)
+    recv, sc = oracle.dispatch(xb, slot, 1, quant=oracle.QUANT_INT8, group=H)
+    assert sc[0, 0] == 1.0
+    assert recv[0, :7].tolist() == [127, 0, 2, 2, 0, -2, -2]
+
+
+def test_worked_example_combine():
+    with open(GOLD) as f:
+        g = json.load(f)
+    slot = np.array(g["slot_idx"], np.int32)
+    H = g["combine_hidden"]
+    y = np.array([[s + 1, -(s + 1) / 2] for s in range(g["S"])], np.float32)
+    out = oracle.combine(oracle.bf16_from_f32(y).reshape(-1, H),
+                         np.array(g["topk_weights"], np.float32), slot)
+    assert np.array_equal(oracle.f32_from_bf16(out), np.array(g["combine_out"], np.float32))
+
+
+def _exact_bf16(q: Fraction) -> int:
+    """Nearest bf16 (ties to even) of an exact rational, found by comparing
+    exactly against the bf16 neighbours of a starting guess."""
+    guess = int(_bf16_bits(torch.tensor([float(q)], dtype=torch.float32).to(torch.bfloat16))[0])
+    cands = []
+    for b in range(guess - 2, guess + 3):
+        if 0 <= b <= 0xFFFF and (b & 0x7F80) != 0x7F80:
+            cands.append(b)
+    if guess & 0x7FFF == 0:          # around zero: both signs' small values
+        cands += [0x0000, 0x8000, 0x0001, 0x8001]
+
+    def val(b):
+        return Fraction(float(oracle.f32_from_bf16(np.array([b], np.uint16))[0]))
+
+    best = min(cands, key=lambda b: (abs(val(b) - q), b % 2, b & 0x8000))
+    return best
+
+
+def test_combine_exact_rational_sums():
+    rng = np.random.default_rng(21)
+    N, K, H, S = 40, 5, 16, 120
+    slot = rng.integers(-1, S, size=(N, K)).astype(np.int32)
+    w = rng.standard_normal((N, K)).astype(np.float32)
+    y = _x(S, H, 22)
+    # heavy cancellation rows: make k=1 cancel k=0 almost exactly
+    slot[:5, 0] = 3
+    slot[:5, 1] = 3
+    w[:5, 1] = -np.nextafter(w[:5, 0], np.float32(0))
+    out = oracle.combine(y, w, slot)
+    yv = oracle.f32_from_bf16(y)
+    for t in range(N):
+        for h in range(H):
+            q = sum((Fraction(float(w[t, k])) * Fraction(float(yv[slot[t, k], h]))
+                     for k in range(K) if slot[t, k] >= 0), Fraction(0))
+            want = _exact_bf16(q)
+            got = int(out[t, h])
+            if q == 0:
+                assert got in (0x0000, 0x8000)
+            else:
+                assert got == want, (t, h, q, got, want)
+
+
+def test_combine_identity_linearity_and_masks():
+    rng = np.random.default_rng(4)
+    N, K, H, S = 64, 4, 64, 200
+    y = _x(S, H, 5)
+    slot = rng.integers(0, S, size=(N, 1)).astype(np.int32)
+    out = oracle.combine(y, np.ones((N, 1), np.float32), slot)
+    assert np.array_equal(out, y[slot[:, 0]])                   # K=1, w=1
+    slot = rng.integers(-1, S, size=(N, K)).astype(np.int32)
+    w = rng.random((N, K)).astype(np.float32)
+    o1 = oracle.f32_from_bf16(oracle.combine(y, w, slot))
+    o2 = oracle.f32_from_bf16(oracle.combine(y, 2 * w, slot))
+    assert np.array_equal(2 * o1, o2)                           # exact scaling
+    slot[7, :] = -1
+    out = oracle.combine(y, w, slot)
+    assert np.all(out[7] == 0)                                  # all masked -> +0
+
+
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+def test_round_trip_returns_x(name):
+    """dispatch -> identity experts -> combine with weights summing to 1
+    gives x back bit for bit (fp32 weights sum to 1 within a few ulp, far
+    inside half a bf16 ulp)."""
+    w = W.WORKLOADS[name]
+    N = min(w.num_tokens, 512)
+    H = min(w.hidden, 512)
+    idx, _ = W.routing(w, num_tokens=N)
+    rng = np.random.default_rng(w.seed)
+    logits = rng.standard_normal(idx.shape)
+    logits[idx < 0] = -np.inf
+    wt = np.exp(logits - logits.max(axis=1, keepdims=True))
+    wt = (wt / wt.sum(axis=1, keepdims=True)).astype(np.float32)
+    wt[~np.isfinite(wt)] = 0
+    s = oracle.slots(idx, w.num_experts, w.num_ranks, w.expert_alignment)
+    x = _x(N, H, 99)
+    recv, _ = oracle.dispatch(x, s["slot_idx"], s["S"])
+    out = oracle.combine(recv, wt, s["slot_idx"])
+    live = (idx >= 0).any(axis=1)
+    assert np.array_equal(out[live], x[live])
+    assert np.all(out[~live] == 0)
+
+
+def test_rounds_equal_one_shot():
+    w = W.WORKLOADS["long_seq_int8"].scaled(num_tokens=1000, hidden=256, quant_group=256)
+    idx, wt = W.routing(w)
+    s = oracle.slots(idx, w.num_experts, w.num_ranks)
+    x = _x(1000, 256, 1)
+    r1, s1 = oracle.dispatch(x, s["slot_idx"], s["S"], quant=w.quant, group=w.quant_group)
+    r4 = np.zeros_like(r1)
+    s4 = np.zeros_like(s1)
+    for b, e in W.round_ranges(1000, 4):
+        oracle.dispatch(x, s["slot_idx"], s["S"], quant=w.quant, group=w.quant_group,
+                        t_begin=b, t_end=e, recv_x=r4, recv_scales=s4)
+    assert np.array_equal(r1, r4) and np.array_equal(s1.view(np.uint32), s4.view(np.uint32))
+    y = _x(s["S"], 256, 2)
+    o1 = oracle.combine(y, wt, s["slot_idx"])
+    o4 = np.zeros_like(o1)
+    for b, e in W.round_ranges(1000, 4):
+        oracle.combine(y, wt, s["slot_idx"], t_begin=b, t_end=e, out=o4)
+    assert np.array_equal(o1, o4)

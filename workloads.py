@@ -1,0 +1,118 @@
+"""Seeded synthetic inputs for the MoE token shuffle.
+
+Holds only input generation (a router stand-in and random activations); none
+of the shuffle's own arithmetic.  Both the HIP path's tests/benchmark and the
+CPU oracle take their inputs from here.
+
+The five workloads follow the shapes named for this path: a tiny correctness
+case, a Qwen3-30B-A3B-shaped prefill, a low-latency decode batch with FP8
+group quantisation, a DeepSeek-V3-shaped prefill with Zipf expert popularity,
+masked entries and 128-row expert alignment, and a long-sequence prefill run
+as four 8192-token rounds with per-token int8 quantisation.  The model names
+stand for shapes only; no weights or datasets are involved.
+"""
+from dataclasses import dataclass, replace
+from typing import Optional
+
+import numpy as np
+import torch
+
+QUANT_NONE, QUANT_FP8, QUANT_INT8 = 0, 1, 2
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    num_tokens: int
+    hidden: int
+    num_experts: int
+    num_ranks: int
+    num_topk: int
+    expert_alignment: int = 1
+    quant: int = QUANT_NONE
+    quant_group: int = 0          # elements per scale; 0 = not quantised
+    mask_prob: float = 0.0
+    routing: str = "uniform"      # uniform | softmax_topk | zipf
+    weights: str = "softmax"      # softmax (renormalised over chosen k) | raw
+    zipf_s: float = 1.2
+    rounds: int = 1
+    seed: int = 0
+    ranks_per_node: int = 8
+
+    def scaled(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 128, 256, 16, 4, 2, routing="softmax_topk", weights="raw",
+                     seed=1001),
+    "qwen3_30b_a3b_prefill": Workload("qwen3_30b_a3b_prefill", 4096, 2048, 128, 16, 8,
+                                      seed=1002),
+    "ll_decode_fp8": Workload("ll_decode_fp8", 128, 7168, 256, 16, 8, quant=QUANT_FP8,
+                              quant_group=128, seed=1003),
+    "deepseek_v3_prefill": Workload("deepseek_v3_prefill", 8192, 7168, 256, 16, 8,
+                                    expert_alignment=128, mask_prob=0.05, routing="zipf",
+                                    seed=1004),
+    "long_seq_int8": Workload("long_seq_int8", 32768, 4096, 64, 8, 6, quant=QUANT_INT8,
+                              quant_group=4096, rounds=4, seed=1005),
+}
+
+
+def _softmax(z, axis=-1):
+    z = z - z.max(axis=axis, keepdims=True)
+    e = np.exp(z)
+    return e / e.sum(axis=axis, keepdims=True)
+
+
+def routing(w: Workload, num_tokens: Optional[int] = None):
+    """Returns (topk_idx int32 [N,K], topk_weights float32 [N,K])."""
+    N = w.num_tokens if num_tokens is None else num_tokens
+    E, K = w.num_experts, w.num_topk
+    rng = np.random.Generator(np.random.PCG64(w.seed))
+    if w.routing == "softmax_topk":
+        p = _softmax(rng.standard_normal((N, E)))
+        idx = np.argsort(-p, axis=1, kind="stable")[:, :K]
+        wts = np.take_along_axis(p, idx, axis=1)
+    elif w.routing == "uniform":
+        idx = np.argsort(rng.random((N, E)), axis=1, kind="stable")[:, :K]
+        wts = None
+    elif w.routing == "zipf":
+        logp = -w.zipf_s * np.log(np.arange(1, E + 1, dtype=np.float64))
+        gumbel = -np.log(-np.log(rng.random((N, E))))
+        idx = np.argsort(-(logp[None, :] + gumbel), axis=1, kind="stable")[:, :K]
+        wts = None
+    else:
+        raise ValueError(w.routing)
+    idx = idx.astype(np.int32)
+    if w.mask_prob > 0:
+        idx[rng.random((N, K)) < w.mask_prob] = -1
+    if wts is None or w.weights == "softmax":
+        logits = rng.standard_normal((N, K))
+        logits[idx < 0] = -np.inf
+        wts = _softmax(logits)
+        wts[~np.isfinite(wts)] = 0.0
+    return np.ascontiguousarray(idx), np.ascontiguousarray(wts.astype(np.float32))
+
+
+def activations(rows: int, hidden: int, seed: int, device="cpu"):
+    """bf16 [rows, hidden] drawn N(0,1) in fp32 by torch's seeded generator on
+    `device`, rounded to bf16."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randn((rows, hidden), generator=g, device=device,
+                       dtype=torch.float32).to(torch.bfloat16)
+
+
+def x_seed(w: Workload) -> int:
+    return w.seed * 10 + 1
+
+
+def y_seed(w: Workload) -> int:
+    return w.seed * 10 + 2
+
+
+def round_ranges(num_tokens: int, rounds: int):
+    """Token ranges [begin, end) of `rounds` equal rounds (the last takes the
+    remainder)."""
+    per = -(-num_tokens // rounds)
+    return [(b, min(b + per, num_tokens)) for b in range(0, num_tokens, per)] or [(0, 0)]
