@@ -1,0 +1,389 @@
+// C-ABI host runtime of libep_amd.so: validation, workspace carving, handle
+// state and kernel launches.  The declarations and their contracts are in
+// include/ep.h.  Validation happens on the host before any HIP call; the
+// library never allocates device memory (the workspace is caller-owned).
+#include "ep.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "ep_internal.hpp"
+
+namespace {
+
+thread_local char g_msg[512] = "";
+
+ep_status fail(ep_status st, const char* file, int line, const char* fmt, ...)
+{
+    char body[400];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(body, sizeof(body), fmt, ap);
+    va_end(ap);
+    const char* base = strrchr(file, '/');
+    snprintf(g_msg, sizeof(g_msg), "%s:%d %s", base ? base + 1 : file, line, body);
+    return st;
+}
+
+#define EP_FAIL(st, ...) fail((st), __FILE__, __LINE__, __VA_ARGS__)
+#define EP_HIP(call)                                                                          \
+    do {                                                                                      \
+        hipError_t e_ = (call);                                                               \
+        if (e_ != hipSuccess) return EP_FAIL(EP_ERR_HIP, "%s: %s", #call, hipGetErrorString(e_)); \
+    } while (0)
+
+constexpr int64_t kAlign = 256;
+
+int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Carve {
+    int64_t ctrl, psum_expert, psum_rank, num_unaligned, recv_list, topk, slot, meta, hist,
+        rank_hist, node_hist, total;
+};
+
+int num_nodes(const ep_config& c)
+{
+    return c.ranks_per_node > 0 ? (c.num_ranks + c.ranks_per_node - 1) / c.ranks_per_node : 0;
+}
+
+int64_t max_slots_for(const ep_config& c, int64_t tokens)
+{
+    return tokens * c.num_topk + (int64_t)c.num_experts * (c.expert_alignment - 1);
+}
+
+ep_status check_config(const ep_config* c)
+{
+    if (!c) return EP_FAIL(EP_ERR_INVALID_ARG, "config is NULL");
+    if (c->hidden <= 0 || c->hidden % 8 != 0)
+        return EP_FAIL(EP_ERR_INVALID_ARG, "hidden=%d must be a positive multiple of 8", c->hidden);
+    if (c->num_topk < 1 || c->num_topk > epk::kMaxTopk)
+        return EP_FAIL(EP_ERR_INVALID_ARG, "num_topk=%d outside [1,%d]", c->num_topk, epk::kMaxTopk);
+    if (c->num_experts < 1 || c->num_experts > epk::kMaxExperts)
+        return EP_FAIL(EP_ERR_INVALID_ARG, "num_experts=%d outside [1,%d]", c->num_experts,
+                       epk::kMaxExperts);
+    if (c->num_ranks < 1 || c->num_ranks > epk::kMaxRanks || c->num_experts % c->num_ranks != 0)
+        return EP_FAIL(EP_ERR_INVALID_ARG,
+                       "num_ranks=%d must be in [1,%d] and divide num_experts=%d", c->num_ranks,
+                       epk::kMaxRanks, c->num_experts);
+    if (c->ranks_per_node < 0)
+        return EP_FAIL(EP_ERR_INVALID_ARG, "ranks_per_node=%d is negative", c->ranks_per_node);
+    if (c->expert_alignment < 1)
+        return EP_FAIL(EP_ERR_INVALID_ARG, "expert_alignment=%d < 1", c->expert_alignment);
+    if (c->quant != EP_QUANT_NONE && c->quant != EP_QUANT_FP8_E4M3 && c->quant != EP_QUANT_INT8)
+        return EP_FAIL(EP_ERR_INVALID_ARG, "quant=%d unknown", c->quant);
+    if (c->quant != EP_QUANT_NONE) {
+        if (c->quant_group == 128) {
+            if (c->hidden % 128 != 0)
+                return EP_FAIL(EP_ERR_INVALID_ARG, "quant_group 128 needs hidden %% 128 == 0 (hidden=%d)",
+                               c->hidden);
+        } else if (c->quant_group == c->hidden) {
+            if (c->hidden > epk::kWave * epk::kMaxVecPerLane * 8)
+                return EP_FAIL(EP_ERR_INVALID_ARG, "channel quantisation supports hidden <= %d (hidden=%d)",
+                               epk::kWave * epk::kMaxVecPerLane * 8, c->hidden);
+        } else {
+            return EP_FAIL(EP_ERR_INVALID_ARG, "quant_group=%d must be 128 or hidden=%d",
+                           c->quant_group, c->hidden);
+        }
+    }
+    return EP_OK;
+}
+
+ep_status carve(const ep_config& c, int64_t max_tokens, Carve* o)
+{
+    if (max_tokens < 0) return EP_FAIL(EP_ERR_INVALID_ARG, "max_tokens=%lld < 0", (long long)max_tokens);
+    const int64_t slots = max_slots_for(c, max_tokens);
+    if (slots >= (int64_t)1 << 31 || max_tokens * c.num_topk >= (int64_t)1 << 31)
+        return EP_FAIL(EP_ERR_INVALID_ARG, "max_tokens=%lld needs %lld receive rows (limit 2^31-1)",
+                       (long long)max_tokens, (long long)slots);
+    const int64_t C = (max_tokens + epk::kLayoutBlock - 1) / epk::kLayoutBlock;
+    const int64_t Cc = C > 0 ? C : 1;
+    int64_t off = 0;
+    auto take = [&](int64_t bytes) {
+        const int64_t at = off;
+        off = align_up(off + (bytes > 0 ? bytes : 4), kAlign);
+        return at;
+    };
+    o->ctrl = take(4 * epk::kCtrlWords);
+    o->psum_expert = take(4 * (int64_t)(c.num_experts + 1));
+    o->psum_rank = take(4 * (int64_t)(c.num_ranks + 1));
+    o->num_unaligned = take(4 * (int64_t)c.num_experts);
+    o->recv_list = take(4 * (int64_t)c.num_experts);
+    o->topk = take(4 * max_tokens * c.num_topk);
+    o->slot = take(4 * max_tokens * c.num_topk);
+    o->meta = take(8 * slots);
+    o->hist = take(4 * Cc * c.num_experts);
+    o->rank_hist = take(4 * Cc * c.num_ranks);
+    o->node_hist = take(4 * Cc * num_nodes(c));
+    o->total = off;
+    return EP_OK;
+}
+
+}  // namespace
+
+struct ep_handle {
+    ep_config cfg;
+    int64_t max_tokens;
+    int64_t max_slots;
+    int nodes;
+    unsigned char* ws;
+    Carve cv;
+    int64_t num_tokens;   // -1 before the first ep_get_layout
+    int64_t host_slots;   // S known on the host, else -1
+
+    template <typename T>
+    T* at(int64_t off) const { return reinterpret_cast<T*>(ws + off); }
+};
+
+extern "C" {
+
+ep_status ep_workspace_size(const ep_config* cfg, int64_t max_tokens, int64_t* bytes)
+{
+    ep_status st = check_config(cfg);
+    if (st != EP_OK) return st;
+    if (!bytes) return EP_FAIL(EP_ERR_INVALID_ARG, "bytes is NULL");
+    Carve cv;
+    st = carve(*cfg, max_tokens, &cv);
+    if (st != EP_OK) return st;
+    *bytes = cv.total;
+    return EP_OK;
+}
+
+ep_status ep_recv_capacity(const ep_config* cfg, int64_t num_tokens, int64_t* rows)
+{
+    ep_status st = check_config(cfg);
+    if (st != EP_OK) return st;
+    if (!rows) return EP_FAIL(EP_ERR_INVALID_ARG, "rows is NULL");
+    if (num_tokens < 0) return EP_FAIL(EP_ERR_INVALID_ARG, "num_tokens < 0");
+    *rows = max_slots_for(*cfg, num_tokens);
+    return EP_OK;
+}
+
+ep_status ep_handle_init(const ep_config* cfg, int64_t max_tokens, void* d_workspace,
+                         int64_t workspace_bytes, void* stream, ep_handle** out)
+{
+    ep_status st = check_config(cfg);
+    if (st != EP_OK) return st;
+    if (!out) return EP_FAIL(EP_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    Carve cv;
+    st = carve(*cfg, max_tokens, &cv);
+    if (st != EP_OK) return st;
+    if (!d_workspace) return EP_FAIL(EP_ERR_WORKSPACE, "workspace is NULL");
+    if (!aligned(d_workspace, kAlign))
+        return EP_FAIL(EP_ERR_WORKSPACE, "workspace is not %lld-byte aligned", (long long)kAlign);
+    if (workspace_bytes < cv.total)
+        return EP_FAIL(EP_ERR_WORKSPACE, "workspace has %lld bytes, needs %lld",
+                       (long long)workspace_bytes, (long long)cv.total);
+    ep_handle* h = new (std::nothrow) ep_handle();
+    if (!h) return EP_FAIL(EP_ERR_INVALID_ARG, "out of host memory");
+    h->cfg = *cfg;
+    h->max_tokens = max_tokens;
+    h->max_slots = max_slots_for(*cfg, max_tokens);
+    h->nodes = num_nodes(*cfg);
+    h->ws = static_cast<unsigned char*>(d_workspace);
+    h->cv = cv;
+    h->num_tokens = -1;
+    h->host_slots = -1;
+    hipError_t e = epk::launch_clear(h->at<uint32_t>(cv.ctrl), epk::kCtrlWords,
+                                     static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) {
+        delete h;
+        return EP_FAIL(EP_ERR_HIP, "clearing the control words: %s", hipGetErrorString(e));
+    }
+    *out = h;
+    return EP_OK;
+}
+
+void ep_handle_free(ep_handle* h) { delete h; }
+
+ep_status ep_get_layout(ep_handle* h, const int32_t* d_topk_idx, int64_t num_tokens,
+                        int32_t* d_num_tokens_per_rank, int32_t* d_num_tokens_per_rdma_rank,
+                        int32_t* d_num_tokens_per_expert, uint8_t* d_is_token_in_rank,
+                        int do_cpu_sync, int32_t* h_num_recv_tokens_per_expert,
+                        int64_t* h_num_recv_slots, void* stream)
+{
+    if (!h) return EP_FAIL(EP_ERR_INVALID_ARG, "handle is NULL");
+    if (num_tokens < 0 || num_tokens > h->max_tokens)
+        return EP_FAIL(EP_ERR_INVALID_ARG, "num_tokens=%lld outside [0, max_tokens=%lld]",
+                       (long long)num_tokens, (long long)h->max_tokens);
+    if (num_tokens > 0 && !d_topk_idx) return EP_FAIL(EP_ERR_INVALID_ARG, "topk_idx is NULL");
+    if (d_topk_idx && !aligned(d_topk_idx, 4))
+        return EP_FAIL(EP_ERR_INVALID_ARG, "topk_idx is not 4-byte aligned");
+    if (d_num_tokens_per_rdma_rank && h->nodes == 0)
+        return EP_FAIL(EP_ERR_INVALID_ARG, "num_tokens_per_rdma_rank needs ranks_per_node > 0");
+    const ep_config& c = h->cfg;
+    epk::LayoutArgs a;
+    a.topk = d_topk_idx;
+    a.num_tokens = num_tokens;
+    a.K = c.num_topk;
+    a.E = c.num_experts;
+    a.R = c.num_ranks;
+    a.nle = c.num_experts / c.num_ranks;
+    a.ranks_per_node = c.ranks_per_node;
+    a.nodes = h->nodes;
+    a.A = c.expert_alignment;
+    a.counts_as_prefix = c.counts_as_prefix ? 1 : 0;
+    a.ctrl = h->at<uint32_t>(h->cv.ctrl);
+    a.topk_clone = h->at<int32_t>(h->cv.topk);
+    a.slot_idx = h->at<int32_t>(h->cv.slot);
+    a.src_meta = h->at<int32_t>(h->cv.meta);
+    a.hist = h->at<int32_t>(h->cv.hist);
+    a.rank_hist = h->at<int32_t>(h->cv.rank_hist);
+    a.node_hist = h->at<int32_t>(h->cv.node_hist);
+    a.psum_expert = h->at<int32_t>(h->cv.psum_expert);
+    a.psum_rank = h->at<int32_t>(h->cv.psum_rank);
+    a.num_unaligned = h->at<int32_t>(h->cv.num_unaligned);
+    a.recv_list = h->at<int32_t>(h->cv.recv_list);
+    a.out_per_rank = d_num_tokens_per_rank;
+    a.out_per_node = d_num_tokens_per_rdma_rank;
+    a.out_per_expert = d_num_tokens_per_expert;
+    a.out_in_rank = d_is_token_in_rank;
+    a.in_rank_words = (c.num_ranks % 4 == 0) && aligned(d_is_token_in_rank, 4);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    EP_HIP(epk::launch_layout(a, s));
+    h->num_tokens = num_tokens;
+    h->host_slots = -1;
+    if (do_cpu_sync) {
+        uint32_t S = 0;
+        if (h_num_recv_tokens_per_expert)
+            EP_HIP(hipMemcpyAsync(h_num_recv_tokens_per_expert, a.recv_list,
+                                  sizeof(int32_t) * c.num_experts, hipMemcpyDeviceToHost, s));
+        EP_HIP(hipMemcpyAsync(&S, a.ctrl + epk::kCtrlNumSlots, sizeof(uint32_t),
+                              hipMemcpyDeviceToHost, s));
+        EP_HIP(hipStreamSynchronize(s));
+        h->host_slots = S;
+        if (h_num_recv_slots) *h_num_recv_slots = S;
+    }
+    return EP_OK;
+}
+
+ep_status ep_dispatch(const ep_handle* h, const void* d_x, int64_t token_begin, int64_t token_end,
+                      void* d_recv_x, float* d_recv_scales, int64_t recv_capacity_rows, void* stream)
+{
+    if (!h) return EP_FAIL(EP_ERR_INVALID_ARG, "handle is NULL");
+    if (h->num_tokens < 0) return EP_FAIL(EP_ERR_STATE, "ep_get_layout has not run on this handle");
+    if (token_begin < 0 || token_begin > token_end || token_end > h->num_tokens)
+        return EP_FAIL(EP_ERR_INVALID_ARG, "token range [%lld,%lld) outside [0,%lld]",
+                       (long long)token_begin, (long long)token_end, (long long)h->num_tokens);
+    if (recv_capacity_rows < 0) return EP_FAIL(EP_ERR_INVALID_ARG, "recv_capacity_rows < 0");
+    const ep_config& c = h->cfg;
+    if (token_end > token_begin) {
+        if (!d_x || !d_recv_x) return EP_FAIL(EP_ERR_INVALID_ARG, "x or recv_x is NULL");
+        if (!aligned(d_x, 16) || !aligned(d_recv_x, 16))
+            return EP_FAIL(EP_ERR_INVALID_ARG, "x and recv_x must be 16-byte aligned");
+        if (c.quant != EP_QUANT_NONE && (!d_recv_scales || !aligned(d_recv_scales, 4)))
+            return EP_FAIL(EP_ERR_INVALID_ARG, "quantised dispatch needs 4-byte aligned recv_scales");
+    }
+    if (c.quant == EP_QUANT_NONE && d_recv_scales)
+        return EP_FAIL(EP_ERR_INVALID_ARG, "recv_scales must be NULL without quantisation");
+    if (h->host_slots >= 0 && h->host_slots > recv_capacity_rows)
+        return EP_FAIL(EP_ERR_CAPACITY, "layout needs %lld receive rows, capacity is %lld",
+                       (long long)h->host_slots, (long long)recv_capacity_rows);
+    if (recv_capacity_rows >= (int64_t)1 << 31) recv_capacity_rows = ((int64_t)1 << 31) - 1;
+    epk::DispatchArgs a;
+    a.x = d_x;
+    a.t_begin = token_begin;
+    a.t_end = token_end;
+    a.H = c.hidden;
+    a.K = c.num_topk;
+    a.slot_idx = h->at<int32_t>(h->cv.slot);
+    a.recv = d_recv_x;
+    a.scales = d_recv_scales;
+    a.capacity = recv_capacity_rows;
+    a.quant = c.quant;
+    a.group = c.quant_group;
+    a.flags = h->at<uint32_t>(h->cv.ctrl) + epk::kCtrlFlags;
+    EP_HIP(epk::launch_dispatch(a, static_cast<hipStream_t>(stream)));
+    return EP_OK;
+}
+
+ep_status ep_combine(const ep_handle* h, const void* d_y, int64_t y_rows,
+                     const float* d_topk_weights, int64_t token_begin, int64_t token_end,
+                     void* d_out, void* stream)
+{
+    if (!h) return EP_FAIL(EP_ERR_INVALID_ARG, "handle is NULL");
+    if (h->num_tokens < 0) return EP_FAIL(EP_ERR_STATE, "ep_get_layout has not run on this handle");
+    if (token_begin < 0 || token_begin > token_end || token_end > h->num_tokens)
+        return EP_FAIL(EP_ERR_INVALID_ARG, "token range [%lld,%lld) outside [0,%lld]",
+                       (long long)token_begin, (long long)token_end, (long long)h->num_tokens);
+    if (y_rows < 0) return EP_FAIL(EP_ERR_INVALID_ARG, "y_rows < 0");
+    if (token_end > token_begin) {
+        if (!d_out || !d_topk_weights || (y_rows > 0 && !d_y))
+            return EP_FAIL(EP_ERR_INVALID_ARG, "y, topk_weights or out is NULL");
+        if ((d_y && !aligned(d_y, 16)) || !aligned(d_out, 16) || !aligned(d_topk_weights, 4))
+            return EP_FAIL(EP_ERR_INVALID_ARG,
+                           "y and out must be 16-byte aligned, topk_weights 4-byte aligned");
+    }
+    const ep_config& c = h->cfg;
+    epk::CombineArgs a;
+    a.y = d_y;
+    a.y_rows = y_rows;
+    a.weights = d_topk_weights;
+    a.slot_idx = h->at<int32_t>(h->cv.slot);
+    a.t_begin = token_begin;
+    a.t_end = token_end;
+    a.H = c.hidden;
+    a.K = c.num_topk;
+    a.out = d_out;
+    a.flags = h->at<uint32_t>(h->cv.ctrl) + epk::kCtrlFlags;
+    EP_HIP(epk::launch_combine(a, static_cast<hipStream_t>(stream)));
+    return EP_OK;
+}
+
+ep_status ep_handle_get_view(const ep_handle* h, ep_handle_view* v)
+{
+    if (!h || !v) return EP_FAIL(EP_ERR_INVALID_ARG, "handle or view is NULL");
+    v->psum_expert = h->at<int32_t>(h->cv.psum_expert);
+    v->psum_rank = h->at<int32_t>(h->cv.psum_rank);
+    v->num_unaligned = h->at<int32_t>(h->cv.num_unaligned);
+    v->slot_idx = h->at<int32_t>(h->cv.slot);
+    v->src_meta = h->at<int32_t>(h->cv.meta);
+    v->topk_idx = h->at<int32_t>(h->cv.topk);
+    v->num_tokens = h->num_tokens;
+    v->max_tokens = h->max_tokens;
+    v->max_slots = h->max_slots;
+    v->num_recv_slots = h->host_slots;
+    return EP_OK;
+}
+
+ep_status ep_check_error(ep_handle* h, void* stream, uint32_t* flags)
+{
+    if (!h) return EP_FAIL(EP_ERR_INVALID_ARG, "handle is NULL");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint32_t f = 0;
+    uint32_t* dflags = h->at<uint32_t>(h->cv.ctrl) + epk::kCtrlFlags;
+    EP_HIP(hipMemcpyAsync(&f, dflags, sizeof(f), hipMemcpyDeviceToHost, s));
+    EP_HIP(hipStreamSynchronize(s));
+    if (f != 0) EP_HIP(epk::launch_clear(dflags, 1, s));
+    if (flags) *flags = f;
+    if (f & (epk::kFlagBadId | epk::kFlagYRows))
+        return EP_FAIL(EP_ERR_DEVICE_INDEX, "device flags 0x%x: expert id or combine slot out of range",
+                       f);
+    if (f & epk::kFlagCapacity)
+        return EP_FAIL(EP_ERR_CAPACITY, "device flags 0x%x: dispatch slot beyond capacity", f);
+    return EP_OK;
+}
+
+const char* ep_status_str(ep_status s)
+{
+    switch (s) {
+        case EP_OK: return "EP_OK";
+        case EP_ERR_INVALID_ARG: return "EP_ERR_INVALID_ARG";
+        case EP_ERR_WORKSPACE: return "EP_ERR_WORKSPACE";
+        case EP_ERR_CAPACITY: return "EP_ERR_CAPACITY";
+        case EP_ERR_DEVICE_INDEX: return "EP_ERR_DEVICE_INDEX";
+        case EP_ERR_HIP: return "EP_ERR_HIP";
+        case EP_ERR_STATE: return "EP_ERR_STATE";
+    }
+    return "EP_ERR_UNKNOWN";
+}
+
+const char* ep_last_error_message(void) { return g_msg; }
+
+}  // extern "C"

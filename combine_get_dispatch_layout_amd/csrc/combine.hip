@@ -1,0 +1,134 @@
+// Combine on gfx950 (a4): gather each token's top-k expert outputs back to
+// source order and reduce them with the routing weights.
+//
+// What is computed ("A2_DEEPEP.md" API table: combine is the paired inverse
+// of dispatch; the reduction is weighted by topk_weights):
+//   out[t] = bf16_rne( sum over k, ascending, with slot(t,k) >= 0 of
+//                      w[t,k] * y[slot(t,k)] )
+// accumulated in fp32 with fused multiply-add, one rounding to bf16 at the
+// end (v_cvt_pk_bf16_f32).
+//
+// Design: one wavefront per (token, column chunk) of VPL 16-byte vectors per
+// lane.  All K gathers of the chunk are issued before the arithmetic so each
+// wave keeps K*VPL 16-byte loads in flight; the output is one 16-byte store
+// per vector.  No atomics: each output element is owned by one lane.
+// HBM-bound (K rows read per row written).
+#include "ep_internal.hpp"
+
+namespace epk {
+
+namespace {
+
+constexpr int kBlock = 256;
+constexpr int kWavesPerBlock = kBlock / kWave;
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    const bf16x2 v = __builtin_convertvector(f32x2{lo, hi}, bf16x2);
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+template <int KMAX, int VPL>
+__global__ __launch_bounds__(kBlock) void k_combine(CombineArgs a, int NV, int NC)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int item = blockIdx.x * kWavesPerBlock + wv;
+    const int64_t t = a.t_begin + item / NC;
+    const int c = item % NC;
+    if (t >= a.t_end) return;
+    const int K = a.K;
+    const int vbase = c * (kWave * VPL) + lane;
+
+    int slot[KMAX];
+    float wk[KMAX];
+    bool oob = false;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        int s = -1;
+        float w = 0.0f;
+        if (k < K) {
+            s = a.slot_idx[t * K + k];
+            w = a.weights[t * K + k];
+            if (s >= a.y_rows) {
+                oob = true;
+                s = -1;
+            }
+        }
+        slot[k] = s;
+        wk[k] = w;
+    }
+    if (oob && lane == 0) atomicOr(a.flags, kFlagYRows);
+
+    const u32x4* y = reinterpret_cast<const u32x4*>(a.y);
+    u32x4 yv[KMAX][VPL];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k)
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            const int v = vbase + kWave * i;
+            yv[k][i] = (slot[k] >= 0 && v < NV)
+                           ? __builtin_nontemporal_load(y + (int64_t)slot[k] * NV + v)
+                           : u32x4{0u, 0u, 0u, 0u};
+        }
+
+    float acc[VPL][8];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        if (slot[k] < 0) continue;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t wd = yv[k][i][j];
+                acc[i][2 * j] = __builtin_fmaf(wk[k], __uint_as_float(wd << 16), acc[i][2 * j]);
+                acc[i][2 * j + 1] =
+                    __builtin_fmaf(wk[k], __uint_as_float(wd & 0xFFFF0000u), acc[i][2 * j + 1]);
+            }
+    }
+
+    u32x4* orow = reinterpret_cast<u32x4*>(a.out) + t * NV;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        const int v = vbase + kWave * i;
+        if (v < NV) {
+            u32x4 o;
+            o[0] = pack_bf16x2(acc[i][0], acc[i][1]);
+            o[1] = pack_bf16x2(acc[i][2], acc[i][3]);
+            o[2] = pack_bf16x2(acc[i][4], acc[i][5]);
+            o[3] = pack_bf16x2(acc[i][6], acc[i][7]);
+            __builtin_nontemporal_store(o, orow + v);
+        }
+    }
+}
+
+template <int KMAX, int VPL>
+hipError_t launch_kv(const CombineArgs& a, int NV, hipStream_t s)
+{
+    const int NC = (NV + kWave * VPL - 1) / (kWave * VPL);
+    const int64_t items = (a.t_end - a.t_begin) * NC;
+    if (items <= 0) return hipSuccess;
+    const int blocks = (int)((items + kWavesPerBlock - 1) / kWavesPerBlock);
+    hipLaunchKernelGGL((k_combine<KMAX, VPL>), dim3(blocks), dim3(kBlock), 0, s, a, NV, NC);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s)
+{
+    const int NV = a.H / 8;
+    if (a.K <= 2) return launch_kv<2, 2>(a, NV, s);
+    if (a.K <= 4) return launch_kv<4, 2>(a, NV, s);
+    if (a.K <= 8) return launch_kv<8, 2>(a, NV, s);
+    return launch_kv<16, 1>(a, NV, s);
+}
+
+}  // namespace epk

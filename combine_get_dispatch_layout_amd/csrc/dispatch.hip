@@ -1,0 +1,198 @@
+// Dispatch on gfx950 (a3): scatter each token's hidden row to its receive
+// rows, optionally quantised.
+//
+// What is computed ("DeepEP V1 vs V2 深度对比分析" §2.1/§2.2, expand form:
+// one receive row per (token, k); quantisation modes from Aliyun "DeepEP
+// 通信库使用指南（v2.1）" §1.3.1 -- group of 128 or channel = hidden -- and
+// "A2_DEEPEP.md" int8 prefill option; FP8 storage type float8_e4m3fn per
+// §7.4 of the first page):
+//   recv[slot(t,k)] = x[t]                          (bf16, bit copy), or
+//   scale = max(amax over the group, 1e-4) / Q,     Q = 448 (E4M3FN) / 127 (int8)
+//   code  = round_nearest_even(x / scale)           (fp32 division)
+//
+// Design: one wavefront per (token, column chunk).  A chunk is VPL 16-byte
+// vectors per lane, lane-contiguous, so each load and store instruction of
+// the wave covers 1 KiB of one row.  The row is read once into registers and
+// written to each of the token's K rows; slots are wave-uniform scalar loads.
+// For 128-element groups a group is exactly 16 lanes x one vector, so the
+// group max is a 4-step butterfly inside a 16-lane row; a channel scale is a
+// full-wave reduction (the chunk then covers the whole row).  Padding rows
+// are never written.  HBM-bound: no LDS, no MFMA.
+#include "ep_internal.hpp"
+
+namespace epk {
+
+namespace {
+
+constexpr int kBlock = 256;
+constexpr int kWavesPerBlock = kBlock / kWave;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+template <int WIDTH>
+__device__ __forceinline__ float group_max(float v)
+{
+#pragma unroll
+    for (int m = 1; m < WIDTH; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, WIDTH));
+    return v;
+}
+
+__device__ __forceinline__ uint32_t pack_int8x4(float a, float b, float c, float d)
+{
+    const int ia = (int)fminf(fmaxf(rintf(a), -127.0f), 127.0f);
+    const int ib = (int)fminf(fmaxf(rintf(b), -127.0f), 127.0f);
+    const int ic = (int)fminf(fmaxf(rintf(c), -127.0f), 127.0f);
+    const int id = (int)fminf(fmaxf(rintf(d), -127.0f), 127.0f);
+    return (uint32_t)(ia & 0xFF) | ((uint32_t)(ib & 0xFF) << 8) | ((uint32_t)(ic & 0xFF) << 16) |
+           ((uint32_t)(id & 0xFF) << 24);
+}
+
+__device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d)
+{
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    return (uint32_t)w;
+}
+
+// QUANT: 0 none, 1 E4M3FN, 2 int8.  CHANNEL: one scale per row (the chunk
+// covers the row), else one per 128 elements.
+template <int QUANT, bool CHANNEL, int VPL>
+__global__ __launch_bounds__(kBlock) void k_dispatch(DispatchArgs a, int NV, int NC)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int item = blockIdx.x * kWavesPerBlock + wv;
+    const int64_t t = a.t_begin + item / NC;
+    const int c = item % NC;
+    if (t >= a.t_end) return;
+    const int K = a.K;
+    const int vbase = c * (kWave * VPL) + lane;
+
+    const u32x4* xrow = reinterpret_cast<const u32x4*>(a.x) + t * NV;
+    u32x4 d[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        const int v = vbase + kWave * i;
+        d[i] = (v < NV) ? __builtin_nontemporal_load(xrow + v) : u32x4{0u, 0u, 0u, 0u};
+    }
+    const int32_t* slots = a.slot_idx + t * K;
+
+    if constexpr (QUANT == 0) {
+        for (int k = 0; k < K; ++k) {
+            const int s = slots[k];
+            if (s < 0) continue;
+            if (s >= a.capacity) {
+                if (lane == 0) atomicOr(a.flags, kFlagCapacity);
+                continue;
+            }
+            u32x4* dst = reinterpret_cast<u32x4*>(a.recv) + (int64_t)s * NV;
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                const int v = vbase + kWave * i;
+                if (v < NV) __builtin_nontemporal_store(d[i], dst + v);
+            }
+        }
+    } else {
+        constexpr float kQ = (QUANT == 1) ? 448.0f : 127.0f;
+        float amax[VPL];
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            float m = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                m = fmaxf(m, fmaxf(fabsf(bf16_lo(d[i][j])), fabsf(bf16_hi(d[i][j]))));
+            amax[i] = m;
+        }
+        float scale[VPL];
+        if constexpr (CHANNEL) {
+            float m = 0.0f;
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) m = fmaxf(m, amax[i]);
+            m = group_max<kWave>(m);
+            const float sc = fmaxf(m, 1e-4f) / kQ;
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) scale[i] = sc;
+        } else {
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) scale[i] = fmaxf(group_max<16>(amax[i]), 1e-4f) / kQ;
+        }
+        u32x2 code[VPL];
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            float q[8];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                q[2 * j] = bf16_lo(d[i][j]) / scale[i];
+                q[2 * j + 1] = bf16_hi(d[i][j]) / scale[i];
+            }
+            if constexpr (QUANT == 1) {
+                code[i] = u32x2{pack_fp8x4(q[0], q[1], q[2], q[3]), pack_fp8x4(q[4], q[5], q[6], q[7])};
+            } else {
+                code[i] = u32x2{pack_int8x4(q[0], q[1], q[2], q[3]), pack_int8x4(q[4], q[5], q[6], q[7])};
+            }
+        }
+        const int G = CHANNEL ? 1 : NV / 16;
+        for (int k = 0; k < K; ++k) {
+            const int s = slots[k];
+            if (s < 0) continue;
+            if (s >= a.capacity) {
+                if (lane == 0) atomicOr(a.flags, kFlagCapacity);
+                continue;
+            }
+            u32x2* dst = reinterpret_cast<u32x2*>(a.recv) + (int64_t)s * NV;
+            float* srow = a.scales + (int64_t)s * G;
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                const int v = vbase + kWave * i;
+                if (v < NV) {
+                    __builtin_nontemporal_store(code[i], dst + v);
+                    if constexpr (CHANNEL) {
+                        if (v == 0) srow[0] = scale[i];
+                    } else {
+                        if ((lane & 15) == 0) srow[v / 16] = scale[i];
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <int QUANT, bool CHANNEL, int VPL>
+hipError_t launch_v(const DispatchArgs& a, int NV, hipStream_t s)
+{
+    const int NC = (NV + kWave * VPL - 1) / (kWave * VPL);
+    const int64_t items = (a.t_end - a.t_begin) * NC;
+    if (items <= 0) return hipSuccess;
+    const int blocks = (int)((items + kWavesPerBlock - 1) / kWavesPerBlock);
+    hipLaunchKernelGGL((k_dispatch<QUANT, CHANNEL, VPL>), dim3(blocks), dim3(kBlock), 0, s, a, NV,
+                       NC);
+    return hipGetLastError();
+}
+
+// Channel scales need the whole row in one wave: smallest VPL with
+// 64*VPL >= NV.
+template <int QUANT>
+hipError_t launch_channel(const DispatchArgs& a, int NV, hipStream_t s)
+{
+    if (NV <= 64) return launch_v<QUANT, true, 1>(a, NV, s);
+    if (NV <= 128) return launch_v<QUANT, true, 2>(a, NV, s);
+    if (NV <= 256) return launch_v<QUANT, true, 4>(a, NV, s);
+    if (NV <= 512) return launch_v<QUANT, true, 8>(a, NV, s);
+    return launch_v<QUANT, true, 16>(a, NV, s);
+}
+
+}  // namespace
+
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s)
+{
+    const int NV = a.H / 8;
+    const bool channel = a.quant != 0 && a.group == a.H && a.H != 128;
+    switch (a.quant) {
+        case 0: return launch_v<0, false, 1>(a, NV, s);
+        case 1: return channel ? launch_channel<1>(a, NV, s) : launch_v<1, false, 1>(a, NV, s);
+        default: return channel ? launch_channel<2>(a, NV, s) : launch_v<2, false, 1>(a, NV, s);
+    }
+}
+
+}  // namespace epk

@@ -1,0 +1,82 @@
+// Internal interface between the C-ABI host runtime (api.cpp) and the HIP
+// kernels (layout.hip, dispatch.hip, combine.hip).  gfx950 only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace epk {
+
+constexpr int kWave = 64;
+constexpr int kMaxTopk = 16;
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxRanks = 1024;
+// Tokens per layout block: 4 waves, one token per lane.
+constexpr int kLayoutBlock = 256;
+// Largest row, in 16-byte vectors, that one wave can hold for a whole-row
+// (channel) quantisation scale: 64 lanes x 16 vectors = 8192 bf16.
+constexpr int kMaxVecPerLane = 16;
+
+constexpr uint32_t kFlagBadId = 1u;
+constexpr uint32_t kFlagCapacity = 2u;
+constexpr uint32_t kFlagYRows = 4u;
+
+// Control words at the start of the workspace.
+enum CtrlWord { kCtrlFlags = 0, kCtrlNumSlots = 1, kCtrlWords = 64 };
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+struct LayoutArgs {
+    const int32_t* topk;        // [N,K] caller's routing
+    int64_t num_tokens;         // N
+    int K, E, R, nle, ranks_per_node, nodes, A, counts_as_prefix;
+    // handle workspace
+    uint32_t* ctrl;
+    int32_t* topk_clone;        // [N,K]
+    int32_t* slot_idx;          // [N,K]
+    int32_t* src_meta;          // [max_slots,2]
+    int32_t* hist;              // [C,E]  block histograms -> exclusive bases
+    int32_t* rank_hist;         // [C,R]
+    int32_t* node_hist;         // [C,nodes]
+    int32_t* psum_expert;       // [E+1]
+    int32_t* psum_rank;         // [R+1]
+    int32_t* num_unaligned;     // [E]
+    int32_t* recv_list;         // [E]
+    // caller outputs (nullable)
+    int32_t* out_per_rank;
+    int32_t* out_per_node;
+    int32_t* out_per_expert;
+    uint8_t* out_in_rank;
+    bool in_rank_words;         // is_token_in_rank rows may be written as u32
+};
+
+struct DispatchArgs {
+    const void* x;              // bf16 [N,H]
+    int64_t t_begin, t_end;
+    int H, K;
+    const int32_t* slot_idx;    // [N,K]
+    void* recv;                 // [cap,H] bf16 / e4m3fn / int8
+    float* scales;              // [cap,G]
+    int64_t capacity;
+    int quant, group;
+    uint32_t* flags;
+};
+
+struct CombineArgs {
+    const void* y;              // bf16 [y_rows,H]
+    int64_t y_rows;
+    const float* weights;       // [N,K]
+    const int32_t* slot_idx;    // [N,K]
+    int64_t t_begin, t_end;
+    int H, K;
+    void* out;                  // bf16 [N,H]
+    uint32_t* flags;
+};
+
+hipError_t launch_clear(uint32_t* words, int n, hipStream_t s);
+hipError_t launch_layout(const LayoutArgs& a, hipStream_t s);
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+
+}  // namespace epk

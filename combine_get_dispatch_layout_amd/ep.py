@@ -1,0 +1,300 @@
+"""Thin Python binding of libep_amd.so (include/ep.h), over torch tensors.
+
+Argument marshalling only: every stage runs in the HIP kernels of the
+library.  torch supplies device memory and the current HIP stream.  The
+functions carry the C names; each returns what the C call writes.
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libep_amd.so")
+
+EP_OK, EP_ERR_INVALID_ARG, EP_ERR_WORKSPACE, EP_ERR_CAPACITY, EP_ERR_DEVICE_INDEX, EP_ERR_HIP, \
+    EP_ERR_STATE = range(7)
+EP_QUANT_NONE, EP_QUANT_FP8_E4M3, EP_QUANT_INT8 = 0, 1, 2
+EP_FLAG_BAD_EXPERT_ID, EP_FLAG_RECV_CAPACITY, EP_FLAG_Y_ROWS = 1, 2, 4
+
+# Every symbol include/ep.h declares.
+SYMBOLS = ("ep_workspace_size", "ep_recv_capacity", "ep_handle_init", "ep_handle_free",
+           "ep_get_layout", "ep_dispatch", "ep_combine", "ep_handle_get_view", "ep_check_error",
+           "ep_status_str", "ep_last_error_message")
+
+
+class ep_config(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("num_topk", ctypes.c_int32),
+                ("num_experts", ctypes.c_int32), ("num_ranks", ctypes.c_int32),
+                ("ranks_per_node", ctypes.c_int32), ("expert_alignment", ctypes.c_int32),
+                ("quant", ctypes.c_int32), ("quant_group", ctypes.c_int32),
+                ("counts_as_prefix", ctypes.c_int32)]
+
+
+class ep_handle_view(ctypes.Structure):
+    _fields_ = [("psum_expert", ctypes.c_void_p), ("psum_rank", ctypes.c_void_p),
+                ("num_unaligned", ctypes.c_void_p), ("slot_idx", ctypes.c_void_p),
+                ("src_meta", ctypes.c_void_p), ("topk_idx", ctypes.c_void_p),
+                ("num_tokens", ctypes.c_int64), ("max_tokens", ctypes.c_int64),
+                ("max_slots", ctypes.c_int64), ("num_recv_slots", ctypes.c_int64)]
+
+
+class EpError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{status_name(status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built (there is no
+    fallback path)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.ep_workspace_size.argtypes = [P, I64, P]
+        L.ep_recv_capacity.argtypes = [P, I64, P]
+        L.ep_handle_init.argtypes = [P, I64, P, I64, P, P]
+        L.ep_handle_free.argtypes = [P]
+        L.ep_handle_free.restype = None
+        L.ep_get_layout.argtypes = [P, P, I64, P, P, P, P, I32, P, P, P]
+        L.ep_dispatch.argtypes = [P, P, I64, I64, P, P, I64, P]
+        L.ep_combine.argtypes = [P, P, I64, P, I64, I64, P, P]
+        L.ep_handle_get_view.argtypes = [P, P]
+        L.ep_check_error.argtypes = [P, P, P]
+        L.ep_status_str.argtypes = [I32]
+        L.ep_status_str.restype = ctypes.c_char_p
+        L.ep_last_error_message.argtypes = []
+        L.ep_last_error_message.restype = ctypes.c_char_p
+        for name in ("ep_workspace_size", "ep_recv_capacity", "ep_handle_init", "ep_get_layout",
+                     "ep_dispatch", "ep_combine", "ep_handle_get_view", "ep_check_error"):
+            getattr(L, name).restype = I32
+        _lib = L
+    return _lib
+
+
+def status_name(st):
+    return lib().ep_status_str(st).decode()
+
+
+def _check(st):
+    if st != EP_OK:
+        raise EpError(st, lib().ep_last_error_message().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device=None):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+@dataclass
+class Config:
+    hidden: int
+    num_topk: int
+    num_experts: int
+    num_ranks: int
+    ranks_per_node: int = 0
+    expert_alignment: int = 1
+    quant: int = EP_QUANT_NONE
+    quant_group: int = 0
+    counts_as_prefix: bool = False
+
+    def c(self):
+        return ep_config(self.hidden, self.num_topk, self.num_experts, self.num_ranks,
+                         self.ranks_per_node, self.expert_alignment, self.quant, self.quant_group,
+                         int(bool(self.counts_as_prefix)))
+
+    @property
+    def num_nodes(self):
+        return -(-self.num_ranks // self.ranks_per_node) if self.ranks_per_node > 0 else 0
+
+    @property
+    def num_groups(self):
+        return self.hidden // self.quant_group if self.quant else 0
+
+
+def ep_workspace_size(cfg: Config, max_tokens: int) -> int:
+    out = ctypes.c_int64()
+    c = cfg.c()
+    _check(lib().ep_workspace_size(ctypes.byref(c), max_tokens, ctypes.byref(out)))
+    return out.value
+
+
+def ep_recv_capacity(cfg: Config, num_tokens: int) -> int:
+    out = ctypes.c_int64()
+    c = cfg.c()
+    _check(lib().ep_recv_capacity(ctypes.byref(c), num_tokens, ctypes.byref(out)))
+    return out.value
+
+
+class Handle:
+    """Owns the C handle and keeps its workspace tensor alive."""
+
+    def __init__(self, cfg: Config, max_tokens: int, workspace: torch.Tensor, ptr: int):
+        self.cfg = cfg
+        self.max_tokens = max_tokens
+        self.workspace = workspace
+        self._ptr = ctypes.c_void_p(ptr)
+
+    @property
+    def ptr(self):
+        if not self._ptr:
+            raise RuntimeError("handle was freed")
+        return self._ptr
+
+    def free(self):
+        if self._ptr:
+            lib().ep_handle_free(self._ptr)
+            self._ptr = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+def ep_handle_init(cfg: Config, max_tokens: int, workspace: Optional[torch.Tensor] = None,
+                   device="cuda") -> Handle:
+    """Creates a handle; allocates the workspace with torch when none is
+    passed (uint8, on `device`)."""
+    nbytes = ep_workspace_size(cfg, max_tokens)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    out = ctypes.c_void_p()
+    c = cfg.c()
+    _check(lib().ep_handle_init(ctypes.byref(c), max_tokens, _ptr(workspace),
+                                workspace.numel() * workspace.element_size(),
+                                _stream(workspace.device), ctypes.byref(out)))
+    return Handle(cfg, max_tokens, workspace, out.value)
+
+
+def ep_handle_free(h: Handle):
+    h.free()
+
+
+def ep_get_layout(h: Handle, topk_idx: torch.Tensor, num_tokens_per_rank=None,
+                  num_tokens_per_rdma_rank=None, num_tokens_per_expert=None,
+                  is_token_in_rank=None, do_cpu_sync=False, alloc_outputs=True):
+    """a1 + a2.  topk_idx: int32 [N,K] on the device.  Outputs are allocated
+    (torch.empty) when not given and alloc_outputs is set.  Returns a dict of
+    the outputs; with do_cpu_sync also the host list and S."""
+    cfg = h.cfg
+    if topk_idx.dtype != torch.int32 or topk_idx.dim() != 2 or topk_idx.shape[1] != cfg.num_topk:
+        raise ValueError("topk_idx must be int32 [N, num_topk]")
+    N = topk_idx.shape[0]
+    dev = topk_idx.device
+    if alloc_outputs:
+        if num_tokens_per_rank is None:
+            num_tokens_per_rank = torch.empty(cfg.num_ranks, dtype=torch.int32, device=dev)
+        if num_tokens_per_expert is None:
+            num_tokens_per_expert = torch.empty(cfg.num_experts, dtype=torch.int32, device=dev)
+        if is_token_in_rank is None:
+            is_token_in_rank = torch.empty((N, cfg.num_ranks), dtype=torch.bool, device=dev)
+        if num_tokens_per_rdma_rank is None and cfg.num_nodes:
+            num_tokens_per_rdma_rank = torch.empty(cfg.num_nodes, dtype=torch.int32, device=dev)
+    host_list = None
+    S = ctypes.c_int64(-1)
+    if do_cpu_sync:
+        host_list = (ctypes.c_int32 * cfg.num_experts)()
+    _check(lib().ep_get_layout(h.ptr, _ptr(topk_idx), N, _ptr(num_tokens_per_rank),
+                               _ptr(num_tokens_per_rdma_rank), _ptr(num_tokens_per_expert),
+                               _ptr(is_token_in_rank), int(bool(do_cpu_sync)),
+                               host_list, ctypes.byref(S) if do_cpu_sync else None,
+                               _stream(dev)))
+    out = dict(num_tokens_per_rank=num_tokens_per_rank,
+               num_tokens_per_rdma_rank=num_tokens_per_rdma_rank,
+               num_tokens_per_expert=num_tokens_per_expert, is_token_in_rank=is_token_in_rank)
+    if do_cpu_sync:
+        out["num_recv_tokens_per_expert_list"] = list(host_list)
+        out["num_recv_slots"] = S.value
+    return out
+
+
+def ep_dispatch(h: Handle, x: torch.Tensor, recv_x: torch.Tensor,
+                recv_scales: Optional[torch.Tensor] = None, token_begin=0, token_end=None):
+    """a3.  x bf16 [N,H]; recv_x [rows,H] bf16 / uint8 (E4M3FN) / int8;
+    recv_scales fp32 [rows,G] when quantised."""
+    cfg = h.cfg
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[1] != cfg.hidden:
+        raise ValueError("x must be bf16 [N, hidden]")
+    want = {EP_QUANT_NONE: (torch.bfloat16,), EP_QUANT_FP8_E4M3: (torch.uint8, torch.float8_e4m3fn),
+            EP_QUANT_INT8: (torch.int8,)}[cfg.quant]
+    if recv_x.dtype not in want or recv_x.dim() != 2 or recv_x.shape[1] != cfg.hidden:
+        raise ValueError(f"recv_x must be {want} [rows, hidden]")
+    if cfg.quant:
+        if (recv_scales is None or recv_scales.dtype != torch.float32
+                or recv_scales.shape != (recv_x.shape[0], cfg.num_groups)):
+            raise ValueError("recv_scales must be fp32 [rows, hidden/quant_group]")
+    token_end = x.shape[0] if token_end is None else token_end
+    if not 0 <= token_begin <= token_end <= x.shape[0]:
+        raise ValueError("token range outside x")
+    _check(lib().ep_dispatch(h.ptr, _ptr(x), token_begin, token_end, _ptr(recv_x),
+                             _ptr(recv_scales), recv_x.shape[0], _stream(x.device)))
+    return recv_x, recv_scales
+
+
+def ep_combine(h: Handle, y: torch.Tensor, topk_weights: torch.Tensor, out: torch.Tensor,
+               token_begin=0, token_end=None):
+    """a4.  y bf16 [rows,H]; topk_weights fp32 [N,K]; out bf16 [N,H]."""
+    cfg = h.cfg
+    if y.dtype != torch.bfloat16 or y.dim() != 2 or y.shape[1] != cfg.hidden:
+        raise ValueError("y must be bf16 [rows, hidden]")
+    if topk_weights.dtype != torch.float32 or topk_weights.dim() != 2 \
+            or topk_weights.shape[1] != cfg.num_topk:
+        raise ValueError("topk_weights must be fp32 [N, num_topk]")
+    if out.dtype != torch.bfloat16 or out.dim() != 2 or out.shape[1] != cfg.hidden:
+        raise ValueError("out must be bf16 [N, hidden]")
+    token_end = out.shape[0] if token_end is None else token_end
+    if not 0 <= token_begin <= token_end <= min(out.shape[0], topk_weights.shape[0]):
+        raise ValueError("token range outside out / topk_weights")
+    _check(lib().ep_combine(h.ptr, _ptr(y), y.shape[0], _ptr(topk_weights), token_begin,
+                            token_end, _ptr(out), _stream(out.device)))
+    return out
+
+
+def ep_handle_get_view(h: Handle):
+    """Device arrays of the handle as int32 tensor views of its workspace."""
+    v = ep_handle_view()
+    _check(lib().ep_handle_get_view(h.ptr, ctypes.byref(v)))
+    ws = h.workspace
+    base = ws.data_ptr()
+    cfg = h.cfg
+
+    def arr(p, n):
+        off = p - base
+        return ws[off:off + 4 * n].view(torch.int32)
+
+    N = max(v.num_tokens, 0)
+    return dict(psum_expert=arr(v.psum_expert, cfg.num_experts + 1),
+                psum_rank=arr(v.psum_rank, cfg.num_ranks + 1),
+                num_unaligned=arr(v.num_unaligned, cfg.num_experts),
+                slot_idx=arr(v.slot_idx, N * cfg.num_topk).view(N, cfg.num_topk),
+                src_meta=arr(v.src_meta, 2 * v.max_slots).view(v.max_slots, 2),
+                topk_idx=arr(v.topk_idx, N * cfg.num_topk).view(N, cfg.num_topk),
+                num_tokens=v.num_tokens, max_tokens=v.max_tokens, max_slots=v.max_slots,
+                num_recv_slots=v.num_recv_slots)
+
+
+def ep_check_error(h: Handle, raise_on_error=False):
+    """Waits for the stream; returns (status, flags) and clears the flags."""
+    flags = ctypes.c_uint32()
+    st = lib().ep_check_error(h.ptr, _stream(h.workspace.device), ctypes.byref(flags))
+    if raise_on_error:
+        _check(st)
+    return st, flags.value

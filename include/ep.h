@@ -1,0 +1,194 @@
+/*
+ * ep.h -- C ABI of libep_amd.so: the MoE expert-parallel token shuffle on one
+ * MI355X (gfx950).  Four stages, each a HIP kernel path:
+ *   routing layout  -> slot assignment  -> dispatch (+quant) -> combine.
+ * Destination EP ranks are partitions of one receive buffer in HBM.
+ *
+ * Sources (web pages), cited by title and section:
+ *   [P3] "DeepEP V1 vs V2 深度对比分析" (backyes.github.io): §2.1 the
+ *        get_dispatch_layout -> dispatch -> combine call sequence and the
+ *        layout outputs; §2.2 one dispatch call with a reusable handle;
+ *        §3.1 the EPHandle fields; §3.2 cached dispatch (handle reuse, no CPU
+ *        sync); §8.4 deterministic receive order.
+ *   [P2] sgl-kernel-npu "A2_DEEPEP.md": the dispatch/combine API table; the
+ *        HCCL_BUFFSIZE note (receive bound; num_local_experts =
+ *        num_experts / ep_world_size); "Ant moving home" long-sequence
+ *        rounds; int8 prefill quantisation; MOE_EXPERT_TOKEN_NUMS_TYPE
+ *        (per-expert counts or prefix sums).
+ *   [P5] Aliyun "DeepEP 通信库使用指南（v2.1）" §1.3.1: int8 quant_size,
+ *        group mode (128) or channel mode (= hidden).
+ *
+ * Conventions for every call:
+ *   - Pointers named d_* are device pointers (HBM of the current HIP device),
+ *     h_* are host pointers.  The caller owns all memory; the library never
+ *     allocates device memory.  Device buffers are contiguous row-major.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are
+ *     stream-ordered and asynchronous unless stated otherwise.
+ *   - A handle is used by one stream at a time.
+ *   - Errors are returned as ep_status; ep_last_error_message() gives a
+ *     "file:line reason" text for the calling thread.  Invalid arguments are
+ *     rejected on the host before any HIP call.  Conditions only the device
+ *     can see (an expert id outside [-1, num_experts), a receive row beyond
+ *     the capacity passed to dispatch, a slot beyond the rows passed to
+ *     combine) set a sticky flag word in the handle's workspace -- the
+ *     offending entry is skipped, never written out of bounds -- and are
+ *     reported by ep_check_error().
+ */
+#ifndef EP_AMD_EP_H
+#define EP_AMD_EP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ep_status {
+    EP_OK = 0,
+    EP_ERR_INVALID_ARG = 1,   /* bad configuration, pointer, size or range      */
+    EP_ERR_WORKSPACE = 2,     /* workspace missing, misaligned or too small     */
+    EP_ERR_CAPACITY = 3,      /* receive rows exceed the capacity passed in     */
+    EP_ERR_DEVICE_INDEX = 4,  /* device saw an expert id or slot out of range   */
+    EP_ERR_HIP = 5,           /* a HIP runtime call failed                      */
+    EP_ERR_STATE = 6          /* handle has no layout yet                       */
+} ep_status;
+
+/* Dispatch-side quantisation ([P5] §1.3.1; [P2] int8 prefill option; FP8
+ * storage type float8_e4m3fn per [P3] §7.4). */
+enum {
+    EP_QUANT_NONE = 0,      /* recv_x is bf16, a bit copy of x                  */
+    EP_QUANT_FP8_E4M3 = 1,  /* recv_x is OCP E4M3FN bytes, one fp32 scale/group */
+    EP_QUANT_INT8 = 2       /* recv_x is int8, one fp32 scale per group         */
+};
+
+/* Flag bits reported by ep_check_error(). */
+enum {
+    EP_FLAG_BAD_EXPERT_ID = 1u,  /* topk_idx entry outside [-1, num_experts)   */
+    EP_FLAG_RECV_CAPACITY = 2u,  /* dispatch: slot >= recv_capacity_rows       */
+    EP_FLAG_Y_ROWS = 4u          /* combine: slot >= y_rows                    */
+};
+
+typedef struct ep_config {
+    int32_t hidden;            /* H: elements per token row, multiple of 8       */
+    int32_t num_topk;          /* K: experts per token, 1..16                    */
+    int32_t num_experts;       /* E: 1..1024, multiple of num_ranks              */
+    int32_t num_ranks;         /* R: simulated EP ranks, 1..1024; rank r owns
+                                  experts [r*E/R, (r+1)*E/R)                     */
+    int32_t ranks_per_node;    /* >0: also count distinct tokens per node of
+                                  this many ranks (num_tokens_per_rdma_rank)     */
+    int32_t expert_alignment;  /* A >= 1: each expert segment is padded to a
+                                  multiple of A rows ([P3] §3.1)                 */
+    int32_t quant;             /* EP_QUANT_*                                     */
+    int32_t quant_group;       /* elements per scale: 128 or hidden (quant only) */
+    int32_t counts_as_prefix;  /* host list: 0 = per-expert aligned counts,
+                                  1 = inclusive prefix restarting per rank
+                                  ([P2] MOE_EXPERT_TOKEN_NUMS_TYPE)              */
+} ep_config;
+
+typedef struct ep_handle ep_handle;
+
+/* Device arrays of a handle ([P3] §3.1 EPHandle). */
+typedef struct ep_handle_view {
+    const int32_t* psum_expert;    /* [E+1] exclusive prefix of aligned counts   */
+    const int32_t* psum_rank;      /* [R+1] psum_expert at each rank's first
+                                      expert: rank r's partition of the receive
+                                      buffer is rows [psum_rank[r], psum_rank[r+1]) */
+    const int32_t* num_unaligned;  /* [E] raw per-expert pair counts             */
+    const int32_t* slot_idx;       /* [num_tokens, K] receive row of (t,k); -1 masked */
+    const int32_t* src_meta;       /* [max_slots, 2] (t,k) of each receive row;
+                                      (-1,-1) on padding rows; rows >= S stale   */
+    const int32_t* topk_idx;       /* [num_tokens, K] clone of the routing (ids
+                                      outside [-1,E) stored as -1)               */
+    int64_t num_tokens;            /* N of the last ep_get_layout                */
+    int64_t max_tokens;            /* capacity the handle was created with       */
+    int64_t max_slots;             /* receive rows that can ever be needed:
+                                      max_tokens*K + E*(A-1)                     */
+    int64_t num_recv_slots;        /* S if known on the host (do_cpu_sync), else -1 */
+} ep_handle_view;
+
+/* Bytes of device workspace a handle needs for up to max_tokens tokens.
+ * Returns EP_ERR_INVALID_ARG for an invalid configuration. */
+ep_status ep_workspace_size(const ep_config* cfg, int64_t max_tokens, int64_t* bytes);
+
+/* Receive rows a dispatch of num_tokens tokens can need in the worst case
+ * (every pair valid, every expert fully padded): num_tokens*K + E*(A-1).
+ * Sizing recv_x / y with this many rows never triggers EP_ERR_CAPACITY. */
+ep_status ep_recv_capacity(const ep_config* cfg, int64_t num_tokens, int64_t* rows);
+
+/* Creates a handle over a caller-owned workspace (d_workspace, 256-byte
+ * aligned, at least ep_workspace_size bytes; it must stay alive and unused by
+ * anything else while the handle lives).  Clears the handle's flag word with
+ * a kernel on `stream`.  The handle (host memory) is freed by ep_handle_free. */
+ep_status ep_handle_init(const ep_config* cfg, int64_t max_tokens, void* d_workspace,
+                         int64_t workspace_bytes, void* stream, ep_handle** out);
+
+/* Frees the host-side handle; never touches the workspace.  NULL is a no-op. */
+void ep_handle_free(ep_handle* h);
+
+/* a1 + a2: routing layout and slot assignment ([P3] §2.1, §3.1, §8.4).
+ *   d_topk_idx: int32 [num_tokens, K]; -1 = masked entry; 0 <= num_tokens <=
+ *   max_tokens.  Outputs (each may be NULL to skip it):
+ *     d_num_tokens_per_rank     int32 [R]  distinct tokens with an expert on r
+ *     d_num_tokens_per_rdma_rank int32 [ceil(R/ranks_per_node)] distinct tokens
+ *                                per node (needs ranks_per_node > 0)
+ *     d_num_tokens_per_expert   int32 [E]  (t,k) pairs routed to e
+ *     d_is_token_in_rank        uint8 [num_tokens, R] 0/1
+ *   The handle receives psum_expert, psum_rank, num_unaligned, slot_idx,
+ *   src_meta and the topk clone.  Slot order inside an expert segment is
+ *   (token, k) ascending, padding rows last: one deterministic result.
+ *   do_cpu_sync != 0: waits for the stream and writes, when non-NULL,
+ *     h_num_recv_tokens_per_expert [E] (aligned counts, or per-rank inclusive
+ *     prefix if counts_as_prefix) and *h_num_recv_slots = S. */
+ep_status ep_get_layout(ep_handle* h, const int32_t* d_topk_idx, int64_t num_tokens,
+                        int32_t* d_num_tokens_per_rank, int32_t* d_num_tokens_per_rdma_rank,
+                        int32_t* d_num_tokens_per_expert, uint8_t* d_is_token_in_rank,
+                        int do_cpu_sync, int32_t* h_num_recv_tokens_per_expert,
+                        int64_t* h_num_recv_slots, void* stream);
+
+/* a3: dispatch ([P3] §2.1/§2.2 expand form: one receive row per (t,k);
+ * [P2] "Ant moving home" rounds = token ranges over one handle).
+ *   d_x: bf16 [num_tokens, H] (the full batch; row t at d_x + t*H).
+ *   Tokens [token_begin, token_end) are sent: for each (t,k) with a slot,
+ *   row slot of d_recv_x receives token t.  Padding rows are not written.
+ *   d_recv_x: [recv_capacity_rows, H] of bf16 (EP_QUANT_NONE), E4M3FN bytes
+ *     or int8; d_recv_scales: fp32 [recv_capacity_rows, H/quant_group], NULL
+ *     iff quant == EP_QUANT_NONE.  Scale = max(amax, 1e-4) / (448 or 127),
+ *     code = x / scale rounded to nearest-even (E4M3FN saturating, int8
+ *     clamped to +-127).
+ *   Reusing a handle across calls is cached dispatch ([P3] §3.2).
+ *   EP_ERR_CAPACITY if S is known on the host and exceeds the capacity;
+ *   otherwise rows beyond it are skipped and flagged on the device. */
+ep_status ep_dispatch(const ep_handle* h, const void* d_x, int64_t token_begin, int64_t token_end,
+                      void* d_recv_x, float* d_recv_scales, int64_t recv_capacity_rows,
+                      void* stream);
+
+/* a4: combine ([P2] API table: the paired inverse of dispatch).
+ *   d_y: bf16 [y_rows, H] expert outputs in receive-row order;
+ *   d_topk_weights: fp32 [num_tokens, K];  d_out: bf16 [num_tokens, H].
+ *   For t in [token_begin, token_end): out[t] = bf16_rne( sum over k with a
+ *   slot, k ascending, of w[t,k] * y[slot] ), accumulated in fp32 with fused
+ *   multiply-add.  Masked entries contribute nothing; an all-masked row is
+ *   +0.  Slots >= y_rows are skipped and flagged. */
+ep_status ep_combine(const ep_handle* h, const void* d_y, int64_t y_rows,
+                     const float* d_topk_weights, int64_t token_begin, int64_t token_end,
+                     void* d_out, void* stream);
+
+/* Device pointers and sizes held by a handle. */
+ep_status ep_handle_get_view(const ep_handle* h, ep_handle_view* view);
+
+/* Waits for `stream`, reads and clears the handle's flag word.  *flags (if
+ * non-NULL) receives the EP_FLAG_* bits.  Returns EP_ERR_DEVICE_INDEX for a
+ * bad expert id or combine slot, EP_ERR_CAPACITY for a dispatch capacity
+ * overflow, EP_OK if no flag was set. */
+ep_status ep_check_error(ep_handle* h, void* stream, uint32_t* flags);
+
+const char* ep_status_str(ep_status s);
+
+/* Text of the last error raised on the calling thread ("" if none). */
+const char* ep_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

@@ -1,0 +1,173 @@
+"""Shared parity machinery: run the HIP path through the C ABI and compare
+every output with the CPU oracle on the same seeded inputs.
+
+Parity bars (written out here, used by every GPU test):
+  * layout outputs, psum/count arrays, slot indices, source metadata and
+    bf16 dispatched rows: bit-exact;
+  * FP8 E4M3FN / int8 codes: at most one step apart on the ordered code line
+    (the kernels decide codes in fp32 exactly as the oracle does, so the
+    observed difference is expected to be zero), fp32 scales bit-exact;
+  * combine: |got - ref| <= 2^-7 * max(|ref|, |got|) (one bf16 ulp), widened
+    where cancellation makes a relative bound meaningless by the error bound
+    of a K-term fp32 fused-multiply-add chain, K * 2^-23 * sum_k |w_k y_k|
+    (K * u * sum|terms| with u = 2^-24, doubled).
+"""
+import numpy as np
+import torch
+
+import oracle
+import workloads as W
+from combine_get_dispatch_layout_amd import ep
+
+
+def bits16(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def config_of(w: W.Workload, counts_as_prefix=False):
+    return ep.Config(hidden=w.hidden, num_topk=w.num_topk, num_experts=w.num_experts,
+                     num_ranks=w.num_ranks, ranks_per_node=w.ranks_per_node,
+                     expert_alignment=w.expert_alignment, quant=w.quant,
+                     quant_group=w.quant_group if w.quant else 0,
+                     counts_as_prefix=counts_as_prefix)
+
+
+def recv_dtype(quant):
+    return {W.QUANT_NONE: torch.bfloat16, W.QUANT_FP8: torch.uint8, W.QUANT_INT8: torch.int8}[quant]
+
+
+class GpuRun:
+    """All device-side buffers of one run of the path."""
+
+    def __init__(self, w: W.Workload, idx, wts, x, y_rows=None, device="cuda", rounds=None):
+        self.w = w
+        self.cfg = config_of(w)
+        N = idx.shape[0]
+        self.h = ep.ep_handle_init(self.cfg, N, device=device)
+        self.topk = torch.from_numpy(idx).to(device)
+        self.wts = torch.from_numpy(wts).to(device)
+        self.x = x.to(device)
+        self.cap = ep.ep_recv_capacity(self.cfg, N)
+        self.recv = torch.zeros((self.cap, w.hidden), dtype=recv_dtype(w.quant), device=device)
+        self.scales = (torch.zeros((self.cap, self.cfg.num_groups), dtype=torch.float32,
+                                   device=device) if w.quant else None)
+        self.out = torch.zeros((N, w.hidden), dtype=torch.bfloat16, device=device)
+        self.rounds = rounds or W.round_ranges(N, w.rounds)
+        self.y_rows = self.cap if y_rows is None else y_rows
+
+    def layout(self, do_cpu_sync=True):
+        self.lay = ep.ep_get_layout(self.h, self.topk, do_cpu_sync=do_cpu_sync)
+        return self.lay
+
+    def dispatch(self):
+        for b, e in self.rounds:
+            ep.ep_dispatch(self.h, self.x, self.recv, self.scales, b, e)
+
+    def combine(self, y):
+        for b, e in self.rounds:
+            ep.ep_combine(self.h, y, self.wts, self.out, b, e)
+
+
+def compare_layout(run: GpuRun, idx, ref_lay, ref_slots):
+    w = run.w
+    lay = run.lay
+    assert np.array_equal(lay["num_tokens_per_expert"].cpu().numpy(), ref_lay["num_tokens_per_expert"])
+    assert np.array_equal(lay["num_tokens_per_rank"].cpu().numpy(), ref_lay["num_tokens_per_rank"])
+    assert np.array_equal(lay["is_token_in_rank"].cpu().numpy().astype(np.uint8),
+                          ref_lay["is_token_in_rank"])
+    if ref_lay["num_tokens_per_rdma_rank"] is not None:
+        assert np.array_equal(lay["num_tokens_per_rdma_rank"].cpu().numpy(),
+                              ref_lay["num_tokens_per_rdma_rank"])
+    v = ep.ep_handle_get_view(run.h)
+    S = ref_slots["S"]
+    assert lay["num_recv_slots"] == S == v["num_recv_slots"]
+    assert np.array_equal(v["psum_expert"].cpu().numpy(), ref_slots["psum_expert"])
+    assert np.array_equal(v["psum_rank"].cpu().numpy(), ref_slots["psum_rank"])
+    assert np.array_equal(v["num_unaligned"].cpu().numpy(), ref_slots["num_unaligned"])
+    assert np.array_equal(v["slot_idx"].cpu().numpy(), ref_slots["slot_idx"])
+    assert np.array_equal(v["src_meta"][:S].cpu().numpy(), ref_slots["src_meta"])
+    assert np.array_equal(v["topk_idx"].cpu().numpy(), idx)
+    lst = oracle.recv_list(ref_slots["psum_expert"], w.num_experts, w.num_ranks, False)
+    assert lay["num_recv_tokens_per_expert_list"] == lst.tolist()
+
+
+def ordered_code(c, quant):
+    c = c.astype(np.int32)
+    if quant == W.QUANT_FP8:
+        mag = c & 0x7F
+        return np.where(c & 0x80, -mag, mag)
+    return np.where(c > 127, c - 256, c)    # int8 viewed as uint8
+
+
+def compare_dispatch(run: GpuRun, ref_recv, ref_scales, ref_slots):
+    """Returns the number of quantised codes that differ (0 for bf16)."""
+    meta = ref_slots["src_meta"]
+    real = meta[:, 0] >= 0
+    S = ref_slots["S"]
+    if run.w.quant == W.QUANT_NONE:
+        got = bits16(run.recv[:S])
+        assert np.array_equal(got[real], ref_recv[:S][real])
+        return 0
+    got = run.recv[:S].view(torch.uint8).cpu().numpy()[real]
+    ref = ref_recv[:S].view(np.uint8)[real]
+    d = np.abs(ordered_code(got, run.w.quant) - ordered_code(ref, run.w.quant))
+    assert d.max(initial=0) <= 1, f"codes differ by {d.max()} steps"
+    gs = run.scales[:S].cpu().numpy()[real]
+    assert np.array_equal(gs.view(np.uint32), ref_scales[:S][real].view(np.uint32))
+    return int((d != 0).sum())
+
+
+def compare_combine(got_bits, ref_bits, y_bits, wts, slot_idx, K):
+    """Checks the combine bar; returns the number of elements that are not
+    bit-identical."""
+    got = oracle.f32_from_bf16(got_bits).astype(np.float64)
+    ref = oracle.f32_from_bf16(ref_bits).astype(np.float64)
+    d = np.abs(got - ref)
+    tol = 2.0 ** -7 * np.maximum(np.abs(ref), np.abs(got))
+    bad = np.argwhere(d > tol)
+    yv = None
+    for t, hcol in bad:
+        if yv is None:
+            yv = y_bits
+        terms = [abs(float(wts[t, k])) *
+                 abs(oracle.f32_from_bf16(yv[slot_idx[t, k], hcol:hcol + 1])[0].item())
+                 for k in range(K) if slot_idx[t, k] >= 0]
+        chain = K * 2.0 ** -23 * sum(terms)
+        assert d[t, hcol] <= tol[t, hcol] + chain, (t, hcol, got[t, hcol], ref[t, hcol], chain)
+    return int((got_bits != ref_bits).sum())
+
+
+def run_and_check(w: W.Workload, device="cuda", rounds=None, seed_x=None, seed_y=None,
+                  check_combine=True, idx=None, wts=None):
+    """Full path for workload `w` on the device and on the oracle; asserts
+    the parity bars.  Returns a dict of statistics."""
+    if idx is None:
+        idx, wts = W.routing(w)
+    N = idx.shape[0]
+    x = W.activations(N, w.hidden, seed_x if seed_x is not None else W.x_seed(w), device=device)
+    run = GpuRun(w, idx, wts, x, device=device, rounds=rounds)
+    run.layout()
+    run.dispatch()
+    st, flags = ep.ep_check_error(run.h)
+    assert st == ep.EP_OK and flags == 0
+    ref_lay = oracle.layout(idx, w.num_experts, w.num_ranks, w.ranks_per_node)
+    ref_slots = oracle.slots(idx, w.num_experts, w.num_ranks, w.expert_alignment)
+    compare_layout(run, idx, ref_lay, ref_slots)
+    x_bits = bits16(x)
+    ref_recv, ref_scales = oracle.dispatch(x_bits, ref_slots["slot_idx"], run.cap, quant=w.quant,
+                                           group=w.quant_group or None)
+    ncode = compare_dispatch(run, ref_recv, ref_scales, ref_slots)
+    stats = dict(S=ref_slots["S"], code_diffs=ncode)
+    if check_combine:
+        S = ref_slots["S"]
+        y = W.activations(max(S, 1), w.hidden,
+                          seed_y if seed_y is not None else W.y_seed(w), device=device)
+        run.combine(y)
+        st, flags = ep.ep_check_error(run.h)
+        assert st == ep.EP_OK and flags == 0
+        y_bits = bits16(y)
+        ref_out = oracle.combine(y_bits, wts, ref_slots["slot_idx"])
+        stats["combine_not_bit_identical"] = compare_combine(bits16(run.out), ref_out, y_bits, wts,
+                                                             ref_slots["slot_idx"], w.num_topk)
+    stats["run"] = run
+    return stats

@@ -1,0 +1,95 @@
+"""CPU-only checks of the C ABI: the library loads, exports every symbol that
+include/ep.h declares, and rejects invalid arguments on the host before any
+HIP call (no compute call is made without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from combine_get_dispatch_layout_amd import ep
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    with open(os.path.join(ROOT, "include", "ep.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ep_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert _declared_functions() == sorted(ep.SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = ep.lib()
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    assert ep.status_name(ep.EP_OK) == "EP_OK"
+    assert ep.status_name(ep.EP_ERR_CAPACITY) == "EP_ERR_CAPACITY"
+    assert ep.status_name(99) == "EP_ERR_UNKNOWN"
+
+
+GOOD = dict(hidden=2048, num_topk=8, num_experts=128, num_ranks=16)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(hidden=0), dict(hidden=2047), dict(num_topk=0), dict(num_topk=17),
+    dict(num_experts=0), dict(num_experts=1025), dict(num_ranks=0), dict(num_ranks=3),
+    dict(num_ranks=2048, num_experts=1024), dict(ranks_per_node=-1), dict(expert_alignment=0),
+    dict(quant=3), dict(quant=1, quant_group=64), dict(quant=2, quant_group=128, hidden=2056),
+    dict(quant=2, quant_group=16384, hidden=16384),
+])
+def test_invalid_configs_rejected(bad):
+    cfg = ep.Config(**{**GOOD, **bad})
+    with pytest.raises(ep.EpError) as ei:
+        ep.ep_workspace_size(cfg, 4096)
+    assert ei.value.status == ep.EP_ERR_INVALID_ARG
+    assert ".cpp:" in str(ei.value)        # "file:line reason"
+
+
+def test_workspace_and_capacity_sizes():
+    cfg = ep.Config(**GOOD, expert_alignment=128)
+    assert ep.ep_recv_capacity(cfg, 4096) == 4096 * 8 + 128 * 127
+    b = ep.ep_workspace_size(cfg, 4096)
+    # at least the slot, clone and metadata arrays
+    assert b >= 4096 * 8 * 4 * 2 + 8 * ep.ep_recv_capacity(cfg, 4096)
+    assert b % 256 == 0
+    with pytest.raises(ep.EpError):
+        ep.ep_workspace_size(cfg, -1)
+    with pytest.raises(ep.EpError):
+        ep.ep_workspace_size(cfg, 1 << 29)      # receive rows beyond 2^31
+
+
+def _init(cfg, max_tokens, ptr, nbytes):
+    out = ctypes.c_void_p()
+    c = cfg.c()
+    return ep.lib().ep_handle_init(ctypes.byref(c), max_tokens, ctypes.c_void_p(ptr), nbytes, None,
+                                   ctypes.byref(out)), out
+
+
+def test_handle_init_workspace_errors():
+    cfg = ep.Config(**GOOD)
+    need = ep.ep_workspace_size(cfg, 1024)
+    st, out = _init(cfg, 1024, 0, need)
+    assert st == ep.EP_ERR_WORKSPACE and not out.value
+    st, out = _init(cfg, 1024, 0x1000 + 16, need)          # misaligned
+    assert st == ep.EP_ERR_WORKSPACE
+    st, out = _init(cfg, 1024, 0x1000, need - 1)           # too small
+    assert st == ep.EP_ERR_WORKSPACE
+    assert "needs" in ep.lib().ep_last_error_message().decode()
+
+
+def test_calls_on_null_handle_rejected():
+    L = ep.lib()
+    assert L.ep_get_layout(None, None, 0, None, None, None, None, 0, None, None, None) == \
+        ep.EP_ERR_INVALID_ARG
+    assert L.ep_dispatch(None, None, 0, 0, None, None, 0, None) == ep.EP_ERR_INVALID_ARG
+    assert L.ep_combine(None, None, 0, None, 0, 0, None, None) == ep.EP_ERR_INVALID_ARG
+    assert L.ep_check_error(None, None, None) == ep.EP_ERR_INVALID_ARG
+    L.ep_handle_free(None)

@@ -1,0 +1,213 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars (see shuffle_check): layout, counts, slots, metadata and bf16 rows
+bit-exact; FP8/int8 codes within one step with fp32 scales bit-exact;
+combine within one bf16 ulp (plus the fp32 chain bound under cancellation).
+
+Sizes: every workload at full size (the sizes the benchmark times, all
+outputs compared), and reduced shapes that still span several layout blocks
+and dispatch/combine chunks with ragged tails, plus edge cases.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from combine_get_dispatch_layout_amd import ep
+from shuffle_check import GpuRun, bits16, run_and_check
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+def test_workload_full_size(name):
+    w = W.WORKLOADS[name]
+    _say(f"[parity] full {name} N={w.num_tokens} H={w.hidden}")
+    st = run_and_check(w)
+    _say(f"[parity] {name}: S={st['S']} code_diffs={st['code_diffs']} "
+         f"combine_not_bit_identical={st.get('combine_not_bit_identical')}")
+
+
+REDUCED = [
+    ("tiny", dict(num_tokens=1000)),
+    ("qwen3_30b_a3b_prefill", dict(num_tokens=777, hidden=1032)),
+    ("ll_decode_fp8", dict(num_tokens=300, hidden=1408)),
+    ("deepseek_v3_prefill", dict(num_tokens=1531, hidden=896)),
+    ("long_seq_int8", dict(num_tokens=2050, hidden=1200, quant_group=1200, rounds=3)),
+    ("long_seq_int8", dict(num_tokens=513, hidden=1024, quant_group=128)),
+    ("ll_decode_fp8", dict(num_tokens=257, hidden=2048, quant_group=2048)),
+]
+
+
+@pytest.mark.parametrize("name,kw", REDUCED)
+def test_workload_reduced(name, kw):
+    w = W.WORKLOADS[name].scaled(**kw)
+    _say(f"[parity] reduced {name} {kw}")
+    run_and_check(w)
+
+
+def _custom(N, H, E, R, K, A=1, quant=W.QUANT_NONE, group=0, mask=0.0, seed=7, rpn=8,
+            routing="uniform"):
+    return W.Workload("custom", N, H, E, R, K, expert_alignment=A, quant=quant, quant_group=group,
+                      mask_prob=mask, seed=seed, ranks_per_node=rpn, routing=routing)
+
+
+@pytest.mark.parametrize("args", [
+    dict(N=1, H=8, E=1, R=1, K=1),                        # smallest everything
+    dict(N=300, H=264, E=1024, R=1024, K=16, rpn=3),      # max E, R=E, max K, ragged H
+    dict(N=700, H=136, E=8, R=1, K=8, A=5, mask=0.3),     # one rank, odd alignment
+    dict(N=64, H=128, E=64, R=8, K=6, A=128),             # heavy padding
+    dict(N=999, H=520, E=96, R=12, K=3, rpn=5, mask=0.5),  # ragged R/node, many masked
+])
+def test_edge_shapes(args):
+    w = _custom(**args)
+    _say(f"[parity] edge {args}")
+    run_and_check(w)
+
+
+def test_duplicates_and_all_masked_rows():
+    w = _custom(N=513, H=256, E=32, R=4, K=8, A=4)
+    rng = np.random.default_rng(3)
+    idx = rng.integers(0, 32, size=(513, 8)).astype(np.int32)
+    idx[::7] = idx[::7, :1]                 # rows that repeat one expert 8 times
+    idx[5::11] = -1                         # rows with every entry masked
+    idx[rng.random(idx.shape) < 0.1] = -1
+    wts = rng.random((513, 8)).astype(np.float32)
+    _say("[parity] duplicates/all-masked")
+    run_and_check(w, idx=idx, wts=wts)
+
+
+def test_empty_batch():
+    w = _custom(N=0, H=256, E=16, R=4, K=2)
+    cfg = ep.Config(256, 2, 16, 4, ranks_per_node=2, expert_alignment=4)
+    h = ep.ep_handle_init(cfg, 16)
+    idx = torch.empty((0, 2), dtype=torch.int32, device="cuda")
+    lay = ep.ep_get_layout(h, idx, do_cpu_sync=True)
+    assert lay["num_recv_slots"] == 0
+    assert lay["num_tokens_per_expert"].cpu().tolist() == [0] * 16
+    assert lay["num_tokens_per_rank"].cpu().tolist() == [0] * 4
+    assert lay["num_tokens_per_rdma_rank"].cpu().tolist() == [0, 0]
+    x = torch.zeros((0, 256), dtype=torch.bfloat16, device="cuda")
+    recv = torch.zeros((4, 256), dtype=torch.bfloat16, device="cuda")
+    ep.ep_dispatch(h, x, recv)
+    out = torch.zeros((0, 256), dtype=torch.bfloat16, device="cuda")
+    ep.ep_combine(h, recv, torch.zeros((0, 2), device="cuda"), out)
+    assert ep.ep_check_error(h) == (ep.EP_OK, 0)
+    del w
+
+
+def test_rounds_match_one_shot_bitwise():
+    w = W.WORKLOADS["long_seq_int8"].scaled(num_tokens=8192, hidden=2048, quant_group=2048)
+    idx, wts = W.routing(w)
+    x = W.activations(8192, 2048, 5, device="cuda")
+    y = W.activations(ep.ep_recv_capacity(ep.Config(2048, 6, 64, 8), 8192), 2048, 6, device="cuda")
+    outs = []
+    for rounds in ([(0, 8192)], W.round_ranges(8192, 4), W.round_ranges(8192, 7)):
+        run = GpuRun(w, idx, wts, x, rounds=rounds)
+        run.layout()
+        run.dispatch()
+        run.combine(y)
+        torch.cuda.synchronize()
+        outs.append((bits16(run.recv), run.scales.cpu().numpy().view(np.uint32), bits16(run.out)))
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert np.array_equal(a, b)
+
+
+def test_deterministic_across_runs():
+    w = W.WORKLOADS["deepseek_v3_prefill"].scaled(num_tokens=4096, hidden=1024)
+    idx, wts = W.routing(w)
+    x = W.activations(4096, 1024, 1, device="cuda")
+    res = []
+    for _ in range(2):
+        run = GpuRun(w, idx, wts, x)
+        run.layout()
+        run.dispatch()
+        y = run.recv
+        run.combine(y)
+        v = ep.ep_handle_get_view(run.h)
+        S = run.layout()["num_recv_slots"]
+        torch.cuda.synchronize()
+        # rows of src_meta beyond S are stale workspace by contract
+        res.append((v["slot_idx"].cpu().numpy(), v["src_meta"][:S].cpu().numpy(),
+                    bits16(run.recv[:S]), bits16(run.out)))
+    for a, b in zip(*res):
+        assert np.array_equal(a, b)
+
+
+def test_round_trip_identity_experts():
+    """dispatch -> identity experts (y = recv_x) -> combine with weights that
+    sum to 1 returns x bit for bit (spec invariant), at the
+    Qwen3-30B-A3B prefill shape."""
+    w = W.WORKLOADS["qwen3_30b_a3b_prefill"]
+    idx, wts = W.routing(w)
+    x = W.activations(w.num_tokens, w.hidden, 3, device="cuda")
+    run = GpuRun(w, idx, wts, x)
+    run.layout()
+    run.dispatch()
+    run.combine(run.recv)
+    assert torch.equal(run.out.view(torch.int16), x.view(torch.int16))
+
+
+def test_invalid_expert_ids_flagged_and_skipped():
+    w = _custom(N=100, H=128, E=16, R=4, K=2)
+    idx, wts = W.routing(w)
+    bad = idx.copy()
+    bad[3, 1] = 16
+    bad[50, 0] = -7
+    x = W.activations(100, 128, 1, device="cuda")
+    run = GpuRun(w, bad, wts, x)
+    run.layout()
+    st, flags = ep.ep_check_error(run.h)
+    assert st == ep.EP_ERR_DEVICE_INDEX and flags & ep.EP_FLAG_BAD_EXPERT_ID
+    # the bad entries behave as masked ones
+    clean = bad.copy()
+    clean[3, 1] = -1
+    clean[50, 0] = -1
+    ref = oracle.slots(clean, 16, 4)
+    v = ep.ep_handle_get_view(run.h)
+    assert np.array_equal(v["slot_idx"].cpu().numpy(), ref["slot_idx"])
+    assert ep.ep_check_error(run.h) == (ep.EP_OK, 0)      # flags were cleared
+
+
+def test_capacity_checks():
+    w = _custom(N=200, H=128, E=16, R=4, K=4)
+    idx, wts = W.routing(w)
+    x = W.activations(200, 128, 1, device="cuda")
+    run = GpuRun(w, idx, wts, x)
+    run.layout(do_cpu_sync=True)
+    small = torch.zeros((100, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ep.EpError) as ei:
+        ep.ep_dispatch(run.h, x, small)
+    assert ei.value.status == ep.EP_ERR_CAPACITY
+    # S unknown on the host: the device skips rows beyond capacity and flags
+    run.layout(do_cpu_sync=False)
+    ep.ep_dispatch(run.h, x, small)
+    st, flags = ep.ep_check_error(run.h)
+    assert st == ep.EP_ERR_CAPACITY and flags == ep.EP_FLAG_RECV_CAPACITY
+    ref = oracle.slots(idx, 16, 4)
+    got = bits16(small)
+    xb = bits16(x)
+    meta = ref["src_meta"][:100]
+    assert np.array_equal(got, xb[meta[:, 0]])
+    # combine with y shorter than S flags instead of reading out of range
+    out = torch.zeros((200, 128), dtype=torch.bfloat16, device="cuda")
+    ep.ep_combine(run.h, small, run.wts, out)
+    st, flags = ep.ep_check_error(run.h)
+    assert st == ep.EP_ERR_DEVICE_INDEX and flags == ep.EP_FLAG_Y_ROWS
+
+
+def test_counts_as_prefix_host_list():
+    w = W.WORKLOADS["deepseek_v3_prefill"].scaled(num_tokens=1000, hidden=256)
+    idx, _ = W.routing(w)
+    from shuffle_check import config_of
+    h = ep.ep_handle_init(config_of(w, counts_as_prefix=True), 1000)
+    lay = ep.ep_get_layout(h, torch.from_numpy(idx).cuda(), do_cpu_sync=True)
+    s = oracle.slots(idx, w.num_experts, w.num_ranks, w.expert_alignment)
+    ref = oracle.recv_list(s["psum_expert"], w.num_experts, w.num_ranks, True)
+    assert lay["num_recv_tokens_per_expert_list"] == ref.tolist()

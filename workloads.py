@@ -59,9 +59,10 @@ WORKLOADS = {
 
 
 def _softmax(z, axis=-1):
-    z = z - z.max(axis=axis, keepdims=True)
-    e = np.exp(z)
-    return e / e.sum(axis=axis, keepdims=True)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        z = z - z.max(axis=axis, keepdims=True)
+        e = np.exp(z)
+        return e / e.sum(axis=axis, keepdims=True)
 
 
 def routing(w: Workload, num_tokens: Optional[int] = None):
