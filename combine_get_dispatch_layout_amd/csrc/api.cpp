@@ -44,7 +44,7 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 struct Carve {
     int64_t ctrl, psum_expert, psum_rank, num_unaligned, recv_list, topk, slot, meta, hist,
-        rank_hist, node_hist, total;
+        acc, total;
 };
 
 int num_nodes(const ep_config& c)
@@ -118,8 +118,7 @@ ep_status carve(const ep_config& c, int64_t max_tokens, Carve* o)
     o->slot = take(4 * max_tokens * c.num_topk);
     o->meta = take(8 * slots);
     o->hist = take(4 * Cc * c.num_experts);
-    o->rank_hist = take(4 * Cc * c.num_ranks);
-    o->node_hist = take(4 * Cc * num_nodes(c));
+    o->acc = take(4 * (int64_t)(c.num_ranks + num_nodes(c)));
     o->total = off;
     return EP_OK;
 }
@@ -192,6 +191,9 @@ ep_status ep_handle_init(const ep_config* cfg, int64_t max_tokens, void* d_works
     h->host_slots = -1;
     hipError_t e = epk::launch_clear(h->at<uint32_t>(cv.ctrl), epk::kCtrlWords,
                                      static_cast<hipStream_t>(stream));
+    if (e == hipSuccess)
+        e = epk::launch_clear(h->at<uint32_t>(cv.acc), cfg->num_ranks + h->nodes,
+                              static_cast<hipStream_t>(stream));
     if (e != hipSuccess) {
         delete h;
         return EP_FAIL(EP_ERR_HIP, "clearing the control words: %s", hipGetErrorString(e));
@@ -226,6 +228,8 @@ ep_status ep_get_layout(ep_handle* h, const int32_t* d_topk_idx, int64_t num_tok
     a.R = c.num_ranks;
     a.nle = c.num_experts / c.num_ranks;
     a.ranks_per_node = c.ranks_per_node;
+    a.nle_magic = epk::div_magic((uint32_t)a.nle);
+    a.rpn_magic = epk::div_magic((uint32_t)(c.ranks_per_node > 0 ? c.ranks_per_node : 1));
     a.nodes = h->nodes;
     a.A = c.expert_alignment;
     a.counts_as_prefix = c.counts_as_prefix ? 1 : 0;
@@ -234,8 +238,8 @@ ep_status ep_get_layout(ep_handle* h, const int32_t* d_topk_idx, int64_t num_tok
     a.slot_idx = h->at<int32_t>(h->cv.slot);
     a.src_meta = h->at<int32_t>(h->cv.meta);
     a.hist = h->at<int32_t>(h->cv.hist);
-    a.rank_hist = h->at<int32_t>(h->cv.rank_hist);
-    a.node_hist = h->at<int32_t>(h->cv.node_hist);
+    a.rank_acc = h->at<int32_t>(h->cv.acc);
+    a.node_acc = a.rank_acc + c.num_ranks;
     a.psum_expert = h->at<int32_t>(h->cv.psum_expert);
     a.psum_rank = h->at<int32_t>(h->cv.psum_rank);
     a.num_unaligned = h->at<int32_t>(h->cv.num_unaligned);

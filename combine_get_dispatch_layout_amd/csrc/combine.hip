@@ -15,12 +15,38 @@
 // HBM-bound (K rows read per row written).
 #include "ep_internal.hpp"
 
+// Launch shape: 16-byte vectors per lane per wave, threads per block, and
+// whether y loads / out stores carry the non-temporal hint.
+#ifndef EP_COMBINE_VPL
+#define EP_COMBINE_VPL 2
+#endif
+#ifndef EP_COMBINE_BLOCK
+#define EP_COMBINE_BLOCK 256
+#endif
+#ifndef EP_COMBINE_NT
+#define EP_COMBINE_NT 1
+#endif
+
 namespace epk {
 
 namespace {
 
-constexpr int kBlock = 256;
+constexpr int kBlock = EP_COMBINE_BLOCK;
 constexpr int kWavesPerBlock = kBlock / kWave;
+
+template <typename T>
+__device__ __forceinline__ T load_stream(const T* p)
+{
+    if constexpr (EP_COMBINE_NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+
+template <typename T>
+__device__ __forceinline__ void store_stream(T v, T* p)
+{
+    if constexpr (EP_COMBINE_NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -71,7 +97,7 @@ __global__ __launch_bounds__(kBlock) void k_combine(CombineArgs a, int NV, int N
         for (int i = 0; i < VPL; ++i) {
             const int v = vbase + kWave * i;
             yv[k][i] = (slot[k] >= 0 && v < NV)
-                           ? __builtin_nontemporal_load(y + (int64_t)slot[k] * NV + v)
+                           ? load_stream(y + (int64_t)slot[k] * NV + v)
                            : u32x4{0u, 0u, 0u, 0u};
         }
 
@@ -104,7 +130,7 @@ __global__ __launch_bounds__(kBlock) void k_combine(CombineArgs a, int NV, int N
             o[1] = pack_bf16x2(acc[i][2], acc[i][3]);
             o[2] = pack_bf16x2(acc[i][4], acc[i][5]);
             o[3] = pack_bf16x2(acc[i][6], acc[i][7]);
-            __builtin_nontemporal_store(o, orow + v);
+            store_stream(o, orow + v);
         }
     }
 }
@@ -125,10 +151,10 @@ hipError_t launch_kv(const CombineArgs& a, int NV, hipStream_t s)
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s)
 {
     const int NV = a.H / 8;
-    if (a.K <= 2) return launch_kv<2, 2>(a, NV, s);
-    if (a.K <= 4) return launch_kv<4, 2>(a, NV, s);
-    if (a.K <= 8) return launch_kv<8, 2>(a, NV, s);
-    return launch_kv<16, 1>(a, NV, s);
+    if (a.K <= 2) return launch_kv<2, EP_COMBINE_VPL>(a, NV, s);
+    if (a.K <= 4) return launch_kv<4, EP_COMBINE_VPL>(a, NV, s);
+    if (a.K <= 8) return launch_kv<8, EP_COMBINE_VPL>(a, NV, s);
+    return launch_kv<16, (EP_COMBINE_VPL > 1 ? EP_COMBINE_VPL / 2 : 1)>(a, NV, s);
 }
 
 }  // namespace epk

@@ -20,12 +20,39 @@
 // are never written.  HBM-bound: no LDS, no MFMA.
 #include "ep_internal.hpp"
 
+// Launch shape of the plain (unquantised) scatter: 16-byte vectors per lane
+// per wave, threads per block, and whether loads/stores carry the
+// non-temporal hint.
+#ifndef EP_DISPATCH_VPL
+#define EP_DISPATCH_VPL 1
+#endif
+#ifndef EP_DISPATCH_BLOCK
+#define EP_DISPATCH_BLOCK 256
+#endif
+#ifndef EP_DISPATCH_NT
+#define EP_DISPATCH_NT 1
+#endif
+
 namespace epk {
 
 namespace {
 
-constexpr int kBlock = 256;
+constexpr int kBlock = EP_DISPATCH_BLOCK;
 constexpr int kWavesPerBlock = kBlock / kWave;
+
+template <typename T>
+__device__ __forceinline__ T load_stream(const T* p)
+{
+    if constexpr (EP_DISPATCH_NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+
+template <typename T>
+__device__ __forceinline__ void store_stream(T v, T* p)
+{
+    if constexpr (EP_DISPATCH_NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -74,7 +101,7 @@ __global__ __launch_bounds__(kBlock) void k_dispatch(DispatchArgs a, int NV, int
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
         const int v = vbase + kWave * i;
-        d[i] = (v < NV) ? __builtin_nontemporal_load(xrow + v) : u32x4{0u, 0u, 0u, 0u};
+        d[i] = (v < NV) ? load_stream(xrow + v) : u32x4{0u, 0u, 0u, 0u};
     }
     const int32_t* slots = a.slot_idx + t * K;
 
@@ -90,7 +117,7 @@ __global__ __launch_bounds__(kBlock) void k_dispatch(DispatchArgs a, int NV, int
 #pragma unroll
             for (int i = 0; i < VPL; ++i) {
                 const int v = vbase + kWave * i;
-                if (v < NV) __builtin_nontemporal_store(d[i], dst + v);
+                if (v < NV) store_stream(d[i], dst + v);
             }
         }
     } else {
@@ -146,7 +173,7 @@ __global__ __launch_bounds__(kBlock) void k_dispatch(DispatchArgs a, int NV, int
             for (int i = 0; i < VPL; ++i) {
                 const int v = vbase + kWave * i;
                 if (v < NV) {
-                    __builtin_nontemporal_store(code[i], dst + v);
+                    store_stream(code[i], dst + v);
                     if constexpr (CHANNEL) {
                         if (v == 0) srow[0] = scale[i];
                     } else {
@@ -189,7 +216,7 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s)
     const int NV = a.H / 8;
     const bool channel = a.quant != 0 && a.group == a.H && a.H != 128;
     switch (a.quant) {
-        case 0: return launch_v<0, false, 1>(a, NV, s);
+        case 0: return launch_v<0, false, EP_DISPATCH_VPL>(a, NV, s);
         case 1: return channel ? launch_channel<1>(a, NV, s) : launch_v<1, false, 1>(a, NV, s);
         default: return channel ? launch_channel<2>(a, NV, s) : launch_v<2, false, 1>(a, NV, s);
     }

@@ -22,7 +22,9 @@ constexpr uint32_t kFlagCapacity = 2u;
 constexpr uint32_t kFlagYRows = 4u;
 
 // Control words at the start of the workspace.
-enum CtrlWord { kCtrlFlags = 0, kCtrlNumSlots = 1, kCtrlWords = 64 };
+// kCtrlTicket counts finished blocks of the routing kernel; the last block
+// resets it to zero for the next call.
+enum CtrlWord { kCtrlFlags = 0, kCtrlNumSlots = 1, kCtrlTicket = 2, kCtrlWords = 64 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -31,14 +33,17 @@ struct LayoutArgs {
     const int32_t* topk;        // [N,K] caller's routing
     int64_t num_tokens;         // N
     int K, E, R, nle, ranks_per_node, nodes, A, counts_as_prefix;
+    // n / nle and n / ranks_per_node as __umulhi(n, magic) (magic 0 = divide
+    // by 1); exact for n < 2^22, see div_magic()
+    uint32_t nle_magic, rpn_magic;
     // handle workspace
     uint32_t* ctrl;
     int32_t* topk_clone;        // [N,K]
     int32_t* slot_idx;          // [N,K]
     int32_t* src_meta;          // [max_slots,2]
     int32_t* hist;              // [C,E]  block histograms -> exclusive bases
-    int32_t* rank_hist;         // [C,R]
-    int32_t* node_hist;         // [C,nodes]
+    int32_t* rank_acc;          // [R] distinct-token accumulators, zero between calls
+    int32_t* node_acc;          // [nodes] likewise
     int32_t* psum_expert;       // [E+1]
     int32_t* psum_rank;         // [R+1]
     int32_t* num_unaligned;     // [E]
@@ -73,6 +78,14 @@ struct CombineArgs {
     void* out;                  // bf16 [N,H]
     uint32_t* flags;
 };
+
+// ceil(2^32 / d) for 2 <= d <= 2^16, 0 for d == 1.  floor(n / d) ==
+// __umulhi(n, magic) whenever n * (magic * d - 2^32) < 2^32, i.e. for all
+// n < 2^32 / d >= 2^16 here (ids and ranks are below 1024).
+inline uint32_t div_magic(uint32_t d)
+{
+    return d <= 1 ? 0u : (uint32_t)((((uint64_t)1 << 32) + d - 1) / d);
+}
 
 hipError_t launch_clear(uint32_t* words, int n, hipStream_t s);
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t s);

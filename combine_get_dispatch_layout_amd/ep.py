@@ -298,3 +298,37 @@ def ep_check_error(h: Handle, raise_on_error=False):
     if raise_on_error:
         _check(st)
     return st, flags.value
+
+
+# ---- pre-bound calls: pointers converted once, one ctypes call per launch --
+
+
+def _bound(fn, *args):
+    def call():
+        st = fn(*args)
+        if st != EP_OK:
+            _check(st)
+    return call
+
+
+def bind_get_layout(h: Handle, topk_idx, num_tokens_per_rank=None, num_tokens_per_rdma_rank=None,
+                    num_tokens_per_expert=None, is_token_in_rank=None, stream=None):
+    """A callable issuing ep_get_layout (no CPU sync) with these tensors."""
+    s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream(topk_idx.device)
+    return _bound(lib().ep_get_layout, h.ptr, _ptr(topk_idx), topk_idx.shape[0],
+                  _ptr(num_tokens_per_rank), _ptr(num_tokens_per_rdma_rank),
+                  _ptr(num_tokens_per_expert), _ptr(is_token_in_rank), 0, None, None, s)
+
+
+def bind_dispatch(h: Handle, x, recv_x, recv_scales, token_begin, token_end, stream=None):
+    """A callable issuing ep_dispatch with these tensors and token range."""
+    s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream(x.device)
+    return _bound(lib().ep_dispatch, h.ptr, _ptr(x), token_begin, token_end, _ptr(recv_x),
+                  _ptr(recv_scales), recv_x.shape[0], s)
+
+
+def bind_combine(h: Handle, y, topk_weights, out, token_begin, token_end, stream=None):
+    """A callable issuing ep_combine with these tensors and token range."""
+    s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream(out.device)
+    return _bound(lib().ep_combine, h.ptr, _ptr(y), y.shape[0], _ptr(topk_weights), token_begin,
+                  token_end, _ptr(out), s)

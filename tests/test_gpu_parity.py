@@ -211,3 +211,34 @@ def test_counts_as_prefix_host_list():
     s = oracle.slots(idx, w.num_experts, w.num_ranks, w.expert_alignment)
     ref = oracle.recv_list(s["psum_expert"], w.num_experts, w.num_ranks, True)
     assert lay["num_recv_tokens_per_expert_list"] == ref.tolist()
+
+
+# Layout paths by size: one fused block (<= 256 tokens: 4 waves; <= 1024: 16
+# waves), per-block count + finish (blocks x experts <= 8192), count + one-
+# block scan + slots (larger).  Each case names the path it drives.
+@pytest.mark.parametrize("args", [
+    dict(N=256, H=64, E=64, R=8, K=8, A=3),                # fused, 4 waves, full block
+    dict(N=1024, H=64, E=256, R=16, K=8, A=16, mask=0.1),  # fused, 16 waves, full
+    dict(N=1025, H=64, E=64, R=8, K=6),                    # count + finish, ragged
+    dict(N=2048, H=64, E=1024, R=64, K=4, A=2),            # count + finish, C*E = 8192
+    dict(N=9000, H=64, E=256, R=32, K=8, A=8, mask=0.05),  # count + scan + slots
+    dict(N=40001, H=32, E=64, R=4, K=2),                   # count + scan + slots, many blocks
+])
+def test_layout_paths(args):
+    w = _custom(**args)
+    _say(f"[parity] layout path {args}")
+    run_and_check(w)
+
+
+def test_empty_batch_scan_path():
+    """An empty batch whose single-block path does not fit in LDS (1024
+    experts, 1024 ranks, one rank per node) still zeroes every output."""
+    cfg = ep.Config(64, 2, 1024, 1024, ranks_per_node=1, expert_alignment=4)
+    h = ep.ep_handle_init(cfg, 8)
+    lay = ep.ep_get_layout(h, torch.empty((0, 2), dtype=torch.int32, device="cuda"),
+                           do_cpu_sync=True)
+    assert lay["num_recv_slots"] == 0
+    assert lay["num_tokens_per_expert"].abs().sum().item() == 0
+    assert lay["num_tokens_per_rank"].abs().sum().item() == 0
+    assert lay["num_tokens_per_rdma_rank"].abs().sum().item() == 0
+    assert ep.ep_check_error(h) == (ep.EP_OK, 0)
