@@ -49,17 +49,75 @@ def kernel_source_hash(kernel):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+def traffic_path(workload):
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+
+
 def traffic_from_profiles(kernel, workload):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when there is none or the kernel source changed since."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, or None when there is none or the kernel source changed since
+    the counters were taken."""
+    path = traffic_path(workload)
     if not os.path.exists(path):
         return None
     with open(path) as f:
-        d = json.load(f)
-    if d.get("source_sha256_16") != kernel_source_hash(kernel):
+        d = json.load(f).get("kernels", {}).get(kernel)
+    if not d or d.get("source_sha256_16") != kernel_source_hash(kernel):
         return None
     return d.get("hbm_bytes_per_launch")
+
+
+def _counter_rows(path, counter):
+    import csv
+    out = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                out.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return out
+
+
+def traffic_summary(fetch_csv, write_csv, workload):
+    """Writes profiles/traffic_<workload>.json from two rocprofv3 --pmc
+    counter_collection CSVs of `bench.py --workload <workload>` (FETCH_SIZE,
+    then WRITE_SIZE; KiB per dispatch).  Each counter is scaled by what it
+    reads for the benchmark's 1 GiB device copy (read 1 GiB, write 1 GiB)."""
+    fetch = _counter_rows(fetch_csv, "FETCH_SIZE")
+    write = _counter_rows(write_csv, "WRITE_SIZE")
+    gib_kib = float(1 << 20)
+    copy_f = max(v for n, v in fetch if "copyBuffer" in n)
+    copy_w = max(v for n, v in write if "copyBuffer" in n)
+    f_fetch, f_write = gib_kib / copy_f, gib_kib / copy_w
+    import workloads as W
+    import numpy as np
+    w = W.WORKLOADS[workload]
+    idx, _ = W.routing(w)
+    V = int((idx >= 0).sum())
+    nbytes = algorithmic_bytes(w, V, 0)
+    kernels = {}
+    for kern in ("dispatch", "combine"):
+        fv = [v for n, v in fetch if f"k_{kern}<" in n]
+        wv = [v for n, v in write if f"k_{kern}<" in n]
+        if not fv or not wv:
+            continue
+        fk, wk = float(np.median(fv)), float(np.median(wv))
+        per_launch_alg = nbytes[kern] / len(W.round_ranges(w.num_tokens, w.rounds))
+        hbm = (fk * f_fetch + wk * f_write) * 1024.0
+        kernels[kern] = dict(fetch_kib=fk, write_kib=wk, hbm_bytes_per_launch=hbm,
+                             algorithmic_bytes_per_launch=per_launch_alg,
+                             traffic_over_algorithmic=hbm / per_launch_alg, launches=len(fv),
+                             source_sha256_16=kernel_source_hash(kern))
+    out = dict(workload=workload, copy_fetch_kib=copy_f, copy_write_kib=copy_w,
+               fetch_scale=f_fetch, write_scale=f_write, kernels=kernels,
+               command=[f"rocprofv3 --pmc FETCH_SIZE -f csv -d <dir> -o fetch -- python3 bench.py "
+                        f"--workload {workload} --steps 4 --warmup 2 --no-cpu-baseline",
+                        f"rocprofv3 --pmc WRITE_SIZE -f csv -d <dir> -o write -- python3 bench.py "
+                        f"--workload {workload} --steps 4 --warmup 2 --no-cpu-baseline",
+                        f"python3 bench.py --traffic-from <dir>/fetch_counter_collection.csv "
+                        f"<dir>/write_counter_collection.csv --workload {workload}"])
+    with open(traffic_path(workload), "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
 
 
 def cpu_baseline(w, idx, wts, budget_s=12.0):
@@ -96,15 +154,55 @@ def cpu_baseline(w, idx, wts, budget_s=12.0):
                        f"slots, dispatch, combine), serial C, {el:.1f} s")
 
 
+class HipEvents:
+    """Raw hipEvent_t handles from the HIP runtime (so the library can attach
+    them to its kernel launches)."""
+
+    def __init__(self, n):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.c_void_p, ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.ev.append(h.value)
+
+    def ms(self, a, b):
+        out = self.ct.c_float()
+        if self.hip.hipEventElapsedTime(self.ct.byref(out), self.ct.c_void_p(self.ev[a]),
+                                        self.ct.c_void_p(self.ev[b])) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return out.value
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(self.ct.c_void_p(e))
+        self.ev = []
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="qwen3_30b_a3b_prefill")
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to rotate (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--timing", choices=("rotate", "all"), default="rotate",
+                    help="rotate: each timed step arms kernel events on one stage, in turn "
+                         "(layout, dispatch, combine); all: every call of every step")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise two rocprofv3 --pmc runs into profiles/ and exit")
     args = ap.parse_args()
+    if args.traffic_from:
+        traffic_summary(args.traffic_from[0], args.traffic_from[1], args.workload)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): this path runs on "
               "one GPU's share of an EP step, with destination ranks simulated as partitions "
@@ -164,49 +262,57 @@ def main():
             [ep.bind_combine(s["h"], s["y"], s["wts"], s["out"], b, e, stream=stream)
              for b, e in rounds])
 
-    def step(i, ev=None):
+    nr = len(rounds)
+    # one (start, stop) event pair per kernel call of every timed step
+    calls_per_step = 1 + 2 * nr
+    hev = HipEvents(2 * calls_per_step * args.steps)
+
+    def armed(i, j):
+        """Whether call j (0 layout, then dispatch rounds, then combine rounds)
+        of timed step i carries kernel events."""
+        if args.timing == "all":
+            return True
+        stage = 0 if j == 0 else (1 if j <= nr else 2)
+        return stage == i % 3
+
+    def step(i, base=None):
         lay_calls, dis_calls, com_calls = sets[i % nsets]["calls"]
-        if ev is not None:
-            ev[0].record(stream)
-        for c in lay_calls:
-            c()
-        if ev is not None:
-            ev[1].record(stream)
-        for c in dis_calls:
-            c()
-        if ev is not None:
-            ev[2].record(stream)
-        for c in com_calls:
-            c()
-        if ev is not None:
-            ev[3].record(stream)
+        for j, c in enumerate(lay_calls + dis_calls + com_calls):
+            if base is None or not armed(i, j):
+                c()
+            else:
+                c((hev.ev[base + 2 * j], hev.ev[base + 2 * j + 1]))
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, evs[i])
+        step(i, 2 * calls_per_step * i)
+    t_enqueue = time.perf_counter() - t0
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    lay = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
-    dis = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
-    com = np.array([e[2].elapsed_time(e[3]) for e in evs]) * 1e-3
+    def durs(j):
+        """Per-step duration (s) of call j over the steps that timed it."""
+        return np.array([hev.ms(2 * calls_per_step * i + 2 * j, 2 * calls_per_step * i + 2 * j + 1)
+                         for i in range(args.steps) if armed(i, j)]) * 1e-3
+
+    lay = durs(0)
+    dis = sum(durs(1 + r) for r in range(nr))
+    com = sum(durs(1 + nr + r) for r in range(nr))
+    hev.close()
     ms_per_step = wall / args.steps * 1e3
     value = N * args.steps / wall
     t_dc = float(np.mean(dis) + np.mean(com))
 
     # per-launch means (one dispatch/combine launch per round)
-    nr = len(rounds)
     stages = dict(layout=(float(np.mean(lay)), nbytes["layout"], 1),
                   dispatch=(float(np.mean(dis)), nbytes["dispatch"], nr),
                   combine=(float(np.mean(com)), nbytes["combine"], nr))
     dom = max(("dispatch", "combine"), key=lambda k: stages[k][0])
     t_dom, b_dom, launches = stages[dom]
-    achieved = b_dom / t_dom / 1e9
+    achieved = b_dom / t_dom / 1e9   # = per-launch bytes / mean per-launch time
     traffic = traffic_from_profiles(dom, w.name)
 
     # achievable reference: a plain 1 GiB device copy
@@ -246,6 +352,8 @@ def main():
                              "frac_of_peak": (nbytes["dispatch"] + nbytes["combine"]) / t_dc / 1e9
                              / HBM_PEAK_GBS},
         "device_copy_GBps": copy_gbs,
+        "timing": {"mode": args.timing, "host_enqueue_ms_per_step": t_enqueue / args.steps * 1e3,
+                   "samples_per_stage": [int(len(lay)), int(len(dis)), int(len(com))]},
         "recv_rows": S, "valid_pairs": V,
     }
     if not args.no_cpu_baseline:

@@ -134,6 +134,15 @@ struct ep_handle {
     Carve cv;
     int64_t num_tokens;   // -1 before the first ep_get_layout
     int64_t host_slots;   // S known on the host, else -1
+    // events armed by ep_set_kernel_events for the next call
+    mutable epk::LaunchEvents armed;
+
+    epk::LaunchEvents take_events() const
+    {
+        epk::LaunchEvents e = armed;
+        armed = epk::LaunchEvents{};
+        return e;
+    }
 
     template <typename T>
     T* at(int64_t off) const { return reinterpret_cast<T*>(ws + off); }
@@ -250,7 +259,7 @@ ep_status ep_get_layout(ep_handle* h, const int32_t* d_topk_idx, int64_t num_tok
     a.out_in_rank = d_is_token_in_rank;
     a.in_rank_words = (c.num_ranks % 4 == 0) && aligned(d_is_token_in_rank, 4);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    EP_HIP(epk::launch_layout(a, s));
+    EP_HIP(epk::launch_layout(a, s, h->take_events()));
     h->num_tokens = num_tokens;
     h->host_slots = -1;
     if (do_cpu_sync) {
@@ -303,7 +312,7 @@ ep_status ep_dispatch(const ep_handle* h, const void* d_x, int64_t token_begin, 
     a.quant = c.quant;
     a.group = c.quant_group;
     a.flags = h->at<uint32_t>(h->cv.ctrl) + epk::kCtrlFlags;
-    EP_HIP(epk::launch_dispatch(a, static_cast<hipStream_t>(stream)));
+    EP_HIP(epk::launch_dispatch(a, static_cast<hipStream_t>(stream), h->take_events()));
     return EP_OK;
 }
 
@@ -336,7 +345,15 @@ ep_status ep_combine(const ep_handle* h, const void* d_y, int64_t y_rows,
     a.K = c.num_topk;
     a.out = d_out;
     a.flags = h->at<uint32_t>(h->cv.ctrl) + epk::kCtrlFlags;
-    EP_HIP(epk::launch_combine(a, static_cast<hipStream_t>(stream)));
+    EP_HIP(epk::launch_combine(a, static_cast<hipStream_t>(stream), h->take_events()));
+    return EP_OK;
+}
+
+ep_status ep_set_kernel_events(ep_handle* h, void* start_event, void* stop_event)
+{
+    if (!h) return EP_FAIL(EP_ERR_INVALID_ARG, "handle is NULL");
+    h->armed.start = static_cast<hipEvent_t>(start_event);
+    h->armed.stop = static_cast<hipEvent_t>(stop_event);
     return EP_OK;
 }
 

@@ -136,25 +136,25 @@ __global__ __launch_bounds__(kBlock) void k_combine(CombineArgs a, int NV, int N
 }
 
 template <int KMAX, int VPL>
-hipError_t launch_kv(const CombineArgs& a, int NV, hipStream_t s)
+hipError_t launch_kv(const CombineArgs& a, int NV, hipStream_t s, LaunchEvents ev)
 {
     const int NC = (NV + kWave * VPL - 1) / (kWave * VPL);
     const int64_t items = (a.t_end - a.t_begin) * NC;
     if (items <= 0) return hipSuccess;
     const int blocks = (int)((items + kWavesPerBlock - 1) / kWavesPerBlock);
-    hipLaunchKernelGGL((k_combine<KMAX, VPL>), dim3(blocks), dim3(kBlock), 0, s, a, NV, NC);
+    launch_k(k_combine<KMAX, VPL>, dim3(blocks), dim3(kBlock), 0, s, ev.start, ev.stop, a, NV, NC);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_combine(const CombineArgs& a, hipStream_t s)
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s, LaunchEvents ev)
 {
     const int NV = a.H / 8;
-    if (a.K <= 2) return launch_kv<2, EP_COMBINE_VPL>(a, NV, s);
-    if (a.K <= 4) return launch_kv<4, EP_COMBINE_VPL>(a, NV, s);
-    if (a.K <= 8) return launch_kv<8, EP_COMBINE_VPL>(a, NV, s);
-    return launch_kv<16, (EP_COMBINE_VPL > 1 ? EP_COMBINE_VPL / 2 : 1)>(a, NV, s);
+    if (a.K <= 2) return launch_kv<2, EP_COMBINE_VPL>(a, NV, s, ev);
+    if (a.K <= 4) return launch_kv<4, EP_COMBINE_VPL>(a, NV, s, ev);
+    if (a.K <= 8) return launch_kv<8, EP_COMBINE_VPL>(a, NV, s, ev);
+    return launch_kv<16, (EP_COMBINE_VPL > 1 ? EP_COMBINE_VPL / 2 : 1)>(a, NV, s, ev);
 }
 
 }  // namespace epk

@@ -186,39 +186,41 @@ __global__ __launch_bounds__(kBlock) void k_dispatch(DispatchArgs a, int NV, int
 }
 
 template <int QUANT, bool CHANNEL, int VPL>
-hipError_t launch_v(const DispatchArgs& a, int NV, hipStream_t s)
+hipError_t launch_v(const DispatchArgs& a, int NV, hipStream_t s, LaunchEvents ev)
 {
     const int NC = (NV + kWave * VPL - 1) / (kWave * VPL);
     const int64_t items = (a.t_end - a.t_begin) * NC;
     if (items <= 0) return hipSuccess;
     const int blocks = (int)((items + kWavesPerBlock - 1) / kWavesPerBlock);
-    hipLaunchKernelGGL((k_dispatch<QUANT, CHANNEL, VPL>), dim3(blocks), dim3(kBlock), 0, s, a, NV,
-                       NC);
+    launch_k(k_dispatch<QUANT, CHANNEL, VPL>, dim3(blocks), dim3(kBlock), 0, s, ev.start, ev.stop,
+             a, NV, NC);
     return hipGetLastError();
 }
 
 // Channel scales need the whole row in one wave: smallest VPL with
 // 64*VPL >= NV.
 template <int QUANT>
-hipError_t launch_channel(const DispatchArgs& a, int NV, hipStream_t s)
+hipError_t launch_channel(const DispatchArgs& a, int NV, hipStream_t s, LaunchEvents ev)
 {
-    if (NV <= 64) return launch_v<QUANT, true, 1>(a, NV, s);
-    if (NV <= 128) return launch_v<QUANT, true, 2>(a, NV, s);
-    if (NV <= 256) return launch_v<QUANT, true, 4>(a, NV, s);
-    if (NV <= 512) return launch_v<QUANT, true, 8>(a, NV, s);
-    return launch_v<QUANT, true, 16>(a, NV, s);
+    if (NV <= 64) return launch_v<QUANT, true, 1>(a, NV, s, ev);
+    if (NV <= 128) return launch_v<QUANT, true, 2>(a, NV, s, ev);
+    if (NV <= 256) return launch_v<QUANT, true, 4>(a, NV, s, ev);
+    if (NV <= 512) return launch_v<QUANT, true, 8>(a, NV, s, ev);
+    return launch_v<QUANT, true, 16>(a, NV, s, ev);
 }
 
 }  // namespace
 
-hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s)
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s, LaunchEvents ev)
 {
     const int NV = a.H / 8;
     const bool channel = a.quant != 0 && a.group == a.H && a.H != 128;
     switch (a.quant) {
-        case 0: return launch_v<0, false, EP_DISPATCH_VPL>(a, NV, s);
-        case 1: return channel ? launch_channel<1>(a, NV, s) : launch_v<1, false, 1>(a, NV, s);
-        default: return channel ? launch_channel<2>(a, NV, s) : launch_v<2, false, 1>(a, NV, s);
+        case 0: return launch_v<0, false, EP_DISPATCH_VPL>(a, NV, s, ev);
+        case 1:
+            return channel ? launch_channel<1>(a, NV, s, ev) : launch_v<1, false, 1>(a, NV, s, ev);
+        default:
+            return channel ? launch_channel<2>(a, NV, s, ev) : launch_v<2, false, 1>(a, NV, s, ev);
     }
 }
 

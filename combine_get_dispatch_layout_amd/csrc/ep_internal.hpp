@@ -2,6 +2,7 @@
 // kernels (layout.hip, dispatch.hip, combine.hip).  gfx950 only.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -87,9 +88,27 @@ inline uint32_t div_magic(uint32_t d)
     return d <= 1 ? 0u : (uint32_t)((((uint64_t)1 << 32) + d - 1) / d);
 }
 
+// Optional timestamps of a call's first kernel start and last kernel end.
+struct LaunchEvents {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+
+// Launches `kernel`; with events it goes through hipExtLaunchKernelGGL so the
+// events take the kernel's own start / end timestamps.
+template <typename K, typename... Args>
+inline void launch_k(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, hipEvent_t start,
+                     hipEvent_t stop, Args... args)
+{
+    if (start != nullptr || stop != nullptr)
+        hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, s, start, stop, 0u, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+}
+
 hipError_t launch_clear(uint32_t* words, int n, hipStream_t s);
-hipError_t launch_layout(const LayoutArgs& a, hipStream_t s);
-hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
-hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+hipError_t launch_layout(const LayoutArgs& a, hipStream_t s, LaunchEvents ev = {});
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s, LaunchEvents ev = {});
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s, LaunchEvents ev = {});
 
 }  // namespace epk

@@ -562,32 +562,32 @@ size_t fused_lds_bytes(const LayoutArgs& a, int waves)
 }
 
 template <int KMAX>
-hipError_t launch_layout_k(const LayoutArgs& a, hipStream_t s)
+hipError_t launch_layout_k(const LayoutArgs& a, hipStream_t s, LaunchEvents ev)
 {
     const int64_t N = a.num_tokens;
     if (N <= kLayoutBlock && fused_lds_bytes(a, 4) <= kMaxLds) {
-        hipLaunchKernelGGL((k_fused<KMAX, 4>), dim3(1), dim3(4 * kWave), fused_lds_bytes(a, 4), s,
-                           a);
+        launch_k(k_fused<KMAX, 4>, dim3(1), dim3(4 * kWave), fused_lds_bytes(a, 4), s, ev.start,
+                 ev.stop, a);
         return hipGetLastError();
     }
     if (N <= kFusedMaxTokens && fused_lds_bytes(a, 16) <= kMaxLds) {
-        hipLaunchKernelGGL((k_fused<KMAX, 16>), dim3(1), dim3(16 * kWave), fused_lds_bytes(a, 16),
-                           s, a);
+        launch_k(k_fused<KMAX, 16>, dim3(1), dim3(16 * kWave), fused_lds_bytes(a, 16), s, ev.start,
+                 ev.stop, a);
         return hipGetLastError();
     }
     const int C = (int)((N + kLayoutBlock - 1) / kLayoutBlock);
     if (C == 0) {   // empty batch whose fused path did not fit: zero outputs
-        hipLaunchKernelGGL(k_scan, dim3(1), dim3(kScanThreads), 0, s, a, 0);
+        launch_k(k_scan, dim3(1), dim3(kScanThreads), 0, s, ev.start, ev.stop, a, 0);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(k_count<KMAX>, dim3(C), dim3(kLayoutBlock),
-                       route_lds_bytes(kLayoutBlock / kWave, a.E, a.R, a.nodes), s, a);
+    launch_k(k_count<KMAX>, dim3(C), dim3(kLayoutBlock),
+             route_lds_bytes(kLayoutBlock / kWave, a.E, a.R, a.nodes), s, ev.start, nullptr, a);
     if ((int64_t)C * a.E <= kFinishMaxInts) {
         const size_t fl = ((size_t)C * a.E + 3 * (size_t)a.E + 1 + 2 * kLayoutBlock) * 4;
-        hipLaunchKernelGGL(k_finish<KMAX>, dim3(C), dim3(kLayoutBlock), fl, s, a, C);
+        launch_k(k_finish<KMAX>, dim3(C), dim3(kLayoutBlock), fl, s, nullptr, ev.stop, a, C);
     } else {
-        hipLaunchKernelGGL(k_scan, dim3(1), dim3(kScanThreads), 0, s, a, C);
-        hipLaunchKernelGGL(k_slots<KMAX>, dim3(C), dim3(kLayoutBlock), 0, s, a);
+        launch_k(k_scan, dim3(1), dim3(kScanThreads), 0, s, nullptr, nullptr, a, C);
+        launch_k(k_slots<KMAX>, dim3(C), dim3(kLayoutBlock), 0, s, nullptr, ev.stop, a);
     }
     return hipGetLastError();
 }
@@ -600,12 +600,12 @@ hipError_t launch_clear(uint32_t* words, int n, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_layout(const LayoutArgs& a, hipStream_t s)
+hipError_t launch_layout(const LayoutArgs& a, hipStream_t s, LaunchEvents ev)
 {
-    if (a.K <= 2) return launch_layout_k<2>(a, s);
-    if (a.K <= 4) return launch_layout_k<4>(a, s);
-    if (a.K <= 8) return launch_layout_k<8>(a, s);
-    return launch_layout_k<16>(a, s);
+    if (a.K <= 2) return launch_layout_k<2>(a, s, ev);
+    if (a.K <= 4) return launch_layout_k<4>(a, s, ev);
+    if (a.K <= 8) return launch_layout_k<8>(a, s, ev);
+    return launch_layout_k<16>(a, s, ev);
 }
 
 }  // namespace epk

@@ -21,8 +21,8 @@ EP_FLAG_BAD_EXPERT_ID, EP_FLAG_RECV_CAPACITY, EP_FLAG_Y_ROWS = 1, 2, 4
 
 # Every symbol include/ep.h declares.
 SYMBOLS = ("ep_workspace_size", "ep_recv_capacity", "ep_handle_init", "ep_handle_free",
-           "ep_get_layout", "ep_dispatch", "ep_combine", "ep_handle_get_view", "ep_check_error",
-           "ep_status_str", "ep_last_error_message")
+           "ep_get_layout", "ep_dispatch", "ep_combine", "ep_set_kernel_events",
+           "ep_handle_get_view", "ep_check_error", "ep_status_str", "ep_last_error_message")
 
 
 class ep_config(ctypes.Structure):
@@ -68,6 +68,7 @@ def lib():
         L.ep_get_layout.argtypes = [P, P, I64, P, P, P, P, I32, P, P, P]
         L.ep_dispatch.argtypes = [P, P, I64, I64, P, P, I64, P]
         L.ep_combine.argtypes = [P, P, I64, P, I64, I64, P, P]
+        L.ep_set_kernel_events.argtypes = [P, P, P]
         L.ep_handle_get_view.argtypes = [P, P]
         L.ep_check_error.argtypes = [P, P, P]
         L.ep_status_str.argtypes = [I32]
@@ -75,7 +76,8 @@ def lib():
         L.ep_last_error_message.argtypes = []
         L.ep_last_error_message.restype = ctypes.c_char_p
         for name in ("ep_workspace_size", "ep_recv_capacity", "ep_handle_init", "ep_get_layout",
-                     "ep_dispatch", "ep_combine", "ep_handle_get_view", "ep_check_error"):
+                     "ep_dispatch", "ep_combine", "ep_set_kernel_events", "ep_handle_get_view",
+                     "ep_check_error"):
             getattr(L, name).restype = I32
         _lib = L
     return _lib
@@ -268,6 +270,12 @@ def ep_combine(h: Handle, y: torch.Tensor, topk_weights: torch.Tensor, out: torc
     return out
 
 
+def ep_set_kernel_events(h: Handle, start_event=None, stop_event=None):
+    """Arms raw hipEvent_t handles (ints or None) to take the start / end
+    timestamps of the next call's first / last kernel."""
+    _check(lib().ep_set_kernel_events(h.ptr, start_event, stop_event))
+
+
 def ep_handle_get_view(h: Handle):
     """Device arrays of the handle as int32 tensor views of its workspace."""
     v = ep_handle_view()
@@ -303,8 +311,15 @@ def ep_check_error(h: Handle, raise_on_error=False):
 # ---- pre-bound calls: pointers converted once, one ctypes call per launch --
 
 
-def _bound(fn, *args):
-    def call():
+def _bound(h, fn, *args):
+    """call(events=None): issues fn(*args); events = (start, stop) raw
+    hipEvent_t handles are armed first (ep_set_kernel_events)."""
+    arm = lib().ep_set_kernel_events
+    hp = h.ptr
+
+    def call(events=None):
+        if events is not None:
+            arm(hp, events[0], events[1])
         st = fn(*args)
         if st != EP_OK:
             _check(st)
@@ -315,7 +330,7 @@ def bind_get_layout(h: Handle, topk_idx, num_tokens_per_rank=None, num_tokens_pe
                     num_tokens_per_expert=None, is_token_in_rank=None, stream=None):
     """A callable issuing ep_get_layout (no CPU sync) with these tensors."""
     s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream(topk_idx.device)
-    return _bound(lib().ep_get_layout, h.ptr, _ptr(topk_idx), topk_idx.shape[0],
+    return _bound(h, lib().ep_get_layout, h.ptr, _ptr(topk_idx), topk_idx.shape[0],
                   _ptr(num_tokens_per_rank), _ptr(num_tokens_per_rdma_rank),
                   _ptr(num_tokens_per_expert), _ptr(is_token_in_rank), 0, None, None, s)
 
@@ -323,12 +338,12 @@ def bind_get_layout(h: Handle, topk_idx, num_tokens_per_rank=None, num_tokens_pe
 def bind_dispatch(h: Handle, x, recv_x, recv_scales, token_begin, token_end, stream=None):
     """A callable issuing ep_dispatch with these tensors and token range."""
     s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream(x.device)
-    return _bound(lib().ep_dispatch, h.ptr, _ptr(x), token_begin, token_end, _ptr(recv_x),
+    return _bound(h, lib().ep_dispatch, h.ptr, _ptr(x), token_begin, token_end, _ptr(recv_x),
                   _ptr(recv_scales), recv_x.shape[0], s)
 
 
 def bind_combine(h: Handle, y, topk_weights, out, token_begin, token_end, stream=None):
     """A callable issuing ep_combine with these tensors and token range."""
     s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream(out.device)
-    return _bound(lib().ep_combine, h.ptr, _ptr(y), y.shape[0], _ptr(topk_weights), token_begin,
+    return _bound(h, lib().ep_combine, h.ptr, _ptr(y), y.shape[0], _ptr(topk_weights), token_begin,
                   token_end, _ptr(out), s)

@@ -173,6 +173,14 @@ ep_status ep_combine(const ep_handle* h, const void* d_y, int64_t y_rows,
                      const float* d_topk_weights, int64_t token_begin, int64_t token_end,
                      void* d_out, void* stream);
 
+/* Profiling: the next ep_get_layout, ep_dispatch or ep_combine call on h
+ * records start_event when its first kernel starts and stop_event when its
+ * last kernel ends (timestamps of the kernel launches themselves, taken with
+ * hipExtLaunchKernelGGL, so no marker is queued between kernels); the events
+ * are then released from the handle.  Both are caller-created hipEvent_t
+ * (either may be NULL).  Not thread-safe with calls on the same handle. */
+ep_status ep_set_kernel_events(ep_handle* h, void* start_event, void* stop_event);
+
 /* Device pointers and sizes held by a handle. */
 ep_status ep_handle_get_view(const ep_handle* h, ep_handle_view* view);
 

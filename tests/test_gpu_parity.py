@@ -142,8 +142,7 @@ def test_deterministic_across_runs():
 
 def test_round_trip_identity_experts():
     """dispatch -> identity experts (y = recv_x) -> combine with weights that
-    sum to 1 returns x bit for bit (spec invariant), at the
-    Qwen3-30B-A3B prefill shape."""
+    sum to 1 returns x bit for bit, at the Qwen3-30B-A3B prefill shape."""
     w = W.WORKLOADS["qwen3_30b_a3b_prefill"]
     idx, wts = W.routing(w)
     x = W.activations(w.num_tokens, w.hidden, 3, device="cuda")

@@ -79,7 +79,7 @@ def test_layout_matches_numpy(N, K, E, R, rpn):
     assert np.array_equal(lay["num_tokens_per_rank"], pr)
     assert np.array_equal(lay["is_token_in_rank"], ir)
     assert np.array_equal(lay["num_tokens_per_rdma_rank"], pn)
-    # spec invariant: counts sum to N*K minus masked entries
+    # counts sum to N*K minus masked entries
     assert lay["num_tokens_per_expert"].sum() == N * K - (idx == -1).sum()
 
 

@@ -4,7 +4,7 @@ Dispatch: row copies checked by numpy fancy indexing; FP8/int8 scales by
 their closed form in numpy float32; codes by torch's float8_e4m3fn converter
 and numpy's rint applied to the fp32 quotient; dequantisation error bounds.
 Combine: the hand-worked example, exact rational sums (fractions.Fraction)
-rounded to nearest-even bf16, K=1 identity, linearity, and the north-star
+rounded to nearest-even bf16, K=1 identity, linearity, and the identity
 round trip (dispatch, identity experts, combine with weights summing to 1
 returns x bit for bit).  Rounds: per-range calls equal the one-shot result.
 """
