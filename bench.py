@@ -194,6 +194,11 @@ def main():
     ap.add_argument("--workload", default="qwen3_30b_a3b_prefill")
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to rotate (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pipeline", choices=("overlap", "serial"), default="overlap",
+                    help="overlap: batch i+1's layout runs on a second stream during batch i's "
+                         "dispatch and combine; serial: one stream, one stage after another")
+    ap.add_argument("--time-every", type=int, default=4,
+                    help="rotate mode: arm kernel events on every N-th timed step")
     ap.add_argument("--timing", choices=("rotate", "all"), default="rotate",
                     help="rotate: each timed step arms kernel events on one stage, in turn "
                          "(layout, dispatch, combine); all: every call of every step")
@@ -253,14 +258,20 @@ def main():
     S = ep.ep_get_layout(sets[0]["h"], sets[0]["topk"], do_cpu_sync=True)["num_recv_slots"]
     nbytes = algorithmic_bytes(w, V, S)
     stream = torch.cuda.current_stream()
+    # overlap: the layout of batch i+1 runs on a second stream while batch i
+    # is dispatched and combined (double-batch overlap); default priority
+    lay_stream = torch.cuda.Stream() if args.pipeline == "overlap" else stream
     for s in sets:
         s["calls"] = (
             [ep.bind_get_layout(s["h"], s["topk"], s["per_rank"], s["per_node"], s["per_expert"],
-                                s["in_rank"], stream=stream)],
+                                s["in_rank"], stream=lay_stream)],
             [ep.bind_dispatch(s["h"], s["x"], s["recv"], s["scales"], b, e, stream=stream)
              for b, e in rounds],
             [ep.bind_combine(s["h"], s["y"], s["wts"], s["out"], b, e, stream=stream)
              for b, e in rounds])
+        s["lay_done"] = torch.cuda.Event()
+        s["main_done"] = torch.cuda.Event()
+        s["main_done"].record(stream)
 
     nr = len(rounds)
     # one (start, stop) event pair per kernel call of every timed step
@@ -269,26 +280,55 @@ def main():
 
     def armed(i, j):
         """Whether call j (0 layout, then dispatch rounds, then combine rounds)
-        of timed step i carries kernel events."""
+        of timed step i carries kernel events: every call of every step
+        ("all"), or, on every time_every-th step, one stage in turn."""
         if args.timing == "all":
             return True
+        if i % args.time_every:
+            return False
         stage = 0 if j == 0 else (1 if j <= nr else 2)
-        return stage == i % 3
+        return stage == (i // args.time_every) % 3
 
-    def step(i, base=None):
-        lay_calls, dis_calls, com_calls = sets[i % nsets]["calls"]
-        for j, c in enumerate(lay_calls + dis_calls + com_calls):
-            if base is None or not armed(i, j):
-                c()
-            else:
-                c((hev.ev[base + 2 * j], hev.ev[base + 2 * j + 1]))
+    def issue(c, i, j, base):
+        if base is None or not armed(i, j):
+            c()
+        else:
+            c((hev.ev[base + 2 * j], hev.ev[base + 2 * j + 1]))
 
-    for i in range(args.warmup):
-        step(i)
+    def layout(i, base):
+        s = sets[i % nsets]
+        if lay_stream is not stream:
+            lay_stream.wait_event(s["main_done"])   # the set's previous batch is combined
+        issue(s["calls"][0][0], i, 0, base)
+        if lay_stream is not stream:
+            s["lay_done"].record(lay_stream)
+
+    def shuffle(i, base):
+        s = sets[i % nsets]
+        if lay_stream is not stream:
+            stream.wait_event(s["lay_done"])
+        for j, c in enumerate(s["calls"][1] + s["calls"][2]):
+            issue(c, i, 1 + j, base)
+        if lay_stream is not stream:
+            s["main_done"].record(stream)
+
+    def run(n, timed):
+        """n steps; with overlap the layout of step i+1 is issued before the
+        dispatch and combine of step i."""
+        def base(i):
+            return 2 * calls_per_step * i if timed else None
+        layout(0, base(0))
+        for i in range(n):
+            if lay_stream is not stream and i + 1 < n:
+                layout(i + 1, base(i + 1))
+            shuffle(i, base(i))
+            if lay_stream is stream and i + 1 < n:
+                layout(i + 1, base(i + 1))
+
+    run(args.warmup, False)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i, 2 * calls_per_step * i)
+    run(args.steps, True)
     t_enqueue = time.perf_counter() - t0
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -352,7 +392,8 @@ def main():
                              "frac_of_peak": (nbytes["dispatch"] + nbytes["combine"]) / t_dc / 1e9
                              / HBM_PEAK_GBS},
         "device_copy_GBps": copy_gbs,
-        "timing": {"mode": args.timing, "host_enqueue_ms_per_step": t_enqueue / args.steps * 1e3,
+        "pipeline": args.pipeline,
+        "timing": {"mode": args.timing, "every": args.time_every, "host_enqueue_ms_per_step": t_enqueue / args.steps * 1e3,
                    "samples_per_stage": [int(len(lay)), int(len(dis)), int(len(com))]},
         "recv_rows": S, "valid_pairs": V,
     }

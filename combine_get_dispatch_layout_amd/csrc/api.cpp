@@ -115,7 +115,9 @@ ep_status carve(const ep_config& c, int64_t max_tokens, Carve* o)
     o->num_unaligned = take(4 * (int64_t)c.num_experts);
     o->recv_list = take(4 * (int64_t)c.num_experts);
     o->topk = take(4 * max_tokens * c.num_topk);
-    o->slot = take(4 * max_tokens * c.num_topk);
+    // slack of kMaxTopk entries: kernels read a token's slots as one batch of
+    // kMaxTopk words and ignore those past K
+    o->slot = take(4 * (max_tokens * c.num_topk + epk::kMaxTopk));
     o->meta = take(8 * slots);
     o->hist = take(4 * Cc * c.num_experts);
     o->acc = take(4 * (int64_t)(c.num_ranks + num_nodes(c)));

@@ -69,23 +69,22 @@ __global__ __launch_bounds__(kBlock) void k_combine(CombineArgs a, int NV, int N
     const int K = a.K;
     const int vbase = c * (kWave * VPL) + lane;
 
+    // one lane-parallel load of the K slots and weights (lane k holds entry
+    // k), broadcast to scalars: a single round trip for any K
+    const int sv = (lane < K) ? a.slot_idx[t * K + lane] : -1;
+    const float wl = (lane < K) ? a.weights[t * K + lane] : 0.0f;
     int slot[KMAX];
     float wk[KMAX];
     bool oob = false;
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
-        int s = -1;
-        float w = 0.0f;
-        if (k < K) {
-            s = a.slot_idx[t * K + k];
-            w = a.weights[t * K + k];
-            if (s >= a.y_rows) {
-                oob = true;
-                s = -1;
-            }
+        int s = __builtin_amdgcn_readlane(sv, k);
+        wk[k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), k));
+        if (s >= a.y_rows) {
+            oob = true;
+            s = -1;
         }
         slot[k] = s;
-        wk[k] = w;
     }
     if (oob && lane == 0) atomicOr(a.flags, kFlagYRows);
 

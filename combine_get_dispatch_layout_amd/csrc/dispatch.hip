@@ -20,17 +20,25 @@
 // are never written.  HBM-bound: no LDS, no MFMA.
 #include "ep_internal.hpp"
 
-// Launch shape of the plain (unquantised) scatter: 16-byte vectors per lane
-// per wave, threads per block, and whether loads/stores carry the
-// non-temporal hint.
+// Launch shape: threads per block and whether loads/stores carry the
+// non-temporal hint.  EP_DISPATCH_VPL / EP_DISPATCH_ROW_WAIT > = 0 force the
+// per-shape choices made in launch_dispatch (for measurements).
 #ifndef EP_DISPATCH_VPL
-#define EP_DISPATCH_VPL 1
+#define EP_DISPATCH_VPL -1
 #endif
 #ifndef EP_DISPATCH_BLOCK
 #define EP_DISPATCH_BLOCK 256
 #endif
 #ifndef EP_DISPATCH_NT
 #define EP_DISPATCH_NT 1
+#endif
+// Receive-row stores through per-row buffer resources (1) or plain global
+// stores (0).
+#ifndef EP_DISPATCH_BUFFER
+#define EP_DISPATCH_BUFFER 1
+#endif
+#ifndef EP_DISPATCH_ROW_WAIT
+#define EP_DISPATCH_ROW_WAIT -1
 #endif
 
 namespace epk {
@@ -47,11 +55,18 @@ __device__ __forceinline__ T load_stream(const T* p)
     else return *p;
 }
 
-template <typename T>
-__device__ __forceinline__ void store_stream(T v, T* p)
+
+// Receive-row stores go through a buffer resource per row (base = the row,
+// bound = the row's bytes; the third word is the gfx9 raw-buffer format):
+// the row address lives in scalar registers and the lane offset in one
+// vector register that never changes, so consecutive stores of a wave need
+// no wait between them, and the hardware drops anything outside the row.
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kStoreAux = EP_DISPATCH_NT ? 2 : 0;   // nt cache policy
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(char* row, int bytes)
 {
-    if constexpr (EP_DISPATCH_NT) __builtin_nontemporal_store(v, p);
-    else *p = v;
+    return __builtin_amdgcn_make_buffer_rsrc(row, 0, bytes, kBufferWord3);
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -84,7 +99,9 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
 
 // QUANT: 0 none, 1 E4M3FN, 2 int8.  CHANNEL: one scale per row (the chunk
 // covers the row), else one per 128 elements.
-template <int QUANT, bool CHANNEL, int VPL>
+// ROW_WAIT: wait for each receive row's stores before writing the next row,
+// which bounds the writes a wave keeps in flight (faster for long rows).
+template <int QUANT, bool CHANNEL, int VPL, int KMAX, bool ROW_WAIT>
 __global__ __launch_bounds__(kBlock) void k_dispatch(DispatchArgs a, int NV, int NC)
 {
     const int lane = threadIdx.x & (kWave - 1);
@@ -103,21 +120,47 @@ __global__ __launch_bounds__(kBlock) void k_dispatch(DispatchArgs a, int NV, int
         const int v = vbase + kWave * i;
         d[i] = (v < NV) ? load_stream(xrow + v) : u32x4{0u, 0u, 0u, 0u};
     }
-    const int32_t* slots = a.slot_idx + t * K;
+    // the token's slots as one batch of scalar loads (the slot array carries
+    // kMaxTopk words of slack, so reading KMAX words is in bounds; words past
+    // K are ignored)
+    int sl[KMAX];
+    const int32_t* srow = a.slot_idx + t * K;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) sl[k] = srow[k];
 
     if constexpr (QUANT == 0) {
-        for (int k = 0; k < K; ++k) {
-            const int s = slots[k];
+        // Wait for the row once (s_waitcnt vmcnt(0), other counters left
+        // alone): the stores below sit in separate branches, and without it
+        // each would wait for every earlier store as well.
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            if (k >= K) break;
+            const int s = sl[k];
             if (s < 0) continue;
             if (s >= a.capacity) {
                 if (lane == 0) atomicOr(a.flags, kFlagCapacity);
                 continue;
             }
-            u32x4* dst = reinterpret_cast<u32x4*>(a.recv) + (int64_t)s * NV;
+            char* row = reinterpret_cast<char*>(a.recv) + (int64_t)s * NV * 16;
+            if constexpr (EP_DISPATCH_BUFFER) {
+                const __amdgpu_buffer_rsrc_t r = row_rsrc(row, NV * 16);
 #pragma unroll
-            for (int i = 0; i < VPL; ++i) {
-                const int v = vbase + kWave * i;
-                if (v < NV) store_stream(d[i], dst + v);
+                for (int i = 0; i < VPL; ++i) {
+                    const int v = vbase + kWave * i;
+                    if (v < NV) __builtin_amdgcn_raw_buffer_store_b128(d[i], r, v * 16, 0, kStoreAux);
+                }
+                if constexpr (ROW_WAIT) __builtin_amdgcn_s_waitcnt(0x0F70);
+            } else {
+#pragma unroll
+                for (int i = 0; i < VPL; ++i) {
+                    const int v = vbase + kWave * i;
+                    u32x4* p = reinterpret_cast<u32x4*>(row) + v;
+                    if (v < NV) {
+                        if constexpr (EP_DISPATCH_NT) __builtin_nontemporal_store(d[i], p);
+                        else *p = d[i];
+                    }
+                }
             }
         }
     } else {
@@ -160,20 +203,23 @@ __global__ __launch_bounds__(kBlock) void k_dispatch(DispatchArgs a, int NV, int
             }
         }
         const int G = CHANNEL ? 1 : NV / 16;
-        for (int k = 0; k < K; ++k) {
-            const int s = slots[k];
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            if (k >= K) break;
+            const int s = sl[k];
             if (s < 0) continue;
             if (s >= a.capacity) {
                 if (lane == 0) atomicOr(a.flags, kFlagCapacity);
                 continue;
             }
-            u32x2* dst = reinterpret_cast<u32x2*>(a.recv) + (int64_t)s * NV;
+            const __amdgpu_buffer_rsrc_t r =
+                row_rsrc(reinterpret_cast<char*>(a.recv) + (int64_t)s * NV * 8, NV * 8);
             float* srow = a.scales + (int64_t)s * G;
 #pragma unroll
             for (int i = 0; i < VPL; ++i) {
                 const int v = vbase + kWave * i;
                 if (v < NV) {
-                    store_stream(code[i], dst + v);
+                    __builtin_amdgcn_raw_buffer_store_b64(code[i], r, v * 8, 0, kStoreAux);
                     if constexpr (CHANNEL) {
                         if (v == 0) srow[0] = scale[i];
                     } else {
@@ -181,20 +227,40 @@ __global__ __launch_bounds__(kBlock) void k_dispatch(DispatchArgs a, int NV, int
                     }
                 }
             }
+            if constexpr (ROW_WAIT) __builtin_amdgcn_s_waitcnt(0x0F70);
         }
     }
 }
 
-template <int QUANT, bool CHANNEL, int VPL>
+template <int QUANT, bool CHANNEL, int VPL, bool ROW_WAIT>
 hipError_t launch_v(const DispatchArgs& a, int NV, hipStream_t s, LaunchEvents ev)
 {
     const int NC = (NV + kWave * VPL - 1) / (kWave * VPL);
     const int64_t items = (a.t_end - a.t_begin) * NC;
     if (items <= 0) return hipSuccess;
     const int blocks = (int)((items + kWavesPerBlock - 1) / kWavesPerBlock);
-    launch_k(k_dispatch<QUANT, CHANNEL, VPL>, dim3(blocks), dim3(kBlock), 0, s, ev.start, ev.stop,
-             a, NV, NC);
+    if (a.K <= 8)
+        launch_k(k_dispatch<QUANT, CHANNEL, VPL, 8, ROW_WAIT>, dim3(blocks), dim3(kBlock), 0, s,
+                 ev.start, ev.stop, a, NV, NC);
+    else
+        launch_k(k_dispatch<QUANT, CHANNEL, VPL, kMaxTopk, ROW_WAIT>, dim3(blocks), dim3(kBlock), 0,
+                 s, ev.start, ev.stop, a, NV, NC);
     return hipGetLastError();
+}
+
+// Row-wait choice: rows of 8 KiB or more are written one row at a time per
+// wave; shorter rows keep all K rows' stores in flight (measured on MI355X:
+// 14 KiB rows 187 us vs 205 us, 4 KiB rows 27.3 us vs 29.2 us).
+inline bool row_wait_for(int row_bytes)
+{
+    return EP_DISPATCH_ROW_WAIT >= 0 ? EP_DISPATCH_ROW_WAIT != 0 : row_bytes >= 8192;
+}
+
+template <int QUANT, bool CHANNEL, int VPL>
+hipError_t launch_w(const DispatchArgs& a, int NV, int row_bytes, hipStream_t s, LaunchEvents ev)
+{
+    return row_wait_for(row_bytes) ? launch_v<QUANT, CHANNEL, VPL, true>(a, NV, s, ev)
+                                   : launch_v<QUANT, CHANNEL, VPL, false>(a, NV, s, ev);
 }
 
 // Channel scales need the whole row in one wave: smallest VPL with
@@ -202,11 +268,28 @@ hipError_t launch_v(const DispatchArgs& a, int NV, hipStream_t s, LaunchEvents e
 template <int QUANT>
 hipError_t launch_channel(const DispatchArgs& a, int NV, hipStream_t s, LaunchEvents ev)
 {
-    if (NV <= 64) return launch_v<QUANT, true, 1>(a, NV, s, ev);
-    if (NV <= 128) return launch_v<QUANT, true, 2>(a, NV, s, ev);
-    if (NV <= 256) return launch_v<QUANT, true, 4>(a, NV, s, ev);
-    if (NV <= 512) return launch_v<QUANT, true, 8>(a, NV, s, ev);
-    return launch_v<QUANT, true, 16>(a, NV, s, ev);
+    const int rb = a.H;   // one byte per element
+    if (NV <= 64) return launch_w<QUANT, true, 1>(a, NV, rb, s, ev);
+    if (NV <= 128) return launch_w<QUANT, true, 2>(a, NV, rb, s, ev);
+    if (NV <= 256) return launch_w<QUANT, true, 4>(a, NV, rb, s, ev);
+    if (NV <= 512) return launch_w<QUANT, true, 8>(a, NV, rb, s, ev);
+    return launch_w<QUANT, true, 16>(a, NV, rb, s, ev);
+}
+
+// Plain scatter: long rows (>= 8 KiB) one 1 KiB piece per wave with row
+// waits; shorter rows as few waves per row as possible (up to 4 KiB per
+// wave), all stores in flight.
+hipError_t launch_plain(const DispatchArgs& a, int NV, hipStream_t s, LaunchEvents ev)
+{
+    const int rb = a.H * 2;
+    int vpl = EP_DISPATCH_VPL;
+    if (vpl < 0) vpl = rb >= 8192 ? 1 : (NV <= 64 ? 1 : NV <= 128 ? 2 : 4);
+    switch (vpl) {
+        case 1: return launch_w<0, false, 1>(a, NV, rb, s, ev);
+        case 2: return launch_w<0, false, 2>(a, NV, rb, s, ev);
+        case 8: return launch_w<0, false, 8>(a, NV, rb, s, ev);
+        default: return launch_w<0, false, 4>(a, NV, rb, s, ev);
+    }
 }
 
 }  // namespace
@@ -216,11 +299,13 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s, LaunchEvents ev
     const int NV = a.H / 8;
     const bool channel = a.quant != 0 && a.group == a.H && a.H != 128;
     switch (a.quant) {
-        case 0: return launch_v<0, false, EP_DISPATCH_VPL>(a, NV, s, ev);
+        case 0: return launch_plain(a, NV, s, ev);
         case 1:
-            return channel ? launch_channel<1>(a, NV, s, ev) : launch_v<1, false, 1>(a, NV, s, ev);
+            return channel ? launch_channel<1>(a, NV, s, ev)
+                           : launch_w<1, false, 1>(a, NV, a.H, s, ev);
         default:
-            return channel ? launch_channel<2>(a, NV, s, ev) : launch_v<2, false, 1>(a, NV, s, ev);
+            return channel ? launch_channel<2>(a, NV, s, ev)
+                           : launch_w<2, false, 1>(a, NV, a.H, s, ev);
     }
 }
 
