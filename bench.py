@@ -43,10 +43,17 @@ def algorithmic_bytes(w, V, S):
     return dict(layout=layout, dispatch=dispatch, combine=combine)
 
 
+KERNEL_SOURCES = {"dispatch": ("dispatch.hip", "scatter.hpp"), "combine": ("combine.hip",),
+                  "layout": ("layout.hip", "route.hpp"),
+                  "layout_dispatch": ("fused.hip", "route.hpp", "scatter.hpp")}
+
+
 def kernel_source_hash(kernel):
-    src = {"dispatch": "dispatch.hip", "combine": "combine.hip", "layout": "layout.hip"}[kernel]
-    with open(os.path.join(ROOT, "combine_get_dispatch_layout_amd", "csrc", src), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for src in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "combine_get_dispatch_layout_amd", "csrc", src), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_path(workload):
@@ -77,11 +84,16 @@ def _counter_rows(path, counter):
     return out
 
 
-def traffic_summary(fetch_csv, write_csv, workload):
-    """Writes profiles/traffic_<workload>.json from two rocprofv3 --pmc
-    counter_collection CSVs of `bench.py --workload <workload>` (FETCH_SIZE,
-    then WRITE_SIZE; KiB per dispatch).  Each counter is scaled by what it
-    reads for the benchmark's 1 GiB device copy (read 1 GiB, write 1 GiB)."""
+KERNEL_SYMBOLS = {"dispatch": "k_dispatch<", "combine": "k_combine<",
+                  "layout_dispatch": "k_route_dispatch<"}
+
+
+def traffic_summary(fetch_csv, write_csv, workload, pipeline):
+    """Adds to profiles/traffic_<workload>.json the HBM bytes per launch of the
+    data-moving kernels found in two rocprofv3 --pmc counter_collection CSVs
+    of `bench.py --workload <workload> --pipeline <pipeline>` (FETCH_SIZE, then
+    WRITE_SIZE; KiB per dispatch).  Each counter is scaled by what it reads
+    for the benchmark's 1 GiB device copy (read 1 GiB, write 1 GiB)."""
     fetch = _counter_rows(fetch_csv, "FETCH_SIZE")
     write = _counter_rows(write_csv, "WRITE_SIZE")
     gib_kib = float(1 << 20)
@@ -94,28 +106,33 @@ def traffic_summary(fetch_csv, write_csv, workload):
     idx, _ = W.routing(w)
     V = int((idx >= 0).sum())
     nbytes = algorithmic_bytes(w, V, 0)
-    kernels = {}
-    for kern in ("dispatch", "combine"):
-        fv = [v for n, v in fetch if f"k_{kern}<" in n]
-        wv = [v for n, v in write if f"k_{kern}<" in n]
+    nbytes["layout_dispatch"] = nbytes["layout"] + nbytes["dispatch"]
+    bench_args = f"--workload {workload} --pipeline {pipeline} --steps 4 --warmup 2 --no-cpu-baseline"
+    command = [f"rocprofv3 --pmc FETCH_SIZE -f csv -d <dir> -o fetch -- python3 bench.py {bench_args}",
+               f"rocprofv3 --pmc WRITE_SIZE -f csv -d <dir> -o write -- python3 bench.py {bench_args}",
+               f"python3 bench.py --traffic-from <dir>/fetch_counter_collection.csv "
+               f"<dir>/write_counter_collection.csv --workload {workload} --pipeline {pipeline}"]
+    path = traffic_path(workload)
+    out = dict(workload=workload, kernels={})
+    if os.path.exists(path):
+        with open(path) as f:
+            out = json.load(f)
+    for kern, sym in KERNEL_SYMBOLS.items():
+        fv = [v for n, v in fetch if sym in n]
+        wv = [v for n, v in write if sym in n]
         if not fv or not wv:
             continue
         fk, wk = float(np.median(fv)), float(np.median(wv))
-        per_launch_alg = nbytes[kern] / len(W.round_ranges(w.num_tokens, w.rounds))
+        launches = 1 if kern == "layout_dispatch" else len(W.round_ranges(w.num_tokens, w.rounds))
+        per_launch_alg = nbytes[kern] / launches
         hbm = (fk * f_fetch + wk * f_write) * 1024.0
-        kernels[kern] = dict(fetch_kib=fk, write_kib=wk, hbm_bytes_per_launch=hbm,
-                             algorithmic_bytes_per_launch=per_launch_alg,
-                             traffic_over_algorithmic=hbm / per_launch_alg, launches=len(fv),
-                             source_sha256_16=kernel_source_hash(kern))
-    out = dict(workload=workload, copy_fetch_kib=copy_f, copy_write_kib=copy_w,
-               fetch_scale=f_fetch, write_scale=f_write, kernels=kernels,
-               command=[f"rocprofv3 --pmc FETCH_SIZE -f csv -d <dir> -o fetch -- python3 bench.py "
-                        f"--workload {workload} --steps 4 --warmup 2 --no-cpu-baseline",
-                        f"rocprofv3 --pmc WRITE_SIZE -f csv -d <dir> -o write -- python3 bench.py "
-                        f"--workload {workload} --steps 4 --warmup 2 --no-cpu-baseline",
-                        f"python3 bench.py --traffic-from <dir>/fetch_counter_collection.csv "
-                        f"<dir>/write_counter_collection.csv --workload {workload}"])
-    with open(traffic_path(workload), "w") as f:
+        out["kernels"][kern] = dict(
+            fetch_kib=fk, write_kib=wk, hbm_bytes_per_launch=hbm,
+            algorithmic_bytes_per_launch=per_launch_alg,
+            traffic_over_algorithmic=hbm / per_launch_alg, launches=len(fv),
+            copy_fetch_kib=copy_f, copy_write_kib=copy_w, fetch_scale=f_fetch,
+            write_scale=f_write, source_sha256_16=kernel_source_hash(kern), command=command)
+    with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))
 
@@ -194,9 +211,11 @@ def main():
     ap.add_argument("--workload", default="qwen3_30b_a3b_prefill")
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to rotate (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--pipeline", choices=("overlap", "serial"), default="overlap",
+    ap.add_argument("--pipeline", choices=("overlap", "serial", "fused"), default="overlap",
                     help="overlap: batch i+1's layout runs on a second stream during batch i's "
-                         "dispatch and combine; serial: one stream, one stage after another")
+                         "dispatch and combine; serial: one stream, one stage after another; "
+                         "fused: ep_layout_dispatch (layout + dispatch in one call) then "
+                         "combine, one stream (one round only)")
     ap.add_argument("--time-every", type=int, default=4,
                     help="rotate mode: arm kernel events on every N-th timed step")
     ap.add_argument("--timing", choices=("rotate", "all"), default="rotate",
@@ -206,7 +225,7 @@ def main():
                     help="summarise two rocprofv3 --pmc runs into profiles/ and exit")
     args = ap.parse_args()
     if args.traffic_from:
-        traffic_summary(args.traffic_from[0], args.traffic_from[1], args.workload)
+        traffic_summary(args.traffic_from[0], args.traffic_from[1], args.workload, args.pipeline)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): this path runs on "
@@ -233,6 +252,10 @@ def main():
     rdt = {0: torch.bfloat16, 1: torch.uint8, 2: torch.int8}[w.quant]
     G = cfg.num_groups
     rounds = W.round_ranges(N, w.rounds)
+    fused = args.pipeline == "fused"
+    if fused and len(rounds) != 1:
+        sys.exit("--pipeline fused dispatches the whole batch in one call: the workload must "
+                 "have one round")
 
     # bytes touched per set; rotate sets so one cycle is >= 1 GiB
     per_set = 2 * N * H * 2 + cap * H * (2 if w.quant == 0 else 1) + cap * H * 2
@@ -262,9 +285,16 @@ def main():
     # is dispatched and combined (double-batch overlap); default priority
     lay_stream = torch.cuda.Stream() if args.pipeline == "overlap" else stream
     for s in sets:
+        if fused:
+            first = ep.bind_layout_dispatch(s["h"], s["topk"], s["x"], s["recv"], s["scales"],
+                                            s["per_rank"], s["per_node"], s["per_expert"],
+                                            s["in_rank"], stream=stream)
+        else:
+            first = ep.bind_get_layout(s["h"], s["topk"], s["per_rank"], s["per_node"],
+                                       s["per_expert"], s["in_rank"], stream=lay_stream)
         s["calls"] = (
-            [ep.bind_get_layout(s["h"], s["topk"], s["per_rank"], s["per_node"], s["per_expert"],
-                                s["in_rank"], stream=lay_stream)],
+            [first],
+            [] if fused else
             [ep.bind_dispatch(s["h"], s["x"], s["recv"], s["scales"], b, e, stream=stream)
              for b, e in rounds],
             [ep.bind_combine(s["h"], s["y"], s["wts"], s["out"], b, e, stream=stream)
@@ -274,8 +304,10 @@ def main():
         s["main_done"].record(stream)
 
     nr = len(rounds)
+    nd = 0 if fused else nr     # dispatch calls per step
+    nstages = 2 if fused else 3
     # one (start, stop) event pair per kernel call of every timed step
-    calls_per_step = 1 + 2 * nr
+    calls_per_step = 1 + nd + nr
     hev = HipEvents(2 * calls_per_step * args.steps)
 
     def armed(i, j):
@@ -286,8 +318,10 @@ def main():
             return True
         if i % args.time_every:
             return False
-        stage = 0 if j == 0 else (1 if j <= nr else 2)
-        return stage == (i // args.time_every) % 3
+        stage = 0 if j == 0 else (1 if j <= nd else 2)
+        if fused:
+            stage = min(stage, 1)
+        return stage == (i // args.time_every) % nstages
 
     def issue(c, i, j, base):
         if base is None or not armed(i, j):
@@ -339,20 +373,27 @@ def main():
                          for i in range(args.steps) if armed(i, j)]) * 1e-3
 
     lay = durs(0)
-    dis = sum(durs(1 + r) for r in range(nr))
-    com = sum(durs(1 + nr + r) for r in range(nr))
+    dis = sum(durs(1 + r) for r in range(nd)) if nd else None
+    com = sum(durs(1 + nd + r) for r in range(nr))
     hev.close()
     ms_per_step = wall / args.steps * 1e3
     value = N * args.steps / wall
-    t_dc = float(np.mean(dis) + np.mean(com))
-
     # per-launch means (one dispatch/combine launch per round)
-    stages = dict(layout=(float(np.mean(lay)), nbytes["layout"], 1),
-                  dispatch=(float(np.mean(dis)), nbytes["dispatch"], nr),
-                  combine=(float(np.mean(com)), nbytes["combine"], nr))
-    dom = max(("dispatch", "combine"), key=lambda k: stages[k][0])
+    if fused:
+        stages = dict(layout_dispatch=(float(np.mean(lay)), nbytes["layout"] + nbytes["dispatch"],
+                                       1),
+                      combine=(float(np.mean(com)), nbytes["combine"], nr))
+        t_dc = float(np.mean(lay) + np.mean(com))
+        dom = max(("layout_dispatch", "combine"), key=lambda k: stages[k][0])
+    else:
+        stages = dict(layout=(float(np.mean(lay)), nbytes["layout"], 1),
+                      dispatch=(float(np.mean(dis)), nbytes["dispatch"], nr),
+                      combine=(float(np.mean(com)), nbytes["combine"], nr))
+        t_dc = float(np.mean(dis) + np.mean(com))
+        dom = max(("dispatch", "combine"), key=lambda k: stages[k][0])
     t_dom, b_dom, launches = stages[dom]
     achieved = b_dom / t_dom / 1e9   # = per-launch bytes / mean per-launch time
+    b_dc = nbytes["dispatch"] + nbytes["combine"] + (nbytes["layout"] if fused else 0)
     traffic = traffic_from_profiles(dom, w.name)
 
     # achievable reference: a plain 1 GiB device copy
@@ -387,14 +428,14 @@ def main():
                      "launches_per_step": launches},
         "stages_us": {k: v[0] * 1e6 for k, v in stages.items()},
         "stages_GBps": {k: v[1] / v[0] / 1e9 for k, v in stages.items()},
-        "dispatch_combine": {"tokens_per_s": N / t_dc,
-                             "GBps": (nbytes["dispatch"] + nbytes["combine"]) / t_dc / 1e9,
-                             "frac_of_peak": (nbytes["dispatch"] + nbytes["combine"]) / t_dc / 1e9
-                             / HBM_PEAK_GBS},
+        ("layout_dispatch_combine" if fused else "dispatch_combine"): {
+                             "tokens_per_s": N / t_dc,
+                             "GBps": b_dc / t_dc / 1e9,
+                             "frac_of_peak": b_dc / t_dc / 1e9 / HBM_PEAK_GBS},
         "device_copy_GBps": copy_gbs,
         "pipeline": args.pipeline,
         "timing": {"mode": args.timing, "every": args.time_every, "host_enqueue_ms_per_step": t_enqueue / args.steps * 1e3,
-                   "samples_per_stage": [int(len(lay)), int(len(dis)), int(len(com))]},
+                   "samples_per_stage": [int(len(x)) for x in (lay, dis, com) if x is not None]},
         "recv_rows": S, "valid_pairs": V,
     }
     if not args.no_cpu_baseline:

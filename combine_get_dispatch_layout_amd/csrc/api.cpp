@@ -54,6 +54,7 @@ int num_nodes(const ep_config& c)
 
 int64_t max_slots_for(const ep_config& c, int64_t tokens)
 {
+    if (c.expert_capacity > 0) return (int64_t)c.num_experts * c.expert_capacity;
     return tokens * c.num_topk + (int64_t)c.num_experts * (c.expert_alignment - 1);
 }
 
@@ -75,6 +76,13 @@ ep_status check_config(const ep_config* c)
         return EP_FAIL(EP_ERR_INVALID_ARG, "ranks_per_node=%d is negative", c->ranks_per_node);
     if (c->expert_alignment < 1)
         return EP_FAIL(EP_ERR_INVALID_ARG, "expert_alignment=%d < 1", c->expert_alignment);
+    if (c->expert_capacity < 0)
+        return EP_FAIL(EP_ERR_INVALID_ARG, "expert_capacity=%d < 0", c->expert_capacity);
+    if (c->expert_capacity > 0 && c->expert_alignment != 1)
+        return EP_FAIL(EP_ERR_INVALID_ARG, "expert_capacity needs expert_alignment == 1 (got %d)",
+                       c->expert_alignment);
+    if ((int64_t)c->num_experts * c->expert_capacity >= (int64_t)1 << 31)
+        return EP_FAIL(EP_ERR_INVALID_ARG, "num_experts * expert_capacity exceeds 2^31 - 1");
     if (c->quant != EP_QUANT_NONE && c->quant != EP_QUANT_FP8_E4M3 && c->quant != EP_QUANT_INT8)
         return EP_FAIL(EP_ERR_INVALID_ARG, "quant=%d unknown", c->quant);
     if (c->quant != EP_QUANT_NONE) {
@@ -150,6 +158,96 @@ struct ep_handle {
     T* at(int64_t off) const { return reinterpret_cast<T*>(ws + off); }
 };
 
+namespace {
+
+// Validates the layout arguments and fills the kernel arguments.
+ep_status layout_args(ep_handle* h, const int32_t* d_topk_idx, int64_t num_tokens,
+                      int32_t* d_num_tokens_per_rank, int32_t* d_num_tokens_per_rdma_rank,
+                      int32_t* d_num_tokens_per_expert, uint8_t* d_is_token_in_rank,
+                      epk::LayoutArgs* out)
+{
+    if (!h) return EP_FAIL(EP_ERR_INVALID_ARG, "handle is NULL");
+    if (num_tokens < 0 || num_tokens > h->max_tokens)
+        return EP_FAIL(EP_ERR_INVALID_ARG, "num_tokens=%lld outside [0, max_tokens=%lld]",
+                       (long long)num_tokens, (long long)h->max_tokens);
+    if (num_tokens > 0 && !d_topk_idx) return EP_FAIL(EP_ERR_INVALID_ARG, "topk_idx is NULL");
+    if (d_topk_idx && !aligned(d_topk_idx, 4))
+        return EP_FAIL(EP_ERR_INVALID_ARG, "topk_idx is not 4-byte aligned");
+    if (d_num_tokens_per_rdma_rank && h->nodes == 0)
+        return EP_FAIL(EP_ERR_INVALID_ARG, "num_tokens_per_rdma_rank needs ranks_per_node > 0");
+    const ep_config& c = h->cfg;
+    epk::LayoutArgs& a = *out;
+    a.topk = d_topk_idx;
+    a.num_tokens = num_tokens;
+    a.K = c.num_topk;
+    a.E = c.num_experts;
+    a.R = c.num_ranks;
+    a.nle = c.num_experts / c.num_ranks;
+    a.ranks_per_node = c.ranks_per_node;
+    a.nle_magic = epk::div_magic((uint32_t)a.nle);
+    a.rpn_magic = epk::div_magic((uint32_t)(c.ranks_per_node > 0 ? c.ranks_per_node : 1));
+    a.nodes = h->nodes;
+    a.A = c.expert_alignment;
+    a.counts_as_prefix = c.counts_as_prefix ? 1 : 0;
+    a.cap = c.expert_capacity;
+    a.ctrl = h->at<uint32_t>(h->cv.ctrl);
+    a.topk_clone = h->at<int32_t>(h->cv.topk);
+    a.slot_idx = h->at<int32_t>(h->cv.slot);
+    a.src_meta = h->at<int32_t>(h->cv.meta);
+    a.hist = h->at<int32_t>(h->cv.hist);
+    a.rank_acc = h->at<int32_t>(h->cv.acc);
+    a.node_acc = a.rank_acc + c.num_ranks;
+    a.psum_expert = h->at<int32_t>(h->cv.psum_expert);
+    a.psum_rank = h->at<int32_t>(h->cv.psum_rank);
+    a.num_unaligned = h->at<int32_t>(h->cv.num_unaligned);
+    a.recv_list = h->at<int32_t>(h->cv.recv_list);
+    a.out_per_rank = d_num_tokens_per_rank;
+    a.out_per_node = d_num_tokens_per_rdma_rank;
+    a.out_per_expert = d_num_tokens_per_expert;
+    a.out_in_rank = d_is_token_in_rank;
+    a.in_rank_words = (c.num_ranks % 4 == 0) && aligned(d_is_token_in_rank, 4);
+    return EP_OK;
+}
+
+// Validates the dispatch arguments for tokens [token_begin, token_end) of a
+// layout over num_tokens tokens and fills the kernel arguments.
+ep_status dispatch_args(const ep_handle* h, int64_t num_tokens, const void* d_x,
+                        int64_t token_begin, int64_t token_end, void* d_recv_x,
+                        float* d_recv_scales, int64_t recv_capacity_rows, epk::DispatchArgs* out)
+{
+    if (token_begin < 0 || token_begin > token_end || token_end > num_tokens)
+        return EP_FAIL(EP_ERR_INVALID_ARG, "token range [%lld,%lld) outside [0,%lld]",
+                       (long long)token_begin, (long long)token_end, (long long)num_tokens);
+    if (recv_capacity_rows < 0) return EP_FAIL(EP_ERR_INVALID_ARG, "recv_capacity_rows < 0");
+    const ep_config& c = h->cfg;
+    if (token_end > token_begin) {
+        if (!d_x || !d_recv_x) return EP_FAIL(EP_ERR_INVALID_ARG, "x or recv_x is NULL");
+        if (!aligned(d_x, 16) || !aligned(d_recv_x, 16))
+            return EP_FAIL(EP_ERR_INVALID_ARG, "x and recv_x must be 16-byte aligned");
+        if (c.quant != EP_QUANT_NONE && (!d_recv_scales || !aligned(d_recv_scales, 4)))
+            return EP_FAIL(EP_ERR_INVALID_ARG, "quantised dispatch needs 4-byte aligned recv_scales");
+    }
+    if (c.quant == EP_QUANT_NONE && d_recv_scales)
+        return EP_FAIL(EP_ERR_INVALID_ARG, "recv_scales must be NULL without quantisation");
+    if (recv_capacity_rows >= (int64_t)1 << 31) recv_capacity_rows = ((int64_t)1 << 31) - 1;
+    epk::DispatchArgs& a = *out;
+    a.x = d_x;
+    a.t_begin = token_begin;
+    a.t_end = token_end;
+    a.H = c.hidden;
+    a.K = c.num_topk;
+    a.slot_idx = h->at<int32_t>(h->cv.slot);
+    a.recv = d_recv_x;
+    a.scales = d_recv_scales;
+    a.capacity = recv_capacity_rows;
+    a.quant = c.quant;
+    a.group = c.quant_group;
+    a.flags = h->at<uint32_t>(h->cv.ctrl) + epk::kCtrlFlags;
+    return EP_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 ep_status ep_workspace_size(const ep_config* cfg, int64_t max_tokens, int64_t* bytes)
@@ -221,45 +319,11 @@ ep_status ep_get_layout(ep_handle* h, const int32_t* d_topk_idx, int64_t num_tok
                         int do_cpu_sync, int32_t* h_num_recv_tokens_per_expert,
                         int64_t* h_num_recv_slots, void* stream)
 {
-    if (!h) return EP_FAIL(EP_ERR_INVALID_ARG, "handle is NULL");
-    if (num_tokens < 0 || num_tokens > h->max_tokens)
-        return EP_FAIL(EP_ERR_INVALID_ARG, "num_tokens=%lld outside [0, max_tokens=%lld]",
-                       (long long)num_tokens, (long long)h->max_tokens);
-    if (num_tokens > 0 && !d_topk_idx) return EP_FAIL(EP_ERR_INVALID_ARG, "topk_idx is NULL");
-    if (d_topk_idx && !aligned(d_topk_idx, 4))
-        return EP_FAIL(EP_ERR_INVALID_ARG, "topk_idx is not 4-byte aligned");
-    if (d_num_tokens_per_rdma_rank && h->nodes == 0)
-        return EP_FAIL(EP_ERR_INVALID_ARG, "num_tokens_per_rdma_rank needs ranks_per_node > 0");
-    const ep_config& c = h->cfg;
     epk::LayoutArgs a;
-    a.topk = d_topk_idx;
-    a.num_tokens = num_tokens;
-    a.K = c.num_topk;
-    a.E = c.num_experts;
-    a.R = c.num_ranks;
-    a.nle = c.num_experts / c.num_ranks;
-    a.ranks_per_node = c.ranks_per_node;
-    a.nle_magic = epk::div_magic((uint32_t)a.nle);
-    a.rpn_magic = epk::div_magic((uint32_t)(c.ranks_per_node > 0 ? c.ranks_per_node : 1));
-    a.nodes = h->nodes;
-    a.A = c.expert_alignment;
-    a.counts_as_prefix = c.counts_as_prefix ? 1 : 0;
-    a.ctrl = h->at<uint32_t>(h->cv.ctrl);
-    a.topk_clone = h->at<int32_t>(h->cv.topk);
-    a.slot_idx = h->at<int32_t>(h->cv.slot);
-    a.src_meta = h->at<int32_t>(h->cv.meta);
-    a.hist = h->at<int32_t>(h->cv.hist);
-    a.rank_acc = h->at<int32_t>(h->cv.acc);
-    a.node_acc = a.rank_acc + c.num_ranks;
-    a.psum_expert = h->at<int32_t>(h->cv.psum_expert);
-    a.psum_rank = h->at<int32_t>(h->cv.psum_rank);
-    a.num_unaligned = h->at<int32_t>(h->cv.num_unaligned);
-    a.recv_list = h->at<int32_t>(h->cv.recv_list);
-    a.out_per_rank = d_num_tokens_per_rank;
-    a.out_per_node = d_num_tokens_per_rdma_rank;
-    a.out_per_expert = d_num_tokens_per_expert;
-    a.out_in_rank = d_is_token_in_rank;
-    a.in_rank_words = (c.num_ranks % 4 == 0) && aligned(d_is_token_in_rank, 4);
+    ep_status st = layout_args(h, d_topk_idx, num_tokens, d_num_tokens_per_rank,
+                               d_num_tokens_per_rdma_rank, d_num_tokens_per_expert,
+                               d_is_token_in_rank, &a);
+    if (st != EP_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     EP_HIP(epk::launch_layout(a, s, h->take_events()));
     h->num_tokens = num_tokens;
@@ -268,7 +332,7 @@ ep_status ep_get_layout(ep_handle* h, const int32_t* d_topk_idx, int64_t num_tok
         uint32_t S = 0;
         if (h_num_recv_tokens_per_expert)
             EP_HIP(hipMemcpyAsync(h_num_recv_tokens_per_expert, a.recv_list,
-                                  sizeof(int32_t) * c.num_experts, hipMemcpyDeviceToHost, s));
+                                  sizeof(int32_t) * h->cfg.num_experts, hipMemcpyDeviceToHost, s));
         EP_HIP(hipMemcpyAsync(&S, a.ctrl + epk::kCtrlNumSlots, sizeof(uint32_t),
                               hipMemcpyDeviceToHost, s));
         EP_HIP(hipStreamSynchronize(s));
@@ -283,38 +347,42 @@ ep_status ep_dispatch(const ep_handle* h, const void* d_x, int64_t token_begin, 
 {
     if (!h) return EP_FAIL(EP_ERR_INVALID_ARG, "handle is NULL");
     if (h->num_tokens < 0) return EP_FAIL(EP_ERR_STATE, "ep_get_layout has not run on this handle");
-    if (token_begin < 0 || token_begin > token_end || token_end > h->num_tokens)
-        return EP_FAIL(EP_ERR_INVALID_ARG, "token range [%lld,%lld) outside [0,%lld]",
-                       (long long)token_begin, (long long)token_end, (long long)h->num_tokens);
-    if (recv_capacity_rows < 0) return EP_FAIL(EP_ERR_INVALID_ARG, "recv_capacity_rows < 0");
-    const ep_config& c = h->cfg;
-    if (token_end > token_begin) {
-        if (!d_x || !d_recv_x) return EP_FAIL(EP_ERR_INVALID_ARG, "x or recv_x is NULL");
-        if (!aligned(d_x, 16) || !aligned(d_recv_x, 16))
-            return EP_FAIL(EP_ERR_INVALID_ARG, "x and recv_x must be 16-byte aligned");
-        if (c.quant != EP_QUANT_NONE && (!d_recv_scales || !aligned(d_recv_scales, 4)))
-            return EP_FAIL(EP_ERR_INVALID_ARG, "quantised dispatch needs 4-byte aligned recv_scales");
-    }
-    if (c.quant == EP_QUANT_NONE && d_recv_scales)
-        return EP_FAIL(EP_ERR_INVALID_ARG, "recv_scales must be NULL without quantisation");
+    epk::DispatchArgs a;
+    ep_status st = dispatch_args(h, h->num_tokens, d_x, token_begin, token_end, d_recv_x,
+                                 d_recv_scales, recv_capacity_rows, &a);
+    if (st != EP_OK) return st;
     if (h->host_slots >= 0 && h->host_slots > recv_capacity_rows)
         return EP_FAIL(EP_ERR_CAPACITY, "layout needs %lld receive rows, capacity is %lld",
                        (long long)h->host_slots, (long long)recv_capacity_rows);
-    if (recv_capacity_rows >= (int64_t)1 << 31) recv_capacity_rows = ((int64_t)1 << 31) - 1;
-    epk::DispatchArgs a;
-    a.x = d_x;
-    a.t_begin = token_begin;
-    a.t_end = token_end;
-    a.H = c.hidden;
-    a.K = c.num_topk;
-    a.slot_idx = h->at<int32_t>(h->cv.slot);
-    a.recv = d_recv_x;
-    a.scales = d_recv_scales;
-    a.capacity = recv_capacity_rows;
-    a.quant = c.quant;
-    a.group = c.quant_group;
-    a.flags = h->at<uint32_t>(h->cv.ctrl) + epk::kCtrlFlags;
     EP_HIP(epk::launch_dispatch(a, static_cast<hipStream_t>(stream), h->take_events()));
+    return EP_OK;
+}
+
+ep_status ep_layout_dispatch(ep_handle* h, const int32_t* d_topk_idx, int64_t num_tokens,
+                             int32_t* d_num_tokens_per_rank, int32_t* d_num_tokens_per_rdma_rank,
+                             int32_t* d_num_tokens_per_expert, uint8_t* d_is_token_in_rank,
+                             const void* d_x, void* d_recv_x, float* d_recv_scales,
+                             int64_t recv_capacity_rows, void* stream)
+{
+    epk::LayoutArgs la;
+    ep_status st = layout_args(h, d_topk_idx, num_tokens, d_num_tokens_per_rank,
+                               d_num_tokens_per_rdma_rank, d_num_tokens_per_expert,
+                               d_is_token_in_rank, &la);
+    if (st != EP_OK) return st;
+    epk::DispatchArgs da;
+    st = dispatch_args(h, num_tokens, d_x, 0, num_tokens, d_recv_x, d_recv_scales,
+                       recv_capacity_rows, &da);
+    if (st != EP_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const epk::LaunchEvents ev = h->take_events();
+    if (epk::route_dispatch_fits(la)) {
+        EP_HIP(epk::launch_route_dispatch(la, da, s, ev));
+    } else {
+        EP_HIP(epk::launch_layout(la, s, epk::LaunchEvents{ev.start, nullptr}));
+        EP_HIP(epk::launch_dispatch(da, s, epk::LaunchEvents{nullptr, ev.stop}));
+    }
+    h->num_tokens = num_tokens;
+    h->host_slots = -1;
     return EP_OK;
 }
 

@@ -17,6 +17,9 @@ constexpr int kLayoutBlock = 256;
 // Largest row, in 16-byte vectors, that one wave can hold for a whole-row
 // (channel) quantisation scale: 64 lanes x 16 vectors = 8192 bf16.
 constexpr int kMaxVecPerLane = 16;
+// Largest batch whose layout + dispatch run as one launch (every block
+// recomputes the routing of the whole batch in LDS).
+constexpr int kRouteDispatchMaxTokens = 256;
 
 constexpr uint32_t kFlagBadId = 1u;
 constexpr uint32_t kFlagCapacity = 2u;
@@ -34,6 +37,7 @@ struct LayoutArgs {
     const int32_t* topk;        // [N,K] caller's routing
     int64_t num_tokens;         // N
     int K, E, R, nle, ranks_per_node, nodes, A, counts_as_prefix;
+    int cap;                    // >0: fixed-capacity layout, rows [e*cap, (e+1)*cap)
     // n / nle and n / ranks_per_node as __umulhi(n, magic) (magic 0 = divide
     // by 1); exact for n < 2^22, see div_magic()
     uint32_t nle_magic, rpn_magic;
@@ -110,5 +114,9 @@ hipError_t launch_clear(uint32_t* words, int n, hipStream_t s);
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t s, LaunchEvents ev = {});
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s, LaunchEvents ev = {});
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s, LaunchEvents ev = {});
+// Layout + dispatch of the whole batch in one launch (small batches).
+bool route_dispatch_fits(const LayoutArgs& la);
+hipError_t launch_route_dispatch(const LayoutArgs& la, const DispatchArgs& da, hipStream_t s,
+                                 LaunchEvents ev = {});
 
 }  // namespace epk

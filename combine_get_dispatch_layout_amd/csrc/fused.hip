@@ -1,0 +1,153 @@
+// Single-launch routing layout + dispatch for small batches (decode).
+//
+// What is computed: exactly ep_get_layout followed by ep_dispatch over the
+// whole batch -- the unified dispatch call of "DeepEP V1 vs V2 深度对比分析"
+// §2.2, which takes the routing and returns the received rows together with
+// the handle.
+//
+// Design: for N <= 256 tokens the whole routing fits one block's LDS, so
+// every block of the dispatch grid recomputes it (one token per thread, the
+// same deterministic code as the layout kernels) instead of waiting for
+// another kernel: each wave first issues the loads of its own row chunk,
+// then the block routes all N tokens and forms the aligned prefix and the
+// final slots in LDS, and the wave scatters its chunk.  Block 0 alone writes
+// the handle arrays and the layout outputs.  One launch replaces two, and
+// the row loads overlap the routing.
+#include "route.hpp"
+#include "scatter.hpp"
+
+namespace epk {
+
+namespace {
+
+using namespace route;
+using namespace scatter;
+
+constexpr int kBlock = 256;                      // 4 waves, one token per thread
+constexpr int kWavesPerBlock = kBlock / kWave;
+constexpr int kKmax = 8;
+
+size_t fused_dispatch_lds(const LayoutArgs& a)
+{
+    return route_lds_bytes(kWavesPerBlock, a.E, a.R, a.nodes) +
+           ((size_t)a.E + 1 + 2 * kBlock) * 4 + (size_t)kRouteDispatchMaxTokens * kKmax * 4;
+}
+
+template <int QUANT, bool CHANNEL, int VPL, bool ROW_WAIT>
+__global__ __launch_bounds__(kBlock) void k_route_dispatch(LayoutArgs la, DispatchArgs da, int NV,
+                                                           int NC)
+{
+    extern __shared__ __align__(16) unsigned char smem[];
+    const RouteLds L = carve_route(smem, kWavesPerBlock, la.E, la.R);
+    int32_t* psum = L.ncnt + la.nodes;         // [E+1]
+    int32_t* scratch = psum + la.E + 1;         // [2*kBlock]
+    int32_t* slot_tab = scratch + 2 * kBlock;   // [N][K] final slots
+    const int K = la.K;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int item = blockIdx.x * kWavesPerBlock + wv;
+    const int64_t t_item = item / NC;
+    const bool has_item = t_item < da.t_end;
+    const int vbase = (item % NC) * (kWave * VPL) + lane;
+
+    // the wave's row chunk is in flight while the block routes
+    u32x4 d[VPL];
+    if (has_item) load_chunk<VPL>(da, t_item, vbase, NV, d);
+
+    const bool lead = blockIdx.x == 0;
+    int ids[kKmax], lr[kKmax];
+    route_block<kKmax, kWavesPerBlock>(la, 0, L, ids, lr, lead);
+    aligned_prefix<kBlock>(la, L.bhist, psum, scratch);
+    int off[kKmax];
+    bool dropped = false;
+#pragma unroll
+    for (int k = 0; k < kKmax; ++k)
+        off[k] = ids[k] >= 0 ? final_slot(la, psum[ids[k]], lr[k], dropped) : 0;
+    const int t = threadIdx.x;
+    if (t < la.num_tokens) {
+#pragma unroll
+        for (int k = 0; k < kKmax; ++k)
+            if (k < K) slot_tab[t * K + k] = ids[k] >= 0 ? off[k] : -1;
+    }
+    if (lead) {
+        flag_dropped<kKmax>(la, dropped);
+        store_slots<kKmax>(la, t, ids, off);
+        write_expert_arrays<kBlock>(la, L.bhist, psum);
+        write_padding<kBlock>(la, L.bhist, psum, 0, 1);
+        for (int r = t; r < la.R; r += kBlock)
+            if (la.out_per_rank) la.out_per_rank[r] = L.rcnt[r];
+        for (int n = t; n < la.nodes; n += kBlock)
+            if (la.out_per_node) la.out_per_node[n] = L.ncnt[n];
+    }
+    __syncthreads();
+    if (!has_item) return;
+    int sl[kKmax];
+#pragma unroll
+    for (int k = 0; k < kKmax; ++k) sl[k] = (k < K) ? slot_tab[t_item * K + k] : -1;
+    scatter_chunk<QUANT, CHANNEL, VPL, kKmax, ROW_WAIT>(da, vbase, NV, d, sl, lane);
+}
+
+template <int QUANT, bool CHANNEL, int VPL, bool ROW_WAIT>
+hipError_t launch_rd(const LayoutArgs& la, const DispatchArgs& da, int NV, hipStream_t s,
+                     LaunchEvents ev)
+{
+    const int NC = (NV + kWave * VPL - 1) / (kWave * VPL);
+    const int64_t items = la.num_tokens * NC;
+    int blocks = (int)((items + kWavesPerBlock - 1) / kWavesPerBlock);
+    if (blocks < 1) blocks = 1;   // the layout outputs are written even for N = 0
+    launch_k(k_route_dispatch<QUANT, CHANNEL, VPL, ROW_WAIT>, dim3(blocks), dim3(kBlock),
+             fused_dispatch_lds(la), s, ev.start, ev.stop, la, da, NV, NC);
+    return hipGetLastError();
+}
+
+template <int QUANT, bool CHANNEL, int VPL>
+hipError_t launch_rw(const LayoutArgs& la, const DispatchArgs& da, int NV, int row_bytes,
+                     hipStream_t s, LaunchEvents ev)
+{
+    return dispatch_row_wait(row_bytes) ? launch_rd<QUANT, CHANNEL, VPL, true>(la, da, NV, s, ev)
+                                        : launch_rd<QUANT, CHANNEL, VPL, false>(la, da, NV, s, ev);
+}
+
+template <int QUANT>
+hipError_t launch_channel(const LayoutArgs& la, const DispatchArgs& da, int NV, hipStream_t s,
+                          LaunchEvents ev)
+{
+    const int rb = da.H;
+    if (NV <= 64) return launch_rw<QUANT, true, 1>(la, da, NV, rb, s, ev);
+    if (NV <= 128) return launch_rw<QUANT, true, 2>(la, da, NV, rb, s, ev);
+    if (NV <= 256) return launch_rw<QUANT, true, 4>(la, da, NV, rb, s, ev);
+    if (NV <= 512) return launch_rw<QUANT, true, 8>(la, da, NV, rb, s, ev);
+    return launch_rw<QUANT, true, 16>(la, da, NV, rb, s, ev);
+}
+
+}  // namespace
+
+bool route_dispatch_fits(const LayoutArgs& la)
+{
+    return la.num_tokens <= kRouteDispatchMaxTokens && la.K <= kKmax &&
+           fused_dispatch_lds(la) <= kMaxLds;
+}
+
+hipError_t launch_route_dispatch(const LayoutArgs& la, const DispatchArgs& da, hipStream_t s,
+                                 LaunchEvents ev)
+{
+    const int NV = da.H / 8;
+    const bool channel = da.quant != 0 && da.group == da.H && da.H != 128;
+    switch (da.quant) {
+        case 0: {
+            const int rb = da.H * 2;
+            const int vpl = dispatch_plain_vpl(NV, rb);
+            if (vpl == 1) return launch_rw<0, false, 1>(la, da, NV, rb, s, ev);
+            if (vpl == 2) return launch_rw<0, false, 2>(la, da, NV, rb, s, ev);
+            return launch_rw<0, false, 4>(la, da, NV, rb, s, ev);
+        }
+        case 1:
+            return channel ? launch_channel<1>(la, da, NV, s, ev)
+                           : launch_rw<1, false, 1>(la, da, NV, da.H, s, ev);
+        default:
+            return channel ? launch_channel<2>(la, da, NV, s, ev)
+                           : launch_rw<2, false, 1>(la, da, NV, da.H, s, ev);
+    }
+}
+
+}  // namespace epk

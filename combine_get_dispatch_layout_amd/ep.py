@@ -21,7 +21,8 @@ EP_FLAG_BAD_EXPERT_ID, EP_FLAG_RECV_CAPACITY, EP_FLAG_Y_ROWS = 1, 2, 4
 
 # Every symbol include/ep.h declares.
 SYMBOLS = ("ep_workspace_size", "ep_recv_capacity", "ep_handle_init", "ep_handle_free",
-           "ep_get_layout", "ep_dispatch", "ep_combine", "ep_set_kernel_events",
+           "ep_get_layout", "ep_dispatch", "ep_layout_dispatch", "ep_combine",
+           "ep_set_kernel_events",
            "ep_handle_get_view", "ep_check_error", "ep_status_str", "ep_last_error_message")
 
 
@@ -30,7 +31,7 @@ class ep_config(ctypes.Structure):
                 ("num_experts", ctypes.c_int32), ("num_ranks", ctypes.c_int32),
                 ("ranks_per_node", ctypes.c_int32), ("expert_alignment", ctypes.c_int32),
                 ("quant", ctypes.c_int32), ("quant_group", ctypes.c_int32),
-                ("counts_as_prefix", ctypes.c_int32)]
+                ("counts_as_prefix", ctypes.c_int32), ("expert_capacity", ctypes.c_int32)]
 
 
 class ep_handle_view(ctypes.Structure):
@@ -67,6 +68,7 @@ def lib():
         L.ep_handle_free.restype = None
         L.ep_get_layout.argtypes = [P, P, I64, P, P, P, P, I32, P, P, P]
         L.ep_dispatch.argtypes = [P, P, I64, I64, P, P, I64, P]
+        L.ep_layout_dispatch.argtypes = [P, P, I64, P, P, P, P, P, P, P, I64, P]
         L.ep_combine.argtypes = [P, P, I64, P, I64, I64, P, P]
         L.ep_set_kernel_events.argtypes = [P, P, P]
         L.ep_handle_get_view.argtypes = [P, P]
@@ -76,7 +78,7 @@ def lib():
         L.ep_last_error_message.argtypes = []
         L.ep_last_error_message.restype = ctypes.c_char_p
         for name in ("ep_workspace_size", "ep_recv_capacity", "ep_handle_init", "ep_get_layout",
-                     "ep_dispatch", "ep_combine", "ep_set_kernel_events", "ep_handle_get_view",
+                     "ep_dispatch", "ep_layout_dispatch", "ep_combine", "ep_set_kernel_events", "ep_handle_get_view",
                      "ep_check_error"):
             getattr(L, name).restype = I32
         _lib = L
@@ -115,11 +117,12 @@ class Config:
     quant: int = EP_QUANT_NONE
     quant_group: int = 0
     counts_as_prefix: bool = False
+    expert_capacity: int = 0
 
     def c(self):
         return ep_config(self.hidden, self.num_topk, self.num_experts, self.num_ranks,
                          self.ranks_per_node, self.expert_alignment, self.quant, self.quant_group,
-                         int(bool(self.counts_as_prefix)))
+                         int(bool(self.counts_as_prefix)), self.expert_capacity)
 
     @property
     def num_nodes(self):
@@ -190,6 +193,36 @@ def ep_handle_free(h: Handle):
     h.free()
 
 
+def _layout_outputs(cfg, topk_idx, per_rank, per_rdma, per_expert, in_rank, alloc):
+    if topk_idx.dtype != torch.int32 or topk_idx.dim() != 2 or topk_idx.shape[1] != cfg.num_topk:
+        raise ValueError("topk_idx must be int32 [N, num_topk]")
+    N = topk_idx.shape[0]
+    dev = topk_idx.device
+    if alloc:
+        if per_rank is None:
+            per_rank = torch.empty(cfg.num_ranks, dtype=torch.int32, device=dev)
+        if per_expert is None:
+            per_expert = torch.empty(cfg.num_experts, dtype=torch.int32, device=dev)
+        if in_rank is None:
+            in_rank = torch.empty((N, cfg.num_ranks), dtype=torch.bool, device=dev)
+        if per_rdma is None and cfg.num_nodes:
+            per_rdma = torch.empty(cfg.num_nodes, dtype=torch.int32, device=dev)
+    return per_rank, per_rdma, per_expert, in_rank
+
+
+def _check_dispatch_tensors(cfg, x, recv_x, recv_scales):
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[1] != cfg.hidden:
+        raise ValueError("x must be bf16 [N, hidden]")
+    want = {EP_QUANT_NONE: (torch.bfloat16,), EP_QUANT_FP8_E4M3: (torch.uint8, torch.float8_e4m3fn),
+            EP_QUANT_INT8: (torch.int8,)}[cfg.quant]
+    if recv_x.dtype not in want or recv_x.dim() != 2 or recv_x.shape[1] != cfg.hidden:
+        raise ValueError(f"recv_x must be {want} [rows, hidden]")
+    if cfg.quant:
+        if (recv_scales is None or recv_scales.dtype != torch.float32
+                or recv_scales.shape != (recv_x.shape[0], cfg.num_groups)):
+            raise ValueError("recv_scales must be fp32 [rows, hidden/quant_group]")
+
+
 def ep_get_layout(h: Handle, topk_idx: torch.Tensor, num_tokens_per_rank=None,
                   num_tokens_per_rdma_rank=None, num_tokens_per_expert=None,
                   is_token_in_rank=None, do_cpu_sync=False, alloc_outputs=True):
@@ -197,19 +230,11 @@ def ep_get_layout(h: Handle, topk_idx: torch.Tensor, num_tokens_per_rank=None,
     (torch.empty) when not given and alloc_outputs is set.  Returns a dict of
     the outputs; with do_cpu_sync also the host list and S."""
     cfg = h.cfg
-    if topk_idx.dtype != torch.int32 or topk_idx.dim() != 2 or topk_idx.shape[1] != cfg.num_topk:
-        raise ValueError("topk_idx must be int32 [N, num_topk]")
+    num_tokens_per_rank, num_tokens_per_rdma_rank, num_tokens_per_expert, is_token_in_rank = \
+        _layout_outputs(cfg, topk_idx, num_tokens_per_rank, num_tokens_per_rdma_rank,
+                        num_tokens_per_expert, is_token_in_rank, alloc_outputs)
     N = topk_idx.shape[0]
     dev = topk_idx.device
-    if alloc_outputs:
-        if num_tokens_per_rank is None:
-            num_tokens_per_rank = torch.empty(cfg.num_ranks, dtype=torch.int32, device=dev)
-        if num_tokens_per_expert is None:
-            num_tokens_per_expert = torch.empty(cfg.num_experts, dtype=torch.int32, device=dev)
-        if is_token_in_rank is None:
-            is_token_in_rank = torch.empty((N, cfg.num_ranks), dtype=torch.bool, device=dev)
-        if num_tokens_per_rdma_rank is None and cfg.num_nodes:
-            num_tokens_per_rdma_rank = torch.empty(cfg.num_nodes, dtype=torch.int32, device=dev)
     host_list = None
     S = ctypes.c_int64(-1)
     if do_cpu_sync:
@@ -232,23 +257,33 @@ def ep_dispatch(h: Handle, x: torch.Tensor, recv_x: torch.Tensor,
                 recv_scales: Optional[torch.Tensor] = None, token_begin=0, token_end=None):
     """a3.  x bf16 [N,H]; recv_x [rows,H] bf16 / uint8 (E4M3FN) / int8;
     recv_scales fp32 [rows,G] when quantised."""
-    cfg = h.cfg
-    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[1] != cfg.hidden:
-        raise ValueError("x must be bf16 [N, hidden]")
-    want = {EP_QUANT_NONE: (torch.bfloat16,), EP_QUANT_FP8_E4M3: (torch.uint8, torch.float8_e4m3fn),
-            EP_QUANT_INT8: (torch.int8,)}[cfg.quant]
-    if recv_x.dtype not in want or recv_x.dim() != 2 or recv_x.shape[1] != cfg.hidden:
-        raise ValueError(f"recv_x must be {want} [rows, hidden]")
-    if cfg.quant:
-        if (recv_scales is None or recv_scales.dtype != torch.float32
-                or recv_scales.shape != (recv_x.shape[0], cfg.num_groups)):
-            raise ValueError("recv_scales must be fp32 [rows, hidden/quant_group]")
+    _check_dispatch_tensors(h.cfg, x, recv_x, recv_scales)
     token_end = x.shape[0] if token_end is None else token_end
     if not 0 <= token_begin <= token_end <= x.shape[0]:
         raise ValueError("token range outside x")
     _check(lib().ep_dispatch(h.ptr, _ptr(x), token_begin, token_end, _ptr(recv_x),
                              _ptr(recv_scales), recv_x.shape[0], _stream(x.device)))
     return recv_x, recv_scales
+
+
+def ep_layout_dispatch(h: Handle, topk_idx: torch.Tensor, x: torch.Tensor, recv_x: torch.Tensor,
+                       recv_scales: Optional[torch.Tensor] = None, num_tokens_per_rank=None,
+                       num_tokens_per_rdma_rank=None, num_tokens_per_expert=None,
+                       is_token_in_rank=None, alloc_outputs=True):
+    """a1 + a2 + a3 in one call, no host sync.  Same arguments as
+    ep_get_layout and ep_dispatch over the whole batch.  Returns the layout
+    outputs dict; recv_x / recv_scales are filled in place."""
+    cfg = h.cfg
+    outs = _layout_outputs(cfg, topk_idx, num_tokens_per_rank, num_tokens_per_rdma_rank,
+                           num_tokens_per_expert, is_token_in_rank, alloc_outputs)
+    _check_dispatch_tensors(cfg, x, recv_x, recv_scales)
+    if x.shape[0] != topk_idx.shape[0]:
+        raise ValueError("x and topk_idx disagree on the number of tokens")
+    _check(lib().ep_layout_dispatch(h.ptr, _ptr(topk_idx), topk_idx.shape[0], *map(_ptr, outs),
+                                    _ptr(x), _ptr(recv_x), _ptr(recv_scales), recv_x.shape[0],
+                                    _stream(x.device)))
+    return dict(num_tokens_per_rank=outs[0], num_tokens_per_rdma_rank=outs[1],
+                num_tokens_per_expert=outs[2], is_token_in_rank=outs[3])
 
 
 def ep_combine(h: Handle, y: torch.Tensor, topk_weights: torch.Tensor, out: torch.Tensor,
@@ -339,6 +374,17 @@ def bind_dispatch(h: Handle, x, recv_x, recv_scales, token_begin, token_end, str
     """A callable issuing ep_dispatch with these tensors and token range."""
     s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream(x.device)
     return _bound(h, lib().ep_dispatch, h.ptr, _ptr(x), token_begin, token_end, _ptr(recv_x),
+                  _ptr(recv_scales), recv_x.shape[0], s)
+
+
+def bind_layout_dispatch(h: Handle, topk_idx, x, recv_x, recv_scales, num_tokens_per_rank=None,
+                         num_tokens_per_rdma_rank=None, num_tokens_per_expert=None,
+                         is_token_in_rank=None, stream=None):
+    """A callable issuing ep_layout_dispatch with these tensors."""
+    s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream(x.device)
+    return _bound(h, lib().ep_layout_dispatch, h.ptr, _ptr(topk_idx), topk_idx.shape[0],
+                  _ptr(num_tokens_per_rank), _ptr(num_tokens_per_rdma_rank),
+                  _ptr(num_tokens_per_expert), _ptr(is_token_in_rank), _ptr(x), _ptr(recv_x),
                   _ptr(recv_scales), recv_x.shape[0], s)
 
 

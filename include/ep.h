@@ -83,6 +83,14 @@ typedef struct ep_config {
     int32_t counts_as_prefix;  /* host list: 0 = per-expert aligned counts,
                                   1 = inclusive prefix restarting per rank
                                   ([P2] MOE_EXPERT_TOKEN_NUMS_TYPE)              */
+    int32_t expert_capacity;   /* 0: packed layout (aligned segments placed by
+                                  prefix sums).  >0: fixed-capacity layout, the
+                                  low-latency buffer shape of [P3] §6.3: expert
+                                  e owns rows [e*cap, (e+1)*cap) whatever its
+                                  count; pairs past cap are dropped (slot -1)
+                                  and flagged EP_FLAG_RECV_CAPACITY.  Needs
+                                  expert_alignment == 1.  The host list then
+                                  holds the filled rows min(count, cap).       */
 } ep_config;
 
 typedef struct ep_handle ep_handle;
@@ -102,7 +110,7 @@ typedef struct ep_handle_view {
     int64_t num_tokens;            /* N of the last ep_get_layout                */
     int64_t max_tokens;            /* capacity the handle was created with       */
     int64_t max_slots;             /* receive rows that can ever be needed:
-                                      max_tokens*K + E*(A-1)                     */
+                                      max_tokens*K + E*(A-1), or E*capacity      */
     int64_t num_recv_slots;        /* S if known on the host (do_cpu_sync), else -1 */
 } ep_handle_view;
 
@@ -111,7 +119,8 @@ typedef struct ep_handle_view {
 ep_status ep_workspace_size(const ep_config* cfg, int64_t max_tokens, int64_t* bytes);
 
 /* Receive rows a dispatch of num_tokens tokens can need in the worst case
- * (every pair valid, every expert fully padded): num_tokens*K + E*(A-1).
+ * (every pair valid, every expert fully padded): num_tokens*K + E*(A-1), or
+ * E*expert_capacity in the fixed-capacity layout.
  * Sizing recv_x / y with this many rows never triggers EP_ERR_CAPACITY. */
 ep_status ep_recv_capacity(const ep_config* cfg, int64_t num_tokens, int64_t* rows);
 
@@ -161,6 +170,25 @@ ep_status ep_get_layout(ep_handle* h, const int32_t* d_topk_idx, int64_t num_tok
 ep_status ep_dispatch(const ep_handle* h, const void* d_x, int64_t token_begin, int64_t token_end,
                       void* d_recv_x, float* d_recv_scales, int64_t recv_capacity_rows,
                       void* stream);
+
+/* a1 + a2 + a3 in one call: the unified dispatch of [P3] §2.2, which takes
+ * the routing and returns the received rows together with the handle, with
+ * no host synchronisation (the decode-step form; [P3] §6 low-latency mode).
+ *   Same result as ep_get_layout(h, d_topk_idx, num_tokens, <the four
+ *   outputs>, do_cpu_sync = 0, ...) followed by ep_dispatch(h, d_x, 0,
+ *   num_tokens, d_recv_x, d_recv_scales, recv_capacity_rows): every argument
+ *   has the meaning, layout and checks given there, and the handle is left
+ *   in the same state (num_recv_slots unknown on the host).
+ *   For num_tokens <= 256 and num_topk <= 8 (when the routing of the whole
+ *   batch fits one workgroup's LDS) this is a single kernel launch; otherwise
+ *   it launches the layout kernels and then the dispatch kernel.
+ *   Receive rows beyond recv_capacity_rows are skipped and flagged on the
+ *   device (ep_check_error); size recv_x with ep_recv_capacity to avoid it. */
+ep_status ep_layout_dispatch(ep_handle* h, const int32_t* d_topk_idx, int64_t num_tokens,
+                             int32_t* d_num_tokens_per_rank, int32_t* d_num_tokens_per_rdma_rank,
+                             int32_t* d_num_tokens_per_expert, uint8_t* d_is_token_in_rank,
+                             const void* d_x, void* d_recv_x, float* d_recv_scales,
+                             int64_t recv_capacity_rows, void* stream);
 
 /* a4: combine ([P2] API table: the paired inverse of dispatch).
  *   d_y: bf16 [y_rows, H] expert outputs in receive-row order;

@@ -30,6 +30,8 @@ def lib():
         L.orc_layout.restype = i32
         L.orc_slots.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, P, i64]
         L.orc_slots.restype = i64
+        L.orc_slots_fixed.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, P]
+        L.orc_slots_fixed.restype = i64
         L.orc_recv_list.argtypes = [P, i32, i32, i32, P]
         L.orc_recv_list.restype = None
         L.orc_dispatch.argtypes = [P, i64, i32, P, i32, i32, i32, i64, i64, P, P]
@@ -134,6 +136,25 @@ def slots(topk_idx, num_experts, num_ranks, expert_alignment=1):
         raise RuntimeError("receive-row capacity exceeded")
     return dict(S=int(S), psum_expert=psum_e, psum_rank=psum_r, num_unaligned=unal,
                 slot_idx=slot, src_meta=meta[:S].copy())
+
+
+def slots_fixed(topk_idx, num_experts, num_ranks, capacity):
+    """Fixed-capacity receive layout.  Returns dict(S = E*capacity,
+    dropped, psum_expert, psum_rank, num_unaligned, slot_idx, src_meta)."""
+    idx = _c(topk_idx, np.int32)
+    N, K = idx.shape
+    E, R = num_experts, num_ranks
+    psum_e = np.zeros(E + 1, np.int32)
+    psum_r = np.zeros(R + 1, np.int32)
+    unal = np.zeros(E, np.int32)
+    slot = np.zeros((N, K), np.int32)
+    meta = np.zeros((max(E * capacity, 1), 2), np.int32)
+    d = lib().orc_slots_fixed(_p(idx), N, K, E, R, capacity, _p(psum_e), _p(psum_r), _p(unal),
+                              _p(slot), _p(meta))
+    if d < 0:
+        raise ValueError("topk_idx holds an id outside [-1, num_experts)")
+    return dict(S=E * capacity, dropped=int(d), psum_expert=psum_e, psum_rank=psum_r,
+                num_unaligned=unal, slot_idx=slot, src_meta=meta[:E * capacity].copy())
 
 
 def recv_list(psum_expert, num_experts, num_ranks, counts_as_prefix):

@@ -222,6 +222,42 @@ int64_t orc_slots(const int32_t* topk_idx, int64_t N, int K, int E, int R, int A
     return S;
 }
 
+int64_t orc_slots_fixed(const int32_t* topk_idx, int64_t N, int K, int E, int R, int cap,
+                        int32_t* psum_expert, int32_t* psum_rank, int32_t* num_unaligned,
+                        int32_t* slot_idx, int32_t* src_meta)
+{
+    if (!ids_valid(topk_idx, N * K, E)) return -1;
+    int nle = E / R;
+    for (int e = 0; e <= E; ++e) psum_expert[e] = e * cap;
+    for (int r = 0; r <= R; ++r) psum_rank[r] = r * nle * cap;
+    for (int64_t s = 0; s < (int64_t)E * cap; ++s) {
+        src_meta[2 * s] = -1;
+        src_meta[2 * s + 1] = -1;
+    }
+    int64_t dropped = 0;
+    for (int e = 0; e < E; ++e) {
+        int32_t pos = 0;
+        for (int64_t t = 0; t < N; ++t)
+            for (int k = 0; k < K; ++k) {
+                if (topk_idx[t * K + k] != e) continue;
+                if (pos < cap) {
+                    int64_t s = (int64_t)e * cap + pos;
+                    slot_idx[t * K + k] = (int32_t)s;
+                    src_meta[2 * s] = (int32_t)t;
+                    src_meta[2 * s + 1] = k;
+                } else {
+                    slot_idx[t * K + k] = -1;
+                    dropped += 1;
+                }
+                pos += 1;
+            }
+        num_unaligned[e] = pos;
+    }
+    for (int64_t i = 0; i < N * K; ++i)
+        if (topk_idx[i] < 0) slot_idx[i] = -1;
+    return dropped;
+}
+
 void orc_recv_list(const int32_t* psum_expert, int E, int R, int counts_as_prefix, int32_t* list)
 {
     int nle = E / R;

@@ -78,6 +78,18 @@ int64_t orc_slots(const int32_t* topk_idx, int64_t N, int K, int E, int R, int A
                   int32_t* psum_expert, int32_t* psum_rank, int32_t* num_unaligned,
                   int32_t* slot_idx, int32_t* src_meta, int64_t meta_cap);
 
+/* Fixed-capacity receive layout (the low-latency buffer shape
+ * [num_local_experts, ranks x max_tokens, hidden] of [P3] §6.3, with one
+ * source rank): expert e owns rows [e*cap, (e+1)*cap) whatever its count;
+ * slot = e*cap + position of (t,k) among the pairs of e in (t,k) order.
+ * A pair whose position reaches cap gets slot -1 (dropped).  psum_expert[e]
+ * = e*cap, psum_rank[r] = r*nle*cap, num_unaligned = raw counts, src_meta
+ * [E*cap, 2] with (-1,-1) on unused rows.  Returns the number of dropped
+ * pairs, or -1 on a bad id. */
+int64_t orc_slots_fixed(const int32_t* topk_idx, int64_t N, int K, int E, int R, int cap,
+                        int32_t* psum_expert, int32_t* psum_rank, int32_t* num_unaligned,
+                        int32_t* slot_idx, int32_t* src_meta);
+
 /* Host list of received tokens per expert ([P2] MOE_EXPERT_TOKEN_NUMS_TYPE):
  * counts_as_prefix == 0: aligned count of each expert;
  * counts_as_prefix != 0: inclusive prefix of those counts restarting at each

@@ -29,7 +29,25 @@ def config_of(w: W.Workload, counts_as_prefix=False):
                      num_ranks=w.num_ranks, ranks_per_node=w.ranks_per_node,
                      expert_alignment=w.expert_alignment, quant=w.quant,
                      quant_group=w.quant_group if w.quant else 0,
-                     counts_as_prefix=counts_as_prefix)
+                     counts_as_prefix=counts_as_prefix, expert_capacity=w.expert_capacity)
+
+
+def oracle_slots(w: W.Workload, idx):
+    """The oracle's slot assignment for the workload's layout mode."""
+    if w.expert_capacity > 0:
+        return oracle.slots_fixed(idx, w.num_experts, w.num_ranks, w.expert_capacity)
+    return oracle.slots(idx, w.num_experts, w.num_ranks, w.expert_alignment)
+
+
+def expected_host_list(w: W.Workload, ref_slots, counts_as_prefix=False):
+    if w.expert_capacity > 0:
+        filled = np.minimum(ref_slots["num_unaligned"], w.expert_capacity).astype(np.int64)
+        if counts_as_prefix:
+            nle = w.num_experts // w.num_ranks
+            filled = filled.reshape(w.num_ranks, nle).cumsum(axis=1).ravel()
+        return filled.tolist()
+    return oracle.recv_list(ref_slots["psum_expert"], w.num_experts, w.num_ranks,
+                            counts_as_prefix).tolist()
 
 
 def recv_dtype(quant):
@@ -59,6 +77,12 @@ class GpuRun:
         self.lay = ep.ep_get_layout(self.h, self.topk, do_cpu_sync=do_cpu_sync)
         return self.lay
 
+    def layout_dispatch(self):
+        """Layout and dispatch of the whole batch in one ep_layout_dispatch call."""
+        assert len(self.rounds) == 1
+        self.lay = ep.ep_layout_dispatch(self.h, self.topk, self.x, self.recv, self.scales)
+        return self.lay
+
     def dispatch(self):
         for b, e in self.rounds:
             ep.ep_dispatch(self.h, self.x, self.recv, self.scales, b, e)
@@ -68,7 +92,7 @@ class GpuRun:
             ep.ep_combine(self.h, y, self.wts, self.out, b, e)
 
 
-def compare_layout(run: GpuRun, idx, ref_lay, ref_slots):
+def compare_layout(run: GpuRun, idx, ref_lay, ref_slots, host_sync=True):
     w = run.w
     lay = run.lay
     assert np.array_equal(lay["num_tokens_per_expert"].cpu().numpy(), ref_lay["num_tokens_per_expert"])
@@ -80,15 +104,18 @@ def compare_layout(run: GpuRun, idx, ref_lay, ref_slots):
                               ref_lay["num_tokens_per_rdma_rank"])
     v = ep.ep_handle_get_view(run.h)
     S = ref_slots["S"]
-    assert lay["num_recv_slots"] == S == v["num_recv_slots"]
+    if host_sync:
+        assert lay["num_recv_slots"] == S == v["num_recv_slots"]
+    else:
+        assert v["num_recv_slots"] == -1
     assert np.array_equal(v["psum_expert"].cpu().numpy(), ref_slots["psum_expert"])
     assert np.array_equal(v["psum_rank"].cpu().numpy(), ref_slots["psum_rank"])
     assert np.array_equal(v["num_unaligned"].cpu().numpy(), ref_slots["num_unaligned"])
     assert np.array_equal(v["slot_idx"].cpu().numpy(), ref_slots["slot_idx"])
     assert np.array_equal(v["src_meta"][:S].cpu().numpy(), ref_slots["src_meta"])
     assert np.array_equal(v["topk_idx"].cpu().numpy(), idx)
-    lst = oracle.recv_list(ref_slots["psum_expert"], w.num_experts, w.num_ranks, False)
-    assert lay["num_recv_tokens_per_expert_list"] == lst.tolist()
+    if host_sync:
+        assert lay["num_recv_tokens_per_expert_list"] == expected_host_list(w, ref_slots)
 
 
 def ordered_code(c, quant):
@@ -138,21 +165,28 @@ def compare_combine(got_bits, ref_bits, y_bits, wts, slot_idx, K):
 
 
 def run_and_check(w: W.Workload, device="cuda", rounds=None, seed_x=None, seed_y=None,
-                  check_combine=True, idx=None, wts=None):
+                  check_combine=True, idx=None, wts=None, fused=False):
     """Full path for workload `w` on the device and on the oracle; asserts
-    the parity bars.  Returns a dict of statistics."""
+    the parity bars.  Returns a dict of statistics.  fused: layout and
+    dispatch through the one-call ep_layout_dispatch (no host sync)."""
     if idx is None:
         idx, wts = W.routing(w)
     N = idx.shape[0]
     x = W.activations(N, w.hidden, seed_x if seed_x is not None else W.x_seed(w), device=device)
     run = GpuRun(w, idx, wts, x, device=device, rounds=rounds)
-    run.layout()
-    run.dispatch()
-    st, flags = ep.ep_check_error(run.h)
-    assert st == ep.EP_OK and flags == 0
+    if fused:
+        run.layout_dispatch()
+    else:
+        run.layout()
+        run.dispatch()
     ref_lay = oracle.layout(idx, w.num_experts, w.num_ranks, w.ranks_per_node)
-    ref_slots = oracle.slots(idx, w.num_experts, w.num_ranks, w.expert_alignment)
-    compare_layout(run, idx, ref_lay, ref_slots)
+    ref_slots = oracle_slots(w, idx)
+    st, flags = ep.ep_check_error(run.h)
+    if ref_slots.get("dropped", 0) > 0:    # full fixed-capacity segments
+        assert st == ep.EP_ERR_CAPACITY and flags == ep.EP_FLAG_RECV_CAPACITY
+    else:
+        assert st == ep.EP_OK and flags == 0
+    compare_layout(run, idx, ref_lay, ref_slots, host_sync=not fused)
     x_bits = bits16(x)
     ref_recv, ref_scales = oracle.dispatch(x_bits, ref_slots["slot_idx"], run.cap, quant=w.quant,
                                            group=w.quant_group or None)

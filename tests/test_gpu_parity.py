@@ -52,9 +52,10 @@ def test_workload_reduced(name, kw):
 
 
 def _custom(N, H, E, R, K, A=1, quant=W.QUANT_NONE, group=0, mask=0.0, seed=7, rpn=8,
-            routing="uniform"):
+            routing="uniform", cap=0):
     return W.Workload("custom", N, H, E, R, K, expert_alignment=A, quant=quant, quant_group=group,
-                      mask_prob=mask, seed=seed, ranks_per_node=rpn, routing=routing)
+                      mask_prob=mask, seed=seed, ranks_per_node=rpn, routing=routing,
+                      expert_capacity=cap)
 
 
 @pytest.mark.parametrize("args", [
@@ -240,4 +241,105 @@ def test_empty_batch_scan_path():
     assert lay["num_tokens_per_expert"].abs().sum().item() == 0
     assert lay["num_tokens_per_rank"].abs().sum().item() == 0
     assert lay["num_tokens_per_rdma_rank"].abs().sum().item() == 0
+    assert ep.ep_check_error(h) == (ep.EP_OK, 0)
+
+
+# Fixed-capacity receive layout (low-latency buffer shape): every layout
+# path, with and without full segments (dropped pairs are flagged).
+@pytest.mark.parametrize("args", [
+    dict(N=128, H=7168, E=256, R=16, K=8, cap=128, quant=W.QUANT_FP8, group=128),  # decode shape
+    dict(N=128, H=512, E=64, R=8, K=8, cap=12),              # fused, some experts overflow
+    dict(N=1000, H=256, E=64, R=8, K=6, cap=200, mask=0.1),  # fused 16 waves
+    dict(N=3000, H=128, E=128, R=16, K=8, cap=150),          # count + finish, overflow
+    dict(N=9000, H=64, E=256, R=32, K=8, cap=400),           # count + scan + slots
+])
+def test_fixed_capacity_layout(args):
+    w = _custom(**args)
+    _say(f"[parity] fixed capacity {args}")
+    run_and_check(w)
+
+
+def test_fixed_capacity_with_zipf_and_host_prefix():
+    w = W.WORKLOADS["deepseek_v3_prefill"].scaled(num_tokens=700, hidden=256, expert_alignment=1,
+                                                  expert_capacity=64)
+    idx, _ = W.routing(w)
+    from shuffle_check import config_of, expected_host_list, oracle_slots
+    h = ep.ep_handle_init(config_of(w, counts_as_prefix=True), 700)
+    lay = ep.ep_get_layout(h, torch.from_numpy(idx).cuda(), do_cpu_sync=True)
+    ref = oracle_slots(w, idx)
+    assert ref["dropped"] > 0                     # Zipf: hot experts overflow 64 rows
+    assert lay["num_recv_slots"] == w.num_experts * 64
+    assert lay["num_recv_tokens_per_expert_list"] == expected_host_list(w, ref, True)
+    v = ep.ep_handle_get_view(h)
+    assert np.array_equal(v["slot_idx"].cpu().numpy(), ref["slot_idx"])
+    assert ep.ep_check_error(h)[1] == ep.EP_FLAG_RECV_CAPACITY
+
+
+# One-call layout + dispatch (ep_layout_dispatch).  Up to 256 tokens with
+# K <= 8 and routing that fits one block's LDS it is a single launch; the
+# other cases drive its two-launch form.  Results must equal the oracle's
+# exactly as the separate calls do; the host list is not produced (no sync).
+@pytest.mark.parametrize("args", [
+    dict(N=128, H=7168, E=256, R=16, K=8, quant=W.QUANT_FP8, group=128),   # decode shape
+    dict(N=256, H=7168, E=256, R=16, K=8),                   # full block, 14 KiB rows
+    dict(N=1, H=8, E=1, R=1, K=1),                           # smallest
+    dict(N=77, H=2048, E=64, R=8, K=6, quant=W.QUANT_INT8, group=2048),  # channel scale
+    dict(N=200, H=1032, E=128, R=16, K=8, A=16, mask=0.2),   # padding rows, ragged H
+    dict(N=128, H=512, E=64, R=8, K=8, cap=12),              # fixed capacity, overflow
+    dict(N=100, H=4096, E=32, R=4, K=4, quant=W.QUANT_INT8, group=128, rpn=3),
+    dict(N=64, H=264, E=1024, R=1024, K=4, rpn=1),           # routing LDS too large: 2 launches
+    dict(N=96, H=256, E=64, R=8, K=16),                      # K > 8: 2 launches
+    dict(N=257, H=512, E=64, R=8, K=8, quant=W.QUANT_FP8, group=128),  # N > 256: 2 launches
+])
+def test_layout_dispatch_one_call(args):
+    w = _custom(**args)
+    _say(f"[parity] layout_dispatch {args}")
+    run_and_check(w, fused=True)
+
+
+def test_layout_dispatch_decode_workload_and_reuse():
+    """The decode workload at full size through the one call, then a cached
+    ep_dispatch over a token range of the same handle and a second one-call
+    step with new routing on the same handle."""
+    w = W.WORKLOADS["ll_decode_fp8"]
+    _say(f"[parity] layout_dispatch decode N={w.num_tokens}")
+    st = run_and_check(w, fused=True)
+    run = st["run"]
+    from shuffle_check import compare_dispatch, oracle_slots
+    idx = run.topk.cpu().numpy()
+    ref_slots = oracle_slots(w, idx)
+    run.recv.zero_()
+    run.scales.zero_()
+    ep.ep_dispatch(run.h, run.x, run.recv, run.scales, 40, 101)
+    x_bits = bits16(run.x)
+    ref_recv, ref_scales = oracle.dispatch(x_bits, ref_slots["slot_idx"], run.cap, quant=w.quant,
+                                           group=w.quant_group, t_begin=40, t_end=101)
+    assert compare_dispatch(run, ref_recv, ref_scales, ref_slots) == 0
+    # new routing, same handle
+    w2 = w.scaled(seed=4242)
+    idx2, _ = W.routing(w2)
+    run.topk.copy_(torch.from_numpy(idx2))
+    run.layout_dispatch()
+    ref2 = oracle_slots(w2, idx2)
+    v = ep.ep_handle_get_view(run.h)
+    assert np.array_equal(v["slot_idx"].cpu().numpy(), ref2["slot_idx"])
+    assert ep.ep_check_error(run.h) == (ep.EP_OK, 0)
+
+
+def test_layout_dispatch_empty_batch():
+    cfg = ep.Config(256, 2, 16, 4, ranks_per_node=2, expert_alignment=4)
+    h = ep.ep_handle_init(cfg, 16)
+    idx = torch.empty((0, 2), dtype=torch.int32, device="cuda")
+    x = torch.zeros((0, 256), dtype=torch.bfloat16, device="cuda")
+    recv = torch.zeros((ep.ep_recv_capacity(cfg, 0), 256), dtype=torch.bfloat16, device="cuda")
+    per_rank = torch.full((4,), 7, dtype=torch.int32, device="cuda")
+    per_expert = torch.full((16,), 7, dtype=torch.int32, device="cuda")
+    per_node = torch.full((2,), 7, dtype=torch.int32, device="cuda")
+    lay = ep.ep_layout_dispatch(h, idx, x, recv, num_tokens_per_rank=per_rank,
+                                num_tokens_per_expert=per_expert, num_tokens_per_rdma_rank=per_node)
+    assert lay["num_tokens_per_expert"].cpu().tolist() == [0] * 16
+    assert lay["num_tokens_per_rank"].cpu().tolist() == [0] * 4
+    assert lay["num_tokens_per_rdma_rank"].cpu().tolist() == [0, 0]
+    v = ep.ep_handle_get_view(h)
+    assert v["psum_expert"].cpu().tolist() == [0] * 17
     assert ep.ep_check_error(h) == (ep.EP_OK, 0)

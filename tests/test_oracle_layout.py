@@ -189,3 +189,66 @@ def test_receive_bound_on_workloads(name):
     lay = oracle.layout(idx, w.num_experts, w.num_ranks)
     assert lay["num_tokens_per_expert"].sum() == w.num_tokens * w.num_topk - (idx == -1).sum()
     _check_slot_invariants(idx, s, w.num_experts, w.num_ranks, w.expert_alignment)
+
+
+def _argsort_slots_fixed(idx, E, cap):
+    """Fixed-capacity slots from numpy's stable sort: position of each pair
+    among its expert's pairs; kept while the position is below cap."""
+    N, K = idx.shape
+    key = np.where(idx >= 0, idx, E).ravel()
+    order = np.argsort(key, kind="stable")
+    cnt = np.bincount(key, minlength=E + 1)[:E]
+    starts = np.concatenate([[0], np.cumsum(cnt)])
+    slot = np.full(N * K, -1, np.int64)
+    for e in range(E):
+        pairs = order[starts[e]:starts[e] + cnt[e]]
+        pos = np.arange(cnt[e])
+        keep = pos < cap
+        slot[pairs[keep]] = e * cap + pos[keep]
+    return slot.reshape(N, K), cnt
+
+
+def _check_fixed(idx, s, E, R, cap):
+    ref_slot, cnt = _argsort_slots_fixed(idx, E, cap)
+    assert np.array_equal(s["slot_idx"], ref_slot)
+    assert np.array_equal(s["num_unaligned"], cnt)
+    assert s["dropped"] == int(np.maximum(cnt - cap, 0).sum())
+    assert s["psum_expert"].tolist() == [e * cap for e in range(E + 1)]
+    assert s["psum_rank"].tolist() == [r * (E // R) * cap for r in range(R + 1)]
+    meta = s["src_meta"]
+    used = ref_slot[ref_slot >= 0]
+    ts, ks = np.nonzero(ref_slot >= 0)
+    assert np.array_equal(meta[used, 0], ts) and np.array_equal(meta[used, 1], ks)
+    assert (meta[:, 0] >= 0).sum() == used.size
+    for e in range(E):
+        seg = meta[e * cap:(e + 1) * cap]
+        assert np.all(seg[min(cnt[e], cap):] == -1)
+
+
+@pytest.mark.parametrize("N,K,E,R,cap", [(1, 1, 1, 1, 1), (64, 8, 32, 4, 64), (200, 4, 16, 4, 10),
+                                          (300, 6, 64, 8, 300), (128, 8, 256, 16, 128)])
+def test_slots_fixed_match_stable_argsort(N, K, E, R, cap):
+    rng = np.random.default_rng(N * 3 + cap)
+    idx = _random_routing(rng, N, K, E)
+    _check_fixed(idx, oracle.slots_fixed(idx, E, R, cap), E, R, cap)
+
+
+def test_slots_fixed_exhaustive_tiny():
+    E, R = 4, 2
+    for cap in (1, 2, 6):
+        for flat in itertools.product(range(-1, E), repeat=6):
+            idx = np.array(flat, np.int32).reshape(3, 2)
+            _check_fixed(idx, oracle.slots_fixed(idx, E, R, cap), E, R, cap)
+
+
+def test_slots_fixed_relates_to_packed_layout():
+    """With enough capacity every pair keeps its position inside the expert,
+    so fixed slot - e*cap == packed slot - psum[e] (A = 1)."""
+    rng = np.random.default_rng(8)
+    idx = _random_routing(rng, 500, 8, 64, dup_p=0.0)
+    f = oracle.slots_fixed(idx, 64, 8, 500)
+    p = oracle.slots(idx, 64, 8, 1)
+    e = np.where(idx >= 0, idx, 0)
+    valid = idx >= 0
+    assert f["dropped"] == 0
+    assert np.array_equal((f["slot_idx"] - e * 500)[valid], (p["slot_idx"] - p["psum_expert"][e])[valid])

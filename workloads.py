@@ -38,6 +38,7 @@ class Workload:
     rounds: int = 1
     seed: int = 0
     ranks_per_node: int = 8
+    expert_capacity: int = 0      # >0: fixed-capacity receive layout
 
     def scaled(self, **kw) -> "Workload":
         return replace(self, **kw)
