@@ -32,6 +32,8 @@ def lib():
         L.orc_slots.restype = i64
         L.orc_slots_fixed.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, P]
         L.orc_slots_fixed.restype = i64
+        L.orc_source_counts.argtypes = [P, i64, i32, i32, i32, i32, P, P]
+        L.orc_source_counts.restype = i32
         L.orc_recv_list.argtypes = [P, i32, i32, i32, P]
         L.orc_recv_list.restype = None
         L.orc_dispatch.argtypes = [P, i64, i32, P, i32, i32, i32, i64, i64, P, P]
@@ -155,6 +157,22 @@ def slots_fixed(topk_idx, num_experts, num_ranks, capacity):
         raise ValueError("topk_idx holds an id outside [-1, num_experts)")
     return dict(S=E * capacity, dropped=int(d), psum_expert=psum_e, psum_rank=psum_r,
                 num_unaligned=unal, slot_idx=slot, src_meta=meta[:E * capacity].copy())
+
+
+def source_counts(topk_idx, num_experts, num_ranks, num_sources):
+    """Per-source receive quantities of a batch of num_sources stacked source
+    ranks.  Returns dict(psum_source_rank [R, P+1], expert_source_base [P, E])."""
+    idx = _c(topk_idx, np.int32)
+    N, K = idx.shape
+    E, R, P = num_experts, num_ranks, num_sources
+    psr = np.zeros((R, P + 1), np.int32)
+    base = np.zeros((P, E), np.int32)
+    rc = lib().orc_source_counts(_p(idx), N, K, E, R, P, _p(psr), _p(base))
+    if rc == -1:
+        raise ValueError("topk_idx holds an id outside [-1, num_experts)")
+    if rc != 0:
+        raise ValueError("num_tokens must be a multiple of num_sources")
+    return dict(psum_source_rank=psr, expert_source_base=base)
 
 
 def recv_list(psum_expert, num_experts, num_ranks, counts_as_prefix):

@@ -258,6 +258,52 @@ int64_t orc_slots_fixed(const int32_t* topk_idx, int64_t N, int K, int E, int R,
     return dropped;
 }
 
+/* Several source ranks in one batch: source p owns tokens [p*Ns, (p+1)*Ns),
+ * Ns = N / P.  Ordering receive rows by (source, token, k) is then the
+ * (t, k) order of the stacked batch, so orc_slots already places them; this
+ * adds the per-source quantities of the EPHandle ([P3] §3.1
+ * psum_num_recv_tokens_per_scaleup_rank, §3.2 its caching):
+ *   psum_source_rank [R][P+1]: for receiving rank r, the exclusive prefix
+ *     over sources of the tokens r receives from each source, a token
+ *     counted once per rank it has an expert on (reading: as for
+ *     num_tokens_per_rank, one copy of a token travels to each rank);
+ *   expert_source_base [P][E]: pairs of expert e from sources before p --
+ *     source p's rows of expert e start at psum_expert[e] + this.
+ * Returns 0, -1 on a bad id, -2 if P < 1 or N is not a multiple of P. */
+int orc_source_counts(const int32_t* topk_idx, int64_t N, int K, int E, int R, int P,
+                      int32_t* psum_source_rank, int32_t* expert_source_base)
+{
+    if (P < 1 || N % P != 0) return -2;
+    if (!ids_valid(topk_idx, N * K, E)) return -1;
+    int nle = E / R;
+    int64_t Ns = N / P;
+    for (int r = 0; r < R; ++r) psum_source_rank[r * (P + 1)] = 0;
+    for (int e = 0; e < E; ++e) expert_source_base[e] = 0;   /* source 0 */
+    for (int p = 0; p < P; ++p) {
+        /* this source's tokens per rank and pairs per expert */
+        for (int r = 0; r < R; ++r) {
+            int32_t c = 0;
+            for (int64_t t = p * Ns; t < (p + 1) * Ns; ++t) {
+                int hit = 0;
+                for (int k = 0; k < K; ++k) {
+                    int e = topk_idx[t * K + k];
+                    if (e >= 0 && rank_of_expert(e, nle) == r) hit = 1;
+                }
+                c += hit;
+            }
+            psum_source_rank[r * (P + 1) + p + 1] = psum_source_rank[r * (P + 1) + p] + c;
+        }
+        if (p + 1 < P)
+            for (int e = 0; e < E; ++e) {
+                int32_t c = 0;
+                for (int64_t t = p * Ns; t < (p + 1) * Ns; ++t)
+                    for (int k = 0; k < K; ++k) c += topk_idx[t * K + k] == e;
+                expert_source_base[(int64_t)(p + 1) * E + e] = expert_source_base[(int64_t)p * E + e] + c;
+            }
+    }
+    return 0;
+}
+
 void orc_recv_list(const int32_t* psum_expert, int E, int R, int counts_as_prefix, int32_t* list)
 {
     int nle = E / R;

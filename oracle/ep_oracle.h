@@ -90,6 +90,17 @@ int64_t orc_slots_fixed(const int32_t* topk_idx, int64_t N, int K, int E, int R,
                         int32_t* psum_expert, int32_t* psum_rank, int32_t* num_unaligned,
                         int32_t* slot_idx, int32_t* src_meta);
 
+/* Several source ranks stacked in one batch ([P3] §3.1
+ * psum_num_recv_tokens_per_scaleup_rank): source p owns tokens
+ * [p*N/P, (p+1)*N/P), so the (source, token, k) receive order is the (t,k)
+ * order of orc_slots.  psum_source_rank [R][P+1]: per receiving rank, the
+ * exclusive prefix over sources of the tokens received from each source
+ * (a token counted once per rank).  expert_source_base [P][E]: pairs of
+ * expert e from the sources before p.  Returns 0, -1 on a bad id, -2 if
+ * P < 1 or N % P != 0. */
+int orc_source_counts(const int32_t* topk_idx, int64_t N, int K, int E, int R, int P,
+                      int32_t* psum_source_rank, int32_t* expert_source_base);
+
 /* Host list of received tokens per expert ([P2] MOE_EXPERT_TOKEN_NUMS_TYPE):
  * counts_as_prefix == 0: aligned count of each expert;
  * counts_as_prefix != 0: inclusive prefix of those counts restarting at each

@@ -252,3 +252,88 @@ def test_slots_fixed_relates_to_packed_layout():
     valid = idx >= 0
     assert f["dropped"] == 0
     assert np.array_equal((f["slot_idx"] - e * 500)[valid], (p["slot_idx"] - p["psum_expert"][e])[valid])
+
+
+# ---- several source ranks stacked in one batch ----------------------------
+
+def test_worked_example_multi_source():
+    g = _gold()
+    idx = np.array(g["topk_idx"], np.int32)
+    E, R = g["num_experts"], g["num_ranks"]
+    for P, want in g["multi_source"].items():
+        got = oracle.source_counts(idx, E, R, int(P))
+        assert got["psum_source_rank"].tolist() == want["psum_source_rank"]
+        assert got["expert_source_base"].tolist() == want["expert_source_base"]
+
+
+def _numpy_source_counts(idx, E, R, P):
+    """Library-routine form: np.add.at over (source, expert) and a reshape of
+    the token x rank membership into (source, token, rank)."""
+    N, K = idx.shape
+    Ns = N // P
+    src = np.repeat(np.arange(N) // Ns, K)
+    flat = idx.ravel()
+    ok = flat >= 0
+    cnt = np.zeros((P, E), np.int64)
+    np.add.at(cnt, (src[ok], flat[ok]), 1)
+    base = np.vstack([np.zeros((1, E), np.int64), np.cumsum(cnt, axis=0)[:-1]])
+    member = np.zeros((N, R), bool)
+    rows = np.repeat(np.arange(N), K)
+    member[rows[ok], flat[ok] // (E // R)] = True
+    per = member.reshape(P, Ns, R).sum(axis=1)          # [P, R]
+    psr = np.hstack([np.zeros((R, 1), np.int64), np.cumsum(per.T, axis=1)])
+    return psr, base
+
+
+@pytest.mark.parametrize("N,K,E,R,P", [(1, 1, 1, 1, 1), (40, 3, 12, 4, 4), (300, 8, 64, 16, 3),
+                                       (256, 8, 256, 16, 16), (64, 2, 8, 8, 64), (90, 6, 64, 8, 1)])
+def test_source_counts_match_numpy(N, K, E, R, P):
+    rng = np.random.default_rng(N * 31 + P)
+    idx = _random_routing(rng, N, K, E)
+    got = oracle.source_counts(idx, E, R, P)
+    psr, base = _numpy_source_counts(idx, E, R, P)
+    assert np.array_equal(got["psum_source_rank"], psr)
+    assert np.array_equal(got["expert_source_base"], base)
+
+
+@pytest.mark.parametrize("A", [1, 4])
+def test_source_bases_place_each_sources_rows(A):
+    """With the slots of the stacked batch, the rows of expert e coming from
+    source p are contiguous and start at psum_expert[e] + base[p, e]; the
+    last prefix entry of each rank is num_tokens_per_rank."""
+    rng = np.random.default_rng(77 + A)
+    N, K, E, R, P = 240, 6, 32, 8, 6
+    idx = _random_routing(rng, N, K, E)
+    sc = oracle.source_counts(idx, E, R, P)
+    s = oracle.slots(idx, E, R, A)
+    lay = oracle.layout(idx, E, R)
+    assert np.array_equal(sc["psum_source_rank"][:, -1], lay["num_tokens_per_rank"])
+    Ns = N // P
+    for p in range(P):
+        part = idx[p * Ns:(p + 1) * Ns]
+        slots = s["slot_idx"][p * Ns:(p + 1) * Ns]
+        for e in range(E):
+            rows = np.sort(slots[part == e])
+            if rows.size == 0:
+                continue
+            start = s["psum_expert"][e] + sc["expert_source_base"][p, e]
+            assert np.array_equal(rows, np.arange(start, start + rows.size))
+
+
+def test_source_counts_degenerate_and_invalid():
+    rng = np.random.default_rng(5)
+    idx = _random_routing(rng, 50, 4, 16)
+    one = oracle.source_counts(idx, 16, 4, 1)
+    lay = oracle.layout(idx, 16, 4)
+    assert np.array_equal(one["psum_source_rank"][:, 1], lay["num_tokens_per_rank"])
+    assert not one["expert_source_base"].any()
+    # one token per source: the per-source rank counts are is_token_in_rank
+    per_tok = oracle.source_counts(idx, 16, 4, 50)
+    assert np.array_equal(np.diff(per_tok["psum_source_rank"], axis=1),
+                          lay["is_token_in_rank"].T.astype(np.int32))
+    with pytest.raises(ValueError):
+        oracle.source_counts(idx, 16, 4, 3)          # 50 tokens do not split into 3
+    bad = idx.copy()
+    bad[3, 1] = 16
+    with pytest.raises(ValueError):
+        oracle.source_counts(bad, 16, 4, 2)
