@@ -6,6 +6,13 @@ assignment (ep_get_layout), dispatch (ep_dispatch, per round) and combine
 Default workload: the Qwen3-30B-A3B-shaped prefill (4096 tokens, hidden 2048
 bf16, 128 experts over 16 simulated ranks, top-8).
 
+--pipeline picks how a step is issued: overlap (default; the layout of the
+next batch runs on a second stream), serial (one stream), fused
+(ep_layout_dispatch + combine, the one-call form for decode batches) or
+cached (dispatch + combine on a handle whose layout was computed once before
+the timed loop: the cached-dispatch decode loop, whose step does not include
+the layout).
+
 Prints one JSON line.  `value` is tokens/s over whole steps; the roofline
 entry is for the kernel with the largest share of the step, with its
 achieved bandwidth = algorithmic bytes per launch / mean launch time taken
@@ -210,12 +217,18 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="qwen3_30b_a3b_prefill")
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to rotate (0 = auto)")
+    ap.add_argument("--num-sources", type=int, default=0,
+                    help=">1: read the batch as this many stacked source ranks (receive order "
+                         "(source, token, k) plus the per-source counts)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--pipeline", choices=("overlap", "serial", "fused"), default="overlap",
+    ap.add_argument("--pipeline", choices=("overlap", "serial", "fused", "cached"),
+                    default="overlap",
                     help="overlap: batch i+1's layout runs on a second stream during batch i's "
                          "dispatch and combine; serial: one stream, one stage after another; "
                          "fused: ep_layout_dispatch (layout + dispatch in one call) then "
-                         "combine, one stream (one round only)")
+                         "combine, one stream (one round only); cached: the layout is computed "
+                         "once per buffer set and each step is dispatch + combine on the cached "
+                         "handle (a decode loop whose routing does not change)")
     ap.add_argument("--time-every", type=int, default=4,
                     help="rotate mode: arm kernel events on every N-th timed step")
     ap.add_argument("--timing", choices=("rotate", "all"), default="rotate",
@@ -239,6 +252,8 @@ def main():
     from combine_get_dispatch_layout_amd import ep
 
     w = W.WORKLOADS[args.workload]
+    if args.num_sources > 1:
+        w = w.scaled(num_sources=args.num_sources)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     idx, wts = W.routing(w)
@@ -247,7 +262,7 @@ def main():
     cfg = ep.Config(hidden=H, num_topk=w.num_topk, num_experts=w.num_experts,
                     num_ranks=w.num_ranks, ranks_per_node=w.ranks_per_node,
                     expert_alignment=w.expert_alignment, quant=w.quant,
-                    quant_group=w.quant_group if w.quant else 0)
+                    quant_group=w.quant_group if w.quant else 0, num_sources=w.num_sources)
     cap = ep.ep_recv_capacity(cfg, N)
     rdt = {0: torch.bfloat16, 1: torch.uint8, 2: torch.int8}[w.quant]
     G = cfg.num_groups
@@ -281,49 +296,58 @@ def main():
     S = ep.ep_get_layout(sets[0]["h"], sets[0]["topk"], do_cpu_sync=True)["num_recv_slots"]
     nbytes = algorithmic_bytes(w, V, S)
     stream = torch.cuda.current_stream()
+    pl = args.pipeline
     # overlap: the layout of batch i+1 runs on a second stream while batch i
     # is dispatched and combined (double-batch overlap); default priority
-    lay_stream = torch.cuda.Stream() if args.pipeline == "overlap" else stream
+    lay_stream = torch.cuda.Stream() if pl == "overlap" else stream
+    stage_names = {"fused": ["layout_dispatch", "combine"], "cached": ["dispatch", "combine"]}.get(
+        pl, ["layout", "dispatch", "combine"])
+    stage_bytes = dict(nbytes, layout_dispatch=nbytes["layout"] + nbytes["dispatch"])
     for s in sets:
-        if fused:
-            first = ep.bind_layout_dispatch(s["h"], s["topk"], s["x"], s["recv"], s["scales"],
-                                            s["per_rank"], s["per_node"], s["per_expert"],
-                                            s["in_rank"], stream=stream)
+        calls = []   # (stage index, bound call) in issue order
+        if pl == "fused":
+            calls.append((0, ep.bind_layout_dispatch(s["h"], s["topk"], s["x"], s["recv"],
+                                                     s["scales"], s["per_rank"], s["per_node"],
+                                                     s["per_expert"], s["in_rank"],
+                                                     stream=stream)))
+        elif pl == "cached":
+            # the handle's layout is computed once and reused by every step
+            ep.ep_get_layout(s["h"], s["topk"], s["per_rank"], s["per_node"], s["per_expert"],
+                             s["in_rank"])
         else:
-            first = ep.bind_get_layout(s["h"], s["topk"], s["per_rank"], s["per_node"],
-                                       s["per_expert"], s["in_rank"], stream=lay_stream)
-        s["calls"] = (
-            [first],
-            [] if fused else
-            [ep.bind_dispatch(s["h"], s["x"], s["recv"], s["scales"], b, e, stream=stream)
-             for b, e in rounds],
-            [ep.bind_combine(s["h"], s["y"], s["wts"], s["out"], b, e, stream=stream)
-             for b, e in rounds])
+            calls.append((0, ep.bind_get_layout(s["h"], s["topk"], s["per_rank"], s["per_node"],
+                                                s["per_expert"], s["in_rank"],
+                                                stream=lay_stream)))
+        if pl != "fused":
+            calls += [(stage_names.index("dispatch"),
+                       ep.bind_dispatch(s["h"], s["x"], s["recv"], s["scales"], b, e,
+                                        stream=stream)) for b, e in rounds]
+        calls += [(stage_names.index("combine"),
+                   ep.bind_combine(s["h"], s["y"], s["wts"], s["out"], b, e, stream=stream))
+                  for b, e in rounds]
+        s["calls"] = calls
         s["lay_done"] = torch.cuda.Event()
         s["main_done"] = torch.cuda.Event()
         s["main_done"].record(stream)
 
-    nr = len(rounds)
-    nd = 0 if fused else nr     # dispatch calls per step
-    nstages = 2 if fused else 3
+    stage_of = [st for st, _ in sets[0]["calls"]]
+    nstages = len(stage_names)
     # one (start, stop) event pair per kernel call of every timed step
-    calls_per_step = 1 + nd + nr
+    calls_per_step = len(stage_of)
     hev = HipEvents(2 * calls_per_step * args.steps)
 
     def armed(i, j):
-        """Whether call j (0 layout, then dispatch rounds, then combine rounds)
-        of timed step i carries kernel events: every call of every step
-        ("all"), or, on every time_every-th step, one stage in turn."""
+        """Whether call j of timed step i carries kernel events: every call of
+        every step ("all"), or, on every time_every-th step, the calls of one
+        stage, the stages in turn."""
         if args.timing == "all":
             return True
         if i % args.time_every:
             return False
-        stage = 0 if j == 0 else (1 if j <= nd else 2)
-        if fused:
-            stage = min(stage, 1)
-        return stage == (i // args.time_every) % nstages
+        return stage_of[j] == (i // args.time_every) % nstages
 
-    def issue(c, i, j, base):
+    def issue(i, j, base):
+        c = sets[i % nsets]["calls"][j][1]
         if base is None or not armed(i, j):
             c()
         else:
@@ -331,33 +355,32 @@ def main():
 
     def layout(i, base):
         s = sets[i % nsets]
-        if lay_stream is not stream:
-            lay_stream.wait_event(s["main_done"])   # the set's previous batch is combined
-        issue(s["calls"][0][0], i, 0, base)
-        if lay_stream is not stream:
-            s["lay_done"].record(lay_stream)
+        lay_stream.wait_event(s["main_done"])   # the set's previous batch is combined
+        issue(i, 0, base)
+        s["lay_done"].record(lay_stream)
 
     def shuffle(i, base):
         s = sets[i % nsets]
-        if lay_stream is not stream:
-            stream.wait_event(s["lay_done"])
-        for j, c in enumerate(s["calls"][1] + s["calls"][2]):
-            issue(c, i, 1 + j, base)
-        if lay_stream is not stream:
-            s["main_done"].record(stream)
+        stream.wait_event(s["lay_done"])
+        for j in range(1, calls_per_step):
+            issue(i, j, base)
+        s["main_done"].record(stream)
 
     def run(n, timed):
         """n steps; with overlap the layout of step i+1 is issued before the
-        dispatch and combine of step i."""
+        dispatch and combine of step i, otherwise each step's calls in order."""
         def base(i):
             return 2 * calls_per_step * i if timed else None
-        layout(0, base(0))
-        for i in range(n):
-            if lay_stream is not stream and i + 1 < n:
-                layout(i + 1, base(i + 1))
-            shuffle(i, base(i))
-            if lay_stream is stream and i + 1 < n:
-                layout(i + 1, base(i + 1))
+        if pl == "overlap":
+            layout(0, base(0))
+            for i in range(n):
+                if i + 1 < n:
+                    layout(i + 1, base(i + 1))
+                shuffle(i, base(i))
+        else:
+            for i in range(n):
+                for j in range(calls_per_step):
+                    issue(i, j, base(i))
 
     run(args.warmup, False)
     torch.cuda.synchronize()
@@ -372,28 +395,21 @@ def main():
         return np.array([hev.ms(2 * calls_per_step * i + 2 * j, 2 * calls_per_step * i + 2 * j + 1)
                          for i in range(args.steps) if armed(i, j)]) * 1e-3
 
-    lay = durs(0)
-    dis = sum(durs(1 + r) for r in range(nd)) if nd else None
-    com = sum(durs(1 + nd + r) for r in range(nr))
+    # per stage: per-step durations (sum over the stage's launches), bytes, launches
+    per_stage = {}
+    for st, name in enumerate(stage_names):
+        js = [j for j in range(calls_per_step) if stage_of[j] == st]
+        per_stage[name] = (sum(durs(j) for j in js), stage_bytes[name], len(js))
     hev.close()
     ms_per_step = wall / args.steps * 1e3
     value = N * args.steps / wall
-    # per-launch means (one dispatch/combine launch per round)
-    if fused:
-        stages = dict(layout_dispatch=(float(np.mean(lay)), nbytes["layout"] + nbytes["dispatch"],
-                                       1),
-                      combine=(float(np.mean(com)), nbytes["combine"], nr))
-        t_dc = float(np.mean(lay) + np.mean(com))
-        dom = max(("layout_dispatch", "combine"), key=lambda k: stages[k][0])
-    else:
-        stages = dict(layout=(float(np.mean(lay)), nbytes["layout"], 1),
-                      dispatch=(float(np.mean(dis)), nbytes["dispatch"], nr),
-                      combine=(float(np.mean(com)), nbytes["combine"], nr))
-        t_dc = float(np.mean(dis) + np.mean(com))
-        dom = max(("dispatch", "combine"), key=lambda k: stages[k][0])
+    stages = {k: (float(np.mean(d)), by, n) for k, (d, by, n) in per_stage.items()}
+    moving = [k for k in stage_names if k != "layout"]   # the dispatch + combine stages
+    t_dc = sum(stages[k][0] for k in moving)
+    dom = max(moving, key=lambda k: stages[k][0])
     t_dom, b_dom, launches = stages[dom]
     achieved = b_dom / t_dom / 1e9   # = per-launch bytes / mean per-launch time
-    b_dc = nbytes["dispatch"] + nbytes["combine"] + (nbytes["layout"] if fused else 0)
+    b_dc = sum(stages[k][1] for k in moving)
     traffic = traffic_from_profiles(dom, w.name)
 
     # achievable reference: a plain 1 GiB device copy
@@ -421,21 +437,22 @@ def main():
         "config": {"workload": w.name, "num_tokens": N, "hidden": H,
                    "num_experts": w.num_experts, "num_ranks": w.num_ranks,
                    "num_topk": w.num_topk, "expert_alignment": w.expert_alignment,
-                   "rounds": len(rounds), "buffer_sets": nsets},
+                   "rounds": len(rounds), "num_sources": w.num_sources, "buffer_sets": nsets},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": b_dom / launches,
                      "launches_per_step": launches},
         "stages_us": {k: v[0] * 1e6 for k, v in stages.items()},
+        "stages_us_p10_p50_p90": {k: [float(np.percentile(d, q)) * 1e6 for q in (10, 50, 90)]
+                                  for k, (d, _, _) in per_stage.items()},
         "stages_GBps": {k: v[1] / v[0] / 1e9 for k, v in stages.items()},
-        ("layout_dispatch_combine" if fused else "dispatch_combine"): {
-                             "tokens_per_s": N / t_dc,
+        "+".join(moving): {"tokens_per_s": N / t_dc,
                              "GBps": b_dc / t_dc / 1e9,
                              "frac_of_peak": b_dc / t_dc / 1e9 / HBM_PEAK_GBS},
         "device_copy_GBps": copy_gbs,
         "pipeline": args.pipeline,
         "timing": {"mode": args.timing, "every": args.time_every, "host_enqueue_ms_per_step": t_enqueue / args.steps * 1e3,
-                   "samples_per_stage": [int(len(x)) for x in (lay, dis, com) if x is not None]},
+                   "samples_per_stage": {k: int(len(d)) for k, (d, _, _) in per_stage.items()}},
         "recv_rows": S, "valid_pairs": V,
     }
     if not args.no_cpu_baseline:

@@ -44,8 +44,10 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 struct Carve {
     int64_t ctrl, psum_expert, psum_rank, num_unaligned, recv_list, topk, slot, meta, hist,
-        acc, total;
+        acc, src_acc, src_base, src_psum, total;
 };
+
+int num_sources(const ep_config& c) { return c.num_sources > 1 ? c.num_sources : 1; }
 
 int num_nodes(const ep_config& c)
 {
@@ -83,6 +85,9 @@ ep_status check_config(const ep_config* c)
                        c->expert_alignment);
     if ((int64_t)c->num_experts * c->expert_capacity >= (int64_t)1 << 31)
         return EP_FAIL(EP_ERR_INVALID_ARG, "num_experts * expert_capacity exceeds 2^31 - 1");
+    if (c->num_sources < 0 || c->num_sources > epk::kMaxSources)
+        return EP_FAIL(EP_ERR_INVALID_ARG, "num_sources=%d outside [0,%d]", c->num_sources,
+                       epk::kMaxSources);
     if (c->quant != EP_QUANT_NONE && c->quant != EP_QUANT_FP8_E4M3 && c->quant != EP_QUANT_INT8)
         return EP_FAIL(EP_ERR_INVALID_ARG, "quant=%d unknown", c->quant);
     if (c->quant != EP_QUANT_NONE) {
@@ -129,6 +134,14 @@ ep_status carve(const ep_config& c, int64_t max_tokens, Carve* o)
     o->meta = take(8 * slots);
     o->hist = take(4 * Cc * c.num_experts);
     o->acc = take(4 * (int64_t)(c.num_ranks + num_nodes(c)));
+    const int64_t P = num_sources(c);
+    if (P > 1) {
+        o->src_acc = take(4 * P * (c.num_experts + c.num_ranks));
+        o->src_base = take(4 * P * c.num_experts);
+        o->src_psum = take(4 * (int64_t)c.num_ranks * (P + 1));
+    } else {
+        o->src_acc = o->src_base = o->src_psum = -1;
+    }
     o->total = off;
     return EP_OK;
 }
@@ -176,6 +189,9 @@ ep_status layout_args(ep_handle* h, const int32_t* d_topk_idx, int64_t num_token
     if (d_num_tokens_per_rdma_rank && h->nodes == 0)
         return EP_FAIL(EP_ERR_INVALID_ARG, "num_tokens_per_rdma_rank needs ranks_per_node > 0");
     const ep_config& c = h->cfg;
+    if (num_tokens % num_sources(c) != 0)
+        return EP_FAIL(EP_ERR_INVALID_ARG, "num_tokens=%lld is not a multiple of num_sources=%d",
+                       (long long)num_tokens, num_sources(c));
     epk::LayoutArgs& a = *out;
     a.topk = d_topk_idx;
     a.num_tokens = num_tokens;
@@ -246,6 +262,30 @@ ep_status dispatch_args(const ep_handle* h, int64_t num_tokens, const void* d_x,
     return EP_OK;
 }
 
+// Layout kernels, preceded with several sources by the per-source counts;
+// `ev` spans all of them.
+hipError_t launch_layout_all(const ep_handle* h, const epk::LayoutArgs& a, hipStream_t s,
+                             epk::LaunchEvents ev)
+{
+    const int P = num_sources(h->cfg);
+    if (P == 1) return epk::launch_layout(a, s, ev);
+    epk::SourceArgs sa;
+    sa.topk = a.topk;
+    sa.tokens_per_source = a.num_tokens / P;
+    sa.K = a.K;
+    sa.E = a.E;
+    sa.R = a.R;
+    sa.nle = a.nle;
+    sa.P = P;
+    sa.acc_expert = h->at<int32_t>(h->cv.src_acc);
+    sa.acc_rank = sa.acc_expert + (int64_t)P * a.E;
+    sa.expert_source_base = h->at<int32_t>(h->cv.src_base);
+    sa.psum_source_rank = h->at<int32_t>(h->cv.src_psum);
+    hipError_t e = epk::launch_sources(sa, s, epk::LaunchEvents{ev.start, nullptr});
+    if (e != hipSuccess) return e;
+    return epk::launch_layout(a, s, epk::LaunchEvents{nullptr, ev.stop});
+}
+
 }  // namespace
 
 extern "C" {
@@ -303,6 +343,10 @@ ep_status ep_handle_init(const ep_config* cfg, int64_t max_tokens, void* d_works
     if (e == hipSuccess)
         e = epk::launch_clear(h->at<uint32_t>(cv.acc), cfg->num_ranks + h->nodes,
                               static_cast<hipStream_t>(stream));
+    if (e == hipSuccess && cv.src_acc >= 0)
+        e = epk::launch_clear(h->at<uint32_t>(cv.src_acc),
+                              num_sources(*cfg) * (cfg->num_experts + cfg->num_ranks),
+                              static_cast<hipStream_t>(stream));
     if (e != hipSuccess) {
         delete h;
         return EP_FAIL(EP_ERR_HIP, "clearing the control words: %s", hipGetErrorString(e));
@@ -325,7 +369,7 @@ ep_status ep_get_layout(ep_handle* h, const int32_t* d_topk_idx, int64_t num_tok
                                d_is_token_in_rank, &a);
     if (st != EP_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    EP_HIP(epk::launch_layout(a, s, h->take_events()));
+    EP_HIP(launch_layout_all(h, a, s, h->take_events()));
     h->num_tokens = num_tokens;
     h->host_slots = -1;
     if (do_cpu_sync) {
@@ -375,10 +419,10 @@ ep_status ep_layout_dispatch(ep_handle* h, const int32_t* d_topk_idx, int64_t nu
     if (st != EP_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const epk::LaunchEvents ev = h->take_events();
-    if (epk::route_dispatch_fits(la)) {
+    if (num_sources(h->cfg) == 1 && epk::route_dispatch_fits(la)) {
         EP_HIP(epk::launch_route_dispatch(la, da, s, ev));
     } else {
-        EP_HIP(epk::launch_layout(la, s, epk::LaunchEvents{ev.start, nullptr}));
+        EP_HIP(launch_layout_all(h, la, s, epk::LaunchEvents{ev.start, nullptr}));
         EP_HIP(epk::launch_dispatch(da, s, epk::LaunchEvents{nullptr, ev.stop}));
     }
     h->num_tokens = num_tokens;
@@ -440,6 +484,9 @@ ep_status ep_handle_get_view(const ep_handle* h, ep_handle_view* v)
     v->max_tokens = h->max_tokens;
     v->max_slots = h->max_slots;
     v->num_recv_slots = h->host_slots;
+    v->num_sources = num_sources(h->cfg);
+    v->psum_source_rank = h->cv.src_psum >= 0 ? h->at<int32_t>(h->cv.src_psum) : nullptr;
+    v->expert_source_base = h->cv.src_base >= 0 ? h->at<int32_t>(h->cv.src_base) : nullptr;
     return EP_OK;
 }
 

@@ -1,5 +1,6 @@
 // Internal interface between the C-ABI host runtime (api.cpp) and the HIP
-// kernels (layout.hip, dispatch.hip, combine.hip).  gfx950 only.
+// kernels (layout.hip, dispatch.hip, fused.hip, sources.hip, combine.hip).
+// gfx950 only.
 #pragma once
 
 #include <hip/hip_ext.h>
@@ -12,6 +13,7 @@ constexpr int kWave = 64;
 constexpr int kMaxTopk = 16;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxRanks = 1024;
+constexpr int kMaxSources = 1024;
 // Tokens per layout block: 4 waves, one token per lane.
 constexpr int kLayoutBlock = 256;
 // Largest row, in 16-byte vectors, that one wave can hold for a whole-row
@@ -73,6 +75,17 @@ struct DispatchArgs {
     uint32_t* flags;
 };
 
+// Per-source counts of a batch of P stacked source ranks.
+struct SourceArgs {
+    const int32_t* topk;        // [P*Ns, K]
+    int64_t tokens_per_source;  // Ns
+    int K, E, R, nle, P;
+    int32_t* acc_expert;        // [P][E] accumulators, zero between calls
+    int32_t* acc_rank;          // [P][R] likewise
+    int32_t* expert_source_base;  // [P][E]
+    int32_t* psum_source_rank;    // [R][P+1]
+};
+
 struct CombineArgs {
     const void* y;              // bf16 [y_rows,H]
     int64_t y_rows;
@@ -114,6 +127,7 @@ hipError_t launch_clear(uint32_t* words, int n, hipStream_t s);
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t s, LaunchEvents ev = {});
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s, LaunchEvents ev = {});
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s, LaunchEvents ev = {});
+hipError_t launch_sources(const SourceArgs& a, hipStream_t s, LaunchEvents ev = {});
 // Layout + dispatch of the whole batch in one launch (small batches).
 bool route_dispatch_fits(const LayoutArgs& la);
 hipError_t launch_route_dispatch(const LayoutArgs& la, const DispatchArgs& da, hipStream_t s,

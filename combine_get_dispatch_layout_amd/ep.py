@@ -31,7 +31,8 @@ class ep_config(ctypes.Structure):
                 ("num_experts", ctypes.c_int32), ("num_ranks", ctypes.c_int32),
                 ("ranks_per_node", ctypes.c_int32), ("expert_alignment", ctypes.c_int32),
                 ("quant", ctypes.c_int32), ("quant_group", ctypes.c_int32),
-                ("counts_as_prefix", ctypes.c_int32), ("expert_capacity", ctypes.c_int32)]
+                ("counts_as_prefix", ctypes.c_int32), ("expert_capacity", ctypes.c_int32),
+                ("num_sources", ctypes.c_int32)]
 
 
 class ep_handle_view(ctypes.Structure):
@@ -39,7 +40,9 @@ class ep_handle_view(ctypes.Structure):
                 ("num_unaligned", ctypes.c_void_p), ("slot_idx", ctypes.c_void_p),
                 ("src_meta", ctypes.c_void_p), ("topk_idx", ctypes.c_void_p),
                 ("num_tokens", ctypes.c_int64), ("max_tokens", ctypes.c_int64),
-                ("max_slots", ctypes.c_int64), ("num_recv_slots", ctypes.c_int64)]
+                ("max_slots", ctypes.c_int64), ("num_recv_slots", ctypes.c_int64),
+                ("num_sources", ctypes.c_int64), ("psum_source_rank", ctypes.c_void_p),
+                ("expert_source_base", ctypes.c_void_p)]
 
 
 class EpError(RuntimeError):
@@ -118,11 +121,12 @@ class Config:
     quant_group: int = 0
     counts_as_prefix: bool = False
     expert_capacity: int = 0
+    num_sources: int = 1
 
     def c(self):
         return ep_config(self.hidden, self.num_topk, self.num_experts, self.num_ranks,
                          self.ranks_per_node, self.expert_alignment, self.quant, self.quant_group,
-                         int(bool(self.counts_as_prefix)), self.expert_capacity)
+                         int(bool(self.counts_as_prefix)), self.expert_capacity, self.num_sources)
 
     @property
     def num_nodes(self):
@@ -324,7 +328,15 @@ def ep_handle_get_view(h: Handle):
         return ws[off:off + 4 * n].view(torch.int32)
 
     N = max(v.num_tokens, 0)
-    return dict(psum_expert=arr(v.psum_expert, cfg.num_experts + 1),
+    P = v.num_sources
+    src = {}
+    if v.psum_source_rank:
+        src = dict(psum_source_rank=arr(v.psum_source_rank,
+                                        cfg.num_ranks * (P + 1)).view(cfg.num_ranks, P + 1),
+                   expert_source_base=arr(v.expert_source_base,
+                                          P * cfg.num_experts).view(P, cfg.num_experts))
+    return dict(**src, num_sources=P,
+                psum_expert=arr(v.psum_expert, cfg.num_experts + 1),
                 psum_rank=arr(v.psum_rank, cfg.num_ranks + 1),
                 num_unaligned=arr(v.num_unaligned, cfg.num_experts),
                 slot_idx=arr(v.slot_idx, N * cfg.num_topk).view(N, cfg.num_topk),

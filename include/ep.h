@@ -91,6 +91,14 @@ typedef struct ep_config {
                                   and flagged EP_FLAG_RECV_CAPACITY.  Needs
                                   expert_alignment == 1.  The host list then
                                   holds the filled rows min(count, cap).       */
+    int32_t num_sources;       /* P: 0 or 1 = one source rank.  P > 1: the batch
+                                  stacks P simulated source ranks, source p
+                                  owning tokens [p*N/P, (p+1)*N/P) (N must be a
+                                  multiple of P; P <= 1024).  Receive rows then
+                                  follow (source, token, k) order, and the
+                                  handle also holds the per-source arrays of
+                                  ep_handle_view ([P3] §3.1
+                                  psum_num_recv_tokens_per_scaleup_rank).      */
 } ep_config;
 
 typedef struct ep_handle ep_handle;
@@ -112,6 +120,15 @@ typedef struct ep_handle_view {
     int64_t max_slots;             /* receive rows that can ever be needed:
                                       max_tokens*K + E*(A-1), or E*capacity      */
     int64_t num_recv_slots;        /* S if known on the host (do_cpu_sync), else -1 */
+    int64_t num_sources;           /* P (1 for a single source)                  */
+    const int32_t* psum_source_rank;   /* [R, P+1] (P > 1, else NULL): for
+                                      receiving rank r, tokens received from the
+                                      sources before p, a token counted once per
+                                      rank it has an expert on; [r][P] equals
+                                      num_tokens_per_rank[r]                      */
+    const int32_t* expert_source_base; /* [P, E] (P > 1, else NULL): pairs of
+                                      expert e from the sources before p; source
+                                      p's rows of e start at psum_expert[e] + this */
 } ep_handle_view;
 
 /* Bytes of device workspace a handle needs for up to max_tokens tokens.
@@ -136,15 +153,17 @@ void ep_handle_free(ep_handle* h);
 
 /* a1 + a2: routing layout and slot assignment ([P3] §2.1, §3.1, §8.4).
  *   d_topk_idx: int32 [num_tokens, K]; -1 = masked entry; 0 <= num_tokens <=
- *   max_tokens.  Outputs (each may be NULL to skip it):
+ *   max_tokens, a multiple of num_sources when that is above 1.  Outputs
+ *   (each may be NULL to skip it):
  *     d_num_tokens_per_rank     int32 [R]  distinct tokens with an expert on r
  *     d_num_tokens_per_rdma_rank int32 [ceil(R/ranks_per_node)] distinct tokens
  *                                per node (needs ranks_per_node > 0)
  *     d_num_tokens_per_expert   int32 [E]  (t,k) pairs routed to e
  *     d_is_token_in_rank        uint8 [num_tokens, R] 0/1
  *   The handle receives psum_expert, psum_rank, num_unaligned, slot_idx,
- *   src_meta and the topk clone.  Slot order inside an expert segment is
- *   (token, k) ascending, padding rows last: one deterministic result.
+ *   src_meta and the topk clone (and, with several sources, the per-source
+ *   arrays).  Slot order inside an expert segment is (token, k) ascending,
+ *   padding rows last: one deterministic result.
  *   do_cpu_sync != 0: waits for the stream and writes, when non-NULL,
  *     h_num_recv_tokens_per_expert [E] (aligned counts, or per-rank inclusive
  *     prefix if counts_as_prefix) and *h_num_recv_slots = S. */
@@ -179,9 +198,9 @@ ep_status ep_dispatch(const ep_handle* h, const void* d_x, int64_t token_begin, 
  *   num_tokens, d_recv_x, d_recv_scales, recv_capacity_rows): every argument
  *   has the meaning, layout and checks given there, and the handle is left
  *   in the same state (num_recv_slots unknown on the host).
- *   For num_tokens <= 256 and num_topk <= 8 (when the routing of the whole
- *   batch fits one workgroup's LDS) this is a single kernel launch; otherwise
- *   it launches the layout kernels and then the dispatch kernel.
+ *   For num_tokens <= 256, num_topk <= 8 and one source (when the routing of
+ *   the whole batch fits one workgroup's LDS) this is a single kernel launch;
+ *   otherwise it launches the layout kernels and then the dispatch kernel.
  *   Receive rows beyond recv_capacity_rows are skipped and flagged on the
  *   device (ep_check_error); size recv_x with ep_recv_capacity to avoid it. */
 ep_status ep_layout_dispatch(ep_handle* h, const int32_t* d_topk_idx, int64_t num_tokens,

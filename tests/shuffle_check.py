@@ -29,7 +29,8 @@ def config_of(w: W.Workload, counts_as_prefix=False):
                      num_ranks=w.num_ranks, ranks_per_node=w.ranks_per_node,
                      expert_alignment=w.expert_alignment, quant=w.quant,
                      quant_group=w.quant_group if w.quant else 0,
-                     counts_as_prefix=counts_as_prefix, expert_capacity=w.expert_capacity)
+                     counts_as_prefix=counts_as_prefix, expert_capacity=w.expert_capacity,
+                     num_sources=w.num_sources)
 
 
 def oracle_slots(w: W.Workload, idx):
@@ -114,6 +115,14 @@ def compare_layout(run: GpuRun, idx, ref_lay, ref_slots, host_sync=True):
     assert np.array_equal(v["slot_idx"].cpu().numpy(), ref_slots["slot_idx"])
     assert np.array_equal(v["src_meta"][:S].cpu().numpy(), ref_slots["src_meta"])
     assert np.array_equal(v["topk_idx"].cpu().numpy(), idx)
+    assert v["num_sources"] == max(w.num_sources, 1)
+    if w.num_sources > 1:
+        ref_src = oracle.source_counts(idx, w.num_experts, w.num_ranks, w.num_sources)
+        assert np.array_equal(v["psum_source_rank"].cpu().numpy(), ref_src["psum_source_rank"])
+        assert np.array_equal(v["expert_source_base"].cpu().numpy(),
+                              ref_src["expert_source_base"])
+    else:
+        assert "psum_source_rank" not in v
     if host_sync:
         assert lay["num_recv_tokens_per_expert_list"] == expected_host_list(w, ref_slots)
 

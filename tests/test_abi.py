@@ -43,7 +43,8 @@ GOOD = dict(hidden=2048, num_topk=8, num_experts=128, num_ranks=16)
     dict(num_experts=0), dict(num_experts=1025), dict(num_ranks=0), dict(num_ranks=3),
     dict(num_ranks=2048, num_experts=1024), dict(ranks_per_node=-1), dict(expert_alignment=0),
     dict(quant=3), dict(quant=1, quant_group=64), dict(quant=2, quant_group=128, hidden=2056),
-    dict(quant=2, quant_group=16384, hidden=16384),
+    dict(quant=2, quant_group=16384, hidden=16384), dict(num_sources=-1),
+    dict(num_sources=1025),
 ])
 def test_invalid_configs_rejected(bad):
     cfg = ep.Config(**{**GOOD, **bad})
@@ -64,6 +65,14 @@ def test_workspace_and_capacity_sizes():
         ep.ep_workspace_size(cfg, -1)
     with pytest.raises(ep.EpError):
         ep.ep_workspace_size(cfg, 1 << 29)      # receive rows beyond 2^31
+
+
+def test_workspace_grows_with_sources():
+    one = ep.ep_workspace_size(ep.Config(**GOOD), 4096)
+    p16 = ep.ep_workspace_size(ep.Config(**GOOD, num_sources=16), 4096)
+    # accumulators [P, E+R], bases [P, E], prefix [R, P+1], each 256-byte aligned
+    assert p16 - one >= 4 * (16 * (128 + 16) + 16 * 128 + 16 * 17)
+    assert ep.ep_workspace_size(ep.Config(**GOOD, num_sources=1), 4096) == one
 
 
 def _init(cfg, max_tokens, ptr, nbytes):

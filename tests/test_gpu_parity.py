@@ -343,3 +343,54 @@ def test_layout_dispatch_empty_batch():
     v = ep.ep_handle_get_view(h)
     assert v["psum_expert"].cpu().tolist() == [0] * 17
     assert ep.ep_check_error(h) == (ep.EP_OK, 0)
+
+
+# Several source ranks stacked in one batch: receive rows in (source, token,
+# k) order and the per-source arrays, through every layout path.
+@pytest.mark.parametrize("args", [
+    dict(N=256, H=64, E=64, R=8, K=8, P=4),                         # one block
+    dict(N=2048, H=7168, E=256, R=16, K=8, P=16, quant=W.QUANT_FP8, group=128),  # EP16 decode
+    dict(N=3000, H=128, E=128, R=16, K=6, P=3, A=4, mask=0.1),      # count + finish
+    dict(N=9000, H=64, E=256, R=32, K=8, P=9, A=8),                 # count + scan + slots
+    dict(N=1024, H=32, E=64, R=8, K=2, P=1024),                     # one token per source
+    dict(N=600, H=256, E=32, R=4, K=4, P=6, cap=100),               # fixed capacity
+])
+def test_multi_source(args):
+    args = dict(args)
+    P = args.pop("P")
+    w = _custom(**args).scaled(num_sources=P)
+    _say(f"[parity] multi source P={P} {args}")
+    run_and_check(w)
+
+
+def test_multi_source_one_call_and_repeat():
+    """The one-call form with several sources, twice on the same handle with
+    new routing: the per-source accumulators start from zero each call."""
+    w = _custom(N=512, H=512, E=64, R=8, K=8).scaled(num_sources=8)
+    _say("[parity] multi source one call")
+    st = run_and_check(w, fused=True)
+    run = st["run"]
+    w2 = w.scaled(seed=99)
+    idx2, _ = W.routing(w2)
+    run.topk.copy_(torch.from_numpy(idx2))
+    run.layout_dispatch()
+    ref = oracle.source_counts(idx2, w.num_experts, w.num_ranks, 8)
+    v = ep.ep_handle_get_view(run.h)
+    assert np.array_equal(v["psum_source_rank"].cpu().numpy(), ref["psum_source_rank"])
+    assert np.array_equal(v["expert_source_base"].cpu().numpy(), ref["expert_source_base"])
+    assert ep.ep_check_error(run.h) == (ep.EP_OK, 0)
+
+
+def test_multi_source_empty_and_uneven():
+    cfg = ep.Config(64, 2, 16, 4, num_sources=4)
+    h = ep.ep_handle_init(cfg, 64)
+    lay = ep.ep_get_layout(h, torch.empty((0, 2), dtype=torch.int32, device="cuda"),
+                           do_cpu_sync=True)
+    assert lay["num_recv_slots"] == 0
+    v = ep.ep_handle_get_view(h)
+    assert v["psum_source_rank"].abs().sum().item() == 0
+    assert v["expert_source_base"].abs().sum().item() == 0
+    with pytest.raises(ep.EpError) as ei:
+        ep.ep_get_layout(h, torch.zeros((6, 2), dtype=torch.int32, device="cuda"))
+    assert ei.value.status == ep.EP_ERR_INVALID_ARG
+    assert ep.ep_check_error(h) == (ep.EP_OK, 0)

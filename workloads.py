@@ -39,6 +39,7 @@ class Workload:
     seed: int = 0
     ranks_per_node: int = 8
     expert_capacity: int = 0      # >0: fixed-capacity receive layout
+    num_sources: int = 1          # >1: the batch stacks this many source ranks
 
     def scaled(self, **kw) -> "Workload":
         return replace(self, **kw)
