@@ -36,8 +36,16 @@ def lib():
         L.orc_source_counts.restype = i32
         L.orc_recv_list.argtypes = [P, i32, i32, i32, P]
         L.orc_recv_list.restype = None
-        L.orc_dispatch.argtypes = [P, i64, i32, P, i32, i32, i32, i64, i64, P, P]
+        L.orc_dispatch.argtypes = [P, i64, i32, P, i32, i32, i32, i32, i64, i64, P, P]
         L.orc_dispatch.restype = None
+        L.orc_combine_q.argtypes = [P, P, i32, i32, P, P, i64, i32, i32, i64, i64, P]
+        L.orc_combine_q.restype = None
+        L.orc_e2m1_from_f32.argtypes = [ctypes.c_float]
+        L.orc_e2m1_from_f32.restype = ctypes.c_uint8
+        L.orc_f32_from_e2m1.argtypes = [ctypes.c_uint8]
+        L.orc_f32_from_e2m1.restype = ctypes.c_float
+        L.orc_f32_from_e8m0.argtypes = [ctypes.c_uint8]
+        L.orc_f32_from_e8m0.restype = ctypes.c_float
         L.orc_combine.argtypes = [P, P, P, i64, i32, i32, i64, i64, P]
         L.orc_combine.restype = None
         for name in ("orc_bf16_from_f32_n", "orc_bf16_from_f64_n", "orc_e4m3fn_from_f32_n",
@@ -182,12 +190,35 @@ def recv_list(psum_expert, num_experts, num_ranks, counts_as_prefix):
     return out
 
 
-QUANT_NONE, QUANT_FP8, QUANT_INT8 = 0, 1, 2
+QUANT_NONE, QUANT_FP8, QUANT_INT8, QUANT_MXFP4 = 0, 1, 2, 3
+SCALE_FP32, SCALE_POW2, SCALE_UE8M0 = 0, 1, 2
+
+
+def e2m1_from_f32(v):
+    return np.array([lib().orc_e2m1_from_f32(float(a)) for a in np.ravel(v)], np.uint8)
+
+
+def f32_from_e2m1(c):
+    return np.array([lib().orc_f32_from_e2m1(int(a)) for a in np.ravel(c)], np.float32)
+
+
+def f32_from_e8m0(b):
+    return np.array([lib().orc_f32_from_e8m0(int(a)) for a in np.ravel(b)], np.float32)
+
+
+def row_bytes(H, quant):
+    return 2 * H if quant == QUANT_NONE else (H // 2 if quant == QUANT_MXFP4 else H)
+
+
+def scale_dtype(quant, scale_mode):
+    return np.uint8 if quant == QUANT_MXFP4 or scale_mode == SCALE_UE8M0 else np.float32
 
 
 def dispatch(x_bits, slot_idx, num_rows, quant=QUANT_NONE, group=None, t_begin=0, t_end=None,
-             recv_x=None, recv_scales=None):
-    """a3. x_bits: uint16 [N,H] bf16 bit patterns.  Returns (recv_x, recv_scales)."""
+             recv_x=None, recv_scales=None, scale_mode=SCALE_FP32):
+    """a3. x_bits: uint16 [N,H] bf16 bit patterns.  Returns (recv_x, recv_scales):
+    bf16 bits, or code bytes [rows, H] (FP8 / int8) or [rows, H/2] (MXFP4); scales
+    fp32 or E8M0 bytes [rows, G]."""
     x = _c(x_bits, np.uint16)
     sl = _c(slot_idx, np.int32)
     N, H = x.shape
@@ -197,18 +228,43 @@ def dispatch(x_bits, slot_idx, num_rows, quant=QUANT_NONE, group=None, t_begin=0
         group = H
         if recv_x is None:
             recv_x = np.zeros((num_rows, H), np.uint16)
-        G = 1
     else:
-        group = H if group is None else group
+        group = 32 if quant == QUANT_MXFP4 else (H if group is None else group)
         G = H // group
         if recv_x is None:
-            recv_x = np.zeros((num_rows, H), np.uint8 if quant == QUANT_FP8 else np.int8)
+            cdt = np.int8 if quant == QUANT_INT8 else np.uint8
+            recv_x = np.zeros((num_rows, row_bytes(H, quant)), cdt)
         if recv_scales is None:
-            recv_scales = np.zeros((num_rows, G), np.float32)
+            recv_scales = np.zeros((num_rows, G), scale_dtype(quant, scale_mode))
     assert recv_x.flags.c_contiguous
-    lib().orc_dispatch(_p(x), N, H, _p(sl), K, quant, group, t_begin, t_end, _p(recv_x),
-                       _p(recv_scales))
+    lib().orc_dispatch(_p(x), N, H, _p(sl), K, quant, group, scale_mode, t_begin, t_end,
+                       _p(recv_x), _p(recv_scales))
     return recv_x, recv_scales
+
+
+def quantize_rows(x_bits, quant, group=None, scale_mode=SCALE_FP32):
+    """Quantises every row on its own (dispatch with row t sent to receive row t)."""
+    x = _c(x_bits, np.uint16)
+    ident = np.arange(x.shape[0], dtype=np.int32)[:, None]
+    return dispatch(x, ident, x.shape[0], quant=quant, group=group, scale_mode=scale_mode)
+
+
+def combine_q(y_codes, y_scales, quant, group, topk_weights, slot_idx, t_begin=0, t_end=None,
+              out=None):
+    """a4 over quantised expert outputs: y_codes [S,H] (E4M3FN bytes or int8),
+    y_scales fp32 [S, H/group].  Returns uint16 bf16 bits [N,H]."""
+    yc = _c(y_codes, np.uint8 if quant == QUANT_FP8 else np.int8)
+    ys = _c(y_scales, np.float32)
+    w = _c(topk_weights, np.float32)
+    sl = _c(slot_idx, np.int32)
+    N, K = sl.shape
+    H = yc.shape[1]
+    t_end = N if t_end is None else t_end
+    if out is None:
+        out = np.zeros((N, H), np.uint16)
+    lib().orc_combine_q(_p(yc), _p(ys), quant, group, _p(w), _p(sl), N, K, H, t_begin, t_end,
+                        _p(out))
+    return out
 
 
 def combine(y_bits, topk_weights, slot_idx, t_begin=0, t_end=None, out=None):

@@ -89,6 +89,40 @@ float orc_f32_from_e4m3fn(uint8_t b)
     return (float)(s ? -a : a);
 }
 
+/* OCP FP4 E2M1 (OCP Microscaling Formats v1.0; the element type of MXFP4,
+ * which "DeepEP 通信库使用指南（v2.1）" §1.3.3 names with its group of 32):
+ * 1 sign, 2 exponent bits with bias 1, 1 mantissa bit: magnitudes 0, 0.5, 1,
+ * 1.5, 2, 3, 4, 6.  Nearest, ties to even; |v| beyond 6 saturates to 6.
+ * Returns the 4-bit code (sign in bit 3). */
+uint8_t orc_e2m1_from_f32(float v)
+{
+    double r = round_to_format((double)v, 2, 0);
+    uint8_t sign = signbit(r) ? 0x8 : 0x0;
+    double a = fabs(r);
+    if (a > 6.0) a = 6.0;
+    if (a == 0.0) return sign;
+    if (a < 1.0) return (uint8_t)(sign | 1);    /* subnormal 0.5 */
+    int e2;
+    frexp(a, &e2);
+    int ex = e2 - 1;                            /* 0 .. 2 */
+    int m = (int)((a / ldexp(1.0, ex) - 1.0) * 2.0);
+    return (uint8_t)(sign | ((ex + 1) << 1) | m);
+}
+
+float orc_f32_from_e2m1(uint8_t code)
+{
+    int s = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+    double a = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return (float)(s ? -a : a);
+}
+
+/* E8M0 (OCP MX scale type): the byte b stands for 2^(b - 127); 0xFF is NaN. */
+float orc_f32_from_e8m0(uint8_t b)
+{
+    if (b == 0xFF) return NAN;
+    return (float)ldexp(1.0, (int)b - 127);
+}
+
 /* Array forms for tests. */
 void orc_bf16_from_f32_n(const float* in, uint16_t* out, int64_t n)
 {
@@ -323,16 +357,45 @@ void orc_recv_list(const int32_t* psum_expert, int E, int R, int counts_as_prefi
  * not the arithmetic): amax = max |x| over the group, floored at 1e-4;
  * scale = amax / qmax in fp32 with qmax = 448 (E4M3FN) or 127 (int8);
  * code = x / scale in fp32, rounded to nearest-even into the format
- * (E4M3FN saturating; int8 clamped to [-127, 127]). */
-static float group_scale(const uint16_t* xg, int len, float qmax)
+ * (E4M3FN saturating; int8 clamped to [-127, 127]).
+ *
+ * Scale modes ("DeepEP 通信库使用指南（v2.1）" §1.3.1 API: round_scale,
+ * use_ue8m0 -- named, not defined).  Readings: round_scale replaces the fp32
+ * quotient amax / qmax by the smallest power of two not below it (so no
+ * code saturates), and use_ue8m0 stores that power of two as one E8M0 byte
+ * (its biased exponent) instead of an fp32 word. */
+static float group_amax(const uint16_t* xg, int len)
 {
     float amax = 0.0f;
     for (int i = 0; i < len; ++i) {
         float a = fabsf(orc_f32_from_bf16(xg[i]));
         if (a > amax) amax = a;
     }
+    return amax;
+}
+
+/* Smallest power of two >= s (s > 0, normal). */
+static float pow2_ceil(float s)
+{
+    int e;
+    double m = frexp((double)s, &e);        /* s = m * 2^e, m in [0.5, 1) */
+    return (float)ldexp(1.0, m == 0.5 ? e - 1 : e);
+}
+
+/* Biased exponent of a power of two: 2^k -> k + 127. */
+static uint8_t e8m0_of_pow2(float s)
+{
+    int e;
+    frexp((double)s, &e);
+    return (uint8_t)(e - 1 + 127);
+}
+
+static float group_scale(const uint16_t* xg, int len, float qmax, int scale_mode)
+{
+    float amax = group_amax(xg, len);
     if (amax < 1e-4f) amax = 1e-4f;
-    return amax / qmax;
+    float s = amax / qmax;
+    return scale_mode != 0 ? pow2_ceil(s) : s;
 }
 
 static int8_t int8_code(float q)
@@ -343,9 +406,24 @@ static int8_t int8_code(float q)
     return (int8_t)r;
 }
 
+/* MXFP4 shared exponent (OCP Microscaling Formats v1.0, conversion of a
+ * block to MX): floor(log2(amax)) minus the exponent of E2M1's largest
+ * value 6 = 1.5 * 2^2, i.e. minus 2, clamped to E8M0's range [-127, 127];
+ * an all-zero group takes -127 (reading: the spec leaves it open). */
+static int mx_shared_exp(float amax)
+{
+    if (amax == 0.0f) return -127;
+    int e;
+    frexp((double)amax, &e);                /* floor(log2 amax) = e - 1 */
+    int x = e - 1 - 2;
+    if (x < -127) x = -127;
+    if (x > 127) x = 127;
+    return x;
+}
+
 void orc_dispatch(const uint16_t* x, int64_t N, int H, const int32_t* slot_idx, int K,
-                  int quant, int group, int64_t t_begin, int64_t t_end,
-                  void* recv_x, float* recv_scales)
+                  int quant, int group, int scale_mode, int64_t t_begin, int64_t t_end,
+                  void* recv_x, void* recv_scales)
 {
     (void)N;
     if (quant == 0) {
@@ -360,15 +438,33 @@ void orc_dispatch(const uint16_t* x, int64_t N, int H, const int32_t* slot_idx, 
     }
 
     int G = H / group;
-    float qmax = (quant == 1) ? 448.0f : 127.0f;
-    uint8_t* codes = (uint8_t*)malloc((size_t)H);
+    /* bytes per received row: one per element, or two E2M1 codes per byte */
+    int row_bytes = quant == 3 ? H / 2 : H;
+    int byte_scales = quant == 3 || scale_mode == 2;
+    uint8_t* codes = (uint8_t*)calloc((size_t)row_bytes, 1);
     float* scales = (float*)malloc(sizeof(float) * (size_t)G);
+    uint8_t* scale_bytes = (uint8_t*)malloc((size_t)G);
     uint8_t* rx = (uint8_t*)recv_x;
     for (int64_t t = t_begin; t < t_end; ++t) {
         const uint16_t* xt = x + t * H;
         for (int g = 0; g < G; ++g) {
-            float scale = group_scale(xt + (int64_t)g * group, group, qmax);
+            const uint16_t* xg = xt + (int64_t)g * group;
+            if (quant == 3) {
+                /* MXFP4: element i of the row in nibble i % 2 of byte i / 2
+                 * (low nibble first; reading) */
+                int sx = mx_shared_exp(group_amax(xg, group));
+                scale_bytes[g] = (uint8_t)(sx + 127);
+                for (int i = g * group; i < (g + 1) * group; ++i) {
+                    float q = (float)ldexp((double)orc_f32_from_bf16(xt[i]), -sx);
+                    uint8_t c = orc_e2m1_from_f32(q);
+                    if (i % 2 == 0) codes[i / 2] = c;
+                    else codes[i / 2] |= (uint8_t)(c << 4);
+                }
+                continue;
+            }
+            float scale = group_scale(xg, group, quant == 1 ? 448.0f : 127.0f, scale_mode);
             scales[g] = scale;
+            scale_bytes[g] = scale_mode == 2 ? e8m0_of_pow2(scale) : 0;
             for (int i = g * group; i < (g + 1) * group; ++i) {
                 float q = orc_f32_from_bf16(xt[i]) / scale;
                 codes[i] = (quant == 1) ? orc_e4m3fn_from_f32(q) : (uint8_t)int8_code(q);
@@ -377,12 +473,16 @@ void orc_dispatch(const uint16_t* x, int64_t N, int H, const int32_t* slot_idx, 
         for (int k = 0; k < K; ++k) {
             int64_t s = slot_idx[t * K + k];
             if (s < 0) continue;
-            for (int h = 0; h < H; ++h) rx[s * H + h] = codes[h];
-            for (int g = 0; g < G; ++g) recv_scales[s * G + g] = scales[g];
+            for (int h = 0; h < row_bytes; ++h) rx[s * row_bytes + h] = codes[h];
+            for (int g = 0; g < G; ++g) {
+                if (byte_scales) ((uint8_t*)recv_scales)[s * G + g] = scale_bytes[g];
+                else ((float*)recv_scales)[s * G + g] = scales[g];
+            }
         }
     }
     free(codes);
     free(scales);
+    free(scale_bytes);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -400,6 +500,34 @@ void orc_combine(const uint16_t* y, const float* topk_weights, const int32_t* sl
                 int64_t s = slot_idx[t * K + k];
                 if (s < 0) continue;
                 acc += (double)topk_weights[t * K + k] * (double)orc_f32_from_bf16(y[s * H + h]);
+            }
+            out[t * H + h] = orc_bf16_from_f64(acc);
+        }
+}
+
+/* Combine of quantised expert outputs ("DeepEP 通信库使用指南（v2.1）":
+ * from v2.1 combine accepts int8 / fp8 quantisation, with the same
+ * quant_size choice as dispatch): y row s holds codes (E4M3FN bytes when
+ * quant == 1, int8 when quant == 2) and fp32 scales [*, H/group]; the value
+ * of element h is code * scale.  The sum is formed in fp64 and rounded once
+ * to bf16, as in orc_combine. */
+void orc_combine_q(const void* y_codes, const float* y_scales, int quant, int group,
+                   const float* topk_weights, const int32_t* slot_idx, int64_t N, int K, int H,
+                   int64_t t_begin, int64_t t_end, uint16_t* out)
+{
+    (void)N;
+    int G = H / group;
+    const uint8_t* yc = (const uint8_t*)y_codes;
+    for (int64_t t = t_begin; t < t_end; ++t)
+        for (int h = 0; h < H; ++h) {
+            double acc = 0.0;
+            for (int k = 0; k < K; ++k) {
+                int64_t s = slot_idx[t * K + k];
+                if (s < 0) continue;
+                uint8_t c = yc[s * H + h];
+                double v = quant == 1 ? (double)orc_f32_from_e4m3fn(c) : (double)(int8_t)c;
+                v *= (double)y_scales[s * G + h / group];
+                acc += (double)topk_weights[t * K + k] * v;
             }
             out[t * H + h] = orc_bf16_from_f64(acc);
         }

@@ -19,7 +19,10 @@
  *        home" long-sequence rounds, the int8 prefill quantisation option and
  *        the MOE_EXPERT_TOKEN_NUMS_TYPE count/prefix option.
  *   [P5] Aliyun "DeepEP 通信库使用指南（v2.1）" §1.3.1 (int8 quant_size:
- *        group mode 128, channel mode = hidden).
+ *        group mode 128, channel mode = hidden; the round_scale, use_ue8m0
+ *        flags; combine int8 / fp8), §1.3.3 (MXFP4, quant_size 32).
+ *   OCP Microscaling Formats (MX) v1.0: the E2M1 element and E8M0 scale
+ *        types and the block conversion MXFP4 uses.
  *
  * Where the pages are silent the oracle takes one stated reading; every
  * reading is listed with the function that takes it.
@@ -54,6 +57,13 @@ float orc_f32_from_bf16(uint16_t b);
 uint8_t orc_e4m3fn_from_f32(float v);
 /* OCP FP8 E4M3FN byte -> fp32 (0x7F/0xFF decode to NaN). */
 float orc_f32_from_e4m3fn(uint8_t b);
+/* fp32 -> OCP FP4 E2M1 code (low 4 bits; sign in bit 3): nearest, ties to
+ * even, |v| beyond 6 saturates to +-6. */
+uint8_t orc_e2m1_from_f32(float v);
+/* E2M1 code -> fp32 (exact). */
+float orc_f32_from_e2m1(uint8_t code);
+/* E8M0 byte -> 2^(b-127) (0xFF -> NaN). */
+float orc_f32_from_e8m0(uint8_t b);
 
 /* ---- a1: routing layout ([P3] §2.1) ----
  * topk_idx: int32 [N,K], entries in [-1, E); -1 = masked.
@@ -107,22 +117,34 @@ int orc_source_counts(const int32_t* topk_idx, int64_t N, int K, int E, int R, i
  * rank's first local expert. list [E]. */
 void orc_recv_list(const int32_t* psum_expert, int E, int R, int counts_as_prefix, int32_t* list);
 
-/* ---- a3: dispatch ([P3] §2.1/§2.2; quantisation [P5] §1.3.1, [P3] §7.4) ----
+/* ---- a3: dispatch ([P3] §2.1/§2.2; quantisation [P5] §1.3.1, §1.3.3,
+ *      [P3] §7.4) ----
  * x: bf16 bits [N,H]. For every t in [t_begin, t_end) and every k with
  * slot_idx[t,k] >= 0, receive row slot_idx[t,k] receives token t.
  * quant 0: recv_x is bf16 [*,H] (bit copy), recv_scales unused.
  * quant 1: recv_x is E4M3FN bytes [*,H]; quant 2: int8 [*,H].
- *   For both, group = elements per scale (128 or H), G = H/group, and
- *   recv_scales is fp32 [*,G]. */
+ *   group = elements per scale (128 or H), G = H/group.  scale_mode 0:
+ *   recv_scales fp32 [*,G] = amax/qmax; 1: fp32, rounded up to a power of
+ *   two; 2: that power of two as an E8M0 byte, recv_scales uint8 [*,G].
+ * quant 3 (MXFP4): group 32; recv_x holds two E2M1 codes per byte [*,H/2]
+ *   (element 2i in the low nibble), recv_scales one E8M0 byte per group
+ *   [*,H/32]; scale_mode unused. */
 void orc_dispatch(const uint16_t* x, int64_t N, int H, const int32_t* slot_idx, int K,
-                  int quant, int group, int64_t t_begin, int64_t t_end,
-                  void* recv_x, float* recv_scales);
+                  int quant, int group, int scale_mode, int64_t t_begin, int64_t t_end,
+                  void* recv_x, void* recv_scales);
 
 /* ---- a4: combine ([P2] API table; weighted reduce) ----
  * out[t,:] = bf16( sum over k with slot_idx[t,k] >= 0 of w[t,k] * y[slot,:] ),
  * sum formed in fp64, rounded once.  Rows with every k masked are +0. */
 void orc_combine(const uint16_t* y, const float* topk_weights, const int32_t* slot_idx,
                  int64_t N, int K, int H, int64_t t_begin, int64_t t_end, uint16_t* out);
+
+/* Combine of quantised expert outputs ([P5]: combine int8 / fp8 from v2.1):
+ * y_codes [*,H] E4M3FN (quant 1) or int8 (quant 2) with fp32 y_scales
+ * [*,H/group]; element value code * scale; otherwise as orc_combine. */
+void orc_combine_q(const void* y_codes, const float* y_scales, int quant, int group,
+                   const float* topk_weights, const int32_t* slot_idx, int64_t N, int K, int H,
+                   int64_t t_begin, int64_t t_end, uint16_t* out);
 
 #ifdef __cplusplus
 }

@@ -127,3 +127,51 @@ def test_e4m3fn_ties_to_even_and_saturation():
     assert list(oracle.e4m3fn_from_f32(big)) == [0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0xFE]
     # signed zero keeps its sign
     assert list(oracle.e4m3fn_from_f32(np.array([0.0, -0.0], np.float32))) == [0x00, 0x80]
+
+
+# ---- OCP FP4 E2M1 and E8M0 (OCP Microscaling Formats v1.0; MXFP4 of
+# 'DeepEP 通信库使用指南（v2.1）' §1.3.3) --------------------------------------
+
+E2M1_MAGNITUDES = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]   # codes 0..7, from the definition
+
+
+def test_e2m1_decode_table():
+    got = oracle.f32_from_e2m1(np.arange(16, dtype=np.uint8))
+    assert got[:8].tolist() == E2M1_MAGNITUDES
+    assert got[8:].tolist() == [-m for m in E2M1_MAGNITUDES]
+    assert np.signbit(got[8])                                     # -0
+
+
+def _e2m1_brute(v: float) -> int:
+    """Nearest of the eight magnitudes by exact distance, ties to the even
+    code, beyond 6 -> 6; sign from the sign bit."""
+    a = Fraction(abs(v))
+    if a > 6:
+        code = 7
+    else:
+        code = min(range(8), key=lambda c: (abs(Fraction(E2M1_MAGNITUDES[c]) - a), c % 2))
+    return code | (8 if np.signbit(v) else 0)
+
+
+def test_e2m1_nearest_ties_even_and_saturation():
+    mags = np.array(E2M1_MAGNITUDES)
+    mids = (mags[:-1] + mags[1:]) / 2
+    rng = np.random.default_rng(17)
+    v = np.concatenate([mags, mids, mids * (1 + 2.0 ** -20), mids * (1 - 2.0 ** -20),
+                        rng.uniform(0, 9, 3000), [6.5, 7.0, 8.0, 100.0, 1e30]]).astype(np.float32)
+    v = np.concatenate([v, -v])
+    got = oracle.e2m1_from_f32(v)
+    want = np.array([_e2m1_brute(float(a)) for a in v], np.uint8)
+    assert np.array_equal(got, want)
+    # every code decodes and re-encodes to itself
+    codes = np.arange(16, dtype=np.uint8)
+    assert np.array_equal(oracle.e2m1_from_f32(oracle.f32_from_e2m1(codes)), codes)
+
+
+def test_e8m0_decode_matches_torch():
+    b = np.arange(256, dtype=np.uint8)
+    got = oracle.f32_from_e8m0(b)
+    ref = torch.from_numpy(b.copy()).view(torch.float8_e8m0fnu).to(torch.float32).numpy()
+    assert np.isnan(got[255]) and np.isnan(ref[255])
+    assert np.array_equal(got[:255], ref[:255])
+    assert got[127] == 1.0 and got[128] == 2.0 and got[0] == np.float32(2.0 ** -127)

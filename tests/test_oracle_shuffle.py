@@ -216,3 +216,119 @@ def test_rounds_equal_one_shot():
     for b, e in W.round_ranges(1000, 4):
         oracle.combine(y, wt, s["slot_idx"], t_begin=b, t_end=e, out=o4)
     assert np.array_equal(o1, o4)
+
+
+# ---- scale modes, MXFP4 and quantised combine inputs ----------------------
+
+@pytest.mark.parametrize("quant,group,H", [(oracle.QUANT_FP8, 128, 512),
+                                          (oracle.QUANT_INT8, 256, 256)])
+@pytest.mark.parametrize("scale_mode", [oracle.SCALE_POW2, oracle.SCALE_UE8M0])
+def test_power_of_two_scales(quant, group, H, scale_mode):
+    """round_scale: the scale is the smallest power of two not below the fp32
+    quotient amax/qmax (no code saturates); with UE8M0 it is stored as its
+    biased exponent, whose float8_e8m0fnu decode by torch is the scale."""
+    idx, s, x = _setup(150, 4, 16, 4, 1, H, 31, mask_p=0.05)
+    x[2, :group] = 0
+    recv, sc = oracle.dispatch(x, s["slot_idx"], s["S"], quant=quant, group=group,
+                               scale_mode=scale_mode)
+    G = H // group
+    xf = oracle.f32_from_bf16(x).reshape(-1, G, group)
+    qmax = np.float32(448.0 if quant == oracle.QUANT_FP8 else 127.0)
+    quot = (np.maximum(np.abs(xf).max(axis=2), np.float32(1e-4)) / qmax).astype(np.float32)
+    m, e = np.frexp(quot.astype(np.float64))
+    scale = np.ldexp(1.0, np.where(m == 0.5, e - 1, e)).astype(np.float32)
+    assert np.all(scale >= quot) and np.all(scale / 2 < quot)
+    e8 = (np.log2(scale.ravel()).astype(np.int64) + 127).astype(np.uint8)
+    q = (xf / scale[:, :, None]).astype(np.float32)          # exact: a power of two
+    assert np.all(np.abs(q) <= qmax)
+    if quant == oracle.QUANT_FP8:
+        codes = torch.from_numpy(q.reshape(-1, H)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    else:
+        codes = np.rint(q).astype(np.int8).reshape(-1, H)
+    meta = s["src_meta"]
+    real = meta[:, 0] >= 0
+    t_of = meta[real, 0]
+    assert np.array_equal(recv[real].view(np.uint8), codes[t_of].view(np.uint8))
+    if scale_mode == oracle.SCALE_UE8M0:
+        assert sc.dtype == np.uint8
+        assert np.array_equal(sc[real], e8.reshape(-1, G)[t_of])
+        dec = torch.from_numpy(sc[real].copy()).view(torch.float8_e8m0fnu).to(torch.float32)
+        assert np.array_equal(dec.numpy(), scale[t_of])
+    else:
+        assert np.array_equal(sc[real].view(np.uint32), scale[t_of].view(np.uint32))
+
+
+def test_mxfp4_dispatch_pins():
+    """MXFP4: per 32 elements, shared exponent floor(log2 amax) - 2 (E8M0
+    byte, clamped to [-127, 127], -127 for an all-zero group), codes the
+    E2M1 nearest-even of x * 2^-shared, two per byte, low nibble first."""
+    H = 256
+    idx, s, x = _setup(120, 4, 16, 4, 1, H, 41, mask_p=0.05)
+    x[5, :32] = 0
+    x[6, 32:64] = oracle.bf16_from_f32(np.full(32, 2.0 ** -130, np.float32))
+    x[7, 64:96] = oracle.bf16_from_f32(np.linspace(-6, 6, 32).astype(np.float32))
+    recv, sc = oracle.dispatch(x, s["slot_idx"], s["S"], quant=oracle.QUANT_MXFP4)
+    assert recv.shape[1] == H // 2 and sc.dtype == np.uint8 and sc.shape[1] == H // 32
+    xf = oracle.f32_from_bf16(x).astype(np.float64).reshape(-1, H // 32, 32)
+    amax = np.abs(xf).max(axis=2)
+    _, e = np.frexp(np.where(amax > 0, amax, 1.0))
+    sx = np.where(amax > 0, np.clip(e - 1 - 2, -127, 127), -127)
+    q = np.ldexp(xf, -sx[:, :, None]).reshape(len(x), H)
+    want = np.array([_e2m1_code(float(v)) for v in q.ravel()], np.uint8).reshape(len(x), H)
+    packed = (want[:, 0::2] | (want[:, 1::2] << 4)).astype(np.uint8)
+    meta = s["src_meta"]
+    real = meta[:, 0] >= 0
+    t_of = meta[real, 0]
+    assert np.array_equal(sc[real], (sx + 127).astype(np.uint8)[t_of])
+    assert np.array_equal(recv[real], packed[t_of])
+    assert sx[5, 0] == -127 and sx[6, 1] == -127 and sx[7, 2] == 0
+    # amax / 2^shared lies in [4, 8): the largest element codes to 4 or 6
+    big = amax > 2.0 ** -120
+    mx = np.abs(q.reshape(-1, H // 32, 32)).max(axis=2)
+    assert np.all((mx[big] >= 4) & (mx[big] < 8))
+
+
+def _e2m1_code(v):
+    mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    a = Fraction(abs(v))
+    code = 7 if a > 6 else min(range(8), key=lambda c: (abs(Fraction(mags[c]) - a), c % 2))
+    return code | (8 if np.signbit(v) else 0)
+
+
+@pytest.mark.parametrize("quant", [oracle.QUANT_FP8, oracle.QUANT_INT8])
+def test_quantised_combine_reduces_to_bf16_combine(quant):
+    """With power-of-two scales every dequantised value code * scale is a
+    bf16 number, so combining the codes equals combining those bf16 rows."""
+    rng = np.random.default_rng(50 + quant)
+    S, H, N, K = 90, 256, 40, 4
+    y = _x(S, H, 51)
+    codes, sc = oracle.quantize_rows(y, quant, group=128, scale_mode=oracle.SCALE_POW2)
+    dec = (oracle.f32_from_e4m3fn(codes.ravel()).reshape(S, H) if quant == oracle.QUANT_FP8
+           else codes.astype(np.float32))
+    deq = dec * np.repeat(sc, 128, axis=1)
+    deq_bits = oracle.bf16_from_f32(deq).reshape(S, H)
+    assert np.array_equal(oracle.f32_from_bf16(deq_bits), deq)          # exact in bf16
+    slot = rng.integers(-1, S, size=(N, K)).astype(np.int32)
+    w = rng.standard_normal((N, K)).astype(np.float32)
+    got = oracle.combine_q(codes, sc, quant, 128, w, slot)
+    assert np.array_equal(got, oracle.combine(deq_bits, w, slot))
+
+
+def test_quantised_combine_exact_rational_sums():
+    rng = np.random.default_rng(61)
+    S, H, N, K = 30, 256, 12, 3
+    y = _x(S, H, 62)
+    codes, sc = oracle.quantize_rows(y, oracle.QUANT_INT8, group=H)      # fp32 scales
+    slot = rng.integers(-1, S, size=(N, K)).astype(np.int32)
+    w = rng.standard_normal((N, K)).astype(np.float32)
+    out = oracle.combine_q(codes, sc, oracle.QUANT_INT8, H, w, slot)
+    for t in range(N):
+        for h in range(0, H, 7):
+            q = sum((Fraction(float(w[t, k])) * int(codes[slot[t, k], h])
+                     * Fraction(float(sc[slot[t, k], 0])) for k in range(K) if slot[t, k] >= 0),
+                    Fraction(0))
+            got = int(out[t, h])
+            if q == 0:
+                assert got in (0x0000, 0x8000)
+            else:
+                assert got == _exact_bf16(q), (t, h)
