@@ -88,9 +88,16 @@ ep_status check_config(const ep_config* c)
     if (c->num_sources < 0 || c->num_sources > epk::kMaxSources)
         return EP_FAIL(EP_ERR_INVALID_ARG, "num_sources=%d outside [0,%d]", c->num_sources,
                        epk::kMaxSources);
-    if (c->quant != EP_QUANT_NONE && c->quant != EP_QUANT_FP8_E4M3 && c->quant != EP_QUANT_INT8)
+    if (c->quant < EP_QUANT_NONE || c->quant > EP_QUANT_MXFP4)
         return EP_FAIL(EP_ERR_INVALID_ARG, "quant=%d unknown", c->quant);
-    if (c->quant != EP_QUANT_NONE) {
+    if (c->scale_mode < EP_SCALE_FP32 || c->scale_mode > EP_SCALE_UE8M0)
+        return EP_FAIL(EP_ERR_INVALID_ARG, "scale_mode=%d unknown", c->scale_mode);
+    if (c->quant == EP_QUANT_MXFP4) {
+        if (c->quant_group != 32 || c->hidden % 32 != 0)
+            return EP_FAIL(EP_ERR_INVALID_ARG,
+                           "MXFP4 needs quant_group 32 and hidden %% 32 == 0 (got %d, %d)",
+                           c->quant_group, c->hidden);
+    } else if (c->quant != EP_QUANT_NONE) {
         if (c->quant_group == 128) {
             if (c->hidden % 128 != 0)
                 return EP_FAIL(EP_ERR_INVALID_ARG, "quant_group 128 needs hidden %% 128 == 0 (hidden=%d)",
@@ -104,6 +111,14 @@ ep_status check_config(const ep_config* c)
                            c->quant_group, c->hidden);
         }
     }
+    if (c->combine_quant != EP_QUANT_NONE && c->combine_quant != EP_QUANT_FP8_E4M3 &&
+        c->combine_quant != EP_QUANT_INT8)
+        return EP_FAIL(EP_ERR_INVALID_ARG, "combine_quant=%d must be none, FP8 or int8",
+                       c->combine_quant);
+    if (c->combine_quant != EP_QUANT_NONE &&
+        !(c->combine_group == c->hidden || (c->combine_group == 128 && c->hidden % 128 == 0)))
+        return EP_FAIL(EP_ERR_INVALID_ARG, "combine_group=%d must be hidden=%d, or 128 dividing it",
+                       c->combine_group, c->hidden);
     return EP_OK;
 }
 
@@ -229,7 +244,7 @@ ep_status layout_args(ep_handle* h, const int32_t* d_topk_idx, int64_t num_token
 // layout over num_tokens tokens and fills the kernel arguments.
 ep_status dispatch_args(const ep_handle* h, int64_t num_tokens, const void* d_x,
                         int64_t token_begin, int64_t token_end, void* d_recv_x,
-                        float* d_recv_scales, int64_t recv_capacity_rows, epk::DispatchArgs* out)
+                        void* d_recv_scales, int64_t recv_capacity_rows, epk::DispatchArgs* out)
 {
     if (token_begin < 0 || token_begin > token_end || token_end > num_tokens)
         return EP_FAIL(EP_ERR_INVALID_ARG, "token range [%lld,%lld) outside [0,%lld]",
@@ -240,8 +255,11 @@ ep_status dispatch_args(const ep_handle* h, int64_t num_tokens, const void* d_x,
         if (!d_x || !d_recv_x) return EP_FAIL(EP_ERR_INVALID_ARG, "x or recv_x is NULL");
         if (!aligned(d_x, 16) || !aligned(d_recv_x, 16))
             return EP_FAIL(EP_ERR_INVALID_ARG, "x and recv_x must be 16-byte aligned");
-        if (c.quant != EP_QUANT_NONE && (!d_recv_scales || !aligned(d_recv_scales, 4)))
-            return EP_FAIL(EP_ERR_INVALID_ARG, "quantised dispatch needs 4-byte aligned recv_scales");
+        const bool byte_scales = c.quant == EP_QUANT_MXFP4 || c.scale_mode == EP_SCALE_UE8M0;
+        if (c.quant != EP_QUANT_NONE &&
+            (!d_recv_scales || (!byte_scales && !aligned(d_recv_scales, 4))))
+            return EP_FAIL(EP_ERR_INVALID_ARG, "quantised dispatch needs recv_scales%s",
+                           byte_scales ? "" : " (4-byte aligned)");
     }
     if (c.quant == EP_QUANT_NONE && d_recv_scales)
         return EP_FAIL(EP_ERR_INVALID_ARG, "recv_scales must be NULL without quantisation");
@@ -258,6 +276,8 @@ ep_status dispatch_args(const ep_handle* h, int64_t num_tokens, const void* d_x,
     a.capacity = recv_capacity_rows;
     a.quant = c.quant;
     a.group = c.quant_group;
+    a.scale_mode = c.scale_mode;
+    a.identity = false;
     a.flags = h->at<uint32_t>(h->cv.ctrl) + epk::kCtrlFlags;
     return EP_OK;
 }
@@ -387,7 +407,7 @@ ep_status ep_get_layout(ep_handle* h, const int32_t* d_topk_idx, int64_t num_tok
 }
 
 ep_status ep_dispatch(const ep_handle* h, const void* d_x, int64_t token_begin, int64_t token_end,
-                      void* d_recv_x, float* d_recv_scales, int64_t recv_capacity_rows, void* stream)
+                      void* d_recv_x, void* d_recv_scales, int64_t recv_capacity_rows, void* stream)
 {
     if (!h) return EP_FAIL(EP_ERR_INVALID_ARG, "handle is NULL");
     if (h->num_tokens < 0) return EP_FAIL(EP_ERR_STATE, "ep_get_layout has not run on this handle");
@@ -405,7 +425,7 @@ ep_status ep_dispatch(const ep_handle* h, const void* d_x, int64_t token_begin, 
 ep_status ep_layout_dispatch(ep_handle* h, const int32_t* d_topk_idx, int64_t num_tokens,
                              int32_t* d_num_tokens_per_rank, int32_t* d_num_tokens_per_rdma_rank,
                              int32_t* d_num_tokens_per_expert, uint8_t* d_is_token_in_rank,
-                             const void* d_x, void* d_recv_x, float* d_recv_scales,
+                             const void* d_x, void* d_recv_x, void* d_recv_scales,
                              int64_t recv_capacity_rows, void* stream)
 {
     epk::LayoutArgs la;
@@ -430,7 +450,7 @@ ep_status ep_layout_dispatch(ep_handle* h, const int32_t* d_topk_idx, int64_t nu
     return EP_OK;
 }
 
-ep_status ep_combine(const ep_handle* h, const void* d_y, int64_t y_rows,
+ep_status ep_combine(const ep_handle* h, const void* d_y, const float* d_y_scales, int64_t y_rows,
                      const float* d_topk_weights, int64_t token_begin, int64_t token_end,
                      void* d_out, void* stream)
 {
@@ -448,8 +468,16 @@ ep_status ep_combine(const ep_handle* h, const void* d_y, int64_t y_rows,
                            "y and out must be 16-byte aligned, topk_weights 4-byte aligned");
     }
     const ep_config& c = h->cfg;
+    if (c.combine_quant == EP_QUANT_NONE && d_y_scales)
+        return EP_FAIL(EP_ERR_INVALID_ARG, "y_scales must be NULL without combine_quant");
+    if (c.combine_quant != EP_QUANT_NONE && token_end > token_begin && y_rows > 0 &&
+        (!d_y_scales || !aligned(d_y_scales, 4)))
+        return EP_FAIL(EP_ERR_INVALID_ARG, "combine_quant needs 4-byte aligned y_scales");
     epk::CombineArgs a;
     a.y = d_y;
+    a.y_scales = d_y_scales;
+    a.yquant = c.combine_quant;
+    a.ygroup = c.combine_group;
     a.y_rows = y_rows;
     a.weights = d_topk_weights;
     a.slot_idx = h->at<int32_t>(h->cv.slot);
@@ -460,6 +488,43 @@ ep_status ep_combine(const ep_handle* h, const void* d_y, int64_t y_rows,
     a.out = d_out;
     a.flags = h->at<uint32_t>(h->cv.ctrl) + epk::kCtrlFlags;
     EP_HIP(epk::launch_combine(a, static_cast<hipStream_t>(stream), h->take_events()));
+    return EP_OK;
+}
+
+ep_status ep_quantize_rows(const ep_config* cfg, const void* d_x, int64_t rows, void* d_codes,
+                           float* d_scales, void* stream)
+{
+    ep_status st = check_config(cfg);
+    if (st != EP_OK) return st;
+    if (cfg->combine_quant == EP_QUANT_NONE)
+        return EP_FAIL(EP_ERR_INVALID_ARG, "ep_quantize_rows needs combine_quant FP8 or int8");
+    if (rows < 0 || rows >= (int64_t)1 << 31)
+        return EP_FAIL(EP_ERR_INVALID_ARG, "rows=%lld outside [0, 2^31)", (long long)rows);
+    if (cfg->combine_group == cfg->hidden && cfg->hidden != 128 &&
+        cfg->hidden > epk::kWave * epk::kMaxVecPerLane * 8)
+        return EP_FAIL(EP_ERR_INVALID_ARG, "row quantisation supports hidden <= %d (hidden=%d)",
+                       epk::kWave * epk::kMaxVecPerLane * 8, cfg->hidden);
+    if (rows == 0) return EP_OK;
+    if (!d_x || !d_codes || !d_scales) return EP_FAIL(EP_ERR_INVALID_ARG, "x, codes or scales is NULL");
+    if (!aligned(d_x, 16) || !aligned(d_codes, 16) || !aligned(d_scales, 4))
+        return EP_FAIL(EP_ERR_INVALID_ARG,
+                       "x and codes must be 16-byte aligned, scales 4-byte aligned");
+    epk::DispatchArgs a;
+    a.x = d_x;
+    a.t_begin = 0;
+    a.t_end = rows;
+    a.H = cfg->hidden;
+    a.K = 1;
+    a.slot_idx = nullptr;
+    a.recv = d_codes;
+    a.scales = d_scales;
+    a.capacity = rows;
+    a.quant = cfg->combine_quant;
+    a.group = cfg->combine_group;
+    a.scale_mode = cfg->scale_mode == EP_SCALE_FP32 ? 0 : 1;   // fp32 storage
+    a.identity = true;
+    a.flags = nullptr;   // row t goes to row t < capacity: never flagged
+    EP_HIP(epk::launch_dispatch(a, static_cast<hipStream_t>(stream)));
     return EP_OK;
 }
 

@@ -6,7 +6,9 @@
 //   out[t] = bf16_rne( sum over k, ascending, with slot(t,k) >= 0 of
 //                      w[t,k] * y[slot(t,k)] )
 // accumulated in fp32 with fused multiply-add, one rounding to bf16 at the
-// end (v_cvt_pk_bf16_f32).
+// end (v_cvt_pk_bf16_f32).  y may also arrive quantised (Aliyun "DeepEP
+// 通信库使用指南（v2.1）": combine int8 / fp8 from v2.1, quant_size 128 or
+// hidden): element = code * scale in fp32, then the same reduction.
 //
 // Design: one wavefront per (token, column chunk) of VPL 16-byte vectors per
 // lane.  All K gathers of the chunk are issued before the arithmetic so each
@@ -57,7 +59,29 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     return __builtin_bit_cast(uint32_t, v);
 }
 
-template <int KMAX, int VPL>
+// Eight dequantised values of one 8-byte vector of codes.
+template <int YQ>
+__device__ __forceinline__ void decode8(u32x2 c, float (&v)[8])
+{
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        if constexpr (YQ == 1) {   // OCP E4M3FN, exact in fp32
+            const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[h], false);
+            const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[h], true);
+            v[4 * h] = lo[0];
+            v[4 * h + 1] = lo[1];
+            v[4 * h + 2] = hi[0];
+            v[4 * h + 3] = hi[1];
+        } else {                   // int8
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[4 * h + j] = (float)((int32_t)(c[h] << (24 - 8 * j)) >> 24);
+        }
+    }
+}
+
+// YQ: expert outputs y as bf16 (0) or as E4M3FN (1) / int8 (2) codes with
+// fp32 scales, one per row (YCH) or per 128 elements.
+template <int KMAX, int VPL, int YQ, bool YCH>
 __global__ __launch_bounds__(kBlock) void k_combine(CombineArgs a, int NV, int NC)
 {
     const int lane = threadIdx.x & (kWave - 1);
@@ -88,35 +112,65 @@ __global__ __launch_bounds__(kBlock) void k_combine(CombineArgs a, int NV, int N
     }
     if (oob && lane == 0) atomicOr(a.flags, kFlagYRows);
 
-    const u32x4* y = reinterpret_cast<const u32x4*>(a.y);
-    u32x4 yv[KMAX][VPL];
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k)
-#pragma unroll
-        for (int i = 0; i < VPL; ++i) {
-            const int v = vbase + kWave * i;
-            yv[k][i] = (slot[k] >= 0 && v < NV)
-                           ? load_stream(y + (int64_t)slot[k] * NV + v)
-                           : u32x4{0u, 0u, 0u, 0u};
-        }
-
     float acc[VPL][8];
 #pragma unroll
     for (int i = 0; i < VPL; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
+
+    if constexpr (YQ == 0) {
+        const u32x4* y = reinterpret_cast<const u32x4*>(a.y);
+        u32x4 yv[KMAX][VPL];
 #pragma unroll
-    for (int k = 0; k < KMAX; ++k) {
-        if (slot[k] < 0) continue;
+        for (int k = 0; k < KMAX; ++k)
 #pragma unroll
-        for (int i = 0; i < VPL; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t wd = yv[k][i][j];
-                acc[i][2 * j] = __builtin_fmaf(wk[k], __uint_as_float(wd << 16), acc[i][2 * j]);
-                acc[i][2 * j + 1] =
-                    __builtin_fmaf(wk[k], __uint_as_float(wd & 0xFFFF0000u), acc[i][2 * j + 1]);
+            for (int i = 0; i < VPL; ++i) {
+                const int v = vbase + kWave * i;
+                yv[k][i] = (slot[k] >= 0 && v < NV)
+                               ? load_stream(y + (int64_t)slot[k] * NV + v)
+                               : u32x4{0u, 0u, 0u, 0u};
             }
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            if (slot[k] < 0) continue;
+#pragma unroll
+            for (int i = 0; i < VPL; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t wd = yv[k][i][j];
+                    acc[i][2 * j] = __builtin_fmaf(wk[k], __uint_as_float(wd << 16), acc[i][2 * j]);
+                    acc[i][2 * j + 1] =
+                        __builtin_fmaf(wk[k], __uint_as_float(wd & 0xFFFF0000u), acc[i][2 * j + 1]);
+                }
+        }
+    } else {
+        // codes: 8 bytes per vector of 8 elements; scale of vector v is
+        // y_scales[slot, v / 16] (128-element groups) or y_scales[slot, 0]
+        const u32x2* y = reinterpret_cast<const u32x2*>(a.y);
+        const int G = YCH ? 1 : NV / 16;
+        u32x2 yv[KMAX][VPL];
+        float ys[KMAX][VPL];
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                const int v = vbase + kWave * i;
+                const bool live = slot[k] >= 0 && v < NV;
+                yv[k][i] = live ? load_stream(y + (int64_t)slot[k] * NV + v) : u32x2{0u, 0u};
+                ys[k][i] = live ? a.y_scales[(int64_t)slot[k] * G + (YCH ? 0 : v / 16)] : 0.0f;
+            }
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            if (slot[k] < 0) continue;
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                float dv[8];
+                decode8<YQ>(yv[k][i], dv);
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    acc[i][j] = __builtin_fmaf(wk[k], dv[j] * ys[k][i], acc[i][j]);
+            }
+        }
     }
 
     u32x4* orow = reinterpret_cast<u32x4*>(a.out) + t * NV;
@@ -134,15 +188,25 @@ __global__ __launch_bounds__(kBlock) void k_combine(CombineArgs a, int NV, int N
     }
 }
 
-template <int KMAX, int VPL>
+template <int KMAX, int VPL, int YQ, bool YCH>
 hipError_t launch_kv(const CombineArgs& a, int NV, hipStream_t s, LaunchEvents ev)
 {
     const int NC = (NV + kWave * VPL - 1) / (kWave * VPL);
     const int64_t items = (a.t_end - a.t_begin) * NC;
     if (items <= 0) return hipSuccess;
     const int blocks = (int)((items + kWavesPerBlock - 1) / kWavesPerBlock);
-    launch_k(k_combine<KMAX, VPL>, dim3(blocks), dim3(kBlock), 0, s, ev.start, ev.stop, a, NV, NC);
+    launch_k(k_combine<KMAX, VPL, YQ, YCH>, dim3(blocks), dim3(kBlock), 0, s, ev.start, ev.stop, a,
+             NV, NC);
     return hipGetLastError();
+}
+
+template <int YQ, bool YCH>
+hipError_t launch_q(const CombineArgs& a, int NV, hipStream_t s, LaunchEvents ev)
+{
+    if (a.K <= 2) return launch_kv<2, EP_COMBINE_VPL, YQ, YCH>(a, NV, s, ev);
+    if (a.K <= 4) return launch_kv<4, EP_COMBINE_VPL, YQ, YCH>(a, NV, s, ev);
+    if (a.K <= 8) return launch_kv<8, EP_COMBINE_VPL, YQ, YCH>(a, NV, s, ev);
+    return launch_kv<16, (EP_COMBINE_VPL > 1 ? EP_COMBINE_VPL / 2 : 1), YQ, YCH>(a, NV, s, ev);
 }
 
 }  // namespace
@@ -150,10 +214,12 @@ hipError_t launch_kv(const CombineArgs& a, int NV, hipStream_t s, LaunchEvents e
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s, LaunchEvents ev)
 {
     const int NV = a.H / 8;
-    if (a.K <= 2) return launch_kv<2, EP_COMBINE_VPL>(a, NV, s, ev);
-    if (a.K <= 4) return launch_kv<4, EP_COMBINE_VPL>(a, NV, s, ev);
-    if (a.K <= 8) return launch_kv<8, EP_COMBINE_VPL>(a, NV, s, ev);
-    return launch_kv<16, (EP_COMBINE_VPL > 1 ? EP_COMBINE_VPL / 2 : 1)>(a, NV, s, ev);
+    const bool ych = a.ygroup == a.H && a.H != 128;
+    switch (a.yquant) {
+        case 0: return launch_q<0, false>(a, NV, s, ev);
+        case 1: return ych ? launch_q<1, true>(a, NV, s, ev) : launch_q<1, false>(a, NV, s, ev);
+        default: return ych ? launch_q<2, true>(a, NV, s, ev) : launch_q<2, false>(a, NV, s, ev);
+    }
 }
 
 }  // namespace epk

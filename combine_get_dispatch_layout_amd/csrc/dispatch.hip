@@ -3,12 +3,17 @@
 //
 // What is computed ("DeepEP V1 vs V2 深度对比分析" §2.1/§2.2, expand form:
 // one receive row per (token, k); quantisation modes from Aliyun "DeepEP
-// 通信库使用指南（v2.1）" §1.3.1 -- group of 128 or channel = hidden -- and
+// 通信库使用指南（v2.1）" §1.3.1 -- group of 128 or channel = hidden, the
+// round_scale and use_ue8m0 flags -- and §1.3.3 (MXFP4, groups of 32);
 // "A2_DEEPEP.md" int8 prefill option; FP8 storage type float8_e4m3fn per
 // §7.4 of the first page):
 //   recv[slot(t,k)] = x[t]                          (bf16, bit copy), or
 //   scale = max(amax over the group, 1e-4) / Q,     Q = 448 (E4M3FN) / 127 (int8)
-//   code  = round_nearest_even(x / scale)           (fp32 division)
+//           (round_scale: the next power of two up; use_ue8m0: stored as
+//           its biased exponent byte)
+//   code  = round_nearest_even(x / scale)           (fp32 division), or
+//   MXFP4 (OCP MX v1.0): per 32 elements the E8M0 exponent
+//   floor(log2 amax) - 2 and E2M1 codes of x * 2^-exponent, two per byte.
 //
 // Design: one wavefront per (token, column chunk).  A chunk is VPL 16-byte
 // vectors per lane, lane-contiguous, so each load and store instruction of
@@ -50,9 +55,14 @@ __global__ __launch_bounds__(kBlock) void k_dispatch(DispatchArgs a, int NV, int
     // kMaxTopk words of slack, so reading KMAX words is in bounds; words past
     // K are ignored)
     int sl[KMAX];
-    const int32_t* srow = a.slot_idx + t * a.K;
+    if (a.identity) {   // row quantisation: row t to receive row t
 #pragma unroll
-    for (int k = 0; k < KMAX; ++k) sl[k] = srow[k];
+        for (int k = 0; k < KMAX; ++k) sl[k] = k == 0 ? (int)t : -1;
+    } else {
+        const int32_t* srow = a.slot_idx + t * a.K;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) sl[k] = srow[k];
+    }
     scatter_chunk<QUANT, CHANNEL, VPL, KMAX, ROW_WAIT>(a, vbase, NV, d, sl, lane);
 }
 
@@ -118,9 +128,11 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s, LaunchEvents ev
         case 1:
             return channel ? launch_channel<1>(a, NV, s, ev)
                            : launch_w<1, false, 1>(a, NV, a.H, s, ev);
-        default:
+        case 2:
             return channel ? launch_channel<2>(a, NV, s, ev)
                            : launch_w<2, false, 1>(a, NV, a.H, s, ev);
+        default:
+            return launch_w<3, false, 1>(a, NV, a.H / 2, s, ev);
     }
 }
 

@@ -67,11 +67,13 @@ struct DispatchArgs {
     const void* x;              // bf16 [N,H]
     int64_t t_begin, t_end;
     int H, K;
-    const int32_t* slot_idx;    // [N,K]
-    void* recv;                 // [cap,H] bf16 / e4m3fn / int8
-    float* scales;              // [cap,G]
+    const int32_t* slot_idx;    // [N,K]; unused when identity
+    void* recv;                 // [cap,H] bf16 / e4m3fn / int8, [cap,H/2] MXFP4 codes
+    void* scales;               // [cap,G] fp32, or E8M0 bytes (scale_mode 2, MXFP4)
     int64_t capacity;
     int quant, group;
+    int scale_mode;             // 0 fp32 amax/qmax, 1 power of two, 2 power of two as E8M0
+    bool identity;              // row t goes to receive row t (K = 1): row quantisation
     uint32_t* flags;
 };
 
@@ -87,7 +89,9 @@ struct SourceArgs {
 };
 
 struct CombineArgs {
-    const void* y;              // bf16 [y_rows,H]
+    const void* y;              // bf16 [y_rows,H], or E4M3FN / int8 codes (yquant)
+    const float* y_scales;      // [y_rows, H/ygroup] when yquant != 0
+    int yquant, ygroup;         // 0 bf16, 1 E4M3FN, 2 int8; elements per scale
     int64_t y_rows;
     const float* weights;       // [N,K]
     const int32_t* slot_idx;    // [N,K]

@@ -144,9 +144,11 @@ hipError_t launch_route_dispatch(const LayoutArgs& la, const DispatchArgs& da, h
         case 1:
             return channel ? launch_channel<1>(la, da, NV, s, ev)
                            : launch_rw<1, false, 1>(la, da, NV, da.H, s, ev);
-        default:
+        case 2:
             return channel ? launch_channel<2>(la, da, NV, s, ev)
                            : launch_rw<2, false, 1>(la, da, NV, da.H, s, ev);
+        default:
+            return launch_rw<3, false, 1>(la, da, NV, da.H / 2, s, ev);
     }
 }
 

@@ -87,6 +87,41 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
     return (uint32_t)w;
 }
 
+// Smallest power of two >= s, for a positive normal s (round_scale).
+__device__ __forceinline__ float pow2_ceil(float s)
+{
+    uint32_t u = __float_as_uint(s);
+    if (u & 0x007FFFFFu) u = (u & 0xFF800000u) + 0x00800000u;
+    return __uint_as_float(u);
+}
+
+// E8M0 byte of a power of two: its biased exponent.
+__device__ __forceinline__ uint8_t e8m0_of_pow2(float s)
+{
+    return (uint8_t)((__float_as_uint(s) >> 23) & 0xFFu);
+}
+
+// MXFP4 shared exponent of a 32-element block with largest magnitude m:
+// floor(log2 m) - 2 (E2M1's largest value is 1.5 * 2^2), clamped to E8M0's
+// [-127, 127]; zero and subnormal m give -127.
+__device__ __forceinline__ int mx_shared_exp(float m)
+{
+    const int e = (int)((__float_as_uint(m) >> 23) & 0xFFu);   // biased; m is finite
+    return e == 0 ? -127 : max(e - 129, -127);
+}
+
+// OCP FP4 E2M1 code of q (sign in bit 3): nearest of 0, 0.5, 1, 1.5, 2, 3,
+// 4, 6 with ties to the even code, saturating at 6.  Each comparison is one
+// boundary between neighbouring codes; a tie stays on the even side.
+__device__ __forceinline__ uint32_t e2m1_code(float q)
+{
+    const float m = fabsf(q);
+    const uint32_t c = (uint32_t)(m > 0.25f) + (uint32_t)(m >= 0.75f) + (uint32_t)(m > 1.25f) +
+                       (uint32_t)(m >= 1.75f) + (uint32_t)(m > 2.5f) + (uint32_t)(m >= 3.5f) +
+                       (uint32_t)(m > 5.0f);
+    return c | ((__float_as_uint(q) >> 28) & 8u);
+}
+
 // Loads the wave's chunk of row t: VPL 16-byte vectors per lane starting at
 // vector vbase (lane-contiguous), zero past the row end.
 template <int VPL>
@@ -103,8 +138,8 @@ __device__ __forceinline__ void load_chunk(const DispatchArgs& a, int64_t t, int
 
 // Writes the chunk (loaded by load_chunk) to the token's receive rows
 // sl[0..K), quantising it first when QUANT != 0.
-// QUANT: 0 none, 1 E4M3FN, 2 int8.  CHANNEL: one scale per row (the chunk
-// covers the row), else one per 128 elements.
+// QUANT: 0 none, 1 E4M3FN, 2 int8, 3 MXFP4.  CHANNEL: one scale per row (the
+// chunk covers the row), else one per 128 elements (32 for MXFP4).
 // ROW_WAIT: wait for each receive row's stores before writing the next row,
 // which bounds the writes a wave keeps in flight (faster for long rows).
 template <int QUANT, bool CHANNEL, int VPL, int KMAX, bool ROW_WAIT>
@@ -135,6 +170,51 @@ __device__ __forceinline__ void scatter_chunk(const DispatchArgs& a, int vbase, 
             }
             if constexpr (ROW_WAIT) __builtin_amdgcn_s_waitcnt(0x0F70);
         }
+    } else if constexpr (QUANT == 3) {
+        // MXFP4: 32 elements = 4 lanes x one vector share an E8M0 scale
+        uint32_t code[VPL];
+        uint32_t sbyte[VPL];
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            float m = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                m = fmaxf(m, fmaxf(fabsf(bf16_lo(d[i][j])), fabsf(bf16_hi(d[i][j]))));
+            m = group_max<4>(m);
+            const int sx = mx_shared_exp(m);
+            const float mul = __uint_as_float((uint32_t)(127 - sx) << 23);   // 2^-sx, exact
+            uint32_t w = 0u;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                w |= e2m1_code(bf16_lo(d[i][j]) * mul) << (8 * j);
+                w |= e2m1_code(bf16_hi(d[i][j]) * mul) << (8 * j + 4);
+            }
+            code[i] = w;
+            sbyte[i] = (uint32_t)(sx + 127);
+        }
+        const int G = NV / 4;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            if (k >= K) break;
+            const int s = sl[k];
+            if (s < 0) continue;
+            if (s >= a.capacity) {
+                if (lane == 0) atomicOr(a.flags, kFlagCapacity);
+                continue;
+            }
+            const __amdgpu_buffer_rsrc_t r =
+                row_rsrc(reinterpret_cast<char*>(a.recv) + (int64_t)s * NV * 4, NV * 4);
+            uint8_t* srow = reinterpret_cast<uint8_t*>(a.scales) + (int64_t)s * G;
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                const int v = vbase + kWave * i;
+                if (v < NV) {
+                    __builtin_amdgcn_raw_buffer_store_b32(code[i], r, v * 4, 0, kStoreAux);
+                    if ((lane & 3) == 0) srow[v / 4] = (uint8_t)sbyte[i];
+                }
+            }
+            if constexpr (ROW_WAIT) __builtin_amdgcn_s_waitcnt(0x0F70);
+        }
     } else {
         constexpr float kQ = (QUANT == 1) ? 448.0f : 127.0f;
         float amax[VPL];
@@ -146,18 +226,23 @@ __device__ __forceinline__ void scatter_chunk(const DispatchArgs& a, int vbase, 
                 m = fmaxf(m, fmaxf(fabsf(bf16_lo(d[i][j])), fabsf(bf16_hi(d[i][j]))));
             amax[i] = m;
         }
+        const bool pow2 = a.scale_mode != 0;
         float scale[VPL];
         if constexpr (CHANNEL) {
             float m = 0.0f;
 #pragma unroll
             for (int i = 0; i < VPL; ++i) m = fmaxf(m, amax[i]);
             m = group_max<kWave>(m);
-            const float sc = fmaxf(m, 1e-4f) / kQ;
+            float sc = fmaxf(m, 1e-4f) / kQ;
+            if (pow2) sc = pow2_ceil(sc);
 #pragma unroll
             for (int i = 0; i < VPL; ++i) scale[i] = sc;
         } else {
 #pragma unroll
-            for (int i = 0; i < VPL; ++i) scale[i] = fmaxf(group_max<16>(amax[i]), 1e-4f) / kQ;
+            for (int i = 0; i < VPL; ++i) {
+                scale[i] = fmaxf(group_max<16>(amax[i]), 1e-4f) / kQ;
+                if (pow2) scale[i] = pow2_ceil(scale[i]);
+            }
         }
         u32x2 code[VPL];
 #pragma unroll
@@ -175,6 +260,7 @@ __device__ __forceinline__ void scatter_chunk(const DispatchArgs& a, int vbase, 
             }
         }
         const int G = CHANNEL ? 1 : NV / 16;
+        const bool byte_scales = a.scale_mode == 2;
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
             if (k >= K) break;
@@ -186,16 +272,18 @@ __device__ __forceinline__ void scatter_chunk(const DispatchArgs& a, int vbase, 
             }
             const __amdgpu_buffer_rsrc_t r =
                 row_rsrc(reinterpret_cast<char*>(a.recv) + (int64_t)s * NV * 8, NV * 8);
-            float* srow = a.scales + (int64_t)s * G;
 #pragma unroll
             for (int i = 0; i < VPL; ++i) {
                 const int v = vbase + kWave * i;
                 if (v < NV) {
                     __builtin_amdgcn_raw_buffer_store_b64(code[i], r, v * 8, 0, kStoreAux);
-                    if constexpr (CHANNEL) {
-                        if (v == 0) srow[0] = scale[i];
-                    } else {
-                        if ((lane & 15) == 0) srow[v / 16] = scale[i];
+                    const bool writer = CHANNEL ? v == 0 : (lane & 15) == 0;
+                    const int64_t at = (int64_t)s * G + (CHANNEL ? 0 : v / 16);
+                    if (writer) {
+                        if (byte_scales)
+                            reinterpret_cast<uint8_t*>(a.scales)[at] = e8m0_of_pow2(scale[i]);
+                        else
+                            reinterpret_cast<float*>(a.scales)[at] = scale[i];
                     }
                 }
             }

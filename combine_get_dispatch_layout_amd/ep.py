@@ -16,14 +16,14 @@ LIB_PATH = os.path.join(_HERE, "libep_amd.so")
 
 EP_OK, EP_ERR_INVALID_ARG, EP_ERR_WORKSPACE, EP_ERR_CAPACITY, EP_ERR_DEVICE_INDEX, EP_ERR_HIP, \
     EP_ERR_STATE = range(7)
-EP_QUANT_NONE, EP_QUANT_FP8_E4M3, EP_QUANT_INT8 = 0, 1, 2
+EP_QUANT_NONE, EP_QUANT_FP8_E4M3, EP_QUANT_INT8, EP_QUANT_MXFP4 = 0, 1, 2, 3
+EP_SCALE_FP32, EP_SCALE_POW2, EP_SCALE_UE8M0 = 0, 1, 2
 EP_FLAG_BAD_EXPERT_ID, EP_FLAG_RECV_CAPACITY, EP_FLAG_Y_ROWS = 1, 2, 4
 
 # Every symbol include/ep.h declares.
 SYMBOLS = ("ep_workspace_size", "ep_recv_capacity", "ep_handle_init", "ep_handle_free",
            "ep_get_layout", "ep_dispatch", "ep_layout_dispatch", "ep_combine",
-           "ep_set_kernel_events",
-           "ep_handle_get_view", "ep_check_error", "ep_status_str", "ep_last_error_message")
+           "ep_quantize_rows", "ep_set_kernel_events", "ep_handle_get_view", "ep_check_error", "ep_status_str", "ep_last_error_message")
 
 
 class ep_config(ctypes.Structure):
@@ -32,7 +32,8 @@ class ep_config(ctypes.Structure):
                 ("ranks_per_node", ctypes.c_int32), ("expert_alignment", ctypes.c_int32),
                 ("quant", ctypes.c_int32), ("quant_group", ctypes.c_int32),
                 ("counts_as_prefix", ctypes.c_int32), ("expert_capacity", ctypes.c_int32),
-                ("num_sources", ctypes.c_int32)]
+                ("num_sources", ctypes.c_int32), ("scale_mode", ctypes.c_int32),
+                ("combine_quant", ctypes.c_int32), ("combine_group", ctypes.c_int32)]
 
 
 class ep_handle_view(ctypes.Structure):
@@ -72,7 +73,8 @@ def lib():
         L.ep_get_layout.argtypes = [P, P, I64, P, P, P, P, I32, P, P, P]
         L.ep_dispatch.argtypes = [P, P, I64, I64, P, P, I64, P]
         L.ep_layout_dispatch.argtypes = [P, P, I64, P, P, P, P, P, P, P, I64, P]
-        L.ep_combine.argtypes = [P, P, I64, P, I64, I64, P, P]
+        L.ep_combine.argtypes = [P, P, P, I64, P, I64, I64, P, P]
+        L.ep_quantize_rows.argtypes = [P, P, I64, P, P, P]
         L.ep_set_kernel_events.argtypes = [P, P, P]
         L.ep_handle_get_view.argtypes = [P, P]
         L.ep_check_error.argtypes = [P, P, P]
@@ -81,7 +83,7 @@ def lib():
         L.ep_last_error_message.argtypes = []
         L.ep_last_error_message.restype = ctypes.c_char_p
         for name in ("ep_workspace_size", "ep_recv_capacity", "ep_handle_init", "ep_get_layout",
-                     "ep_dispatch", "ep_layout_dispatch", "ep_combine", "ep_set_kernel_events", "ep_handle_get_view",
+                     "ep_dispatch", "ep_layout_dispatch", "ep_combine", "ep_quantize_rows", "ep_set_kernel_events", "ep_handle_get_view",
                      "ep_check_error"):
             getattr(L, name).restype = I32
         _lib = L
@@ -122,11 +124,15 @@ class Config:
     counts_as_prefix: bool = False
     expert_capacity: int = 0
     num_sources: int = 1
+    scale_mode: int = EP_SCALE_FP32
+    combine_quant: int = EP_QUANT_NONE
+    combine_group: int = 0
 
     def c(self):
         return ep_config(self.hidden, self.num_topk, self.num_experts, self.num_ranks,
                          self.ranks_per_node, self.expert_alignment, self.quant, self.quant_group,
-                         int(bool(self.counts_as_prefix)), self.expert_capacity, self.num_sources)
+                         int(bool(self.counts_as_prefix)), self.expert_capacity, self.num_sources,
+                         self.scale_mode, self.combine_quant, self.combine_group)
 
     @property
     def num_nodes(self):
@@ -135,6 +141,22 @@ class Config:
     @property
     def num_groups(self):
         return self.hidden // self.quant_group if self.quant else 0
+
+    @property
+    def recv_row_elems(self):
+        """Elements (bytes for codes) of one receive row."""
+        return self.hidden // 2 if self.quant == EP_QUANT_MXFP4 else self.hidden
+
+    @property
+    def recv_dtype(self):
+        return {EP_QUANT_NONE: torch.bfloat16, EP_QUANT_FP8_E4M3: torch.uint8,
+                EP_QUANT_INT8: torch.int8, EP_QUANT_MXFP4: torch.uint8}[self.quant]
+
+    @property
+    def scales_dtype(self):
+        if self.quant == EP_QUANT_MXFP4 or self.scale_mode == EP_SCALE_UE8M0:
+            return torch.uint8
+        return torch.float32
 
 
 def ep_workspace_size(cfg: Config, max_tokens: int) -> int:
@@ -218,13 +240,15 @@ def _check_dispatch_tensors(cfg, x, recv_x, recv_scales):
     if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[1] != cfg.hidden:
         raise ValueError("x must be bf16 [N, hidden]")
     want = {EP_QUANT_NONE: (torch.bfloat16,), EP_QUANT_FP8_E4M3: (torch.uint8, torch.float8_e4m3fn),
-            EP_QUANT_INT8: (torch.int8,)}[cfg.quant]
-    if recv_x.dtype not in want or recv_x.dim() != 2 or recv_x.shape[1] != cfg.hidden:
-        raise ValueError(f"recv_x must be {want} [rows, hidden]")
+            EP_QUANT_INT8: (torch.int8,), EP_QUANT_MXFP4: (torch.uint8,)}[cfg.quant]
+    if recv_x.dtype not in want or recv_x.dim() != 2 or recv_x.shape[1] != cfg.recv_row_elems:
+        raise ValueError(f"recv_x must be {want} [rows, {cfg.recv_row_elems}]")
     if cfg.quant:
-        if (recv_scales is None or recv_scales.dtype != torch.float32
+        if (recv_scales is None or recv_scales.dtype != cfg.scales_dtype
                 or recv_scales.shape != (recv_x.shape[0], cfg.num_groups)):
-            raise ValueError("recv_scales must be fp32 [rows, hidden/quant_group]")
+            raise ValueError(f"recv_scales must be {cfg.scales_dtype} [rows, hidden/quant_group]")
+    elif recv_scales is not None:
+        raise ValueError("recv_scales must be None without quantisation")
 
 
 def ep_get_layout(h: Handle, topk_idx: torch.Tensor, num_tokens_per_rank=None,
@@ -290,12 +314,29 @@ def ep_layout_dispatch(h: Handle, topk_idx: torch.Tensor, x: torch.Tensor, recv_
                 num_tokens_per_expert=outs[2], is_token_in_rank=outs[3])
 
 
+def _check_y(cfg, y, y_scales):
+    if cfg.combine_quant == EP_QUANT_NONE:
+        if y.dtype != torch.bfloat16 or y.dim() != 2 or y.shape[1] != cfg.hidden:
+            raise ValueError("y must be bf16 [rows, hidden]")
+        if y_scales is not None:
+            raise ValueError("y_scales must be None without combine_quant")
+        return
+    want = torch.int8 if cfg.combine_quant == EP_QUANT_INT8 else (torch.uint8,
+                                                                   torch.float8_e4m3fn)
+    want = want if isinstance(want, tuple) else (want,)
+    if y.dtype not in want or y.dim() != 2 or y.shape[1] != cfg.hidden:
+        raise ValueError(f"y must be {want} codes [rows, hidden]")
+    G = cfg.hidden // cfg.combine_group
+    if y_scales is None or y_scales.dtype != torch.float32 or y_scales.shape != (y.shape[0], G):
+        raise ValueError("y_scales must be fp32 [rows, hidden/combine_group]")
+
+
 def ep_combine(h: Handle, y: torch.Tensor, topk_weights: torch.Tensor, out: torch.Tensor,
-               token_begin=0, token_end=None):
-    """a4.  y bf16 [rows,H]; topk_weights fp32 [N,K]; out bf16 [N,H]."""
+               token_begin=0, token_end=None, y_scales: Optional[torch.Tensor] = None):
+    """a4.  y bf16 [rows,H] (or codes with y_scales under combine_quant);
+    topk_weights fp32 [N,K]; out bf16 [N,H]."""
     cfg = h.cfg
-    if y.dtype != torch.bfloat16 or y.dim() != 2 or y.shape[1] != cfg.hidden:
-        raise ValueError("y must be bf16 [rows, hidden]")
+    _check_y(cfg, y, y_scales)
     if topk_weights.dtype != torch.float32 or topk_weights.dim() != 2 \
             or topk_weights.shape[1] != cfg.num_topk:
         raise ValueError("topk_weights must be fp32 [N, num_topk]")
@@ -304,9 +345,31 @@ def ep_combine(h: Handle, y: torch.Tensor, topk_weights: torch.Tensor, out: torc
     token_end = out.shape[0] if token_end is None else token_end
     if not 0 <= token_begin <= token_end <= min(out.shape[0], topk_weights.shape[0]):
         raise ValueError("token range outside out / topk_weights")
-    _check(lib().ep_combine(h.ptr, _ptr(y), y.shape[0], _ptr(topk_weights), token_begin,
-                            token_end, _ptr(out), _stream(out.device)))
+    _check(lib().ep_combine(h.ptr, _ptr(y), _ptr(y_scales), y.shape[0], _ptr(topk_weights),
+                            token_begin, token_end, _ptr(out), _stream(out.device)))
     return out
+
+
+def ep_quantize_rows(cfg: Config, x: torch.Tensor, codes: Optional[torch.Tensor] = None,
+                     scales: Optional[torch.Tensor] = None):
+    """Quantises bf16 rows x [rows, H] into the (codes, fp32 scales) form
+    ep_combine reads under cfg.combine_quant.  Allocates missing outputs."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[1] != cfg.hidden:
+        raise ValueError("x must be bf16 [rows, hidden]")
+    if cfg.combine_quant == EP_QUANT_NONE:
+        raise ValueError("ep_quantize_rows needs combine_quant")
+    rows = x.shape[0]
+    if codes is None:
+        codes = torch.empty((rows, cfg.hidden), device=x.device,
+                            dtype=torch.int8 if cfg.combine_quant == EP_QUANT_INT8 else torch.uint8)
+    if scales is None:
+        scales = torch.empty((rows, cfg.hidden // cfg.combine_group), dtype=torch.float32,
+                             device=x.device)
+    _check_y(cfg, codes, scales)
+    c = cfg.c()
+    _check(lib().ep_quantize_rows(ctypes.byref(c), _ptr(x), rows, _ptr(codes), _ptr(scales),
+                                  _stream(x.device)))
+    return codes, scales
 
 
 def ep_set_kernel_events(h: Handle, start_event=None, stop_event=None):
@@ -400,8 +463,9 @@ def bind_layout_dispatch(h: Handle, topk_idx, x, recv_x, recv_scales, num_tokens
                   _ptr(recv_scales), recv_x.shape[0], s)
 
 
-def bind_combine(h: Handle, y, topk_weights, out, token_begin, token_end, stream=None):
+def bind_combine(h: Handle, y, topk_weights, out, token_begin, token_end, stream=None,
+                 y_scales=None):
     """A callable issuing ep_combine with these tensors and token range."""
     s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream(out.device)
-    return _bound(h, lib().ep_combine, h.ptr, _ptr(y), y.shape[0], _ptr(topk_weights), token_begin,
-                  token_end, _ptr(out), s)
+    return _bound(h, lib().ep_combine, h.ptr, _ptr(y), _ptr(y_scales), y.shape[0],
+                  _ptr(topk_weights), token_begin, token_end, _ptr(out), s)

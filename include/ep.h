@@ -57,8 +57,20 @@ typedef enum ep_status {
  * storage type float8_e4m3fn per [P3] §7.4). */
 enum {
     EP_QUANT_NONE = 0,      /* recv_x is bf16, a bit copy of x                  */
-    EP_QUANT_FP8_E4M3 = 1,  /* recv_x is OCP E4M3FN bytes, one fp32 scale/group */
-    EP_QUANT_INT8 = 2       /* recv_x is int8, one fp32 scale per group         */
+    EP_QUANT_FP8_E4M3 = 1,  /* recv_x is OCP E4M3FN bytes, one scale per group  */
+    EP_QUANT_INT8 = 2,      /* recv_x is int8, one scale per group              */
+    EP_QUANT_MXFP4 = 3      /* [P5] §1.3.3 / OCP MX v1.0: recv_x holds two E2M1
+                               codes per byte (element 2i in the low nibble),
+                               one E8M0 scale byte per 32 elements              */
+};
+
+/* Scale format of EP_QUANT_FP8_E4M3 / EP_QUANT_INT8 ([P5] §1.3.1 API flags
+ * round_scale and use_ue8m0; the pages name them, the readings are ours). */
+enum {
+    EP_SCALE_FP32 = 0,      /* fp32 amax / qmax                                */
+    EP_SCALE_POW2 = 1,      /* round_scale: the smallest power of two >= that  */
+    EP_SCALE_UE8M0 = 2      /* use_ue8m0: that power of two as one E8M0 byte
+                               (2^(b-127)); recv_scales is then uint8          */
 };
 
 /* Flag bits reported by ep_check_error(). */
@@ -79,7 +91,8 @@ typedef struct ep_config {
     int32_t expert_alignment;  /* A >= 1: each expert segment is padded to a
                                   multiple of A rows ([P3] §3.1)                 */
     int32_t quant;             /* EP_QUANT_*                                     */
-    int32_t quant_group;       /* elements per scale: 128 or hidden (quant only) */
+    int32_t quant_group;       /* elements per scale: 128 or hidden (FP8, int8),
+                                  32 (MXFP4)                                     */
     int32_t counts_as_prefix;  /* host list: 0 = per-expert aligned counts,
                                   1 = inclusive prefix restarting per rank
                                   ([P2] MOE_EXPERT_TOKEN_NUMS_TYPE)              */
@@ -99,6 +112,14 @@ typedef struct ep_config {
                                   handle also holds the per-source arrays of
                                   ep_handle_view ([P3] §3.1
                                   psum_num_recv_tokens_per_scaleup_rank).      */
+    int32_t scale_mode;        /* EP_SCALE_* for FP8 / int8 dispatch scales and
+                                  ep_quantize_rows (there UE8M0 = POW2, stored
+                                  fp32)                                          */
+    int32_t combine_quant;     /* EP_QUANT_NONE: ep_combine reads bf16 y.
+                                  EP_QUANT_FP8_E4M3 / EP_QUANT_INT8: y holds
+                                  codes with fp32 scales ([P5] combine int8/fp8
+                                  from v2.1)                                     */
+    int32_t combine_group;     /* elements per y scale: 128 or hidden           */
 } ep_config;
 
 typedef struct ep_handle ep_handle;
@@ -179,15 +200,20 @@ ep_status ep_get_layout(ep_handle* h, const int32_t* d_topk_idx, int64_t num_tok
  *   Tokens [token_begin, token_end) are sent: for each (t,k) with a slot,
  *   row slot of d_recv_x receives token t.  Padding rows are not written.
  *   d_recv_x: [recv_capacity_rows, H] of bf16 (EP_QUANT_NONE), E4M3FN bytes
- *     or int8; d_recv_scales: fp32 [recv_capacity_rows, H/quant_group], NULL
- *     iff quant == EP_QUANT_NONE.  Scale = max(amax, 1e-4) / (448 or 127),
- *     code = x / scale rounded to nearest-even (E4M3FN saturating, int8
- *     clamped to +-127).
+ *     or int8, or [recv_capacity_rows, H/2] bytes of E2M1 pairs (MXFP4);
+ *     d_recv_scales: [recv_capacity_rows, H/quant_group] of fp32, or of E8M0
+ *     bytes (EP_SCALE_UE8M0, MXFP4); NULL iff quant == EP_QUANT_NONE.
+ *     FP8 / int8: scale = max(amax, 1e-4) / (448 or 127) (rounded up to a
+ *     power of two unless EP_SCALE_FP32), code = x / scale rounded to
+ *     nearest-even (E4M3FN saturating, int8 clamped to +-127).  MXFP4: per 32
+ *     elements e = floor(log2 amax) - 2 clamped to [-127, 127] (-127 when
+ *     amax is 0), scale byte e + 127, codes E2M1(x * 2^-e) nearest-even,
+ *     saturating at 6.
  *   Reusing a handle across calls is cached dispatch ([P3] §3.2).
  *   EP_ERR_CAPACITY if S is known on the host and exceeds the capacity;
  *   otherwise rows beyond it are skipped and flagged on the device. */
 ep_status ep_dispatch(const ep_handle* h, const void* d_x, int64_t token_begin, int64_t token_end,
-                      void* d_recv_x, float* d_recv_scales, int64_t recv_capacity_rows,
+                      void* d_recv_x, void* d_recv_scales, int64_t recv_capacity_rows,
                       void* stream);
 
 /* a1 + a2 + a3 in one call: the unified dispatch of [P3] §2.2, which takes
@@ -206,19 +232,31 @@ ep_status ep_dispatch(const ep_handle* h, const void* d_x, int64_t token_begin, 
 ep_status ep_layout_dispatch(ep_handle* h, const int32_t* d_topk_idx, int64_t num_tokens,
                              int32_t* d_num_tokens_per_rank, int32_t* d_num_tokens_per_rdma_rank,
                              int32_t* d_num_tokens_per_expert, uint8_t* d_is_token_in_rank,
-                             const void* d_x, void* d_recv_x, float* d_recv_scales,
+                             const void* d_x, void* d_recv_x, void* d_recv_scales,
                              int64_t recv_capacity_rows, void* stream);
 
 /* a4: combine ([P2] API table: the paired inverse of dispatch).
- *   d_y: bf16 [y_rows, H] expert outputs in receive-row order;
+ *   d_y: bf16 [y_rows, H] expert outputs in receive-row order, or with
+ *   combine_quant set their E4M3FN / int8 codes [y_rows, H] and d_y_scales
+ *   fp32 [y_rows, H/combine_group] (element = code * scale; NULL iff
+ *   combine_quant == EP_QUANT_NONE);
  *   d_topk_weights: fp32 [num_tokens, K];  d_out: bf16 [num_tokens, H].
  *   For t in [token_begin, token_end): out[t] = bf16_rne( sum over k with a
  *   slot, k ascending, of w[t,k] * y[slot] ), accumulated in fp32 with fused
  *   multiply-add.  Masked entries contribute nothing; an all-masked row is
  *   +0.  Slots >= y_rows are skipped and flagged. */
-ep_status ep_combine(const ep_handle* h, const void* d_y, int64_t y_rows,
+ep_status ep_combine(const ep_handle* h, const void* d_y, const float* d_y_scales, int64_t y_rows,
                      const float* d_topk_weights, int64_t token_begin, int64_t token_end,
                      void* d_out, void* stream);
+
+/* Quantises bf16 rows d_x [rows, H] one row at a time into the form
+ * ep_combine reads with combine_quant (the sending side of a quantised
+ * combine, [P5] v2.1): d_codes [rows, H] E4M3FN / int8 codes, d_scales fp32
+ * [rows, H/combine_group], the arithmetic of ep_dispatch's FP8 / int8 mode
+ * (scale_mode POW2 or UE8M0: power-of-two scales, stored fp32).
+ * EP_ERR_INVALID_ARG if combine_quant is EP_QUANT_NONE. */
+ep_status ep_quantize_rows(const ep_config* cfg, const void* d_x, int64_t rows, void* d_codes,
+                           float* d_scales, void* stream);
 
 /* Profiling: the next ep_get_layout, ep_dispatch or ep_combine call on h
  * records start_event when its first kernel starts and stop_event when its

@@ -30,7 +30,8 @@ def config_of(w: W.Workload, counts_as_prefix=False):
                      expert_alignment=w.expert_alignment, quant=w.quant,
                      quant_group=w.quant_group if w.quant else 0,
                      counts_as_prefix=counts_as_prefix, expert_capacity=w.expert_capacity,
-                     num_sources=w.num_sources)
+                     num_sources=w.num_sources, scale_mode=w.scale_mode,
+                     combine_quant=w.combine_quant, combine_group=w.combine_group)
 
 
 def oracle_slots(w: W.Workload, idx):
@@ -51,8 +52,6 @@ def expected_host_list(w: W.Workload, ref_slots, counts_as_prefix=False):
                             counts_as_prefix).tolist()
 
 
-def recv_dtype(quant):
-    return {W.QUANT_NONE: torch.bfloat16, W.QUANT_FP8: torch.uint8, W.QUANT_INT8: torch.int8}[quant]
 
 
 class GpuRun:
@@ -67,8 +66,9 @@ class GpuRun:
         self.wts = torch.from_numpy(wts).to(device)
         self.x = x.to(device)
         self.cap = ep.ep_recv_capacity(self.cfg, N)
-        self.recv = torch.zeros((self.cap, w.hidden), dtype=recv_dtype(w.quant), device=device)
-        self.scales = (torch.zeros((self.cap, self.cfg.num_groups), dtype=torch.float32,
+        self.recv = torch.zeros((self.cap, self.cfg.recv_row_elems), dtype=self.cfg.recv_dtype,
+                                device=device)
+        self.scales = (torch.zeros((self.cap, self.cfg.num_groups), dtype=self.cfg.scales_dtype,
                                    device=device) if w.quant else None)
         self.out = torch.zeros((N, w.hidden), dtype=torch.bfloat16, device=device)
         self.rounds = rounds or W.round_ranges(N, w.rounds)
@@ -88,9 +88,9 @@ class GpuRun:
         for b, e in self.rounds:
             ep.ep_dispatch(self.h, self.x, self.recv, self.scales, b, e)
 
-    def combine(self, y):
+    def combine(self, y, y_scales=None):
         for b, e in self.rounds:
-            ep.ep_combine(self.h, y, self.wts, self.out, b, e)
+            ep.ep_combine(self.h, y, self.wts, self.out, b, e, y_scales=y_scales)
 
 
 def compare_layout(run: GpuRun, idx, ref_lay, ref_slots, host_sync=True):
@@ -136,7 +136,9 @@ def ordered_code(c, quant):
 
 
 def compare_dispatch(run: GpuRun, ref_recv, ref_scales, ref_slots):
-    """Returns the number of quantised codes that differ (0 for bf16)."""
+    """Returns the number of quantised codes that differ (0 for bf16).
+    MXFP4 codes and every scale (fp32 words or E8M0 bytes) must match
+    exactly; FP8 / int8 codes within one step."""
     meta = ref_slots["src_meta"]
     real = meta[:, 0] >= 0
     S = ref_slots["S"]
@@ -146,31 +148,47 @@ def compare_dispatch(run: GpuRun, ref_recv, ref_scales, ref_slots):
         return 0
     got = run.recv[:S].view(torch.uint8).cpu().numpy()[real]
     ref = ref_recv[:S].view(np.uint8)[real]
+    gs = run.scales[:S].cpu().numpy()[real]
+    rs = ref_scales[:S][real]
+    if gs.dtype == np.uint8:
+        assert np.array_equal(gs, rs.view(np.uint8))
+    else:
+        assert np.array_equal(gs.view(np.uint32), rs.view(np.uint32))
+    if run.w.quant == W.QUANT_MXFP4:
+        assert np.array_equal(got, ref)
+        return 0
     d = np.abs(ordered_code(got, run.w.quant) - ordered_code(ref, run.w.quant))
     assert d.max(initial=0) <= 1, f"codes differ by {d.max()} steps"
-    gs = run.scales[:S].cpu().numpy()[real]
-    assert np.array_equal(gs.view(np.uint32), ref_scales[:S][real].view(np.uint32))
     return int((d != 0).sum())
 
 
-def compare_combine(got_bits, ref_bits, y_bits, wts, slot_idx, K):
+def compare_combine(got_bits, ref_bits, yval, wts, slot_idx, K):
     """Checks the combine bar; returns the number of elements that are not
-    bit-identical."""
+    bit-identical.  yval(s, h): the value of expert-output element (s, h)
+    (needed only for the chain bound of elements off by more than an ulp)."""
     got = oracle.f32_from_bf16(got_bits).astype(np.float64)
     ref = oracle.f32_from_bf16(ref_bits).astype(np.float64)
     d = np.abs(got - ref)
     tol = 2.0 ** -7 * np.maximum(np.abs(ref), np.abs(got))
     bad = np.argwhere(d > tol)
-    yv = None
     for t, hcol in bad:
-        if yv is None:
-            yv = y_bits
-        terms = [abs(float(wts[t, k])) *
-                 abs(oracle.f32_from_bf16(yv[slot_idx[t, k], hcol:hcol + 1])[0].item())
+        terms = [abs(float(wts[t, k])) * abs(yval(slot_idx[t, k], hcol))
                  for k in range(K) if slot_idx[t, k] >= 0]
         chain = K * 2.0 ** -23 * sum(terms)
         assert d[t, hcol] <= tol[t, hcol] + chain, (t, hcol, got[t, hcol], ref[t, hcol], chain)
     return int((got_bits != ref_bits).sum())
+
+
+def bf16_values(y_bits):
+    return lambda s, h: float(oracle.f32_from_bf16(y_bits[s, h:h + 1])[0])
+
+
+def quantised_values(codes, scales, quant, group):
+    def val(s, h):
+        c = codes[s, h:h + 1]          # uint8 (E4M3FN) or int8
+        v = (float(oracle.f32_from_e4m3fn(c)[0]) if quant == W.QUANT_FP8 else float(c[0]))
+        return v * float(scales[s, h // group])
+    return val
 
 
 def run_and_check(w: W.Workload, device="cuda", rounds=None, seed_x=None, seed_y=None,
@@ -198,19 +216,29 @@ def run_and_check(w: W.Workload, device="cuda", rounds=None, seed_x=None, seed_y
     compare_layout(run, idx, ref_lay, ref_slots, host_sync=not fused)
     x_bits = bits16(x)
     ref_recv, ref_scales = oracle.dispatch(x_bits, ref_slots["slot_idx"], run.cap, quant=w.quant,
-                                           group=w.quant_group or None)
+                                           group=w.quant_group or None, scale_mode=w.scale_mode)
     ncode = compare_dispatch(run, ref_recv, ref_scales, ref_slots)
     stats = dict(S=ref_slots["S"], code_diffs=ncode)
     if check_combine:
         S = ref_slots["S"]
         y = W.activations(max(S, 1), w.hidden,
                           seed_y if seed_y is not None else W.y_seed(w), device=device)
-        run.combine(y)
+        y_bits = bits16(y)
+        if w.combine_quant:
+            # expert outputs as codes + fp32 scales, quantised by the oracle
+            cq, cs = oracle.quantize_rows(y_bits, w.combine_quant, group=w.combine_group,
+                                          scale_mode=min(w.scale_mode, 1))
+            run.combine(torch.from_numpy(cq).to(device), torch.from_numpy(cs).to(device))
+            ref_out = oracle.combine_q(cq, cs, w.combine_quant, w.combine_group, wts,
+                                       ref_slots["slot_idx"])
+            yval = quantised_values(cq, cs, w.combine_quant, w.combine_group)
+        else:
+            run.combine(y)
+            ref_out = oracle.combine(y_bits, wts, ref_slots["slot_idx"])
+            yval = bf16_values(y_bits)
         st, flags = ep.ep_check_error(run.h)
         assert st == ep.EP_OK and flags == 0
-        y_bits = bits16(y)
-        ref_out = oracle.combine(y_bits, wts, ref_slots["slot_idx"])
-        stats["combine_not_bit_identical"] = compare_combine(bits16(run.out), ref_out, y_bits, wts,
+        stats["combine_not_bit_identical"] = compare_combine(bits16(run.out), ref_out, yval, wts,
                                                              ref_slots["slot_idx"], w.num_topk)
     stats["run"] = run
     return stats

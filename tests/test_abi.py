@@ -44,7 +44,9 @@ GOOD = dict(hidden=2048, num_topk=8, num_experts=128, num_ranks=16)
     dict(num_ranks=2048, num_experts=1024), dict(ranks_per_node=-1), dict(expert_alignment=0),
     dict(quant=3), dict(quant=1, quant_group=64), dict(quant=2, quant_group=128, hidden=2056),
     dict(quant=2, quant_group=16384, hidden=16384), dict(num_sources=-1),
-    dict(num_sources=1025),
+    dict(num_sources=1025), dict(quant=3, quant_group=128), dict(quant=3, quant_group=32, hidden=2056),
+    dict(quant=4), dict(scale_mode=3), dict(combine_quant=3, combine_group=128),
+    dict(combine_quant=1, combine_group=64), dict(combine_quant=2, combine_group=128, hidden=2056),
 ])
 def test_invalid_configs_rejected(bad):
     cfg = ep.Config(**{**GOOD, **bad})
@@ -65,6 +67,18 @@ def test_workspace_and_capacity_sizes():
         ep.ep_workspace_size(cfg, -1)
     with pytest.raises(ep.EpError):
         ep.ep_workspace_size(cfg, 1 << 29)      # receive rows beyond 2^31
+
+
+def test_quantize_rows_host_checks():
+    L = ep.lib()
+    c = ep.Config(**GOOD).c()            # combine_quant none: rejected
+    assert L.ep_quantize_rows(ctypes.byref(c), None, 4, None, None, None) == ep.EP_ERR_INVALID_ARG
+    c = ep.Config(**GOOD, combine_quant=1, combine_group=128).c()
+    assert L.ep_quantize_rows(ctypes.byref(c), None, 0, None, None, None) == ep.EP_OK   # no rows
+    assert L.ep_quantize_rows(ctypes.byref(c), None, 4, None, None, None) == ep.EP_ERR_INVALID_ARG
+    c = ep.Config(hidden=16384, num_topk=8, num_experts=128, num_ranks=16, combine_quant=2,
+                  combine_group=16384).c()    # one row is too long for one wave's scale
+    assert L.ep_quantize_rows(ctypes.byref(c), None, 4, None, None, None) == ep.EP_ERR_INVALID_ARG
 
 
 def test_workspace_grows_with_sources():
@@ -99,6 +113,8 @@ def test_calls_on_null_handle_rejected():
     assert L.ep_get_layout(None, None, 0, None, None, None, None, 0, None, None, None) == \
         ep.EP_ERR_INVALID_ARG
     assert L.ep_dispatch(None, None, 0, 0, None, None, 0, None) == ep.EP_ERR_INVALID_ARG
-    assert L.ep_combine(None, None, 0, None, 0, 0, None, None) == ep.EP_ERR_INVALID_ARG
+    assert L.ep_combine(None, None, None, 0, None, 0, 0, None, None) == ep.EP_ERR_INVALID_ARG
+    assert L.ep_layout_dispatch(None, None, 0, None, None, None, None, None, None, None, 0,
+                                None) == ep.EP_ERR_INVALID_ARG
     assert L.ep_check_error(None, None, None) == ep.EP_ERR_INVALID_ARG
     L.ep_handle_free(None)

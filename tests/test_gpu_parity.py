@@ -394,3 +394,92 @@ def test_multi_source_empty_and_uneven():
         ep.ep_get_layout(h, torch.zeros((6, 2), dtype=torch.int32, device="cuda"))
     assert ei.value.status == ep.EP_ERR_INVALID_ARG
     assert ep.ep_check_error(h) == (ep.EP_OK, 0)
+
+
+# Scale formats (round_scale, UE8M0), MXFP4 dispatch and quantised combine
+# inputs, through the separate calls and the one-call form.
+QUANT_VARIANTS = [
+    dict(N=300, H=1024, E=64, R=8, K=8, quant=W.QUANT_FP8, group=128, sm=W.SCALE_POW2),
+    dict(N=128, H=7168, E=256, R=16, K=8, quant=W.QUANT_FP8, group=128, sm=W.SCALE_UE8M0),
+    dict(N=513, H=2048, E=64, R=8, K=6, quant=W.QUANT_INT8, group=2048, sm=W.SCALE_POW2),
+    dict(N=200, H=640, E=32, R=4, K=4, quant=W.QUANT_INT8, group=128, sm=W.SCALE_UE8M0),
+    dict(N=77, H=4096, E=64, R=8, K=6, quant=W.QUANT_INT8, group=4096, sm=W.SCALE_UE8M0),
+    dict(N=128, H=7168, E=256, R=16, K=8, quant=W.QUANT_MXFP4, group=32),   # decode shape
+    dict(N=1001, H=1184, E=96, R=12, K=8, quant=W.QUANT_MXFP4, group=32, mask=0.1),  # ragged
+    dict(N=64, H=32, E=32, R=2, K=16, quant=W.QUANT_MXFP4, group=32),       # one group, K=16
+]
+
+
+def _variant(args):
+    args = dict(args)
+    sm = args.pop("sm", W.SCALE_FP32)
+    return _custom(**args).scaled(scale_mode=sm)
+
+
+@pytest.mark.parametrize("args", QUANT_VARIANTS)
+@pytest.mark.parametrize("fused", [False, True])
+def test_quant_variants(args, fused):
+    w = _variant(args)
+    _say(f"[parity] quant variant fused={fused} {args}")
+    run_and_check(w, fused=fused)
+
+
+def test_mxfp4_special_groups():
+    """Zero, tiny (subnormal), saturating and tie-valued groups."""
+    w = _custom(N=16, H=256, E=8, R=2, K=2, quant=W.QUANT_MXFP4, group=32)
+    idx, wts = W.routing(w)
+    xf = torch.randn(16, 256)
+    xf[0, :32] = 0
+    xf[1, 32:64] = 2.0 ** -130
+    xf[2, 64:96] = torch.linspace(-6, 6, 32)
+    xf[3, :32] = torch.tensor([7.0, 5.0, 3.5, 2.5, 1.75, 1.25, 0.75, 0.25] * 4)  # ties at amax 7
+    xf[4, :32] = 3.0e38
+    x = xf.to(torch.bfloat16)
+    from shuffle_check import compare_dispatch, oracle_slots
+    run = GpuRun(w, idx, wts, x)
+    run.layout()
+    run.dispatch()
+    assert ep.ep_check_error(run.h) == (ep.EP_OK, 0)
+    ref_slots = oracle_slots(w, idx)
+    ref_recv, ref_scales = oracle.dispatch(bits16(x), ref_slots["slot_idx"], run.cap,
+                                           quant=W.QUANT_MXFP4)
+    compare_dispatch(run, ref_recv, ref_scales, ref_slots)
+
+
+QUANT_COMBINE = [
+    dict(N=400, H=2048, E=64, R=8, K=8, cq=W.QUANT_FP8, cg=128),
+    dict(N=300, H=1024, E=32, R=4, K=6, cq=W.QUANT_INT8, cg=1024),
+    dict(N=257, H=7168, E=256, R=16, K=8, cq=W.QUANT_INT8, cg=128, sm=W.SCALE_POW2),
+    dict(N=100, H=520, E=16, R=4, K=16, cq=W.QUANT_FP8, cg=520, mask=0.2),  # K=16, channel
+    dict(N=4096, H=2048, E=128, R=16, K=8, cq=W.QUANT_FP8, cg=128),          # prefill shape
+]
+
+
+@pytest.mark.parametrize("args", QUANT_COMBINE)
+def test_quantised_combine(args):
+    args = dict(args)
+    cq, cg, sm = args.pop("cq"), args.pop("cg"), args.pop("sm", W.SCALE_FP32)
+    w = _custom(**args).scaled(combine_quant=cq, combine_group=cg, scale_mode=sm)
+    _say(f"[parity] quantised combine cq={cq} cg={cg} sm={sm} {args}")
+    st = run_and_check(w)
+    _say(f"[parity] quantised combine: not bit-identical {st['combine_not_bit_identical']}")
+
+
+@pytest.mark.parametrize("cq,cg,H,sm", [(W.QUANT_FP8, 128, 2048, W.SCALE_FP32),
+                                        (W.QUANT_FP8, 7168, 7168, W.SCALE_POW2),
+                                        (W.QUANT_INT8, 128, 1024, W.SCALE_UE8M0),
+                                        (W.QUANT_INT8, 264, 264, W.SCALE_FP32)])
+def test_quantize_rows(cq, cg, H, sm):
+    cfg = ep.Config(hidden=H, num_topk=1, num_experts=1, num_ranks=1, combine_quant=cq,
+                    combine_group=cg, scale_mode=sm)
+    rows = 333
+    x = W.activations(rows, H, 123, device="cuda")
+    x[5] = 0
+    codes, scales = ep.ep_quantize_rows(cfg, x)
+    torch.cuda.synchronize()
+    rc, rs = oracle.quantize_rows(bits16(x), cq, group=cg, scale_mode=min(sm, 1))
+    assert np.array_equal(scales.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+    from shuffle_check import ordered_code
+    d = np.abs(ordered_code(codes.view(torch.uint8).cpu().numpy(), cq)
+               - ordered_code(rc.view(np.uint8), cq))
+    assert d.max() <= 1

@@ -17,7 +17,8 @@ from typing import Optional
 import numpy as np
 import torch
 
-QUANT_NONE, QUANT_FP8, QUANT_INT8 = 0, 1, 2
+QUANT_NONE, QUANT_FP8, QUANT_INT8, QUANT_MXFP4 = 0, 1, 2, 3
+SCALE_FP32, SCALE_POW2, SCALE_UE8M0 = 0, 1, 2
 
 
 @dataclass(frozen=True)
@@ -40,6 +41,9 @@ class Workload:
     ranks_per_node: int = 8
     expert_capacity: int = 0      # >0: fixed-capacity receive layout
     num_sources: int = 1          # >1: the batch stacks this many source ranks
+    scale_mode: int = SCALE_FP32  # FP8 / int8 scale format
+    combine_quant: int = QUANT_NONE   # expert outputs arrive as FP8 / int8 codes
+    combine_group: int = 0        # elements per expert-output scale
 
     def scaled(self, **kw) -> "Workload":
         return replace(self, **kw)
