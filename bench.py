@@ -38,16 +38,22 @@ def algorithmic_bytes(w, V, S):
 
     layout:   topk read 4NK, clone + in-block rank + slot writes/reads 16NK,
               is_token_in_rank NR, metadata 8V
-    dispatch: x read 2NH, slot read 4NK, receive rows V*(b*H + 4G)
-    combine:  y rows read 2VH, weights + slots read 8NK, out write 2NH
+    dispatch: x read 2NH, slot read 4NK, receive rows V*(b*H + c*G) with b
+              bytes per element (2 bf16, 1 FP8 / int8, 1/2 MXFP4) and c bytes
+              per scale (4 fp32, 1 E8M0)
+    combine:  y rows read V*(b'*H + 4*G') (b' = 2 bf16, 1 FP8 / int8 codes
+              with G' fp32 scales), weights + slots read 8NK, out write 2NH
     """
     N, H, K, R = w.num_tokens, w.hidden, w.num_topk, w.num_ranks
-    b = 2 if w.quant == 0 else 1
+    b = {0: 2.0, 1: 1.0, 2: 1.0, 3: 0.5}[w.quant]
     G = (H // w.quant_group) if w.quant else 0
+    c = 1 if (w.quant == 3 or w.scale_mode == 2) else 4
     layout = 4 * N * K + 16 * N * K + N * R + 8 * V
-    dispatch = 2 * N * H + 4 * N * K + V * (b * H + 4 * G)
-    combine = 2 * V * H + 8 * N * K + 2 * N * H
-    return dict(layout=layout, dispatch=dispatch, combine=combine)
+    dispatch = 2 * N * H + 4 * N * K + V * (b * H + c * G)
+    yb = 2 if w.combine_quant == 0 else 1
+    Gc = (H // w.combine_group) if w.combine_quant else 0
+    combine = V * (yb * H + 4 * Gc) + 8 * N * K + 2 * N * H
+    return dict(layout=int(layout), dispatch=int(dispatch), combine=int(combine))
 
 
 KERNEL_SOURCES = {"dispatch": ("dispatch.hip", "scatter.hpp"), "combine": ("combine.hip",),
@@ -157,8 +163,13 @@ def cpu_baseline(w, idx, wts, budget_s=12.0):
     y = W.activations(max(s0["S"], 1), w.hidden, W.y_seed(w)).view(torch.int16).numpy() \
         .view(np.uint16)
     cap = oracle.max_slots(N, w.num_topk, w.num_experts, w.expert_alignment)
-    recv = np.zeros((cap, w.hidden), np.uint16 if w.quant == 0 else np.uint8)
-    scales = np.zeros((cap, w.hidden // w.quant_group), np.float32) if w.quant else None
+    recv = np.zeros((cap, oracle.row_bytes(w.hidden, w.quant) // (2 if w.quant == 0 else 1)),
+                    np.uint16 if w.quant == 0 else np.uint8)
+    scales = (np.zeros((cap, w.hidden // w.quant_group), oracle.scale_dtype(w.quant, w.scale_mode))
+              if w.quant else None)
+    if w.combine_quant:
+        yc, ys = oracle.quantize_rows(y, w.combine_quant, group=w.combine_group,
+                                      scale_mode=min(w.scale_mode, 1))
     out = np.zeros((N, w.hidden), np.uint16)
     reps, t0 = 0, time.perf_counter()
     while True:
@@ -166,9 +177,14 @@ def cpu_baseline(w, idx, wts, budget_s=12.0):
         s = oracle.slots(idx, w.num_experts, w.num_ranks, w.expert_alignment)
         for b, e in W.round_ranges(N, w.rounds):
             oracle.dispatch(x, s["slot_idx"], cap, quant=w.quant, group=w.quant_group or None,
-                            t_begin=b, t_end=e, recv_x=recv, recv_scales=scales)
+                            t_begin=b, t_end=e, recv_x=recv, recv_scales=scales,
+                            scale_mode=w.scale_mode)
         for b, e in W.round_ranges(N, w.rounds):
-            oracle.combine(y, wts, s["slot_idx"], t_begin=b, t_end=e, out=out)
+            if w.combine_quant:
+                oracle.combine_q(yc, ys, w.combine_quant, w.combine_group, wts, s["slot_idx"],
+                                 t_begin=b, t_end=e, out=out)
+            else:
+                oracle.combine(y, wts, s["slot_idx"], t_begin=b, t_end=e, out=out)
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
@@ -217,6 +233,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="qwen3_30b_a3b_prefill")
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to rotate (0 = auto)")
+    ap.add_argument("--quant", choices=("none", "fp8", "int8", "mxfp4"),
+                    help="override the workload's dispatch quantisation")
+    ap.add_argument("--quant-group", type=int, default=0,
+                    help="elements per dispatch scale (default: 128, 32 for MXFP4)")
+    ap.add_argument("--scale-mode", choices=("fp32", "pow2", "ue8m0"),
+                    help="FP8 / int8 scale format (round_scale, use_ue8m0)")
+    ap.add_argument("--combine-quant", choices=("none", "fp8", "int8"),
+                    help="expert outputs as FP8 / int8 codes with fp32 scales (quantised once, "
+                         "before the timed loop, with ep_quantize_rows)")
+    ap.add_argument("--combine-group", type=int, default=128)
     ap.add_argument("--num-sources", type=int, default=0,
                     help=">1: read the batch as this many stacked source ranks (receive order "
                          "(source, token, k) plus the per-source counts)")
@@ -254,6 +280,14 @@ def main():
     w = W.WORKLOADS[args.workload]
     if args.num_sources > 1:
         w = w.scaled(num_sources=args.num_sources)
+    qnames = {"none": 0, "fp8": 1, "int8": 2, "mxfp4": 3}
+    if args.quant:
+        q = qnames[args.quant]
+        w = w.scaled(quant=q, quant_group=(args.quant_group or (32 if q == 3 else 128)) if q else 0)
+    if args.scale_mode:
+        w = w.scaled(scale_mode={"fp32": 0, "pow2": 1, "ue8m0": 2}[args.scale_mode])
+    if args.combine_quant and args.combine_quant != "none":
+        w = w.scaled(combine_quant=qnames[args.combine_quant], combine_group=args.combine_group)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     idx, wts = W.routing(w)
@@ -262,9 +296,10 @@ def main():
     cfg = ep.Config(hidden=H, num_topk=w.num_topk, num_experts=w.num_experts,
                     num_ranks=w.num_ranks, ranks_per_node=w.ranks_per_node,
                     expert_alignment=w.expert_alignment, quant=w.quant,
-                    quant_group=w.quant_group if w.quant else 0, num_sources=w.num_sources)
+                    quant_group=w.quant_group if w.quant else 0, num_sources=w.num_sources,
+                    scale_mode=w.scale_mode, combine_quant=w.combine_quant,
+                    combine_group=w.combine_group)
     cap = ep.ep_recv_capacity(cfg, N)
-    rdt = {0: torch.bfloat16, 1: torch.uint8, 2: torch.int8}[w.quant]
     G = cfg.num_groups
     rounds = W.round_ranges(N, w.rounds)
     fused = args.pipeline == "fused"
@@ -274,6 +309,7 @@ def main():
 
     # bytes touched per set; rotate sets so one cycle is >= 1 GiB
     per_set = 2 * N * H * 2 + cap * H * (2 if w.quant == 0 else 1) + cap * H * 2
+    per_set += cap * H * (2 if w.combine_quant else 0)   # y codes besides the bf16 y
     nsets = args.sets or max(2, min(8, -(-(1 << 30) // per_set)))
     sets = []
     topk_d = torch.from_numpy(idx).to(dev)
@@ -283,14 +319,18 @@ def main():
                  topk=topk_d.clone(), wts=wts_d.clone(),
                  x=W.activations(N, H, W.x_seed(w) + i, device=dev),
                  y=W.activations(cap, H, W.y_seed(w) + i, device=dev),
-                 recv=torch.empty((cap, H), dtype=rdt, device=dev),
-                 scales=torch.empty((cap, G), dtype=torch.float32, device=dev) if w.quant else None,
+                 recv=torch.empty((cap, cfg.recv_row_elems), dtype=cfg.recv_dtype, device=dev),
+                 scales=(torch.empty((cap, G), dtype=cfg.scales_dtype, device=dev) if w.quant
+                         else None),
                  out=torch.empty((N, H), dtype=torch.bfloat16, device=dev),
                  per_rank=torch.empty(w.num_ranks, dtype=torch.int32, device=dev),
                  per_expert=torch.empty(w.num_experts, dtype=torch.int32, device=dev),
                  per_node=(torch.empty(cfg.num_nodes, dtype=torch.int32, device=dev)
                            if cfg.num_nodes else None),
                  in_rank=torch.empty((N, w.num_ranks), dtype=torch.bool, device=dev))
+        s["y_scales"] = None
+        if w.combine_quant:
+            s["y"], s["y_scales"] = ep.ep_quantize_rows(cfg, s["y"])
         sets.append(s)
     # S from one synced layout (for the byte counts)
     S = ep.ep_get_layout(sets[0]["h"], sets[0]["topk"], do_cpu_sync=True)["num_recv_slots"]
@@ -323,7 +363,8 @@ def main():
                        ep.bind_dispatch(s["h"], s["x"], s["recv"], s["scales"], b, e,
                                         stream=stream)) for b, e in rounds]
         calls += [(stage_names.index("combine"),
-                   ep.bind_combine(s["h"], s["y"], s["wts"], s["out"], b, e, stream=stream))
+                   ep.bind_combine(s["h"], s["y"], s["wts"], s["out"], b, e, stream=stream,
+                                   y_scales=s["y_scales"]))
                   for b, e in rounds]
         s["calls"] = calls
         s["lay_done"] = torch.cuda.Event()
@@ -432,12 +473,16 @@ def main():
         "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
-        "dtype": {0: "bf16", 1: "bf16->fp8_e4m3fn", 2: "bf16->int8"}[w.quant],
+        "dtype": {0: "bf16", 1: "bf16->fp8_e4m3fn", 2: "bf16->int8", 3: "bf16->mxfp4"}[w.quant]
+                 + {0: "", 1: "; combine fp8_e4m3fn in", 2: "; combine int8 in"}[w.combine_quant],
         "data": "synthetic (seeded routing and N(0,1) activations)",
         "config": {"workload": w.name, "num_tokens": N, "hidden": H,
                    "num_experts": w.num_experts, "num_ranks": w.num_ranks,
                    "num_topk": w.num_topk, "expert_alignment": w.expert_alignment,
-                   "rounds": len(rounds), "num_sources": w.num_sources, "buffer_sets": nsets},
+                   "rounds": len(rounds), "num_sources": w.num_sources, "quant": w.quant,
+                   "quant_group": w.quant_group, "scale_mode": w.scale_mode,
+                   "combine_quant": w.combine_quant, "combine_group": w.combine_group,
+                   "buffer_sets": nsets},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": b_dom / launches,
