@@ -32,6 +32,10 @@ def lib():
         L.orc_slots.restype = i64
         L.orc_slots_fixed.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, P]
         L.orc_slots_fixed.restype = i64
+        L.orc_slots_nonexpand.argtypes = [P, i64, i32, i32, i32, P, P, P]
+        L.orc_slots_nonexpand.restype = i64
+        L.orc_recv_topk.argtypes = [P, P, P, i64, i32, i32, i32, P, P]
+        L.orc_recv_topk.restype = None
         L.orc_source_counts.argtypes = [P, i64, i32, i32, i32, i32, P, P]
         L.orc_source_counts.restype = i32
         L.orc_recv_list.argtypes = [P, i32, i32, i32, P]
@@ -165,6 +169,34 @@ def slots_fixed(topk_idx, num_experts, num_ranks, capacity):
         raise ValueError("topk_idx holds an id outside [-1, num_experts)")
     return dict(S=E * capacity, dropped=int(d), psum_expert=psum_e, psum_rank=psum_r,
                 num_unaligned=unal, slot_idx=slot, src_meta=meta[:E * capacity].copy())
+
+
+def slots_nonexpand(topk_idx, num_experts, num_ranks):
+    """Non-expand layout: dict(S = rows, psum_rank [R+1], slot_idx [N,K],
+    src_meta [S,2])."""
+    idx = _c(topk_idx, np.int32)
+    N, K = idx.shape
+    psum_r = np.zeros(num_ranks + 1, np.int32)
+    slot = np.zeros((N, K), np.int32)
+    meta = np.zeros((max(N * min(K, num_ranks), 1), 2), np.int32)
+    S = lib().orc_slots_nonexpand(_p(idx), N, K, num_experts, num_ranks, _p(psum_r), _p(slot),
+                                  _p(meta))
+    if S < 0:
+        raise ValueError("topk_idx holds an id outside [-1, num_experts)")
+    return dict(S=int(S), psum_rank=psum_r, slot_idx=slot, src_meta=meta[:S].copy())
+
+
+def recv_topk(topk_idx, topk_weights, src_meta, num_experts, num_ranks):
+    """recv_topk_idx int32 [rows,K] and recv_topk_weights fp32 [rows,K] of
+    the non-expand layout."""
+    idx = _c(topk_idx, np.int32)
+    w = _c(topk_weights, np.float32)
+    meta = _c(src_meta, np.int32)
+    rows, K = meta.shape[0], idx.shape[1]
+    ri = np.zeros((rows, K), np.int32)
+    rw = np.zeros((rows, K), np.float32)
+    lib().orc_recv_topk(_p(idx), _p(w), _p(meta), rows, K, num_experts, num_ranks, _p(ri), _p(rw))
+    return ri, rw
 
 
 def source_counts(topk_idx, num_experts, num_ranks, num_sources):

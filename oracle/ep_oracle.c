@@ -338,6 +338,81 @@ int orc_source_counts(const int32_t* topk_idx, int64_t N, int K, int E, int R, i
     return 0;
 }
 
+/* Non-expand receive layout (the V1 normal dispatch of "DeepEP V1 vs V2
+ * 深度对比分析" §2.1, which returns recv_x with recv_topk_idx /
+ * recv_topk_weights; EPHandle.do_expand of §3.1 chooses between the two
+ * forms): a token travels once to each rank that holds one of its experts.
+ * Rank r's rows are [psum_rank[r], psum_rank[r+1]), psum_rank the exclusive
+ * prefix of num_tokens_per_rank, in source-token order.  slot_idx[t,k] is the
+ * row of (t, rank of expert idx[t,k]) for the first k of the row on that
+ * rank, -1 for later k on the same rank and for masked entries (reading: the
+ * row belongs to the token's first entry on the rank).  src_meta[row] =
+ * (t, that first k).  Returns the number of rows, or -1 on a bad id. */
+int64_t orc_slots_nonexpand(const int32_t* topk_idx, int64_t N, int K, int E, int R,
+                            int32_t* psum_rank, int32_t* slot_idx, int32_t* src_meta)
+{
+    if (!ids_valid(topk_idx, N * K, E)) return -1;
+    int nle = E / R;
+    /* rows per rank: distinct tokens */
+    for (int r = 0; r <= R; ++r) psum_rank[r] = 0;
+    for (int64_t t = 0; t < N; ++t)
+        for (int k = 0; k < K; ++k) {
+            int e = topk_idx[t * K + k];
+            if (e < 0) continue;
+            int r = rank_of_expert(e, nle), first = 1;
+            for (int q = 0; q < k; ++q) {
+                int eq = topk_idx[t * K + q];
+                if (eq >= 0 && rank_of_expert(eq, nle) == r) first = 0;
+            }
+            if (first) psum_rank[r + 1] += 1;
+        }
+    for (int r = 0; r < R; ++r) psum_rank[r + 1] += psum_rank[r];
+    /* rows in token order within each rank */
+    for (int r = 0; r < R; ++r) {
+        int32_t next = psum_rank[r];
+        for (int64_t t = 0; t < N; ++t)
+            for (int k = 0; k < K; ++k) {
+                int e = topk_idx[t * K + k];
+                if (e < 0 || rank_of_expert(e, nle) != r) continue;
+                int first = 1;
+                for (int q = 0; q < k; ++q) {
+                    int eq = topk_idx[t * K + q];
+                    if (eq >= 0 && rank_of_expert(eq, nle) == r) first = 0;
+                }
+                if (!first) continue;
+                src_meta[2 * (int64_t)next] = (int32_t)t;
+                src_meta[2 * (int64_t)next + 1] = k;
+                next += 1;
+            }
+    }
+    for (int64_t t = 0; t < N; ++t)
+        for (int k = 0; k < K; ++k) slot_idx[t * K + k] = -1;
+    for (int64_t s = 0; s < psum_rank[R]; ++s)
+        slot_idx[(int64_t)src_meta[2 * s] * K + src_meta[2 * s + 1]] = (int32_t)s;
+    return psum_rank[R];
+}
+
+/* Per received row of the non-expand layout, the token's routing as seen by
+ * the receiving rank ([P3] §2.1 recv_topk_idx / recv_topk_weights): entry k
+ * is the local expert id idx[t,k] - r*nle and the weight w[t,k] when expert
+ * idx[t,k] is on the row's rank r, else -1 and 0.  rows = psum_rank[R]. */
+void orc_recv_topk(const int32_t* topk_idx, const float* topk_weights, const int32_t* src_meta,
+                   int64_t rows, int K, int E, int R, int32_t* recv_topk_idx,
+                   float* recv_topk_weights)
+{
+    int nle = E / R;
+    for (int64_t s = 0; s < rows; ++s) {
+        int64_t t = src_meta[2 * s];
+        int r = rank_of_expert(topk_idx[t * K + src_meta[2 * s + 1]], nle);
+        for (int k = 0; k < K; ++k) {
+            int e = topk_idx[t * K + k];
+            int on = e >= 0 && rank_of_expert(e, nle) == r;
+            recv_topk_idx[s * K + k] = on ? e - r * nle : -1;
+            recv_topk_weights[s * K + k] = on ? topk_weights[t * K + k] : 0.0f;
+        }
+    }
+}
+
 void orc_recv_list(const int32_t* psum_expert, int E, int R, int counts_as_prefix, int32_t* list)
 {
     int nle = E / R;

@@ -111,6 +111,22 @@ int64_t orc_slots_fixed(const int32_t* topk_idx, int64_t N, int K, int E, int R,
 int orc_source_counts(const int32_t* topk_idx, int64_t N, int K, int E, int R, int P,
                       int32_t* psum_source_rank, int32_t* expert_source_base);
 
+/* Non-expand receive layout ([P3] §2.1 V1 normal dispatch, §3.1 do_expand):
+ * one row per (token, rank holding one of its experts); rank r's rows are
+ * [psum_rank[r], psum_rank[r+1]) in token order; slot_idx[t,k] is the row of
+ * (t, rank of idx[t,k]) for the row's first k on that rank, else -1;
+ * src_meta [rows,2] = (t, first k).  psum_rank [R+1].  Returns the number of
+ * rows, -1 on a bad id. */
+int64_t orc_slots_nonexpand(const int32_t* topk_idx, int64_t N, int K, int E, int R,
+                            int32_t* psum_rank, int32_t* slot_idx, int32_t* src_meta);
+
+/* recv_topk_idx / recv_topk_weights [rows,K] of the non-expand layout: local
+ * expert id and weight where expert idx[t,k] is on the row's rank, else -1
+ * and 0. */
+void orc_recv_topk(const int32_t* topk_idx, const float* topk_weights, const int32_t* src_meta,
+                   int64_t rows, int K, int E, int R, int32_t* recv_topk_idx,
+                   float* recv_topk_weights);
+
 /* Host list of received tokens per expert ([P2] MOE_EXPERT_TOKEN_NUMS_TYPE):
  * counts_as_prefix == 0: aligned count of each expert;
  * counts_as_prefix != 0: inclusive prefix of those counts restarting at each

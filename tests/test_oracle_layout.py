@@ -337,3 +337,119 @@ def test_source_counts_degenerate_and_invalid():
     bad[3, 1] = 16
     with pytest.raises(ValueError):
         oracle.source_counts(bad, 16, 4, 2)
+
+
+# ---- non-expand layout ----------------------------------------------------
+
+def test_worked_example_non_expand():
+    g = _gold()
+    idx = np.array(g["topk_idx"], np.int32)
+    E, R = g["num_experts"], g["num_ranks"]
+    want = g["non_expand"]
+    s = oracle.slots_nonexpand(idx, E, R)
+    assert s["S"] == want["S"]
+    assert s["psum_rank"].tolist() == want["psum_rank"]
+    assert s["slot_idx"].tolist() == want["slot_idx"]
+    assert s["src_meta"].tolist() == want["src_meta"]
+    ri, rw = oracle.recv_topk(idx, np.array(g["topk_weights"], np.float32), s["src_meta"], E, R)
+    assert ri.tolist() == want["recv_topk_idx"]
+    assert rw.tolist() == want["recv_topk_weights"]
+
+
+def _numpy_nonexpand(idx, E, R):
+    """Rows from the token x rank membership: a column cumsum gives each
+    token's ordinal inside its rank; the first k of a row on a rank owns it."""
+    N, K = idx.shape
+    nle = E // R
+    member = np.zeros((N, R), np.int64)
+    rk = np.where(idx >= 0, idx // nle, -1)
+    for k in range(K):
+        ok = rk[:, k] >= 0
+        member[np.nonzero(ok)[0], rk[ok, k]] = 1
+    per = member.sum(axis=0)
+    psum = np.concatenate([[0], np.cumsum(per)])
+    ordinal = np.cumsum(member, axis=0) - member          # earlier tokens on the rank
+    slot = np.full((N, K), -1, np.int64)
+    for k in range(K):
+        first = rk[:, k] >= 0
+        for q in range(k):
+            first &= rk[:, q] != rk[:, k]
+        t = np.nonzero(first)[0]
+        slot[t, k] = psum[rk[t, k]] + ordinal[t, rk[t, k]]
+    return psum, slot
+
+
+@pytest.mark.parametrize("N,K,E,R", [(1, 1, 1, 1), (60, 4, 16, 4), (300, 8, 64, 16),
+                                     (200, 8, 256, 16), (90, 6, 12, 12), (50, 3, 8, 1)])
+def test_nonexpand_matches_numpy(N, K, E, R):
+    rng = np.random.default_rng(N + 7 * R)
+    idx = _random_routing(rng, N, K, E)
+    s = oracle.slots_nonexpand(idx, E, R)
+    psum, slot = _numpy_nonexpand(idx, E, R)
+    assert np.array_equal(s["psum_rank"], psum)
+    assert np.array_equal(s["slot_idx"], slot)
+    lay = oracle.layout(idx, E, R)
+    assert np.array_equal(np.diff(s["psum_rank"]), lay["num_tokens_per_rank"])
+    # src_meta inverts the slots
+    meta = s["src_meta"]
+    assert np.array_equal(s["slot_idx"][meta[:, 0], meta[:, 1]], np.arange(s["S"]))
+
+
+def test_nonexpand_is_expand_layout_of_rank_ids():
+    """The non-expand rows are the expand layout (alignment 1) of the derived
+    routing whose entries are rank ids, repeats of a rank in a row masked,
+    with one expert per rank."""
+    rng = np.random.default_rng(3)
+    N, K, E, R = 400, 8, 64, 8
+    idx = _random_routing(rng, N, K, E)
+    rk = np.where(idx >= 0, idx // (E // R), -1).astype(np.int32)
+    for k in range(K):
+        for q in range(k):
+            rk[:, k] = np.where((rk[:, k] >= 0) & (rk[:, q] == rk[:, k]), -1, rk[:, k])
+    ex = oracle.slots(rk, R, R, 1)
+    ne = oracle.slots_nonexpand(idx, E, R)
+    assert ex["S"] == ne["S"]
+    assert np.array_equal(ex["psum_expert"], ne["psum_rank"])
+    assert np.array_equal(ex["slot_idx"], ne["slot_idx"])
+    assert np.array_equal(ex["src_meta"], ne["src_meta"])
+
+
+def test_recv_topk_matches_numpy():
+    rng = np.random.default_rng(12)
+    N, K, E, R = 150, 8, 32, 4
+    idx = _random_routing(rng, N, K, E)
+    w = rng.random((N, K)).astype(np.float32)
+    s = oracle.slots_nonexpand(idx, E, R)
+    ri, rw = oracle.recv_topk(idx, w, s["src_meta"], E, R)
+    t = s["src_meta"][:, 0]
+    r = idx[t, s["src_meta"][:, 1]] // (E // R)
+    on = (idx[t] >= 0) & (idx[t] // (E // R) == r[:, None])
+    assert np.array_equal(ri, np.where(on, idx[t] - (r * (E // R))[:, None], -1))
+    assert np.array_equal(rw, np.where(on, w[t], 0))
+    # every valid entry of a token appears in exactly one of its rows
+    cnt = np.zeros((N, K), np.int64)
+    np.add.at(cnt, t, on.astype(np.int64))
+    assert np.array_equal(cnt, (idx >= 0).astype(np.int64))
+
+
+def test_group_limited_generator_brute_force():
+    """The group-limited router against a per-token loop: top groups by the
+    sum of their best two sigmoid affinities, then the best two experts of
+    each chosen group, listed by affinity; weights normalised."""
+    rng = np.random.default_rng(8)
+    N, E, G, TG, K = 40, 64, 8, 4, 8
+    logits = rng.standard_normal((N, E))
+    idx, w = W._group_limited(logits, G, TG, K)
+    aff = 1 / (1 + np.exp(-logits))
+    per = K // TG
+    for t in range(N):
+        score = [sum(sorted(aff[t, g * 8:(g + 1) * 8], reverse=True)[:per]) for g in range(G)]
+        groups = sorted(range(G), key=lambda g: (-score[g], g))[:TG]
+        chosen = []
+        for g in groups:
+            ex = sorted(range(g * 8, (g + 1) * 8), key=lambda e: (-aff[t, e], e))[:per]
+            chosen += ex
+        chosen = sorted(chosen, key=lambda e: -aff[t, e])
+        assert sorted(idx[t].tolist()) == sorted(chosen)
+        assert np.allclose(aff[t, idx[t]], sorted(aff[t, idx[t]], reverse=True))
+        assert abs(w[t].sum() - 1) < 1e-12

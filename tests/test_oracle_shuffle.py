@@ -332,3 +332,23 @@ def test_quantised_combine_exact_rational_sums():
                 assert got in (0x0000, 0x8000)
             else:
                 assert got == _exact_bf16(q), (t, h)
+
+
+def test_nonexpand_combine_sums_rank_rows():
+    """Non-expand combine: each token's rank rows summed once (unit
+    weights), the sum exact before the single bf16 rounding."""
+    rng = np.random.default_rng(70)
+    N, K, E, R, H = 60, 8, 32, 8, 16
+    idx = np.argsort(rng.random((N, E)), axis=1)[:, :K].astype(np.int32)
+    idx[rng.random((N, K)) < 0.1] = -1
+    s = oracle.slots_nonexpand(idx, E, R)
+    y = _x(s["S"], H, 71)
+    out = oracle.combine(y, np.ones((N, K), np.float32), s["slot_idx"])
+    yv = oracle.f32_from_bf16(y)
+    for t in range(N):
+        rows = [r for r in s["slot_idx"][t] if r >= 0]
+        assert len(rows) == len({int(a) // (E // R) for a in idx[t] if a >= 0})
+        for h in range(H):
+            q = sum((Fraction(float(yv[r, h])) for r in rows), Fraction(0))
+            got = int(out[t, h])
+            assert got in (0, 0x8000) if q == 0 else got == _exact_bf16(q)

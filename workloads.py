@@ -33,8 +33,8 @@ class Workload:
     quant: int = QUANT_NONE
     quant_group: int = 0          # elements per scale; 0 = not quantised
     mask_prob: float = 0.0
-    routing: str = "uniform"      # uniform | softmax_topk | zipf
-    weights: str = "softmax"      # softmax (renormalised over chosen k) | raw
+    routing: str = "uniform"      # uniform | softmax_topk | zipf | group_limited
+    weights: str = "softmax"      # softmax (renormalised over chosen k) | raw (the router's own)
     zipf_s: float = 1.2
     rounds: int = 1
     seed: int = 0
@@ -44,6 +44,9 @@ class Workload:
     scale_mode: int = SCALE_FP32  # FP8 / int8 scale format
     combine_quant: int = QUANT_NONE   # expert outputs arrive as FP8 / int8 codes
     combine_group: int = 0        # elements per expert-output scale
+    non_expand: bool = False      # one receive row per (token, rank) instead of per (token, k)
+    expert_groups: int = 32       # group_limited routing: expert groups ...
+    topk_groups: int = 4          # ... of which each token uses this many
 
     def scaled(self, **kw) -> "Workload":
         return replace(self, **kw)
@@ -61,6 +64,11 @@ WORKLOADS = {
                                     seed=1004),
     "long_seq_int8": Workload("long_seq_int8", 32768, 4096, 64, 8, 6, quant=QUANT_INT8,
                               quant_group=4096, rounds=4, seed=1005),
+    # DeepSeek-V3 gating (256 experts in 32 groups, top-4 groups, top-2 per
+    # group) with the non-expand dispatch that sends a token once per rank
+    "deepseek_v3_group_limited": Workload("deepseek_v3_group_limited", 8192, 7168, 256, 16, 8,
+                                          routing="group_limited", weights="raw",
+                                          non_expand=True, seed=1006),
 }
 
 
@@ -69,6 +77,36 @@ def _softmax(z, axis=-1):
         z = z - z.max(axis=axis, keepdims=True)
         e = np.exp(z)
         return e / e.sum(axis=axis, keepdims=True)
+
+
+def _group_limited(logits, n_groups, topk_groups, K):
+    """Group-limited gating ("DeepEP V1 vs V2 深度对比分析" §8.1: experts in
+    groups, each token picks its top groups, then the top experts inside
+    each picked group).  Readings where the page is silent: affinity =
+    sigmoid(logit); a group's score is the sum of its best K/topk_groups
+    affinities (the ones it would contribute); ties go to the lower id; the
+    chosen experts are listed by affinity, highest first; weights are their
+    affinities normalised to sum 1."""
+    N, E = logits.shape
+    per = K // topk_groups
+    aff = 1.0 / (1.0 + np.exp(-logits))
+    g = aff.reshape(N, n_groups, E // n_groups)
+    top_in_group = -np.sort(-g, axis=2)[:, :, :per]
+    gscore = top_in_group.sum(axis=2)
+    gsel = np.argsort(-gscore, axis=1, kind="stable")[:, :topk_groups]
+    allowed = np.zeros((N, n_groups), bool)
+    np.put_along_axis(allowed, gsel, True, axis=1)
+    masked = np.where(np.repeat(allowed, E // n_groups, axis=1), aff, -np.inf)
+    # the best `per` experts of every group, then the K best of those (all
+    # from the allowed groups, `per` from each)
+    order = np.argsort(-masked.reshape(N, n_groups, E // n_groups), axis=2, kind="stable")[:, :, :per]
+    base = (np.arange(n_groups) * (E // n_groups))[None, :, None]
+    cand = (order + base).reshape(N, -1)                 # [N, n_groups*per]
+    cand_aff = np.take_along_axis(masked, cand, axis=1)
+    pick = np.argsort(-cand_aff, axis=1, kind="stable")[:, :K]
+    idx = np.take_along_axis(cand, pick, axis=1)
+    w = np.take_along_axis(aff, idx, axis=1)
+    return idx, w / w.sum(axis=1, keepdims=True)
 
 
 def routing(w: Workload, num_tokens: Optional[int] = None):
@@ -83,6 +121,8 @@ def routing(w: Workload, num_tokens: Optional[int] = None):
     elif w.routing == "uniform":
         idx = np.argsort(rng.random((N, E)), axis=1, kind="stable")[:, :K]
         wts = None
+    elif w.routing == "group_limited":
+        idx, wts = _group_limited(rng.standard_normal((N, E)), w.expert_groups, w.topk_groups, K)
     elif w.routing == "zipf":
         logp = -w.zipf_s * np.log(np.arange(1, E + 1, dtype=np.float64))
         gumbel = -np.log(-np.log(rng.random((N, E))))
