@@ -38,21 +38,24 @@ def algorithmic_bytes(w, V, S):
 
     layout:   topk read 4NK, clone + in-block rank + slot writes/reads 16NK,
               is_token_in_rank NR, metadata 8V
-    dispatch: x read 2NH, slot read 4NK, receive rows V*(b*H + c*G) with b
+    dispatch: x read 2NH, slot read 4NK, receive rows M*(b*H + c*G) with b
               bytes per element (2 bf16, 1 FP8 / int8, 1/2 MXFP4) and c bytes
               per scale (4 fp32, 1 E8M0)
-    combine:  y rows read V*(b'*H + 4*G') (b' = 2 bf16, 1 FP8 / int8 codes
+    combine:  y rows read M*(b'*H + 4*G') (b' = 2 bf16, 1 FP8 / int8 codes
               with G' fp32 scales), weights + slots read 8NK, out write 2NH
+    M, the rows moved, is V (valid pairs), or S (one row per token and rank)
+    with the non-expand dispatch.
     """
     N, H, K, R = w.num_tokens, w.hidden, w.num_topk, w.num_ranks
+    M = S if w.non_expand else V
     b = {0: 2.0, 1: 1.0, 2: 1.0, 3: 0.5}[w.quant]
     G = (H // w.quant_group) if w.quant else 0
     c = 1 if (w.quant == 3 or w.scale_mode == 2) else 4
     layout = 4 * N * K + 16 * N * K + N * R + 8 * V
-    dispatch = 2 * N * H + 4 * N * K + V * (b * H + c * G)
+    dispatch = 2 * N * H + 4 * N * K + M * (b * H + c * G)
     yb = 2 if w.combine_quant == 0 else 1
     Gc = (H // w.combine_group) if w.combine_quant else 0
-    combine = V * (yb * H + 4 * Gc) + 8 * N * K + 2 * N * H
+    combine = M * (yb * H + 4 * Gc) + 8 * N * K + 2 * N * H
     return dict(layout=int(layout), dispatch=int(dispatch), combine=int(combine))
 
 
@@ -118,7 +121,9 @@ def traffic_summary(fetch_csv, write_csv, workload, pipeline):
     w = W.WORKLOADS[workload]
     idx, _ = W.routing(w)
     V = int((idx >= 0).sum())
-    nbytes = algorithmic_bytes(w, V, 0)
+    ranks = np.where(idx >= 0, idx // (w.num_experts // w.num_ranks), -1)
+    rows = sum(len(set(r[r >= 0].tolist())) for r in ranks)   # non-expand rows
+    nbytes = algorithmic_bytes(w, V, rows)
     nbytes["layout_dispatch"] = nbytes["layout"] + nbytes["dispatch"]
     bench_args = f"--workload {workload} --pipeline {pipeline} --steps 4 --warmup 2 --no-cpu-baseline"
     command = [f"rocprofv3 --pmc FETCH_SIZE -f csv -d <dir> -o fetch -- python3 bench.py {bench_args}",
@@ -159,7 +164,8 @@ def cpu_baseline(w, idx, wts, budget_s=12.0):
     import torch
     N = w.num_tokens
     x = W.activations(N, w.hidden, W.x_seed(w)).view(torch.int16).numpy().view(np.uint16)
-    s0 = oracle.slots(idx, w.num_experts, w.num_ranks, w.expert_alignment)
+    s0 = (oracle.slots_nonexpand(idx, w.num_experts, w.num_ranks) if w.non_expand
+          else oracle.slots(idx, w.num_experts, w.num_ranks, w.expert_alignment))
     y = W.activations(max(s0["S"], 1), w.hidden, W.y_seed(w)).view(torch.int16).numpy() \
         .view(np.uint16)
     cap = oracle.max_slots(N, w.num_topk, w.num_experts, w.expert_alignment)
@@ -171,10 +177,13 @@ def cpu_baseline(w, idx, wts, budget_s=12.0):
         yc, ys = oracle.quantize_rows(y, w.combine_quant, group=w.combine_group,
                                       scale_mode=min(w.scale_mode, 1))
     out = np.zeros((N, w.hidden), np.uint16)
+    ones = np.ones_like(wts)
     reps, t0 = 0, time.perf_counter()
     while True:
         oracle.layout(idx, w.num_experts, w.num_ranks, w.ranks_per_node)
         s = oracle.slots(idx, w.num_experts, w.num_ranks, w.expert_alignment)
+        if w.non_expand:
+            s = oracle.slots_nonexpand(idx, w.num_experts, w.num_ranks)
         for b, e in W.round_ranges(N, w.rounds):
             oracle.dispatch(x, s["slot_idx"], cap, quant=w.quant, group=w.quant_group or None,
                             t_begin=b, t_end=e, recv_x=recv, recv_scales=scales,
@@ -184,7 +193,8 @@ def cpu_baseline(w, idx, wts, budget_s=12.0):
                 oracle.combine_q(yc, ys, w.combine_quant, w.combine_group, wts, s["slot_idx"],
                                  t_begin=b, t_end=e, out=out)
             else:
-                oracle.combine(y, wts, s["slot_idx"], t_begin=b, t_end=e, out=out)
+                oracle.combine(y, ones if w.non_expand else wts, s["slot_idx"], t_begin=b,
+                               t_end=e, out=out)
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
@@ -298,7 +308,7 @@ def main():
                     expert_alignment=w.expert_alignment, quant=w.quant,
                     quant_group=w.quant_group if w.quant else 0, num_sources=w.num_sources,
                     scale_mode=w.scale_mode, combine_quant=w.combine_quant,
-                    combine_group=w.combine_group)
+                    combine_group=w.combine_group, non_expand=w.non_expand)
     cap = ep.ep_recv_capacity(cfg, N)
     G = cfg.num_groups
     rounds = W.round_ranges(N, w.rounds)
@@ -363,8 +373,8 @@ def main():
                        ep.bind_dispatch(s["h"], s["x"], s["recv"], s["scales"], b, e,
                                         stream=stream)) for b, e in rounds]
         calls += [(stage_names.index("combine"),
-                   ep.bind_combine(s["h"], s["y"], s["wts"], s["out"], b, e, stream=stream,
-                                   y_scales=s["y_scales"]))
+                   ep.bind_combine(s["h"], s["y"], None if w.non_expand else s["wts"], s["out"],
+                                   b, e, stream=stream, y_scales=s["y_scales"]))
                   for b, e in rounds]
         s["calls"] = calls
         s["lay_done"] = torch.cuda.Event()

@@ -44,7 +44,7 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 struct Carve {
     int64_t ctrl, psum_expert, psum_rank, num_unaligned, recv_list, topk, slot, meta, hist,
-        acc, src_acc, src_base, src_psum, total;
+        acc, src_acc, src_base, src_psum, rank_ids, ne_scratch, total;
 };
 
 int num_sources(const ep_config& c) { return c.num_sources > 1 ? c.num_sources : 1; }
@@ -54,10 +54,19 @@ int num_nodes(const ep_config& c)
     return c.ranks_per_node > 0 ? (c.num_ranks + c.ranks_per_node - 1) / c.ranks_per_node : 0;
 }
 
-int64_t max_slots_for(const ep_config& c, int64_t tokens)
+// Rows of the expert-level layout (the source metadata array holds them).
+int64_t expert_rows_for(const ep_config& c, int64_t tokens)
 {
     if (c.expert_capacity > 0) return (int64_t)c.num_experts * c.expert_capacity;
     return tokens * c.num_topk + (int64_t)c.num_experts * (c.expert_alignment - 1);
+}
+
+// Receive rows a dispatch can need: one per (token, k), plus padding, or
+// with non_expand one per (token, rank).
+int64_t max_slots_for(const ep_config& c, int64_t tokens)
+{
+    if (c.non_expand) return tokens * (c.num_topk < c.num_ranks ? c.num_topk : c.num_ranks);
+    return expert_rows_for(c, tokens);
 }
 
 ep_status check_config(const ep_config* c)
@@ -111,6 +120,10 @@ ep_status check_config(const ep_config* c)
                            c->quant_group, c->hidden);
         }
     }
+    if (c->non_expand != 0 && c->non_expand != 1)
+        return EP_FAIL(EP_ERR_INVALID_ARG, "non_expand=%d must be 0 or 1", c->non_expand);
+    if (c->non_expand && c->expert_capacity > 0)
+        return EP_FAIL(EP_ERR_INVALID_ARG, "non_expand needs expert_capacity == 0");
     if (c->combine_quant != EP_QUANT_NONE && c->combine_quant != EP_QUANT_FP8_E4M3 &&
         c->combine_quant != EP_QUANT_INT8)
         return EP_FAIL(EP_ERR_INVALID_ARG, "combine_quant=%d must be none, FP8 or int8",
@@ -125,7 +138,7 @@ ep_status check_config(const ep_config* c)
 ep_status carve(const ep_config& c, int64_t max_tokens, Carve* o)
 {
     if (max_tokens < 0) return EP_FAIL(EP_ERR_INVALID_ARG, "max_tokens=%lld < 0", (long long)max_tokens);
-    const int64_t slots = max_slots_for(c, max_tokens);
+    const int64_t slots = expert_rows_for(c, max_tokens);
     if (slots >= (int64_t)1 << 31 || max_tokens * c.num_topk >= (int64_t)1 << 31)
         return EP_FAIL(EP_ERR_INVALID_ARG, "max_tokens=%lld needs %lld receive rows (limit 2^31-1)",
                        (long long)max_tokens, (long long)slots);
@@ -156,6 +169,12 @@ ep_status carve(const ep_config& c, int64_t max_tokens, Carve* o)
         o->src_psum = take(4 * (int64_t)c.num_ranks * (P + 1));
     } else {
         o->src_acc = o->src_base = o->src_psum = -1;
+    }
+    if (c.non_expand) {
+        o->rank_ids = take(4 * max_tokens * c.num_topk);
+        o->ne_scratch = take(4 * (3 * (int64_t)c.num_ranks + 1));   // psum', counts', list'
+    } else {
+        o->rank_ids = o->ne_scratch = -1;
     }
     o->total = off;
     return EP_OK;
@@ -306,6 +325,56 @@ hipError_t launch_layout_all(const ep_handle* h, const epk::LayoutArgs& a, hipSt
     return epk::launch_layout(a, s, epk::LaunchEvents{nullptr, ev.stop});
 }
 
+// Non-expand: the expert-level layout (counts, per-expert arrays, host list)
+// followed by the layout of the derived rank-id routing, whose rows are the
+// receive rows (one per token and rank); it writes slot_idx, src_meta, the
+// row count and, through its per-"expert" prefix, psum_rank.
+hipError_t launch_layout_nonexpand(const ep_handle* h, const epk::LayoutArgs& a, hipStream_t s,
+                                   epk::LaunchEvents ev)
+{
+    hipError_t e = launch_layout_all(h, a, s, epk::LaunchEvents{ev.start, nullptr});
+    if (e != hipSuccess) return e;
+    epk::RankIdArgs ra;
+    ra.topk = a.topk;
+    ra.num_tokens = a.num_tokens;
+    ra.K = a.K;
+    ra.E = a.E;
+    ra.nle = a.nle;
+    ra.rank_ids = h->at<int32_t>(h->cv.rank_ids);
+    e = epk::launch_rank_ids(ra, s);
+    if (e != hipSuccess) return e;
+    epk::LayoutArgs b = a;
+    int32_t* scratch = h->at<int32_t>(h->cv.ne_scratch);
+    b.topk = ra.rank_ids;
+    b.topk_clone = ra.rank_ids;            // rewrites the same values
+    b.E = a.R;
+    b.nle = 1;
+    b.nle_magic = 0;
+    b.ranks_per_node = 0;
+    b.rpn_magic = 0;
+    b.nodes = 0;
+    b.A = 1;
+    b.counts_as_prefix = 0;
+    b.cap = 0;
+    b.psum_expert = a.psum_rank;           // the rank partitions of the receive rows
+    b.psum_rank = scratch;                 // [R+1] (same values)
+    b.num_unaligned = scratch + a.R + 1;   // [R]
+    b.recv_list = scratch + 2 * a.R + 1;   // [R]
+    b.out_per_rank = nullptr;
+    b.out_per_node = nullptr;
+    b.out_per_expert = nullptr;
+    b.out_in_rank = nullptr;
+    b.in_rank_words = false;
+    return epk::launch_layout(b, s, epk::LaunchEvents{nullptr, ev.stop});
+}
+
+hipError_t launch_layout_any(const ep_handle* h, const epk::LayoutArgs& a, hipStream_t s,
+                             epk::LaunchEvents ev)
+{
+    return h->cfg.non_expand ? launch_layout_nonexpand(h, a, s, ev)
+                             : launch_layout_all(h, a, s, ev);
+}
+
 }  // namespace
 
 extern "C" {
@@ -389,7 +458,7 @@ ep_status ep_get_layout(ep_handle* h, const int32_t* d_topk_idx, int64_t num_tok
                                d_is_token_in_rank, &a);
     if (st != EP_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    EP_HIP(launch_layout_all(h, a, s, h->take_events()));
+    EP_HIP(launch_layout_any(h, a, s, h->take_events()));
     h->num_tokens = num_tokens;
     h->host_slots = -1;
     if (do_cpu_sync) {
@@ -439,14 +508,49 @@ ep_status ep_layout_dispatch(ep_handle* h, const int32_t* d_topk_idx, int64_t nu
     if (st != EP_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const epk::LaunchEvents ev = h->take_events();
-    if (num_sources(h->cfg) == 1 && epk::route_dispatch_fits(la)) {
+    if (num_sources(h->cfg) == 1 && !h->cfg.non_expand && epk::route_dispatch_fits(la)) {
         EP_HIP(epk::launch_route_dispatch(la, da, s, ev));
     } else {
-        EP_HIP(launch_layout_all(h, la, s, epk::LaunchEvents{ev.start, nullptr}));
+        EP_HIP(launch_layout_any(h, la, s, epk::LaunchEvents{ev.start, nullptr}));
         EP_HIP(epk::launch_dispatch(da, s, epk::LaunchEvents{nullptr, ev.stop}));
     }
     h->num_tokens = num_tokens;
     h->host_slots = -1;
+    return EP_OK;
+}
+
+ep_status ep_dispatch_topk(const ep_handle* h, const float* d_topk_weights, int64_t token_begin,
+                           int64_t token_end, int32_t* d_recv_topk_idx, float* d_recv_topk_weights,
+                           int64_t recv_capacity_rows, void* stream)
+{
+    if (!h) return EP_FAIL(EP_ERR_INVALID_ARG, "handle is NULL");
+    if (!h->cfg.non_expand) return EP_FAIL(EP_ERR_INVALID_ARG, "ep_dispatch_topk needs non_expand");
+    if (h->num_tokens < 0) return EP_FAIL(EP_ERR_STATE, "ep_get_layout has not run on this handle");
+    if (token_begin < 0 || token_begin > token_end || token_end > h->num_tokens)
+        return EP_FAIL(EP_ERR_INVALID_ARG, "token range [%lld,%lld) outside [0,%lld]",
+                       (long long)token_begin, (long long)token_end, (long long)h->num_tokens);
+    if (recv_capacity_rows < 0) return EP_FAIL(EP_ERR_INVALID_ARG, "recv_capacity_rows < 0");
+    if (d_recv_topk_weights && !d_topk_weights)
+        return EP_FAIL(EP_ERR_INVALID_ARG, "recv_topk_weights needs topk_weights");
+    if (!aligned(d_topk_weights, 4) || !aligned(d_recv_topk_idx, 4) ||
+        !aligned(d_recv_topk_weights, 4))
+        return EP_FAIL(EP_ERR_INVALID_ARG, "arrays must be 4-byte aligned");
+    if (h->host_slots >= 0 && h->host_slots > recv_capacity_rows)
+        return EP_FAIL(EP_ERR_CAPACITY, "layout needs %lld receive rows, capacity is %lld",
+                       (long long)h->host_slots, (long long)recv_capacity_rows);
+    epk::RecvTopkArgs a;
+    a.topk = h->at<int32_t>(h->cv.topk);
+    a.slot_idx = h->at<int32_t>(h->cv.slot);
+    a.weights = d_topk_weights;
+    a.t_begin = token_begin;
+    a.t_end = token_end;
+    a.K = h->cfg.num_topk;
+    a.nle = h->cfg.num_experts / h->cfg.num_ranks;
+    a.capacity = recv_capacity_rows;
+    a.recv_topk_idx = d_recv_topk_idx;
+    a.recv_topk_weights = d_recv_topk_weights;
+    a.flags = h->at<uint32_t>(h->cv.ctrl) + epk::kCtrlFlags;
+    EP_HIP(epk::launch_recv_topk(a, static_cast<hipStream_t>(stream), h->take_events()));
     return EP_OK;
 }
 
@@ -461,8 +565,8 @@ ep_status ep_combine(const ep_handle* h, const void* d_y, const float* d_y_scale
                        (long long)token_begin, (long long)token_end, (long long)h->num_tokens);
     if (y_rows < 0) return EP_FAIL(EP_ERR_INVALID_ARG, "y_rows < 0");
     if (token_end > token_begin) {
-        if (!d_out || !d_topk_weights || (y_rows > 0 && !d_y))
-            return EP_FAIL(EP_ERR_INVALID_ARG, "y, topk_weights or out is NULL");
+        if (!d_out || (y_rows > 0 && !d_y))
+            return EP_FAIL(EP_ERR_INVALID_ARG, "y or out is NULL");
         if ((d_y && !aligned(d_y, 16)) || !aligned(d_out, 16) || !aligned(d_topk_weights, 4))
             return EP_FAIL(EP_ERR_INVALID_ARG,
                            "y and out must be 16-byte aligned, topk_weights 4-byte aligned");

@@ -96,7 +96,7 @@ __global__ __launch_bounds__(kBlock) void k_combine(CombineArgs a, int NV, int N
     // one lane-parallel load of the K slots and weights (lane k holds entry
     // k), broadcast to scalars: a single round trip for any K
     const int sv = (lane < K) ? a.slot_idx[t * K + lane] : -1;
-    const float wl = (lane < K) ? a.weights[t * K + lane] : 0.0f;
+    const float wl = (lane < K) ? (a.weights ? a.weights[t * K + lane] : 1.0f) : 0.0f;
     int slot[KMAX];
     float wk[KMAX];
     bool oob = false;

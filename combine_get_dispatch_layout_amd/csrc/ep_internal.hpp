@@ -1,5 +1,6 @@
 // Internal interface between the C-ABI host runtime (api.cpp) and the HIP
-// kernels (layout.hip, dispatch.hip, fused.hip, sources.hip, combine.hip).
+// kernels (layout.hip, dispatch.hip, fused.hip, sources.hip, nonexpand.hip,
+// combine.hip).
 // gfx950 only.
 #pragma once
 
@@ -77,6 +78,28 @@ struct DispatchArgs {
     uint32_t* flags;
 };
 
+// Non-expand layout: the derived routing (rank of each entry, repeats of a
+// rank in a row masked).
+struct RankIdArgs {
+    const int32_t* topk;        // [N,K] caller's routing
+    int64_t num_tokens;
+    int K, E, nle;
+    int32_t* rank_ids;          // [N,K] out
+};
+
+// Non-expand per-row routing (recv_topk_idx / recv_topk_weights).
+struct RecvTopkArgs {
+    const int32_t* topk;        // [N,K] the handle's clone
+    const int32_t* slot_idx;    // [N,K] non-expand rows (-1: none)
+    const float* weights;       // [N,K] (may be NULL when recv_topk_weights is)
+    int64_t t_begin, t_end;
+    int K, nle;
+    int64_t capacity;
+    int32_t* recv_topk_idx;     // [capacity,K] (nullable)
+    float* recv_topk_weights;   // [capacity,K] (nullable)
+    uint32_t* flags;
+};
+
 // Per-source counts of a batch of P stacked source ranks.
 struct SourceArgs {
     const int32_t* topk;        // [P*Ns, K]
@@ -93,7 +116,7 @@ struct CombineArgs {
     const float* y_scales;      // [y_rows, H/ygroup] when yquant != 0
     int yquant, ygroup;         // 0 bf16, 1 E4M3FN, 2 int8; elements per scale
     int64_t y_rows;
-    const float* weights;       // [N,K]
+    const float* weights;       // [N,K]; NULL: every weight is 1
     const int32_t* slot_idx;    // [N,K]
     int64_t t_begin, t_end;
     int H, K;
@@ -132,6 +155,8 @@ hipError_t launch_layout(const LayoutArgs& a, hipStream_t s, LaunchEvents ev = {
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s, LaunchEvents ev = {});
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s, LaunchEvents ev = {});
 hipError_t launch_sources(const SourceArgs& a, hipStream_t s, LaunchEvents ev = {});
+hipError_t launch_rank_ids(const RankIdArgs& a, hipStream_t s, LaunchEvents ev = {});
+hipError_t launch_recv_topk(const RecvTopkArgs& a, hipStream_t s, LaunchEvents ev = {});
 // Layout + dispatch of the whole batch in one launch (small batches).
 bool route_dispatch_fits(const LayoutArgs& la);
 hipError_t launch_route_dispatch(const LayoutArgs& la, const DispatchArgs& da, hipStream_t s,

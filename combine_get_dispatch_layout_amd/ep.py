@@ -22,8 +22,8 @@ EP_FLAG_BAD_EXPERT_ID, EP_FLAG_RECV_CAPACITY, EP_FLAG_Y_ROWS = 1, 2, 4
 
 # Every symbol include/ep.h declares.
 SYMBOLS = ("ep_workspace_size", "ep_recv_capacity", "ep_handle_init", "ep_handle_free",
-           "ep_get_layout", "ep_dispatch", "ep_layout_dispatch", "ep_combine",
-           "ep_quantize_rows", "ep_set_kernel_events", "ep_handle_get_view", "ep_check_error", "ep_status_str", "ep_last_error_message")
+           "ep_get_layout", "ep_dispatch", "ep_layout_dispatch", "ep_dispatch_topk",
+           "ep_combine", "ep_quantize_rows", "ep_set_kernel_events", "ep_handle_get_view", "ep_check_error", "ep_status_str", "ep_last_error_message")
 
 
 class ep_config(ctypes.Structure):
@@ -33,7 +33,8 @@ class ep_config(ctypes.Structure):
                 ("quant", ctypes.c_int32), ("quant_group", ctypes.c_int32),
                 ("counts_as_prefix", ctypes.c_int32), ("expert_capacity", ctypes.c_int32),
                 ("num_sources", ctypes.c_int32), ("scale_mode", ctypes.c_int32),
-                ("combine_quant", ctypes.c_int32), ("combine_group", ctypes.c_int32)]
+                ("combine_quant", ctypes.c_int32), ("combine_group", ctypes.c_int32),
+                ("non_expand", ctypes.c_int32)]
 
 
 class ep_handle_view(ctypes.Structure):
@@ -75,6 +76,7 @@ def lib():
         L.ep_layout_dispatch.argtypes = [P, P, I64, P, P, P, P, P, P, P, I64, P]
         L.ep_combine.argtypes = [P, P, P, I64, P, I64, I64, P, P]
         L.ep_quantize_rows.argtypes = [P, P, I64, P, P, P]
+        L.ep_dispatch_topk.argtypes = [P, P, I64, I64, P, P, I64, P]
         L.ep_set_kernel_events.argtypes = [P, P, P]
         L.ep_handle_get_view.argtypes = [P, P]
         L.ep_check_error.argtypes = [P, P, P]
@@ -83,7 +85,8 @@ def lib():
         L.ep_last_error_message.argtypes = []
         L.ep_last_error_message.restype = ctypes.c_char_p
         for name in ("ep_workspace_size", "ep_recv_capacity", "ep_handle_init", "ep_get_layout",
-                     "ep_dispatch", "ep_layout_dispatch", "ep_combine", "ep_quantize_rows", "ep_set_kernel_events", "ep_handle_get_view",
+                     "ep_dispatch", "ep_layout_dispatch", "ep_combine", "ep_quantize_rows",
+                     "ep_dispatch_topk", "ep_set_kernel_events", "ep_handle_get_view",
                      "ep_check_error"):
             getattr(L, name).restype = I32
         _lib = L
@@ -127,12 +130,14 @@ class Config:
     scale_mode: int = EP_SCALE_FP32
     combine_quant: int = EP_QUANT_NONE
     combine_group: int = 0
+    non_expand: bool = False
 
     def c(self):
         return ep_config(self.hidden, self.num_topk, self.num_experts, self.num_ranks,
                          self.ranks_per_node, self.expert_alignment, self.quant, self.quant_group,
                          int(bool(self.counts_as_prefix)), self.expert_capacity, self.num_sources,
-                         self.scale_mode, self.combine_quant, self.combine_group)
+                         self.scale_mode, self.combine_quant, self.combine_group,
+                         int(bool(self.non_expand)))
 
     @property
     def num_nodes(self):
@@ -337,17 +342,39 @@ def ep_combine(h: Handle, y: torch.Tensor, topk_weights: torch.Tensor, out: torc
     topk_weights fp32 [N,K]; out bf16 [N,H]."""
     cfg = h.cfg
     _check_y(cfg, y, y_scales)
-    if topk_weights.dtype != torch.float32 or topk_weights.dim() != 2 \
-            or topk_weights.shape[1] != cfg.num_topk:
-        raise ValueError("topk_weights must be fp32 [N, num_topk]")
+    if topk_weights is not None and (topk_weights.dtype != torch.float32
+                                     or topk_weights.dim() != 2
+                                     or topk_weights.shape[1] != cfg.num_topk):
+        raise ValueError("topk_weights must be fp32 [N, num_topk] or None (weights of 1)")
     if out.dtype != torch.bfloat16 or out.dim() != 2 or out.shape[1] != cfg.hidden:
         raise ValueError("out must be bf16 [N, hidden]")
     token_end = out.shape[0] if token_end is None else token_end
-    if not 0 <= token_begin <= token_end <= min(out.shape[0], topk_weights.shape[0]):
+    n_w = out.shape[0] if topk_weights is None else topk_weights.shape[0]
+    if not 0 <= token_begin <= token_end <= min(out.shape[0], n_w):
         raise ValueError("token range outside out / topk_weights")
     _check(lib().ep_combine(h.ptr, _ptr(y), _ptr(y_scales), y.shape[0], _ptr(topk_weights),
                             token_begin, token_end, _ptr(out), _stream(out.device)))
     return out
+
+
+def ep_dispatch_topk(h: Handle, topk_weights: Optional[torch.Tensor], recv_topk_idx=None,
+                     recv_topk_weights=None, token_begin=0, token_end=None, rows=None):
+    """Non-expand: per received row the local expert ids (int32 [rows, K]) and
+    weights (fp32 [rows, K]).  Allocates the outputs (rows = the receive
+    capacity of the handle's last batch) unless given."""
+    cfg = h.cfg
+    N = ep_handle_get_view(h)["num_tokens"]
+    dev = h.workspace.device
+    rows = ep_recv_capacity(cfg, N) if rows is None else rows
+    if recv_topk_idx is None:
+        recv_topk_idx = torch.empty((rows, cfg.num_topk), dtype=torch.int32, device=dev)
+    if recv_topk_weights is None and topk_weights is not None:
+        recv_topk_weights = torch.empty((rows, cfg.num_topk), dtype=torch.float32, device=dev)
+    cap = recv_topk_idx.shape[0]
+    token_end = N if token_end is None else token_end
+    _check(lib().ep_dispatch_topk(h.ptr, _ptr(topk_weights), token_begin, token_end,
+                                  _ptr(recv_topk_idx), _ptr(recv_topk_weights), cap, _stream(dev)))
+    return recv_topk_idx, recv_topk_weights
 
 
 def ep_quantize_rows(cfg: Config, x: torch.Tensor, codes: Optional[torch.Tensor] = None,

@@ -120,6 +120,18 @@ typedef struct ep_config {
                                   codes with fp32 scales ([P5] combine int8/fp8
                                   from v2.1)                                     */
     int32_t combine_group;     /* elements per y scale: 128 or hidden           */
+    int32_t non_expand;        /* 0: one receive row per (token, k) ([P3] §3.1
+                                  do_expand).  1: one row per (token, rank
+                                  holding one of its experts), the V1 normal
+                                  dispatch of [P3] §2.1: rank r's rows are
+                                  [psum_rank[r], psum_rank[r+1]) in token
+                                  order; slot_idx[t,k] is the row of the
+                                  token's first entry on that rank, -1 for
+                                  later entries on the same rank; src_meta =
+                                  (t, that k).  psum_expert, num_unaligned and
+                                  the host list stay per expert (aligned by
+                                  expert_alignment); S is the row count.  Needs
+                                  expert_capacity == 0.                          */
 } ep_config;
 
 typedef struct ep_handle ep_handle;
@@ -158,7 +170,8 @@ ep_status ep_workspace_size(const ep_config* cfg, int64_t max_tokens, int64_t* b
 
 /* Receive rows a dispatch of num_tokens tokens can need in the worst case
  * (every pair valid, every expert fully padded): num_tokens*K + E*(A-1), or
- * E*expert_capacity in the fixed-capacity layout.
+ * E*expert_capacity in the fixed-capacity layout, or num_tokens*min(K, R)
+ * with non_expand.
  * Sizing recv_x / y with this many rows never triggers EP_ERR_CAPACITY. */
 ep_status ep_recv_capacity(const ep_config* cfg, int64_t num_tokens, int64_t* rows);
 
@@ -235,12 +248,26 @@ ep_status ep_layout_dispatch(ep_handle* h, const int32_t* d_topk_idx, int64_t nu
                              const void* d_x, void* d_recv_x, void* d_recv_scales,
                              int64_t recv_capacity_rows, void* stream);
 
+/* Non-expand only: the routing of each received row ([P3] §2.1
+ * recv_topk_idx / recv_topk_weights), for tokens [token_begin, token_end):
+ * row s of (t, rank r) gets, for every k, the local expert id idx[t,k] -
+ * r*nle and the weight d_topk_weights[t,k] where expert idx[t,k] is on r,
+ * else -1 and 0.  d_recv_topk_idx int32 [recv_capacity_rows, K] and
+ * d_recv_topk_weights fp32 [recv_capacity_rows, K] may each be NULL (the
+ * weights output needs d_topk_weights fp32 [num_tokens, K]).  Rows beyond
+ * the capacity are skipped and flagged. */
+ep_status ep_dispatch_topk(const ep_handle* h, const float* d_topk_weights, int64_t token_begin,
+                           int64_t token_end, int32_t* d_recv_topk_idx, float* d_recv_topk_weights,
+                           int64_t recv_capacity_rows, void* stream);
+
 /* a4: combine ([P2] API table: the paired inverse of dispatch).
  *   d_y: bf16 [y_rows, H] expert outputs in receive-row order, or with
  *   combine_quant set their E4M3FN / int8 codes [y_rows, H] and d_y_scales
  *   fp32 [y_rows, H/combine_group] (element = code * scale; NULL iff
  *   combine_quant == EP_QUANT_NONE);
- *   d_topk_weights: fp32 [num_tokens, K];  d_out: bf16 [num_tokens, H].
+ *   d_topk_weights: fp32 [num_tokens, K], or NULL for weights of 1 (the
+ *   non-expand combine, whose rank rows already carry the weights);
+ *   d_out: bf16 [num_tokens, H].
  *   For t in [token_begin, token_end): out[t] = bf16_rne( sum over k with a
  *   slot, k ascending, of w[t,k] * y[slot] ), accumulated in fp32 with fused
  *   multiply-add.  Masked entries contribute nothing; an all-masked row is

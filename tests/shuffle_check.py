@@ -31,11 +31,15 @@ def config_of(w: W.Workload, counts_as_prefix=False):
                      quant_group=w.quant_group if w.quant else 0,
                      counts_as_prefix=counts_as_prefix, expert_capacity=w.expert_capacity,
                      num_sources=w.num_sources, scale_mode=w.scale_mode,
-                     combine_quant=w.combine_quant, combine_group=w.combine_group)
+                     combine_quant=w.combine_quant, combine_group=w.combine_group,
+                     non_expand=w.non_expand)
 
 
 def oracle_slots(w: W.Workload, idx):
-    """The oracle's slot assignment for the workload's layout mode."""
+    """The oracle's slot assignment for the workload's layout mode (the
+    receive rows: per (token, rank) with non_expand)."""
+    if w.non_expand:
+        return oracle.slots_nonexpand(idx, w.num_experts, w.num_ranks)
     if w.expert_capacity > 0:
         return oracle.slots_fixed(idx, w.num_experts, w.num_ranks, w.expert_capacity)
     return oracle.slots(idx, w.num_experts, w.num_ranks, w.expert_alignment)
@@ -105,13 +109,17 @@ def compare_layout(run: GpuRun, idx, ref_lay, ref_slots, host_sync=True):
                               ref_lay["num_tokens_per_rdma_rank"])
     v = ep.ep_handle_get_view(run.h)
     S = ref_slots["S"]
+    # per-expert arrays: the expert-level layout (the receive layout itself
+    # with expand)
+    ref_exp = oracle.slots(idx, w.num_experts, w.num_ranks, w.expert_alignment) \
+        if w.non_expand else ref_slots
     if host_sync:
         assert lay["num_recv_slots"] == S == v["num_recv_slots"]
     else:
         assert v["num_recv_slots"] == -1
-    assert np.array_equal(v["psum_expert"].cpu().numpy(), ref_slots["psum_expert"])
+    assert np.array_equal(v["psum_expert"].cpu().numpy(), ref_exp["psum_expert"])
     assert np.array_equal(v["psum_rank"].cpu().numpy(), ref_slots["psum_rank"])
-    assert np.array_equal(v["num_unaligned"].cpu().numpy(), ref_slots["num_unaligned"])
+    assert np.array_equal(v["num_unaligned"].cpu().numpy(), ref_exp["num_unaligned"])
     assert np.array_equal(v["slot_idx"].cpu().numpy(), ref_slots["slot_idx"])
     assert np.array_equal(v["src_meta"][:S].cpu().numpy(), ref_slots["src_meta"])
     assert np.array_equal(v["topk_idx"].cpu().numpy(), idx)
@@ -124,7 +132,7 @@ def compare_layout(run: GpuRun, idx, ref_lay, ref_slots, host_sync=True):
     else:
         assert "psum_source_rank" not in v
     if host_sync:
-        assert lay["num_recv_tokens_per_expert_list"] == expected_host_list(w, ref_slots)
+        assert lay["num_recv_tokens_per_expert_list"] == expected_host_list(w, ref_exp)
 
 
 def ordered_code(c, quant):
@@ -219,6 +227,14 @@ def run_and_check(w: W.Workload, device="cuda", rounds=None, seed_x=None, seed_y
                                            group=w.quant_group or None, scale_mode=w.scale_mode)
     ncode = compare_dispatch(run, ref_recv, ref_scales, ref_slots)
     stats = dict(S=ref_slots["S"], code_diffs=ncode)
+    if w.non_expand:
+        ri, rw = ep.ep_dispatch_topk(run.h, run.wts, rows=run.cap)
+        ref_ri, ref_rw = oracle.recv_topk(idx, wts, ref_slots["src_meta"], w.num_experts,
+                                          w.num_ranks)
+        S = ref_slots["S"]
+        assert np.array_equal(ri[:S].cpu().numpy(), ref_ri)
+        assert np.array_equal(rw[:S].cpu().numpy().view(np.uint32), ref_rw.view(np.uint32))
+        assert ep.ep_check_error(run.h) == (ep.EP_OK, 0)
     if check_combine:
         S = ref_slots["S"]
         y = W.activations(max(S, 1), w.hidden,
@@ -232,13 +248,20 @@ def run_and_check(w: W.Workload, device="cuda", rounds=None, seed_x=None, seed_y
             ref_out = oracle.combine_q(cq, cs, w.combine_quant, w.combine_group, wts,
                                        ref_slots["slot_idx"])
             yval = quantised_values(cq, cs, w.combine_quant, w.combine_group)
+        elif w.non_expand:
+            # rank rows already weighted on the expert side: unit weights
+            for b, e in run.rounds:
+                ep.ep_combine(run.h, y, None, run.out, b, e)
+            ref_out = oracle.combine(y_bits, np.ones_like(wts), ref_slots["slot_idx"])
+            yval = bf16_values(y_bits)
         else:
             run.combine(y)
             ref_out = oracle.combine(y_bits, wts, ref_slots["slot_idx"])
             yval = bf16_values(y_bits)
         st, flags = ep.ep_check_error(run.h)
         assert st == ep.EP_OK and flags == 0
-        stats["combine_not_bit_identical"] = compare_combine(bits16(run.out), ref_out, yval, wts,
-                                                             ref_slots["slot_idx"], w.num_topk)
+        stats["combine_not_bit_identical"] = compare_combine(
+            bits16(run.out), ref_out, yval, np.ones_like(wts) if w.non_expand else wts,
+            ref_slots["slot_idx"], w.num_topk)
     stats["run"] = run
     return stats

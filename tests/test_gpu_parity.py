@@ -483,3 +483,28 @@ def test_quantize_rows(cq, cg, H, sm):
     d = np.abs(ordered_code(codes.view(torch.uint8).cpu().numpy(), cq)
                - ordered_code(rc.view(np.uint8), cq))
     assert d.max() <= 1
+
+
+# Non-expand dispatch: one receive row per (token, rank), the per-row local
+# routing, and the unit-weight combine of rank rows; every layout path.
+@pytest.mark.parametrize("args", [
+    dict(N=128, H=7168, E=256, R=16, K=8, quant=W.QUANT_FP8, group=128),    # one block
+    dict(N=777, H=1032, E=128, R=16, K=8, A=4, mask=0.1),                   # fused 16 waves
+    dict(N=3000, H=256, E=64, R=8, K=6),                                    # count + finish
+    dict(N=9000, H=64, E=256, R=32, K=8, mask=0.05),                        # count + scan
+    dict(N=300, H=264, E=1024, R=1024, K=16, rpn=3),                        # K=16, R=E
+    dict(N=500, H=512, E=64, R=1, K=8),                                     # one rank
+])
+def test_non_expand(args):
+    w = _custom(**args).scaled(non_expand=True)
+    _say(f"[parity] non-expand {args}")
+    run_and_check(w)
+
+
+def test_non_expand_group_limited_one_call_and_sources():
+    """The group-limited gating workload (reduced) through the one-call form
+    and with stacked sources."""
+    w = W.WORKLOADS["deepseek_v3_group_limited"].scaled(num_tokens=1024, hidden=1024)
+    _say("[parity] non-expand group-limited one call")
+    run_and_check(w, fused=True)
+    run_and_check(w.scaled(num_sources=8))
