@@ -387,15 +387,18 @@ def main():
     calls_per_step = len(stage_of)
     hev = HipEvents(2 * calls_per_step * args.steps)
 
+    # a short run still times every stage: the rotation period shrinks
+    every = max(1, min(args.time_every, args.steps // nstages))
+
     def armed(i, j):
         """Whether call j of timed step i carries kernel events: every call of
-        every step ("all"), or, on every time_every-th step, the calls of one
+        every step ("all"), or, on every `every`-th step, the calls of one
         stage, the stages in turn."""
         if args.timing == "all":
             return True
-        if i % args.time_every:
+        if i % every:
             return False
-        return stage_of[j] == (i // args.time_every) % nstages
+        return stage_of[j] == (i // every) % nstages
 
     def issue(i, j, base):
         c = sets[i % nsets]["calls"][j][1]
@@ -498,15 +501,15 @@ def main():
                      "traffic": traffic, "algorithmic_bytes_per_launch": b_dom / launches,
                      "launches_per_step": launches},
         "stages_us": {k: v[0] * 1e6 for k, v in stages.items()},
-        "stages_us_p10_p50_p90": {k: [float(np.percentile(d, q)) * 1e6 for q in (10, 50, 90)]
-                                  for k, (d, _, _) in per_stage.items()},
+        "stages_us_p10_p50_p90": {k: ([float(np.percentile(d, q)) * 1e6 for q in (10, 50, 90)]
+                                      if len(d) else None) for k, (d, _, _) in per_stage.items()},
         "stages_GBps": {k: v[1] / v[0] / 1e9 for k, v in stages.items()},
         "+".join(moving): {"tokens_per_s": N / t_dc,
                              "GBps": b_dc / t_dc / 1e9,
                              "frac_of_peak": b_dc / t_dc / 1e9 / HBM_PEAK_GBS},
         "device_copy_GBps": copy_gbs,
         "pipeline": args.pipeline,
-        "timing": {"mode": args.timing, "every": args.time_every, "host_enqueue_ms_per_step": t_enqueue / args.steps * 1e3,
+        "timing": {"mode": args.timing, "every": every, "host_enqueue_ms_per_step": t_enqueue / args.steps * 1e3,
                    "samples_per_stage": {k: int(len(d)) for k, (d, _, _) in per_stage.items()}},
         "recv_rows": S, "valid_pairs": V,
     }
