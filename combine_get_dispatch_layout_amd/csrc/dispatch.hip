@@ -103,6 +103,17 @@ hipError_t launch_channel(const DispatchArgs& a, int NV, hipStream_t s, LaunchEv
     return launch_w<QUANT, true, 16>(a, NV, rb, s, ev);
 }
 
+// Per-group scales: 1, 2 or 4 vectors per lane (dispatch_quant_vpl).
+template <int QUANT>
+hipError_t launch_group(const DispatchArgs& a, int NV, int row_bytes, hipStream_t s, LaunchEvents ev)
+{
+    switch (dispatch_quant_vpl(NV)) {
+        case 2: return launch_w<QUANT, false, 2>(a, NV, row_bytes, s, ev);
+        case 4: return launch_w<QUANT, false, 4>(a, NV, row_bytes, s, ev);
+        default: return launch_w<QUANT, false, 1>(a, NV, row_bytes, s, ev);
+    }
+}
+
 // Plain scatter: long rows (>= 8 KiB) one 1 KiB piece per wave with row
 // waits; shorter rows as few waves per row as possible (up to 4 KiB per
 // wave), all stores in flight.
@@ -126,13 +137,11 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s, LaunchEvents ev
     switch (a.quant) {
         case 0: return launch_plain(a, NV, s, ev);
         case 1:
-            return channel ? launch_channel<1>(a, NV, s, ev)
-                           : launch_w<1, false, 1>(a, NV, a.H, s, ev);
+            return channel ? launch_channel<1>(a, NV, s, ev) : launch_group<1>(a, NV, a.H, s, ev);
         case 2:
-            return channel ? launch_channel<2>(a, NV, s, ev)
-                           : launch_w<2, false, 1>(a, NV, a.H, s, ev);
+            return channel ? launch_channel<2>(a, NV, s, ev) : launch_group<2>(a, NV, a.H, s, ev);
         default:
-            return launch_w<3, false, 1>(a, NV, a.H / 2, s, ev);
+            return launch_group<3>(a, NV, a.H / 2, s, ev);
     }
 }
 

@@ -109,6 +109,17 @@ hipError_t launch_rw(const LayoutArgs& la, const DispatchArgs& da, int NV, int r
 }
 
 template <int QUANT>
+hipError_t launch_group(const LayoutArgs& la, const DispatchArgs& da, int NV, int row_bytes,
+                        hipStream_t s, LaunchEvents ev)
+{
+    switch (dispatch_quant_vpl(NV)) {
+        case 2: return launch_rw<QUANT, false, 2>(la, da, NV, row_bytes, s, ev);
+        case 4: return launch_rw<QUANT, false, 4>(la, da, NV, row_bytes, s, ev);
+        default: return launch_rw<QUANT, false, 1>(la, da, NV, row_bytes, s, ev);
+    }
+}
+
+template <int QUANT>
 hipError_t launch_channel(const LayoutArgs& la, const DispatchArgs& da, int NV, hipStream_t s,
                           LaunchEvents ev)
 {
@@ -143,12 +154,12 @@ hipError_t launch_route_dispatch(const LayoutArgs& la, const DispatchArgs& da, h
         }
         case 1:
             return channel ? launch_channel<1>(la, da, NV, s, ev)
-                           : launch_rw<1, false, 1>(la, da, NV, da.H, s, ev);
+                           : launch_group<1>(la, da, NV, da.H, s, ev);
         case 2:
             return channel ? launch_channel<2>(la, da, NV, s, ev)
-                           : launch_rw<2, false, 1>(la, da, NV, da.H, s, ev);
+                           : launch_group<2>(la, da, NV, da.H, s, ev);
         default:
-            return launch_rw<3, false, 1>(la, da, NV, da.H / 2, s, ev);
+            return launch_group<3>(la, da, NV, da.H / 2, s, ev);
     }
 }
 
