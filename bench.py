@@ -1,13 +1,18 @@
 """Benchmark of the MoE token shuffle on one MI355X.
 
 One step = the whole hot path over one batch: routing layout + slot
-assignment (ep_get_layout), dispatch (ep_dispatch, per round) and combine
-(ep_combine, per round), all through the C ABI with inputs resident in HBM.
+assignment, dispatch and combine, all through the C ABI with inputs resident
+in HBM.  By default (merged) a step dispatches and combines one batch with
+ep_dispatch_overlap / ep_combine_overlap while laying out the next batch
+inside the same two launches, so in steady state each step carries one
+batch's layout, dispatch and combine.
 Default workload: the Qwen3-30B-A3B-shaped prefill (4096 tokens, hidden 2048
 bf16, 128 experts over 16 simulated ranks, top-8).
 
---pipeline picks how a step is issued: overlap (default; the layout of the
-next batch runs on a second stream), serial (one stream), fused
+--pipeline picks how a step is issued: merged (default; the layout of the
+next batch runs inside this batch's dispatch and combine launches, one
+stream), overlap (the layout of the next batch runs on a second stream),
+serial (one stream), fused
 (ep_layout_dispatch + combine, the one-call form for decode batches) or
 cached (dispatch + combine on a handle whose layout was computed once before
 the timed loop: the cached-dispatch decode loop, whose step does not include
@@ -59,9 +64,12 @@ def algorithmic_bytes(w, V, S):
     return dict(layout=int(layout), dispatch=int(dispatch), combine=int(combine))
 
 
-KERNEL_SOURCES = {"dispatch": ("dispatch.hip", "scatter.hpp"), "combine": ("combine.hip",),
+KERNEL_SOURCES = {"dispatch": ("dispatch.hip", "scatter.hpp"),
+                  "combine": ("combine.hip", "gather.hpp"),
                   "layout": ("layout.hip", "route.hpp"),
-                  "layout_dispatch": ("fused.hip", "route.hpp", "scatter.hpp")}
+                  "layout_dispatch": ("fused.hip", "route.hpp", "scatter.hpp"),
+                  "dispatch_layout": ("overlap.hip", "scatter.hpp", "route.hpp"),
+                  "combine_layout": ("overlap.hip", "gather.hpp", "route.hpp")}
 
 
 def kernel_source_hash(kernel):
@@ -101,7 +109,8 @@ def _counter_rows(path, counter):
 
 
 KERNEL_SYMBOLS = {"dispatch": "k_dispatch<", "combine": "k_combine<",
-                  "layout_dispatch": "k_route_dispatch<"}
+                  "layout_dispatch": "k_route_dispatch<",
+                  "dispatch_layout": "k_dispatch_layout<", "combine_layout": "k_combine_layout<"}
 
 
 def traffic_summary(fetch_csv, write_csv, workload, pipeline):
@@ -125,6 +134,10 @@ def traffic_summary(fetch_csv, write_csv, workload, pipeline):
     rows = sum(len(set(r[r >= 0].tolist())) for r in ranks)   # non-expand rows
     nbytes = algorithmic_bytes(w, V, rows)
     nbytes["layout_dispatch"] = nbytes["layout"] + nbytes["dispatch"]
+    # the launches that also lay out the next batch are priced at their
+    # dispatch / combine bytes alone
+    nbytes["dispatch_layout"] = nbytes["dispatch"]
+    nbytes["combine_layout"] = nbytes["combine"]
     bench_args = f"--workload {workload} --pipeline {pipeline} --steps 4 --warmup 2 --no-cpu-baseline"
     command = [f"rocprofv3 --pmc FETCH_SIZE -f csv -d <dir> -o fetch -- python3 bench.py {bench_args}",
                f"rocprofv3 --pmc WRITE_SIZE -f csv -d <dir> -o write -- python3 bench.py {bench_args}",
@@ -257,10 +270,13 @@ def main():
                     help=">1: read the batch as this many stacked source ranks (receive order "
                          "(source, token, k) plus the per-source counts)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--pipeline", choices=("overlap", "serial", "fused", "cached"),
-                    default="overlap",
-                    help="overlap: batch i+1's layout runs on a second stream during batch i's "
-                         "dispatch and combine; serial: one stream, one stage after another; "
+    ap.add_argument("--pipeline", choices=("merged", "overlap", "serial", "fused", "cached"),
+                    default="merged",
+                    help="merged: batch i+1's layout runs inside batch i's dispatch and "
+                         "combine launches (ep_dispatch_overlap / ep_combine_overlap), one "
+                         "stream; overlap: batch i+1's layout runs on a second stream during "
+                         "batch i's dispatch and combine; serial: one stream, one stage after "
+                         "another; "
                          "fused: ep_layout_dispatch (layout + dispatch in one call) then "
                          "combine, one stream (one round only); cached: the layout is computed "
                          "once per buffer set and each step is dispatch + combine on the cached "
@@ -350,11 +366,27 @@ def main():
     # overlap: the layout of batch i+1 runs on a second stream while batch i
     # is dispatched and combined (double-batch overlap); default priority
     lay_stream = torch.cuda.Stream() if pl == "overlap" else stream
-    stage_names = {"fused": ["layout_dispatch", "combine"], "cached": ["dispatch", "combine"]}.get(
-        pl, ["layout", "dispatch", "combine"])
+    stage_names = {"fused": ["layout_dispatch", "combine"], "cached": ["dispatch", "combine"],
+                   "merged": ["dispatch", "combine"]}.get(pl, ["layout", "dispatch", "combine"])
     stage_bytes = dict(nbytes, layout_dispatch=nbytes["layout"] + nbytes["dispatch"])
-    for s in sets:
+    for si, s in enumerate(sets):
         calls = []   # (stage index, bound call) in issue order
+        if pl == "merged":
+            # this set's batch is dispatched and combined while the next set's
+            # batch (the next step's) is laid out inside the same launches
+            t = sets[(si + 1) % nsets]
+            calls.append((0, ep.bind_dispatch_overlap(s["h"], s["x"], s["recv"], s["scales"], 0, N,
+                                                      t["h"], t["topk"], t["per_rank"],
+                                                      t["per_node"], t["per_expert"], t["in_rank"],
+                                                      stream=stream)))
+            calls.append((1, ep.bind_combine_overlap(s["h"], s["y"],
+                                                     None if w.non_expand else s["wts"], s["out"],
+                                                     0, N, t["h"], stream=stream,
+                                                     y_scales=s["y_scales"])))
+            s["calls"] = calls
+            s["lay_done"] = torch.cuda.Event()
+            s["main_done"] = torch.cuda.Event()
+            continue
         if pl == "fused":
             calls.append((0, ep.bind_layout_dispatch(s["h"], s["topk"], s["x"], s["recv"],
                                                      s["scales"], s["per_rank"], s["per_node"],
@@ -420,11 +452,29 @@ def main():
             issue(i, j, base)
         s["main_done"].record(stream)
 
+    if pl == "merged":
+        if len(rounds) != 1:
+            sys.exit("--pipeline merged overlaps whole batches: the workload must have one round")
+        # the first batch's layout; every later one is laid out one step ahead
+        ep.ep_get_layout(sets[0]["h"], sets[0]["topk"], sets[0]["per_rank"], sets[0]["per_node"],
+                         sets[0]["per_expert"], sets[0]["in_rank"])
+    gstep = [0]   # steps issued so far (the merged pipeline's set rotation)
+
     def run(n, timed):
         """n steps; with overlap the layout of step i+1 is issued before the
         dispatch and combine of step i, otherwise each step's calls in order."""
         def base(i):
             return 2 * calls_per_step * i if timed else None
+        if pl == "merged":
+            for i in range(n):
+                c = sets[gstep[0] % nsets]["calls"]
+                gstep[0] += 1
+                for j in range(calls_per_step):
+                    if base(i) is None or not armed(i, j):
+                        c[j][1]()
+                    else:
+                        c[j][1]((hev.ev[base(i) + 2 * j], hev.ev[base(i) + 2 * j + 1]))
+            return
         if pl == "overlap":
             layout(0, base(0))
             for i in range(n):
@@ -464,7 +514,10 @@ def main():
     t_dom, b_dom, launches = stages[dom]
     achieved = b_dom / t_dom / 1e9   # = per-launch bytes / mean per-launch time
     b_dc = sum(stages[k][1] for k in moving)
-    traffic = traffic_from_profiles(dom, w.name)
+    # the kernel that carries the stage (merged: the launch that also lays
+    # out the next batch)
+    traffic = traffic_from_profiles({"dispatch": "dispatch_layout", "combine": "combine_layout"}
+                                    .get(dom, dom) if pl == "merged" else dom, w.name)
 
     # achievable reference: a plain 1 GiB device copy
     a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -496,7 +549,13 @@ def main():
                    "quant_group": w.quant_group, "scale_mode": w.scale_mode,
                    "combine_quant": w.combine_quant, "combine_group": w.combine_group,
                    "buffer_sets": nsets},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved,
+        "roofline": {"bound": "hbm",
+                     "kernel": ({"dispatch": "k_dispatch_layout (dispatch + next batch's layout "
+                                             "count phase)",
+                                 "combine": "k_combine_layout (combine + next batch's layout "
+                                            "finish phase)"}.get(dom, dom)
+                                if pl == "merged" else dom),
+                     "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": b_dom / launches,
                      "launches_per_step": launches},

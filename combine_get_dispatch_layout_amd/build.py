@@ -17,7 +17,7 @@ LIB = os.path.join(PKG, "libep_amd.so")
 ARCH = "gfx950"
 
 SOURCES = ["layout.hip", "dispatch.hip", "fused.hip", "sources.hip", "nonexpand.hip",
-           "combine.hip", "api.cpp"]
+           "combine.hip", "overlap.hip", "api.cpp"]
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 instructions.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

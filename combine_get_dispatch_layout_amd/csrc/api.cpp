@@ -191,6 +191,11 @@ struct ep_handle {
     Carve cv;
     int64_t num_tokens;   // -1 before the first ep_get_layout
     int64_t host_slots;   // S known on the host, else -1
+    // layout counted inside a dispatch launch, to be finished inside the
+    // next ep_combine_overlap launch (see ep_dispatch_overlap)
+    bool pending = false;
+    epk::LayoutArgs pending_args;
+    epk::OverlapPlan pending_plan;
     // events armed by ep_set_kernel_events for the next call
     mutable epk::LaunchEvents armed;
 
@@ -375,6 +380,66 @@ hipError_t launch_layout_any(const ep_handle* h, const epk::LayoutArgs& a, hipSt
                              : launch_layout_all(h, a, s, ev);
 }
 
+// Validates the combine arguments and fills the kernel arguments.
+ep_status combine_args(const ep_handle* h, const void* d_y, const float* d_y_scales,
+                       int64_t y_rows, const float* d_topk_weights, int64_t token_begin,
+                       int64_t token_end, void* d_out, epk::CombineArgs* out)
+{
+    if (!h) return EP_FAIL(EP_ERR_INVALID_ARG, "handle is NULL");
+    if (h->num_tokens < 0) return EP_FAIL(EP_ERR_STATE, "ep_get_layout has not run on this handle");
+    if (h->pending) return EP_FAIL(EP_ERR_STATE, "the handle's layout is waiting for ep_combine_overlap");
+    if (token_begin < 0 || token_begin > token_end || token_end > h->num_tokens)
+        return EP_FAIL(EP_ERR_INVALID_ARG, "token range [%lld,%lld) outside [0,%lld]",
+                       (long long)token_begin, (long long)token_end, (long long)h->num_tokens);
+    if (y_rows < 0) return EP_FAIL(EP_ERR_INVALID_ARG, "y_rows < 0");
+    if (token_end > token_begin) {
+        if (!d_out || (y_rows > 0 && !d_y))
+            return EP_FAIL(EP_ERR_INVALID_ARG, "y or out is NULL");
+        if ((d_y && !aligned(d_y, 16)) || !aligned(d_out, 16) || !aligned(d_topk_weights, 4))
+            return EP_FAIL(EP_ERR_INVALID_ARG,
+                           "y and out must be 16-byte aligned, topk_weights 4-byte aligned");
+    }
+    const ep_config& c = h->cfg;
+    if (c.combine_quant == EP_QUANT_NONE && d_y_scales)
+        return EP_FAIL(EP_ERR_INVALID_ARG, "y_scales must be NULL without combine_quant");
+    if (c.combine_quant != EP_QUANT_NONE && token_end > token_begin && y_rows > 0 &&
+        (!d_y_scales || !aligned(d_y_scales, 4)))
+        return EP_FAIL(EP_ERR_INVALID_ARG, "combine_quant needs 4-byte aligned y_scales");
+    epk::CombineArgs& a = *out;
+    a.y = d_y;
+    a.y_scales = d_y_scales;
+    a.yquant = c.combine_quant;
+    a.ygroup = c.combine_group;
+    a.y_rows = y_rows;
+    a.weights = d_topk_weights;
+    a.slot_idx = h->at<int32_t>(h->cv.slot);
+    a.t_begin = token_begin;
+    a.t_end = token_end;
+    a.H = c.hidden;
+    a.K = c.num_topk;
+    a.out = d_out;
+    a.flags = h->at<uint32_t>(h->cv.ctrl) + epk::kCtrlFlags;
+    return EP_OK;
+}
+
+// The next batch's layout for the overlapped calls: the checks of
+// ep_get_layout, and which phases can run inside the launches.
+ep_status next_layout(const ep_handle* h, ep_handle* h_next, const int32_t* d_topk_next,
+                      int64_t num_tokens_next, int32_t* d_per_rank, int32_t* d_per_rdma,
+                      int32_t* d_per_expert, uint8_t* d_in_rank, epk::LayoutArgs* la,
+                      epk::OverlapPlan* plan)
+{
+    if (h_next == h) return EP_FAIL(EP_ERR_INVALID_ARG, "h_next must differ from h");
+    if (memcmp(&h->cfg, &h_next->cfg, sizeof(ep_config)) != 0)
+        return EP_FAIL(EP_ERR_INVALID_ARG, "h and h_next must have the same configuration");
+    ep_status st = layout_args(h_next, d_topk_next, num_tokens_next, d_per_rank, d_per_rdma,
+                               d_per_expert, d_in_rank, la);
+    if (st != EP_OK) return st;
+    const ep_config& c = h_next->cfg;
+    *plan = (c.non_expand || num_sources(c) > 1) ? epk::OverlapPlan{} : epk::plan_overlap(*la);
+    return EP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -461,6 +526,7 @@ ep_status ep_get_layout(ep_handle* h, const int32_t* d_topk_idx, int64_t num_tok
     EP_HIP(launch_layout_any(h, a, s, h->take_events()));
     h->num_tokens = num_tokens;
     h->host_slots = -1;
+    h->pending = false;
     if (do_cpu_sync) {
         uint32_t S = 0;
         if (h_num_recv_tokens_per_expert)
@@ -480,6 +546,7 @@ ep_status ep_dispatch(const ep_handle* h, const void* d_x, int64_t token_begin, 
 {
     if (!h) return EP_FAIL(EP_ERR_INVALID_ARG, "handle is NULL");
     if (h->num_tokens < 0) return EP_FAIL(EP_ERR_STATE, "ep_get_layout has not run on this handle");
+    if (h->pending) return EP_FAIL(EP_ERR_STATE, "the handle's layout is waiting for ep_combine_overlap");
     epk::DispatchArgs a;
     ep_status st = dispatch_args(h, h->num_tokens, d_x, token_begin, token_end, d_recv_x,
                                  d_recv_scales, recv_capacity_rows, &a);
@@ -516,6 +583,7 @@ ep_status ep_layout_dispatch(ep_handle* h, const int32_t* d_topk_idx, int64_t nu
     }
     h->num_tokens = num_tokens;
     h->host_slots = -1;
+    h->pending = false;
     return EP_OK;
 }
 
@@ -526,6 +594,7 @@ ep_status ep_dispatch_topk(const ep_handle* h, const float* d_topk_weights, int6
     if (!h) return EP_FAIL(EP_ERR_INVALID_ARG, "handle is NULL");
     if (!h->cfg.non_expand) return EP_FAIL(EP_ERR_INVALID_ARG, "ep_dispatch_topk needs non_expand");
     if (h->num_tokens < 0) return EP_FAIL(EP_ERR_STATE, "ep_get_layout has not run on this handle");
+    if (h->pending) return EP_FAIL(EP_ERR_STATE, "the handle's layout is waiting for ep_combine_overlap");
     if (token_begin < 0 || token_begin > token_end || token_end > h->num_tokens)
         return EP_FAIL(EP_ERR_INVALID_ARG, "token range [%lld,%lld) outside [0,%lld]",
                        (long long)token_begin, (long long)token_end, (long long)h->num_tokens);
@@ -558,40 +627,77 @@ ep_status ep_combine(const ep_handle* h, const void* d_y, const float* d_y_scale
                      const float* d_topk_weights, int64_t token_begin, int64_t token_end,
                      void* d_out, void* stream)
 {
+    epk::CombineArgs a;
+    ep_status st = combine_args(h, d_y, d_y_scales, y_rows, d_topk_weights, token_begin, token_end,
+                                d_out, &a);
+    if (st != EP_OK) return st;
+    EP_HIP(epk::launch_combine(a, static_cast<hipStream_t>(stream), h->take_events()));
+    return EP_OK;
+}
+
+ep_status ep_dispatch_overlap(const ep_handle* h, const void* d_x, int64_t token_begin,
+                              int64_t token_end, void* d_recv_x, void* d_recv_scales,
+                              int64_t recv_capacity_rows, ep_handle* h_next,
+                              const int32_t* d_topk_next, int64_t num_tokens_next,
+                              int32_t* d_num_tokens_per_rank, int32_t* d_num_tokens_per_rdma_rank,
+                              int32_t* d_num_tokens_per_expert, uint8_t* d_is_token_in_rank,
+                              void* stream)
+{
     if (!h) return EP_FAIL(EP_ERR_INVALID_ARG, "handle is NULL");
     if (h->num_tokens < 0) return EP_FAIL(EP_ERR_STATE, "ep_get_layout has not run on this handle");
-    if (token_begin < 0 || token_begin > token_end || token_end > h->num_tokens)
-        return EP_FAIL(EP_ERR_INVALID_ARG, "token range [%lld,%lld) outside [0,%lld]",
-                       (long long)token_begin, (long long)token_end, (long long)h->num_tokens);
-    if (y_rows < 0) return EP_FAIL(EP_ERR_INVALID_ARG, "y_rows < 0");
-    if (token_end > token_begin) {
-        if (!d_out || (y_rows > 0 && !d_y))
-            return EP_FAIL(EP_ERR_INVALID_ARG, "y or out is NULL");
-        if ((d_y && !aligned(d_y, 16)) || !aligned(d_out, 16) || !aligned(d_topk_weights, 4))
-            return EP_FAIL(EP_ERR_INVALID_ARG,
-                           "y and out must be 16-byte aligned, topk_weights 4-byte aligned");
+    if (h->pending) return EP_FAIL(EP_ERR_STATE, "the handle's layout is waiting for ep_combine_overlap");
+    epk::DispatchArgs da;
+    ep_status st = dispatch_args(h, h->num_tokens, d_x, token_begin, token_end, d_recv_x,
+                                 d_recv_scales, recv_capacity_rows, &da);
+    if (st != EP_OK) return st;
+    if (h->host_slots >= 0 && h->host_slots > recv_capacity_rows)
+        return EP_FAIL(EP_ERR_CAPACITY, "layout needs %lld receive rows, capacity is %lld",
+                       (long long)h->host_slots, (long long)recv_capacity_rows);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!h_next) {
+        EP_HIP(epk::launch_dispatch(da, s, h->take_events()));
+        return EP_OK;
     }
-    const ep_config& c = h->cfg;
-    if (c.combine_quant == EP_QUANT_NONE && d_y_scales)
-        return EP_FAIL(EP_ERR_INVALID_ARG, "y_scales must be NULL without combine_quant");
-    if (c.combine_quant != EP_QUANT_NONE && token_end > token_begin && y_rows > 0 &&
-        (!d_y_scales || !aligned(d_y_scales, 4)))
-        return EP_FAIL(EP_ERR_INVALID_ARG, "combine_quant needs 4-byte aligned y_scales");
-    epk::CombineArgs a;
-    a.y = d_y;
-    a.y_scales = d_y_scales;
-    a.yquant = c.combine_quant;
-    a.ygroup = c.combine_group;
-    a.y_rows = y_rows;
-    a.weights = d_topk_weights;
-    a.slot_idx = h->at<int32_t>(h->cv.slot);
-    a.t_begin = token_begin;
-    a.t_end = token_end;
-    a.H = c.hidden;
-    a.K = c.num_topk;
-    a.out = d_out;
-    a.flags = h->at<uint32_t>(h->cv.ctrl) + epk::kCtrlFlags;
-    EP_HIP(epk::launch_combine(a, static_cast<hipStream_t>(stream), h->take_events()));
+    epk::LayoutArgs la;
+    epk::OverlapPlan plan;
+    st = next_layout(h, h_next, d_topk_next, num_tokens_next, d_num_tokens_per_rank,
+                     d_num_tokens_per_rdma_rank, d_num_tokens_per_expert, d_is_token_in_rank, &la,
+                     &plan);
+    if (st != EP_OK) return st;
+    const epk::LaunchEvents ev = h->take_events();
+    if (plan.ok) {
+        EP_HIP(epk::launch_dispatch_layout(da, la, plan, s, ev));
+    } else {
+        EP_HIP(epk::launch_dispatch(da, s, epk::LaunchEvents{ev.start, nullptr}));
+        EP_HIP(launch_layout_any(h_next, la, s, epk::LaunchEvents{nullptr, ev.stop}));
+    }
+    h_next->num_tokens = num_tokens_next;
+    h_next->host_slots = -1;
+    h_next->pending = plan.ok && !plan.fused;
+    h_next->pending_args = la;
+    h_next->pending_plan = plan;
+    return EP_OK;
+}
+
+ep_status ep_combine_overlap(const ep_handle* h, const void* d_y, const float* d_y_scales,
+                             int64_t y_rows, const float* d_topk_weights, int64_t token_begin,
+                             int64_t token_end, void* d_out, ep_handle* h_next, void* stream)
+{
+    epk::CombineArgs ca;
+    ep_status st = combine_args(h, d_y, d_y_scales, y_rows, d_topk_weights, token_begin, token_end,
+                                d_out, &ca);
+    if (st != EP_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!h_next || !h_next->pending) {
+        EP_HIP(epk::launch_combine(ca, s, h->take_events()));
+        return EP_OK;
+    }
+    if (h_next == h) return EP_FAIL(EP_ERR_INVALID_ARG, "h_next must differ from h");
+    if (memcmp(&h->cfg, &h_next->cfg, sizeof(ep_config)) != 0)
+        return EP_FAIL(EP_ERR_INVALID_ARG, "h and h_next must have the same configuration");
+    EP_HIP(epk::launch_combine_layout(ca, h_next->pending_args, h_next->pending_plan, s,
+                                      h->take_events()));
+    h_next->pending = false;
     return EP_OK;
 }
 

@@ -42,28 +42,7 @@ constexpr int kWavesPerBlock = kBlock / kWave;
 template <int QUANT, bool CHANNEL, int VPL, int KMAX, bool ROW_WAIT>
 __global__ __launch_bounds__(kBlock) void k_dispatch(DispatchArgs a, int NV, int NC)
 {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int item = blockIdx.x * kWavesPerBlock + wv;
-    const int64_t t = a.t_begin + item / NC;
-    const int c = item % NC;
-    if (t >= a.t_end) return;
-    const int vbase = c * (kWave * VPL) + lane;
-    u32x4 d[VPL];
-    load_chunk<VPL>(a, t, vbase, NV, d);
-    // the token's slots as one batch of scalar loads (the slot array carries
-    // kMaxTopk words of slack, so reading KMAX words is in bounds; words past
-    // K are ignored)
-    int sl[KMAX];
-    if (a.identity) {   // row quantisation: row t to receive row t
-#pragma unroll
-        for (int k = 0; k < KMAX; ++k) sl[k] = k == 0 ? (int)t : -1;
-    } else {
-        const int32_t* srow = a.slot_idx + t * a.K;
-#pragma unroll
-        for (int k = 0; k < KMAX; ++k) sl[k] = srow[k];
-    }
-    scatter_chunk<QUANT, CHANNEL, VPL, KMAX, ROW_WAIT>(a, vbase, NV, d, sl, lane);
+    dispatch_wave<QUANT, CHANNEL, VPL, KMAX, ROW_WAIT, kWavesPerBlock>(a, NV, NC, blockIdx.x);
 }
 
 template <int QUANT, bool CHANNEL, int VPL, bool ROW_WAIT>
@@ -82,67 +61,15 @@ hipError_t launch_v(const DispatchArgs& a, int NV, hipStream_t s, LaunchEvents e
     return hipGetLastError();
 }
 
-
-template <int QUANT, bool CHANNEL, int VPL>
-hipError_t launch_w(const DispatchArgs& a, int NV, int row_bytes, hipStream_t s, LaunchEvents ev)
-{
-    return dispatch_row_wait(row_bytes) ? launch_v<QUANT, CHANNEL, VPL, true>(a, NV, s, ev)
-                                   : launch_v<QUANT, CHANNEL, VPL, false>(a, NV, s, ev);
-}
-
-// Channel scales need the whole row in one wave: smallest VPL with
-// 64*VPL >= NV.
-template <int QUANT>
-hipError_t launch_channel(const DispatchArgs& a, int NV, hipStream_t s, LaunchEvents ev)
-{
-    const int rb = a.H;   // one byte per element
-    if (NV <= 64) return launch_w<QUANT, true, 1>(a, NV, rb, s, ev);
-    if (NV <= 128) return launch_w<QUANT, true, 2>(a, NV, rb, s, ev);
-    if (NV <= 256) return launch_w<QUANT, true, 4>(a, NV, rb, s, ev);
-    if (NV <= 512) return launch_w<QUANT, true, 8>(a, NV, rb, s, ev);
-    return launch_w<QUANT, true, 16>(a, NV, rb, s, ev);
-}
-
-// Per-group scales: 1, 2 or 4 vectors per lane (dispatch_quant_vpl).
-template <int QUANT>
-hipError_t launch_group(const DispatchArgs& a, int NV, int row_bytes, hipStream_t s, LaunchEvents ev)
-{
-    switch (dispatch_quant_vpl(NV)) {
-        case 2: return launch_w<QUANT, false, 2>(a, NV, row_bytes, s, ev);
-        case 4: return launch_w<QUANT, false, 4>(a, NV, row_bytes, s, ev);
-        default: return launch_w<QUANT, false, 1>(a, NV, row_bytes, s, ev);
-    }
-}
-
-// Plain scatter: long rows (>= 8 KiB) one 1 KiB piece per wave with row
-// waits; shorter rows as few waves per row as possible (up to 4 KiB per
-// wave), all stores in flight.
-hipError_t launch_plain(const DispatchArgs& a, int NV, hipStream_t s, LaunchEvents ev)
-{
-    const int rb = a.H * 2;
-    switch (dispatch_plain_vpl(NV, rb)) {
-        case 1: return launch_w<0, false, 1>(a, NV, rb, s, ev);
-        case 2: return launch_w<0, false, 2>(a, NV, rb, s, ev);
-        case 8: return launch_w<0, false, 8>(a, NV, rb, s, ev);
-        default: return launch_w<0, false, 4>(a, NV, rb, s, ev);
-    }
-}
-
 }  // namespace
 
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s, LaunchEvents ev)
 {
-    const int NV = a.H / 8;
-    const bool channel = a.quant != 0 && a.group == a.H && a.H != 128;
-    switch (a.quant) {
-        case 0: return launch_plain(a, NV, s, ev);
-        case 1:
-            return channel ? launch_channel<1>(a, NV, s, ev) : launch_group<1>(a, NV, a.H, s, ev);
-        case 2:
-            return channel ? launch_channel<2>(a, NV, s, ev) : launch_group<2>(a, NV, a.H, s, ev);
-        default:
-            return launch_group<3>(a, NV, a.H / 2, s, ev);
-    }
+    auto launch = [&](auto q, auto ch, auto vpl, auto rw, int NV) {
+        return launch_v<decltype(q)::value, decltype(ch)::value, decltype(vpl)::value,
+                        decltype(rw)::value>(a, NV, s, ev);
+    };
+    return dispatch_shape(a, launch);
 }
 
 }  // namespace epk

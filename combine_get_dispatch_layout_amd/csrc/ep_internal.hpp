@@ -1,6 +1,6 @@
 // Internal interface between the C-ABI host runtime (api.cpp) and the HIP
 // kernels (layout.hip, dispatch.hip, fused.hip, sources.hip, nonexpand.hip,
-// combine.hip).
+// combine.hip, overlap.hip).
 // gfx950 only.
 #pragma once
 
@@ -157,6 +157,22 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s, LaunchEvents ev =
 hipError_t launch_sources(const SourceArgs& a, hipStream_t s, LaunchEvents ev = {});
 hipError_t launch_rank_ids(const RankIdArgs& a, hipStream_t s, LaunchEvents ev = {});
 hipError_t launch_recv_topk(const RecvTopkArgs& a, hipStream_t s, LaunchEvents ev = {});
+// The next batch's layout inside the current batch's dispatch and combine
+// launches (overlap.hip): which phase goes where, and the LDS each launch
+// needs for it.
+struct OverlapPlan {
+    bool ok = false;          // false: lay the next batch out on its own
+    bool fused = false;       // the whole layout in one block of the dispatch launch
+    int dispatch_blocks = 0;  // layout blocks in front of the dispatch blocks
+    int combine_blocks = 0;   // layout blocks in front of the combine blocks
+    size_t dispatch_lds = 0;
+    size_t combine_lds = 0;
+};
+OverlapPlan plan_overlap(const LayoutArgs& la);
+hipError_t launch_dispatch_layout(const DispatchArgs& da, const LayoutArgs& la,
+                                  const OverlapPlan& p, hipStream_t s, LaunchEvents ev = {});
+hipError_t launch_combine_layout(const CombineArgs& ca, const LayoutArgs& la, const OverlapPlan& p,
+                                 hipStream_t s, LaunchEvents ev = {});
 // Layout + dispatch of the whole batch in one launch (small batches).
 bool route_dispatch_fits(const LayoutArgs& la);
 hipError_t launch_route_dispatch(const LayoutArgs& la, const DispatchArgs& da, hipStream_t s,

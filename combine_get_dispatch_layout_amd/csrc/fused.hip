@@ -100,37 +100,6 @@ hipError_t launch_rd(const LayoutArgs& la, const DispatchArgs& da, int NV, hipSt
     return hipGetLastError();
 }
 
-template <int QUANT, bool CHANNEL, int VPL>
-hipError_t launch_rw(const LayoutArgs& la, const DispatchArgs& da, int NV, int row_bytes,
-                     hipStream_t s, LaunchEvents ev)
-{
-    return dispatch_row_wait(row_bytes) ? launch_rd<QUANT, CHANNEL, VPL, true>(la, da, NV, s, ev)
-                                        : launch_rd<QUANT, CHANNEL, VPL, false>(la, da, NV, s, ev);
-}
-
-template <int QUANT>
-hipError_t launch_group(const LayoutArgs& la, const DispatchArgs& da, int NV, int row_bytes,
-                        hipStream_t s, LaunchEvents ev)
-{
-    switch (dispatch_quant_vpl(NV)) {
-        case 2: return launch_rw<QUANT, false, 2>(la, da, NV, row_bytes, s, ev);
-        case 4: return launch_rw<QUANT, false, 4>(la, da, NV, row_bytes, s, ev);
-        default: return launch_rw<QUANT, false, 1>(la, da, NV, row_bytes, s, ev);
-    }
-}
-
-template <int QUANT>
-hipError_t launch_channel(const LayoutArgs& la, const DispatchArgs& da, int NV, hipStream_t s,
-                          LaunchEvents ev)
-{
-    const int rb = da.H;
-    if (NV <= 64) return launch_rw<QUANT, true, 1>(la, da, NV, rb, s, ev);
-    if (NV <= 128) return launch_rw<QUANT, true, 2>(la, da, NV, rb, s, ev);
-    if (NV <= 256) return launch_rw<QUANT, true, 4>(la, da, NV, rb, s, ev);
-    if (NV <= 512) return launch_rw<QUANT, true, 8>(la, da, NV, rb, s, ev);
-    return launch_rw<QUANT, true, 16>(la, da, NV, rb, s, ev);
-}
-
 }  // namespace
 
 bool route_dispatch_fits(const LayoutArgs& la)
@@ -142,25 +111,11 @@ bool route_dispatch_fits(const LayoutArgs& la)
 hipError_t launch_route_dispatch(const LayoutArgs& la, const DispatchArgs& da, hipStream_t s,
                                  LaunchEvents ev)
 {
-    const int NV = da.H / 8;
-    const bool channel = da.quant != 0 && da.group == da.H && da.H != 128;
-    switch (da.quant) {
-        case 0: {
-            const int rb = da.H * 2;
-            const int vpl = dispatch_plain_vpl(NV, rb);
-            if (vpl == 1) return launch_rw<0, false, 1>(la, da, NV, rb, s, ev);
-            if (vpl == 2) return launch_rw<0, false, 2>(la, da, NV, rb, s, ev);
-            return launch_rw<0, false, 4>(la, da, NV, rb, s, ev);
-        }
-        case 1:
-            return channel ? launch_channel<1>(la, da, NV, s, ev)
-                           : launch_group<1>(la, da, NV, da.H, s, ev);
-        case 2:
-            return channel ? launch_channel<2>(la, da, NV, s, ev)
-                           : launch_group<2>(la, da, NV, da.H, s, ev);
-        default:
-            return launch_group<3>(la, da, NV, da.H / 2, s, ev);
-    }
+    auto launch = [&](auto q, auto ch, auto vpl, auto rw, int NV) {
+        return launch_rd<decltype(q)::value, decltype(ch)::value, decltype(vpl)::value,
+                         decltype(rw)::value>(la, da, NV, s, ev);
+    };
+    return dispatch_shape(da, launch);
 }
 
 }  // namespace epk

@@ -54,70 +54,17 @@ __global__ void k_clear(uint32_t* w, int n)
 template <int KMAX, int WAVES>
 __global__ __launch_bounds__(WAVES * kWave) void k_fused(LayoutArgs a)
 {
-    constexpr int NT = WAVES * kWave;
     extern __shared__ __align__(16) unsigned char smem[];
-    const RouteLds L = carve_route(smem, WAVES, a.E, a.R);
-    int ids[KMAX], lr[KMAX];
-    route_block<KMAX, WAVES>(a, 0, L, ids, lr);
-    // prefix [E+1] and scan scratch [2*NT] follow the routing LDS
-    int32_t* psum = L.ncnt + a.nodes;
-    int32_t* scratch = psum + a.E + 1;
-    aligned_prefix<NT>(a, L.bhist, psum, scratch);
-    int off[KMAX];
-    bool dropped = false;
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k)
-        off[k] = ids[k] >= 0 ? final_slot(a, psum[ids[k]], lr[k], dropped) : 0;
-    flag_dropped<KMAX>(a, dropped);
-    store_slots<KMAX>(a, threadIdx.x, ids, off);
-    write_expert_arrays<NT>(a, L.bhist, psum);
-    write_padding<NT>(a, L.bhist, psum, 0, 1);
-    for (int r = threadIdx.x; r < a.R; r += NT)
-        if (a.out_per_rank) a.out_per_rank[r] = L.rcnt[r];
-    for (int n = threadIdx.x; n < a.nodes; n += NT)
-        if (a.out_per_node) a.out_per_node[n] = L.ncnt[n];
+    fused_body<KMAX, WAVES>(a, smem);
 }
 
 // ---- paths B and C: per-block routing ---------------------------------------
 
-// Writes the block histogram, the in-block ranks (into slot_idx, finished by
-// the next kernel) and adds the distinct-token counts to the accumulators.
 template <int KMAX>
 __global__ __launch_bounds__(kLayoutBlock) void k_count(LayoutArgs a)
 {
     extern __shared__ __align__(16) unsigned char smem[];
-    constexpr int WAVES = kLayoutBlock / kWave;
-    const RouteLds L = carve_route(smem, WAVES, a.E, a.R);
-    int ids[KMAX], lr[KMAX];
-    const int64_t t0 = (int64_t)blockIdx.x * kLayoutBlock;
-    route_block<KMAX, WAVES>(a, t0, L, ids, lr);
-    const int tid = threadIdx.x, K = a.K;
-    const int64_t t = t0 + tid;
-    if (t < a.num_tokens) {
-#pragma unroll
-        for (int k = 0; k < KMAX; ++k)
-            if (k < K) a.slot_idx[t * K + k] = lr[k];
-    }
-    for (int e = tid; e < a.E; e += kLayoutBlock) a.hist[(int64_t)blockIdx.x * a.E + e] = L.bhist[e];
-    for (int r = tid; r < a.R; r += kLayoutBlock)
-        if (L.rcnt[r] != 0) atomicAdd(a.rank_acc + r, L.rcnt[r]);
-    for (int n = tid; n < a.nodes; n += kLayoutBlock)
-        if (L.ncnt[n] != 0) atomicAdd(a.node_acc + n, L.ncnt[n]);
-}
-
-// Distinct-token totals from the accumulators, which are re-zeroed for the
-// next call.
-template <int NT>
-__device__ void flush_rank_totals(const LayoutArgs& a)
-{
-    for (int r = threadIdx.x; r < a.R; r += NT) {
-        const int v = atomicExch(a.rank_acc + r, 0);
-        if (a.out_per_rank) a.out_per_rank[r] = v;
-    }
-    for (int n = threadIdx.x; n < a.nodes; n += NT) {
-        const int v = atomicExch(a.node_acc + n, 0);
-        if (a.out_per_node) a.out_per_node[n] = v;
-    }
+    count_body<KMAX>(a, blockIdx.x, smem);
 }
 
 // Path B: every block stages the whole C x E histogram (C*E <=

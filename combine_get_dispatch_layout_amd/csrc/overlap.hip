@@ -1,0 +1,155 @@
+// The next batch's routing layout, run inside the current batch's dispatch
+// and combine launches (double-batch overlap on one stream).
+//
+// What is computed: exactly ep_get_layout for the next batch (no host sync),
+// and exactly ep_dispatch / ep_combine for the current one.  "DeepEP V1 vs
+// V2 深度对比分析" §5.2 overlaps one micro-batch's communication with
+// another's computation; here the latency-bound layout of batch i+1 hides
+// under the bandwidth-bound dispatch and combine of batch i.
+//
+// Design: a launch whose first blocks do layout work and whose other blocks
+// are the ordinary dispatch (or combine) waves.  The layout blocks have the
+// lowest block ids, so they are scheduled first and finish inside the
+// shadow of the streaming blocks; nothing waits on another stream or an
+// event.
+//   dispatch launch: the whole layout in one block (N <= 256), or the count
+//                    phase, one block per 256 tokens;
+//   combine launch:  the second phase (finish_lean, one block per 256
+//                    tokens), which reads the histogram from memory so the
+//                    launch's LDS stays small for the combine blocks.
+// Kernel boundaries order the phases: the count phase's histogram and ranks
+// are complete before the combine launch starts, the final slots before the
+// next dispatch.
+#include "gather.hpp"
+#include "route.hpp"
+#include "scatter.hpp"
+
+namespace epk {
+
+namespace {
+
+constexpr int kBlock = 256;
+constexpr int kWPB = kBlock / kWave;
+// LDS a layout phase may add to every block of the launch.
+constexpr size_t kOverlapMaxLds = 24 * 1024;
+
+template <int QUANT, bool CHANNEL, int VPL, bool ROW_WAIT, int LK>
+__global__ __launch_bounds__(kBlock) void k_dispatch_layout(DispatchArgs da, int NV, int NC,
+                                                            LayoutArgs la, int lblocks, int fused)
+{
+    extern __shared__ __align__(16) unsigned char smem[];
+    if ((int)blockIdx.x < lblocks) {
+        if (fused) route::fused_body<LK, kWPB>(la, smem);
+        else route::count_body<LK>(la, blockIdx.x, smem);
+        return;
+    }
+    scatter::dispatch_wave<QUANT, CHANNEL, VPL, 8, ROW_WAIT, kWPB>(da, NV, NC, blockIdx.x - lblocks);
+}
+
+template <int KMAX, int VPL, int YQ, bool YCH>
+__global__ __launch_bounds__(kBlock) void k_combine_layout(CombineArgs ca, int NV, int NC,
+                                                           LayoutArgs la, int lblocks)
+{
+    extern __shared__ __align__(16) unsigned char smem[];
+    if ((int)blockIdx.x < lblocks) {
+        route::finish_lean<KMAX>(la, lblocks, blockIdx.x, smem);
+        return;
+    }
+    gather::combine_wave<KMAX, VPL, YQ, YCH, kWPB>(ca, NV, NC, blockIdx.x - lblocks);
+}
+
+template <int QUANT, bool CHANNEL, int VPL, bool ROW_WAIT, int LK>
+hipError_t launch_dl(const DispatchArgs& da, int NV, const LayoutArgs& la, const OverlapPlan& p,
+                     hipStream_t s, LaunchEvents ev)
+{
+    const int NC = (NV + kWave * VPL - 1) / (kWave * VPL);
+    const int64_t items = (da.t_end - da.t_begin) * NC;
+    const int dblocks = items > 0 ? (int)((items + kWPB - 1) / kWPB) : 0;
+    launch_k(k_dispatch_layout<QUANT, CHANNEL, VPL, ROW_WAIT, LK>, dim3(p.dispatch_blocks + dblocks),
+             dim3(kBlock), p.dispatch_lds, s, ev.start, ev.stop, da, NV, NC, la, p.dispatch_blocks,
+             p.fused ? 1 : 0);
+    return hipGetLastError();
+}
+
+template <int KMAX, int YQ, bool YCH>
+hipError_t launch_cl(const CombineArgs& ca, const LayoutArgs& la, const OverlapPlan& p,
+                     hipStream_t s, LaunchEvents ev)
+{
+    constexpr int VPL = 2;
+    const int NV = ca.H / 8;
+    const int NC = (NV + kWave * VPL - 1) / (kWave * VPL);
+    const int64_t items = (ca.t_end - ca.t_begin) * NC;
+    const int cblocks = items > 0 ? (int)((items + kWPB - 1) / kWPB) : 0;
+    if (p.combine_blocks + cblocks == 0) return hipSuccess;
+    launch_k(k_combine_layout<KMAX, VPL, YQ, YCH>, dim3(p.combine_blocks + cblocks), dim3(kBlock),
+             p.combine_lds, s, ev.start, ev.stop, ca, NV, NC, la, p.combine_blocks);
+    return hipGetLastError();
+}
+
+template <int LK>
+hipError_t launch_dl_k(const DispatchArgs& da, const LayoutArgs& la, const OverlapPlan& p,
+                       hipStream_t s, LaunchEvents ev)
+{
+    auto launch = [&](auto q, auto ch, auto vpl, auto rw, int NV) {
+        return launch_dl<decltype(q)::value, decltype(ch)::value, decltype(vpl)::value,
+                         decltype(rw)::value, LK>(da, NV, la, p, s, ev);
+    };
+    return dispatch_shape(da, launch);
+}
+
+template <int KMAX>
+hipError_t launch_cl_k(const CombineArgs& ca, const LayoutArgs& la, const OverlapPlan& p,
+                       hipStream_t s, LaunchEvents ev)
+{
+    const bool ych = ca.ygroup == ca.H && ca.H != 128;
+    switch (ca.yquant) {
+        case 0: return launch_cl<KMAX, 0, false>(ca, la, p, s, ev);
+        case 1: return ych ? launch_cl<KMAX, 1, true>(ca, la, p, s, ev)
+                           : launch_cl<KMAX, 1, false>(ca, la, p, s, ev);
+        default: return ych ? launch_cl<KMAX, 2, true>(ca, la, p, s, ev)
+                            : launch_cl<KMAX, 2, false>(ca, la, p, s, ev);
+    }
+}
+
+}  // namespace
+
+OverlapPlan plan_overlap(const LayoutArgs& la)
+{
+    OverlapPlan p;
+    if (la.K > 8) return p;   // the layout's registers would cut the streaming blocks' occupancy
+    const size_t fused = route::fused_lds_bytes(la, kWPB);
+    if (la.num_tokens <= kLayoutBlock && fused <= kOverlapMaxLds) {
+        p.ok = true;
+        p.fused = true;
+        p.dispatch_blocks = 1;
+        p.dispatch_lds = fused;
+        return p;
+    }
+    const size_t count = route::route_lds_bytes(kWPB, la.E, la.R, la.nodes);
+    const size_t finish = route::finish_lean_lds_bytes(la);
+    if (count > kOverlapMaxLds || finish > kOverlapMaxLds) return p;
+    const int C = (int)((la.num_tokens + kLayoutBlock - 1) / kLayoutBlock);
+    if (C == 0) return p;   // an empty batch whose one-block layout does not fit
+    p.ok = true;
+    p.dispatch_blocks = C;
+    p.combine_blocks = C;
+    p.dispatch_lds = count;
+    p.combine_lds = finish;
+    return p;
+}
+
+// One instantiation for every K <= 8 (entries past K are masked), which
+// keeps the number of merged kernels down.
+hipError_t launch_dispatch_layout(const DispatchArgs& da, const LayoutArgs& la,
+                                  const OverlapPlan& p, hipStream_t s, LaunchEvents ev)
+{
+    return launch_dl_k<8>(da, la, p, s, ev);
+}
+
+hipError_t launch_combine_layout(const CombineArgs& ca, const LayoutArgs& la, const OverlapPlan& p,
+                                 hipStream_t s, LaunchEvents ev)
+{
+    return launch_cl_k<8>(ca, la, p, s, ev);
+}
+
+}  // namespace epk

@@ -1,6 +1,7 @@
 // Device building blocks of the routing layout, shared by the layout
-// kernels (layout.hip) and the single-launch layout + dispatch (fused.hip).
-// See layout.hip for what is computed and its sources.
+// kernels (layout.hip), the single-launch layout + dispatch (fused.hip) and
+// the launches that run the next batch's layout beside dispatch and combine
+// (overlap.hip).  See layout.hip for what is computed and its sources.
 #pragma once
 
 #include "ep_internal.hpp"
@@ -335,6 +336,163 @@ inline size_t fused_lds_bytes(const LayoutArgs& a, int waves)
 {
     return route_lds_bytes(waves, a.E, a.R, a.nodes) +
            ((size_t)a.E + 1 + 2 * (size_t)waves * kWave) * 4;
+}
+
+// ---- block bodies (used by the layout kernels and by the launches that run
+// a layout phase of the next batch beside dispatch or combine) ------------
+
+// Path A: one block of WAVES waves does the whole layout of N <= WAVES*64
+// tokens in LDS (fused_lds_bytes).
+template <int KMAX, int WAVES>
+__device__ __forceinline__ void fused_body(const LayoutArgs& a, unsigned char* smem)
+{
+    constexpr int NT = WAVES * kWave;
+    const RouteLds L = carve_route(smem, WAVES, a.E, a.R);
+    int ids[KMAX], lr[KMAX];
+    route_block<KMAX, WAVES>(a, 0, L, ids, lr);
+    // prefix [E+1] and scan scratch [2*NT] follow the routing LDS
+    int32_t* psum = L.ncnt + a.nodes;
+    int32_t* scratch = psum + a.E + 1;
+    aligned_prefix<NT>(a, L.bhist, psum, scratch);
+    int off[KMAX];
+    bool dropped = false;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k)
+        off[k] = ids[k] >= 0 ? final_slot(a, psum[ids[k]], lr[k], dropped) : 0;
+    flag_dropped<KMAX>(a, dropped);
+    store_slots<KMAX>(a, threadIdx.x, ids, off);
+    write_expert_arrays<NT>(a, L.bhist, psum);
+    write_padding<NT>(a, L.bhist, psum, 0, 1);
+    for (int r = threadIdx.x; r < a.R; r += NT)
+        if (a.out_per_rank) a.out_per_rank[r] = L.rcnt[r];
+    for (int n = threadIdx.x; n < a.nodes; n += NT)
+        if (a.out_per_node) a.out_per_node[n] = L.ncnt[n];
+}
+
+// Paths B and C, first phase, layout block b (tokens [256b, 256b+256)):
+// writes the block histogram, the in-block ranks (into slot_idx, finished by
+// the second phase) and adds the distinct-token counts to the accumulators.
+template <int KMAX>
+__device__ __forceinline__ void count_body(const LayoutArgs& a, int b, unsigned char* smem)
+{
+    constexpr int WAVES = kLayoutBlock / kWave;
+    const RouteLds L = carve_route(smem, WAVES, a.E, a.R);
+    int ids[KMAX], lr[KMAX];
+    const int64_t t0 = (int64_t)b * kLayoutBlock;
+    route_block<KMAX, WAVES>(a, t0, L, ids, lr);
+    const int tid = threadIdx.x, K = a.K;
+    const int64_t t = t0 + tid;
+    if (t < a.num_tokens) {
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+            if (k < K) a.slot_idx[t * K + k] = lr[k];
+    }
+    for (int e = tid; e < a.E; e += kLayoutBlock) a.hist[(int64_t)b * a.E + e] = L.bhist[e];
+    for (int r = tid; r < a.R; r += kLayoutBlock)
+        if (L.rcnt[r] != 0) atomicAdd(a.rank_acc + r, L.rcnt[r]);
+    for (int n = tid; n < a.nodes; n += kLayoutBlock)
+        if (L.ncnt[n] != 0) atomicAdd(a.node_acc + n, L.ncnt[n]);
+}
+
+// Distinct-token totals from the accumulators, which are re-zeroed for the
+// next call.
+template <int NT>
+__device__ void flush_rank_totals(const LayoutArgs& a)
+{
+    for (int r = threadIdx.x; r < a.R; r += NT) {
+        const int v = atomicExch(a.rank_acc + r, 0);
+        if (a.out_per_rank) a.out_per_rank[r] = v;
+    }
+    for (int n = threadIdx.x; n < a.nodes; n += NT) {
+        const int v = atomicExch(a.node_acc + n, 0);
+        if (a.out_per_node) a.out_per_node[n] = v;
+    }
+}
+
+// LDS of finish_lean: totals, bases [E] each, prefix [E+1], scan scratch
+// [2*256] and the column partials [2*256].
+inline size_t finish_lean_lds_bytes(const LayoutArgs& a)
+{
+    return ((size_t)3 * a.E + 1 + 4 * kLayoutBlock) * 4;
+}
+
+// Paths B's second phase for layout block b of C, reading the C x E
+// histogram straight from memory (a few KiB of LDS, so it can share a launch
+// with bandwidth-bound blocks): each column's total and the part before
+// block b, split over 256/E threads per column with batched loads; then the
+// aligned prefix and block b's final slots; padding rows of experts b, b+C,
+// ...; block 0 writes the per-expert arrays and flushes the rank totals.
+template <int KMAX>
+__device__ __forceinline__ void finish_lean(const LayoutArgs& a, int C, int b, unsigned char* smem)
+{
+    constexpr int NT = kLayoutBlock;
+    constexpr int kBatch = 8;
+    const int E = a.E, K = a.K, tid = threadIdx.x;
+    int32_t* tot = reinterpret_cast<int32_t*>(smem);   // [E]
+    int32_t* base = tot + E;                            // [E]
+    int32_t* psum = base + E;                           // [E+1]
+    int32_t* scratch = psum + E + 1;                    // [2*NT]
+    int32_t* part_pre = scratch + 2 * NT;               // [NT]
+    int32_t* part_all = part_pre + NT;                  // [NT]
+
+    const int64_t t = (int64_t)b * kLayoutBlock + tid;
+    const bool tv = t < a.num_tokens;
+    int ids[KMAX], lr[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        ids[k] = (tv && k < K) ? a.topk_clone[t * K + k] : -1;
+        lr[k] = (tv && k < K) ? a.slot_idx[t * K + k] : 0;
+    }
+
+    const int EPT = E < NT ? E : NT;
+    int P = NT / EPT;
+    if (P > C) P = C;
+    for (int eb = 0; eb < E; eb += EPT) {
+        const int e = eb + tid % EPT, p = tid / EPT;
+        const bool act = e < E && p < P;
+        const int r0 = act ? p * C / P : 0;
+        const int r1 = act ? (p + 1) * C / P : 0;
+        int pre = 0, all = 0;
+        for (int r = r0; r < r1; r += kBatch) {
+            int v[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) v[j] = r + j < r1 ? a.hist[(int64_t)(r + j) * E + e] : 0;
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                all += v[j];
+                pre += (r + j < b) ? v[j] : 0;
+            }
+        }
+        if (act) {
+            part_pre[p * EPT + (e - eb)] = pre;
+            part_all[p * EPT + (e - eb)] = all;
+        }
+        __syncthreads();
+        if (act && p == 0) {
+            int sp = 0, sa = 0;
+            for (int q = 0; q < P; ++q) {
+                sp += part_pre[q * EPT + (e - eb)];
+                sa += part_all[q * EPT + (e - eb)];
+            }
+            base[e] = sp;
+            tot[e] = sa;
+        }
+        __syncthreads();
+    }
+    aligned_prefix<NT>(a, tot, psum, scratch);
+
+    int off[KMAX];
+    bool dropped = false;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k)
+        off[k] = ids[k] >= 0 ? final_slot(a, psum[ids[k]], base[ids[k]] + lr[k], dropped) : 0;
+    flag_dropped<KMAX>(a, dropped);
+    store_slots<KMAX>(a, t, ids, off);
+    write_padding<NT>(a, tot, psum, b, C);
+    if (b == 0) {
+        write_expert_arrays<NT>(a, tot, psum);
+        flush_rank_totals<NT>(a);
+    }
 }
 
 }  // namespace route

@@ -1,8 +1,11 @@
 // Device building blocks of the dispatch scatter (load a row chunk, quantise,
 // write it to the token's receive rows), shared by the dispatch kernel
-// (dispatch.hip) and the single-launch layout + dispatch (fused.hip).  See
+// (dispatch.hip), the single-launch layout + dispatch (fused.hip) and the
+// dispatch launch that also runs the next batch's layout (overlap.hip).  See
 // dispatch.hip for what is computed and its sources.
 #pragma once
+
+#include <type_traits>
 
 #include "ep_internal.hpp"
 
@@ -50,6 +53,67 @@ inline int dispatch_quant_vpl(int NV)
 {
     if (EP_DISPATCH_QVPL >= 0) return EP_DISPATCH_QVPL;
     return dispatch_plain_vpl(NV, NV * 16);
+}
+
+// The dispatch launch shape for a's format and row size: calls
+// launch(quant, channel, vpl, row_wait, NV) with the first four as
+// std::integral_constant / std::bool_constant values, NV = H/8 vectors.
+//   bf16: dispatch_plain_vpl vectors per lane;
+//   FP8 / int8 per 128 elements, MXFP4: dispatch_quant_vpl;
+//   FP8 / int8 per row: the whole row in one wave (VPL = 64*VPL >= NV).
+// Row waits follow dispatch_row_wait on the receive row's bytes.
+template <int Q, bool CH, int VPL, class L>
+inline hipError_t shape_rw(int NV, int row_bytes, L& launch)
+{
+    using RW1 = std::bool_constant<true>;
+    using RW0 = std::bool_constant<false>;
+    using QC = std::integral_constant<int, Q>;
+    using CC = std::bool_constant<CH>;
+    using VC = std::integral_constant<int, VPL>;
+    return dispatch_row_wait(row_bytes) ? launch(QC{}, CC{}, VC{}, RW1{}, NV)
+                                        : launch(QC{}, CC{}, VC{}, RW0{}, NV);
+}
+
+template <int Q, class L>
+inline hipError_t shape_group(int NV, int row_bytes, L& launch)
+{
+    switch (dispatch_quant_vpl(NV)) {
+        case 2: return shape_rw<Q, false, 2>(NV, row_bytes, launch);
+        case 4: return shape_rw<Q, false, 4>(NV, row_bytes, launch);
+        default: return shape_rw<Q, false, 1>(NV, row_bytes, launch);
+    }
+}
+
+template <int Q, class L>
+inline hipError_t shape_channel(int NV, L& launch)
+{
+    const int rb = NV * 8;   // one byte per element
+    if (NV <= 64) return shape_rw<Q, true, 1>(NV, rb, launch);
+    if (NV <= 128) return shape_rw<Q, true, 2>(NV, rb, launch);
+    if (NV <= 256) return shape_rw<Q, true, 4>(NV, rb, launch);
+    if (NV <= 512) return shape_rw<Q, true, 8>(NV, rb, launch);
+    return shape_rw<Q, true, 16>(NV, rb, launch);
+}
+
+template <class L>
+inline hipError_t dispatch_shape(const DispatchArgs& a, L& launch)
+{
+    const int NV = a.H / 8;
+    const bool channel = a.quant != 0 && a.group == a.H && a.H != 128;
+    switch (a.quant) {
+        case 0: {
+            const int rb = a.H * 2;
+            switch (dispatch_plain_vpl(NV, rb)) {
+                case 1: return shape_rw<0, false, 1>(NV, rb, launch);
+                case 2: return shape_rw<0, false, 2>(NV, rb, launch);
+                case 8: return shape_rw<0, false, 8>(NV, rb, launch);
+                default: return shape_rw<0, false, 4>(NV, rb, launch);
+            }
+        }
+        case 1: return channel ? shape_channel<1>(NV, launch) : shape_group<1>(NV, a.H, launch);
+        case 2: return channel ? shape_channel<2>(NV, launch) : shape_group<2>(NV, a.H, launch);
+        default: return shape_group<3>(NV, a.H / 2, launch);
+    }
 }
 
 namespace scatter {
@@ -305,6 +369,35 @@ __device__ __forceinline__ void scatter_chunk(const DispatchArgs& a, int vbase, 
             if constexpr (ROW_WAIT) __builtin_amdgcn_s_waitcnt(0x0F70);
         }
     }
+}
+
+// One wave's share of the dispatch: block `block` of a launch with WPB waves
+// per block; wave item -> (token, column chunk of VPL vectors per lane).
+template <int QUANT, bool CHANNEL, int VPL, int KMAX, bool ROW_WAIT, int WPB>
+__device__ __forceinline__ void dispatch_wave(const DispatchArgs& a, int NV, int NC, int block)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int item = block * WPB + wv;
+    const int64_t t = a.t_begin + item / NC;
+    const int c = item % NC;
+    if (t >= a.t_end) return;
+    const int vbase = c * (kWave * VPL) + lane;
+    u32x4 d[VPL];
+    load_chunk<VPL>(a, t, vbase, NV, d);
+    // the token's slots as one batch of scalar loads (the slot array carries
+    // kMaxTopk words of slack, so reading KMAX words is in bounds; words past
+    // K are ignored)
+    int sl[KMAX];
+    if (a.identity) {   // row quantisation: row t to receive row t
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) sl[k] = k == 0 ? (int)t : -1;
+    } else {
+        const int32_t* srow = a.slot_idx + t * a.K;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) sl[k] = srow[k];
+    }
+    scatter_chunk<QUANT, CHANNEL, VPL, KMAX, ROW_WAIT>(a, vbase, NV, d, sl, lane);
 }
 
 }  // namespace scatter

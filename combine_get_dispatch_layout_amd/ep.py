@@ -23,7 +23,7 @@ EP_FLAG_BAD_EXPERT_ID, EP_FLAG_RECV_CAPACITY, EP_FLAG_Y_ROWS = 1, 2, 4
 # Every symbol include/ep.h declares.
 SYMBOLS = ("ep_workspace_size", "ep_recv_capacity", "ep_handle_init", "ep_handle_free",
            "ep_get_layout", "ep_dispatch", "ep_layout_dispatch", "ep_dispatch_topk",
-           "ep_combine", "ep_quantize_rows", "ep_set_kernel_events", "ep_handle_get_view", "ep_check_error", "ep_status_str", "ep_last_error_message")
+           "ep_combine", "ep_dispatch_overlap", "ep_combine_overlap", "ep_quantize_rows", "ep_set_kernel_events", "ep_handle_get_view", "ep_check_error", "ep_status_str", "ep_last_error_message")
 
 
 class ep_config(ctypes.Structure):
@@ -77,6 +77,8 @@ def lib():
         L.ep_combine.argtypes = [P, P, P, I64, P, I64, I64, P, P]
         L.ep_quantize_rows.argtypes = [P, P, I64, P, P, P]
         L.ep_dispatch_topk.argtypes = [P, P, I64, I64, P, P, I64, P]
+        L.ep_dispatch_overlap.argtypes = [P, P, I64, I64, P, P, I64, P, P, I64, P, P, P, P, P]
+        L.ep_combine_overlap.argtypes = [P, P, P, I64, P, I64, I64, P, P, P]
         L.ep_set_kernel_events.argtypes = [P, P, P]
         L.ep_handle_get_view.argtypes = [P, P]
         L.ep_check_error.argtypes = [P, P, P]
@@ -86,7 +88,7 @@ def lib():
         L.ep_last_error_message.restype = ctypes.c_char_p
         for name in ("ep_workspace_size", "ep_recv_capacity", "ep_handle_init", "ep_get_layout",
                      "ep_dispatch", "ep_layout_dispatch", "ep_combine", "ep_quantize_rows",
-                     "ep_dispatch_topk", "ep_set_kernel_events", "ep_handle_get_view",
+                     "ep_dispatch_topk", "ep_dispatch_overlap", "ep_combine_overlap", "ep_set_kernel_events", "ep_handle_get_view",
                      "ep_check_error"):
             getattr(L, name).restype = I32
         _lib = L
@@ -357,6 +359,49 @@ def ep_combine(h: Handle, y: torch.Tensor, topk_weights: torch.Tensor, out: torc
     return out
 
 
+def ep_dispatch_overlap(h: Handle, x: torch.Tensor, recv_x: torch.Tensor,
+                        recv_scales: Optional[torch.Tensor] = None, token_begin=0, token_end=None,
+                        h_next: Optional[Handle] = None, topk_next: Optional[torch.Tensor] = None,
+                        num_tokens_per_rank=None, num_tokens_per_rdma_rank=None,
+                        num_tokens_per_expert=None, is_token_in_rank=None, alloc_outputs=True):
+    """ep_dispatch of h's batch and, with h_next, the start (or all) of the
+    next batch's layout in the same launch.  Returns the next batch's layout
+    outputs (None without h_next); they are final after the ep_combine_overlap
+    that names h_next."""
+    _check_dispatch_tensors(h.cfg, x, recv_x, recv_scales)
+    token_end = x.shape[0] if token_end is None else token_end
+    if not 0 <= token_begin <= token_end <= x.shape[0]:
+        raise ValueError("token range outside x")
+    outs = (None, None, None, None)
+    n_next = 0
+    if h_next is not None:
+        outs = _layout_outputs(h_next.cfg, topk_next, num_tokens_per_rank,
+                               num_tokens_per_rdma_rank, num_tokens_per_expert, is_token_in_rank,
+                               alloc_outputs)
+        n_next = topk_next.shape[0]
+    _check(lib().ep_dispatch_overlap(h.ptr, _ptr(x), token_begin, token_end, _ptr(recv_x),
+                                     _ptr(recv_scales), recv_x.shape[0],
+                                     h_next.ptr if h_next is not None else None, _ptr(topk_next),
+                                     n_next, *map(_ptr, outs), _stream(x.device)))
+    if h_next is None:
+        return None
+    return dict(num_tokens_per_rank=outs[0], num_tokens_per_rdma_rank=outs[1],
+                num_tokens_per_expert=outs[2], is_token_in_rank=outs[3])
+
+
+def ep_combine_overlap(h: Handle, y: torch.Tensor, topk_weights: Optional[torch.Tensor],
+                       out: torch.Tensor, token_begin=0, token_end=None,
+                       y_scales: Optional[torch.Tensor] = None, h_next: Optional[Handle] = None):
+    """ep_combine of h's batch and the rest of h_next's layout, if it waits."""
+    cfg = h.cfg
+    _check_y(cfg, y, y_scales)
+    token_end = out.shape[0] if token_end is None else token_end
+    _check(lib().ep_combine_overlap(h.ptr, _ptr(y), _ptr(y_scales), y.shape[0], _ptr(topk_weights),
+                                    token_begin, token_end, _ptr(out),
+                                    h_next.ptr if h_next is not None else None, _stream(out.device)))
+    return out
+
+
 def ep_dispatch_topk(h: Handle, topk_weights: Optional[torch.Tensor], recv_topk_idx=None,
                      recv_topk_weights=None, token_begin=0, token_end=None, rows=None):
     """Non-expand: per received row the local expert ids (int32 [rows, K]) and
@@ -488,6 +533,25 @@ def bind_layout_dispatch(h: Handle, topk_idx, x, recv_x, recv_scales, num_tokens
                   _ptr(num_tokens_per_rank), _ptr(num_tokens_per_rdma_rank),
                   _ptr(num_tokens_per_expert), _ptr(is_token_in_rank), _ptr(x), _ptr(recv_x),
                   _ptr(recv_scales), recv_x.shape[0], s)
+
+
+def bind_dispatch_overlap(h: Handle, x, recv_x, recv_scales, token_begin, token_end, h_next,
+                          topk_next, num_tokens_per_rank=None, num_tokens_per_rdma_rank=None,
+                          num_tokens_per_expert=None, is_token_in_rank=None, stream=None):
+    """A callable issuing ep_dispatch_overlap with these tensors."""
+    s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream(x.device)
+    return _bound(h, lib().ep_dispatch_overlap, h.ptr, _ptr(x), token_begin, token_end,
+                  _ptr(recv_x), _ptr(recv_scales), recv_x.shape[0], h_next.ptr, _ptr(topk_next),
+                  topk_next.shape[0], _ptr(num_tokens_per_rank), _ptr(num_tokens_per_rdma_rank),
+                  _ptr(num_tokens_per_expert), _ptr(is_token_in_rank), s)
+
+
+def bind_combine_overlap(h: Handle, y, topk_weights, out, token_begin, token_end, h_next,
+                         stream=None, y_scales=None):
+    """A callable issuing ep_combine_overlap with these tensors."""
+    s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream(out.device)
+    return _bound(h, lib().ep_combine_overlap, h.ptr, _ptr(y), _ptr(y_scales), y.shape[0],
+                  _ptr(topk_weights), token_begin, token_end, _ptr(out), h_next.ptr, s)
 
 
 def bind_combine(h: Handle, y, topk_weights, out, token_begin, token_end, stream=None,

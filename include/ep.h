@@ -25,6 +25,8 @@
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are
  *     stream-ordered and asynchronous unless stated otherwise.
  *   - A handle is used by one stream at a time.
+ *   - EP_ERR_STATE: the handle has no layout yet, or its layout is half done
+ *     (ep_dispatch_overlap) and waits for ep_combine_overlap.
  *   - Errors are returned as ep_status; ep_last_error_message() gives a
  *     "file:line reason" text for the calling thread.  Invalid arguments are
  *     rejected on the host before any HIP call.  Conditions only the device
@@ -50,7 +52,7 @@ typedef enum ep_status {
     EP_ERR_CAPACITY = 3,      /* receive rows exceed the capacity passed in     */
     EP_ERR_DEVICE_INDEX = 4,  /* device saw an expert id or slot out of range   */
     EP_ERR_HIP = 5,           /* a HIP runtime call failed                      */
-    EP_ERR_STATE = 6          /* handle has no layout yet                       */
+    EP_ERR_STATE = 6          /* handle has no layout yet, or it is half done   */
 } ep_status;
 
 /* Dispatch-side quantisation ([P5] §1.3.1; [P2] int8 prefill option; FP8
@@ -275,6 +277,37 @@ ep_status ep_dispatch_topk(const ep_handle* h, const float* d_topk_weights, int6
 ep_status ep_combine(const ep_handle* h, const void* d_y, const float* d_y_scales, int64_t y_rows,
                      const float* d_topk_weights, int64_t token_begin, int64_t token_end,
                      void* d_out, void* stream);
+
+/* Double-batch overlap on one stream ([P3] §5.2 overlaps one micro-batch's
+ * communication with another's computation): the next batch's layout runs
+ * inside the current batch's dispatch and combine launches, so its latency
+ * hides under their HBM-bound work and nothing waits on another stream.
+ *
+ * ep_dispatch_overlap: ep_dispatch(h, d_x, token_begin, token_end, d_recv_x,
+ *   d_recv_scales, recv_capacity_rows) and, when h_next is non-NULL, the
+ *   start of ep_get_layout(h_next, d_topk_next, num_tokens_next, <the four
+ *   outputs>, do_cpu_sync = 0): every argument has the meaning, layout and
+ *   checks given there.  h_next must differ from h and have the same
+ *   configuration.  For num_tokens_next <= 256 the layout completes in this
+ *   launch; otherwise it completes in the next ep_combine_overlap(..., h_next)
+ *   call, and until then h_next may be used only there (other calls return
+ *   EP_ERR_STATE; ep_get_layout or ep_layout_dispatch on it start over).
+ *   Configurations whose layout cannot share the launch (num_topk > 8,
+ *   stacked sources, non_expand, a routing LDS above 24 KiB) lay h_next out
+ *   with the ordinary kernels after the dispatch.
+ * ep_combine_overlap: ep_combine(h, ...) and, when h_next is waiting, the
+ *   rest of its layout.  With h_next NULL or not waiting it is ep_combine.
+ * Kernel events armed on h (ep_set_kernel_events) span the call's launches. */
+ep_status ep_dispatch_overlap(const ep_handle* h, const void* d_x, int64_t token_begin,
+                              int64_t token_end, void* d_recv_x, void* d_recv_scales,
+                              int64_t recv_capacity_rows, ep_handle* h_next,
+                              const int32_t* d_topk_next, int64_t num_tokens_next,
+                              int32_t* d_num_tokens_per_rank, int32_t* d_num_tokens_per_rdma_rank,
+                              int32_t* d_num_tokens_per_expert, uint8_t* d_is_token_in_rank,
+                              void* stream);
+ep_status ep_combine_overlap(const ep_handle* h, const void* d_y, const float* d_y_scales,
+                             int64_t y_rows, const float* d_topk_weights, int64_t token_begin,
+                             int64_t token_end, void* d_out, ep_handle* h_next, void* stream);
 
 /* Quantises bf16 rows d_x [rows, H] one row at a time into the form
  * ep_combine reads with combine_quant (the sending side of a quantised

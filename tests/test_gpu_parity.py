@@ -508,3 +508,119 @@ def test_non_expand_group_limited_one_call_and_sources():
     _say("[parity] non-expand group-limited one call")
     run_and_check(w, fused=True)
     run_and_check(w.scaled(num_sources=8))
+
+
+# Double-batch overlap on one stream (ep_dispatch_overlap /
+# ep_combine_overlap): a sequence of batches over two handles in turn; after
+# every step the finished batch's rows and combine output and the next
+# batch's layout are compared with the oracle.
+def _overlap_sequence(w, sizes, seeds):
+    from shuffle_check import (bits16, compare_combine, compare_dispatch, compare_layout,
+                               config_of, oracle_slots, bf16_values)
+    cfg = config_of(w)
+    nmax = max(sizes)
+    hs = [ep.ep_handle_init(cfg, nmax), ep.ep_handle_init(cfg, nmax)]
+    batches = []
+    for n, sd in zip(sizes, seeds):
+        wb = w.scaled(num_tokens=n, seed=sd)
+        idx, wts = W.routing(wb)
+        x = W.activations(n, w.hidden, sd * 7 + 1, device="cuda")
+        cap = ep.ep_recv_capacity(cfg, n)
+        b = dict(w=wb, idx=idx, wts=wts, topk=torch.from_numpy(idx).cuda(),
+                 wts_d=torch.from_numpy(wts).cuda(), x=x,
+                 recv=torch.zeros((cap, cfg.recv_row_elems), dtype=cfg.recv_dtype, device="cuda"),
+                 scales=(torch.zeros((cap, cfg.num_groups), dtype=cfg.scales_dtype, device="cuda")
+                         if w.quant else None),
+                 out=torch.zeros((n, w.hidden), dtype=torch.bfloat16, device="cuda"), cap=cap)
+        batches.append(b)
+    lay = ep.ep_get_layout(hs[0], batches[0]["topk"])
+    for i, b in enumerate(batches):
+        h, hn = hs[i % 2], hs[(i + 1) % 2]
+        nxt = batches[i + 1] if i + 1 < len(batches) else None
+        if nxt is not None:
+            nlay = ep.ep_dispatch_overlap(h, b["x"], b["recv"], b["scales"], h_next=hn,
+                                          topk_next=nxt["topk"])
+        else:
+            ep.ep_dispatch_overlap(h, b["x"], b["recv"], b["scales"])
+        S = oracle_slots(b["w"], b["idx"])["S"]
+        y = W.activations(max(S, 1), w.hidden, 900 + i, device="cuda")
+        ep.ep_combine_overlap(h, y, b["wts_d"], b["out"], h_next=hn if nxt is not None else None)
+        st, flags = ep.ep_check_error(h)
+        # the finished batch: rows and combine
+        ref_slots = oracle_slots(b["w"], b["idx"])
+        dropped = ref_slots.get("dropped", 0) > 0
+        assert st == (ep.EP_ERR_CAPACITY if dropped else ep.EP_OK), (i, st, flags)
+
+        class R:
+            pass
+        run = R()
+        run.w, run.recv, run.scales = b["w"], b["recv"], b["scales"]
+        ref_recv, ref_scales = oracle.dispatch(bits16(b["x"]), ref_slots["slot_idx"], b["cap"],
+                                               quant=w.quant, group=w.quant_group or None,
+                                               scale_mode=w.scale_mode)
+        compare_dispatch(run, ref_recv, ref_scales, ref_slots)
+        y_bits = bits16(y)
+        ref_out = oracle.combine(y_bits, b["wts"], ref_slots["slot_idx"])
+        compare_combine(bits16(b["out"]), ref_out, bf16_values(y_bits), b["wts"],
+                        ref_slots["slot_idx"], w.num_topk)
+        # the next batch's layout, complete after this combine
+        if nxt is not None:
+            run.lay, run.h = nlay, hn
+            ref_lay = oracle.layout(nxt["idx"], w.num_experts, w.num_ranks, w.ranks_per_node)
+            compare_layout(run, nxt["idx"], ref_lay, oracle_slots(nxt["w"], nxt["idx"]),
+                           host_sync=False)
+    return hs
+
+
+@pytest.mark.parametrize("args,sizes", [
+    (dict(N=1, H=1024, E=64, R=8, K=8), [1000, 1000, 1000]),                  # count + finish
+    (dict(N=1, H=7168, E=256, R=16, K=8, quant=W.QUANT_FP8, group=128), [128, 200, 256]),  # one block
+    (dict(N=1, H=520, E=128, R=16, K=6, A=4, mask=0.1), [3000, 257, 777, 1]),  # padding, mixed
+    (dict(N=1, H=256, E=64, R=8, K=8, cap=40), [600, 600]),                    # fixed capacity
+    (dict(N=1, H=2048, E=32, R=4, K=2, quant=W.QUANT_MXFP4, group=32), [4096, 100]),
+    (dict(N=1, H=256, E=64, R=8, K=16), [500, 300]),                           # K > 8: separate
+    (dict(N=1, H=256, E=1024, R=1024, K=4, rpn=1), [300, 300]),                # LDS too large
+])
+def test_overlap_sequence(args, sizes):
+    w = _custom(**args)
+    _say(f"[parity] overlap {args} sizes {sizes}")
+    _overlap_sequence(w, sizes, [11 + i for i in range(len(sizes))])
+
+
+def test_overlap_empty_and_non_expand():
+    w = _custom(N=1, H=512, E=64, R=8, K=8)
+    _say("[parity] overlap with an empty batch and non-expand")
+    _overlap_sequence(w, [700, 0, 300], [3, 4, 5])
+    _overlap_sequence(w.scaled(non_expand=True), [500, 400], [6, 7])
+
+
+def test_overlap_states():
+    cfg = ep.Config(256, 8, 64, 8)
+    h0, h1 = ep.ep_handle_init(cfg, 1024), ep.ep_handle_init(cfg, 1024)
+    other = ep.ep_handle_init(ep.Config(256, 8, 64, 4), 1024)
+    w = _custom(N=1000, H=256, E=64, R=8, K=8)
+    idx, wts = W.routing(w)
+    topk = torch.from_numpy(idx).cuda()
+    x = W.activations(1000, 256, 5, device="cuda")
+    recv = torch.zeros((ep.ep_recv_capacity(cfg, 1000), 256), dtype=torch.bfloat16, device="cuda")
+    ep.ep_get_layout(h0, topk)
+    for bad in (h0, other):
+        with pytest.raises(ep.EpError) as ei:
+            ep.ep_dispatch_overlap(h0, x, recv, h_next=bad, topk_next=topk)
+        assert ei.value.status == ep.EP_ERR_INVALID_ARG
+    ep.ep_dispatch_overlap(h0, x, recv, h_next=h1, topk_next=topk)
+    # h1 is counted, not finished: only the overlapped combine may use it
+    with pytest.raises(ep.EpError) as ei:
+        ep.ep_dispatch(h1, x, recv)
+    assert ei.value.status == ep.EP_ERR_STATE
+    out = torch.zeros((1000, 256), dtype=torch.bfloat16, device="cuda")
+    y = torch.zeros((ep.ep_recv_capacity(cfg, 1000), 256), dtype=torch.bfloat16, device="cuda")
+    wd = torch.from_numpy(wts).cuda()
+    with pytest.raises(ep.EpError) as ei:
+        ep.ep_combine(h1, y, wd, out)
+    assert ei.value.status == ep.EP_ERR_STATE
+    ep.ep_combine_overlap(h0, y, wd, out, h_next=h1)
+    ep.ep_dispatch(h1, x, recv)                     # finished: usable
+    v = ep.ep_handle_get_view(h1)
+    assert np.array_equal(v["slot_idx"].cpu().numpy(), oracle.slots(idx, 64, 8, 1)["slot_idx"])
+    assert ep.ep_check_error(h0) == (ep.EP_OK, 0) and ep.ep_check_error(h1) == (ep.EP_OK, 0)
