@@ -11,7 +11,8 @@ bf16, 128 experts over 16 simulated ranks, top-8).
 
 --pipeline picks how a step is issued: merged (default; the layout of the
 next batch runs inside this batch's dispatch and combine launches, one
-stream), overlap (the layout of the next batch runs on a second stream),
+stream), overlap (the default for workloads of several rounds; the layout of
+the next batch runs on a second stream),
 serial (one stream), fused
 (ep_layout_dispatch + combine, the one-call form for decode batches) or
 cached (dispatch + combine on a handle whose layout was computed once before
@@ -271,8 +272,9 @@ def main():
                          "(source, token, k) plus the per-source counts)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pipeline", choices=("merged", "overlap", "serial", "fused", "cached"),
-                    default="merged",
-                    help="merged: batch i+1's layout runs inside batch i's dispatch and "
+                    default=None,
+                    help="(default: merged, or overlap for a workload of several rounds) "
+                         "merged: batch i+1's layout runs inside batch i's dispatch and "
                          "combine launches (ep_dispatch_overlap / ep_combine_overlap), one "
                          "stream; overlap: batch i+1's layout runs on a second stream during "
                          "batch i's dispatch and combine; serial: one stream, one stage after "
@@ -289,6 +291,9 @@ def main():
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc runs into profiles/ and exit")
     args = ap.parse_args()
+    if args.pipeline is None:
+        import workloads as W
+        args.pipeline = "merged" if W.WORKLOADS[args.workload].rounds == 1 else "overlap"
     if args.traffic_from:
         traffic_summary(args.traffic_from[0], args.traffic_from[1], args.workload, args.pipeline)
         return
