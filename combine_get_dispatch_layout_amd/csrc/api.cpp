@@ -261,6 +261,8 @@ ep_status layout_args(ep_handle* h, const int32_t* d_topk_idx, int64_t num_token
     a.out_per_expert = d_num_tokens_per_expert;
     a.out_in_rank = d_is_token_in_rank;
     a.in_rank_words = (c.num_ranks % 4 == 0) && aligned(d_is_token_in_rank, 4);
+    a.row_vec = c.num_topk % 4 == 0;
+    a.topk_vec = a.row_vec && aligned(d_topk_idx, 16);
     return EP_OK;
 }
 
@@ -370,6 +372,7 @@ hipError_t launch_layout_nonexpand(const ep_handle* h, const epk::LayoutArgs& a,
     b.out_per_expert = nullptr;
     b.out_in_rank = nullptr;
     b.in_rank_words = false;
+    b.topk_vec = b.row_vec;                // workspace rows are 256-byte aligned
     return epk::launch_layout(b, s, epk::LaunchEvents{nullptr, ev.stop});
 }
 

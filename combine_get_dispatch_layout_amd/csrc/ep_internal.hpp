@@ -62,6 +62,9 @@ struct LayoutArgs {
     int32_t* out_per_expert;
     uint8_t* out_in_rank;
     bool in_rank_words;         // is_token_in_rank rows may be written as u32
+    // [N,K] rows move as 16-byte vectors: row_vec for the workspace arrays
+    // (K % 4 == 0), topk_vec for the caller's routing (also 16-byte aligned)
+    bool row_vec, topk_vec;
 };
 
 struct DispatchArgs {

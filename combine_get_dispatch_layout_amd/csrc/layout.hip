@@ -88,11 +88,8 @@ __global__ __launch_bounds__(kLayoutBlock) void k_finish(LayoutArgs a, int C)
     const int64_t t = (int64_t)b * kLayoutBlock + tid;
     const bool tv = t < a.num_tokens;
     int ids[KMAX], lr[KMAX];
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k) {
-        ids[k] = (tv && k < K) ? a.topk_clone[t * K + k] : -1;
-        lr[k] = (tv && k < K) ? a.slot_idx[t * K + k] : 0;
-    }
+    load_row<KMAX>(a.topk_clone + t * K, K, a.row_vec, tv, -1, ids);
+    load_row<KMAX>(a.slot_idx + t * K, K, a.row_vec, tv, 0, lr);
     const int n = C * E;
 #pragma unroll 8
     for (int i = tid; i < n; i += NT) tile[i] = a.hist[i];
@@ -211,11 +208,8 @@ __global__ __launch_bounds__(kLayoutBlock) void k_slots(LayoutArgs a)
     const int K = a.K;
     const int32_t* base = a.hist + (int64_t)blockIdx.x * a.E;
     int ids[KMAX], lr[KMAX], off[KMAX];
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k) {
-        ids[k] = (k < K) ? a.topk_clone[t * K + k] : -1;
-        lr[k] = (k < K) ? a.slot_idx[t * K + k] : 0;
-    }
+    load_row<KMAX>(a.topk_clone + t * K, K, a.row_vec, true, -1, ids);
+    load_row<KMAX>(a.slot_idx + t * K, K, a.row_vec, true, 0, lr);
     bool dropped = false;
 #pragma unroll
     for (int k = 0; k < KMAX; ++k)

@@ -33,9 +33,16 @@ constexpr int kWPB = kBlock / kWave;
 // LDS a layout phase may add to every block of the launch.
 constexpr size_t kOverlapMaxLds = 24 * 1024;
 
+// Occupancy asked of the dispatch launch that also lays out the next batch:
+// the layout code's scalar registers would otherwise hold it at 7 waves per
+// SIMD, below the plain dispatch's 8.  Shapes whose scatter already needs
+// more than 64 vector registers (channel scales over 8+ vectors per lane)
+// are left to the compiler.
+constexpr int dl_waves(bool channel, int vpl) { return (channel && vpl >= 8) ? 1 : 8; }
+
 template <int QUANT, bool CHANNEL, int VPL, bool ROW_WAIT, int LK>
-__global__ __launch_bounds__(kBlock) void k_dispatch_layout(DispatchArgs da, int NV, int NC,
-                                                            LayoutArgs la, int lblocks, int fused)
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(dl_waves(CHANNEL, VPL))))
+void k_dispatch_layout(DispatchArgs da, int NV, int NC, LayoutArgs la, int lblocks, int fused)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     if ((int)blockIdx.x < lblocks) {

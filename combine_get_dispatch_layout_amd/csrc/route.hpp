@@ -49,6 +49,60 @@ __device__ inline RouteLds carve_route(unsigned char* smem, int waves, int E, in
     return L;
 }
 
+// K entries of an [N,K] int32 row.  vec: K % 4 == 0 and the row is 16-byte
+// aligned, so the row moves as K/4 16-byte vectors.
+template <int KMAX>
+__device__ __forceinline__ void load_row(const int32_t* p, int K, bool vec, bool valid, int fill,
+                                         int (&v)[KMAX])
+{
+    if constexpr (KMAX >= 4) {
+        if (vec) {
+#pragma unroll
+            for (int q = 0; q < KMAX / 4; ++q) {
+                int4 x = make_int4(fill, fill, fill, fill);
+                if (valid && 4 * q < K) x = reinterpret_cast<const int4*>(p)[q];
+                v[4 * q] = x.x;
+                v[4 * q + 1] = x.y;
+                v[4 * q + 2] = x.z;
+                v[4 * q + 3] = x.w;
+            }
+            return;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) v[k] = (valid && k < K) ? p[k] : fill;
+}
+
+template <int KMAX>
+__device__ __forceinline__ void store_row(int32_t* p, int K, bool vec, const int (&v)[KMAX])
+{
+    if constexpr (KMAX >= 4) {
+        if (vec) {
+#pragma unroll
+            for (int q = 0; q < KMAX / 4; ++q)
+                if (4 * q < K)
+                    reinterpret_cast<int4*>(p)[q] =
+                        make_int4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+            return;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k)
+        if (k < K) p[k] = v[k];
+}
+
+// Per-wave counts of the set bits of a 64-bit mask held by every lane, for
+// bits [0, n): lane b receives the number of lanes with bit b set.
+__device__ __forceinline__ int wave_bit_counts(uint64_t m, int n, int lane)
+{
+    int mine = 0;
+    for (int b = 0; b < n; ++b) {
+        const int c = __popcll(__ballot((m >> b) & 1ull));
+        mine = lane == b ? c : mine;
+    }
+    return mine;
+}
+
 // Routing phase for the block's tokens t0 .. t0 + WAVES*64 - 1 (one per
 // thread).  Leaves the sanitised ids and the in-block rank of every pair in
 // registers, the block histogram in L.bhist and the distinct-token counts in
@@ -66,61 +120,76 @@ __device__ __forceinline__ void route_block(const LayoutArgs& a, int64_t t0, con
     const int64_t t = t0 + tid;
     const bool tv = t < a.num_tokens;
 
-    for (int i = tid; i < WAVES * E; i += NT) L.wcnt[i] = 0;
     for (int i = tid; i < R; i += NT) L.rcnt[i] = 0;
     for (int i = tid; i < a.nodes; i += NT) L.ncnt[i] = 0;
 
+    load_row<KMAX>(a.topk + t * K, K, a.topk_vec, tv, -1, ids);
     bool bad = false;
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
-        int v = -1;
-        if (k < K && tv) {
-            v = a.topk[t * K + k];
-            if (v < -1 || v >= E) {
-                bad = true;
-                v = -1;
-            }
-            if (write_rows) a.topk_clone[t * K + k] = v;
+        if (ids[k] < -1 || ids[k] >= E) {
+            bad = true;
+            ids[k] = -1;
         }
-        ids[k] = v;
     }
+    if (tv && write_rows) store_row<KMAX>(a.topk_clone + t * K, K, a.row_vec, ids);
     if (__ballot(bad) != 0ull && lane == 0) atomicOr(a.ctrl + kCtrlFlags, kFlagBadId);
 
-    // occ[k]: copies of ids[k] earlier in the same row.
-    int occ[KMAX];
+    // Copies of ids[k] earlier in the same row (its occurrence level), 4 bits
+    // each; the in-block rank starts there and lr accumulates the rest.
+    static_assert(KMAX <= 16, "occurrence levels are packed 4 bits per entry");
+    uint64_t occp = 0ull;
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
         int c = 0;
 #pragma unroll
         for (int q = 0; q < k; ++q) c += (ids[q] == ids[k]) ? 1 : 0;
-        occ[k] = c;
+        lr[k] = c;
+        occp |= (uint64_t)c << (4 * k);
     }
 
-    int rank[KMAX];
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k) rank[k] = 0;
     unsigned long long* mytab = L.tab + w * E;
     int32_t* mycnt = L.wcnt + w * E;
 
     // Each wave owns its table and counts, so the occurrence levels need only
     // wave-level ordering: a wave's LDS operations complete in issue order,
-    // and the wavefront fences keep the compiler from reordering them.
-    __syncthreads();   // counters zeroed
+    // and the wavefront fences keep the compiler from reordering them.  Level
+    // 0 always runs (it writes the wave's counts); later levels only while a
+    // row of the wave repeats an expert.
     for (int j = 0; j < KMAX; ++j) {
-        bool have = false;
+        if (j > 0) {
+            bool have = false;
 #pragma unroll
-        for (int k = 0; k < KMAX; ++k) have |= (ids[k] >= 0 && occ[k] == j);
-        if (__ballot(have) == 0ull) break;
+            for (int k = 0; k < KMAX; ++k)
+                have |= (ids[k] >= 0 && (int)((occp >> (4 * k)) & 15ull) == j);
+            if (__ballot(have) == 0ull) break;
+        }
         for (int e = lane; e < E; e += kWave) mytab[e] = 0ull;
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 #pragma unroll
         for (int k = 0; k < KMAX; ++k)
-            if (ids[k] >= 0 && occ[k] == j) atomicOr(mytab + ids[k], 1ull << lane);
+            if (ids[k] >= 0 && (int)((occp >> (4 * k)) & 15ull) == j)
+                atomicOr(mytab + ids[k], 1ull << lane);
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 #pragma unroll
         for (int k = 0; k < KMAX; ++k)
-            if (ids[k] >= 0) rank[k] += count_below(mytab[ids[k]]);
-        for (int e = lane; e < E; e += kWave) mycnt[e] += __popcll(mytab[e]);
+            if (ids[k] >= 0) lr[k] += count_below(mytab[ids[k]]);
+        // the level's per-expert counts, four table words in flight per lane
+        for (int e0 = lane; e0 < E; e0 += 4 * kWave) {
+            unsigned long long m[4];
+            int c[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int e = e0 + i * kWave;
+                m[i] = e < E ? mytab[e] : 0ull;
+                c[i] = (j > 0 && e < E) ? mycnt[e] : 0;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int e = e0 + i * kWave;
+                if (e < E) mycnt[e] = c[i] + __popcll(m[i]);
+            }
+        }
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     }
     __syncthreads();
@@ -137,65 +206,85 @@ __device__ __forceinline__ void route_block(const LayoutArgs& a, int64_t t0, con
         L.bhist[e] = run;
     }
 
-    // Count each token once per rank and once per node.
-    int rk[KMAX];
+    // Count each token once per rank and once per node, and write its
+    // is_token_in_rank row.
+    uint8_t* row = (a.out_in_rank != nullptr && tv && write_rows) ? a.out_in_rank + t * R : nullptr;
+    if (R <= 64) {
+        // the token's ranks as a bit mask; per-wave counts by ballot, one
+        // LDS add per rank and wave
+        uint64_t m = 0ull;
 #pragma unroll
-    for (int k = 0; k < KMAX; ++k) rk[k] = ids[k] >= 0 ? div_by(ids[k], a.nle_magic) : -1;
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k) {
-        if (rk[k] < 0) continue;
-        bool first = true;
-#pragma unroll
-        for (int q = 0; q < k; ++q) first &= (rk[q] != rk[k]);
-        if (first) atomicAdd(L.rcnt + rk[k], 1);
-    }
-    if (a.nodes > 0) {
-        int nd[KMAX];
-#pragma unroll
-        for (int k = 0; k < KMAX; ++k) nd[k] = rk[k] >= 0 ? div_by(rk[k], a.rpn_magic) : -1;
+        for (int k = 0; k < KMAX; ++k)
+            if (ids[k] >= 0) m |= 1ull << div_by(ids[k], a.nle_magic);
+        const int rc = wave_bit_counts(m, R, lane);
+        if (lane < R && rc != 0) atomicAdd(L.rcnt + lane, rc);
+        if (a.nodes > 0) {
+            const int rpn = a.ranks_per_node;
+            const uint64_t gm = rpn >= 64 ? ~0ull : (1ull << rpn) - 1ull;
+            uint64_t nm = 0ull;
+            for (int n = 0; n < a.nodes; ++n)
+                if ((m >> (n * rpn)) & gm) nm |= 1ull << n;
+            const int nc = wave_bit_counts(nm, a.nodes, lane);
+            if (lane < a.nodes && nc != 0) atomicAdd(L.ncnt + lane, nc);
+        }
+        if (row != nullptr) {
+            if (a.in_rank_words) {
+                uint32_t* roww = reinterpret_cast<uint32_t*>(row);
+                for (int q = 0; q < R / 4; ++q) {
+                    const uint32_t nib = (uint32_t)(m >> (4 * q));
+                    roww[q] =
+                        (nib & 1u) | ((nib & 2u) << 7) | ((nib & 4u) << 14) | ((nib & 8u) << 21);
+                }
+            } else {
+                for (int r = 0; r < R; ++r) row[r] = (uint8_t)((m >> r) & 1ull);
+            }
+        }
+    } else {
+        // more ranks than a mask holds: first occurrence of each rank (and
+        // node) in the row, by comparison
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
-            if (nd[k] < 0) continue;
-            bool first = true;
+            if (ids[k] < 0) continue;
+            const int rk = div_by(ids[k], a.nle_magic);
+            bool first = true, nfirst = true;
+            const int nd = a.nodes > 0 ? div_by(rk, a.rpn_magic) : 0;
 #pragma unroll
-            for (int q = 0; q < k; ++q) first &= (nd[q] != nd[k]);
-            if (first) atomicAdd(L.ncnt + nd[k], 1);
+            for (int q = 0; q < k; ++q) {
+                if (ids[q] < 0) continue;
+                const int rq = div_by(ids[q], a.nle_magic);
+                first &= rq != rk;
+                if (a.nodes > 0) nfirst &= div_by(rq, a.rpn_magic) != nd;
+            }
+            if (first) atomicAdd(L.rcnt + rk, 1);
+            if (a.nodes > 0 && nfirst) atomicAdd(L.ncnt + nd, 1);
         }
-    }
-    if (a.out_in_rank != nullptr && tv && write_rows) {
-        uint8_t* row = a.out_in_rank + t * R;
-        if (a.in_rank_words && R <= 64) {
-            uint64_t m = 0ull;
+        if (row != nullptr) {
+            if (a.in_rank_words) {
+                uint32_t* roww = reinterpret_cast<uint32_t*>(row);
+                for (int q = 0; q < R / 4; ++q) {
+                    uint32_t word = 0u;
 #pragma unroll
-            for (int k = 0; k < KMAX; ++k)
-                if (rk[k] >= 0) m |= 1ull << rk[k];
-            uint32_t* roww = reinterpret_cast<uint32_t*>(row);
-            for (int q = 0; q < R / 4; ++q) {
-                const uint32_t nib = (uint32_t)(m >> (4 * q));
-                roww[q] = (nib & 1u) | ((nib & 2u) << 7) | ((nib & 4u) << 14) | ((nib & 8u) << 21);
-            }
-        } else if (a.in_rank_words) {
-            uint32_t* roww = reinterpret_cast<uint32_t*>(row);
-            for (int q = 0; q < R / 4; ++q) {
-                uint32_t word = 0u;
+                    for (int k = 0; k < KMAX; ++k) {
+                        if (ids[k] < 0) continue;
+                        const int rk = div_by(ids[k], a.nle_magic);
+                        if ((rk >> 2) == q) word |= 1u << ((rk & 3) * 8);
+                    }
+                    roww[q] = word;
+                }
+            } else {
+                for (int r = 0; r < R; ++r) {
+                    uint8_t b = 0;
 #pragma unroll
-                for (int k = 0; k < KMAX; ++k)
-                    if (rk[k] >= 0 && (rk[k] >> 2) == q) word |= 1u << ((rk[k] & 3) * 8);
-                roww[q] = word;
-            }
-        } else {
-            for (int r = 0; r < R; ++r) {
-                uint8_t b = 0;
-#pragma unroll
-                for (int k = 0; k < KMAX; ++k) b |= (rk[k] == r) ? 1 : 0;
-                row[r] = b;
+                    for (int k = 0; k < KMAX; ++k)
+                        b |= (ids[k] >= 0 && div_by(ids[k], a.nle_magic) == r) ? 1 : 0;
+                    row[r] = b;
+                }
             }
         }
     }
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < KMAX; ++k)
-        lr[k] = ids[k] >= 0 ? rank[k] + occ[k] + L.wcnt[w * E + ids[k]] : -1;
+    for (int k = 0; k < KMAX; ++k) lr[k] = ids[k] >= 0 ? lr[k] + L.wcnt[w * E + ids[k]] : -1;
 }
 
 // Exclusive prefix of the aligned counts cnt[0..E) into psum[0..E]; NT
@@ -203,8 +292,8 @@ __device__ __forceinline__ void route_block(const LayoutArgs& a, int64_t t0, con
 // shuffle scan inside each wave, one barrier, then the wave offsets.
 // scratch: NT/64 ints.
 template <int NT>
-__device__ void aligned_prefix(const LayoutArgs& a, const int32_t* cnt, int32_t* psum,
-                               int32_t* scratch)
+__device__ __forceinline__ void aligned_prefix(const LayoutArgs& a, const int32_t* cnt,
+                                               int32_t* psum, int32_t* scratch)
 {
     constexpr int EPT = (kMaxExperts + NT - 1) / NT;
     constexpr int WAVES = NT / kWave;
@@ -247,7 +336,8 @@ __device__ void aligned_prefix(const LayoutArgs& a, const int32_t* cnt, int32_t*
 // Per-expert handle arrays and caller outputs from the counts and prefix
 // (both in LDS).
 template <int NT>
-__device__ void write_expert_arrays(const LayoutArgs& a, const int32_t* cnt, const int32_t* psum)
+__device__ __forceinline__ void write_expert_arrays(const LayoutArgs& a, const int32_t* cnt,
+                                                    const int32_t* psum)
 {
     const int tid = threadIdx.x, E = a.E;
     for (int e = tid; e <= E; e += NT) a.psum_expert[e] = psum[e];
@@ -271,8 +361,8 @@ __device__ void write_expert_arrays(const LayoutArgs& a, const int32_t* cnt, con
 // most A-1 rows per expert: the (expert, row) pairs are flattened so that
 // consecutive threads write consecutive rows.
 template <int NT>
-__device__ void write_padding(const LayoutArgs& a, const int32_t* cnt, const int32_t* psum, int e0,
-                              int step)
+__device__ __forceinline__ void write_padding(const LayoutArgs& a, const int32_t* cnt,
+                                              const int32_t* psum, int e0, int step)
 {
     // unused rows per expert: at most A-1 (packed) or cap (fixed capacity)
     const int W = a.cap > 0 ? a.cap : a.A - 1;
@@ -315,16 +405,18 @@ __device__ __forceinline__ void store_slots(const LayoutArgs& a, int64_t t, cons
 {
     const int K = a.K;
     if (t >= a.num_tokens) return;
+    int sl[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) sl[k] = ids[k] >= 0 ? off[k] : -1;   // off is -1 when dropped
+    store_row<KMAX>(a.slot_idx + t * K, K, a.row_vec, sl);
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
         if (k >= K) break;
-        const int s = ids[k] >= 0 ? off[k] : -1;   // off is -1 for a dropped pair
-        a.slot_idx[t * K + k] = s;
-        if (s >= 0) {
+        if (sl[k] >= 0) {
             int2 m;
             m.x = (int)t;
             m.y = k;
-            reinterpret_cast<int2*>(a.src_meta)[s] = m;
+            reinterpret_cast<int2*>(a.src_meta)[sl[k]] = m;
         }
     }
 }
@@ -382,11 +474,7 @@ __device__ __forceinline__ void count_body(const LayoutArgs& a, int b, unsigned 
     route_block<KMAX, WAVES>(a, t0, L, ids, lr);
     const int tid = threadIdx.x, K = a.K;
     const int64_t t = t0 + tid;
-    if (t < a.num_tokens) {
-#pragma unroll
-        for (int k = 0; k < KMAX; ++k)
-            if (k < K) a.slot_idx[t * K + k] = lr[k];
-    }
+    if (t < a.num_tokens) store_row<KMAX>(a.slot_idx + t * K, K, a.row_vec, lr);
     for (int e = tid; e < a.E; e += kLayoutBlock) a.hist[(int64_t)b * a.E + e] = L.bhist[e];
     for (int r = tid; r < a.R; r += kLayoutBlock)
         if (L.rcnt[r] != 0) atomicAdd(a.rank_acc + r, L.rcnt[r]);
@@ -397,7 +485,7 @@ __device__ __forceinline__ void count_body(const LayoutArgs& a, int b, unsigned 
 // Distinct-token totals from the accumulators, which are re-zeroed for the
 // next call.
 template <int NT>
-__device__ void flush_rank_totals(const LayoutArgs& a)
+__device__ __forceinline__ void flush_rank_totals(const LayoutArgs& a)
 {
     for (int r = threadIdx.x; r < a.R; r += NT) {
         const int v = atomicExch(a.rank_acc + r, 0);
@@ -438,11 +526,8 @@ __device__ __forceinline__ void finish_lean(const LayoutArgs& a, int C, int b, u
     const int64_t t = (int64_t)b * kLayoutBlock + tid;
     const bool tv = t < a.num_tokens;
     int ids[KMAX], lr[KMAX];
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k) {
-        ids[k] = (tv && k < K) ? a.topk_clone[t * K + k] : -1;
-        lr[k] = (tv && k < K) ? a.slot_idx[t * K + k] : 0;
-    }
+    load_row<KMAX>(a.topk_clone + t * K, K, a.row_vec, tv, -1, ids);
+    load_row<KMAX>(a.slot_idx + t * K, K, a.row_vec, tv, 0, lr);
 
     const int EPT = E < NT ? E : NT;
     int P = NT / EPT;
@@ -456,7 +541,8 @@ __device__ __forceinline__ void finish_lean(const LayoutArgs& a, int C, int b, u
         for (int r = r0; r < r1; r += kBatch) {
             int v[kBatch];
 #pragma unroll
-            for (int j = 0; j < kBatch; ++j) v[j] = r + j < r1 ? a.hist[(int64_t)(r + j) * E + e] : 0;
+            for (int j = 0; j < kBatch; ++j)
+                v[j] = r + j < r1 ? a.hist[(int64_t)(r + j) * E + e] : 0;
 #pragma unroll
             for (int j = 0; j < kBatch; ++j) {
                 all += v[j];
