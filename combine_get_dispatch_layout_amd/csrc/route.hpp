@@ -32,7 +32,7 @@ struct RouteLds {
     int32_t* ncnt;             // [nodes]
 };
 
-inline size_t route_lds_bytes(int waves, int E, int R, int nodes)
+__host__ __device__ inline size_t route_lds_bytes(int waves, int E, int R, int nodes)
 {
     return (size_t)waves * E * 8 + (size_t)waves * E * 4 + (size_t)E * 4 + (size_t)R * 4 +
            (size_t)nodes * 4;
@@ -103,6 +103,120 @@ __device__ __forceinline__ int wave_bit_counts(uint64_t m, int n, int lane)
     return mine;
 }
 
+// Token t's routing row with ids outside [-1, E) replaced by -1; returns
+// whether it had any.
+template <int KMAX>
+__device__ __forceinline__ bool load_ids(const LayoutArgs& a, int64_t t, bool valid,
+                                         int (&ids)[KMAX])
+{
+    load_row<KMAX>(a.topk + t * a.K, a.K, a.topk_vec, valid, -1, ids);
+    bool bad = false;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        if (ids[k] < -1 || ids[k] >= a.E) {
+            bad = true;
+            ids[k] = -1;
+        }
+    }
+    return bad;
+}
+
+// The token's ranks as a bit mask (R <= 64; 0 otherwise).
+template <int KMAX>
+__device__ __forceinline__ uint64_t rank_mask(const LayoutArgs& a, const int (&ids)[KMAX])
+{
+    uint64_t m = 0ull;
+    if (a.R <= 64) {
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+            if (ids[k] >= 0) m |= 1ull << div_by(ids[k], a.nle_magic);
+    }
+    return m;
+}
+
+// Adds the wave's tokens to the distinct-token counts per rank and node in
+// LDS (every lane of the wave calls it).  R <= 64: per-wave counts by
+// ballot over the rank masks, one LDS add per rank; otherwise the first
+// occurrence of each rank (and node) in a row, by comparison.
+template <int KMAX>
+__device__ __forceinline__ void add_rank_counts(const LayoutArgs& a, const int (&ids)[KMAX],
+                                                uint64_t m, int lane, int32_t* rcnt, int32_t* ncnt)
+{
+    const int R = a.R;
+    if (R <= 64) {
+        const int rc = wave_bit_counts(m, R, lane);
+        if (lane < R && rc != 0) atomicAdd(rcnt + lane, rc);
+        if (a.nodes > 0) {
+            const int rpn = a.ranks_per_node;
+            const uint64_t gm = rpn >= 64 ? ~0ull : (1ull << rpn) - 1ull;
+            uint64_t nm = 0ull;
+            for (int n = 0; n < a.nodes; ++n)
+                if ((m >> (n * rpn)) & gm) nm |= 1ull << n;
+            const int nc = wave_bit_counts(nm, a.nodes, lane);
+            if (lane < a.nodes && nc != 0) atomicAdd(ncnt + lane, nc);
+        }
+        return;
+    }
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        if (ids[k] < 0) continue;
+        const int rk = div_by(ids[k], a.nle_magic);
+        const int nd = a.nodes > 0 ? div_by(rk, a.rpn_magic) : 0;
+        bool first = true, nfirst = true;
+#pragma unroll
+        for (int q = 0; q < k; ++q) {
+            if (ids[q] < 0) continue;
+            const int rq = div_by(ids[q], a.nle_magic);
+            first &= rq != rk;
+            if (a.nodes > 0) nfirst &= div_by(rq, a.rpn_magic) != nd;
+        }
+        if (first) atomicAdd(rcnt + rk, 1);
+        if (a.nodes > 0 && nfirst) atomicAdd(ncnt + nd, 1);
+    }
+}
+
+// One token's is_token_in_rank row (m from rank_mask when R <= 64).
+template <int KMAX>
+__device__ __forceinline__ void write_in_rank_row(const LayoutArgs& a, const int (&ids)[KMAX],
+                                                  uint64_t m, uint8_t* row)
+{
+    const int R = a.R;
+    if (R <= 64) {
+        if (a.in_rank_words) {
+            uint32_t* roww = reinterpret_cast<uint32_t*>(row);
+            for (int q = 0; q < R / 4; ++q) {
+                const uint32_t nib = (uint32_t)(m >> (4 * q));
+                roww[q] =
+                    (nib & 1u) | ((nib & 2u) << 7) | ((nib & 4u) << 14) | ((nib & 8u) << 21);
+            }
+        } else {
+            for (int r = 0; r < R; ++r) row[r] = (uint8_t)((m >> r) & 1ull);
+        }
+        return;
+    }
+    if (a.in_rank_words) {
+        uint32_t* roww = reinterpret_cast<uint32_t*>(row);
+        for (int q = 0; q < R / 4; ++q) {
+            uint32_t word = 0u;
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k) {
+                if (ids[k] < 0) continue;
+                const int rk = div_by(ids[k], a.nle_magic);
+                if ((rk >> 2) == q) word |= 1u << ((rk & 3) * 8);
+            }
+            roww[q] = word;
+        }
+    } else {
+        for (int r = 0; r < R; ++r) {
+            uint8_t b = 0;
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k)
+                b |= (ids[k] >= 0 && div_by(ids[k], a.nle_magic) == r) ? 1 : 0;
+            row[r] = b;
+        }
+    }
+}
+
 // Routing phase for the block's tokens t0 .. t0 + WAVES*64 - 1 (one per
 // thread).  Leaves the sanitised ids and the in-block rank of every pair in
 // registers, the block histogram in L.bhist and the distinct-token counts in
@@ -123,15 +237,7 @@ __device__ __forceinline__ void route_block(const LayoutArgs& a, int64_t t0, con
     for (int i = tid; i < R; i += NT) L.rcnt[i] = 0;
     for (int i = tid; i < a.nodes; i += NT) L.ncnt[i] = 0;
 
-    load_row<KMAX>(a.topk + t * K, K, a.topk_vec, tv, -1, ids);
-    bool bad = false;
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k) {
-        if (ids[k] < -1 || ids[k] >= E) {
-            bad = true;
-            ids[k] = -1;
-        }
-    }
+    const bool bad = load_ids<KMAX>(a, t, tv, ids);
     if (tv && write_rows) store_row<KMAX>(a.topk_clone + t * K, K, a.row_vec, ids);
     if (__ballot(bad) != 0ull && lane == 0) atomicOr(a.ctrl + kCtrlFlags, kFlagBadId);
 
@@ -208,80 +314,10 @@ __device__ __forceinline__ void route_block(const LayoutArgs& a, int64_t t0, con
 
     // Count each token once per rank and once per node, and write its
     // is_token_in_rank row.
-    uint8_t* row = (a.out_in_rank != nullptr && tv && write_rows) ? a.out_in_rank + t * R : nullptr;
-    if (R <= 64) {
-        // the token's ranks as a bit mask; per-wave counts by ballot, one
-        // LDS add per rank and wave
-        uint64_t m = 0ull;
-#pragma unroll
-        for (int k = 0; k < KMAX; ++k)
-            if (ids[k] >= 0) m |= 1ull << div_by(ids[k], a.nle_magic);
-        const int rc = wave_bit_counts(m, R, lane);
-        if (lane < R && rc != 0) atomicAdd(L.rcnt + lane, rc);
-        if (a.nodes > 0) {
-            const int rpn = a.ranks_per_node;
-            const uint64_t gm = rpn >= 64 ? ~0ull : (1ull << rpn) - 1ull;
-            uint64_t nm = 0ull;
-            for (int n = 0; n < a.nodes; ++n)
-                if ((m >> (n * rpn)) & gm) nm |= 1ull << n;
-            const int nc = wave_bit_counts(nm, a.nodes, lane);
-            if (lane < a.nodes && nc != 0) atomicAdd(L.ncnt + lane, nc);
-        }
-        if (row != nullptr) {
-            if (a.in_rank_words) {
-                uint32_t* roww = reinterpret_cast<uint32_t*>(row);
-                for (int q = 0; q < R / 4; ++q) {
-                    const uint32_t nib = (uint32_t)(m >> (4 * q));
-                    roww[q] =
-                        (nib & 1u) | ((nib & 2u) << 7) | ((nib & 4u) << 14) | ((nib & 8u) << 21);
-                }
-            } else {
-                for (int r = 0; r < R; ++r) row[r] = (uint8_t)((m >> r) & 1ull);
-            }
-        }
-    } else {
-        // more ranks than a mask holds: first occurrence of each rank (and
-        // node) in the row, by comparison
-#pragma unroll
-        for (int k = 0; k < KMAX; ++k) {
-            if (ids[k] < 0) continue;
-            const int rk = div_by(ids[k], a.nle_magic);
-            bool first = true, nfirst = true;
-            const int nd = a.nodes > 0 ? div_by(rk, a.rpn_magic) : 0;
-#pragma unroll
-            for (int q = 0; q < k; ++q) {
-                if (ids[q] < 0) continue;
-                const int rq = div_by(ids[q], a.nle_magic);
-                first &= rq != rk;
-                if (a.nodes > 0) nfirst &= div_by(rq, a.rpn_magic) != nd;
-            }
-            if (first) atomicAdd(L.rcnt + rk, 1);
-            if (a.nodes > 0 && nfirst) atomicAdd(L.ncnt + nd, 1);
-        }
-        if (row != nullptr) {
-            if (a.in_rank_words) {
-                uint32_t* roww = reinterpret_cast<uint32_t*>(row);
-                for (int q = 0; q < R / 4; ++q) {
-                    uint32_t word = 0u;
-#pragma unroll
-                    for (int k = 0; k < KMAX; ++k) {
-                        if (ids[k] < 0) continue;
-                        const int rk = div_by(ids[k], a.nle_magic);
-                        if ((rk >> 2) == q) word |= 1u << ((rk & 3) * 8);
-                    }
-                    roww[q] = word;
-                }
-            } else {
-                for (int r = 0; r < R; ++r) {
-                    uint8_t b = 0;
-#pragma unroll
-                    for (int k = 0; k < KMAX; ++k)
-                        b |= (ids[k] >= 0 && div_by(ids[k], a.nle_magic) == r) ? 1 : 0;
-                    row[r] = b;
-                }
-            }
-        }
-    }
+    const uint64_t m = rank_mask<KMAX>(a, ids);
+    add_rank_counts<KMAX>(a, ids, m, lane, L.rcnt, L.ncnt);
+    if (a.out_in_rank != nullptr && tv && write_rows)
+        write_in_rank_row<KMAX>(a, ids, m, a.out_in_rank + t * R);
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) lr[k] = ids[k] >= 0 ? lr[k] + L.wcnt[w * E + ids[k]] : -1;

@@ -219,8 +219,12 @@ def test_counts_as_prefix_host_list():
 @pytest.mark.parametrize("args", [
     dict(N=256, H=64, E=64, R=8, K=8, A=3),                # fused, 4 waves, full block
     dict(N=1024, H=64, E=256, R=16, K=8, A=16, mask=0.1),  # fused, 16 waves, full
+    dict(N=700, H=64, E=64, R=8, K=16, A=2),               # fused, 16 waves, K > 8
     dict(N=1025, H=64, E=64, R=8, K=6),                    # count + finish, ragged
+    dict(N=2000, H=64, E=256, R=128, K=8, rpn=8, mask=0.1),  # count + finish, R > 64
     dict(N=2048, H=64, E=1024, R=64, K=4, A=2),            # count + finish, C*E = 8192
+    dict(N=8192, H=32, E=256, R=16, K=8, A=4),             # count + finish, 32 blocks
+    dict(N=8300, H=32, E=32, R=4, K=4, A=3, mask=0.1),     # count + finish, ragged
     dict(N=9000, H=64, E=256, R=32, K=8, A=8, mask=0.05),  # count + scan + slots
     dict(N=40001, H=32, E=64, R=4, K=2),                   # count + scan + slots, many blocks
 ])
@@ -251,6 +255,7 @@ def test_empty_batch_scan_path():
     dict(N=128, H=512, E=64, R=8, K=8, cap=12),              # fused, some experts overflow
     dict(N=1000, H=256, E=64, R=8, K=6, cap=200, mask=0.1),  # fused 16 waves
     dict(N=3000, H=128, E=128, R=16, K=8, cap=150),          # count + finish, overflow
+    dict(N=8300, H=64, E=32, R=4, K=4, cap=900),             # count + finish, overflow
     dict(N=9000, H=64, E=256, R=32, K=8, cap=400),           # count + scan + slots
 ])
 def test_fixed_capacity_layout(args):
@@ -351,6 +356,7 @@ def test_layout_dispatch_empty_batch():
     dict(N=256, H=64, E=64, R=8, K=8, P=4),                         # one block
     dict(N=2048, H=7168, E=256, R=16, K=8, P=16, quant=W.QUANT_FP8, group=128),  # EP16 decode
     dict(N=3000, H=128, E=128, R=16, K=6, P=3, A=4, mask=0.1),      # count + finish
+    dict(N=8400, H=64, E=32, R=4, K=4, P=12, A=2),                  # count + finish
     dict(N=9000, H=64, E=256, R=32, K=8, P=9, A=8),                 # count + scan + slots
     dict(N=1024, H=32, E=64, R=8, K=2, P=1024),                     # one token per source
     dict(N=600, H=256, E=32, R=4, K=4, P=6, cap=100),               # fixed capacity
@@ -491,6 +497,7 @@ def test_quantize_rows(cq, cg, H, sm):
     dict(N=128, H=7168, E=256, R=16, K=8, quant=W.QUANT_FP8, group=128),    # one block
     dict(N=777, H=1032, E=128, R=16, K=8, A=4, mask=0.1),                   # fused 16 waves
     dict(N=3000, H=256, E=64, R=8, K=6),                                    # count + finish
+    dict(N=8500, H=64, E=32, R=8, K=4),                                     # count + finish
     dict(N=9000, H=64, E=256, R=32, K=8, mask=0.05),                        # count + scan
     dict(N=300, H=264, E=1024, R=1024, K=16, rpn=3),                        # K=16, R=E
     dict(N=500, H=512, E=64, R=1, K=8),                                     # one rank
@@ -574,6 +581,7 @@ def _overlap_sequence(w, sizes, seeds):
 
 @pytest.mark.parametrize("args,sizes", [
     (dict(N=1, H=1024, E=64, R=8, K=8), [1000, 1000, 1000]),                  # count + finish
+    (dict(N=1, H=64, E=64, R=8, K=8, A=2), [8500, 9000, 8193]),               # count + finish
     (dict(N=1, H=7168, E=256, R=16, K=8, quant=W.QUANT_FP8, group=128), [128, 200, 256]),  # one block
     (dict(N=1, H=520, E=128, R=16, K=6, A=4, mask=0.1), [3000, 257, 777, 1]),  # padding, mixed
     (dict(N=1, H=256, E=64, R=8, K=8, cap=40), [600, 600]),                    # fixed capacity
@@ -594,31 +602,36 @@ def test_overlap_empty_and_non_expand():
     _overlap_sequence(w.scaled(non_expand=True), [500, 400], [6, 7])
 
 
-def test_overlap_states():
-    cfg = ep.Config(256, 8, 64, 8)
-    h0, h1 = ep.ep_handle_init(cfg, 1024), ep.ep_handle_init(cfg, 1024)
-    other = ep.ep_handle_init(ep.Config(256, 8, 64, 4), 1024)
-    w = _custom(N=1000, H=256, E=64, R=8, K=8)
+@pytest.mark.parametrize("n,two_phase", [(1000, True), (200, False)])
+def test_overlap_states(n, two_phase):
+    """Above 256 tokens the next batch's layout is split over the dispatch
+    and combine launches and the handle is unusable in between; up to 256 it
+    is complete after the dispatch launch."""
+    cfg = ep.Config(64, 8, 64, 8)
+    h0, h1 = ep.ep_handle_init(cfg, n), ep.ep_handle_init(cfg, n)
+    other = ep.ep_handle_init(ep.Config(64, 8, 64, 4), n)
+    w = _custom(N=n, H=64, E=64, R=8, K=8)
     idx, wts = W.routing(w)
     topk = torch.from_numpy(idx).cuda()
-    x = W.activations(1000, 256, 5, device="cuda")
-    recv = torch.zeros((ep.ep_recv_capacity(cfg, 1000), 256), dtype=torch.bfloat16, device="cuda")
+    x = W.activations(n, 64, 5, device="cuda")
+    recv = torch.zeros((ep.ep_recv_capacity(cfg, n), 64), dtype=torch.bfloat16, device="cuda")
     ep.ep_get_layout(h0, topk)
     for bad in (h0, other):
         with pytest.raises(ep.EpError) as ei:
             ep.ep_dispatch_overlap(h0, x, recv, h_next=bad, topk_next=topk)
         assert ei.value.status == ep.EP_ERR_INVALID_ARG
     ep.ep_dispatch_overlap(h0, x, recv, h_next=h1, topk_next=topk)
-    # h1 is counted, not finished: only the overlapped combine may use it
-    with pytest.raises(ep.EpError) as ei:
-        ep.ep_dispatch(h1, x, recv)
-    assert ei.value.status == ep.EP_ERR_STATE
-    out = torch.zeros((1000, 256), dtype=torch.bfloat16, device="cuda")
-    y = torch.zeros((ep.ep_recv_capacity(cfg, 1000), 256), dtype=torch.bfloat16, device="cuda")
+    out = torch.zeros((n, 64), dtype=torch.bfloat16, device="cuda")
+    y = torch.zeros((ep.ep_recv_capacity(cfg, n), 64), dtype=torch.bfloat16, device="cuda")
     wd = torch.from_numpy(wts).cuda()
-    with pytest.raises(ep.EpError) as ei:
-        ep.ep_combine(h1, y, wd, out)
-    assert ei.value.status == ep.EP_ERR_STATE
+    if two_phase:
+        # h1 is counted, not finished: only the overlapped combine may use it
+        with pytest.raises(ep.EpError) as ei:
+            ep.ep_dispatch(h1, x, recv)
+        assert ei.value.status == ep.EP_ERR_STATE
+        with pytest.raises(ep.EpError) as ei:
+            ep.ep_combine(h1, y, wd, out)
+        assert ei.value.status == ep.EP_ERR_STATE
     ep.ep_combine_overlap(h0, y, wd, out, h_next=h1)
     ep.ep_dispatch(h1, x, recv)                     # finished: usable
     v = ep.ep_handle_get_view(h1)
