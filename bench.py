@@ -288,6 +288,11 @@ def main():
     ap.add_argument("--timing", choices=("rotate", "all"), default="rotate",
                     help="rotate: each timed step arms kernel events on one stage, in turn "
                          "(layout, dispatch, combine); all: every call of every step")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one rotation of steps (one step per buffer set) in a HIP "
+                         "graph and time its replays (steps rounded up to whole rotations); "
+                         "kernel times then come from an eager pass of the same calls after "
+                         "the timed replays (merged, serial, fused and cached pipelines)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc runs into profiles/ and exit")
     args = ap.parse_args()
@@ -366,8 +371,11 @@ def main():
     # S from one synced layout (for the byte counts)
     S = ep.ep_get_layout(sets[0]["h"], sets[0]["topk"], do_cpu_sync=True)["num_recv_slots"]
     nbytes = algorithmic_bytes(w, V, S)
-    stream = torch.cuda.current_stream()
     pl = args.pipeline
+    if args.graph and pl == "overlap":
+        sys.exit("--graph captures one stream: use the merged, serial, fused or cached pipeline")
+    # a graph is captured on a stream of its own (default priority)
+    stream = torch.cuda.Stream() if args.graph else torch.cuda.current_stream()
     # overlap: the layout of batch i+1 runs on a second stream while batch i
     # is dispatched and combined (double-batch overlap); default priority
     lay_stream = torch.cuda.Stream() if pl == "overlap" else stream
@@ -491,13 +499,39 @@ def main():
                 for j in range(calls_per_step):
                     issue(i, j, base(i))
 
-    run(args.warmup, False)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    run(args.steps, True)
-    t_enqueue = time.perf_counter() - t0
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    torch.cuda.synchronize()   # set-up work on the default stream is done
+    if args.graph:
+        # one rotation (a step per buffer set) as one graph: the merged
+        # pipeline's host bookkeeping advances by a whole rotation during the
+        # capture, the device catches up on each replay
+        run(args.warmup, False)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            run(nsets, False)
+        reps = -(-args.steps // nsets)
+        args.steps = reps * nsets
+        graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            graph.replay()
+        t_enqueue = time.perf_counter() - t0
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        # kernel times: an eager pass of the same calls
+        hev.close()
+        hev = HipEvents(2 * calls_per_step * args.steps)
+        run(args.steps, True)
+        torch.cuda.synchronize()
+    else:
+        run(args.warmup, False)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        run(args.steps, True)
+        t_enqueue = time.perf_counter() - t0
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
 
     def durs(j):
         """Per-step duration (s) of call j over the steps that timed it."""
@@ -573,7 +607,8 @@ def main():
                              "frac_of_peak": b_dc / t_dc / 1e9 / HBM_PEAK_GBS},
         "device_copy_GBps": copy_gbs,
         "pipeline": args.pipeline,
-        "timing": {"mode": args.timing, "every": every, "host_enqueue_ms_per_step": t_enqueue / args.steps * 1e3,
+        "timing": {"mode": args.timing, "every": every, "graph": args.graph,
+                   "host_enqueue_ms_per_step": t_enqueue / args.steps * 1e3,
                    "samples_per_stage": {k: int(len(d)) for k, (d, _, _) in per_stage.items()}},
         "recv_rows": S, "valid_pairs": V,
     }

@@ -637,3 +637,83 @@ def test_overlap_states(n, two_phase):
     v = ep.ep_handle_get_view(h1)
     assert np.array_equal(v["slot_idx"].cpu().numpy(), oracle.slots(idx, 64, 8, 1)["slot_idx"])
     assert ep.ep_check_error(h0) == (ep.EP_OK, 0) and ep.ep_check_error(h1) == (ep.EP_OK, 0)
+
+
+# HIP graph capture of a decode loop's calls: the one-call layout + dispatch
+# and combine, dispatch + combine on a cached handle, and the merged
+# double-batch steps over two handles.  The calls launch kernels only (no
+# memset, no host synchronisation), so they capture; every replay, with the
+# program's own eager work and synchronisations between replays, matches the
+# eager run bit for bit.
+@pytest.mark.parametrize("pipeline", ["fused", "cached", "merged"])
+def test_graph_replay(pipeline):
+    from shuffle_check import config_of
+    w = W.WORKLOADS["ll_decode_fp8"].scaled(num_tokens=128, hidden=1024)
+    cfg = config_of(w)
+    N, H = w.num_tokens, w.hidden
+    _say(f"[parity] graph replay {pipeline}")
+    routes = [W.routing(w), W.routing(w.scaled(seed=77))]
+    hs = [ep.ep_handle_init(cfg, N), ep.ep_handle_init(cfg, N)]
+    other = ep.ep_handle_init(cfg, N)
+    cap = ep.ep_recv_capacity(cfg, N)
+    topk = [torch.from_numpy(r[0]).cuda() for r in routes]
+    wd = [torch.from_numpy(r[1]).cuda() for r in routes]
+    x = [W.activations(N, H, 11 + i, device="cuda") for i in range(2)]
+    y = [W.activations(cap, H, 21 + i, device="cuda") for i in range(2)]
+    recv = [torch.zeros((cap, cfg.recv_row_elems), dtype=cfg.recv_dtype, device="cuda")
+            for _ in range(2)]
+    scales = [torch.zeros((cap, cfg.num_groups), dtype=cfg.scales_dtype, device="cuda")
+              for _ in range(2)]
+    out = [torch.zeros((N, H), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    s = torch.cuda.Stream()
+    if pipeline == "fused":
+        calls = [ep.bind_layout_dispatch(hs[0], topk[0], x[0], recv[0], scales[0], stream=s),
+                 ep.bind_combine(hs[0], y[0], wd[0], out[0], 0, N, stream=s)]
+    elif pipeline == "cached":
+        ep.ep_get_layout(hs[0], topk[0])
+        calls = [ep.bind_dispatch(hs[0], x[0], recv[0], scales[0], 0, N, stream=s),
+                 ep.bind_combine(hs[0], y[0], wd[0], out[0], 0, N, stream=s)]
+    else:
+        ep.ep_get_layout(hs[0], topk[0])
+        calls = []
+        for i in range(2):
+            h, hn = hs[i], hs[1 - i]
+            calls.append(ep.bind_dispatch_overlap(h, x[i], recv[i], scales[i], 0, N, hn,
+                                                  topk[1 - i], stream=s))
+            calls.append(ep.bind_combine_overlap(h, y[i], wd[i], out[i], 0, N, hn, stream=s))
+    bufs = recv + scales + out
+
+    def zero():
+        for t in bufs:
+            t.zero_()
+
+    zero()
+    torch.cuda.synchronize()
+    for c in calls:
+        c()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in bufs]
+    used = 1 if pipeline != "merged" else 2
+    ref_slots = [ep.ep_handle_get_view(hs[i])["slot_idx"].clone() for i in range(used)]
+    for i in range(used):
+        exp = oracle.slots(routes[i][0], w.num_experts, w.num_ranks, w.expert_alignment)
+        assert np.array_equal(ref_slots[i].cpu().numpy(), exp["slot_idx"])
+
+    graph = torch.cuda.CUDAGraph()
+    zero()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=s):
+        for c in calls:
+            c()
+    for r in range(3):
+        zero()
+        ep.ep_get_layout(other, topk[r % 2])   # eager library work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(ref, bufs):
+            assert torch.equal(a, b), (pipeline, r)
+        for i in range(used):
+            assert torch.equal(ep.ep_handle_get_view(hs[i])["slot_idx"], ref_slots[i])
+        for h in hs[:used]:
+            assert ep.ep_check_error(h) == (ep.EP_OK, 0)
