@@ -429,8 +429,8 @@ ep_status combine_args(const ep_handle* h, const void* d_y, const float* d_y_sca
 // ep_get_layout, and which phases can run inside the launches.
 ep_status next_layout(const ep_handle* h, ep_handle* h_next, const int32_t* d_topk_next,
                       int64_t num_tokens_next, int32_t* d_per_rank, int32_t* d_per_rdma,
-                      int32_t* d_per_expert, uint8_t* d_in_rank, epk::LayoutArgs* la,
-                      epk::OverlapPlan* plan)
+                      int32_t* d_per_expert, uint8_t* d_in_rank, int64_t dispatch_bytes,
+                      epk::LayoutArgs* la, epk::OverlapPlan* plan)
 {
     if (h_next == h) return EP_FAIL(EP_ERR_INVALID_ARG, "h_next must differ from h");
     if (memcmp(&h->cfg, &h_next->cfg, sizeof(ep_config)) != 0)
@@ -439,7 +439,8 @@ ep_status next_layout(const ep_handle* h, ep_handle* h_next, const int32_t* d_to
                                d_per_expert, d_in_rank, la);
     if (st != EP_OK) return st;
     const ep_config& c = h_next->cfg;
-    *plan = (c.non_expand || num_sources(c) > 1) ? epk::OverlapPlan{} : epk::plan_overlap(*la);
+    *plan = (c.non_expand || num_sources(c) > 1) ? epk::OverlapPlan{}
+                                                 : epk::plan_overlap(*la, dispatch_bytes);
     return EP_OK;
 }
 
@@ -663,9 +664,12 @@ ep_status ep_dispatch_overlap(const ep_handle* h, const void* d_x, int64_t token
     }
     epk::LayoutArgs la;
     epk::OverlapPlan plan;
+    // bytes this dispatch writes: one row per pair (codes: one byte per element)
+    const int64_t dispatch_bytes = (token_end - token_begin) * h->cfg.num_topk *
+                                   h->cfg.hidden * (h->cfg.quant == EP_QUANT_NONE ? 2 : 1);
     st = next_layout(h, h_next, d_topk_next, num_tokens_next, d_num_tokens_per_rank,
-                     d_num_tokens_per_rdma_rank, d_num_tokens_per_expert, d_is_token_in_rank, &la,
-                     &plan);
+                     d_num_tokens_per_rdma_rank, d_num_tokens_per_expert, d_is_token_in_rank,
+                     dispatch_bytes, &la, &plan);
     if (st != EP_OK) return st;
     const epk::LaunchEvents ev = h->take_events();
     if (plan.ok) {

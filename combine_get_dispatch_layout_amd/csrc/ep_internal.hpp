@@ -171,7 +171,9 @@ struct OverlapPlan {
     size_t dispatch_lds = 0;
     size_t combine_lds = 0;
 };
-OverlapPlan plan_overlap(const LayoutArgs& la);
+// dispatch_bytes: what the dispatch launch that takes the layout's first
+// phase moves (decides whether a small batch is laid out in one block).
+OverlapPlan plan_overlap(const LayoutArgs& la, int64_t dispatch_bytes);
 hipError_t launch_dispatch_layout(const DispatchArgs& da, const LayoutArgs& la,
                                   const OverlapPlan& p, hipStream_t s, LaunchEvents ev = {});
 hipError_t launch_combine_layout(const CombineArgs& ca, const LayoutArgs& la, const OverlapPlan& p,

@@ -12,8 +12,9 @@
 // lowest block ids, so they are scheduled first and finish inside the
 // shadow of the streaming blocks; nothing waits on another stream or an
 // event.
-//   dispatch launch: the whole layout in one block (N <= 256), or the count
-//                    phase, one block per 256 tokens;
+//   dispatch launch: the whole layout in one block (N <= 256, when the
+//                    launch moves under 4 MiB), or the count phase, one
+//                    block per 256 tokens;
 //   combine launch:  the second phase (finish_lean, one block per 256
 //                    tokens), which reads the histogram from memory so the
 //                    launch's LDS stays small for the combine blocks.
@@ -32,6 +33,9 @@ constexpr int kBlock = 256;
 constexpr int kWPB = kBlock / kWave;
 // LDS a layout phase may add to every block of the launch.
 constexpr size_t kOverlapMaxLds = 24 * 1024;
+// Dispatch bytes from which a small batch's layout is split over the two
+// launches rather than run by one block.
+constexpr int64_t kOverlapSplitMinBytes = 4 << 20;
 
 // Occupancy asked of the dispatch launch that also lays out the next batch:
 // the layout code's scalar registers would otherwise hold it at 7 waves per
@@ -120,23 +124,29 @@ hipError_t launch_cl_k(const CombineArgs& ca, const LayoutArgs& la, const Overla
 
 }  // namespace
 
-OverlapPlan plan_overlap(const LayoutArgs& la)
+OverlapPlan plan_overlap(const LayoutArgs& la, int64_t dispatch_bytes)
 {
     OverlapPlan p;
     if (la.K > 8) return p;   // the layout's registers would cut the streaming blocks' occupancy
     const size_t fused = route::fused_lds_bytes(la, kWPB);
-    if (la.num_tokens <= kLayoutBlock && fused <= kOverlapMaxLds) {
+    const size_t count = route::route_lds_bytes(kWPB, la.E, la.R, la.nodes);
+    const size_t finish = route::finish_lean_lds_bytes(la);
+    const int C = (int)((la.num_tokens + kLayoutBlock - 1) / kLayoutBlock);
+    const bool split = C > 0 && count <= kOverlapMaxLds && finish <= kOverlapMaxLds;
+    // A batch of <= 256 tokens is laid out by one block of the dispatch
+    // launch, unless the two launches stream enough to hide a phase each
+    // (the one block then outlasts the dispatch; measured on MI355X, decode
+    // shape 128 x 7168 FP8: 12.5 us per step split, 14.3 in one block; a
+    // 128 x 256 batch: 9.0 in one block, 10.4 split).
+    if (la.num_tokens <= kLayoutBlock && fused <= kOverlapMaxLds &&
+        !(split && dispatch_bytes >= kOverlapSplitMinBytes)) {
         p.ok = true;
         p.fused = true;
         p.dispatch_blocks = 1;
         p.dispatch_lds = fused;
         return p;
     }
-    const size_t count = route::route_lds_bytes(kWPB, la.E, la.R, la.nodes);
-    const size_t finish = route::finish_lean_lds_bytes(la);
-    if (count > kOverlapMaxLds || finish > kOverlapMaxLds) return p;
-    const int C = (int)((la.num_tokens + kLayoutBlock - 1) / kLayoutBlock);
-    if (C == 0) return p;   // an empty batch whose one-block layout does not fit
+    if (!split) return p;   // LDS too large, or an empty batch whose one block does not fit
     p.ok = true;
     p.dispatch_blocks = C;
     p.combine_blocks = C;

@@ -582,7 +582,8 @@ def _overlap_sequence(w, sizes, seeds):
 @pytest.mark.parametrize("args,sizes", [
     (dict(N=1, H=1024, E=64, R=8, K=8), [1000, 1000, 1000]),                  # count + finish
     (dict(N=1, H=64, E=64, R=8, K=8, A=2), [8500, 9000, 8193]),               # count + finish
-    (dict(N=1, H=7168, E=256, R=16, K=8, quant=W.QUANT_FP8, group=128), [128, 200, 256]),  # one block
+    (dict(N=1, H=7168, E=256, R=16, K=8, quant=W.QUANT_FP8, group=128), [128, 200, 256]),  # split: 7+ MiB
+    (dict(N=1, H=512, E=256, R=16, K=8, quant=W.QUANT_FP8, group=128), [128, 200, 256]),   # one block
     (dict(N=1, H=520, E=128, R=16, K=6, A=4, mask=0.1), [3000, 257, 777, 1]),  # padding, mixed
     (dict(N=1, H=256, E=64, R=8, K=8, cap=40), [600, 600]),                    # fixed capacity
     (dict(N=1, H=2048, E=32, R=4, K=2, quant=W.QUANT_MXFP4, group=32), [4096, 100]),
@@ -605,8 +606,9 @@ def test_overlap_empty_and_non_expand():
 @pytest.mark.parametrize("n,two_phase", [(1000, True), (200, False)])
 def test_overlap_states(n, two_phase):
     """Above 256 tokens the next batch's layout is split over the dispatch
-    and combine launches and the handle is unusable in between; up to 256 it
-    is complete after the dispatch launch."""
+    and combine launches and the handle is unusable in between; up to 256
+    (with a dispatch that moves under 4 MiB, as here) it is complete after
+    the dispatch launch."""
     cfg = ep.Config(64, 8, 64, 8)
     h0, h1 = ep.ep_handle_init(cfg, n), ep.ep_handle_init(cfg, n)
     other = ep.ep_handle_init(ep.Config(64, 8, 64, 4), n)
