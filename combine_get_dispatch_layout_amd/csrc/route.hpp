@@ -324,8 +324,8 @@ __device__ __forceinline__ void route_block(const LayoutArgs& a, int64_t t0, con
 }
 
 // Exclusive prefix of the aligned counts cnt[0..E) into psum[0..E]; NT
-// threads, each owning up to kMaxExperts/NT consecutive experts: a
-// shuffle scan inside each wave, one barrier, then the wave offsets.
+// threads, each owning ceil(E/NT) consecutive experts: a shuffle scan
+// inside each wave, one barrier, then the wave offsets.
 // scratch: NT/64 ints.
 template <int NT>
 __device__ __forceinline__ void aligned_prefix(const LayoutArgs& a, const int32_t* cnt,
@@ -339,13 +339,15 @@ __device__ __forceinline__ void aligned_prefix(const LayoutArgs& a, const int32_
         __syncthreads();
         return;
     }
+    // thread tid owns experts [tid*ept, tid*ept + ept): one each while E <= NT
+    const int ept = (E + NT - 1) / NT;
     int al[EPT];
     int own = 0;
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
-        const int e = tid * EPT + j;
-        const int c = e < E ? cnt[e] : 0;
-        al[j] = ((c + a.A - 1) / a.A) * a.A;
+        const int e = tid * ept + j;
+        const int c = (j < ept && e < E) ? cnt[e] : 0;
+        al[j] = a.A == 1 ? c : ((c + a.A - 1) / a.A) * a.A;
         own += al[j];
     }
     int incl = own;
@@ -360,8 +362,8 @@ __device__ __forceinline__ void aligned_prefix(const LayoutArgs& a, const int32_
     for (int q = 0; q < w; ++q) run += scratch[q];
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
-        const int e = tid * EPT + j;
-        if (e < E) psum[e] = run;
+        const int e = tid * ept + j;
+        if (j < ept && e < E) psum[e] = run;
         run += al[j];
     }
     if (tid == NT - 1) psum[E] = run;

@@ -83,6 +83,21 @@ def test_duplicates_and_all_masked_rows():
     run_and_check(w, idx=idx, wts=wts)
 
 
+def test_duplicates_and_all_masked_rows_one_call():
+    """The same kinds of rows through the one-launch layout + dispatch, whose
+    blocks each place their own tokens from the routing histograms."""
+    w = _custom(N=200, H=1024, E=32, R=4, K=8, A=4, quant=W.QUANT_FP8, group=128)
+    rng = np.random.default_rng(5)
+    idx = rng.integers(0, 32, size=(200, 8)).astype(np.int32)
+    idx[::7] = idx[::7, :1]                 # rows that repeat one expert 8 times
+    idx[3::5, 2:5] = idx[3::5, 1:2]          # runs of one expert inside a row
+    idx[5::11] = -1                         # rows with every entry masked
+    idx[rng.random(idx.shape) < 0.1] = -1
+    wts = rng.random((200, 8)).astype(np.float32)
+    _say("[parity] duplicates/all-masked, one call")
+    run_and_check(w, idx=idx, wts=wts, fused=True)
+
+
 def test_empty_batch():
     w = _custom(N=0, H=256, E=16, R=4, K=2)
     cfg = ep.Config(256, 2, 16, 4, ranks_per_node=2, expert_alignment=4)
@@ -154,7 +169,8 @@ def test_round_trip_identity_experts():
     assert torch.equal(run.out.view(torch.int16), x.view(torch.int16))
 
 
-def test_invalid_expert_ids_flagged_and_skipped():
+@pytest.mark.parametrize("one_call", [False, True])
+def test_invalid_expert_ids_flagged_and_skipped(one_call):
     w = _custom(N=100, H=128, E=16, R=4, K=2)
     idx, wts = W.routing(w)
     bad = idx.copy()
@@ -162,7 +178,10 @@ def test_invalid_expert_ids_flagged_and_skipped():
     bad[50, 0] = -7
     x = W.activations(100, 128, 1, device="cuda")
     run = GpuRun(w, bad, wts, x)
-    run.layout()
+    if one_call:
+        run.layout_dispatch()
+    else:
+        run.layout()
     st, flags = ep.ep_check_error(run.h)
     assert st == ep.EP_ERR_DEVICE_INDEX and flags & ep.EP_FLAG_BAD_EXPERT_ID
     # the bad entries behave as masked ones
@@ -292,7 +311,7 @@ def test_fixed_capacity_with_zipf_and_host_prefix():
     dict(N=200, H=1032, E=128, R=16, K=8, A=16, mask=0.2),   # padding rows, ragged H
     dict(N=128, H=512, E=64, R=8, K=8, cap=12),              # fixed capacity, overflow
     dict(N=100, H=4096, E=32, R=4, K=4, quant=W.QUANT_INT8, group=128, rpn=3),
-    dict(N=64, H=264, E=1024, R=1024, K=4, rpn=1),           # routing LDS too large: 2 launches
+    dict(N=64, H=264, E=1024, R=1024, K=4, rpn=1),           # most experts and ranks, one launch
     dict(N=96, H=256, E=64, R=8, K=16),                      # K > 8: 2 launches
     dict(N=257, H=512, E=64, R=8, K=8, quant=W.QUANT_FP8, group=128),  # N > 256: 2 launches
 ])
