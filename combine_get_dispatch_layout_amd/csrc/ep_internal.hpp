@@ -167,9 +167,9 @@ struct OverlapPlan {
     bool ok = false;          // false: lay the next batch out on its own
     bool fused = false;       // the whole layout in one block of the dispatch launch
     int dispatch_blocks = 0;  // layout blocks in front of the dispatch blocks
-    int combine_blocks = 0;   // layout blocks in front of the combine blocks
+    int combine_blocks = 0;   // count blocks whose finish phase the combine launch runs
     size_t dispatch_lds = 0;
-    size_t combine_lds = 0;
+    size_t combine_lds = 0;   // LDS of the finish phase
 };
 // dispatch_bytes: what the dispatch launch that takes the layout's first
 // phase moves (decides whether a small batch is laid out in one block).

@@ -535,33 +535,38 @@ __device__ __forceinline__ void flush_rank_totals(const LayoutArgs& a)
     }
 }
 
-// LDS of finish_lean: totals, bases [E] each, prefix [E+1], scan scratch
-// [2*256] and the column partials [2*256].
-inline size_t finish_lean_lds_bytes(const LayoutArgs& a)
+// LDS of finish_lean with NT threads: totals [E], bases [NT/256][E], prefix
+// [E+1], scan scratch [2*NT] and the column partials [2*NT].
+__host__ __device__ inline size_t finish_lean_lds_bytes(const LayoutArgs& a, int NT)
 {
-    return ((size_t)3 * a.E + 1 + 4 * kLayoutBlock) * 4;
+    return ((size_t)(2 + NT / kLayoutBlock) * a.E + 1 + 4 * (size_t)NT) * 4;
 }
 
-// Paths B's second phase for layout block b of C, reading the C x E
-// histogram straight from memory (a few KiB of LDS, so it can share a launch
-// with bandwidth-bound blocks): each column's total and the part before
-// block b, split over 256/E threads per column with batched loads; then the
-// aligned prefix and block b's final slots; padding rows of experts b, b+C,
-// ...; block 0 writes the per-expert arrays and flushes the rank totals.
-template <int KMAX>
+// Path B's second phase for finish block b of ceil(C / (NT/256)), reading
+// the C x E histogram straight from memory (a few KiB of LDS, so it can
+// share a launch with bandwidth-bound blocks).  The block finishes the
+// NT/256 count blocks cb0 = b*NT/256 ...: each column's total and the part
+// before cb0, split over NT/E threads per column with batched loads; the
+// base of each later count block adds the histogram rows in between; then
+// the aligned prefix and the final slots of the block's NT tokens; padding
+// rows of experts b, b + blocks, ...; block 0 writes the per-expert arrays
+// and flushes the rank totals.
+template <int KMAX, int NT>
 __device__ __forceinline__ void finish_lean(const LayoutArgs& a, int C, int b, unsigned char* smem)
 {
-    constexpr int NT = kLayoutBlock;
+    constexpr int G = NT / kLayoutBlock;   // count blocks per finish block
     constexpr int kBatch = 8;
     const int E = a.E, K = a.K, tid = threadIdx.x;
+    const int cb0 = b * G;
+    const int blocks = (C + G - 1) / G;
     int32_t* tot = reinterpret_cast<int32_t*>(smem);   // [E]
-    int32_t* base = tot + E;                            // [E]
-    int32_t* psum = base + E;                           // [E+1]
+    int32_t* base = tot + E;                            // [G][E]
+    int32_t* psum = base + G * E;                       // [E+1]
     int32_t* scratch = psum + E + 1;                    // [2*NT]
     int32_t* part_pre = scratch + 2 * NT;               // [NT]
     int32_t* part_all = part_pre + NT;                  // [NT]
 
-    const int64_t t = (int64_t)b * kLayoutBlock + tid;
+    const int64_t t = (int64_t)b * NT + tid;
     const bool tv = t < a.num_tokens;
     int ids[KMAX], lr[KMAX];
     load_row<KMAX>(a.topk_clone + t * K, K, a.row_vec, tv, -1, ids);
@@ -584,7 +589,7 @@ __device__ __forceinline__ void finish_lean(const LayoutArgs& a, int C, int b, u
 #pragma unroll
             for (int j = 0; j < kBatch; ++j) {
                 all += v[j];
-                pre += (r + j < b) ? v[j] : 0;
+                pre += (r + j < cb0) ? v[j] : 0;
             }
         }
         if (act) {
@@ -599,20 +604,27 @@ __device__ __forceinline__ void finish_lean(const LayoutArgs& a, int C, int b, u
                 sa += part_all[q * EPT + (e - eb)];
             }
             base[e] = sp;
+#pragma unroll
+            for (int g = 1; g < G; ++g) {
+                const int r = cb0 + g - 1;
+                sp += r < C ? a.hist[(int64_t)r * E + e] : 0;
+                base[g * E + e] = sp;
+            }
             tot[e] = sa;
         }
         __syncthreads();
     }
     aligned_prefix<NT>(a, tot, psum, scratch);
 
+    const int32_t* mybase = base + (tid / kLayoutBlock) * E;
     int off[KMAX];
     bool dropped = false;
 #pragma unroll
     for (int k = 0; k < KMAX; ++k)
-        off[k] = ids[k] >= 0 ? final_slot(a, psum[ids[k]], base[ids[k]] + lr[k], dropped) : 0;
+        off[k] = ids[k] >= 0 ? final_slot(a, psum[ids[k]], mybase[ids[k]] + lr[k], dropped) : 0;
     flag_dropped<KMAX>(a, dropped);
     store_slots<KMAX>(a, t, ids, off);
-    write_padding<NT>(a, tot, psum, b, C);
+    write_padding<NT>(a, tot, psum, b, blocks);
     if (b == 0) {
         write_expert_arrays<NT>(a, tot, psum);
         flush_rank_totals<NT>(a);
