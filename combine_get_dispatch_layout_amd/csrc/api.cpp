@@ -44,7 +44,7 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 struct Carve {
     int64_t ctrl, psum_expert, psum_rank, num_unaligned, recv_list, topk, slot, meta, hist,
-        acc, src_acc, src_base, src_psum, rank_ids, ne_scratch, total;
+        acc, src_acc, src_base, src_psum, rank_ids, ne_scratch, ne_hist, total;
 };
 
 int num_sources(const ep_config& c) { return c.num_sources > 1 ? c.num_sources : 1; }
@@ -173,8 +173,9 @@ ep_status carve(const ep_config& c, int64_t max_tokens, Carve* o)
     if (c.non_expand) {
         o->rank_ids = take(4 * max_tokens * c.num_topk);
         o->ne_scratch = take(4 * (3 * (int64_t)c.num_ranks + 1));   // psum', counts', list'
+        o->ne_hist = take(4 * Cc * c.num_ranks);   // the rank level's block histograms
     } else {
-        o->rank_ids = o->ne_scratch = -1;
+        o->rank_ids = o->ne_scratch = o->ne_hist = -1;
     }
     o->total = off;
     return EP_OK;
@@ -194,7 +195,7 @@ struct ep_handle {
     // layout counted inside a dispatch launch, to be finished inside the
     // next ep_combine_overlap launch (see ep_dispatch_overlap)
     bool pending = false;
-    epk::LayoutArgs pending_args;
+    epk::LayoutArgs pending_args, pending_args2;   // second: the rank level (non-expand)
     epk::OverlapPlan pending_plan;
     // events armed by ep_set_kernel_events for the next call
     mutable epk::LaunchEvents armed;
@@ -263,6 +264,11 @@ ep_status layout_args(ep_handle* h, const int32_t* d_topk_idx, int64_t num_token
     a.in_rank_words = (c.num_ranks % 4 == 0) && aligned(d_is_token_in_rank, 4);
     a.row_vec = c.num_topk % 4 == 0;
     a.topk_vec = a.row_vec && aligned(d_topk_idx, 16);
+    a.derive_src = nullptr;
+    a.derive_magic = 0u;
+    a.derive_E = 0;
+    a.counts_only = false;
+    a.no_rank_counts = false;
     return EP_OK;
 }
 
@@ -336,24 +342,23 @@ hipError_t launch_layout_all(const ep_handle* h, const epk::LayoutArgs& a, hipSt
 // followed by the layout of the derived rank-id routing, whose rows are the
 // receive rows (one per token and rank); it writes slot_idx, src_meta, the
 // row count and, through its per-"expert" prefix, psum_rank.
-hipError_t launch_layout_nonexpand(const ep_handle* h, const epk::LayoutArgs& a, hipStream_t s,
-                                   epk::LaunchEvents ev)
+// The rank-level layout of a non-expand handle: the expand layout
+// (alignment 1) of the derived routing whose entries are the ranks of the
+// expert routing's entries, each rank once per row, over R one-expert ranks.
+// Its slots are the receive rows; its per-"expert" prefix is psum_rank.  The
+// routing is derived inline from the expert routing (the derived rows are
+// kept in rank_ids, the level's clone).
+epk::LayoutArgs rank_level_args(const ep_handle* h, const epk::LayoutArgs& a)
 {
-    hipError_t e = launch_layout_all(h, a, s, epk::LaunchEvents{ev.start, nullptr});
-    if (e != hipSuccess) return e;
-    epk::RankIdArgs ra;
-    ra.topk = a.topk;
-    ra.num_tokens = a.num_tokens;
-    ra.K = a.K;
-    ra.E = a.E;
-    ra.nle = a.nle;
-    ra.rank_ids = h->at<int32_t>(h->cv.rank_ids);
-    e = epk::launch_rank_ids(ra, s);
-    if (e != hipSuccess) return e;
     epk::LayoutArgs b = a;
     int32_t* scratch = h->at<int32_t>(h->cv.ne_scratch);
-    b.topk = ra.rank_ids;
-    b.topk_clone = ra.rank_ids;            // rewrites the same values
+    b.derive_src = a.topk;
+    b.derive_magic = a.nle_magic;
+    b.derive_E = a.E;
+    b.topk_clone = h->at<int32_t>(h->cv.rank_ids);
+    b.hist = h->at<int32_t>(h->cv.ne_hist);
+    b.no_rank_counts = true;               // the expert level counts tokens per rank
+    b.counts_only = false;
     b.E = a.R;
     b.nle = 1;
     b.nle_magic = 0;
@@ -372,8 +377,15 @@ hipError_t launch_layout_nonexpand(const ep_handle* h, const epk::LayoutArgs& a,
     b.out_per_expert = nullptr;
     b.out_in_rank = nullptr;
     b.in_rank_words = false;
-    b.topk_vec = b.row_vec;                // workspace rows are 256-byte aligned
-    return epk::launch_layout(b, s, epk::LaunchEvents{nullptr, ev.stop});
+    return b;
+}
+
+hipError_t launch_layout_nonexpand(const ep_handle* h, const epk::LayoutArgs& a, hipStream_t s,
+                                   epk::LaunchEvents ev)
+{
+    hipError_t e = launch_layout_all(h, a, s, epk::LaunchEvents{ev.start, nullptr});
+    if (e != hipSuccess) return e;
+    return epk::launch_layout(rank_level_args(h, a), s, epk::LaunchEvents{nullptr, ev.stop});
 }
 
 hipError_t launch_layout_any(const ep_handle* h, const epk::LayoutArgs& a, hipStream_t s,
@@ -430,7 +442,7 @@ ep_status combine_args(const ep_handle* h, const void* d_y, const float* d_y_sca
 ep_status next_layout(const ep_handle* h, ep_handle* h_next, const int32_t* d_topk_next,
                       int64_t num_tokens_next, int32_t* d_per_rank, int32_t* d_per_rdma,
                       int32_t* d_per_expert, uint8_t* d_in_rank, int64_t dispatch_bytes,
-                      epk::LayoutArgs* la, epk::OverlapPlan* plan)
+                      epk::LayoutArgs* la, epk::LayoutArgs* lb, epk::OverlapPlan* plan)
 {
     if (h_next == h) return EP_FAIL(EP_ERR_INVALID_ARG, "h_next must differ from h");
     if (memcmp(&h->cfg, &h_next->cfg, sizeof(ep_config)) != 0)
@@ -439,8 +451,17 @@ ep_status next_layout(const ep_handle* h, ep_handle* h_next, const int32_t* d_to
                                d_per_expert, d_in_rank, la);
     if (st != EP_OK) return st;
     const ep_config& c = h_next->cfg;
-    *plan = (c.non_expand || num_sources(c) > 1) ? epk::OverlapPlan{}
-                                                 : epk::plan_overlap(*la, dispatch_bytes);
+    *lb = *la;
+    if (num_sources(c) > 1) {
+        *plan = epk::OverlapPlan{};
+    } else if (c.non_expand) {
+        // both levels side by side; the expert level only counts
+        *lb = rank_level_args(h_next, *la);
+        *plan = epk::plan_overlap_twin(*la, *lb);
+        if (plan->ok) la->counts_only = true;
+    } else {
+        *plan = epk::plan_overlap(*la, dispatch_bytes);
+    }
     return EP_OK;
 }
 
@@ -662,18 +683,18 @@ ep_status ep_dispatch_overlap(const ep_handle* h, const void* d_x, int64_t token
         EP_HIP(epk::launch_dispatch(da, s, h->take_events()));
         return EP_OK;
     }
-    epk::LayoutArgs la;
+    epk::LayoutArgs la, lb;
     epk::OverlapPlan plan;
     // bytes this dispatch writes: one row per pair (codes: one byte per element)
     const int64_t dispatch_bytes = (token_end - token_begin) * h->cfg.num_topk *
                                    h->cfg.hidden * (h->cfg.quant == EP_QUANT_NONE ? 2 : 1);
     st = next_layout(h, h_next, d_topk_next, num_tokens_next, d_num_tokens_per_rank,
                      d_num_tokens_per_rdma_rank, d_num_tokens_per_expert, d_is_token_in_rank,
-                     dispatch_bytes, &la, &plan);
+                     dispatch_bytes, &la, &lb, &plan);
     if (st != EP_OK) return st;
     const epk::LaunchEvents ev = h->take_events();
     if (plan.ok) {
-        EP_HIP(epk::launch_dispatch_layout(da, la, plan, s, ev));
+        EP_HIP(epk::launch_dispatch_layout(da, la, lb, plan, s, ev));
     } else {
         EP_HIP(epk::launch_dispatch(da, s, epk::LaunchEvents{ev.start, nullptr}));
         EP_HIP(launch_layout_any(h_next, la, s, epk::LaunchEvents{nullptr, ev.stop}));
@@ -682,6 +703,7 @@ ep_status ep_dispatch_overlap(const ep_handle* h, const void* d_x, int64_t token
     h_next->host_slots = -1;
     h_next->pending = plan.ok && !plan.fused;
     h_next->pending_args = la;
+    h_next->pending_args2 = lb;
     h_next->pending_plan = plan;
     return EP_OK;
 }
@@ -702,7 +724,8 @@ ep_status ep_combine_overlap(const ep_handle* h, const void* d_y, const float* d
     if (h_next == h) return EP_FAIL(EP_ERR_INVALID_ARG, "h_next must differ from h");
     if (memcmp(&h->cfg, &h_next->cfg, sizeof(ep_config)) != 0)
         return EP_FAIL(EP_ERR_INVALID_ARG, "h and h_next must have the same configuration");
-    EP_HIP(epk::launch_combine_layout(ca, h_next->pending_args, h_next->pending_plan, s,
+    EP_HIP(epk::launch_combine_layout(ca, h_next->pending_args, h_next->pending_args2,
+                                      h_next->pending_plan, s,
                                       h->take_events()));
     h_next->pending = false;
     return EP_OK;

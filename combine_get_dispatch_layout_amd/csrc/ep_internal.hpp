@@ -65,6 +65,17 @@ struct LayoutArgs {
     // [N,K] rows move as 16-byte vectors: row_vec for the workspace arrays
     // (K % 4 == 0), topk_vec for the caller's routing (also 16-byte aligned)
     bool row_vec, topk_vec;
+    // Non-expand in two concurrent layouts (one per level):
+    //   derive_src:     non-null: the ids are the ranks of this [N,K] expert
+    //                   routing (expert / nle via derive_magic, ids outside
+    //                   [0, derive_E) and repeats of a rank in a row masked)
+    //   counts_only:    no in-block ranks, slots, source metadata, padding
+    //                   rows, psum_rank or slot count (the other level's)
+    //   no_rank_counts: no distinct-token accumulation or flush
+    const int32_t* derive_src;
+    uint32_t derive_magic;
+    int derive_E;
+    bool counts_only, no_rank_counts;
 };
 
 struct DispatchArgs {
@@ -79,15 +90,6 @@ struct DispatchArgs {
     int scale_mode;             // 0 fp32 amax/qmax, 1 power of two, 2 power of two as E8M0
     bool identity;              // row t goes to receive row t (K = 1): row quantisation
     uint32_t* flags;
-};
-
-// Non-expand layout: the derived routing (rank of each entry, repeats of a
-// rank in a row masked).
-struct RankIdArgs {
-    const int32_t* topk;        // [N,K] caller's routing
-    int64_t num_tokens;
-    int K, E, nle;
-    int32_t* rank_ids;          // [N,K] out
 };
 
 // Non-expand per-row routing (recv_topk_idx / recv_topk_weights).
@@ -158,7 +160,6 @@ hipError_t launch_layout(const LayoutArgs& a, hipStream_t s, LaunchEvents ev = {
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s, LaunchEvents ev = {});
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s, LaunchEvents ev = {});
 hipError_t launch_sources(const SourceArgs& a, hipStream_t s, LaunchEvents ev = {});
-hipError_t launch_rank_ids(const RankIdArgs& a, hipStream_t s, LaunchEvents ev = {});
 hipError_t launch_recv_topk(const RecvTopkArgs& a, hipStream_t s, LaunchEvents ev = {});
 // The next batch's layout inside the current batch's dispatch and combine
 // launches (overlap.hip): which phase goes where, and the LDS each launch
@@ -166,6 +167,7 @@ hipError_t launch_recv_topk(const RecvTopkArgs& a, hipStream_t s, LaunchEvents e
 struct OverlapPlan {
     bool ok = false;          // false: lay the next batch out on its own
     bool fused = false;       // the whole layout in one block of the dispatch launch
+    bool twin = false;        // non-expand: two layouts (expert level, rank level), C blocks each
     int dispatch_blocks = 0;  // layout blocks in front of the dispatch blocks
     int combine_blocks = 0;   // count blocks whose finish phase the combine launch runs
     size_t dispatch_lds = 0;
@@ -174,10 +176,14 @@ struct OverlapPlan {
 // dispatch_bytes: what the dispatch launch that takes the layout's first
 // phase moves (decides whether a small batch is laid out in one block).
 OverlapPlan plan_overlap(const LayoutArgs& la, int64_t dispatch_bytes);
+// Non-expand: the expert-level layout `la` (counts only) and the rank-level
+// layout `lb` (rank ids derived from la's routing) side by side.
+OverlapPlan plan_overlap_twin(const LayoutArgs& la, const LayoutArgs& lb);
 hipError_t launch_dispatch_layout(const DispatchArgs& da, const LayoutArgs& la,
-                                  const OverlapPlan& p, hipStream_t s, LaunchEvents ev = {});
-hipError_t launch_combine_layout(const CombineArgs& ca, const LayoutArgs& la, const OverlapPlan& p,
-                                 hipStream_t s, LaunchEvents ev = {});
+                                  const LayoutArgs& lb, const OverlapPlan& p, hipStream_t s,
+                                  LaunchEvents ev = {});
+hipError_t launch_combine_layout(const CombineArgs& ca, const LayoutArgs& la, const LayoutArgs& lb,
+                                 const OverlapPlan& p, hipStream_t s, LaunchEvents ev = {});
 // Layout + dispatch of the whole batch in one launch (small batches).
 bool route_dispatch_fits(const LayoutArgs& la);
 hipError_t launch_route_dispatch(const LayoutArgs& la, const DispatchArgs& da, hipStream_t s,

@@ -8,12 +8,11 @@
 // k on r, later entries on r get slot -1.  That is exactly the expand layout
 // (alignment 1) of a derived routing whose entry k is the rank of expert
 // idx[t,k], with repeats of a rank inside a row masked, over R "experts"
-// (one per rank).  So the host runs the ordinary layout kernels a second
-// time on that derived routing (k_rank_ids writes it), and dispatch and
-// combine run unchanged: a -1 slot is skipped, so each (t, r) row is written
-// once and summed once.
+// (one per rank).  So the layout kernels run a second time, on that derived
+// routing, which they compute from the expert routing as they load it
+// (LayoutArgs::derive_src); dispatch and combine run unchanged: a -1 slot is
+// skipped, so each (t, r) row is written once and summed once.
 //
-//   k_rank_ids   one thread per token: the derived routing [N,K]
 //   k_recv_topk  one thread per (t,k) owning a row: the row's local expert
 //                ids (idx - r*nle where the expert is on r, else -1) and
 //                weights (0 where not on r)
@@ -24,32 +23,6 @@ namespace epk {
 namespace {
 
 constexpr int kBlock = 256;
-
-template <int KMAX>
-__global__ __launch_bounds__(kBlock) void k_rank_ids(RankIdArgs a)
-{
-    const int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    if (t >= a.num_tokens) return;
-    const int K = a.K;
-    int rk[KMAX];
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k) {
-        int r = -1;
-        if (k < K) {
-            const int e = a.topk[t * K + k];
-            if (e >= 0 && e < a.E) r = e / a.nle;   // bad ids are flagged by the expert pass
-        }
-        rk[k] = r;
-    }
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k) {
-        if (k >= K) break;
-        bool first = rk[k] >= 0;
-#pragma unroll
-        for (int q = 0; q < k; ++q) first &= rk[q] != rk[k];
-        a.rank_ids[t * K + k] = first ? rk[k] : -1;
-    }
-}
 
 template <int KMAX>
 __global__ __launch_bounds__(kBlock) void k_recv_topk(RecvTopkArgs a)
@@ -75,24 +48,7 @@ __global__ __launch_bounds__(kBlock) void k_recv_topk(RecvTopkArgs a)
     }
 }
 
-template <int KMAX>
-hipError_t launch_rank_ids_k(const RankIdArgs& a, hipStream_t s, LaunchEvents ev)
-{
-    const int blocks = (int)((a.num_tokens + kBlock - 1) / kBlock);
-    if (blocks == 0) return hipSuccess;
-    launch_k(k_rank_ids<KMAX>, dim3(blocks), dim3(kBlock), 0, s, ev.start, ev.stop, a);
-    return hipGetLastError();
-}
-
 }  // namespace
-
-hipError_t launch_rank_ids(const RankIdArgs& a, hipStream_t s, LaunchEvents ev)
-{
-    if (a.K <= 2) return launch_rank_ids_k<2>(a, s, ev);
-    if (a.K <= 4) return launch_rank_ids_k<4>(a, s, ev);
-    if (a.K <= 8) return launch_rank_ids_k<8>(a, s, ev);
-    return launch_rank_ids_k<16>(a, s, ev);
-}
 
 hipError_t launch_recv_topk(const RecvTopkArgs& a, hipStream_t s, LaunchEvents ev)
 {

@@ -44,49 +44,69 @@ constexpr int64_t kOverlapSplitMinBytes = 4 << 20;
 // are left to the compiler.
 constexpr int dl_waves(bool channel, int vpl) { return (channel && vpl >= 8) ? 1 : 8; }
 
+// Layout work of the dispatch launch's first blocks.
+constexpr int kModeCount = 0, kModeFused = 1, kModeTwin = 2;
+
+// lblocks layout blocks come first: the one-block layout (kModeFused), the
+// count phase of la (kModeCount), or (kModeTwin, non-expand) the count
+// phases of la in blocks [0, lblocks/2) and of lb in the rest.
 template <int QUANT, bool CHANNEL, int VPL, bool ROW_WAIT, int LK>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(dl_waves(CHANNEL, VPL))))
-void k_dispatch_layout(DispatchArgs da, int NV, int NC, LayoutArgs la, int lblocks, int fused)
+void k_dispatch_layout(DispatchArgs da, int NV, int NC, LayoutArgs la, LayoutArgs lb, int lblocks,
+                       int mode)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     if ((int)blockIdx.x < lblocks) {
-        if (fused) route::fused_body<LK, kWPB>(la, smem);
-        else route::count_body<LK>(la, blockIdx.x, smem);
+        if (mode == kModeFused) {
+            route::fused_body<LK, kWPB>(la, smem);
+        } else if (mode == kModeTwin) {
+            const int C = lblocks / 2;
+            if ((int)blockIdx.x < C) route::count_body<LK>(la, blockIdx.x, smem);
+            else route::count_body<LK>(lb, blockIdx.x - C, smem);
+        } else {
+            route::count_body<LK>(la, blockIdx.x, smem);
+        }
         return;
     }
     scatter::dispatch_wave<QUANT, CHANNEL, VPL, 8, ROW_WAIT, kWPB>(da, NV, NC, blockIdx.x - lblocks);
 }
 
 // C: the count blocks of the layout; lblocks = ceil(C / (BLOCK/256)) finish
-// blocks come first.
+// blocks come first -- twice as many with twin (non-expand): those of la,
+// then those of lb.
 template <int KMAX, int VPL, int YQ, bool YCH, int BLOCK>
 __global__ __launch_bounds__(BLOCK) void k_combine_layout(CombineArgs ca, int NV, int NC,
-                                                          LayoutArgs la, int lblocks, int C)
+                                                          LayoutArgs la, LayoutArgs lb, int lblocks,
+                                                          int C, int twin)
 {
     extern __shared__ __align__(16) unsigned char smem[];
-    if ((int)blockIdx.x < lblocks) {
-        route::finish_lean<KMAX, BLOCK>(la, C, blockIdx.x, smem);
+    const int all = twin ? 2 * lblocks : lblocks;
+    if ((int)blockIdx.x < all) {
+        if ((int)blockIdx.x < lblocks) route::finish_lean<KMAX, BLOCK>(la, C, blockIdx.x, smem);
+        else route::finish_lean<KMAX, BLOCK>(lb, C, blockIdx.x - lblocks, smem);
         return;
     }
-    gather::combine_wave<KMAX, VPL, YQ, YCH, BLOCK / kWave>(ca, NV, NC, blockIdx.x - lblocks);
+    gather::combine_wave<KMAX, VPL, YQ, YCH, BLOCK / kWave>(ca, NV, NC, blockIdx.x - all);
 }
 
 template <int QUANT, bool CHANNEL, int VPL, bool ROW_WAIT, int LK>
-hipError_t launch_dl(const DispatchArgs& da, int NV, const LayoutArgs& la, const OverlapPlan& p,
-                     hipStream_t s, LaunchEvents ev)
+hipError_t launch_dl(const DispatchArgs& da, int NV, const LayoutArgs& la, const LayoutArgs& lb,
+                     const OverlapPlan& p, hipStream_t s, LaunchEvents ev)
 {
     const int NC = (NV + kWave * VPL - 1) / (kWave * VPL);
     const int64_t items = (da.t_end - da.t_begin) * NC;
     const int dblocks = items > 0 ? (int)((items + kWPB - 1) / kWPB) : 0;
+    if (p.dispatch_blocks + dblocks == 0) return hipSuccess;
+    const int mode = p.fused ? kModeFused : p.twin ? kModeTwin : kModeCount;
     launch_k(k_dispatch_layout<QUANT, CHANNEL, VPL, ROW_WAIT, LK>, dim3(p.dispatch_blocks + dblocks),
-             dim3(kBlock), p.dispatch_lds, s, ev.start, ev.stop, da, NV, NC, la, p.dispatch_blocks,
-             p.fused ? 1 : 0);
+             dim3(kBlock), p.dispatch_lds, s, ev.start, ev.stop, da, NV, NC, la, lb,
+             p.dispatch_blocks, mode);
     return hipGetLastError();
 }
 
 template <int KMAX, int YQ, bool YCH>
-hipError_t launch_cl(const CombineArgs& ca, const LayoutArgs& la, const OverlapPlan& p,
-                     hipStream_t s, LaunchEvents ev)
+hipError_t launch_cl(const CombineArgs& ca, const LayoutArgs& la, const LayoutArgs& lb,
+                     const OverlapPlan& p, hipStream_t s, LaunchEvents ev)
 {
     constexpr int VPL = 2;
     const int NV = ca.H / 8;
@@ -96,11 +116,14 @@ hipError_t launch_cl(const CombineArgs& ca, const LayoutArgs& la, const OverlapP
     auto go = [&](auto block) {
         constexpr int B = decltype(block)::value, WPB = B / kWave, G = B / kLayoutBlock;
         const int lblocks = (C + G - 1) / G;
+        const int all = p.twin ? 2 * lblocks : lblocks;
         const int cblocks = items > 0 ? (int)((items + WPB - 1) / WPB) : 0;
-        if (lblocks + cblocks == 0) return hipSuccess;
-        const size_t lds = C > 0 ? route::finish_lean_lds_bytes(la, B) : 0;
-        launch_k(k_combine_layout<KMAX, VPL, YQ, YCH, B>, dim3(lblocks + cblocks), dim3(B), lds,
-                 s, ev.start, ev.stop, ca, NV, NC, la, lblocks, C);
+        if (all + cblocks == 0) return hipSuccess;
+        size_t lds = C > 0 ? route::finish_lean_lds_bytes(la, B) : 0;
+        if (p.twin && route::finish_lean_lds_bytes(lb, B) > lds)
+            lds = route::finish_lean_lds_bytes(lb, B);
+        launch_k(k_combine_layout<KMAX, VPL, YQ, YCH, B>, dim3(all + cblocks), dim3(B), lds, s,
+                 ev.start, ev.stop, ca, NV, NC, la, lb, lblocks, C, p.twin ? 1 : 0);
         return hipGetLastError();
     };
     // 256-thread blocks: at the combine's 5 waves per SIMD a CU holds five
@@ -110,27 +133,27 @@ hipError_t launch_cl(const CombineArgs& ca, const LayoutArgs& la, const OverlapP
 }
 
 template <int LK>
-hipError_t launch_dl_k(const DispatchArgs& da, const LayoutArgs& la, const OverlapPlan& p,
-                       hipStream_t s, LaunchEvents ev)
+hipError_t launch_dl_k(const DispatchArgs& da, const LayoutArgs& la, const LayoutArgs& lb,
+                       const OverlapPlan& p, hipStream_t s, LaunchEvents ev)
 {
     auto launch = [&](auto q, auto ch, auto vpl, auto rw, int NV) {
         return launch_dl<decltype(q)::value, decltype(ch)::value, decltype(vpl)::value,
-                         decltype(rw)::value, LK>(da, NV, la, p, s, ev);
+                         decltype(rw)::value, LK>(da, NV, la, lb, p, s, ev);
     };
     return dispatch_shape(da, launch);
 }
 
 template <int KMAX>
-hipError_t launch_cl_k(const CombineArgs& ca, const LayoutArgs& la, const OverlapPlan& p,
-                       hipStream_t s, LaunchEvents ev)
+hipError_t launch_cl_k(const CombineArgs& ca, const LayoutArgs& la, const LayoutArgs& lb,
+                       const OverlapPlan& p, hipStream_t s, LaunchEvents ev)
 {
     const bool ych = ca.ygroup == ca.H && ca.H != 128;
     switch (ca.yquant) {
-        case 0: return launch_cl<KMAX, 0, false>(ca, la, p, s, ev);
-        case 1: return ych ? launch_cl<KMAX, 1, true>(ca, la, p, s, ev)
-                           : launch_cl<KMAX, 1, false>(ca, la, p, s, ev);
-        default: return ych ? launch_cl<KMAX, 2, true>(ca, la, p, s, ev)
-                            : launch_cl<KMAX, 2, false>(ca, la, p, s, ev);
+        case 0: return launch_cl<KMAX, 0, false>(ca, la, lb, p, s, ev);
+        case 1: return ych ? launch_cl<KMAX, 1, true>(ca, la, lb, p, s, ev)
+                           : launch_cl<KMAX, 1, false>(ca, la, lb, p, s, ev);
+        default: return ych ? launch_cl<KMAX, 2, true>(ca, la, lb, p, s, ev)
+                            : launch_cl<KMAX, 2, false>(ca, la, lb, p, s, ev);
     }
 }
 
@@ -167,18 +190,44 @@ OverlapPlan plan_overlap(const LayoutArgs& la, int64_t dispatch_bytes)
     return p;
 }
 
+// Non-expand: the count and finish phases of both levels, C blocks each.
+// The expert level only counts (its slots are not the receive rows); the
+// rank level takes its routing straight from the expert routing and leaves
+// the distinct-token totals to the expert level.
+OverlapPlan plan_overlap_twin(const LayoutArgs& la, const LayoutArgs& lb)
+{
+    OverlapPlan p;
+    if (la.K > 8) return p;
+    const int C = (int)((la.num_tokens + kLayoutBlock - 1) / kLayoutBlock);
+    if (C == 0) return p;
+    const size_t ca = route::route_lds_bytes(kWPB, la.E, la.R, la.nodes);
+    const size_t cb = route::route_lds_bytes(kWPB, lb.E, lb.R, lb.nodes);
+    const size_t fa = route::finish_lean_lds_bytes(la, kBlock);
+    const size_t fb = route::finish_lean_lds_bytes(lb, kBlock);
+    const size_t count = ca > cb ? ca : cb, finish = fa > fb ? fa : fb;
+    if (count > kOverlapMaxLds || finish > kOverlapMaxLds) return p;
+    p.ok = true;
+    p.twin = true;
+    p.dispatch_blocks = 2 * C;
+    p.combine_blocks = C;
+    p.dispatch_lds = count;
+    p.combine_lds = finish;
+    return p;
+}
+
 // One instantiation for every K <= 8 (entries past K are masked), which
 // keeps the number of merged kernels down.
 hipError_t launch_dispatch_layout(const DispatchArgs& da, const LayoutArgs& la,
-                                  const OverlapPlan& p, hipStream_t s, LaunchEvents ev)
+                                  const LayoutArgs& lb, const OverlapPlan& p, hipStream_t s,
+                                  LaunchEvents ev)
 {
-    return launch_dl_k<8>(da, la, p, s, ev);
+    return launch_dl_k<8>(da, la, lb, p, s, ev);
 }
 
-hipError_t launch_combine_layout(const CombineArgs& ca, const LayoutArgs& la, const OverlapPlan& p,
-                                 hipStream_t s, LaunchEvents ev)
+hipError_t launch_combine_layout(const CombineArgs& ca, const LayoutArgs& la, const LayoutArgs& lb,
+                                 const OverlapPlan& p, hipStream_t s, LaunchEvents ev)
 {
-    return launch_cl_k<8>(ca, la, p, s, ev);
+    return launch_cl_k<8>(ca, la, lb, p, s, ev);
 }
 
 }  // namespace epk

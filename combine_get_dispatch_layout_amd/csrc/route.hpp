@@ -109,6 +109,22 @@ template <int KMAX>
 __device__ __forceinline__ bool load_ids(const LayoutArgs& a, int64_t t, bool valid,
                                          int (&ids)[KMAX])
 {
+    if (a.derive_src != nullptr) {
+        // the ranks of the expert routing's row, each rank once (bad expert
+        // ids are masked here and flagged by the expert-level layout)
+        load_row<KMAX>(a.derive_src + t * a.K, a.K, a.topk_vec, valid, -1, ids);
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+            ids[k] = (ids[k] >= 0 && ids[k] < a.derive_E) ? div_by(ids[k], a.derive_magic) : -1;
+#pragma unroll
+        for (int k = KMAX - 1; k > 0; --k) {
+            bool rep = false;
+#pragma unroll
+            for (int q = 0; q < k; ++q) rep |= ids[q] == ids[k];
+            if (rep) ids[k] = -1;
+        }
+        return false;
+    }
     load_row<KMAX>(a.topk + t * a.K, a.K, a.topk_vec, valid, -1, ids);
     bool bad = false;
 #pragma unroll
@@ -391,6 +407,7 @@ __device__ __forceinline__ void write_expert_arrays(const LayoutArgs& a, const i
             a.recv_list[e] = a.counts_as_prefix ? psum[e + 1] - psum[first] : psum[e + 1] - psum[e];
         }
     }
+    if (a.counts_only) return;   // the rank-level layout writes these
     for (int r = tid; r <= a.R; r += NT) a.psum_rank[r] = psum[r * a.nle];
     if (tid == 0) a.ctrl[kCtrlNumSlots] = (uint32_t)psum[E];
 }
@@ -512,8 +529,9 @@ __device__ __forceinline__ void count_body(const LayoutArgs& a, int b, unsigned 
     route_block<KMAX, WAVES>(a, t0, L, ids, lr);
     const int tid = threadIdx.x, K = a.K;
     const int64_t t = t0 + tid;
-    if (t < a.num_tokens) store_row<KMAX>(a.slot_idx + t * K, K, a.row_vec, lr);
+    if (t < a.num_tokens && !a.counts_only) store_row<KMAX>(a.slot_idx + t * K, K, a.row_vec, lr);
     for (int e = tid; e < a.E; e += kLayoutBlock) a.hist[(int64_t)b * a.E + e] = L.bhist[e];
+    if (a.no_rank_counts) return;
     for (int r = tid; r < a.R; r += kLayoutBlock)
         if (L.rcnt[r] != 0) atomicAdd(a.rank_acc + r, L.rcnt[r]);
     for (int n = tid; n < a.nodes; n += kLayoutBlock)
@@ -567,7 +585,7 @@ __device__ __forceinline__ void finish_lean(const LayoutArgs& a, int C, int b, u
     int32_t* part_all = part_pre + NT;                  // [NT]
 
     const int64_t t = (int64_t)b * NT + tid;
-    const bool tv = t < a.num_tokens;
+    const bool tv = t < a.num_tokens && !a.counts_only;
     int ids[KMAX], lr[KMAX];
     load_row<KMAX>(a.topk_clone + t * K, K, a.row_vec, tv, -1, ids);
     load_row<KMAX>(a.slot_idx + t * K, K, a.row_vec, tv, 0, lr);
@@ -616,18 +634,21 @@ __device__ __forceinline__ void finish_lean(const LayoutArgs& a, int C, int b, u
     }
     aligned_prefix<NT>(a, tot, psum, scratch);
 
-    const int32_t* mybase = base + (tid / kLayoutBlock) * E;
-    int off[KMAX];
-    bool dropped = false;
+    if (!a.counts_only) {
+        const int32_t* mybase = base + (tid / kLayoutBlock) * E;
+        int off[KMAX];
+        bool dropped = false;
 #pragma unroll
-    for (int k = 0; k < KMAX; ++k)
-        off[k] = ids[k] >= 0 ? final_slot(a, psum[ids[k]], mybase[ids[k]] + lr[k], dropped) : 0;
-    flag_dropped<KMAX>(a, dropped);
-    store_slots<KMAX>(a, t, ids, off);
-    write_padding<NT>(a, tot, psum, b, blocks);
+        for (int k = 0; k < KMAX; ++k)
+            off[k] =
+                ids[k] >= 0 ? final_slot(a, psum[ids[k]], mybase[ids[k]] + lr[k], dropped) : 0;
+        flag_dropped<KMAX>(a, dropped);
+        store_slots<KMAX>(a, t, ids, off);
+        write_padding<NT>(a, tot, psum, b, blocks);
+    }
     if (b == 0) {
         write_expert_arrays<NT>(a, tot, psum);
-        flush_rank_totals<NT>(a);
+        if (!a.no_rank_counts) flush_rank_totals<NT>(a);
     }
 }
 

@@ -589,6 +589,13 @@ def _overlap_sequence(w, sizes, seeds):
         ref_out = oracle.combine(y_bits, b["wts"], ref_slots["slot_idx"])
         compare_combine(bits16(b["out"]), ref_out, bf16_values(y_bits), b["wts"],
                         ref_slots["slot_idx"], w.num_topk)
+        if w.non_expand and ref_slots["S"] > 0:
+            ri, rw = ep.ep_dispatch_topk(h, b["wts_d"], rows=b["cap"])
+            ref_ri, ref_rw = oracle.recv_topk(b["idx"], b["wts"], ref_slots["src_meta"],
+                                              w.num_experts, w.num_ranks)
+            S = ref_slots["S"]
+            assert np.array_equal(ri[:S].cpu().numpy(), ref_ri)
+            assert np.array_equal(rw[:S].cpu().numpy().view(np.uint32), ref_rw.view(np.uint32))
         # the next batch's layout, complete after this combine
         if nxt is not None:
             run.lay, run.h = nlay, hn
@@ -621,6 +628,15 @@ def test_overlap_empty_and_non_expand():
     _say("[parity] overlap with an empty batch and non-expand")
     _overlap_sequence(w, [700, 0, 300], [3, 4, 5])
     _overlap_sequence(w.scaled(non_expand=True), [500, 400], [6, 7])
+
+
+def test_overlap_non_expand_group_limited():
+    """Non-expand batches whose expert-level and rank-level layouts both run
+    inside the dispatch and combine launches (group-limited gating routing,
+    ragged block counts, a batch of one token)."""
+    w = W.WORKLOADS["deepseek_v3_group_limited"].scaled(hidden=512)
+    _say("[parity] overlap non-expand group-limited")
+    _overlap_sequence(w, [3000, 1000, 2049, 1, 700], [21, 22, 23, 24, 25])
 
 
 @pytest.mark.parametrize("n,two_phase", [(1000, True), (200, False)])
