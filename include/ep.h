@@ -288,13 +288,14 @@ ep_status ep_combine(const ep_handle* h, const void* d_y, const float* d_y_scale
  *   start of ep_get_layout(h_next, d_topk_next, num_tokens_next, <the four
  *   outputs>, do_cpu_sync = 0): every argument has the meaning, layout and
  *   checks given there.  h_next must differ from h and have the same
- *   configuration.  For num_tokens_next <= 256 the layout completes in this
- *   launch; otherwise it completes in the next ep_combine_overlap(..., h_next)
- *   call, and until then h_next may be used only there (other calls return
+ *   configuration.  For num_tokens_next <= 256 (and a dispatch that moves
+ *   under 4 MiB; without non_expand) the layout completes in this launch;
+ *   otherwise it completes in the next ep_combine_overlap(..., h_next) call,
+ *   and until then h_next may be used only there (other calls return
  *   EP_ERR_STATE; ep_get_layout or ep_layout_dispatch on it start over).
  *   Configurations whose layout cannot share the launch (num_topk > 8,
- *   stacked sources, non_expand, a routing LDS above 24 KiB) lay h_next out
- *   with the ordinary kernels after the dispatch.
+ *   stacked sources, a routing LDS above 24 KiB) lay h_next out with the
+ *   ordinary kernels after the dispatch.
  * ep_combine_overlap: ep_combine(h, ...) and, when h_next is waiting, the
  *   rest of its layout.  With h_next NULL or not waiting it is ep_combine.
  * Kernel events armed on h (ep_set_kernel_events) span the call's launches. */
