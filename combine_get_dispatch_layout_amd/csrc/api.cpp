@@ -196,6 +196,7 @@ struct ep_handle {
     // next ep_combine_overlap launch (see ep_dispatch_overlap)
     bool pending = false;
     epk::LayoutArgs pending_args, pending_args2;   // second: the rank level (non-expand)
+    epk::SourceArgs pending_src;                   // stacked sources
     epk::OverlapPlan pending_plan;
     // events armed by ep_set_kernel_events for the next call
     mutable epk::LaunchEvents armed;
@@ -316,11 +317,10 @@ ep_status dispatch_args(const ep_handle* h, int64_t num_tokens, const void* d_x,
 
 // Layout kernels, preceded with several sources by the per-source counts;
 // `ev` spans all of them.
-hipError_t launch_layout_all(const ep_handle* h, const epk::LayoutArgs& a, hipStream_t s,
-                             epk::LaunchEvents ev)
+// The per-source counts of a stacked-sources layout `a` (P > 1).
+epk::SourceArgs source_args(const ep_handle* h, const epk::LayoutArgs& a)
 {
     const int P = num_sources(h->cfg);
-    if (P == 1) return epk::launch_layout(a, s, ev);
     epk::SourceArgs sa;
     sa.topk = a.topk;
     sa.tokens_per_source = a.num_tokens / P;
@@ -333,6 +333,14 @@ hipError_t launch_layout_all(const ep_handle* h, const epk::LayoutArgs& a, hipSt
     sa.acc_rank = sa.acc_expert + (int64_t)P * a.E;
     sa.expert_source_base = h->at<int32_t>(h->cv.src_base);
     sa.psum_source_rank = h->at<int32_t>(h->cv.src_psum);
+    return sa;
+}
+
+hipError_t launch_layout_all(const ep_handle* h, const epk::LayoutArgs& a, hipStream_t s,
+                             epk::LaunchEvents ev)
+{
+    if (num_sources(h->cfg) == 1) return epk::launch_layout(a, s, ev);
+    const epk::SourceArgs sa = source_args(h, a);
     hipError_t e = epk::launch_sources(sa, s, epk::LaunchEvents{ev.start, nullptr});
     if (e != hipSuccess) return e;
     return epk::launch_layout(a, s, epk::LaunchEvents{nullptr, ev.stop});
@@ -442,7 +450,8 @@ ep_status combine_args(const ep_handle* h, const void* d_y, const float* d_y_sca
 ep_status next_layout(const ep_handle* h, ep_handle* h_next, const int32_t* d_topk_next,
                       int64_t num_tokens_next, int32_t* d_per_rank, int32_t* d_per_rdma,
                       int32_t* d_per_expert, uint8_t* d_in_rank, int64_t dispatch_bytes,
-                      epk::LayoutArgs* la, epk::LayoutArgs* lb, epk::OverlapPlan* plan)
+                      epk::LayoutArgs* la, epk::LayoutArgs* lb, epk::SourceArgs* sa,
+                      epk::OverlapPlan* plan)
 {
     if (h_next == h) return EP_FAIL(EP_ERR_INVALID_ARG, "h_next must differ from h");
     if (memcmp(&h->cfg, &h_next->cfg, sizeof(ep_config)) != 0)
@@ -452,8 +461,15 @@ ep_status next_layout(const ep_handle* h, ep_handle* h_next, const int32_t* d_to
     if (st != EP_OK) return st;
     const ep_config& c = h_next->cfg;
     *lb = *la;
+    *sa = epk::SourceArgs{};
     if (num_sources(c) > 1) {
-        *plan = epk::OverlapPlan{};
+        // stacked sources: the per-source counts ride in the same launches
+        if (c.non_expand) {
+            *plan = epk::OverlapPlan{};
+        } else {
+            *sa = source_args(h_next, *la);
+            *plan = epk::plan_overlap_sources(*la, *sa, dispatch_bytes);
+        }
     } else if (c.non_expand) {
         // both levels side by side; the expert level only counts
         *lb = rank_level_args(h_next, *la);
@@ -684,26 +700,29 @@ ep_status ep_dispatch_overlap(const ep_handle* h, const void* d_x, int64_t token
         return EP_OK;
     }
     epk::LayoutArgs la, lb;
+    epk::SourceArgs sa;
     epk::OverlapPlan plan;
     // bytes this dispatch writes: one row per pair (codes: one byte per element)
     const int64_t dispatch_bytes = (token_end - token_begin) * h->cfg.num_topk *
                                    h->cfg.hidden * (h->cfg.quant == EP_QUANT_NONE ? 2 : 1);
     st = next_layout(h, h_next, d_topk_next, num_tokens_next, d_num_tokens_per_rank,
                      d_num_tokens_per_rdma_rank, d_num_tokens_per_expert, d_is_token_in_rank,
-                     dispatch_bytes, &la, &lb, &plan);
+                     dispatch_bytes, &la, &lb, &sa, &plan);
     if (st != EP_OK) return st;
     const epk::LaunchEvents ev = h->take_events();
     if (plan.ok) {
-        EP_HIP(epk::launch_dispatch_layout(da, la, lb, plan, s, ev));
+        EP_HIP(epk::launch_dispatch_layout(da, la, lb, sa, plan, s, ev));
     } else {
         EP_HIP(epk::launch_dispatch(da, s, epk::LaunchEvents{ev.start, nullptr}));
         EP_HIP(launch_layout_any(h_next, la, s, epk::LaunchEvents{nullptr, ev.stop}));
     }
     h_next->num_tokens = num_tokens_next;
     h_next->host_slots = -1;
-    h_next->pending = plan.ok && !plan.fused;
+    // pending until the combine launch finishes the layout or the source counts
+    h_next->pending = plan.ok && (!plan.fused || plan.src_combine_blocks > 0);
     h_next->pending_args = la;
     h_next->pending_args2 = lb;
+    h_next->pending_src = sa;
     h_next->pending_plan = plan;
     return EP_OK;
 }
@@ -725,7 +744,7 @@ ep_status ep_combine_overlap(const ep_handle* h, const void* d_y, const float* d
     if (memcmp(&h->cfg, &h_next->cfg, sizeof(ep_config)) != 0)
         return EP_FAIL(EP_ERR_INVALID_ARG, "h and h_next must have the same configuration");
     EP_HIP(epk::launch_combine_layout(ca, h_next->pending_args, h_next->pending_args2,
-                                      h_next->pending_plan, s,
+                                      h_next->pending_src, h_next->pending_plan, s,
                                       h->take_events()));
     h_next->pending = false;
     return EP_OK;

@@ -21,7 +21,7 @@ constexpr int kLayoutBlock = 256;
 // (channel) quantisation scale: 64 lanes x 16 vectors = 8192 bf16.
 constexpr int kMaxVecPerLane = 16;
 // Largest batch whose layout + dispatch run as one launch (every block
-// recomputes the routing of the whole batch in LDS).
+// counts the whole batch's routing in LDS).
 constexpr int kRouteDispatchMaxTokens = 256;
 
 constexpr uint32_t kFlagBadId = 1u;
@@ -29,9 +29,7 @@ constexpr uint32_t kFlagCapacity = 2u;
 constexpr uint32_t kFlagYRows = 4u;
 
 // Control words at the start of the workspace.
-// kCtrlTicket counts finished blocks of the routing kernel; the last block
-// resets it to zero for the next call.
-enum CtrlWord { kCtrlFlags = 0, kCtrlNumSlots = 1, kCtrlTicket = 2, kCtrlWords = 64 };
+enum CtrlWord { kCtrlFlags = 0, kCtrlNumSlots = 1, kCtrlWords = 64 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -172,6 +170,8 @@ struct OverlapPlan {
     int combine_blocks = 0;   // count blocks whose finish phase the combine launch runs
     size_t dispatch_lds = 0;
     size_t combine_lds = 0;   // LDS of the finish phase
+    int src_dispatch_blocks = 0;   // stacked sources: per-source histogram blocks
+    int src_combine_blocks = 0;    // ... and per-source scan blocks
 };
 // dispatch_bytes: what the dispatch launch that takes the layout's first
 // phase moves (decides whether a small batch is laid out in one block).
@@ -179,11 +179,15 @@ OverlapPlan plan_overlap(const LayoutArgs& la, int64_t dispatch_bytes);
 // Non-expand: the expert-level layout `la` (counts only) and the rank-level
 // layout `lb` (rank ids derived from la's routing) side by side.
 OverlapPlan plan_overlap_twin(const LayoutArgs& la, const LayoutArgs& lb);
+// Stacked sources: plan_overlap plus the per-source counts (sa).
+OverlapPlan plan_overlap_sources(const LayoutArgs& la, const SourceArgs& sa,
+                                 int64_t dispatch_bytes);
 hipError_t launch_dispatch_layout(const DispatchArgs& da, const LayoutArgs& la,
-                                  const LayoutArgs& lb, const OverlapPlan& p, hipStream_t s,
-                                  LaunchEvents ev = {});
+                                  const LayoutArgs& lb, const SourceArgs& sa,
+                                  const OverlapPlan& p, hipStream_t s, LaunchEvents ev = {});
 hipError_t launch_combine_layout(const CombineArgs& ca, const LayoutArgs& la, const LayoutArgs& lb,
-                                 const OverlapPlan& p, hipStream_t s, LaunchEvents ev = {});
+                                 const SourceArgs& sa, const OverlapPlan& p, hipStream_t s,
+                                 LaunchEvents ev = {});
 // Layout + dispatch of the whole batch in one launch (small batches).
 bool route_dispatch_fits(const LayoutArgs& la);
 hipError_t launch_route_dispatch(const LayoutArgs& la, const DispatchArgs& da, hipStream_t s,

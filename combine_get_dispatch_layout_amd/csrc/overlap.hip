@@ -24,6 +24,7 @@
 #include "gather.hpp"
 #include "route.hpp"
 #include "scatter.hpp"
+#include "sources.hpp"
 
 namespace epk {
 
@@ -49,13 +50,19 @@ constexpr int kModeCount = 0, kModeFused = 1, kModeTwin = 2;
 
 // lblocks layout blocks come first: the one-block layout (kModeFused), the
 // count phase of la (kModeCount), or (kModeTwin, non-expand) the count
-// phases of la in blocks [0, lblocks/2) and of lb in the rest.
+// phases of la in blocks [0, lblocks/2) and of lb in the rest; then, with
+// stacked sources, sblocks blocks of the per-source histogram.
 template <int QUANT, bool CHANNEL, int VPL, bool ROW_WAIT, int LK>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(dl_waves(CHANNEL, VPL))))
-void k_dispatch_layout(DispatchArgs da, int NV, int NC, LayoutArgs la, LayoutArgs lb, int lblocks,
-                       int mode)
+void k_dispatch_layout(DispatchArgs da, int NV, int NC, LayoutArgs la, LayoutArgs lb,
+                       SourceArgs sa, int lblocks, int mode, int sblocks)
 {
     extern __shared__ __align__(16) unsigned char smem[];
+    if ((int)blockIdx.x >= lblocks && (int)blockIdx.x < lblocks + sblocks) {
+        const int i = blockIdx.x - lblocks, chunks = sources::hist_chunks(sa);
+        sources::hist_body<LK>(sa, i % chunks, i / chunks, reinterpret_cast<int32_t*>(smem));
+        return;
+    }
     if ((int)blockIdx.x < lblocks) {
         if (mode == kModeFused) {
             route::fused_body<LK, kWPB>(la, smem);
@@ -68,16 +75,19 @@ void k_dispatch_layout(DispatchArgs da, int NV, int NC, LayoutArgs la, LayoutArg
         }
         return;
     }
-    scatter::dispatch_wave<QUANT, CHANNEL, VPL, 8, ROW_WAIT, kWPB>(da, NV, NC, blockIdx.x - lblocks);
+    scatter::dispatch_wave<QUANT, CHANNEL, VPL, 8, ROW_WAIT, kWPB>(da, NV, NC,
+                                                                 blockIdx.x - lblocks - sblocks);
 }
 
 // C: the count blocks of the layout; lblocks = ceil(C / (BLOCK/256)) finish
 // blocks come first -- twice as many with twin (non-expand): those of la,
-// then those of lb.
+// then those of lb -- then, with stacked sources, sblocks blocks of the
+// per-source scan.
 template <int KMAX, int VPL, int YQ, bool YCH, int BLOCK>
 __global__ __launch_bounds__(BLOCK) void k_combine_layout(CombineArgs ca, int NV, int NC,
-                                                          LayoutArgs la, LayoutArgs lb, int lblocks,
-                                                          int C, int twin)
+                                                          LayoutArgs la, LayoutArgs lb,
+                                                          SourceArgs sa, int lblocks, int C,
+                                                          int twin, int sblocks)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     const int all = twin ? 2 * lblocks : lblocks;
@@ -86,27 +96,33 @@ __global__ __launch_bounds__(BLOCK) void k_combine_layout(CombineArgs ca, int NV
         else route::finish_lean<KMAX, BLOCK>(lb, C, blockIdx.x - lblocks, smem);
         return;
     }
-    gather::combine_wave<KMAX, VPL, YQ, YCH, BLOCK / kWave>(ca, NV, NC, blockIdx.x - all);
+    if ((int)blockIdx.x < all + sblocks) {
+        if (BLOCK == sources::kScanBlock) sources::scan_body(sa, blockIdx.x - all);
+        return;
+    }
+    gather::combine_wave<KMAX, VPL, YQ, YCH, BLOCK / kWave>(ca, NV, NC,
+                                                          blockIdx.x - all - sblocks);
 }
 
 template <int QUANT, bool CHANNEL, int VPL, bool ROW_WAIT, int LK>
 hipError_t launch_dl(const DispatchArgs& da, int NV, const LayoutArgs& la, const LayoutArgs& lb,
-                     const OverlapPlan& p, hipStream_t s, LaunchEvents ev)
+                     const SourceArgs& sa, const OverlapPlan& p, hipStream_t s, LaunchEvents ev)
 {
     const int NC = (NV + kWave * VPL - 1) / (kWave * VPL);
     const int64_t items = (da.t_end - da.t_begin) * NC;
     const int dblocks = items > 0 ? (int)((items + kWPB - 1) / kWPB) : 0;
-    if (p.dispatch_blocks + dblocks == 0) return hipSuccess;
+    const int blocks = p.dispatch_blocks + p.src_dispatch_blocks + dblocks;
+    if (blocks == 0) return hipSuccess;
     const int mode = p.fused ? kModeFused : p.twin ? kModeTwin : kModeCount;
-    launch_k(k_dispatch_layout<QUANT, CHANNEL, VPL, ROW_WAIT, LK>, dim3(p.dispatch_blocks + dblocks),
-             dim3(kBlock), p.dispatch_lds, s, ev.start, ev.stop, da, NV, NC, la, lb,
-             p.dispatch_blocks, mode);
+    launch_k(k_dispatch_layout<QUANT, CHANNEL, VPL, ROW_WAIT, LK>, dim3(blocks), dim3(kBlock),
+             p.dispatch_lds, s, ev.start, ev.stop, da, NV, NC, la, lb, sa, p.dispatch_blocks, mode,
+             p.src_dispatch_blocks);
     return hipGetLastError();
 }
 
 template <int KMAX, int YQ, bool YCH>
 hipError_t launch_cl(const CombineArgs& ca, const LayoutArgs& la, const LayoutArgs& lb,
-                     const OverlapPlan& p, hipStream_t s, LaunchEvents ev)
+                     const SourceArgs& sa, const OverlapPlan& p, hipStream_t s, LaunchEvents ev)
 {
     constexpr int VPL = 2;
     const int NV = ca.H / 8;
@@ -117,13 +133,15 @@ hipError_t launch_cl(const CombineArgs& ca, const LayoutArgs& la, const LayoutAr
         constexpr int B = decltype(block)::value, WPB = B / kWave, G = B / kLayoutBlock;
         const int lblocks = (C + G - 1) / G;
         const int all = p.twin ? 2 * lblocks : lblocks;
+        const int sblocks = p.src_combine_blocks;
         const int cblocks = items > 0 ? (int)((items + WPB - 1) / WPB) : 0;
-        if (all + cblocks == 0) return hipSuccess;
+        if (all + sblocks + cblocks == 0) return hipSuccess;
         size_t lds = C > 0 ? route::finish_lean_lds_bytes(la, B) : 0;
         if (p.twin && route::finish_lean_lds_bytes(lb, B) > lds)
             lds = route::finish_lean_lds_bytes(lb, B);
-        launch_k(k_combine_layout<KMAX, VPL, YQ, YCH, B>, dim3(all + cblocks), dim3(B), lds, s,
-                 ev.start, ev.stop, ca, NV, NC, la, lb, lblocks, C, p.twin ? 1 : 0);
+        launch_k(k_combine_layout<KMAX, VPL, YQ, YCH, B>, dim3(all + sblocks + cblocks), dim3(B),
+                 lds, s, ev.start, ev.stop, ca, NV, NC, la, lb, sa, lblocks, C, p.twin ? 1 : 0,
+                 sblocks);
         return hipGetLastError();
     };
     // 256-thread blocks: at the combine's 5 waves per SIMD a CU holds five
@@ -134,26 +152,26 @@ hipError_t launch_cl(const CombineArgs& ca, const LayoutArgs& la, const LayoutAr
 
 template <int LK>
 hipError_t launch_dl_k(const DispatchArgs& da, const LayoutArgs& la, const LayoutArgs& lb,
-                       const OverlapPlan& p, hipStream_t s, LaunchEvents ev)
+                       const SourceArgs& sa, const OverlapPlan& p, hipStream_t s, LaunchEvents ev)
 {
     auto launch = [&](auto q, auto ch, auto vpl, auto rw, int NV) {
         return launch_dl<decltype(q)::value, decltype(ch)::value, decltype(vpl)::value,
-                         decltype(rw)::value, LK>(da, NV, la, lb, p, s, ev);
+                         decltype(rw)::value, LK>(da, NV, la, lb, sa, p, s, ev);
     };
     return dispatch_shape(da, launch);
 }
 
 template <int KMAX>
 hipError_t launch_cl_k(const CombineArgs& ca, const LayoutArgs& la, const LayoutArgs& lb,
-                       const OverlapPlan& p, hipStream_t s, LaunchEvents ev)
+                       const SourceArgs& sa, const OverlapPlan& p, hipStream_t s, LaunchEvents ev)
 {
     const bool ych = ca.ygroup == ca.H && ca.H != 128;
     switch (ca.yquant) {
-        case 0: return launch_cl<KMAX, 0, false>(ca, la, lb, p, s, ev);
-        case 1: return ych ? launch_cl<KMAX, 1, true>(ca, la, lb, p, s, ev)
-                           : launch_cl<KMAX, 1, false>(ca, la, lb, p, s, ev);
-        default: return ych ? launch_cl<KMAX, 2, true>(ca, la, lb, p, s, ev)
-                            : launch_cl<KMAX, 2, false>(ca, la, lb, p, s, ev);
+        case 0: return launch_cl<KMAX, 0, false>(ca, la, lb, sa, p, s, ev);
+        case 1: return ych ? launch_cl<KMAX, 1, true>(ca, la, lb, sa, p, s, ev)
+                           : launch_cl<KMAX, 1, false>(ca, la, lb, sa, p, s, ev);
+        default: return ych ? launch_cl<KMAX, 2, true>(ca, la, lb, sa, p, s, ev)
+                            : launch_cl<KMAX, 2, false>(ca, la, lb, sa, p, s, ev);
     }
 }
 
@@ -217,17 +235,34 @@ OverlapPlan plan_overlap_twin(const LayoutArgs& la, const LayoutArgs& lb)
 
 // One instantiation for every K <= 8 (entries past K are masked), which
 // keeps the number of merged kernels down.
-hipError_t launch_dispatch_layout(const DispatchArgs& da, const LayoutArgs& la,
-                                  const LayoutArgs& lb, const OverlapPlan& p, hipStream_t s,
-                                  LaunchEvents ev)
+// Stacked sources: the layout's own plan, plus the per-source histogram
+// blocks in the dispatch launch and the per-source scan blocks in the
+// combine launch (the source arrays are then complete after the combine).
+OverlapPlan plan_overlap_sources(const LayoutArgs& la, const SourceArgs& sa,
+                                 int64_t dispatch_bytes)
 {
-    return launch_dl_k<8>(da, la, lb, p, s, ev);
+    OverlapPlan p = plan_overlap(la, dispatch_bytes);
+    if (!p.ok) return p;
+    const size_t hist = sources::hist_lds_bytes(sa);
+    if (hist > kOverlapMaxLds) return OverlapPlan{};
+    if (hist > p.dispatch_lds) p.dispatch_lds = hist;
+    p.src_dispatch_blocks = sources::hist_chunks(sa) * sa.P;
+    p.src_combine_blocks = sources::scan_blocks(sa);
+    return p;
+}
+
+hipError_t launch_dispatch_layout(const DispatchArgs& da, const LayoutArgs& la,
+                                  const LayoutArgs& lb, const SourceArgs& sa,
+                                  const OverlapPlan& p, hipStream_t s, LaunchEvents ev)
+{
+    return launch_dl_k<8>(da, la, lb, sa, p, s, ev);
 }
 
 hipError_t launch_combine_layout(const CombineArgs& ca, const LayoutArgs& la, const LayoutArgs& lb,
-                                 const OverlapPlan& p, hipStream_t s, LaunchEvents ev)
+                                 const SourceArgs& sa, const OverlapPlan& p, hipStream_t s,
+                                 LaunchEvents ev)
 {
-    return launch_cl_k<8>(ca, la, lb, p, s, ev);
+    return launch_cl_k<8>(ca, la, lb, sa, p, s, ev);
 }
 
 }  // namespace epk

@@ -19,98 +19,34 @@
 //   k_source_scan  one thread per expert or rank column: exclusive prefix
 //                  over sources, loads batched 8 deep; the accumulators are
 //                  re-zeroed behind the reads.
-#include "ep_internal.hpp"
+#include "sources.hpp"
 
 namespace epk {
 
 namespace {
 
-constexpr int kHistBlock = 256;
-constexpr int kScanBlock = 256;
-constexpr int kScanBatch = 8;
+using namespace sources;
 
 template <int KMAX>
 __global__ __launch_bounds__(kHistBlock) void k_source_hist(SourceArgs a)
 {
     extern __shared__ __align__(16) int32_t lds[];
-    int32_t* hist = lds;          // [E]
-    int32_t* rc = lds + a.E;      // [R]
-    const int tid = threadIdx.x;
-    const int p = blockIdx.y;
-    for (int i = tid; i < a.E + a.R; i += kHistBlock) lds[i] = 0;
-    const int64_t tl = (int64_t)blockIdx.x * kHistBlock + tid;
-    int ids[KMAX];
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k) {
-        int v = -1;
-        if (k < a.K && tl < a.tokens_per_source) {
-            v = a.topk[((int64_t)p * a.tokens_per_source + tl) * a.K + k];
-            if (v < 0 || v >= a.E) v = -1;   // bad ids are flagged by the layout kernels
-        }
-        ids[k] = v;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k)
-        if (ids[k] >= 0) atomicAdd(hist + ids[k], 1);
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k) {
-        if (ids[k] < 0) continue;
-        const int r = ids[k] / a.nle;
-        bool first = true;
-#pragma unroll
-        for (int q = 0; q < k; ++q) first &= (ids[q] < 0 || ids[q] / a.nle != r);
-        if (first) atomicAdd(rc + r, 1);
-    }
-    __syncthreads();
-    for (int e = tid; e < a.E; e += kHistBlock)
-        if (hist[e] != 0) atomicAdd(a.acc_expert + (int64_t)p * a.E + e, hist[e]);
-    for (int r = tid; r < a.R; r += kHistBlock)
-        if (rc[r] != 0) atomicAdd(a.acc_rank + (int64_t)p * a.R + r, rc[r]);
+    hist_body<KMAX>(a, blockIdx.x, blockIdx.y, lds);
 }
 
 __global__ __launch_bounds__(kScanBlock) void k_source_scan(SourceArgs a)
 {
-    const int col = blockIdx.x * kScanBlock + threadIdx.x;
-    if (col >= a.E + a.R) return;
-    const bool is_expert = col < a.E;
-    const int c = is_expert ? col : col - a.E;
-    const int stride = is_expert ? a.E : a.R;
-    int32_t* acc = is_expert ? a.acc_expert : a.acc_rank;
-    const int P = a.P;
-    int run = 0;
-    if (!is_expert) a.psum_source_rank[(int64_t)c * (P + 1)] = 0;
-    for (int p0 = 0; p0 < P; p0 += kScanBatch) {
-        int v[kScanBatch];
-#pragma unroll
-        for (int j = 0; j < kScanBatch; ++j)
-            v[j] = p0 + j < P ? acc[(int64_t)(p0 + j) * stride + c] : 0;
-#pragma unroll
-        for (int j = 0; j < kScanBatch; ++j) {
-            const int p = p0 + j;
-            if (p >= P) break;
-            acc[(int64_t)p * stride + c] = 0;
-            if (is_expert) {
-                a.expert_source_base[(int64_t)p * a.E + c] = run;
-                run += v[j];
-            } else {
-                run += v[j];
-                a.psum_source_rank[(int64_t)c * (P + 1) + p + 1] = run;
-            }
-        }
-    }
+    scan_body(a, blockIdx.x);
 }
 
 template <int KMAX>
 hipError_t launch_sources_k(const SourceArgs& a, hipStream_t s, LaunchEvents ev)
 {
-    const int chunks = (int)((a.tokens_per_source + kHistBlock - 1) / kHistBlock);
-    const size_t lds = (size_t)(a.E + a.R) * 4;
+    const int chunks = hist_chunks(a);
     if (chunks > 0)
-        launch_k(k_source_hist<KMAX>, dim3(chunks, a.P), dim3(kHistBlock), lds, s, ev.start,
-                 nullptr, a);
-    const int cols = a.E + a.R;
-    launch_k(k_source_scan, dim3((cols + kScanBlock - 1) / kScanBlock), dim3(kScanBlock), 0, s,
+        launch_k(k_source_hist<KMAX>, dim3(chunks, a.P), dim3(kHistBlock), hist_lds_bytes(a), s,
+                 ev.start, nullptr, a);
+    launch_k(k_source_scan, dim3(scan_blocks(a)), dim3(kScanBlock), 0, s,
              chunks > 0 ? nullptr : ev.start, ev.stop, a);
     return hipGetLastError();
 }

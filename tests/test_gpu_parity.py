@@ -630,6 +630,16 @@ def test_overlap_empty_and_non_expand():
     _overlap_sequence(w.scaled(non_expand=True), [500, 400], [6, 7])
 
 
+@pytest.mark.parametrize("P,sizes", [(4, [1000, 256, 4096, 8]), (16, [4096, 2048])])
+def test_overlap_stacked_sources(P, sizes):
+    """Stacked sources: the per-source counts ride in the dispatch (histogram)
+    and combine (scan) launches beside the layout, for the split layout and
+    the one-block layout of a small batch."""
+    w = _custom(N=1, H=256, E=128, R=16, K=8, A=4).scaled(num_sources=P)
+    _say(f"[parity] overlap stacked sources P={P} sizes {sizes}")
+    _overlap_sequence(w, sizes, [31 + i for i in range(len(sizes))])
+
+
 def test_overlap_non_expand_group_limited():
     """Non-expand batches whose expert-level and rank-level layouts both run
     inside the dispatch and combine launches (group-limited gating routing,
