@@ -10,9 +10,9 @@ Default workload: the Qwen3-30B-A3B-shaped prefill (4096 tokens, hidden 2048
 bf16, 128 experts over 16 simulated ranks, top-8).
 
 --pipeline picks how a step is issued: merged (default; the layout of the
-next batch runs inside this batch's dispatch and combine launches, one
-stream), overlap (the default for workloads of several rounds; the layout of
-the next batch runs on a second stream),
+next batch runs inside this batch's dispatch and combine launches -- those of
+its first round -- on one stream), overlap (the layout of the next batch runs
+on a second stream),
 serial (one stream), fused
 (ep_layout_dispatch + combine, the one-call form for decode batches) or
 cached (dispatch + combine on a handle whose layout was computed once before
@@ -273,7 +273,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pipeline", choices=("merged", "overlap", "serial", "fused", "cached"),
                     default=None,
-                    help="(default: merged, or overlap for a workload of several rounds) "
+                    help="(default: merged) "
                          "merged: batch i+1's layout runs inside batch i's dispatch and "
                          "combine launches (ep_dispatch_overlap / ep_combine_overlap), one "
                          "stream; overlap: batch i+1's layout runs on a second stream during "
@@ -297,8 +297,7 @@ def main():
                     help="summarise two rocprofv3 --pmc runs into profiles/ and exit")
     args = ap.parse_args()
     if args.pipeline is None:
-        import workloads as W
-        args.pipeline = "merged" if W.WORKLOADS[args.workload].rounds == 1 else "overlap"
+        args.pipeline = "merged"
     if args.traffic_from:
         traffic_summary(args.traffic_from[0], args.traffic_from[1], args.workload, args.pipeline)
         return
@@ -386,16 +385,21 @@ def main():
         calls = []   # (stage index, bound call) in issue order
         if pl == "merged":
             # this set's batch is dispatched and combined while the next set's
-            # batch (the next step's) is laid out inside the same launches
+            # batch (the next step's) is laid out inside the same launches:
+            # those of the first round; later rounds are plain calls
             t = sets[(si + 1) % nsets]
-            calls.append((0, ep.bind_dispatch_overlap(s["h"], s["x"], s["recv"], s["scales"], 0, N,
-                                                      t["h"], t["topk"], t["per_rank"],
+            wts = None if w.non_expand else s["wts"]
+            (b0, e0), rest = rounds[0], rounds[1:]
+            calls.append((0, ep.bind_dispatch_overlap(s["h"], s["x"], s["recv"], s["scales"], b0,
+                                                      e0, t["h"], t["topk"], t["per_rank"],
                                                       t["per_node"], t["per_expert"], t["in_rank"],
                                                       stream=stream)))
-            calls.append((1, ep.bind_combine_overlap(s["h"], s["y"],
-                                                     None if w.non_expand else s["wts"], s["out"],
-                                                     0, N, t["h"], stream=stream,
-                                                     y_scales=s["y_scales"])))
+            calls += [(0, ep.bind_dispatch(s["h"], s["x"], s["recv"], s["scales"], b, e,
+                                           stream=stream)) for b, e in rest]
+            calls.append((1, ep.bind_combine_overlap(s["h"], s["y"], wts, s["out"], b0, e0, t["h"],
+                                                     stream=stream, y_scales=s["y_scales"])))
+            calls += [(1, ep.bind_combine(s["h"], s["y"], wts, s["out"], b, e, stream=stream,
+                                          y_scales=s["y_scales"])) for b, e in rest]
             s["calls"] = calls
             s["lay_done"] = torch.cuda.Event()
             s["main_done"] = torch.cuda.Event()
@@ -466,8 +470,6 @@ def main():
         s["main_done"].record(stream)
 
     if pl == "merged":
-        if len(rounds) != 1:
-            sys.exit("--pipeline merged overlaps whole batches: the workload must have one round")
         # the first batch's layout; every later one is laid out one step ahead
         ep.ep_get_layout(sets[0]["h"], sets[0]["topk"], sets[0]["per_rank"], sets[0]["per_node"],
                          sets[0]["per_expert"], sets[0]["in_rank"])
@@ -553,10 +555,11 @@ def main():
     t_dom, b_dom, launches = stages[dom]
     achieved = b_dom / t_dom / 1e9   # = per-launch bytes / mean per-launch time
     b_dc = sum(stages[k][1] for k in moving)
-    # the kernel that carries the stage (merged: the launch that also lays
-    # out the next batch)
+    # the kernel that carries the stage (merged, one round: the launch that
+    # also lays out the next batch; with rounds, most launches are plain)
+    merged1 = pl == "merged" and len(rounds) == 1
     traffic = traffic_from_profiles({"dispatch": "dispatch_layout", "combine": "combine_layout"}
-                                    .get(dom, dom) if pl == "merged" else dom, w.name)
+                                    .get(dom, dom) if merged1 else dom, w.name)
 
     # achievable reference: a plain 1 GiB device copy
     a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -593,7 +596,7 @@ def main():
                                              "count phase)",
                                  "combine": "k_combine_layout (combine + next batch's layout "
                                             "finish phase)"}.get(dom, dom)
-                                if pl == "merged" else dom),
+                                if merged1 else dom),
                      "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": b_dom / launches,

@@ -630,6 +630,58 @@ def test_overlap_empty_and_non_expand():
     _overlap_sequence(w.scaled(non_expand=True), [500, 400], [6, 7])
 
 
+def test_overlap_with_rounds():
+    """A batch dispatched and combined in rounds (token ranges of one handle)
+    while the next batch is laid out inside the first round's launches."""
+    from shuffle_check import bits16, compare_layout, config_of, oracle_slots
+    w = W.WORKLOADS["long_seq_int8"].scaled(num_tokens=3000, hidden=1024, quant_group=1024)
+    cfg = config_of(w)
+    rounds = W.round_ranges(3000, 3)
+    hs = [ep.ep_handle_init(cfg, 3000), ep.ep_handle_init(cfg, 3000)]
+    bs = []
+    for sd in (41, 42):
+        wb = w.scaled(seed=sd)
+        idx, wts = W.routing(wb)
+        cap = ep.ep_recv_capacity(cfg, 3000)
+        bs.append(dict(w=wb, idx=idx, wts=wts, topk=torch.from_numpy(idx).cuda(),
+                       wd=torch.from_numpy(wts).cuda(), x=W.activations(3000, 1024, sd, device="cuda"),
+                       recv=torch.zeros((cap, cfg.recv_row_elems), dtype=cfg.recv_dtype,
+                                        device="cuda"),
+                       scales=torch.zeros((cap, cfg.num_groups), dtype=cfg.scales_dtype,
+                                          device="cuda"),
+                       out=torch.zeros((3000, 1024), dtype=torch.bfloat16, device="cuda")))
+    _say("[parity] overlap with rounds")
+    ep.ep_get_layout(hs[0], bs[0]["topk"])
+    b, nb = bs[0], bs[1]
+    (b0, e0), rest = rounds[0], rounds[1:]
+    nlay = ep.ep_dispatch_overlap(hs[0], b["x"], b["recv"], b["scales"], b0, e0, h_next=hs[1],
+                                  topk_next=nb["topk"])
+    for lo, hi in rest:
+        ep.ep_dispatch(hs[0], b["x"], b["recv"], b["scales"], lo, hi)
+    ref = oracle_slots(b["w"], b["idx"])
+    y = W.activations(max(ref["S"], 1), 1024, 77, device="cuda")
+    ep.ep_combine_overlap(hs[0], y, b["wd"], b["out"], b0, e0, h_next=hs[1])
+    for lo, hi in rest:
+        ep.ep_combine(hs[0], y, b["wd"], b["out"], lo, hi)
+    assert ep.ep_check_error(hs[0]) == (ep.EP_OK, 0)
+    ref_recv, ref_scales = oracle.dispatch(bits16(b["x"]), ref["slot_idx"], b["recv"].shape[0],
+                                           quant=w.quant, group=w.quant_group)
+
+    class R:
+        pass
+    run = R()
+    run.w, run.recv, run.scales = b["w"], b["recv"], b["scales"]
+    from shuffle_check import compare_dispatch, compare_combine, bf16_values
+    compare_dispatch(run, ref_recv, ref_scales, ref)
+    y_bits = bits16(y)
+    compare_combine(bits16(b["out"]), oracle.combine(y_bits, b["wts"], ref["slot_idx"]),
+                    bf16_values(y_bits), b["wts"], ref["slot_idx"], w.num_topk)
+    run.lay, run.h = nlay, hs[1]
+    compare_layout(run, nb["idx"], oracle.layout(nb["idx"], w.num_experts, w.num_ranks,
+                                                 w.ranks_per_node),
+                   oracle_slots(nb["w"], nb["idx"]), host_sync=False)
+
+
 @pytest.mark.parametrize("P,sizes", [(4, [1000, 256, 4096, 8]), (16, [4096, 2048])])
 def test_overlap_stacked_sources(P, sizes):
     """Stacked sources: the per-source counts ride in the dispatch (histogram)
