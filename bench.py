@@ -69,8 +69,8 @@ KERNEL_SOURCES = {"dispatch": ("dispatch.hip", "scatter.hpp"),
                   "combine": ("combine.hip", "gather.hpp"),
                   "layout": ("layout.hip", "route.hpp"),
                   "layout_dispatch": ("fused.hip", "route.hpp", "scatter.hpp"),
-                  "dispatch_layout": ("overlap.hip", "scatter.hpp", "route.hpp"),
-                  "combine_layout": ("overlap.hip", "gather.hpp", "route.hpp")}
+                  "dispatch_layout": ("overlap.hip", "scatter.hpp", "route.hpp", "sources.hpp"),
+                  "combine_layout": ("overlap.hip", "gather.hpp", "route.hpp", "sources.hpp")}
 
 
 def kernel_source_hash(kernel):
