@@ -21,7 +21,9 @@
 // written to each of the token's K rows; slots are wave-uniform scalar loads.
 // For 128-element groups a group is exactly 16 lanes x one vector, so the
 // group max is a 4-step butterfly inside a 16-lane row; a channel scale is a
-// full-wave reduction (the chunk then covers the whole row).  Padding rows
+// full-wave reduction (the chunk then covers the whole row).  The quotient
+// x / scale takes one reciprocal per group and a fused multiply-add
+// correction per element, which rounds exactly as the division would.  Padding rows
 // are never written.  HBM-bound: no LDS, no MFMA.
 #include "scatter.hpp"
 

@@ -223,7 +223,8 @@ ep_status ep_get_layout(ep_handle* h, const int32_t* d_topk_idx, int64_t num_tok
  *     nearest-even (E4M3FN saturating, int8 clamped to +-127).  MXFP4: per 32
  *     elements e = floor(log2 amax) - 2 clamped to [-127, 127] (-127 when
  *     amax is 0), scale byte e + 127, codes E2M1(x * 2^-e) nearest-even,
- *     saturating at 6.
+ *     saturating at 6.  The quantised formats expect finite x: a row or
+ *     group holding an infinity or NaN gets unspecified codes and scale.
  *   Reusing a handle across calls is cached dispatch ([P3] §3.2).
  *   EP_ERR_CAPACITY if S is known on the host and exceeds the capacity;
  *   otherwise rows beyond it are skipped and flagged on the device. */
