@@ -271,6 +271,8 @@ def main():
                     help=">1: read the batch as this many stacked source ranks (receive order "
                          "(source, token, k) plus the per-source counts)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle passes behind cpu_baseline")
     ap.add_argument("--pipeline", choices=("merged", "overlap", "serial", "fused", "cached"),
                     default=None,
                     help="(default: merged) "
@@ -388,7 +390,7 @@ def main():
             # batch (the next step's) is laid out inside the same launches:
             # those of the first round; later rounds are plain calls
             t = sets[(si + 1) % nsets]
-            wts = None if w.non_expand else s["wts"]
+            cw = None if w.non_expand else s["wts"]
             (b0, e0), rest = rounds[0], rounds[1:]
             calls.append((0, ep.bind_dispatch_overlap(s["h"], s["x"], s["recv"], s["scales"], b0,
                                                       e0, t["h"], t["topk"], t["per_rank"],
@@ -396,9 +398,9 @@ def main():
                                                       stream=stream)))
             calls += [(0, ep.bind_dispatch(s["h"], s["x"], s["recv"], s["scales"], b, e,
                                            stream=stream)) for b, e in rest]
-            calls.append((1, ep.bind_combine_overlap(s["h"], s["y"], wts, s["out"], b0, e0, t["h"],
+            calls.append((1, ep.bind_combine_overlap(s["h"], s["y"], cw, s["out"], b0, e0, t["h"],
                                                      stream=stream, y_scales=s["y_scales"])))
-            calls += [(1, ep.bind_combine(s["h"], s["y"], wts, s["out"], b, e, stream=stream,
+            calls += [(1, ep.bind_combine(s["h"], s["y"], cw, s["out"], b, e, stream=stream,
                                           y_scales=s["y_scales"])) for b, e in rest]
             s["calls"] = calls
             s["lay_done"] = torch.cuda.Event()
@@ -616,7 +618,7 @@ def main():
         "recv_rows": S, "valid_pairs": V,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, idx, wts)
+        line["cpu_baseline"] = cpu_baseline(w, idx, wts, budget_s=args.cpu_budget)
     print(json.dumps(line), flush=True)
 
 

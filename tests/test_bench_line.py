@@ -1,0 +1,44 @@
+"""The benchmark's command-line contract: `python bench.py` prints one JSON
+line with the metric, the roofline of the dominant kernel and the oracle's
+CPU baseline; more than one GPU is refused with a message."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _run(args, timeout):
+    return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args], cwd=ROOT,
+                          capture_output=True, text=True, timeout=timeout)
+
+
+def test_more_than_one_gpu_refused():
+    r = _run(["--gpus", "2"], 120)
+    assert r.returncode != 0
+    assert "one GPU" in r.stdout + r.stderr
+
+
+@pytest.mark.gpu
+def test_default_line_has_the_contract_fields():
+    # the default workload and pipeline, few steps, a short oracle budget
+    print("bench.py --steps 20 --warmup 5 --cpu-budget 2", flush=True)
+    r = _run(["--steps", "20", "--warmup", "5", "--cpu-budget", "2"], 300)
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-4000:]
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    for k in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+              "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config"):
+        assert k in line, k
+    assert line["n_gpus"] == 1 and line["steps"] == 20 and line["warmup"] == 5
+    assert line["value"] > 0 and line["config"]["workload"] == "qwen3_30b_a3b_prefill"
+    rf = line["roofline"]
+    assert rf["bound"] == "hbm" and rf["unit"] == "GB/s" and rf["peak"] == 8000.0
+    assert 0 < rf["achieved"] < rf["peak"]
+    assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-9
+    assert rf["traffic"] is None or rf["traffic"] > 0
+    cb = line["cpu_baseline"]
+    assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1
+    assert cb["unit"] == line["unit"] and cb["sample"]
