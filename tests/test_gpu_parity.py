@@ -429,10 +429,29 @@ QUANT_VARIANTS = [
     dict(N=513, H=2048, E=64, R=8, K=6, quant=W.QUANT_INT8, group=2048, sm=W.SCALE_POW2),
     dict(N=200, H=640, E=32, R=4, K=4, quant=W.QUANT_INT8, group=128, sm=W.SCALE_UE8M0),
     dict(N=77, H=4096, E=64, R=8, K=6, quant=W.QUANT_INT8, group=4096, sm=W.SCALE_UE8M0),
+    # per-row scales at the largest row one wave holds (8192 elements)
+    dict(N=100, H=8192, E=32, R=4, K=4, quant=W.QUANT_FP8, group=8192),
+    dict(N=65, H=8192, E=16, R=4, K=3, quant=W.QUANT_INT8, group=8192, mask=0.2),
     dict(N=128, H=7168, E=256, R=16, K=8, quant=W.QUANT_MXFP4, group=32),   # decode shape
     dict(N=1001, H=1184, E=96, R=12, K=8, quant=W.QUANT_MXFP4, group=32, mask=0.1),  # ragged
     dict(N=64, H=32, E=32, R=2, K=16, quant=W.QUANT_MXFP4, group=32),       # one group, K=16
 ]
+
+
+# The quotient x / scale is formed exactly (one reciprocal per group and an
+# FMA correction) and both sides round it to nearest even, so FP8 and int8
+# codes match the oracle bit for bit, not just within the one-step bar.
+@pytest.mark.parametrize("args", [
+    dict(N=300, H=1024, E=64, R=8, K=8, quant=W.QUANT_FP8, group=128),
+    dict(N=100, H=8192, E=32, R=4, K=4, quant=W.QUANT_FP8, group=8192),
+    dict(N=300, H=1024, E=64, R=8, K=8, quant=W.QUANT_INT8, group=128),
+    dict(N=513, H=2048, E=64, R=8, K=6, quant=W.QUANT_INT8, group=2048, sm=W.SCALE_POW2),
+])
+def test_quant_codes_bit_exact(args):
+    w = _variant(args)
+    _say(f"[parity] quant codes bit-exact {args}")
+    st = run_and_check(w, check_combine=False)
+    assert st["code_diffs"] == 0
 
 
 def _variant(args):
