@@ -214,6 +214,22 @@ struct ep_handle {
 
 namespace {
 
+// A layout counted inside a dispatch launch and not finished (the caller lays
+// the handle out again instead of calling ep_combine_overlap) has added its
+// distinct-token counts, and with stacked sources its per-source counts, to
+// accumulators that only the finish phase reads and re-zeroes: clear them
+// before the handle is laid out again.
+hipError_t drop_pending(ep_handle* h, hipStream_t s)
+{
+    if (!h->pending) return hipSuccess;
+    hipError_t e = epk::launch_clear(h->at<uint32_t>(h->cv.acc), h->cfg.num_ranks + h->nodes, s);
+    if (e == hipSuccess && h->cv.src_acc >= 0)
+        e = epk::launch_clear(h->at<uint32_t>(h->cv.src_acc),
+                              num_sources(h->cfg) * (h->cfg.num_experts + h->cfg.num_ranks), s);
+    if (e == hipSuccess) h->pending = false;
+    return e;
+}
+
 // Validates the layout arguments and fills the kernel arguments.
 ep_status layout_args(ep_handle* h, const int32_t* d_topk_idx, int64_t num_tokens,
                       int32_t* d_num_tokens_per_rank, int32_t* d_num_tokens_per_rdma_rank,
@@ -564,6 +580,7 @@ ep_status ep_get_layout(ep_handle* h, const int32_t* d_topk_idx, int64_t num_tok
                                d_is_token_in_rank, &a);
     if (st != EP_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    EP_HIP(drop_pending(h, s));
     EP_HIP(launch_layout_any(h, a, s, h->take_events()));
     h->num_tokens = num_tokens;
     h->host_slots = -1;
@@ -615,6 +632,7 @@ ep_status ep_layout_dispatch(ep_handle* h, const int32_t* d_topk_idx, int64_t nu
                        recv_capacity_rows, &da);
     if (st != EP_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    EP_HIP(drop_pending(h, s));
     const epk::LaunchEvents ev = h->take_events();
     if (num_sources(h->cfg) == 1 && !h->cfg.non_expand && epk::route_dispatch_fits(la)) {
         EP_HIP(epk::launch_route_dispatch(la, da, s, ev));
@@ -709,6 +727,7 @@ ep_status ep_dispatch_overlap(const ep_handle* h, const void* d_x, int64_t token
                      d_num_tokens_per_rdma_rank, d_num_tokens_per_expert, d_is_token_in_rank,
                      dispatch_bytes, &la, &lb, &sa, &plan);
     if (st != EP_OK) return st;
+    EP_HIP(drop_pending(h_next, s));
     const epk::LaunchEvents ev = h->take_events();
     if (plan.ok) {
         EP_HIP(epk::launch_dispatch_layout(da, la, lb, sa, plan, s, ev));

@@ -293,7 +293,9 @@ ep_status ep_combine(const ep_handle* h, const void* d_y, const float* d_y_scale
  *   under 4 MiB; without non_expand) the layout completes in this launch;
  *   otherwise it completes in the next ep_combine_overlap(..., h_next) call,
  *   and until then h_next may be used only there (other calls return
- *   EP_ERR_STATE; ep_get_layout or ep_layout_dispatch on it start over).
+ *   EP_ERR_STATE; ep_get_layout, ep_layout_dispatch or another
+ *   ep_dispatch_overlap naming it as h_next start over, discarding the
+ *   counted part).
  *   Configurations whose layout cannot share the launch (num_topk > 8,
  *   stacked sources, a routing LDS above 24 KiB) lay h_next out with the
  *   ordinary kernels after the dispatch.

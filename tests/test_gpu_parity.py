@@ -758,6 +758,49 @@ def test_overlap_states(n, two_phase):
     assert ep.ep_check_error(h0) == (ep.EP_OK, 0) and ep.ep_check_error(h1) == (ep.EP_OK, 0)
 
 
+@pytest.mark.parametrize("P,non_expand", [(1, False), (4, False), (1, True)])
+def test_overlap_abandoned_layout_starts_over(P, non_expand):
+    """A next-batch layout counted inside a dispatch launch and never
+    finished leaves no trace when the handle is laid out again: through
+    ep_get_layout, and through another ep_dispatch_overlap that names it.
+    Its distinct-token (and per-source) additions must not reach the new
+    layout's counts."""
+    from shuffle_check import compare_layout, config_of, oracle_slots
+    n = 1000
+    w = _custom(N=n, H=64, E=64, R=8, K=8, rpn=4).scaled(num_sources=P, non_expand=non_expand)
+    cfg = config_of(w)
+    _say(f"[parity] abandoned overlap layout P={P} non_expand={non_expand}")
+    h0, h1 = ep.ep_handle_init(cfg, n), ep.ep_handle_init(cfg, n)
+    routes = [W.routing(w.scaled(seed=sd)) for sd in (51, 52, 53)]
+    topk = [torch.from_numpy(r[0]).cuda() for r in routes]
+    x = W.activations(n, 64, 5, device="cuda")
+    recv = torch.zeros((ep.ep_recv_capacity(cfg, n), 64), dtype=torch.bfloat16, device="cuda")
+    y = torch.zeros((ep.ep_recv_capacity(cfg, n), 64), dtype=torch.bfloat16, device="cuda")
+    out = torch.zeros((n, 64), dtype=torch.bfloat16, device="cuda")
+    wd = None if non_expand else torch.from_numpy(routes[0][1]).cuda()
+
+    class R:
+        pass
+
+    def check(lay, i, host_sync):
+        run = R()
+        run.w, run.lay, run.h = w, lay, h1
+        idx = routes[i][0]
+        compare_layout(run, idx, oracle.layout(idx, w.num_experts, w.num_ranks, w.ranks_per_node),
+                       oracle_slots(w, idx), host_sync=host_sync)
+
+    ep.ep_get_layout(h0, topk[0])
+    # counted, then laid out again with ep_get_layout
+    ep.ep_dispatch_overlap(h0, x, recv, h_next=h1, topk_next=topk[1])
+    check(ep.ep_get_layout(h1, topk[2], do_cpu_sync=True), 2, True)
+    # counted, then counted again by another overlapped dispatch and finished
+    ep.ep_dispatch_overlap(h0, x, recv, h_next=h1, topk_next=topk[1])
+    lay = ep.ep_dispatch_overlap(h0, x, recv, h_next=h1, topk_next=topk[2])
+    ep.ep_combine_overlap(h0, y, wd, out, h_next=h1)
+    check(lay, 2, False)
+    assert ep.ep_check_error(h0) == (ep.EP_OK, 0) and ep.ep_check_error(h1) == (ep.EP_OK, 0)
+
+
 # HIP graph capture of a decode loop's calls: the one-call layout + dispatch
 # and combine, dispatch + combine on a cached handle, and the merged
 # double-batch steps over two handles.  The calls launch kernels only (no
