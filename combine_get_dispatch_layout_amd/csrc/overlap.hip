@@ -16,8 +16,9 @@
 //                    launch moves under 4 MiB), or the count phase, one
 //                    block per 256 tokens;
 //   combine launch:  the second phase (finish_lean, one block per 256
-//                    tokens), which reads the histogram from memory so the
-//                    launch's LDS stays small for the combine blocks.
+//                    tokens), which reads the histogram from memory so its
+//                    LDS stays small; the launch's LDS is set to hold the
+//                    combine blocks at four per CU.
 // Kernel boundaries order the phases: the count phase's histogram and ranks
 // are complete before the combine launch starts, the final slots before the
 // next dispatch.
@@ -34,6 +35,12 @@ constexpr int kBlock = 256;
 constexpr int kWPB = kBlock / kWave;
 // LDS a layout phase may add to every block of the launch.
 constexpr size_t kOverlapMaxLds = 24 * 1024;
+// Every block of the combine launch takes at least this much LDS: a 160 KiB
+// CU then holds four 256-thread blocks (16 waves) rather than five.  The
+// gather runs best at 16 waves per CU (measured on MI355X, per step:
+// DeepSeek-V3 360.5 us against 363.6 at 20 waves, group-limited non-expand
+// 195.2 against 196.9, Qwen3 57.6 either way and 58.3 at 12 waves).
+constexpr size_t kCombineOccupancyLds = 160 * 1024 / 5 + 1024;
 // Dispatch bytes from which a small batch's layout is split over the two
 // launches rather than run by one block.
 constexpr int64_t kOverlapSplitMinBytes = 4 << 20;
@@ -139,6 +146,7 @@ hipError_t launch_cl(const CombineArgs& ca, const LayoutArgs& la, const LayoutAr
         size_t lds = C > 0 ? route::finish_lean_lds_bytes(la, B) : 0;
         if (p.twin && route::finish_lean_lds_bytes(lb, B) > lds)
             lds = route::finish_lean_lds_bytes(lb, B);
+        if (lds < kCombineOccupancyLds) lds = kCombineOccupancyLds;
         launch_k(k_combine_layout<KMAX, VPL, YQ, YCH, B>, dim3(all + sblocks + cblocks), dim3(B),
                  lds, s, ev.start, ev.stop, ca, NV, NC, la, lb, sa, lblocks, C, p.twin ? 1 : 0,
                  sblocks);
