@@ -624,6 +624,18 @@ def _overlap_sequence(w, sizes, seeds):
     return hs
 
 
+# Full-size workloads in the launch configuration the benchmark times by
+# default: batch 1 is laid out inside batch 0's dispatch and combine launches,
+# then dispatched and combined itself (every output checked against the
+# oracle).
+@pytest.mark.parametrize("name", ["qwen3_30b_a3b_prefill", "deepseek_v3_prefill",
+                                  "deepseek_v3_group_limited", "ll_decode_fp8", "tiny"])
+def test_workload_full_size_merged(name):
+    w = W.WORKLOADS[name]
+    _say(f"[parity] full merged {name} N={w.num_tokens} H={w.hidden}")
+    _overlap_sequence(w, [w.num_tokens, w.num_tokens], [w.seed, w.seed + 1])
+
+
 @pytest.mark.parametrize("args,sizes", [
     (dict(N=1, H=1024, E=64, R=8, K=8), [1000, 1000, 1000]),                  # count + finish
     (dict(N=1, H=64, E=64, R=8, K=8, A=2), [8500, 9000, 8193]),               # count + finish
