@@ -265,3 +265,70 @@ def run_and_check(w: W.Workload, device="cuda", rounds=None, seed_x=None, seed_y
             ref_slots["slot_idx"], w.num_topk)
     stats["run"] = run
     return stats
+
+
+def run_overlap_sequence(w: W.Workload, sizes, seeds, device="cuda"):
+    """Batches of the given sizes through the merged calls (ep_dispatch_overlap
+    / ep_combine_overlap over two handles): batch i+1 is laid out inside batch
+    i's launches.  Checks every batch's rows and combine output, and every
+    next batch's layout, against the oracle.  Returns the two handles."""
+    cfg = config_of(w)
+    nmax = max(sizes)
+    hs = [ep.ep_handle_init(cfg, nmax, device=device), ep.ep_handle_init(cfg, nmax, device=device)]
+    batches = []
+    for n, sd in zip(sizes, seeds):
+        wb = w.scaled(num_tokens=n, seed=sd)
+        idx, wts = W.routing(wb)
+        x = W.activations(n, w.hidden, sd * 7 + 1, device=device)
+        cap = ep.ep_recv_capacity(cfg, n)
+        b = dict(w=wb, idx=idx, wts=wts, topk=torch.from_numpy(idx).to(device),
+                 wts_d=torch.from_numpy(wts).to(device), x=x,
+                 recv=torch.zeros((cap, cfg.recv_row_elems), dtype=cfg.recv_dtype, device=device),
+                 scales=(torch.zeros((cap, cfg.num_groups), dtype=cfg.scales_dtype, device=device)
+                         if w.quant else None),
+                 out=torch.zeros((n, w.hidden), dtype=torch.bfloat16, device=device), cap=cap)
+        batches.append(b)
+    lay = ep.ep_get_layout(hs[0], batches[0]["topk"])
+    for i, b in enumerate(batches):
+        h, hn = hs[i % 2], hs[(i + 1) % 2]
+        nxt = batches[i + 1] if i + 1 < len(batches) else None
+        if nxt is not None:
+            nlay = ep.ep_dispatch_overlap(h, b["x"], b["recv"], b["scales"], h_next=hn,
+                                          topk_next=nxt["topk"])
+        else:
+            ep.ep_dispatch_overlap(h, b["x"], b["recv"], b["scales"])
+        S = oracle_slots(b["w"], b["idx"])["S"]
+        y = W.activations(max(S, 1), w.hidden, 900 + i, device=device)
+        ep.ep_combine_overlap(h, y, b["wts_d"], b["out"], h_next=hn if nxt is not None else None)
+        st, flags = ep.ep_check_error(h)
+        # the finished batch: rows and combine
+        ref_slots = oracle_slots(b["w"], b["idx"])
+        dropped = ref_slots.get("dropped", 0) > 0
+        assert st == (ep.EP_ERR_CAPACITY if dropped else ep.EP_OK), (i, st, flags)
+
+        class R:
+            pass
+        run = R()
+        run.w, run.recv, run.scales = b["w"], b["recv"], b["scales"]
+        ref_recv, ref_scales = oracle.dispatch(bits16(b["x"]), ref_slots["slot_idx"], b["cap"],
+                                               quant=w.quant, group=w.quant_group or None,
+                                               scale_mode=w.scale_mode)
+        compare_dispatch(run, ref_recv, ref_scales, ref_slots)
+        y_bits = bits16(y)
+        ref_out = oracle.combine(y_bits, b["wts"], ref_slots["slot_idx"])
+        compare_combine(bits16(b["out"]), ref_out, bf16_values(y_bits), b["wts"],
+                        ref_slots["slot_idx"], w.num_topk)
+        if w.non_expand and ref_slots["S"] > 0:
+            ri, rw = ep.ep_dispatch_topk(h, b["wts_d"], rows=b["cap"])
+            ref_ri, ref_rw = oracle.recv_topk(b["idx"], b["wts"], ref_slots["src_meta"],
+                                              w.num_experts, w.num_ranks)
+            S = ref_slots["S"]
+            assert np.array_equal(ri[:S].cpu().numpy(), ref_ri)
+            assert np.array_equal(rw[:S].cpu().numpy().view(np.uint32), ref_rw.view(np.uint32))
+        # the next batch's layout, complete after this combine
+        if nxt is not None:
+            run.lay, run.h = nlay, hn
+            ref_lay = oracle.layout(nxt["idx"], w.num_experts, w.num_ranks, w.ranks_per_node)
+            compare_layout(run, nxt["idx"], ref_lay, oracle_slots(nxt["w"], nxt["idx"]),
+                           host_sync=False)
+    return hs

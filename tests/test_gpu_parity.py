@@ -15,7 +15,7 @@ import torch
 import oracle
 import workloads as W
 from combine_get_dispatch_layout_amd import ep
-from shuffle_check import GpuRun, bits16, run_and_check
+from shuffle_check import GpuRun, bits16, run_and_check, run_overlap_sequence as _overlap_sequence
 
 pytestmark = pytest.mark.gpu
 
@@ -559,69 +559,6 @@ def test_non_expand_group_limited_one_call_and_sources():
 # ep_combine_overlap): a sequence of batches over two handles in turn; after
 # every step the finished batch's rows and combine output and the next
 # batch's layout are compared with the oracle.
-def _overlap_sequence(w, sizes, seeds):
-    from shuffle_check import (bits16, compare_combine, compare_dispatch, compare_layout,
-                               config_of, oracle_slots, bf16_values)
-    cfg = config_of(w)
-    nmax = max(sizes)
-    hs = [ep.ep_handle_init(cfg, nmax), ep.ep_handle_init(cfg, nmax)]
-    batches = []
-    for n, sd in zip(sizes, seeds):
-        wb = w.scaled(num_tokens=n, seed=sd)
-        idx, wts = W.routing(wb)
-        x = W.activations(n, w.hidden, sd * 7 + 1, device="cuda")
-        cap = ep.ep_recv_capacity(cfg, n)
-        b = dict(w=wb, idx=idx, wts=wts, topk=torch.from_numpy(idx).cuda(),
-                 wts_d=torch.from_numpy(wts).cuda(), x=x,
-                 recv=torch.zeros((cap, cfg.recv_row_elems), dtype=cfg.recv_dtype, device="cuda"),
-                 scales=(torch.zeros((cap, cfg.num_groups), dtype=cfg.scales_dtype, device="cuda")
-                         if w.quant else None),
-                 out=torch.zeros((n, w.hidden), dtype=torch.bfloat16, device="cuda"), cap=cap)
-        batches.append(b)
-    lay = ep.ep_get_layout(hs[0], batches[0]["topk"])
-    for i, b in enumerate(batches):
-        h, hn = hs[i % 2], hs[(i + 1) % 2]
-        nxt = batches[i + 1] if i + 1 < len(batches) else None
-        if nxt is not None:
-            nlay = ep.ep_dispatch_overlap(h, b["x"], b["recv"], b["scales"], h_next=hn,
-                                          topk_next=nxt["topk"])
-        else:
-            ep.ep_dispatch_overlap(h, b["x"], b["recv"], b["scales"])
-        S = oracle_slots(b["w"], b["idx"])["S"]
-        y = W.activations(max(S, 1), w.hidden, 900 + i, device="cuda")
-        ep.ep_combine_overlap(h, y, b["wts_d"], b["out"], h_next=hn if nxt is not None else None)
-        st, flags = ep.ep_check_error(h)
-        # the finished batch: rows and combine
-        ref_slots = oracle_slots(b["w"], b["idx"])
-        dropped = ref_slots.get("dropped", 0) > 0
-        assert st == (ep.EP_ERR_CAPACITY if dropped else ep.EP_OK), (i, st, flags)
-
-        class R:
-            pass
-        run = R()
-        run.w, run.recv, run.scales = b["w"], b["recv"], b["scales"]
-        ref_recv, ref_scales = oracle.dispatch(bits16(b["x"]), ref_slots["slot_idx"], b["cap"],
-                                               quant=w.quant, group=w.quant_group or None,
-                                               scale_mode=w.scale_mode)
-        compare_dispatch(run, ref_recv, ref_scales, ref_slots)
-        y_bits = bits16(y)
-        ref_out = oracle.combine(y_bits, b["wts"], ref_slots["slot_idx"])
-        compare_combine(bits16(b["out"]), ref_out, bf16_values(y_bits), b["wts"],
-                        ref_slots["slot_idx"], w.num_topk)
-        if w.non_expand and ref_slots["S"] > 0:
-            ri, rw = ep.ep_dispatch_topk(h, b["wts_d"], rows=b["cap"])
-            ref_ri, ref_rw = oracle.recv_topk(b["idx"], b["wts"], ref_slots["src_meta"],
-                                              w.num_experts, w.num_ranks)
-            S = ref_slots["S"]
-            assert np.array_equal(ri[:S].cpu().numpy(), ref_ri)
-            assert np.array_equal(rw[:S].cpu().numpy().view(np.uint32), ref_rw.view(np.uint32))
-        # the next batch's layout, complete after this combine
-        if nxt is not None:
-            run.lay, run.h = nlay, hn
-            ref_lay = oracle.layout(nxt["idx"], w.num_experts, w.num_ranks, w.ranks_per_node)
-            compare_layout(run, nxt["idx"], ref_lay, oracle_slots(nxt["w"], nxt["idx"]),
-                           host_sync=False)
-    return hs
 
 
 # Full-size workloads in the launch configuration the benchmark times by
