@@ -161,5 +161,5 @@ def y_seed(w: Workload) -> int:
 def round_ranges(num_tokens: int, rounds: int):
     """Token ranges [begin, end) of `rounds` equal rounds (the last takes the
     remainder)."""
-    per = -(-num_tokens // rounds)
+    per = max(-(-num_tokens // rounds), 1)
     return [(b, min(b + per, num_tokens)) for b in range(0, num_tokens, per)] or [(0, 0)]
