@@ -129,9 +129,15 @@ __global__ __launch_bounds__(kLayoutBlock) void k_finish(LayoutArgs a, int C)
 
     int off[KMAX];
     bool dropped = false;
+    int start[KMAX], pos[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        start[k] = psum[safe_id(ids[k])];
+        pos[k] = base[safe_id(ids[k])] + lr[k];
+    }
 #pragma unroll
     for (int k = 0; k < KMAX; ++k)
-        off[k] = ids[k] >= 0 ? final_slot(a, psum[ids[k]], base[ids[k]] + lr[k], dropped) : 0;
+        off[k] = ids[k] >= 0 ? final_slot(a, start[k], pos[k], dropped) : 0;
     flag_dropped<KMAX>(a, dropped);
     store_slots<KMAX>(a, t, ids, off);
     write_padding<NT>(a, tot, psum, b, C);
@@ -211,10 +217,15 @@ __global__ __launch_bounds__(kLayoutBlock) void k_slots(LayoutArgs a)
     load_row<KMAX>(a.topk_clone + t * K, K, a.row_vec, true, -1, ids);
     load_row<KMAX>(a.slot_idx + t * K, K, a.row_vec, true, 0, lr);
     bool dropped = false;
+    int start[KMAX], pos[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        start[k] = a.psum_expert[safe_id(ids[k])];
+        pos[k] = base[safe_id(ids[k])] + lr[k];
+    }
 #pragma unroll
     for (int k = 0; k < KMAX; ++k)
-        off[k] = ids[k] >= 0 ? final_slot(a, a.psum_expert[ids[k]], base[ids[k]] + lr[k], dropped)
-                             : 0;
+        off[k] = ids[k] >= 0 ? final_slot(a, start[k], pos[k], dropped) : 0;
     flag_dropped<KMAX>(a, dropped);
     store_slots<KMAX>(a, t, ids, off);
 }

@@ -72,13 +72,13 @@ void k_dispatch_layout(DispatchArgs da, int NV, int NC, LayoutArgs la, LayoutArg
     }
     if ((int)blockIdx.x < lblocks) {
         if (mode == kModeFused) {
-            route::fused_body<LK, kWPB>(la, smem);
+            route::fused_body<LK, kWPB, true>(la, smem);
         } else if (mode == kModeTwin) {
             const int C = lblocks / 2;
-            if ((int)blockIdx.x < C) route::count_body<LK>(la, blockIdx.x, smem);
-            else route::count_body<LK>(lb, blockIdx.x - C, smem);
+            if ((int)blockIdx.x < C) route::count_body<LK, true>(la, blockIdx.x, smem);
+            else route::count_body<LK, true>(lb, blockIdx.x - C, smem);
         } else {
-            route::count_body<LK>(la, blockIdx.x, smem);
+            route::count_body<LK, true>(la, blockIdx.x, smem);
         }
         return;
     }

@@ -18,6 +18,11 @@ __device__ __forceinline__ int count_below(uint64_t m)
                                      __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
+// An entry's id when it is valid, else 0: an always-valid index, so that a
+// row's K table reads are issued together and waited for once (a read under
+// a per-entry branch is waited for before the next one is issued).
+__device__ __forceinline__ int safe_id(int id) { return id >= 0 ? id : 0; }
+
 __device__ __forceinline__ int div_by(int n, uint32_t magic)
 {
     return magic == 0u ? n : (int)__umulhi((uint32_t)n, magic);
@@ -234,10 +239,12 @@ __device__ __forceinline__ void write_in_rank_row(const LayoutArgs& a, const int
 }
 
 // Routing phase for the block's tokens t0 .. t0 + WAVES*64 - 1 (one per
-// thread).  Leaves the sanitised ids and the in-block rank of every pair in
+// thread).  LEAN: the kernel shares its launch with streaming blocks and
+// must stay within 64 vector registers, so the per-entry table reads of the
+// level loop are not batched.  Leaves the sanitised ids and the in-block rank of every pair in
 // registers, the block histogram in L.bhist and the distinct-token counts in
 // L.rcnt / L.ncnt; writes the topk clone and the is_token_in_rank rows.
-template <int KMAX, int WAVES>
+template <int KMAX, int WAVES, bool LEAN = false>
 __device__ __forceinline__ void route_block(const LayoutArgs& a, int64_t t0, const RouteLds& L,
                                             int (&ids)[KMAX], int (&lr)[KMAX],
                                             bool write_rows = true)
@@ -293,9 +300,18 @@ __device__ __forceinline__ void route_block(const LayoutArgs& a, int64_t t0, con
             if (ids[k] >= 0 && (int)((occp >> (4 * k)) & 15ull) == j)
                 atomicOr(mytab + ids[k], 1ull << lane);
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        if constexpr (LEAN) {
 #pragma unroll
-        for (int k = 0; k < KMAX; ++k)
-            if (ids[k] >= 0) lr[k] += count_below(mytab[ids[k]]);
+            for (int k = 0; k < KMAX; ++k)
+                if (ids[k] >= 0) lr[k] += count_below(mytab[ids[k]]);
+        } else {
+            unsigned long long mk[KMAX];
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k) mk[k] = mytab[safe_id(ids[k])];
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k)
+                if (ids[k] >= 0) lr[k] += count_below(mk[k]);
+        }
         // the level's per-expert counts, four table words in flight per lane
         for (int e0 = lane; e0 < E; e0 += 4 * kWave) {
             unsigned long long m[4];
@@ -303,8 +319,16 @@ __device__ __forceinline__ void route_block(const LayoutArgs& a, int64_t t0, con
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int e = e0 + i * kWave;
-                m[i] = e < E ? mytab[e] : 0ull;
-                c[i] = (j > 0 && e < E) ? mycnt[e] : 0;
+                if constexpr (LEAN) {
+                    m[i] = e < E ? mytab[e] : 0ull;
+                    c[i] = (j > 0 && e < E) ? mycnt[e] : 0;
+                } else {   // in-range reads, issued unconditionally
+                    const int ec = e < E ? e : E - 1;
+                    m[i] = mytab[ec];
+                    c[i] = mycnt[ec];
+                    if (e >= E) m[i] = 0ull;
+                    if (j == 0 || e >= E) c[i] = 0;
+                }
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -318,12 +342,14 @@ __device__ __forceinline__ void route_block(const LayoutArgs& a, int64_t t0, con
 
     // Block totals; wcnt[w][e] becomes the count of earlier waves.
     for (int e = tid; e < E; e += NT) {
+        int v[WAVES];   // all reads first, then the writes: one wait
+#pragma unroll
+        for (int q = 0; q < WAVES; ++q) v[q] = L.wcnt[q * E + e];
         int run = 0;
 #pragma unroll
         for (int q = 0; q < WAVES; ++q) {
-            const int v = L.wcnt[q * E + e];
             L.wcnt[q * E + e] = run;
-            run += v;
+            run += v[q];
         }
         L.bhist[e] = run;
     }
@@ -335,8 +361,11 @@ __device__ __forceinline__ void route_block(const LayoutArgs& a, int64_t t0, con
     if (a.out_in_rank != nullptr && tv && write_rows)
         write_in_rank_row<KMAX>(a, ids, m, a.out_in_rank + t * R);
     __syncthreads();
+    int before[KMAX];
 #pragma unroll
-    for (int k = 0; k < KMAX; ++k) lr[k] = ids[k] >= 0 ? lr[k] + L.wcnt[w * E + ids[k]] : -1;
+    for (int k = 0; k < KMAX; ++k) before[k] = L.wcnt[w * E + safe_id(ids[k])];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) lr[k] = ids[k] >= 0 ? lr[k] + before[k] : -1;
 }
 
 // Exclusive prefix of the aligned counts cnt[0..E) into psum[0..E]; NT
@@ -490,22 +519,25 @@ inline size_t fused_lds_bytes(const LayoutArgs& a, int waves)
 
 // Path A: one block of WAVES waves does the whole layout of N <= WAVES*64
 // tokens in LDS (fused_lds_bytes).
-template <int KMAX, int WAVES>
+template <int KMAX, int WAVES, bool LEAN = false>
 __device__ __forceinline__ void fused_body(const LayoutArgs& a, unsigned char* smem)
 {
     constexpr int NT = WAVES * kWave;
     const RouteLds L = carve_route(smem, WAVES, a.E, a.R);
     int ids[KMAX], lr[KMAX];
-    route_block<KMAX, WAVES>(a, 0, L, ids, lr);
+    route_block<KMAX, WAVES, LEAN>(a, 0, L, ids, lr);
     // prefix [E+1] and scan scratch [2*NT] follow the routing LDS
     int32_t* psum = L.ncnt + a.nodes;
     int32_t* scratch = psum + a.E + 1;
     aligned_prefix<NT>(a, L.bhist, psum, scratch);
     int off[KMAX];
     bool dropped = false;
+    int start[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) start[k] = psum[safe_id(ids[k])];
 #pragma unroll
     for (int k = 0; k < KMAX; ++k)
-        off[k] = ids[k] >= 0 ? final_slot(a, psum[ids[k]], lr[k], dropped) : 0;
+        off[k] = ids[k] >= 0 ? final_slot(a, start[k], lr[k], dropped) : 0;
     flag_dropped<KMAX>(a, dropped);
     store_slots<KMAX>(a, threadIdx.x, ids, off);
     write_expert_arrays<NT>(a, L.bhist, psum);
@@ -519,14 +551,14 @@ __device__ __forceinline__ void fused_body(const LayoutArgs& a, unsigned char* s
 // Paths B and C, first phase, layout block b (tokens [256b, 256b+256)):
 // writes the block histogram, the in-block ranks (into slot_idx, finished by
 // the second phase) and adds the distinct-token counts to the accumulators.
-template <int KMAX>
+template <int KMAX, bool LEAN = false>
 __device__ __forceinline__ void count_body(const LayoutArgs& a, int b, unsigned char* smem)
 {
     constexpr int WAVES = kLayoutBlock / kWave;
     const RouteLds L = carve_route(smem, WAVES, a.E, a.R);
     int ids[KMAX], lr[KMAX];
     const int64_t t0 = (int64_t)b * kLayoutBlock;
-    route_block<KMAX, WAVES>(a, t0, L, ids, lr);
+    route_block<KMAX, WAVES, LEAN>(a, t0, L, ids, lr);
     const int tid = threadIdx.x, K = a.K;
     const int64_t t = t0 + tid;
     if (t < a.num_tokens && !a.counts_only) store_row<KMAX>(a.slot_idx + t * K, K, a.row_vec, lr);
@@ -638,10 +670,15 @@ __device__ __forceinline__ void finish_lean(const LayoutArgs& a, int C, int b, u
         const int32_t* mybase = base + (tid / kLayoutBlock) * E;
         int off[KMAX];
         bool dropped = false;
+        int start[KMAX], pos[KMAX];
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            start[k] = psum[safe_id(ids[k])];
+            pos[k] = mybase[safe_id(ids[k])] + lr[k];
+        }
 #pragma unroll
         for (int k = 0; k < KMAX; ++k)
-            off[k] =
-                ids[k] >= 0 ? final_slot(a, psum[ids[k]], mybase[ids[k]] + lr[k], dropped) : 0;
+            off[k] = ids[k] >= 0 ? final_slot(a, start[k], pos[k], dropped) : 0;
         flag_dropped<KMAX>(a, dropped);
         store_slots<KMAX>(a, t, ids, off);
         write_padding<NT>(a, tot, psum, b, blocks);
