@@ -90,9 +90,14 @@ __global__ __launch_bounds__(kLayoutBlock) void k_finish(LayoutArgs a, int C)
     int ids[KMAX], lr[KMAX];
     load_row<KMAX>(a.topk_clone + t * K, K, a.row_vec, tv, -1, ids);
     load_row<KMAX>(a.slot_idx + t * K, K, a.row_vec, tv, 0, lr);
-    const int n = C * E;
+    // the histogram as 16-byte vectors (workspace and LDS are 16-byte
+    // aligned), then the tail
+    const int n = C * E, nv = n / 4;
+    const int4* src = reinterpret_cast<const int4*>(a.hist);
+    int4* dst = reinterpret_cast<int4*>(tile);
 #pragma unroll 8
-    for (int i = tid; i < n; i += NT) tile[i] = a.hist[i];
+    for (int i = tid; i < nv; i += NT) dst[i] = src[i];
+    for (int i = 4 * nv + tid; i < n; i += NT) tile[i] = a.hist[i];
     __syncthreads();
 
     const int EPT = E < NT ? E : NT;
