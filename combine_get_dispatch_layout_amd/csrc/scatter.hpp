@@ -70,8 +70,16 @@ inline hipError_t shape_rw(int NV, int row_bytes, L& launch)
     using QC = std::integral_constant<int, Q>;
     using CC = std::bool_constant<CH>;
     using VC = std::integral_constant<int, VPL>;
-    return dispatch_row_wait(row_bytes) ? launch(QC{}, CC{}, VC{}, RW1{}, NV)
-                                        : launch(QC{}, CC{}, VC{}, RW0{}, NV);
+    // Receive rows of 8 KiB or more come with one vector per lane, or with a
+    // whole row per wave (channel scales, 16 vectors per lane); the other
+    // shapes are not instantiated with row waits (the wait is a performance
+    // choice only: the rows written are the same).
+    constexpr bool may_wait = VPL == 1 || (CH && VPL == 16) || EP_DISPATCH_VPL >= 0;
+    if constexpr (may_wait)
+        return dispatch_row_wait(row_bytes) ? launch(QC{}, CC{}, VC{}, RW1{}, NV)
+                                            : launch(QC{}, CC{}, VC{}, RW0{}, NV);
+    else
+        return launch(QC{}, CC{}, VC{}, RW0{}, NV);
 }
 
 template <int Q, class L>
