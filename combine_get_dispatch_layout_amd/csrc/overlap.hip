@@ -35,12 +35,28 @@ constexpr int kBlock = 256;
 constexpr int kWPB = kBlock / kWave;
 // LDS a layout phase may add to every block of the launch.
 constexpr size_t kOverlapMaxLds = 24 * 1024;
-// Every block of the combine launch takes at least this much LDS: a 160 KiB
-// CU then holds four 256-thread blocks (16 waves) rather than five.  The
+// Every block of the combine launch takes at least this much LDS, so that a
+// CU holds four 256-thread blocks (16 waves) rather than five: a fifth of the
+// CU's LDS (160 KiB on MI355X, read from the device once) plus 1 KiB.  The
 // gather runs best at 16 waves per CU (measured on MI355X, per step:
 // DeepSeek-V3 360.5 us against 363.6 at 20 waves, group-limited non-expand
 // 195.2 against 196.9, Qwen3 57.6 either way and 58.3 at 12 waves).
-constexpr size_t kCombineOccupancyLds = 160 * 1024 / 5 + 1024;
+size_t combine_occupancy_lds()
+{
+    static const size_t lds = [] {
+        int dev = 0, per_cu = 0, per_block = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor,
+                                  dev) != hipSuccess ||
+            hipDeviceGetAttribute(&per_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
+                hipSuccess ||
+            per_cu <= 0)
+            return (size_t)0;   // unknown: leave the occupancy alone
+        const size_t v = (size_t)per_cu / 5 + 1024;
+        return v <= (size_t)per_block ? v : (size_t)0;
+    }();
+    return lds;
+}
 // Dispatch bytes from which a small batch's layout is split over the two
 // launches rather than run by one block.
 constexpr int64_t kOverlapSplitMinBytes = 4 << 20;
@@ -160,7 +176,7 @@ hipError_t launch_cl(const CombineArgs& ca, const LayoutArgs& la, const LayoutAr
         size_t lds = C > 0 ? route::finish_lean_lds_bytes(la, B) : 0;
         if (p.twin && route::finish_lean_lds_bytes(lb, B) > lds)
             lds = route::finish_lean_lds_bytes(lb, B);
-        if (lds < kCombineOccupancyLds) lds = kCombineOccupancyLds;
+        if (lds < combine_occupancy_lds()) lds = combine_occupancy_lds();
         launch_k(k_combine_layout<KMAX, VPL, YQ, YCH, B>, dim3(all + sblocks + cblocks), dim3(B),
                  lds, s, ev.start, ev.stop, ca, NV, NC, la, lb, sa, lblocks, C, p.twin ? 1 : 0,
                  sblocks);
