@@ -24,6 +24,10 @@ constexpr int kMaxVecPerLane = 16;
 // counts the whole batch's routing in LDS).
 constexpr int kRouteDispatchMaxTokens = 256;
 
+// Most copies of the distinct-token accumulators: a layout of many count
+// blocks spreads their atomics over several copies (LayoutArgs::acc_copies).
+constexpr int kAccCopies = 8;
+
 constexpr uint32_t kFlagBadId = 1u;
 constexpr uint32_t kFlagCapacity = 2u;
 constexpr uint32_t kFlagYRows = 4u;
@@ -48,8 +52,11 @@ struct LayoutArgs {
     int32_t* slot_idx;          // [N,K]
     int32_t* src_meta;          // [max_slots,2]
     int32_t* hist;              // [C,E]  block histograms -> exclusive bases
-    int32_t* rank_acc;          // [R] distinct-token accumulators, zero between calls
-    int32_t* node_acc;          // [nodes] likewise
+    int32_t* rank_acc;          // [kAccCopies][acc_stride]: distinct-token accumulators
+                                // per rank (first R words of a copy), zero between calls
+    int32_t* node_acc;          // rank_acc + R: the per-node ones, likewise
+    int acc_stride;             // R + nodes
+    int acc_copies;             // copies in use: count block b adds into b % acc_copies
     int32_t* psum_expert;       // [E+1]
     int32_t* psum_rank;         // [R+1]
     int32_t* num_unaligned;     // [E]

@@ -564,24 +564,45 @@ __device__ __forceinline__ void count_body(const LayoutArgs& a, int b, unsigned 
     if (t < a.num_tokens && !a.counts_only) store_row<KMAX>(a.slot_idx + t * K, K, a.row_vec, lr);
     for (int e = tid; e < a.E; e += kLayoutBlock) a.hist[(int64_t)b * a.E + e] = L.bhist[e];
     if (a.no_rank_counts) return;
+    // this block's copy of the accumulators (spreads the atomics of many
+    // blocks over several addresses per rank)
+    const int copy = a.acc_copies > 1 ? (b % a.acc_copies) * a.acc_stride : 0;
     for (int r = tid; r < a.R; r += kLayoutBlock)
-        if (L.rcnt[r] != 0) atomicAdd(a.rank_acc + r, L.rcnt[r]);
+        if (L.rcnt[r] != 0) atomicAdd(a.rank_acc + copy + r, L.rcnt[r]);
     for (int n = tid; n < a.nodes; n += kLayoutBlock)
-        if (L.ncnt[n] != 0) atomicAdd(a.node_acc + n, L.ncnt[n]);
+        if (L.ncnt[n] != 0) atomicAdd(a.node_acc + copy + n, L.ncnt[n]);
 }
 
-// Distinct-token totals from the accumulators, which are re-zeroed for the
-// next call.
+// Distinct-token totals from the accumulators (the sum of their copies),
+// which are re-zeroed for the next call.  The additions were made by an
+// earlier launch, so plain loads see them; all kAccCopies copies are read
+// at once (the unused ones hold zero).
 template <int NT>
 __device__ __forceinline__ void flush_rank_totals(const LayoutArgs& a)
 {
     for (int r = threadIdx.x; r < a.R; r += NT) {
-        const int v = atomicExch(a.rank_acc + r, 0);
-        if (a.out_per_rank) a.out_per_rank[r] = v;
+        int v[kAccCopies];
+#pragma unroll
+        for (int c = 0; c < kAccCopies; ++c) v[c] = a.rank_acc[c * a.acc_stride + r];
+        int sum = 0;
+#pragma unroll
+        for (int c = 0; c < kAccCopies; ++c) {
+            sum += v[c];
+            a.rank_acc[c * a.acc_stride + r] = 0;
+        }
+        if (a.out_per_rank) a.out_per_rank[r] = sum;
     }
     for (int n = threadIdx.x; n < a.nodes; n += NT) {
-        const int v = atomicExch(a.node_acc + n, 0);
-        if (a.out_per_node) a.out_per_node[n] = v;
+        int v[kAccCopies];
+#pragma unroll
+        for (int c = 0; c < kAccCopies; ++c) v[c] = a.node_acc[c * a.acc_stride + n];
+        int sum = 0;
+#pragma unroll
+        for (int c = 0; c < kAccCopies; ++c) {
+            sum += v[c];
+            a.node_acc[c * a.acc_stride + n] = 0;
+        }
+        if (a.out_per_node) a.out_per_node[n] = sum;
     }
 }
 

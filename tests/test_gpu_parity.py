@@ -576,6 +576,7 @@ def test_workload_full_size_merged(name):
 @pytest.mark.parametrize("args,sizes", [
     (dict(N=1, H=1024, E=64, R=8, K=8), [1000, 1000, 1000]),                  # count + finish
     (dict(N=1, H=64, E=64, R=8, K=8, A=2), [8500, 9000, 8193]),               # count + finish
+    (dict(N=1, H=64, E=64, R=8, K=6, rpn=4), [20000, 17000, 16384]),          # accumulator copies
     (dict(N=1, H=2048, E=128, R=16, K=6, A=4, mask=0.1), [4097, 3000, 4096]),  # odd block count
     (dict(N=1, H=7168, E=256, R=16, K=8, quant=W.QUANT_FP8, group=128), [128, 200, 256]),  # split: 7+ MiB
     (dict(N=1, H=512, E=256, R=16, K=8, quant=W.QUANT_FP8, group=128), [128, 200, 256]),   # one block
