@@ -4,7 +4,8 @@ Each case draws a configuration the ABI accepts (ranks, experts per rank,
 top-k, hidden size, alignment, masking, repeated experts, per-node grouping,
 fixed capacity, stacked sources, non-expand, dispatch and combine
 quantisation) and runs it through one pipeline: the separate calls, the
-one-call layout + dispatch, or the merged calls over a sequence of batches.
+one-call layout + dispatch, or the merged calls over a sequence of batches;
+the separate calls may split the batch into token rounds on one handle.
 Every output is held to the same bars as the hand-picked cases (layout,
 slots and bf16 rows bit-exact, codes within one step with scales exact,
 combine within one bf16 ulp plus the fp32 chain bound).  Sizes stay small
@@ -18,7 +19,7 @@ import workloads as W
 from shuffle_check import run_and_check, run_overlap_sequence
 
 PIPELINES = ("serial", "fused", "merged")
-NUM_CASES = 36
+NUM_CASES = 60
 
 
 def _draw(i):
@@ -76,15 +77,17 @@ def _draw(i):
         if cg == H and H > 8192:
             cq, cg = W.QUANT_NONE, 0
     dup = pipeline != "merged" and K > 1 and rng.random() < 0.3
-    w = W.Workload("sweep", N, H, E, R, K, expert_alignment=A, quant=quant, quant_group=group,
-                   mask_prob=mask, seed=5000 + i, ranks_per_node=rpn, routing=routing,
-                   expert_capacity=cap, num_sources=sources, scale_mode=sm,
-                   combine_quant=cq, combine_group=cg, non_expand=non_expand)
     sizes = None
     if pipeline == "merged":
         m = int(rng.integers(2, 4))
         sizes = [N] + [int(rng.integers(0, N + 1)) for _ in range(m - 1)]
         sizes = [s - s % sources for s in sizes]
+    # token rounds over one handle (the separate calls only)
+    rounds = int(rng.choice([1, 1, 2, 3, 4])) if pipeline == "serial" else 1
+    w = W.Workload("sweep", N, H, E, R, K, expert_alignment=A, quant=quant, quant_group=group,
+                   mask_prob=mask, seed=5000 + i, ranks_per_node=rpn, routing=routing,
+                   expert_capacity=cap, num_sources=sources, scale_mode=sm,
+                   combine_quant=cq, combine_group=cg, non_expand=non_expand, rounds=rounds)
     return w, pipeline, sizes, dup
 
 
@@ -107,7 +110,7 @@ def test_random_config(i):
     print(f"[sweep] case {i} {pipeline} N={w.num_tokens} H={w.hidden} E={w.num_experts} "
           f"R={w.num_ranks} K={w.num_topk} A={w.expert_alignment} quant={w.quant}/"
           f"{w.quant_group}/{w.scale_mode} mask={w.mask_prob} rpn={w.ranks_per_node} "
-          f"{w.routing} cap={w.expert_capacity} P={w.num_sources} ne={int(w.non_expand)} "
+          f"{w.routing} cap={w.expert_capacity} rounds={w.rounds} P={w.num_sources} ne={int(w.non_expand)} "
           f"cq={w.combine_quant}/{w.combine_group} dup={dup} sizes={sizes}", flush=True)
     if pipeline == "merged":
         run_overlap_sequence(w, sizes, [5000 + 10 * i + j for j in range(len(sizes))])
@@ -131,3 +134,4 @@ def test_draws_cover_the_paths():
     assert any(w.combine_quant for w, _, _, _ in ws)
     assert any(w.expert_capacity for w, _, _, _ in ws)
     assert any(d for _, _, _, d in ws)
+    assert any(w.rounds > 1 for w, _, _, _ in ws)
