@@ -85,6 +85,40 @@ def traffic_path(workload):
     return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
 
 
+QNAMES = {"none": 0, "fp8": 1, "int8": 2, "mxfp4": 3}
+SCALE_MODES = {"fp32": 0, "pow2": 1, "ue8m0": 2}
+# fields the variant flags may change, and their short names in a tag
+VARIANT_FIELDS = (("num_sources", "src"), ("quant", "q"), ("quant_group", "qg"),
+                  ("scale_mode", "sm"), ("combine_quant", "cq"), ("combine_group", "cg"))
+
+
+def variant_of(args):
+    """The workload that --workload and the variant flags name, its tag, and
+    the flags as bench.py arguments.  The tag is the workload's name, plus
+    one suffix per field the flags changed; it keys the traffic records, so
+    a variant never reports another configuration's counted bytes."""
+    import workloads as W
+    base = W.WORKLOADS[args.workload]
+    w, flags = base, []
+    if args.num_sources > 1:
+        w = w.scaled(num_sources=args.num_sources)
+        flags += ["--num-sources", str(args.num_sources)]
+    if args.quant:
+        q = QNAMES[args.quant]
+        w = w.scaled(quant=q, quant_group=(args.quant_group or (32 if q == 3 else 128)) if q else 0)
+        flags += ["--quant", args.quant] + (["--quant-group", str(args.quant_group)]
+                                            if args.quant_group else [])
+    if args.scale_mode:
+        w = w.scaled(scale_mode=SCALE_MODES[args.scale_mode])
+        flags += ["--scale-mode", args.scale_mode]
+    if args.combine_quant and args.combine_quant != "none":
+        w = w.scaled(combine_quant=QNAMES[args.combine_quant], combine_group=args.combine_group)
+        flags += ["--combine-quant", args.combine_quant, "--combine-group", str(args.combine_group)]
+    tag = args.workload + "".join(f"_{short}{getattr(w, f)}" for f, short in VARIANT_FIELDS
+                                  if getattr(w, f) != getattr(base, f))
+    return w, tag, flags
+
+
 def traffic_from_profiles(kernel, workload):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary, or None when there is none or the kernel source changed since
@@ -114,12 +148,15 @@ KERNEL_SYMBOLS = {"dispatch": "k_dispatch<", "combine": "k_combine<",
                   "dispatch_layout": "k_dispatch_layout<", "combine_layout": "k_combine_layout<"}
 
 
-def traffic_summary(fetch_csv, write_csv, workload, pipeline):
-    """Adds to profiles/traffic_<workload>.json the HBM bytes per launch of the
+def traffic_summary(fetch_csv, write_csv, args):
+    """Adds to profiles/traffic_<tag>.json the HBM bytes per launch of the
     data-moving kernels found in two rocprofv3 --pmc counter_collection CSVs
-    of `bench.py --workload <workload> --pipeline <pipeline>` (FETCH_SIZE, then
-    WRITE_SIZE; KiB per dispatch).  Each counter is scaled by what it reads
-    for the benchmark's 1 GiB device copy (read 1 GiB, write 1 GiB)."""
+    of `bench.py --workload <workload> <variant flags> --pipeline <pipeline>`
+    (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), where <tag> names the
+    workload and its variant.  Each counter is scaled by what it reads for
+    the benchmark's 1 GiB device copy (read 1 GiB, write 1 GiB)."""
+    workload, pipeline = args.workload, args.pipeline
+    w, tag, flags = variant_of(args)
     fetch = _counter_rows(fetch_csv, "FETCH_SIZE")
     write = _counter_rows(write_csv, "WRITE_SIZE")
     gib_kib = float(1 << 20)
@@ -128,7 +165,6 @@ def traffic_summary(fetch_csv, write_csv, workload, pipeline):
     f_fetch, f_write = gib_kib / copy_f, gib_kib / copy_w
     import workloads as W
     import numpy as np
-    w = W.WORKLOADS[workload]
     idx, _ = W.routing(w)
     V = int((idx >= 0).sum())
     ranks = np.where(idx >= 0, idx // (w.num_experts // w.num_ranks), -1)
@@ -139,17 +175,26 @@ def traffic_summary(fetch_csv, write_csv, workload, pipeline):
     # dispatch / combine bytes alone
     nbytes["dispatch_layout"] = nbytes["dispatch"]
     nbytes["combine_layout"] = nbytes["combine"]
-    bench_args = f"--workload {workload} --pipeline {pipeline} --steps 4 --warmup 2 --no-cpu-baseline"
+    vflags = "".join(" " + f for f in flags)
+    bench_args = (f"--workload {workload}{vflags} --pipeline {pipeline} --steps 4 --warmup 2 "
+                  "--no-cpu-baseline")
     command = [f"rocprofv3 --pmc FETCH_SIZE -f csv -d <dir> -o fetch -- python3 bench.py {bench_args}",
                f"rocprofv3 --pmc WRITE_SIZE -f csv -d <dir> -o write -- python3 bench.py {bench_args}",
                f"python3 bench.py --traffic-from <dir>/fetch_counter_collection.csv "
-               f"<dir>/write_counter_collection.csv --workload {workload} --pipeline {pipeline}"]
-    path = traffic_path(workload)
-    out = dict(workload=workload, kernels={})
+               f"<dir>/write_counter_collection.csv --workload {workload}{vflags} --pipeline {pipeline}"]
+    path = traffic_path(tag)
+    out = dict(workload=tag, kernels={})
     if os.path.exists(path):
         with open(path) as f:
             out = json.load(f)
     for kern, sym in KERNEL_SYMBOLS.items():
+        if kern == "dispatch":
+            # ep_quantize_rows (expert outputs as codes, before the timed
+            # loop) runs the dispatch kernel too, with the combine's format as
+            # its first template argument: keep the step's own dispatch only
+            if w.combine_quant and w.combine_quant == w.quant:
+                continue
+            sym = f"k_dispatch<{w.quant},"
         fv = [v for n, v in fetch if sym in n]
         wv = [v for n, v in write if sym in n]
         if not fv or not wv:
@@ -301,7 +346,7 @@ def main():
     if args.pipeline is None:
         args.pipeline = "merged"
     if args.traffic_from:
-        traffic_summary(args.traffic_from[0], args.traffic_from[1], args.workload, args.pipeline)
+        traffic_summary(args.traffic_from[0], args.traffic_from[1], args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): this path runs on "
@@ -314,17 +359,7 @@ def main():
     import workloads as W
     from combine_get_dispatch_layout_amd import ep
 
-    w = W.WORKLOADS[args.workload]
-    if args.num_sources > 1:
-        w = w.scaled(num_sources=args.num_sources)
-    qnames = {"none": 0, "fp8": 1, "int8": 2, "mxfp4": 3}
-    if args.quant:
-        q = qnames[args.quant]
-        w = w.scaled(quant=q, quant_group=(args.quant_group or (32 if q == 3 else 128)) if q else 0)
-    if args.scale_mode:
-        w = w.scaled(scale_mode={"fp32": 0, "pow2": 1, "ue8m0": 2}[args.scale_mode])
-    if args.combine_quant and args.combine_quant != "none":
-        w = w.scaled(combine_quant=qnames[args.combine_quant], combine_group=args.combine_group)
+    w, tag, _ = variant_of(args)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     idx, wts = W.routing(w)
@@ -561,7 +596,7 @@ def main():
     # also lays out the next batch; with rounds, most launches are plain)
     merged1 = pl == "merged" and len(rounds) == 1
     traffic = traffic_from_profiles({"dispatch": "dispatch_layout", "combine": "combine_layout"}
-                                    .get(dom, dom) if merged1 else dom, w.name)
+                                    .get(dom, dom) if merged1 else dom, tag)
 
     # achievable reference: a plain 1 GiB device copy
     a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)

@@ -42,3 +42,31 @@ def test_default_line_has_the_contract_fields():
     cb = line["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1
     assert cb["unit"] == line["unit"] and cb["sample"]
+
+
+def _variant(**kw):
+    import argparse
+    sys.path.insert(0, ROOT) if ROOT not in sys.path else None
+    import bench
+    a = dict(workload="qwen3_30b_a3b_prefill", num_sources=0, quant=None, quant_group=0,
+             scale_mode=None, combine_quant=None, combine_group=128)
+    a.update(kw)
+    return bench, bench.variant_of(argparse.Namespace(**a))
+
+
+def test_variant_flags_key_their_own_traffic():
+    """A run with variant flags is priced and looked up under its own tag:
+    it never reports the plain workload's counted bytes."""
+    bench, (w, tag, flags) = _variant()
+    assert tag == "qwen3_30b_a3b_prefill" and flags == [] and w.quant == 0
+    _, (w, tag, flags) = _variant(quant="mxfp4")
+    assert (w.quant, w.quant_group) == (3, 32)
+    assert tag == "qwen3_30b_a3b_prefill_q3_qg32" and flags == ["--quant", "mxfp4"]
+    _, (w, tag, _) = _variant(num_sources=16, combine_quant="fp8")
+    assert tag == "qwen3_30b_a3b_prefill_src16_cq1_cg128" and w.combine_group == 128
+    # the plain workload's record exists; no variant borrows it
+    assert bench.traffic_from_profiles("dispatch", "qwen3_30b_a3b_prefill") is not None
+    assert bench.traffic_from_profiles("dispatch", "qwen3_30b_a3b_prefill_q3_qg32") is None
+    # flags that restate the workload's own settings keep its tag
+    _, (_, tag, _) = _variant(workload="ll_decode_fp8", quant="fp8")
+    assert tag == "ll_decode_fp8"
