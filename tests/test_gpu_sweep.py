@@ -12,6 +12,8 @@ combine within one bf16 ulp plus the fp32 chain bound).  Sizes stay small
 enough for the oracle yet reach every layout path: the one-block layout,
 count + finish, and count + scan + slots.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -19,7 +21,9 @@ import workloads as W
 from shuffle_check import run_and_check, run_overlap_sequence
 
 PIPELINES = ("serial", "fused", "merged")
-NUM_CASES = 60
+# EP_SWEEP_CASES widens the sweep (the draws are a pure function of the case
+# number, so a wider run repeats the default cases first)
+NUM_CASES = int(os.environ.get("EP_SWEEP_CASES", "60"))
 
 
 def _draw(i):
