@@ -7,7 +7,12 @@ It shares no code with the HIP library.
 Parity status: every function is pinned by the CPU tests (see the
 ``test_oracle_*`` files): number formats against torch's own converters and
 exhaustive format properties, layout and slots against numpy routines,
-brute force and invariants, combine against exact rational sums.
+brute force and invariants, combine against exact rational sums (the fp32
+chain of ``combine_fma`` step by step against exactly rounded fused
+multiply-adds).
+
+``dispatch``, ``combine*`` take ``parallel=True`` to run on the OpenMP build
+(same results; for timing the oracle on a host's cores only).
 """
 import ctypes
 import os
@@ -16,13 +21,14 @@ import numpy as np
 
 from . import build as _build
 
-_lib = None
+_libs = {}
 
 
-def lib():
-    global _lib
-    if _lib is None:
-        path = _build.build(force=False)
+def lib(parallel=False):
+    """The serial oracle library, or with parallel the OpenMP build."""
+    L = _libs.get(parallel)
+    if L is None:
+        path = _build.build(force=False, openmp=parallel)
         L = ctypes.CDLL(path)
         P = ctypes.c_void_p
         i64, i32 = ctypes.c_int64, ctypes.c_int
@@ -52,12 +58,25 @@ def lib():
         L.orc_f32_from_e8m0.restype = ctypes.c_float
         L.orc_combine.argtypes = [P, P, P, i64, i32, i32, i64, i64, P]
         L.orc_combine.restype = None
+        L.orc_combine_fma.argtypes = [P, P, P, i64, i32, i32, i64, i64, P]
+        L.orc_combine_fma.restype = None
+        L.orc_combine_q_fma.argtypes = [P, P, i32, i32, P, P, i64, i32, i32, i64, i64, P]
+        L.orc_combine_q_fma.restype = None
+        L.orc_recv_list_fixed.argtypes = [P, i32, i32, i32, i32, P]
+        L.orc_recv_list_fixed.restype = None
+        L.orc_num_threads.argtypes = []
+        L.orc_num_threads.restype = i32
         for name in ("orc_bf16_from_f32_n", "orc_bf16_from_f64_n", "orc_e4m3fn_from_f32_n",
                      "orc_f32_from_e4m3fn_n"):
             getattr(L, name).argtypes = [P, P, i64]
             getattr(L, name).restype = None
-        _lib = L
-    return _lib
+        _libs[parallel] = L
+    return L
+
+
+def num_threads(parallel=False):
+    """Threads the per-token loops run on (1 for the serial build)."""
+    return int(lib(parallel).orc_num_threads())
 
 
 def _p(a):
@@ -222,6 +241,16 @@ def recv_list(psum_expert, num_experts, num_ranks, counts_as_prefix):
     return out
 
 
+def recv_list_fixed(num_unaligned, num_experts, num_ranks, capacity, counts_as_prefix):
+    """Host list of the fixed-capacity layout: min(count, capacity) per
+    expert, or its inclusive prefix restarting per rank."""
+    cnt = _c(num_unaligned, np.int32)
+    out = np.zeros(num_experts, np.int32)
+    lib().orc_recv_list_fixed(_p(cnt), num_experts, num_ranks, capacity,
+                              int(bool(counts_as_prefix)), _p(out))
+    return out
+
+
 QUANT_NONE, QUANT_FP8, QUANT_INT8, QUANT_MXFP4 = 0, 1, 2, 3
 SCALE_FP32, SCALE_POW2, SCALE_UE8M0 = 0, 1, 2
 
@@ -247,7 +276,7 @@ def scale_dtype(quant, scale_mode):
 
 
 def dispatch(x_bits, slot_idx, num_rows, quant=QUANT_NONE, group=None, t_begin=0, t_end=None,
-             recv_x=None, recv_scales=None, scale_mode=SCALE_FP32):
+             recv_x=None, recv_scales=None, scale_mode=SCALE_FP32, parallel=False):
     """a3. x_bits: uint16 [N,H] bf16 bit patterns.  Returns (recv_x, recv_scales):
     bf16 bits, or code bytes [rows, H] (FP8 / int8) or [rows, H/2] (MXFP4); scales
     fp32 or E8M0 bytes [rows, G]."""
@@ -269,7 +298,7 @@ def dispatch(x_bits, slot_idx, num_rows, quant=QUANT_NONE, group=None, t_begin=0
         if recv_scales is None:
             recv_scales = np.zeros((num_rows, G), scale_dtype(quant, scale_mode))
     assert recv_x.flags.c_contiguous
-    lib().orc_dispatch(_p(x), N, H, _p(sl), K, quant, group, scale_mode, t_begin, t_end,
+    lib(parallel).orc_dispatch(_p(x), N, H, _p(sl), K, quant, group, scale_mode, t_begin, t_end,
                        _p(recv_x), _p(recv_scales))
     return recv_x, recv_scales
 
@@ -282,9 +311,10 @@ def quantize_rows(x_bits, quant, group=None, scale_mode=SCALE_FP32):
 
 
 def combine_q(y_codes, y_scales, quant, group, topk_weights, slot_idx, t_begin=0, t_end=None,
-              out=None):
+              out=None, fp32=False, parallel=False):
     """a4 over quantised expert outputs: y_codes [S,H] (E4M3FN bytes or int8),
-    y_scales fp32 [S, H/group].  Returns uint16 bf16 bits [N,H]."""
+    y_scales fp32 [S, H/group].  Returns uint16 bf16 bits [N,H]: the exact sum
+    rounded once, or with fp32 the fp32 fused multiply-add chain."""
     yc = _c(y_codes, np.uint8 if quant == QUANT_FP8 else np.int8)
     ys = _c(y_scales, np.float32)
     w = _c(topk_weights, np.float32)
@@ -294,13 +324,17 @@ def combine_q(y_codes, y_scales, quant, group, topk_weights, slot_idx, t_begin=0
     t_end = N if t_end is None else t_end
     if out is None:
         out = np.zeros((N, H), np.uint16)
-    lib().orc_combine_q(_p(yc), _p(ys), quant, group, _p(w), _p(sl), N, K, H, t_begin, t_end,
-                        _p(out))
+    L = lib(parallel)
+    fn = L.orc_combine_q_fma if fp32 else L.orc_combine_q
+    fn(_p(yc), _p(ys), quant, group, _p(w), _p(sl), N, K, H, t_begin, t_end, _p(out))
     return out
 
 
-def combine(y_bits, topk_weights, slot_idx, t_begin=0, t_end=None, out=None):
-    """a4. y_bits uint16 [S,H]; topk_weights fp32 [N,K].  Returns uint16 [N,H]."""
+def combine(y_bits, topk_weights, slot_idx, t_begin=0, t_end=None, out=None, fp32=False,
+            parallel=False):
+    """a4. y_bits uint16 [S,H]; topk_weights fp32 [N,K].  Returns uint16 [N,H]:
+    the exact weighted sum rounded once to bf16, or with fp32 the fp32 fused
+    multiply-add chain over k ascending (combine_fma)."""
     y = _c(y_bits, np.uint16)
     w = _c(topk_weights, np.float32)
     sl = _c(slot_idx, np.int32)
@@ -310,5 +344,16 @@ def combine(y_bits, topk_weights, slot_idx, t_begin=0, t_end=None, out=None):
     if out is None:
         out = np.zeros((N, H), np.uint16)
     assert out.flags.c_contiguous
-    lib().orc_combine(_p(y), _p(w), _p(sl), N, K, H, t_begin, t_end, _p(out))
+    L = lib(parallel)
+    fn = L.orc_combine_fma if fp32 else L.orc_combine
+    fn(_p(y), _p(w), _p(sl), N, K, H, t_begin, t_end, _p(out))
     return out
+
+
+def combine_fma(y_bits, topk_weights, slot_idx, **kw):
+    """The combine in fp32: k ascending, one fused multiply-add per term."""
+    return combine(y_bits, topk_weights, slot_idx, fp32=True, **kw)
+
+
+def combine_q_fma(y_codes, y_scales, quant, group, topk_weights, slot_idx, **kw):
+    return combine_q(y_codes, y_scales, quant, group, topk_weights, slot_idx, fp32=True, **kw)

@@ -13,6 +13,22 @@
 #include <math.h>
 #include <string.h>
 #include <stdlib.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* The plain build is serial.  The same source built with OpenMP runs the
+ * per-token loops of dispatch and combine on several threads (each token's
+ * results depend on that token alone, so both builds give the same bits);
+ * that build only serves to time the oracle on a host's cores. */
+int orc_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 /* ------------------------------------------------------------------------ */
 /* Number formats                                                            */
@@ -423,6 +439,23 @@ void orc_recv_list(const int32_t* psum_expert, int E, int R, int counts_as_prefi
     }
 }
 
+/* Host list of the fixed-capacity layout: expert e's segment holds the
+ * rows actually filled, min(count, cap) (pairs past cap are dropped), so
+ * the list counts those, and with counts_as_prefix their inclusive prefix
+ * restarting at each rank's first local expert ("A2_DEEPEP.md"
+ * MOE_EXPERT_TOKEN_NUMS_TYPE, over the low-latency receive buffer of
+ * "DeepEP V1 vs V2 深度对比分析" §6.3). */
+void orc_recv_list_fixed(const int32_t* num_unaligned, int E, int R, int cap,
+                         int counts_as_prefix, int32_t* list)
+{
+    int nle = E / R;
+    for (int e = 0; e < E; ++e) {
+        int32_t c = num_unaligned[e] < cap ? num_unaligned[e] : cap;
+        if (counts_as_prefix && e % nle != 0) c += list[e - 1];
+        list[e] = c;
+    }
+}
+
 /* ------------------------------------------------------------------------ */
 /* a3: dispatch                                                              */
 /* ------------------------------------------------------------------------ */
@@ -503,6 +536,7 @@ void orc_dispatch(const uint16_t* x, int64_t N, int H, const int32_t* slot_idx, 
     (void)N;
     if (quant == 0) {
         uint16_t* rx = (uint16_t*)recv_x;
+#pragma omp parallel for schedule(static)
         for (int64_t t = t_begin; t < t_end; ++t)
             for (int k = 0; k < K; ++k) {
                 int64_t s = slot_idx[t * K + k];
@@ -516,10 +550,14 @@ void orc_dispatch(const uint16_t* x, int64_t N, int H, const int32_t* slot_idx, 
     /* bytes per received row: one per element, or two E2M1 codes per byte */
     int row_bytes = quant == 3 ? H / 2 : H;
     int byte_scales = quant == 3 || scale_mode == 2;
+    uint8_t* rx = (uint8_t*)recv_x;
+#pragma omp parallel
+    {
+    /* one token's codes and scales (per thread in the OpenMP build) */
     uint8_t* codes = (uint8_t*)calloc((size_t)row_bytes, 1);
     float* scales = (float*)malloc(sizeof(float) * (size_t)G);
     uint8_t* scale_bytes = (uint8_t*)malloc((size_t)G);
-    uint8_t* rx = (uint8_t*)recv_x;
+#pragma omp for schedule(static)
     for (int64_t t = t_begin; t < t_end; ++t) {
         const uint16_t* xt = x + t * H;
         for (int g = 0; g < G; ++g) {
@@ -558,16 +596,22 @@ void orc_dispatch(const uint16_t* x, int64_t N, int H, const int32_t* slot_idx, 
     free(codes);
     free(scales);
     free(scale_bytes);
+    }
 }
 
 /* ------------------------------------------------------------------------ */
 /* a4: combine                                                               */
 /* ------------------------------------------------------------------------ */
 
+/* Combine, the plain definition: the weighted sum of the token's expert
+ * outputs is formed exactly enough (fp64: each product of an fp32 weight and
+ * a bf16 value is exact, and K <= 16 such terms lose at most a few ulps of
+ * fp64) and rounded once to bf16. */
 void orc_combine(const uint16_t* y, const float* topk_weights, const int32_t* slot_idx,
                  int64_t N, int K, int H, int64_t t_begin, int64_t t_end, uint16_t* out)
 {
     (void)N;
+#pragma omp parallel for schedule(static)
     for (int64_t t = t_begin; t < t_end; ++t)
         for (int h = 0; h < H; ++h) {
             double acc = 0.0;
@@ -578,6 +622,37 @@ void orc_combine(const uint16_t* y, const float* topk_weights, const int32_t* sl
             }
             out[t * H + h] = orc_bf16_from_f64(acc);
         }
+}
+
+/* Combine accumulated in fp32 (the stated precision of the reduction; the
+ * order and the fused multiply-add are the reading): acc starts at +0 and,
+ * for k = 0, 1, ..., K-1 with a slot, acc = fmaf(w[t,k], y[slot, h], acc),
+ * one rounding per step; out = bf16(acc), nearest-even.  fmaf is the C
+ * library's correctly rounded fused multiply-add. */
+void orc_combine_fma(const uint16_t* y, const float* topk_weights, const int32_t* slot_idx,
+                     int64_t N, int K, int H, int64_t t_begin, int64_t t_end, uint16_t* out)
+{
+    (void)N;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = t_begin; t < t_end; ++t)
+        for (int h = 0; h < H; ++h) {
+            float acc = 0.0f;
+            for (int k = 0; k < K; ++k) {
+                int64_t s = slot_idx[t * K + k];
+                if (s < 0) continue;
+                acc = fmaf(topk_weights[t * K + k], orc_f32_from_bf16(y[s * H + h]), acc);
+            }
+            out[t * H + h] = orc_bf16_from_f32(acc);
+        }
+}
+
+/* Value of element h of a quantised expert-output row: code * scale. */
+static double code_value(const uint8_t* yc, const float* y_scales, int quant, int group, int H,
+                         int64_t s, int h)
+{
+    uint8_t c = yc[s * H + h];
+    double v = quant == 1 ? (double)orc_f32_from_e4m3fn(c) : (double)(int8_t)c;
+    return v * (double)y_scales[s * (H / group) + h / group];
 }
 
 /* Combine of quantised expert outputs ("DeepEP 通信库使用指南（v2.1）":
@@ -591,19 +666,42 @@ void orc_combine_q(const void* y_codes, const float* y_scales, int quant, int gr
                    int64_t t_begin, int64_t t_end, uint16_t* out)
 {
     (void)N;
-    int G = H / group;
     const uint8_t* yc = (const uint8_t*)y_codes;
+#pragma omp parallel for schedule(static)
     for (int64_t t = t_begin; t < t_end; ++t)
         for (int h = 0; h < H; ++h) {
             double acc = 0.0;
             for (int k = 0; k < K; ++k) {
                 int64_t s = slot_idx[t * K + k];
                 if (s < 0) continue;
-                uint8_t c = yc[s * H + h];
-                double v = quant == 1 ? (double)orc_f32_from_e4m3fn(c) : (double)(int8_t)c;
-                v *= (double)y_scales[s * G + h / group];
-                acc += (double)topk_weights[t * K + k] * v;
+                acc += (double)topk_weights[t * K + k] *
+                       code_value(yc, y_scales, quant, group, H, s, h);
             }
             out[t * H + h] = orc_bf16_from_f64(acc);
+        }
+}
+
+/* The same in fp32, as orc_combine_fma: the element value is the fp32
+ * product code * scale (one rounding), then acc = fmaf(w, value, acc) for k
+ * ascending, out = bf16(acc). */
+void orc_combine_q_fma(const void* y_codes, const float* y_scales, int quant, int group,
+                       const float* topk_weights, const int32_t* slot_idx, int64_t N, int K,
+                       int H, int64_t t_begin, int64_t t_end, uint16_t* out)
+{
+    (void)N;
+    const uint8_t* yc = (const uint8_t*)y_codes;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = t_begin; t < t_end; ++t)
+        for (int h = 0; h < H; ++h) {
+            float acc = 0.0f;
+            for (int k = 0; k < K; ++k) {
+                int64_t s = slot_idx[t * K + k];
+                if (s < 0) continue;
+                uint8_t c = yc[s * H + h];
+                float code = quant == 1 ? orc_f32_from_e4m3fn(c) : (float)(int8_t)c;
+                float v = code * y_scales[s * (H / group) + h / group];
+                acc = fmaf(topk_weights[t * K + k], v, acc);
+            }
+            out[t * H + h] = orc_bf16_from_f32(acc);
         }
 }

@@ -28,8 +28,16 @@
  * reading is listed with the function that takes it.
  *
  * Floating point: quantisation codes are decided in fp32 (the precision the
- * kernels decide them in); scales are fp32; the combine sum is formed in
- * fp64 and rounded once to bf16.
+ * kernels decide them in); scales are fp32.  The combine is given twice: as
+ * its plain definition (the weighted sum formed in fp64, rounded once to
+ * bf16) and as the fp32 reduction the path states (k ascending, one fused
+ * multiply-add per term, then bf16); the tests pin the second against
+ * exact arithmetic and the first.
+ *
+ * Threads: the plain build (libep_oracle.so) is serial and is the parity
+ * reference.  The same source built with OpenMP (libep_oracle_omp.so) runs
+ * the per-token loops of dispatch and combine in parallel, with the same
+ * results; it exists to time the oracle on a host's cores.
  *
  * Parity status: every function here is pinned by the CPU test suite
  * (closed forms, exhaustive format checks against torch's converters,
@@ -43,6 +51,9 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+/* Threads the library runs its per-token loops on (1 in the plain build). */
+int orc_num_threads(void);
 
 /* ---- number formats (written from the format definitions) ---- */
 
@@ -133,6 +144,13 @@ void orc_recv_topk(const int32_t* topk_idx, const float* topk_weights, const int
  * rank's first local expert. list [E]. */
 void orc_recv_list(const int32_t* psum_expert, int E, int R, int counts_as_prefix, int32_t* list);
 
+/* Host list of the fixed-capacity layout (orc_slots_fixed): the rows each
+ * expert's segment actually holds, min(num_unaligned[e], cap), or with
+ * counts_as_prefix their inclusive prefix restarting at each rank's first
+ * local expert.  list [E]. */
+void orc_recv_list_fixed(const int32_t* num_unaligned, int E, int R, int cap,
+                         int counts_as_prefix, int32_t* list);
+
 /* ---- a3: dispatch ([P3] §2.1/§2.2; quantisation [P5] §1.3.1, §1.3.3,
  *      [P3] §7.4) ----
  * x: bf16 bits [N,H]. For every t in [t_begin, t_end) and every k with
@@ -155,12 +173,23 @@ void orc_dispatch(const uint16_t* x, int64_t N, int H, const int32_t* slot_idx, 
 void orc_combine(const uint16_t* y, const float* topk_weights, const int32_t* slot_idx,
                  int64_t N, int K, int H, int64_t t_begin, int64_t t_end, uint16_t* out);
 
+/* The combine in fp32: acc = +0; for k ascending with slot_idx[t,k] >= 0,
+ * acc = fmaf(w[t,k], y[slot,h], acc); out[t,h] = bf16(acc), nearest-even. */
+void orc_combine_fma(const uint16_t* y, const float* topk_weights, const int32_t* slot_idx,
+                     int64_t N, int K, int H, int64_t t_begin, int64_t t_end, uint16_t* out);
+
 /* Combine of quantised expert outputs ([P5]: combine int8 / fp8 from v2.1):
  * y_codes [*,H] E4M3FN (quant 1) or int8 (quant 2) with fp32 y_scales
  * [*,H/group]; element value code * scale; otherwise as orc_combine. */
 void orc_combine_q(const void* y_codes, const float* y_scales, int quant, int group,
                    const float* topk_weights, const int32_t* slot_idx, int64_t N, int K, int H,
                    int64_t t_begin, int64_t t_end, uint16_t* out);
+
+/* The same in fp32: value = code * scale rounded to fp32, then the fmaf
+ * chain of orc_combine_fma. */
+void orc_combine_q_fma(const void* y_codes, const float* y_scales, int quant, int group,
+                       const float* topk_weights, const int32_t* slot_idx, int64_t N, int K,
+                       int H, int64_t t_begin, int64_t t_end, uint16_t* out);
 
 #ifdef __cplusplus
 }

@@ -254,6 +254,63 @@ def test_slots_fixed_relates_to_packed_layout():
     assert np.array_equal((f["slot_idx"] - e * 500)[valid], (p["slot_idx"] - p["psum_expert"][e])[valid])
 
 
+def test_worked_example_fixed_capacity():
+    """The hand-worked fixed-capacity layouts (capacity 1: three pairs
+    dropped; capacity 2: none) and their host lists."""
+    g = _gold()
+    idx = np.array(g["topk_idx"], np.int32)
+    E, R = g["num_experts"], g["num_ranks"]
+    for cap_s, want in g["fixed_capacity"].items():
+        cap = int(cap_s)
+        s = oracle.slots_fixed(idx, E, R, cap)
+        assert s["dropped"] == want["dropped"]
+        assert s["psum_expert"].tolist() == want["psum_expert"]
+        assert s["psum_rank"].tolist() == want["psum_rank"]
+        assert s["slot_idx"].tolist() == want["slot_idx"]
+        assert s["src_meta"].tolist() == want["src_meta"]
+        assert s["num_unaligned"].tolist() == g["num_unaligned"]
+        for prefix, key in ((False, "recv_list_counts"), (True, "recv_list_prefix")):
+            got = oracle.recv_list_fixed(s["num_unaligned"], E, R, cap, prefix)
+            assert got.tolist() == want[key], (cap, key)
+
+
+@pytest.mark.parametrize("N,K,E,R,cap", [(1, 1, 1, 1, 1), (200, 4, 16, 4, 10), (300, 6, 64, 8, 40),
+                                          (128, 8, 256, 16, 3), (64, 8, 32, 1, 64)])
+def test_recv_list_fixed_counts_filled_rows(N, K, E, R, cap):
+    """The fixed-capacity host list read off the layout itself: the rows of
+    each expert's segment that hold a pair (src_meta t >= 0), and for the
+    prefix form the filled rows of the rank's partition up to and including
+    the expert."""
+    rng = np.random.default_rng(N + 7 * cap)
+    idx = _random_routing(rng, N, K, E)
+    s = oracle.slots_fixed(idx, E, R, cap)
+    filled = (s["src_meta"][:, 0] >= 0).reshape(E, cap).sum(axis=1)
+    counts = oracle.recv_list_fixed(s["num_unaligned"], E, R, cap, False)
+    assert np.array_equal(counts, filled)
+    pref = oracle.recv_list_fixed(s["num_unaligned"], E, R, cap, True)
+    nle = E // R
+    for e in range(E):
+        first = (e // nle) * nle
+        rows = s["src_meta"][first * cap:(e + 1) * cap, 0]
+        assert pref[e] == (rows >= 0).sum(), e
+    # every rank's last entry is the pairs its partition holds
+    for r in range(R):
+        part = s["src_meta"][s["psum_rank"][r]:s["psum_rank"][r + 1], 0]
+        assert pref[(r + 1) * nle - 1] == (part >= 0).sum()
+
+
+def test_recv_list_fixed_with_room_is_packed_list():
+    """With room for every pair the fixed-capacity list equals the packed
+    layout's list at alignment 1 (both forms)."""
+    rng = np.random.default_rng(9)
+    idx = _random_routing(rng, 300, 8, 64)
+    f = oracle.slots_fixed(idx, 64, 8, 300 * 8)
+    p = oracle.slots(idx, 64, 8, 1)
+    for prefix in (False, True):
+        assert np.array_equal(oracle.recv_list_fixed(f["num_unaligned"], 64, 8, 300 * 8, prefix),
+                              oracle.recv_list(p["psum_expert"], 64, 8, prefix))
+
+
 # ---- several source ranks stacked in one batch ----------------------------
 
 def test_worked_example_multi_source():

@@ -352,3 +352,169 @@ def test_nonexpand_combine_sums_rank_rows():
             q = sum((Fraction(float(yv[r, h])) for r in rows), Fraction(0))
             got = int(out[t, h])
             assert got in (0, 0x8000) if q == 0 else got == _exact_bf16(q)
+
+
+# ---- the combine in fp32 (fused multiply-add chain) ------------------------
+
+def _nearest_f32(q: Fraction) -> np.float32:
+    """Nearest fp32 of an exact rational (ties to the even significand),
+    chosen by exact comparison among the fp32 neighbours of a starting
+    guess; the guess float(q) -> fp32 is within one ulp of the answer."""
+    g = np.float32(float(q))
+    cands = [np.nextafter(g, np.float32(-np.inf)), g, np.nextafter(g, np.float32(np.inf))]
+
+    def key(c):
+        return (abs(Fraction(float(c)) - q), int(np.array([c], np.float32).view(np.uint32)[0]) & 1)
+    return min(cands, key=key)
+
+
+def _fma_chain_bits(terms):
+    """bf16 bits of acc = +0, acc = fma(w, v, acc) over the (w, v) terms, each
+    step the exact w*v + acc rounded once to fp32; bf16 by torch's
+    nearest-even conversion."""
+    acc = np.float32(0.0)
+    for w, v in terms:
+        q = Fraction(float(w)) * Fraction(float(v)) + Fraction(float(acc))
+        acc = np.float32(0.0) if q == 0 else _nearest_f32(q)
+    return int(_bf16_bits(torch.tensor([acc], dtype=torch.float32).to(torch.bfloat16))[0])
+
+
+def test_combine_fma_is_the_exact_fma_chain():
+    rng = np.random.default_rng(23)
+    N, K, H, S = 40, 6, 16, 150
+    slot = rng.integers(-1, S, size=(N, K)).astype(np.int32)
+    w = rng.standard_normal((N, K)).astype(np.float32)
+    y = _x(S, H, 24)
+    slot[:6, 0] = 5
+    slot[:6, 1] = 5
+    slot[:6, 2:] = -1
+    w[:6, 1] = -w[:6, 0]                               # exact cancellation to +0
+    w[6:10, 1] = -np.nextafter(w[6:10, 0], np.float32(0))
+    slot[6:10, 1] = slot[6:10, 0]                      # near-total cancellation
+    slot[10] = -1                                      # all masked
+    out = oracle.combine_fma(y, w, slot)
+    yv = oracle.f32_from_bf16(y)
+    for t in range(N):
+        for h in range(H):
+            terms = [(w[t, k], yv[slot[t, k], h]) for k in range(K) if slot[t, k] >= 0]
+            assert int(out[t, h]) == _fma_chain_bits(terms), (t, h)
+    assert np.all(out[10] == 0)
+    # w*y - w*y: the exact sum is 0, the chain keeps the rounding error of
+    # the first product, at most half an fp32 ulp of w*y
+    assert np.all(oracle.combine(y, w, slot)[:6] == 0)
+    resid = np.abs(oracle.f32_from_bf16(out[:6]).astype(np.float64))
+    prod = np.abs(w[:6, :1].astype(np.float64) * yv[5].astype(np.float64))
+    assert np.all(resid <= 2.0 ** -24 * prod * (1 + 2.0 ** -7))
+
+
+def test_combine_fma_against_exact_sum():
+    """The fp32 chain and the exact sum round to the same bf16 value or to
+    neighbours, except where cancellation leaves the sum far below its
+    terms: there the difference stays within K * 2^-24 * sum|w*y| (the fp32
+    chain's error bound) plus the two bf16 roundings."""
+    rng = np.random.default_rng(25)
+    N, K, H, S = 512, 8, 256, 4096
+    slot = rng.integers(-1, S, size=(N, K)).astype(np.int32)
+    w = rng.standard_normal((N, K)).astype(np.float32)
+    y = _x(S, H, 26)
+    f = oracle.f32_from_bf16(oracle.combine_fma(y, w, slot)).astype(np.float64)
+    e = oracle.f32_from_bf16(oracle.combine(y, w, slot)).astype(np.float64)
+    yv = oracle.f32_from_bf16(y).astype(np.float64)
+    mag = np.zeros((N, H))
+    for k in range(K):
+        live = slot[:, k] >= 0
+        mag[live] += np.abs(w[live, k, None].astype(np.float64) * yv[slot[live, k]])
+    d = np.abs(f - e)
+    assert np.all(d <= 2.0 ** -8 * (np.abs(f) + np.abs(e)) + K * 2.0 ** -24 * mag)
+    assert (d > 2.0 ** -7 * np.abs(e)).mean() < 1e-3     # only cancellation elements
+    assert (f == e).mean() > 0.99
+
+
+def test_combine_fma_identities():
+    rng = np.random.default_rng(27)
+    N, S, H = 64, 200, 64
+    y = _x(S, H, 28)
+    slot = rng.integers(0, S, size=(N, 1)).astype(np.int32)
+    assert np.array_equal(oracle.combine_fma(y, np.ones((N, 1), np.float32), slot), y[slot[:, 0]])
+    slot = rng.integers(-1, S, size=(N, 4)).astype(np.int32)
+    wt = rng.random((N, 4)).astype(np.float32)
+    o1 = oracle.f32_from_bf16(oracle.combine_fma(y, wt, slot))
+    o2 = oracle.f32_from_bf16(oracle.combine_fma(y, 2 * wt, slot))
+    assert np.array_equal(2 * o1, o2)                   # scaling by 2 is exact in fp32
+
+
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+def test_round_trip_returns_x_fp32(name):
+    """The identity round trip holds for the fp32 chain too: with weights
+    summing to 1 its error (a few fp32 ulps) stays below half a bf16 ulp."""
+    w = W.WORKLOADS[name]
+    N, H = min(w.num_tokens, 256), min(w.hidden, 256)
+    idx, _ = W.routing(w, num_tokens=N)
+    rng = np.random.default_rng(w.seed + 1)
+    logits = rng.standard_normal(idx.shape)
+    logits[idx < 0] = -np.inf
+    wt = np.exp(logits - logits.max(axis=1, keepdims=True))
+    wt = (wt / wt.sum(axis=1, keepdims=True)).astype(np.float32)
+    wt[~np.isfinite(wt)] = 0
+    s = oracle.slots(idx, w.num_experts, w.num_ranks, w.expert_alignment)
+    x = _x(N, H, 98)
+    recv, _ = oracle.dispatch(x, s["slot_idx"], s["S"])
+    out = oracle.combine_fma(recv, wt, s["slot_idx"])
+    live = (idx >= 0).any(axis=1)
+    assert np.array_equal(out[live], x[live]) and np.all(out[~live] == 0)
+
+
+@pytest.mark.parametrize("quant,group", [(oracle.QUANT_FP8, 128), (oracle.QUANT_INT8, 256)])
+def test_combine_q_fma_is_the_exact_fma_chain(quant, group):
+    """Quantised inputs: each value is the fp32 product code * scale (one
+    rounding), then the fused multiply-add chain."""
+    rng = np.random.default_rng(29 + quant)
+    S, H, N, K = 40, 256, 10, 4
+    y = _x(S, H, 30)
+    codes, sc = oracle.quantize_rows(y, quant, group=group)          # fp32 scales
+    slot = rng.integers(-1, S, size=(N, K)).astype(np.int32)
+    w = rng.standard_normal((N, K)).astype(np.float32)
+    out = oracle.combine_q_fma(codes, sc, quant, group, w, slot)
+    dec = (oracle.f32_from_e4m3fn(codes.ravel()).reshape(S, H) if quant == oracle.QUANT_FP8
+           else codes.astype(np.float32))
+    for t in range(N):
+        for h in range(0, H, 5):
+            terms = []
+            for k in range(K):
+                s_ = slot[t, k]
+                if s_ >= 0:
+                    v = _nearest_f32(Fraction(float(dec[s_, h])) * Fraction(float(sc[s_, h // group])))
+                    terms.append((w[t, k], v))
+            assert int(out[t, h]) == _fma_chain_bits(terms), (t, h)
+
+
+# ---- the OpenMP build ---------------------------------------------------------
+
+@pytest.mark.parametrize("quant,group,scale_mode", [(oracle.QUANT_NONE, None, 0),
+                                                    (oracle.QUANT_FP8, 128, 0),
+                                                    (oracle.QUANT_INT8, 256, 0),
+                                                    (oracle.QUANT_FP8, 128, oracle.SCALE_UE8M0),
+                                                    (oracle.QUANT_MXFP4, 32, 0)])
+def test_openmp_build_matches_serial(quant, group, scale_mode):
+    """The OpenMP build (per-token loops on several threads) gives the
+    serial build's bits for dispatch and every combine form."""
+    assert oracle.num_threads(False) == 1 and oracle.num_threads(True) >= 1
+    idx, s, x = _setup(700, 6, 64, 8, 4, 256, 33, mask_p=0.05)
+    r1, s1 = oracle.dispatch(x, s["slot_idx"], s["S"], quant=quant, group=group,
+                             scale_mode=scale_mode)
+    r2, s2 = oracle.dispatch(x, s["slot_idx"], s["S"], quant=quant, group=group,
+                             scale_mode=scale_mode, parallel=True)
+    assert np.array_equal(r1.view(np.uint8), r2.view(np.uint8))
+    if s1 is not None:
+        assert np.array_equal(s1.view(np.uint8), s2.view(np.uint8))
+    rng = np.random.default_rng(34)
+    wt = rng.standard_normal(idx.shape).astype(np.float32)
+    y = _x(s["S"], 256, 35)
+    for fp32 in (False, True):
+        assert np.array_equal(oracle.combine(y, wt, s["slot_idx"], fp32=fp32),
+                              oracle.combine(y, wt, s["slot_idx"], fp32=fp32, parallel=True))
+        if quant in (oracle.QUANT_FP8, oracle.QUANT_INT8) and scale_mode == 0:
+            yc, ys = oracle.quantize_rows(y, quant, group=group)
+            assert np.array_equal(
+                oracle.combine_q(yc, ys, quant, group, wt, s["slot_idx"], fp32=fp32),
+                oracle.combine_q(yc, ys, quant, group, wt, s["slot_idx"], fp32=fp32, parallel=True))
