@@ -2,7 +2,9 @@
 
 Bars (see shuffle_check): layout, counts, slots, metadata and bf16 rows
 bit-exact; FP8/int8 codes within one step with fp32 scales bit-exact;
-combine within one bf16 ulp (plus the fp32 chain bound under cancellation).
+combine bit-exact against the oracle's fp32 reduction, and against its exact
+sum within one bf16 ulp except where cancellation leaves the sum far below
+its terms (those elements are counted and held to the fp32 chain bound).
 
 Sizes: every workload at full size (the sizes the benchmark times, all
 outputs compared), and reduced shapes that still span several layout blocks
@@ -29,8 +31,9 @@ def test_workload_full_size(name):
     w = W.WORKLOADS[name]
     _say(f"[parity] full {name} N={w.num_tokens} H={w.hidden}")
     st = run_and_check(w)
-    _say(f"[parity] {name}: S={st['S']} code_diffs={st['code_diffs']} "
-         f"combine_not_bit_identical={st.get('combine_not_bit_identical')}")
+    _say(f"[parity] {name}: S={st['S']} code_diffs={st['code_diffs']} combine vs exact sum: "
+         f"not bit-identical {st.get('combine_not_bit_identical')}, beyond 2^-7*|ref| "
+         f"{st.get('combine_beyond_strict_bar')} of {w.num_tokens * w.hidden}")
 
 
 REDUCED = [
@@ -146,7 +149,7 @@ def test_deterministic_across_runs():
         run.dispatch()
         y = run.recv
         run.combine(y)
-        v = ep.ep_handle_get_view(run.h)
+        v = ep.ep_handle_view(run.h)
         S = run.layout()["num_recv_slots"]
         torch.cuda.synchronize()
         # rows of src_meta beyond S are stale workspace by contract
@@ -189,7 +192,7 @@ def test_invalid_expert_ids_flagged_and_skipped(one_call):
     clean[3, 1] = -1
     clean[50, 0] = -1
     ref = oracle.slots(clean, 16, 4)
-    v = ep.ep_handle_get_view(run.h)
+    v = ep.ep_handle_view(run.h)
     assert np.array_equal(v["slot_idx"].cpu().numpy(), ref["slot_idx"])
     assert ep.ep_check_error(run.h) == (ep.EP_OK, 0)      # flags were cleared
 
@@ -294,7 +297,7 @@ def test_fixed_capacity_with_zipf_and_host_prefix():
     assert ref["dropped"] > 0                     # Zipf: hot experts overflow 64 rows
     assert lay["num_recv_slots"] == w.num_experts * 64
     assert lay["num_recv_tokens_per_expert_list"] == expected_host_list(w, ref, True)
-    v = ep.ep_handle_get_view(h)
+    v = ep.ep_handle_view(h)
     assert np.array_equal(v["slot_idx"].cpu().numpy(), ref["slot_idx"])
     assert ep.ep_check_error(h)[1] == ep.EP_FLAG_RECV_CAPACITY
 
@@ -345,7 +348,7 @@ def test_layout_dispatch_decode_workload_and_reuse():
     run.topk.copy_(torch.from_numpy(idx2))
     run.layout_dispatch()
     ref2 = oracle_slots(w2, idx2)
-    v = ep.ep_handle_get_view(run.h)
+    v = ep.ep_handle_view(run.h)
     assert np.array_equal(v["slot_idx"].cpu().numpy(), ref2["slot_idx"])
     assert ep.ep_check_error(run.h) == (ep.EP_OK, 0)
 
@@ -364,7 +367,7 @@ def test_layout_dispatch_empty_batch():
     assert lay["num_tokens_per_expert"].cpu().tolist() == [0] * 16
     assert lay["num_tokens_per_rank"].cpu().tolist() == [0] * 4
     assert lay["num_tokens_per_rdma_rank"].cpu().tolist() == [0, 0]
-    v = ep.ep_handle_get_view(h)
+    v = ep.ep_handle_view(h)
     assert v["psum_expert"].cpu().tolist() == [0] * 17
     assert ep.ep_check_error(h) == (ep.EP_OK, 0)
 
@@ -400,7 +403,7 @@ def test_multi_source_one_call_and_repeat():
     run.topk.copy_(torch.from_numpy(idx2))
     run.layout_dispatch()
     ref = oracle.source_counts(idx2, w.num_experts, w.num_ranks, 8)
-    v = ep.ep_handle_get_view(run.h)
+    v = ep.ep_handle_view(run.h)
     assert np.array_equal(v["psum_source_rank"].cpu().numpy(), ref["psum_source_rank"])
     assert np.array_equal(v["expert_source_base"].cpu().numpy(), ref["expert_source_base"])
     assert ep.ep_check_error(run.h) == (ep.EP_OK, 0)
@@ -412,7 +415,7 @@ def test_multi_source_empty_and_uneven():
     lay = ep.ep_get_layout(h, torch.empty((0, 2), dtype=torch.int32, device="cuda"),
                            do_cpu_sync=True)
     assert lay["num_recv_slots"] == 0
-    v = ep.ep_handle_get_view(h)
+    v = ep.ep_handle_view(h)
     assert v["psum_source_rank"].abs().sum().item() == 0
     assert v["expert_source_base"].abs().sum().item() == 0
     with pytest.raises(ep.EpError) as ei:
@@ -640,10 +643,10 @@ def test_overlap_with_rounds():
         pass
     run = R()
     run.w, run.recv, run.scales = b["w"], b["recv"], b["scales"]
-    from shuffle_check import compare_dispatch, compare_combine, bf16_values
+    from shuffle_check import compare_dispatch, compare_combine, combine_refs, bf16_values
     compare_dispatch(run, ref_recv, ref_scales, ref)
     y_bits = bits16(y)
-    compare_combine(bits16(b["out"]), oracle.combine(y_bits, b["wts"], ref["slot_idx"]),
+    compare_combine(bits16(b["out"]), combine_refs(y_bits, b["wts"], ref["slot_idx"]),
                     bf16_values(y_bits), b["wts"], ref["slot_idx"], w.num_topk)
     run.lay, run.h = nlay, hs[1]
     compare_layout(run, nb["idx"], oracle.layout(nb["idx"], w.num_experts, w.num_ranks,
@@ -703,7 +706,7 @@ def test_overlap_states(n, two_phase):
         assert ei.value.status == ep.EP_ERR_STATE
     ep.ep_combine_overlap(h0, y, wd, out, h_next=h1)
     ep.ep_dispatch(h1, x, recv)                     # finished: usable
-    v = ep.ep_handle_get_view(h1)
+    v = ep.ep_handle_view(h1)
     assert np.array_equal(v["slot_idx"].cpu().numpy(), oracle.slots(idx, 64, 8, 1)["slot_idx"])
     assert ep.ep_check_error(h0) == (ep.EP_OK, 0) and ep.ep_check_error(h1) == (ep.EP_OK, 0)
 
@@ -806,7 +809,7 @@ def test_graph_replay(pipeline):
     torch.cuda.synchronize()
     ref = [t.clone() for t in bufs]
     used = 1 if pipeline != "merged" else 2
-    ref_slots = [ep.ep_handle_get_view(hs[i])["slot_idx"].clone() for i in range(used)]
+    ref_slots = [ep.ep_handle_view(hs[i])["slot_idx"].clone() for i in range(used)]
     for i in range(used):
         exp = oracle.slots(routes[i][0], w.num_experts, w.num_ranks, w.expert_alignment)
         assert np.array_equal(ref_slots[i].cpu().numpy(), exp["slot_idx"])
@@ -826,6 +829,6 @@ def test_graph_replay(pipeline):
         for a, b in zip(ref, bufs):
             assert torch.equal(a, b), (pipeline, r)
         for i in range(used):
-            assert torch.equal(ep.ep_handle_get_view(hs[i])["slot_idx"], ref_slots[i])
+            assert torch.equal(ep.ep_handle_view(hs[i])["slot_idx"], ref_slots[i])
         for h in hs[:used]:
             assert ep.ep_check_error(h) == (ep.EP_OK, 0)
