@@ -23,7 +23,9 @@ EP_FLAG_BAD_EXPERT_ID, EP_FLAG_RECV_CAPACITY, EP_FLAG_Y_ROWS = 1, 2, 4
 # Every symbol include/ep.h declares.
 SYMBOLS = ("ep_workspace_size", "ep_recv_capacity", "ep_handle_init", "ep_handle_free",
            "ep_get_layout", "ep_dispatch", "ep_layout_dispatch", "ep_dispatch_topk",
-           "ep_combine", "ep_dispatch_overlap", "ep_combine_overlap", "ep_quantize_rows", "ep_set_kernel_events", "ep_handle_get_view", "ep_check_error", "ep_status_str", "ep_last_error_message")
+           "ep_combine", "ep_dispatch_overlap", "ep_combine_overlap", "ep_quantize_rows",
+           "ep_set_kernel_events", "ep_handle_view", "ep_handle_get_view", "ep_check_error",
+           "ep_status_str", "ep_last_error_message")
 
 
 class ep_config(ctypes.Structure):
@@ -37,7 +39,7 @@ class ep_config(ctypes.Structure):
                 ("non_expand", ctypes.c_int32)]
 
 
-class ep_handle_view(ctypes.Structure):
+class ep_handle_view_t(ctypes.Structure):
     _fields_ = [("psum_expert", ctypes.c_void_p), ("psum_rank", ctypes.c_void_p),
                 ("num_unaligned", ctypes.c_void_p), ("slot_idx", ctypes.c_void_p),
                 ("src_meta", ctypes.c_void_p), ("topk_idx", ctypes.c_void_p),
@@ -80,6 +82,7 @@ def lib():
         L.ep_dispatch_overlap.argtypes = [P, P, I64, I64, P, P, I64, P, P, I64, P, P, P, P, P]
         L.ep_combine_overlap.argtypes = [P, P, P, I64, P, I64, I64, P, P, P]
         L.ep_set_kernel_events.argtypes = [P, P, P]
+        L.ep_handle_view.argtypes = [P, P]
         L.ep_handle_get_view.argtypes = [P, P]
         L.ep_check_error.argtypes = [P, P, P]
         L.ep_status_str.argtypes = [I32]
@@ -88,7 +91,8 @@ def lib():
         L.ep_last_error_message.restype = ctypes.c_char_p
         for name in ("ep_workspace_size", "ep_recv_capacity", "ep_handle_init", "ep_get_layout",
                      "ep_dispatch", "ep_layout_dispatch", "ep_combine", "ep_quantize_rows",
-                     "ep_dispatch_topk", "ep_dispatch_overlap", "ep_combine_overlap", "ep_set_kernel_events", "ep_handle_get_view",
+                     "ep_dispatch_topk", "ep_dispatch_overlap", "ep_combine_overlap",
+                     "ep_set_kernel_events", "ep_handle_view", "ep_handle_get_view",
                      "ep_check_error"):
             getattr(L, name).restype = I32
         _lib = L
@@ -107,6 +111,8 @@ def _check(st):
 def _ptr(t: Optional[torch.Tensor]):
     if t is None:
         return None
+    if t.device.type != "cuda":
+        raise ValueError("tensors passed to the library must be on the GPU")
     if not t.is_contiguous():
         raise ValueError("tensors passed to the library must be contiguous")
     return ctypes.c_void_p(t.data_ptr())
@@ -226,8 +232,18 @@ def ep_handle_free(h: Handle):
     h.free()
 
 
+def _check_tensor(name, t, dtypes, shape, device):
+    """t must have one of dtypes, exactly `shape`, and live on `device`."""
+    if t is None:
+        return
+    if t.dtype not in dtypes or tuple(t.shape) != tuple(shape) or t.device != device:
+        raise ValueError(f"{name} must be {'/'.join(map(str, dtypes))} {list(shape)} on {device} "
+                         f"(got {t.dtype} {list(t.shape)} on {t.device})")
+
+
 def _layout_outputs(cfg, topk_idx, per_rank, per_rdma, per_expert, in_rank, alloc):
-    if topk_idx.dtype != torch.int32 or topk_idx.dim() != 2 or topk_idx.shape[1] != cfg.num_topk:
+    if (topk_idx is None or topk_idx.dtype != torch.int32 or topk_idx.dim() != 2
+            or topk_idx.shape[1] != cfg.num_topk):
         raise ValueError("topk_idx must be int32 [N, num_topk]")
     N = topk_idx.shape[0]
     dev = topk_idx.device
@@ -240,15 +256,26 @@ def _layout_outputs(cfg, topk_idx, per_rank, per_rdma, per_expert, in_rank, allo
             in_rank = torch.empty((N, cfg.num_ranks), dtype=torch.bool, device=dev)
         if per_rdma is None and cfg.num_nodes:
             per_rdma = torch.empty(cfg.num_nodes, dtype=torch.int32, device=dev)
+    # caller-supplied outputs: the library writes exactly these extents
+    _check_tensor("num_tokens_per_rank", per_rank, (torch.int32,), (cfg.num_ranks,), dev)
+    _check_tensor("num_tokens_per_expert", per_expert, (torch.int32,), (cfg.num_experts,), dev)
+    _check_tensor("is_token_in_rank", in_rank, (torch.bool, torch.uint8), (N, cfg.num_ranks), dev)
+    if per_rdma is not None:
+        if not cfg.num_nodes:
+            raise ValueError("num_tokens_per_rdma_rank needs ranks_per_node > 0")
+        _check_tensor("num_tokens_per_rdma_rank", per_rdma, (torch.int32,), (cfg.num_nodes,), dev)
     return per_rank, per_rdma, per_expert, in_rank
 
 
-def _check_dispatch_tensors(cfg, x, recv_x, recv_scales):
-    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[1] != cfg.hidden:
+def _check_dispatch_tensors(cfg, x, recv_x, recv_scales, token_begin=0, token_end=None):
+    """Dtypes and shapes of a dispatch's tensors; returns the token range
+    (token_end defaults to the rows of x)."""
+    if x is None or x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[1] != cfg.hidden:
         raise ValueError("x must be bf16 [N, hidden]")
     want = {EP_QUANT_NONE: (torch.bfloat16,), EP_QUANT_FP8_E4M3: (torch.uint8, torch.float8_e4m3fn),
             EP_QUANT_INT8: (torch.int8,), EP_QUANT_MXFP4: (torch.uint8,)}[cfg.quant]
-    if recv_x.dtype not in want or recv_x.dim() != 2 or recv_x.shape[1] != cfg.recv_row_elems:
+    if (recv_x is None or recv_x.dtype not in want or recv_x.dim() != 2
+            or recv_x.shape[1] != cfg.recv_row_elems):
         raise ValueError(f"recv_x must be {want} [rows, {cfg.recv_row_elems}]")
     if cfg.quant:
         if (recv_scales is None or recv_scales.dtype != cfg.scales_dtype
@@ -256,6 +283,12 @@ def _check_dispatch_tensors(cfg, x, recv_x, recv_scales):
             raise ValueError(f"recv_scales must be {cfg.scales_dtype} [rows, hidden/quant_group]")
     elif recv_scales is not None:
         raise ValueError("recv_scales must be None without quantisation")
+    if recv_x.device != x.device or (recv_scales is not None and recv_scales.device != x.device):
+        raise ValueError("x, recv_x and recv_scales must be on one device")
+    token_end = x.shape[0] if token_end is None else token_end
+    if not 0 <= token_begin <= token_end <= x.shape[0]:
+        raise ValueError("token range outside x")
+    return token_begin, token_end
 
 
 def ep_get_layout(h: Handle, topk_idx: torch.Tensor, num_tokens_per_rank=None,
@@ -292,10 +325,8 @@ def ep_dispatch(h: Handle, x: torch.Tensor, recv_x: torch.Tensor,
                 recv_scales: Optional[torch.Tensor] = None, token_begin=0, token_end=None):
     """a3.  x bf16 [N,H]; recv_x [rows,H] bf16 / uint8 (E4M3FN) / int8;
     recv_scales fp32 [rows,G] when quantised."""
-    _check_dispatch_tensors(h.cfg, x, recv_x, recv_scales)
-    token_end = x.shape[0] if token_end is None else token_end
-    if not 0 <= token_begin <= token_end <= x.shape[0]:
-        raise ValueError("token range outside x")
+    token_begin, token_end = _check_dispatch_tensors(h.cfg, x, recv_x, recv_scales, token_begin,
+                                                     token_end)
     _check(lib().ep_dispatch(h.ptr, _ptr(x), token_begin, token_end, _ptr(recv_x),
                              _ptr(recv_scales), recv_x.shape[0], _stream(x.device)))
     return recv_x, recv_scales
@@ -312,8 +343,8 @@ def ep_layout_dispatch(h: Handle, topk_idx: torch.Tensor, x: torch.Tensor, recv_
     outs = _layout_outputs(cfg, topk_idx, num_tokens_per_rank, num_tokens_per_rdma_rank,
                            num_tokens_per_expert, is_token_in_rank, alloc_outputs)
     _check_dispatch_tensors(cfg, x, recv_x, recv_scales)
-    if x.shape[0] != topk_idx.shape[0]:
-        raise ValueError("x and topk_idx disagree on the number of tokens")
+    if x.shape[0] != topk_idx.shape[0] or x.device != topk_idx.device:
+        raise ValueError("x and topk_idx disagree on the number of tokens or the device")
     _check(lib().ep_layout_dispatch(h.ptr, _ptr(topk_idx), topk_idx.shape[0], *map(_ptr, outs),
                                     _ptr(x), _ptr(recv_x), _ptr(recv_scales), recv_x.shape[0],
                                     _stream(x.device)))
@@ -338,11 +369,10 @@ def _check_y(cfg, y, y_scales):
         raise ValueError("y_scales must be fp32 [rows, hidden/combine_group]")
 
 
-def ep_combine(h: Handle, y: torch.Tensor, topk_weights: torch.Tensor, out: torch.Tensor,
-               token_begin=0, token_end=None, y_scales: Optional[torch.Tensor] = None):
-    """a4.  y bf16 [rows,H] (or codes with y_scales under combine_quant);
-    topk_weights fp32 [N,K]; out bf16 [N,H]."""
-    cfg = h.cfg
+def _check_combine_tensors(cfg, y, y_scales, topk_weights, out, token_begin, token_end):
+    """Dtypes and shapes of a combine's tensors; returns the token range
+    (token_end defaults to the rows of out).  The library reads weights and
+    writes out rows [token_begin, token_end) only, so both must hold them."""
     _check_y(cfg, y, y_scales)
     if topk_weights is not None and (topk_weights.dtype != torch.float32
                                      or topk_weights.dim() != 2
@@ -350,10 +380,22 @@ def ep_combine(h: Handle, y: torch.Tensor, topk_weights: torch.Tensor, out: torc
         raise ValueError("topk_weights must be fp32 [N, num_topk] or None (weights of 1)")
     if out.dtype != torch.bfloat16 or out.dim() != 2 or out.shape[1] != cfg.hidden:
         raise ValueError("out must be bf16 [N, hidden]")
+    for t in (y, y_scales, topk_weights):
+        if t is not None and t.device != out.device:
+            raise ValueError("y, y_scales, topk_weights and out must be on one device")
     token_end = out.shape[0] if token_end is None else token_end
     n_w = out.shape[0] if topk_weights is None else topk_weights.shape[0]
     if not 0 <= token_begin <= token_end <= min(out.shape[0], n_w):
         raise ValueError("token range outside out / topk_weights")
+    return token_begin, token_end
+
+
+def ep_combine(h: Handle, y: torch.Tensor, topk_weights: torch.Tensor, out: torch.Tensor,
+               token_begin=0, token_end=None, y_scales: Optional[torch.Tensor] = None):
+    """a4.  y bf16 [rows,H] (or codes with y_scales under combine_quant);
+    topk_weights fp32 [N,K]; out bf16 [N,H]."""
+    token_begin, token_end = _check_combine_tensors(h.cfg, y, y_scales, topk_weights, out,
+                                                    token_begin, token_end)
     _check(lib().ep_combine(h.ptr, _ptr(y), _ptr(y_scales), y.shape[0], _ptr(topk_weights),
                             token_begin, token_end, _ptr(out), _stream(out.device)))
     return out
@@ -368,10 +410,8 @@ def ep_dispatch_overlap(h: Handle, x: torch.Tensor, recv_x: torch.Tensor,
     next batch's layout in the same launch.  Returns the next batch's layout
     outputs (None without h_next); they are final after the ep_combine_overlap
     that names h_next."""
-    _check_dispatch_tensors(h.cfg, x, recv_x, recv_scales)
-    token_end = x.shape[0] if token_end is None else token_end
-    if not 0 <= token_begin <= token_end <= x.shape[0]:
-        raise ValueError("token range outside x")
+    token_begin, token_end = _check_dispatch_tensors(h.cfg, x, recv_x, recv_scales, token_begin,
+                                                     token_end)
     outs = (None, None, None, None)
     n_next = 0
     if h_next is not None:
@@ -393,9 +433,8 @@ def ep_combine_overlap(h: Handle, y: torch.Tensor, topk_weights: Optional[torch.
                        out: torch.Tensor, token_begin=0, token_end=None,
                        y_scales: Optional[torch.Tensor] = None, h_next: Optional[Handle] = None):
     """ep_combine of h's batch and the rest of h_next's layout, if it waits."""
-    cfg = h.cfg
-    _check_y(cfg, y, y_scales)
-    token_end = out.shape[0] if token_end is None else token_end
+    token_begin, token_end = _check_combine_tensors(h.cfg, y, y_scales, topk_weights, out,
+                                                    token_begin, token_end)
     _check(lib().ep_combine_overlap(h.ptr, _ptr(y), _ptr(y_scales), y.shape[0], _ptr(topk_weights),
                                     token_begin, token_end, _ptr(out),
                                     h_next.ptr if h_next is not None else None, _stream(out.device)))
@@ -408,7 +447,7 @@ def ep_dispatch_topk(h: Handle, topk_weights: Optional[torch.Tensor], recv_topk_
     weights (fp32 [rows, K]).  Allocates the outputs (rows = the receive
     capacity of the handle's last batch) unless given."""
     cfg = h.cfg
-    N = ep_handle_get_view(h)["num_tokens"]
+    N = ep_handle_view(h)["num_tokens"]
     dev = h.workspace.device
     rows = ep_recv_capacity(cfg, N) if rows is None else rows
     if recv_topk_idx is None:
@@ -416,7 +455,17 @@ def ep_dispatch_topk(h: Handle, topk_weights: Optional[torch.Tensor], recv_topk_
     if recv_topk_weights is None and topk_weights is not None:
         recv_topk_weights = torch.empty((rows, cfg.num_topk), dtype=torch.float32, device=dev)
     cap = recv_topk_idx.shape[0]
+    _check_tensor("recv_topk_idx", recv_topk_idx, (torch.int32,), (cap, cfg.num_topk), dev)
+    _check_tensor("recv_topk_weights", recv_topk_weights, (torch.float32,), (cap, cfg.num_topk),
+                  dev)
     token_end = N if token_end is None else token_end
+    if not 0 <= token_begin <= token_end <= N:
+        raise ValueError("token range outside the handle's batch")
+    if topk_weights is not None and (topk_weights.dtype != torch.float32 or topk_weights.dim() != 2
+                                     or topk_weights.shape[1] != cfg.num_topk
+                                     or topk_weights.shape[0] < token_end
+                                     or topk_weights.device != dev):
+        raise ValueError("topk_weights must be fp32 [>= token_end, num_topk] on the handle's device")
     _check(lib().ep_dispatch_topk(h.ptr, _ptr(topk_weights), token_begin, token_end,
                                   _ptr(recv_topk_idx), _ptr(recv_topk_weights), cap, _stream(dev)))
     return recv_topk_idx, recv_topk_weights
@@ -450,10 +499,10 @@ def ep_set_kernel_events(h: Handle, start_event=None, stop_event=None):
     _check(lib().ep_set_kernel_events(h.ptr, start_event, stop_event))
 
 
-def ep_handle_get_view(h: Handle):
+def ep_handle_view(h: Handle):
     """Device arrays of the handle as int32 tensor views of its workspace."""
-    v = ep_handle_view()
-    _check(lib().ep_handle_get_view(h.ptr, ctypes.byref(v)))
+    v = ep_handle_view_t()
+    _check(lib().ep_handle_view(h.ptr, ctypes.byref(v)))
     ws = h.workspace
     base = ws.data_ptr()
     cfg = h.cfg
@@ -479,6 +528,9 @@ def ep_handle_get_view(h: Handle):
                 topk_idx=arr(v.topk_idx, N * cfg.num_topk).view(N, cfg.num_topk),
                 num_tokens=v.num_tokens, max_tokens=v.max_tokens, max_slots=v.max_slots,
                 num_recv_slots=v.num_recv_slots)
+
+
+ep_handle_get_view = ep_handle_view
 
 
 def ep_check_error(h: Handle, raise_on_error=False):
@@ -511,6 +563,8 @@ def _bound(h, fn, *args):
 def bind_get_layout(h: Handle, topk_idx, num_tokens_per_rank=None, num_tokens_per_rdma_rank=None,
                     num_tokens_per_expert=None, is_token_in_rank=None, stream=None):
     """A callable issuing ep_get_layout (no CPU sync) with these tensors."""
+    _layout_outputs(h.cfg, topk_idx, num_tokens_per_rank, num_tokens_per_rdma_rank,
+                    num_tokens_per_expert, is_token_in_rank, False)
     s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream(topk_idx.device)
     return _bound(h, lib().ep_get_layout, h.ptr, _ptr(topk_idx), topk_idx.shape[0],
                   _ptr(num_tokens_per_rank), _ptr(num_tokens_per_rdma_rank),
@@ -519,6 +573,8 @@ def bind_get_layout(h: Handle, topk_idx, num_tokens_per_rank=None, num_tokens_pe
 
 def bind_dispatch(h: Handle, x, recv_x, recv_scales, token_begin, token_end, stream=None):
     """A callable issuing ep_dispatch with these tensors and token range."""
+    token_begin, token_end = _check_dispatch_tensors(h.cfg, x, recv_x, recv_scales, token_begin,
+                                                     token_end)
     s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream(x.device)
     return _bound(h, lib().ep_dispatch, h.ptr, _ptr(x), token_begin, token_end, _ptr(recv_x),
                   _ptr(recv_scales), recv_x.shape[0], s)
@@ -528,6 +584,11 @@ def bind_layout_dispatch(h: Handle, topk_idx, x, recv_x, recv_scales, num_tokens
                          num_tokens_per_rdma_rank=None, num_tokens_per_expert=None,
                          is_token_in_rank=None, stream=None):
     """A callable issuing ep_layout_dispatch with these tensors."""
+    _layout_outputs(h.cfg, topk_idx, num_tokens_per_rank, num_tokens_per_rdma_rank,
+                    num_tokens_per_expert, is_token_in_rank, False)
+    _check_dispatch_tensors(h.cfg, x, recv_x, recv_scales)
+    if x.shape[0] != topk_idx.shape[0] or x.device != topk_idx.device:
+        raise ValueError("x and topk_idx disagree on the number of tokens or the device")
     s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream(x.device)
     return _bound(h, lib().ep_layout_dispatch, h.ptr, _ptr(topk_idx), topk_idx.shape[0],
                   _ptr(num_tokens_per_rank), _ptr(num_tokens_per_rdma_rank),
@@ -539,6 +600,10 @@ def bind_dispatch_overlap(h: Handle, x, recv_x, recv_scales, token_begin, token_
                           topk_next, num_tokens_per_rank=None, num_tokens_per_rdma_rank=None,
                           num_tokens_per_expert=None, is_token_in_rank=None, stream=None):
     """A callable issuing ep_dispatch_overlap with these tensors."""
+    token_begin, token_end = _check_dispatch_tensors(h.cfg, x, recv_x, recv_scales, token_begin,
+                                                     token_end)
+    _layout_outputs(h_next.cfg, topk_next, num_tokens_per_rank, num_tokens_per_rdma_rank,
+                    num_tokens_per_expert, is_token_in_rank, False)
     s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream(x.device)
     return _bound(h, lib().ep_dispatch_overlap, h.ptr, _ptr(x), token_begin, token_end,
                   _ptr(recv_x), _ptr(recv_scales), recv_x.shape[0], h_next.ptr, _ptr(topk_next),
@@ -549,6 +614,8 @@ def bind_dispatch_overlap(h: Handle, x, recv_x, recv_scales, token_begin, token_
 def bind_combine_overlap(h: Handle, y, topk_weights, out, token_begin, token_end, h_next,
                          stream=None, y_scales=None):
     """A callable issuing ep_combine_overlap with these tensors."""
+    token_begin, token_end = _check_combine_tensors(h.cfg, y, y_scales, topk_weights, out,
+                                                    token_begin, token_end)
     s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream(out.device)
     return _bound(h, lib().ep_combine_overlap, h.ptr, _ptr(y), _ptr(y_scales), y.shape[0],
                   _ptr(topk_weights), token_begin, token_end, _ptr(out), h_next.ptr, s)
@@ -557,6 +624,8 @@ def bind_combine_overlap(h: Handle, y, topk_weights, out, token_begin, token_end
 def bind_combine(h: Handle, y, topk_weights, out, token_begin, token_end, stream=None,
                  y_scales=None):
     """A callable issuing ep_combine with these tensors and token range."""
+    token_begin, token_end = _check_combine_tensors(h.cfg, y, y_scales, topk_weights, out,
+                                                    token_begin, token_end)
     s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream(out.device)
     return _bound(h, lib().ep_combine, h.ptr, _ptr(y), _ptr(y_scales), y.shape[0],
                   _ptr(topk_weights), token_begin, token_end, _ptr(out), s)
