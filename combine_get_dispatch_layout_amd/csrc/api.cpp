@@ -821,7 +821,7 @@ ep_status ep_set_kernel_events(ep_handle* h, void* start_event, void* stop_event
     return EP_OK;
 }
 
-ep_status ep_handle_get_view(const ep_handle* h, ep_handle_view* v)
+ep_status ep_handle_view(const ep_handle* h, ep_handle_view_t* v)
 {
     if (!h || !v) return EP_FAIL(EP_ERR_INVALID_ARG, "handle or view is NULL");
     v->psum_expert = h->at<int32_t>(h->cv.psum_expert);
@@ -839,6 +839,8 @@ ep_status ep_handle_get_view(const ep_handle* h, ep_handle_view* v)
     v->expert_source_base = h->cv.src_base >= 0 ? h->at<int32_t>(h->cv.src_base) : nullptr;
     return EP_OK;
 }
+
+ep_status ep_handle_get_view(const ep_handle* h, ep_handle_view_t* v) { return ep_handle_view(h, v); }
 
 ep_status ep_check_error(ep_handle* h, void* stream, uint32_t* flags)
 {

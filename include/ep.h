@@ -17,6 +17,8 @@
  *        (per-expert counts or prefix sums).
  *   [P5] Aliyun "DeepEP 通信库使用指南（v2.1）" §1.3.1: int8 quant_size,
  *        group mode (128) or channel mode (= hidden).
+ *   [P4] lmdeploy PR #4783 "Integrate DeepEPv2": its status-check macro turns
+ *        a failed call into an error text carrying the source file and line.
  *
  * Conventions for every call:
  *   - Pointers named d_* are device pointers (HBM of the current HIP device),
@@ -138,8 +140,9 @@ typedef struct ep_config {
 
 typedef struct ep_handle ep_handle;
 
-/* Device arrays of a handle ([P3] §3.1 EPHandle). */
-typedef struct ep_handle_view {
+/* Device arrays of a handle ([P3] §3.1 EPHandle), as ep_handle_view fills
+ * them. */
+typedef struct ep_handle_view_s {
     const int32_t* psum_expert;    /* [E+1] exclusive prefix of aligned counts   */
     const int32_t* psum_rank;      /* [R+1] psum_expert at each rank's first
                                       expert: rank r's partition of the receive
@@ -164,27 +167,35 @@ typedef struct ep_handle_view {
     const int32_t* expert_source_base; /* [P, E] (P > 1, else NULL): pairs of
                                       expert e from the sources before p; source
                                       p's rows of e start at psum_expert[e] + this */
-} ep_handle_view;
+} ep_handle_view_t;
 
-/* Bytes of device workspace a handle needs for up to max_tokens tokens.
+/* Bytes of device workspace a handle needs for up to max_tokens tokens: the
+ * EPHandle arrays of [P3] §3.1 (prefix sums, the topk clone, slot indices,
+ * source metadata for ep_recv_capacity rows) plus the layout's block
+ * histograms, accumulators and flag word.  Sizing memory up front from the
+ * shape is the buffer rule of [P2]'s HCCL_BUFFSIZE note.
  * Returns EP_ERR_INVALID_ARG for an invalid configuration. */
 ep_status ep_workspace_size(const ep_config* cfg, int64_t max_tokens, int64_t* bytes);
 
 /* Receive rows a dispatch of num_tokens tokens can need in the worst case
- * (every pair valid, every expert fully padded): num_tokens*K + E*(A-1), or
+ * ([P2] HCCL_BUFFSIZE note: the receive buffer is sized from the token
+ * count, ranks, local experts and top-k; here every pair valid and every
+ * expert fully padded): num_tokens*K + E*(A-1), or
  * E*expert_capacity in the fixed-capacity layout, or num_tokens*min(K, R)
  * with non_expand.
  * Sizing recv_x / y with this many rows never triggers EP_ERR_CAPACITY. */
 ep_status ep_recv_capacity(const ep_config* cfg, int64_t num_tokens, int64_t* rows);
 
-/* Creates a handle over a caller-owned workspace (d_workspace, 256-byte
+/* Creates a handle, the routing state of [P3] §3.1 EPHandle that dispatch
+ * returns and combine reuses, over a caller-owned workspace (d_workspace, 256-byte
  * aligned, at least ep_workspace_size bytes; it must stay alive and unused by
  * anything else while the handle lives).  Clears the handle's flag word with
  * a kernel on `stream`.  The handle (host memory) is freed by ep_handle_free. */
 ep_status ep_handle_init(const ep_config* cfg, int64_t max_tokens, void* d_workspace,
                          int64_t workspace_bytes, void* stream, ep_handle** out);
 
-/* Frees the host-side handle; never touches the workspace.  NULL is a no-op. */
+/* Frees the host-side handle ([P3] §3.1 EPHandle); never touches the
+ * workspace.  NULL is a no-op. */
 void ep_handle_free(ep_handle* h);
 
 /* a1 + a2: routing layout and slot assignment ([P3] §2.1, §3.1, §8.4).
@@ -309,6 +320,8 @@ ep_status ep_dispatch_overlap(const ep_handle* h, const void* d_x, int64_t token
                               int32_t* d_num_tokens_per_rank, int32_t* d_num_tokens_per_rdma_rank,
                               int32_t* d_num_tokens_per_expert, uint8_t* d_is_token_in_rank,
                               void* stream);
+/* The combine half of the double-batch overlap ([P3] §5.2): ep_combine of h
+ * and the finish of h_next's layout, as described above. */
 ep_status ep_combine_overlap(const ep_handle* h, const void* d_y, const float* d_y_scales,
                              int64_t y_rows, const float* d_topk_weights, int64_t token_begin,
                              int64_t token_end, void* d_out, ep_handle* h_next, void* stream);
@@ -322,7 +335,8 @@ ep_status ep_combine_overlap(const ep_handle* h, const void* d_y, const float* d
 ep_status ep_quantize_rows(const ep_config* cfg, const void* d_x, int64_t rows, void* d_codes,
                            float* d_scales, void* stream);
 
-/* Profiling: the next ep_get_layout, ep_dispatch or ep_combine call on h
+/* Profiling (the per-stage timing behind the bandwidth figures of [P3] §4.3,
+ * measured on one GPU): the next ep_get_layout, ep_dispatch or ep_combine call on h
  * records start_event when its first kernel starts and stop_event when its
  * last kernel ends (timestamps of the kernel launches themselves, taken with
  * hipExtLaunchKernelGGL, so no marker is queued between kernels); the events
@@ -330,18 +344,34 @@ ep_status ep_quantize_rows(const ep_config* cfg, const void* d_x, int64_t rows, 
  * (either may be NULL).  Not thread-safe with calls on the same handle. */
 ep_status ep_set_kernel_events(ep_handle* h, void* start_event, void* stop_event);
 
-/* Device pointers and sizes held by a handle. */
-ep_status ep_handle_get_view(const ep_handle* h, ep_handle_view* view);
+/* Device pointers and sizes held by a handle: the EPHandle fields of [P3]
+ * §3.1 (psum_num_recv_tokens_per_expert = psum_expert,
+ * num_unaligned_recv_tokens_per_expert = num_unaligned, dst_buffer_slot_idx =
+ * slot_idx, recv_src_metadata = src_meta, the topk_idx clone,
+ * psum_num_recv_tokens_per_scaleup_rank = psum_source_rank).  The pointers
+ * stay valid while the handle lives; their contents change with the next
+ * layout on the handle. */
+ep_status ep_handle_view(const ep_handle* h, ep_handle_view_t* view);
 
-/* Waits for `stream`, reads and clears the handle's flag word.  *flags (if
+/* Another name for ep_handle_view (same arguments and result). */
+ep_status ep_handle_get_view(const ep_handle* h, ep_handle_view_t* view);
+
+/* Reports what only the device could see ([P4]'s convention: a failure is
+ * returned with a "file:line reason" text rather than lost).
+ * Waits for `stream`, reads and clears the handle's flag word.  *flags (if
  * non-NULL) receives the EP_FLAG_* bits.  Returns EP_ERR_DEVICE_INDEX for a
  * bad expert id or combine slot, EP_ERR_CAPACITY for a dispatch capacity
  * overflow, EP_OK if no flag was set. */
 ep_status ep_check_error(ep_handle* h, void* stream, uint32_t* flags);
 
+/* Name of a status code ("EP_OK", "EP_ERR_CAPACITY", ...; "EP_ERR_UNKNOWN"
+ * for a value outside ep_status): the status half of [P4]'s error text. */
 const char* ep_status_str(ep_status s);
 
-/* Text of the last error raised on the calling thread ("" if none). */
+/* Text of the last error raised on the calling thread ("" if none), in the
+ * "file:line reason" form of [P4]'s status checks, e.g.
+ * "api.cpp:123 num_topk=17 outside [1,16]".  Owned by the library; valid
+ * until the thread's next failing call. */
 const char* ep_last_error_message(void);
 
 #ifdef __cplusplus

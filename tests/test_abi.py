@@ -27,6 +27,30 @@ def test_library_exports_every_declared_symbol():
     L = ep.lib()
     for name in _declared_functions():
         assert hasattr(L, name), name
+    # the boundary's calls by their contract names
+    for name in ("ep_workspace_size", "ep_handle_init", "ep_handle_free", "ep_get_layout",
+                 "ep_dispatch", "ep_combine", "ep_handle_view", "ep_check_error",
+                 "ep_status_str", "ep_last_error_message"):
+        assert name in _declared_functions() and hasattr(L, name), name
+
+
+def test_every_call_cites_a_passage():
+    """Each declaration in include/ep.h is preceded by a comment that names
+    the page passage ([P2] ... [P5]) defining the operation."""
+    with open(os.path.join(ROOT, "include", "ep.h")) as f:
+        text = f.read()
+    body = text.split('extern "C" {', 1)[1]
+    decls = list(re.finditer(r"^(?:ep_status|void|const char\*) (ep_[a-z_]+)\(", body, flags=re.M))
+    assert len(decls) == len(ep.SYMBOLS)
+    missing, prev = [], 0
+    for m in decls:
+        before = body[prev:m.start()]
+        prev = m.end()
+        if m.group(1) == "ep_handle_get_view":
+            continue                      # the alias of ep_handle_view
+        if not re.search(r"\[P[2-5]\]", before):
+            missing.append(m.group(1))
+    assert not missing, missing
 
 
 def test_status_strings():
