@@ -19,12 +19,19 @@ cached (dispatch + combine on a handle whose layout was computed once before
 the timed loop: the cached-dispatch decode loop, whose step does not include
 the layout).
 
-Prints one JSON line.  `value` is tokens/s over whole steps; the roofline
-entry is for the kernel with the largest share of the step, with its
-achieved bandwidth = algorithmic bytes per launch / mean launch time taken
-from HIP events recorded on the launch stream inside the timed region.
-Buffers rotate over several independent sets so each step streams memory
-that the 256 MB Infinity Cache does not hold.
+Prints one JSON line.  `value` is tokens/s over whole steps, timed by the
+host clock around the K steps (no events inside that region).  Kernel times
+come from a second, eager pass of the same steps right after it, with HIP
+events on every launch (taken on the launch stream from the kernels' own
+start and end); the roofline entry is for the kernel with the largest share
+of the step, its achieved bandwidth = algorithmic bytes per launch / median
+launch time.  Buffers rotate over several independent sets so each step
+streams memory that the 256 MB Infinity Cache does not hold (--sets 1 gives
+the warm figures, labelled as such).
+
+cpu_baseline times the CPU oracle on the host: layout and slots serial, the
+per-token loops of dispatch and combine on the OpenMP build (all the
+threads OpenMP gives it); per-stage medians over full passes.
 """
 import argparse
 import hashlib
@@ -214,14 +221,18 @@ def traffic_summary(fetch_csv, write_csv, args):
     print(json.dumps(out, indent=1))
 
 
-def cpu_baseline(w, idx, wts, budget_s=12.0):
-    """The oracle, as it stands (serial C), on the same workload: repeated
-    full passes (layout, slots, dispatch, combine) until budget_s is spent."""
+def cpu_baseline(w, idx, wts, budget_s=10.0):
+    """The oracle, as it stands, on the same workload: full passes (layout,
+    slots, dispatch, combine) until budget_s is spent (at least 3).  Layout
+    and slots run on the serial build; dispatch and combine (the fp32
+    reduction) on the OpenMP build, which gives the same bits.  Reports the
+    median pass and per-stage medians."""
     import numpy as np
     import oracle
     import workloads as W
     import torch
     N = w.num_tokens
+    threads = oracle.num_threads(parallel=True)
     x = W.activations(N, w.hidden, W.x_seed(w)).view(torch.int16).numpy().view(np.uint16)
     s0 = (oracle.slots_nonexpand(idx, w.num_experts, w.num_ranks) if w.non_expand
           else oracle.slots(idx, w.num_experts, w.num_ranks, w.expert_alignment))
@@ -237,30 +248,45 @@ def cpu_baseline(w, idx, wts, budget_s=12.0):
                                       scale_mode=min(w.scale_mode, 1))
     out = np.zeros((N, w.hidden), np.uint16)
     ones = np.ones_like(wts)
-    reps, t0 = 0, time.perf_counter()
+    rounds = W.round_ranges(N, w.rounds)
+    times = {"layout": [], "slots": [], "dispatch": [], "combine": []}
+    t_start = time.perf_counter()
     while True:
+        t0 = time.perf_counter()
         oracle.layout(idx, w.num_experts, w.num_ranks, w.ranks_per_node)
-        s = oracle.slots(idx, w.num_experts, w.num_ranks, w.expert_alignment)
-        if w.non_expand:
-            s = oracle.slots_nonexpand(idx, w.num_experts, w.num_ranks)
-        for b, e in W.round_ranges(N, w.rounds):
+        t1 = time.perf_counter()
+        s = (oracle.slots_nonexpand(idx, w.num_experts, w.num_ranks) if w.non_expand
+             else oracle.slots(idx, w.num_experts, w.num_ranks, w.expert_alignment))
+        t2 = time.perf_counter()
+        for b, e in rounds:
             oracle.dispatch(x, s["slot_idx"], cap, quant=w.quant, group=w.quant_group or None,
                             t_begin=b, t_end=e, recv_x=recv, recv_scales=scales,
-                            scale_mode=w.scale_mode)
-        for b, e in W.round_ranges(N, w.rounds):
+                            scale_mode=w.scale_mode, parallel=True)
+        t3 = time.perf_counter()
+        for b, e in rounds:
             if w.combine_quant:
                 oracle.combine_q(yc, ys, w.combine_quant, w.combine_group, wts, s["slot_idx"],
-                                 t_begin=b, t_end=e, out=out)
+                                 t_begin=b, t_end=e, out=out, fp32=True, parallel=True)
             else:
                 oracle.combine(y, ones if w.non_expand else wts, s["slot_idx"], t_begin=b,
-                               t_end=e, out=out)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
+                               t_end=e, out=out, fp32=True, parallel=True)
+        t4 = time.perf_counter()
+        for k, a, b in (("layout", t0, t1), ("slots", t1, t2), ("dispatch", t2, t3),
+                        ("combine", t3, t4)):
+            times[k].append(b - a)
+        if len(times["layout"]) >= 3 and t4 - t_start >= budget_s:
             break
-    return dict(value=N * reps / el, unit="tokens/s", cores=1, kind="oracle",
-                sample=f"{reps} full pass(es) of the {w.name} workload ({N} tokens: layout, "
-                       f"slots, dispatch, combine), serial C, {el:.1f} s")
+    passes = len(times["layout"])
+    total = np.array(times["layout"]) + np.array(times["slots"]) + np.array(times["dispatch"]) \
+        + np.array(times["combine"])
+    med = {k: float(np.median(v)) for k, v in times.items()}
+    return dict(value=N / float(np.median(total)), unit="tokens/s", cores=threads,
+                host_cpus=os.cpu_count(), kind="oracle",
+                stages_ms={k: v * 1e3 for k, v in med.items()},
+                sample=f"{passes} full passes of the {w.name} workload ({N} tokens: layout and "
+                       f"slots serial, dispatch and fp32 combine over tokens on {threads} "
+                       f"OpenMP threads), median pass {np.median(total) * 1e3:.1f} ms, "
+                       f"{time.perf_counter() - t_start:.1f} s")
 
 
 class HipEvents:
@@ -316,7 +342,7 @@ def main():
                     help=">1: read the batch as this many stacked source ranks (receive order "
                          "(source, token, k) plus the per-source counts)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=12.0,
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle passes behind cpu_baseline")
     ap.add_argument("--pipeline", choices=("merged", "overlap", "serial", "fused", "cached"),
                     default=None,
@@ -330,16 +356,13 @@ def main():
                          "combine, one stream (one round only); cached: the layout is computed "
                          "once per buffer set and each step is dispatch + combine on the cached "
                          "handle (a decode loop whose routing does not change)")
-    ap.add_argument("--time-every", type=int, default=4,
-                    help="rotate mode: arm kernel events on every N-th timed step")
-    ap.add_argument("--timing", choices=("rotate", "all"), default="rotate",
-                    help="rotate: each timed step arms kernel events on one stage, in turn "
-                         "(layout, dispatch, combine); all: every call of every step")
+    ap.add_argument("--event-steps", type=int, default=50,
+                    help="steps of the eager pass after the timed region that takes kernel "
+                         "times (HIP events on every launch; at least 10)")
     ap.add_argument("--graph", action="store_true",
                     help="capture one rotation of steps (one step per buffer set) in a HIP "
-                         "graph and time its replays (steps rounded up to whole rotations); "
-                         "kernel times then come from an eager pass of the same calls after "
-                         "the timed replays (merged, serial, fused and cached pipelines)")
+                         "graph and time its replays (steps rounded up to whole rotations) "
+                         "(merged, serial, fused and cached pipelines)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc runs into profiles/ and exit")
     args = ap.parse_args()
@@ -468,27 +491,13 @@ def main():
         s["main_done"].record(stream)
 
     stage_of = [st for st, _ in sets[0]["calls"]]
-    nstages = len(stage_names)
-    # one (start, stop) event pair per kernel call of every timed step
     calls_per_step = len(stage_of)
-    hev = HipEvents(2 * calls_per_step * args.steps)
-
-    # a short run still times every stage: the rotation period shrinks
-    every = max(1, min(args.time_every, args.steps // nstages))
-
-    def armed(i, j):
-        """Whether call j of timed step i carries kernel events: every call of
-        every step ("all"), or, on every `every`-th step, the calls of one
-        stage, the stages in turn."""
-        if args.timing == "all":
-            return True
-        if i % every:
-            return False
-        return stage_of[j] == (i // every) % nstages
+    ev_steps = max(10, args.event_steps)
+    hev = None   # the eager pass's (start, stop) event pair per call of every step
 
     def issue(i, j, base):
         c = sets[i % nsets]["calls"][j][1]
-        if base is None or not armed(i, j):
+        if base is None:
             c()
         else:
             c((hev.ev[base + 2 * j], hev.ev[base + 2 * j + 1]))
@@ -514,7 +523,8 @@ def main():
 
     def run(n, timed):
         """n steps; with overlap the layout of step i+1 is issued before the
-        dispatch and combine of step i, otherwise each step's calls in order."""
+        dispatch and combine of step i, otherwise each step's calls in order.
+        timed: every call carries kernel events (the eager timing pass)."""
         def base(i):
             return 2 * calls_per_step * i if timed else None
         if pl == "merged":
@@ -522,7 +532,7 @@ def main():
                 c = sets[gstep[0] % nsets]["calls"]
                 gstep[0] += 1
                 for j in range(calls_per_step):
-                    if base(i) is None or not armed(i, j):
+                    if base(i) is None:
                         c[j][1]()
                     else:
                         c[j][1]((hev.ev[base(i) + 2 * j], hev.ev[base(i) + 2 * j + 1]))
@@ -539,12 +549,12 @@ def main():
                     issue(i, j, base(i))
 
     torch.cuda.synchronize()   # set-up work on the default stream is done
+    run(args.warmup, False)
+    torch.cuda.synchronize()
     if args.graph:
         # one rotation (a step per buffer set) as one graph: the merged
         # pipeline's host bookkeeping advances by a whole rotation during the
         # capture, the device catches up on each replay
-        run(args.warmup, False)
-        torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=stream):
             run(nsets, False)
@@ -558,24 +568,24 @@ def main():
         t_enqueue = time.perf_counter() - t0
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        # kernel times: an eager pass of the same calls
-        hev.close()
-        hev = HipEvents(2 * calls_per_step * args.steps)
-        run(args.steps, True)
-        torch.cuda.synchronize()
     else:
-        run(args.warmup, False)
-        torch.cuda.synchronize()
         t0 = time.perf_counter()
-        run(args.steps, True)
+        run(args.steps, False)
         t_enqueue = time.perf_counter() - t0
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
 
+    # kernel times: an eager pass of the same steps with events on every call
+    # (the host then issues slower than the GPU runs, which the kernels' own
+    # start / end timestamps do not see)
+    hev = HipEvents(2 * calls_per_step * ev_steps)
+    run(ev_steps, True)
+    torch.cuda.synchronize()
+
     def durs(j):
-        """Per-step duration (s) of call j over the steps that timed it."""
+        """Per-step duration (s) of call j over the eager pass."""
         return np.array([hev.ms(2 * calls_per_step * i + 2 * j, 2 * calls_per_step * i + 2 * j + 1)
-                         for i in range(args.steps) if armed(i, j)]) * 1e-3
+                         for i in range(ev_steps)]) * 1e-3
 
     # per stage: per-step durations (sum over the stage's launches), bytes, launches
     per_stage = {}
@@ -585,12 +595,12 @@ def main():
     hev.close()
     ms_per_step = wall / args.steps * 1e3
     value = N * args.steps / wall
-    stages = {k: (float(np.mean(d)), by, n) for k, (d, by, n) in per_stage.items()}
+    stages = {k: (float(np.median(d)), by, n) for k, (d, by, n) in per_stage.items()}
     moving = [k for k in stage_names if k != "layout"]   # the dispatch + combine stages
     t_dc = sum(stages[k][0] for k in moving)
     dom = max(moving, key=lambda k: stages[k][0])
     t_dom, b_dom, launches = stages[dom]
-    achieved = b_dom / t_dom / 1e9   # = per-launch bytes / mean per-launch time
+    achieved = b_dom / t_dom / 1e9   # = per-launch bytes / median per-launch time
     b_dc = sum(stages[k][1] for k in moving)
     # the kernel that carries the stage (merged, one round: the launch that
     # also lays out the next batch; with rounds, most launches are plain)
@@ -647,7 +657,14 @@ def main():
                              "frac_of_peak": b_dc / t_dc / 1e9 / HBM_PEAK_GBS},
         "device_copy_GBps": copy_gbs,
         "pipeline": args.pipeline,
-        "timing": {"mode": args.timing, "every": every, "graph": args.graph,
+        "cache": ("warm: one buffer set, reused every step (Infinity-Cache-resident where it "
+                  "fits)" if nsets == 1 else
+                  f"cold: {nsets} buffer sets rotate, {nsets * per_set / 2**30:.2f} GiB per "
+                  "cycle against a 256 MB Infinity Cache"),
+        "timing": {"wall_clock": "host clock around the timed steps, no events inside",
+                   "kernels": "eager pass after the timed steps, HIP events on every launch, "
+                              "medians",
+                   "graph": args.graph,
                    "host_enqueue_ms_per_step": t_enqueue / args.steps * 1e3,
                    "samples_per_stage": {k: int(len(d)) for k, (d, _, _) in per_stage.items()}},
         "recv_rows": S, "valid_pairs": V,

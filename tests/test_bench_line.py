@@ -39,8 +39,13 @@ def test_default_line_has_the_contract_fields():
     assert 0 < rf["achieved"] < rf["peak"]
     assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-9
     assert rf["traffic"] is None or rf["traffic"] > 0
+    # kernel times from an eager pass with every launch timed: medians of
+    # at least 10 samples per stage
+    assert all(n >= 10 for n in line["timing"]["samples_per_stage"].values())
     cb = line["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1
+    assert cb["host_cpus"] >= 1 and set(cb["stages_ms"]) == {"layout", "slots", "dispatch",
+                                                             "combine"}
     assert cb["unit"] == line["unit"] and cb["sample"]
 
 

@@ -52,6 +52,26 @@ def test_zipf_masked_routing():
     assert 6500 < cnt[0] < 7800
 
 
+def test_permuted_zipf_routing():
+    """The permuted variant: the same popularity law over a seeded
+    permutation of the experts, so sorted counts match the un-permuted
+    workload's closely while the hot experts spread over the ranks."""
+    w = W.WORKLOADS["deepseek_v3_prefill_permuted"]
+    idx, wts = W.routing(w)
+    _distinct_valid(idx, w.num_experts)
+    assert abs((idx < 0).mean() - w.mask_prob) < 0.005
+    cnt = np.bincount(idx[idx >= 0], minlength=w.num_experts)
+    ref_idx, _ = W.routing(W.WORKLOADS["deepseek_v3_prefill"])
+    ref = np.bincount(ref_idx[ref_idx >= 0], minlength=w.num_experts)
+    srt, rsrt = np.sort(cnt)[::-1], np.sort(ref)[::-1]
+    assert np.abs(srt - rsrt).max() < 0.05 * rsrt[0] + 5 * np.sqrt(rsrt[0])
+    assert cnt.argmax() != 0                       # the hottest expert moved
+    nle = w.num_experts // w.num_ranks
+    per_rank = cnt.reshape(w.num_ranks, nle).sum(axis=1)
+    ref_rank = ref.reshape(w.num_ranks, nle).sum(axis=1)
+    assert per_rank.max() < ref_rank.max()         # rank 0 no longer takes the hot block
+
+
 def test_softmax_topk_routing_raw_weights():
     w = W.WORKLOADS["tiny"]
     idx, wts = W.routing(w)

@@ -33,7 +33,7 @@ class Workload:
     quant: int = QUANT_NONE
     quant_group: int = 0          # elements per scale; 0 = not quantised
     mask_prob: float = 0.0
-    routing: str = "uniform"      # uniform | softmax_topk | zipf | group_limited
+    routing: str = "uniform"      # uniform | softmax_topk | zipf | zipf_permuted | group_limited
     weights: str = "softmax"      # softmax (renormalised over chosen k) | raw (the router's own)
     zipf_s: float = 1.2
     rounds: int = 1
@@ -64,6 +64,11 @@ WORKLOADS = {
                                     seed=1004),
     "long_seq_int8": Workload("long_seq_int8", 32768, 4096, 64, 8, 6, quant=QUANT_INT8,
                               quant_group=4096, rounds=4, seed=1005),
+    # the same shape with the Zipf popularity spread over the experts by a
+    # seeded permutation, so the hot experts no longer sit on rank 0
+    "deepseek_v3_prefill_permuted": Workload("deepseek_v3_prefill_permuted", 8192, 7168, 256, 16,
+                                             8, expert_alignment=128, mask_prob=0.05,
+                                             routing="zipf_permuted", seed=1007),
     # DeepSeek-V3 gating (256 experts in 32 groups, top-4 groups, top-2 per
     # group) with the non-expand dispatch that sends a token once per rank
     "deepseek_v3_group_limited": Workload("deepseek_v3_group_limited", 8192, 7168, 256, 16, 8,
@@ -123,8 +128,11 @@ def routing(w: Workload, num_tokens: Optional[int] = None):
         wts = None
     elif w.routing == "group_limited":
         idx, wts = _group_limited(rng.standard_normal((N, E)), w.expert_groups, w.topk_groups, K)
-    elif w.routing == "zipf":
-        logp = -w.zipf_s * np.log(np.arange(1, E + 1, dtype=np.float64))
+    elif w.routing in ("zipf", "zipf_permuted"):
+        # p_e proportional to (rank_e + 1)^-s; rank_e = e, or a seeded
+        # permutation of the experts
+        rank = rng.permutation(E) if w.routing == "zipf_permuted" else np.arange(E)
+        logp = -w.zipf_s * np.log(rank.astype(np.float64) + 1.0)
         gumbel = -np.log(-np.log(rng.random((N, E))))
         idx = np.argsort(-(logp[None, :] + gumbel), axis=1, kind="stable")[:, :K]
         wts = None
