@@ -9,9 +9,18 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "ep_internal.hpp"
+
+// Workspace of the handles made by ep_handle_init_static, for callers that
+// cannot allocate device memory.  Each GPU the library is loaded on holds
+// its own copy until the process ends.  Host code never uses this name as a
+// device address: the address comes from hipGetSymbolAddress, once per
+// device (static_scratch_ptr below).
+constexpr int64_t kStaticScratchBytes = EP_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 
 namespace {
 
@@ -195,6 +204,7 @@ struct ep_handle {
     // layout counted inside a dispatch launch, to be finished inside the
     // next ep_combine_overlap launch (see ep_dispatch_overlap)
     bool pending = false;
+    bool is_static = false;   // ep_handle_init_static's per-device handle: never deleted
     epk::LayoutArgs pending_args, pending_args2;   // second: the rank level (non-expand)
     epk::SourceArgs pending_src;                   // stacked sources
     epk::OverlapPlan pending_plan;
@@ -504,6 +514,29 @@ ep_status next_layout(const ep_handle* h, ep_handle* h_next, const int32_t* d_to
     return EP_OK;
 }
 
+// Per-device state of ep_handle_init_static: the device address of
+// `scratch` (looked up once per device, with that device current) and the
+// one handle whose workspace it is.
+constexpr int kMaxStaticDevices = 64;
+std::mutex g_static_mu;
+unsigned char* g_static_ws[kMaxStaticDevices] = {};
+ep_handle g_static_handles[kMaxStaticDevices];
+
+ep_status static_scratch_ptr(int dev, unsigned char** ws)
+{
+    std::lock_guard<std::mutex> lock(g_static_mu);
+    if (!g_static_ws[dev]) {
+        void* p = nullptr;
+        hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return EP_FAIL(EP_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                           hipGetErrorString(e));
+        g_static_ws[dev] = static_cast<unsigned char*>(p);
+    }
+    *ws = g_static_ws[dev];
+    return EP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -573,7 +606,58 @@ ep_status ep_handle_init(const ep_config* cfg, int64_t max_tokens, void* d_works
     return EP_OK;
 }
 
-void ep_handle_free(ep_handle* h) { delete h; }
+void ep_handle_free(ep_handle* h)
+{
+    if (h && !h->is_static) delete h;
+}
+
+ep_status ep_handle_init_static(const ep_config* cfg, int64_t max_tokens, void* stream,
+                                ep_handle** out)
+{
+    ep_status st = check_config(cfg);
+    if (st != EP_OK) return st;
+    if (!out) return EP_FAIL(EP_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    Carve cv;
+    st = carve(*cfg, max_tokens, &cv);
+    if (st != EP_OK) return st;
+    if (cv.total > kStaticScratchBytes)
+        return EP_FAIL(EP_ERR_WORKSPACE,
+                       "the handle needs %lld bytes of workspace; the static scratch holds %lld "
+                       "(use ep_handle_init with a workspace)",
+                       (long long)cv.total, (long long)kStaticScratchBytes);
+    int dev = 0;
+    EP_HIP(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxStaticDevices)
+        return EP_FAIL(EP_ERR_INVALID_ARG, "device %d beyond the %d static handles", dev,
+                       kMaxStaticDevices);
+    unsigned char* ws = nullptr;
+    st = static_scratch_ptr(dev, &ws);
+    if (st != EP_OK) return st;
+    ep_handle* h = &g_static_handles[dev];
+    *h = ep_handle{};
+    h->is_static = true;
+    h->cfg = *cfg;
+    h->max_tokens = max_tokens;
+    h->max_slots = max_slots_for(*cfg, max_tokens);
+    h->nodes = num_nodes(*cfg);
+    h->ws = ws;
+    h->cv = cv;
+    h->num_tokens = -1;
+    h->host_slots = -1;
+    // the array keeps the last call's contents: clear what starts at zero
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = epk::launch_clear(h->at<uint32_t>(cv.ctrl), epk::kCtrlWords, s);
+    if (e == hipSuccess)
+        e = epk::launch_clear(h->at<uint32_t>(cv.acc), epk::kAccCopies * (cfg->num_ranks + h->nodes),
+                              s);
+    if (e == hipSuccess && cv.src_acc >= 0)
+        e = epk::launch_clear(h->at<uint32_t>(cv.src_acc),
+                              num_sources(*cfg) * (cfg->num_experts + cfg->num_ranks), s);
+    if (e != hipSuccess) return EP_FAIL(EP_ERR_HIP, "clearing the control words: %s", hipGetErrorString(e));
+    *out = h;
+    return EP_OK;
+}
 
 ep_status ep_get_layout(ep_handle* h, const int32_t* d_topk_idx, int64_t num_tokens,
                         int32_t* d_num_tokens_per_rank, int32_t* d_num_tokens_per_rdma_rank,

@@ -21,7 +21,8 @@ EP_SCALE_FP32, EP_SCALE_POW2, EP_SCALE_UE8M0 = 0, 1, 2
 EP_FLAG_BAD_EXPERT_ID, EP_FLAG_RECV_CAPACITY, EP_FLAG_Y_ROWS = 1, 2, 4
 
 # Every symbol include/ep.h declares.
-SYMBOLS = ("ep_workspace_size", "ep_recv_capacity", "ep_handle_init", "ep_handle_free",
+SYMBOLS = ("ep_workspace_size", "ep_recv_capacity", "ep_handle_init", "ep_handle_init_static",
+           "ep_handle_free",
            "ep_get_layout", "ep_dispatch", "ep_layout_dispatch", "ep_dispatch_topk",
            "ep_combine", "ep_dispatch_overlap", "ep_combine_overlap", "ep_quantize_rows",
            "ep_set_kernel_events", "ep_handle_view", "ep_handle_get_view", "ep_check_error",
@@ -71,6 +72,7 @@ def lib():
         L.ep_workspace_size.argtypes = [P, I64, P]
         L.ep_recv_capacity.argtypes = [P, I64, P]
         L.ep_handle_init.argtypes = [P, I64, P, I64, P, P]
+        L.ep_handle_init_static.argtypes = [P, I64, P, P]
         L.ep_handle_free.argtypes = [P]
         L.ep_handle_free.restype = None
         L.ep_get_layout.argtypes = [P, P, I64, P, P, P, P, I32, P, P, P]
@@ -89,7 +91,8 @@ def lib():
         L.ep_status_str.restype = ctypes.c_char_p
         L.ep_last_error_message.argtypes = []
         L.ep_last_error_message.restype = ctypes.c_char_p
-        for name in ("ep_workspace_size", "ep_recv_capacity", "ep_handle_init", "ep_get_layout",
+        for name in ("ep_workspace_size", "ep_recv_capacity", "ep_handle_init",
+                     "ep_handle_init_static", "ep_get_layout",
                      "ep_dispatch", "ep_layout_dispatch", "ep_combine", "ep_quantize_rows",
                      "ep_dispatch_topk", "ep_dispatch_overlap", "ep_combine_overlap",
                      "ep_set_kernel_events", "ep_handle_view", "ep_handle_get_view",
@@ -187,13 +190,20 @@ def ep_recv_capacity(cfg: Config, num_tokens: int) -> int:
 
 
 class Handle:
-    """Owns the C handle and keeps its workspace tensor alive."""
+    """Owns the C handle and keeps its workspace tensor alive (None for the
+    library's static handle, whose workspace is the library's own)."""
 
-    def __init__(self, cfg: Config, max_tokens: int, workspace: torch.Tensor, ptr: int):
+    def __init__(self, cfg: Config, max_tokens: int, workspace: Optional[torch.Tensor], ptr: int,
+                 device=None):
         self.cfg = cfg
         self.max_tokens = max_tokens
         self.workspace = workspace
+        self._device = workspace.device if workspace is not None else torch.device(device)
         self._ptr = ctypes.c_void_p(ptr)
+
+    @property
+    def device(self):
+        return self._device
 
     @property
     def ptr(self):
@@ -226,6 +236,21 @@ def ep_handle_init(cfg: Config, max_tokens: int, workspace: Optional[torch.Tenso
                                 workspace.numel() * workspace.element_size(),
                                 _stream(workspace.device), ctypes.byref(out)))
     return Handle(cfg, max_tokens, workspace, out.value)
+
+
+def ep_handle_init_static(cfg: Config, max_tokens: int, device="cuda") -> Handle:
+    """The handle whose workspace is the library's static device array (one
+    per GPU; allocates nothing).  Every call on a device returns the same C
+    handle, set up again: the previous one's layout is gone."""
+    dev = torch.device(device)
+    if dev.index is None:
+        dev = torch.device("cuda", torch.cuda.current_device())
+    out = ctypes.c_void_p()
+    c = cfg.c()
+    with torch.cuda.device(dev):
+        _check(lib().ep_handle_init_static(ctypes.byref(c), max_tokens, _stream(dev),
+                                           ctypes.byref(out)))
+    return Handle(cfg, max_tokens, None, out.value, device=dev)
 
 
 def ep_handle_free(h: Handle):
@@ -448,7 +473,7 @@ def ep_dispatch_topk(h: Handle, topk_weights: Optional[torch.Tensor], recv_topk_
     capacity of the handle's last batch) unless given."""
     cfg = h.cfg
     N = ep_handle_view(h)["num_tokens"]
-    dev = h.workspace.device
+    dev = h.device
     rows = ep_recv_capacity(cfg, N) if rows is None else rows
     if recv_topk_idx is None:
         recv_topk_idx = torch.empty((rows, cfg.num_topk), dtype=torch.int32, device=dev)
@@ -500,15 +525,26 @@ def ep_set_kernel_events(h: Handle, start_event=None, stop_event=None):
 
 
 def ep_handle_view(h: Handle):
-    """Device arrays of the handle as int32 tensor views of its workspace."""
+    """Device arrays of the handle as int32 tensor views of its workspace.
+    For the static handle (no workspace tensor) each array is given as
+    (device address, int32 element count) instead."""
     v = ep_handle_view_t()
     _check(lib().ep_handle_view(h.ptr, ctypes.byref(v)))
     ws = h.workspace
-    base = ws.data_ptr()
     cfg = h.cfg
 
+    class _Raw:
+        def __init__(self, p, n):
+            self.addr, self.numel = p, n
+
+        def view(self, *shape):
+            self.shape = shape
+            return self
+
     def arr(p, n):
-        off = p - base
+        if ws is None:
+            return _Raw(p, n)
+        off = p - ws.data_ptr()
         return ws[off:off + 4 * n].view(torch.int32)
 
     N = max(v.num_tokens, 0)
@@ -536,7 +572,7 @@ ep_handle_get_view = ep_handle_view
 def ep_check_error(h: Handle, raise_on_error=False):
     """Waits for the stream; returns (status, flags) and clears the flags."""
     flags = ctypes.c_uint32()
-    st = lib().ep_check_error(h.ptr, _stream(h.workspace.device), ctypes.byref(flags))
+    st = lib().ep_check_error(h.ptr, _stream(h.device), ctypes.byref(flags))
     if raise_on_error:
         _check(st)
     return st, flags.value

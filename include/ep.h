@@ -194,6 +194,30 @@ ep_status ep_recv_capacity(const ep_config* cfg, int64_t num_tokens, int64_t* ro
 ep_status ep_handle_init(const ep_config* cfg, int64_t max_tokens, void* d_workspace,
                          int64_t workspace_bytes, void* stream, ep_handle** out);
 
+/* Workspace limit of ep_handle_init_static (4 MiB: the largest workload
+ * here, 32768 tokens with top-6 over 64 experts, needs about 3.1 MiB). */
+#define EP_STATIC_SCRATCH_BYTES (4ll << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): a
+ * handle without a workspace argument.  Its workspace is a static device
+ * array of EP_STATIC_SCRATCH_BYTES inside the library, one per GPU, held
+ * until the process ends; the call allocates nothing, on the device or the
+ * host, and launches on `stream` the same clearing kernels as
+ * ep_handle_init (so it may be captured).
+ *   - There is one such handle per device: every call on a device returns
+ *     the same handle, set up again for cfg and max_tokens (the layout it
+ *     held is discarded, and views taken from it then show the new one).
+ *     Calls that use it from several streams or threads at once on one GPU
+ *     race; so do two overlapped batches, which need two handles.
+ *   - EP_ERR_WORKSPACE, with the sizes in the message, if
+ *     ep_workspace_size(cfg, max_tokens) exceeds EP_STATIC_SCRATCH_BYTES.
+ *   - ep_handle_free on it does nothing.
+ * Every other call takes it like a handle from ep_handle_init, with the
+ * same results. */
+ep_status ep_handle_init_static(const ep_config* cfg, int64_t max_tokens, void* stream,
+                                ep_handle** out);
+
 /* Frees the host-side handle ([P3] §3.1 EPHandle); never touches the
  * workspace.  NULL is a no-op. */
 void ep_handle_free(ep_handle* h);

@@ -48,6 +48,10 @@ def test_every_call_cites_a_passage():
         prev = m.end()
         if m.group(1) == "ep_handle_get_view":
             continue                      # the alias of ep_handle_view
+        if m.group(1) == "ep_handle_init_static":
+            # not an operation of the pages: its comment names its callers
+            assert "cannot allocate" in before
+            continue
         if not re.search(r"\[P[2-5]\]", before):
             missing.append(m.group(1))
     assert not missing, missing
@@ -142,3 +146,20 @@ def test_calls_on_null_handle_rejected():
                                 None) == ep.EP_ERR_INVALID_ARG
     assert L.ep_check_error(None, None, None) == ep.EP_ERR_INVALID_ARG
     L.ep_handle_free(None)
+
+
+def test_static_handle_rejects_workspace_beyond_its_limit():
+    """ep_handle_init_static refuses, before any HIP call, a handle whose
+    workspace would not fit the library's static array."""
+    cfg = ep.Config(**GOOD)
+    need = ep.ep_workspace_size(cfg, 1 << 18)
+    assert need > (4 << 20)
+    out = ctypes.c_void_p()
+    c = cfg.c()
+    st = ep.lib().ep_handle_init_static(ctypes.byref(c), 1 << 18, None, ctypes.byref(out))
+    assert st == ep.EP_ERR_WORKSPACE and not out.value
+    msg = ep.lib().ep_last_error_message().decode()
+    assert str(need) in msg and str(4 << 20) in msg
+    c = ep.Config(**{**GOOD, "num_topk": 0}).c()
+    assert ep.lib().ep_handle_init_static(ctypes.byref(c), 16, None, ctypes.byref(out)) == \
+        ep.EP_ERR_INVALID_ARG

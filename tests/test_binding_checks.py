@@ -18,6 +18,7 @@ CFG = ep.Config(hidden=256, num_topk=4, num_experts=32, num_ranks=8)
 def _handle(cfg=CFG, n=16):
     h = ep.Handle.__new__(ep.Handle)
     h.cfg, h.max_tokens, h.workspace = cfg, n, torch.empty(0, dtype=torch.uint8)
+    h._device = torch.device("cpu")
     h._ptr = ctypes.c_void_p()          # no C handle: .ptr raises RuntimeError
     return h
 
