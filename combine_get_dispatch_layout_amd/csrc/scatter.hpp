@@ -246,6 +246,19 @@ __device__ __forceinline__ uint32_t e2m1_code(float q)
     return c | ((__float_as_uint(q) >> 28) & 8u);
 }
 
+// Lane exchanges inside a quad of lanes (DPP quad_perm): the value of lane
+// (lane ^ 1), and the value of quad lane j.
+__device__ __forceinline__ uint32_t swap_pair(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);   // [1,0,3,2]
+}
+
+template <int J>
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, J * 0x55, 0xF, 0xF, false);   // [J,J,J,J]
+}
+
 // Loads the wave's chunk of row t: VPL 16-byte vectors per lane starting at
 // vector vbase (lane-contiguous), zero past the row end.
 template <int VPL>
@@ -312,7 +325,37 @@ __device__ __forceinline__ void scatter_chunk(const DispatchArgs& a, int vbase, 
             code[i] = w;
             sbyte[i] = (uint32_t)(sx + 127);
         }
+        // 16-byte code stores: the quad of lanes holding a group's 4 vectors
+        // holds its 16 code bytes; quad lane q gathers the quad's codes of
+        // slot q (four DPP broadcasts per slot) and stores them at once
+        const int q = lane & 3;
+        u32x4 pk = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            const u32x4 g = {quad_bcast<0>(code[i]), quad_bcast<1>(code[i]), quad_bcast<2>(code[i]),
+                             quad_bcast<3>(code[i])};
+            if (q == i) pk = g;
+        }
+        const int vq = vbase - q + kWave * q;      // first vector of the group lane q stores
+        const bool quad_store = q < VPL && vq < NV;
         const int G = NV / 4;
+        // Scale bytes: slot i's 16 groups (one per quad) are 16 consecutive
+        // bytes; lane i gathers them (16 shuffles from the quads' lane i) and
+        // stores them at once, when the rows' scale bytes sit on 16-byte
+        // boundaries (H a multiple of 512, an aligned scales array) and the
+        // wave's groups fill the 16; otherwise each quad stores its byte.
+        const int g0 = (vbase - lane) / 4;          // the wave's first group
+        const bool wide_scales = G % 16 == 0 && (reinterpret_cast<uintptr_t>(a.scales) & 15) == 0;
+        u32x4 sb = {0u, 0u, 0u, 0u};
+        if (wide_scales) {
+            const uint32_t mine = sbyte[q < VPL ? q : VPL - 1];
+#pragma unroll
+            for (int Q = 0; Q < 16; ++Q) {
+                const uint32_t b = (uint32_t)__shfl((int)mine, 4 * Q + q);
+                sb[Q / 4] |= b << (8 * (Q % 4));
+            }
+        }
+        const int gs = g0 + 16 * q;                 // first group of lane q's slot
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
             if (k >= K) break;
@@ -325,12 +368,14 @@ __device__ __forceinline__ void scatter_chunk(const DispatchArgs& a, int vbase, 
             const __amdgpu_buffer_rsrc_t r =
                 row_rsrc(reinterpret_cast<char*>(a.recv) + (int64_t)s * NV * 4, NV * 4);
             uint8_t* srow = reinterpret_cast<uint8_t*>(a.scales) + (int64_t)s * G;
+            if (quad_store) __builtin_amdgcn_raw_buffer_store_b128(pk, r, vq * 4, 0, kStoreAux);
+            if (wide_scales) {
+                if (lane < VPL && gs + 16 <= G) *reinterpret_cast<u32x4*>(srow + gs) = sb;
+            } else {
 #pragma unroll
-            for (int i = 0; i < VPL; ++i) {
-                const int v = vbase + kWave * i;
-                if (v < NV) {
-                    __builtin_amdgcn_raw_buffer_store_b32(code[i], r, v * 4, 0, kStoreAux);
-                    if ((lane & 3) == 0) srow[v / 4] = (uint8_t)sbyte[i];
+                for (int i = 0; i < VPL; ++i) {
+                    const int v = vbase + kWave * i;
+                    if (v < NV && q == 0) srow[v / 4] = (uint8_t)sbyte[i];
                 }
             }
             if constexpr (ROW_WAIT) __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -374,8 +419,53 @@ __device__ __forceinline__ void scatter_chunk(const DispatchArgs& a, int vbase, 
                 code[i] = u32x2{pack_int8x4(q[0], q[1], q[2], q[3]), pack_int8x4(q[4], q[5], q[6], q[7])};
             }
         }
+        // 16-byte code stores: adjacent lanes hold adjacent vectors, whose 16
+        // codes are contiguous.  For each pair of slots (i, i+1) the even lane
+        // stores the pair's codes of slot i and the odd lane those of slot
+        // i+1, after one DPP swap of the halves each needs; a lone last slot
+        // (VPL odd) is stored by the even lanes.
+        constexpr int NP = (VPL + 1) / 2;
+        const bool odd = lane & 1;
+        u32x4 pk[NP];
+        int pv[NP];   // first vector of the pair the lane stores (-1: none)
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const int i0 = 2 * p, i1 = 2 * p + 1;
+            if (i1 < VPL) {
+                const u32x2 send = odd ? code[i0] : code[i1];
+                const u32x2 recv = {swap_pair(send[0]), swap_pair(send[1])};
+                pk[p] = odd ? u32x4{recv[0], recv[1], code[i1][0], code[i1][1]}
+                            : u32x4{code[i0][0], code[i0][1], recv[0], recv[1]};
+                pv[p] = vbase - (lane & 1) + kWave * (odd ? i1 : i0);
+            } else {
+                const u32x2 recv = {swap_pair(code[i0][0]), swap_pair(code[i0][1])};
+                pk[p] = u32x4{code[i0][0], code[i0][1], recv[0], recv[1]};
+                pv[p] = odd ? -1 : vbase + kWave * i0;
+            }
+        }
         const int G = CHANNEL ? 1 : NV / 16;
         const bool byte_scales = a.scale_mode == 2;
+        // Group scales: slot i's 4 groups (16 lanes each) hold consecutive
+        // scales; lane i gathers them (4 shuffles) and stores 16 bytes (fp32)
+        // or 4 (E8M0) at once when the rows' scales sit on those boundaries
+        // (H a multiple of 512, an aligned scales array).
+        const int g0 = (vbase - lane) / 16;         // the wave's first group
+        const bool wide_scales =
+            !CHANNEL && G % 4 == 0 &&
+            (reinterpret_cast<uintptr_t>(a.scales) & (byte_scales ? 3 : 15)) == 0;
+        u32x4 sw = {0u, 0u, 0u, 0u};
+        if (wide_scales) {
+            const int li = lane & 15;
+            const float mine = scale[li < VPL ? li : VPL - 1];
+            const uint32_t bits = byte_scales ? (uint32_t)e8m0_of_pow2(mine) : __float_as_uint(mine);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t b = (uint32_t)__shfl((int)bits, 16 * j + li);
+                if (byte_scales) sw[0] |= b << (8 * j);
+                else sw[j] = b;
+            }
+        }
+        const int gs = g0 + 4 * (lane & 15);        // first group of lane i's slot
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
             if (k >= K) break;
@@ -388,13 +478,28 @@ __device__ __forceinline__ void scatter_chunk(const DispatchArgs& a, int vbase, 
             const __amdgpu_buffer_rsrc_t r =
                 row_rsrc(reinterpret_cast<char*>(a.recv) + (int64_t)s * NV * 8, NV * 8);
 #pragma unroll
-            for (int i = 0; i < VPL; ++i) {
-                const int v = vbase + kWave * i;
-                if (v < NV) {
-                    __builtin_amdgcn_raw_buffer_store_b64(code[i], r, v * 8, 0, kStoreAux);
+            for (int p = 0; p < NP; ++p) {
+                const int v = pv[p];
+                // a row of odd length (per-row scales) ends in half a pair
+                if (v >= 0 && v + 1 < NV)
+                    __builtin_amdgcn_raw_buffer_store_b128(pk[p], r, v * 8, 0, kStoreAux);
+                else if (v >= 0 && v < NV)
+                    __builtin_amdgcn_raw_buffer_store_b64(u32x2{pk[p][0], pk[p][1]}, r, v * 8, 0,
+                                                         kStoreAux);
+            }
+            if (wide_scales) {
+                if (lane < VPL && gs < G) {
+                    const int64_t at = (int64_t)s * G + gs;
+                    if (byte_scales) reinterpret_cast<uint32_t*>(a.scales)[at / 4] = sw[0];
+                    else *reinterpret_cast<u32x4*>(reinterpret_cast<float*>(a.scales) + at) = sw;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < VPL; ++i) {
+                    const int v = vbase + kWave * i;
                     const bool writer = CHANNEL ? v == 0 : (lane & 15) == 0;
-                    const int64_t at = (int64_t)s * G + (CHANNEL ? 0 : v / 16);
-                    if (writer) {
+                    if (v < NV && writer) {
+                        const int64_t at = (int64_t)s * G + (CHANNEL ? 0 : v / 16);
                         if (byte_scales)
                             reinterpret_cast<uint8_t*>(a.scales)[at] = e8m0_of_pow2(scale[i]);
                         else
