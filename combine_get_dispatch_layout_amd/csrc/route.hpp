@@ -577,9 +577,51 @@ __device__ __forceinline__ void count_body(const LayoutArgs& a, int b, unsigned 
 // which are re-zeroed for the next call.  The additions were made by an
 // earlier launch, so plain loads see them; all kAccCopies copies are read
 // at once (the unused ones hold zero).
+//   RankTotals: when every rank and node has a thread of its own
+//   (R, nodes <= NT) the loads are issued by rank_totals_load at the start
+//   of a block, beside its other loads, so that rank_totals_store at its
+//   end waits for nothing; otherwise rank_totals_store reads them itself.
+struct RankTotals {
+    int r[kAccCopies], n[kAccCopies];
+    bool early;
+};
+
 template <int NT>
-__device__ __forceinline__ void flush_rank_totals(const LayoutArgs& a)
+__device__ __forceinline__ void rank_totals_load(const LayoutArgs& a, RankTotals& rt)
 {
+    const int tid = threadIdx.x;
+    rt.early = a.R <= NT && a.nodes <= NT;
+    if (!rt.early) return;
+#pragma unroll
+    for (int c = 0; c < kAccCopies; ++c) {
+        rt.r[c] = tid < a.R ? a.rank_acc[c * a.acc_stride + tid] : 0;
+        rt.n[c] = tid < a.nodes ? a.node_acc[c * a.acc_stride + tid] : 0;
+    }
+}
+
+template <int NT>
+__device__ __forceinline__ void rank_totals_store(const LayoutArgs& a, const RankTotals& rt)
+{
+    if (rt.early) {
+        const int tid = threadIdx.x;
+        int rs = 0, ns = 0;
+#pragma unroll
+        for (int c = 0; c < kAccCopies; ++c) {
+            rs += rt.r[c];
+            ns += rt.n[c];
+        }
+        if (tid < a.R) {
+#pragma unroll
+            for (int c = 0; c < kAccCopies; ++c) a.rank_acc[c * a.acc_stride + tid] = 0;
+            if (a.out_per_rank) a.out_per_rank[tid] = rs;
+        }
+        if (tid < a.nodes) {
+#pragma unroll
+            for (int c = 0; c < kAccCopies; ++c) a.node_acc[c * a.acc_stride + tid] = 0;
+            if (a.out_per_node) a.out_per_node[tid] = ns;
+        }
+        return;
+    }
     for (int r = threadIdx.x; r < a.R; r += NT) {
         int v[kAccCopies];
 #pragma unroll
@@ -604,6 +646,14 @@ __device__ __forceinline__ void flush_rank_totals(const LayoutArgs& a)
         }
         if (a.out_per_node) a.out_per_node[n] = sum;
     }
+}
+
+template <int NT>
+__device__ __forceinline__ void flush_rank_totals(const LayoutArgs& a)
+{
+    RankTotals rt;
+    rt.early = false;
+    rank_totals_store<NT>(a, rt);
 }
 
 // LDS of finish_lean with NT threads: totals [E], bases [NT/256][E], prefix
@@ -642,6 +692,10 @@ __device__ __forceinline__ void finish_lean(const LayoutArgs& a, int C, int b, u
     int ids[KMAX], lr[KMAX];
     load_row<KMAX>(a.topk_clone + t * K, K, a.row_vec, tv, -1, ids);
     load_row<KMAX>(a.slot_idx + t * K, K, a.row_vec, tv, 0, lr);
+    // block 0's rank totals: loaded now, beside the rows and the histogram
+    RankTotals rt;
+    rt.early = false;
+    if (b == 0 && !a.no_rank_counts) rank_totals_load<NT>(a, rt);
 
     const int EPT = E < NT ? E : NT;
     int P = NT / EPT;
@@ -706,7 +760,7 @@ __device__ __forceinline__ void finish_lean(const LayoutArgs& a, int C, int b, u
     }
     if (b == 0) {
         write_expert_arrays<NT>(a, tot, psum);
-        if (!a.no_rank_counts) flush_rank_totals<NT>(a);
+        if (!a.no_rank_counts) rank_totals_store<NT>(a, rt);
     }
 }
 
