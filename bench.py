@@ -289,6 +289,59 @@ def cpu_baseline(w, idx, wts, budget_s=10.0):
                        f"{time.perf_counter() - t_start:.1f} s")
 
 
+def ceilings(gib=1.0, reps=10):
+    """Achievable HBM bandwidth of plain streaming kernels (libep_probe.so):
+    for read, write and copy, the best of a sweep over workgroup counts,
+    workgroup sizes, 16-byte vectors per lane and the non-temporal hint,
+    each timed over `reps` launches on `gib` GiB buffers (torch events on the
+    launch stream).  Prints one JSON line."""
+    import ctypes
+    import torch
+    L = ctypes.CDLL(os.path.join(ROOT, "combine_get_dispatch_layout_amd", "libep_probe.so"))
+    L.ep_probe_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                  ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    nbytes = int(gib * (1 << 30))
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    names = {0: "read", 1: "write", 2: "copy"}
+    results = []
+    for mode in (0, 1, 2):
+        moved = nbytes * (2 if mode == 2 else 1)
+        for threads in (256, 512, 1024):
+            for vpl in (1, 2, 4, 8):
+                for nt in (0, 1):
+                    for blocks in (256, 512, 1024, 2048, 4096, 8192):
+                        args = (mode, ctypes.c_void_p(src.data_ptr()),
+                                ctypes.c_void_p(dst.data_ptr()), nbytes, blocks, threads, vpl,
+                                nt, sp)
+                        if L.ep_probe_stream(*args) != 0:
+                            raise RuntimeError("ep_probe_stream failed")
+                        e0 = torch.cuda.Event(enable_timing=True)
+                        e1 = torch.cuda.Event(enable_timing=True)
+                        e0.record(stream)
+                        for _ in range(reps):
+                            L.ep_probe_stream(*args)
+                        e1.record(stream)
+                        e1.synchronize()
+                        gbs = moved * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+                        results.append(dict(mode=names[mode], threads=threads, vec_per_lane=vpl,
+                                            nontemporal=nt, blocks=blocks, GBps=gbs))
+        print(f"[ceilings] {names[mode]} done", file=sys.stderr, flush=True)
+    best = {}
+    for r in results:
+        if r["GBps"] > best.get(r["mode"], {}).get("GBps", 0):
+            best[r["mode"]] = r
+    line = dict(ceilings={k: dict(v, frac_of_peak=v["GBps"] / HBM_PEAK_GBS) for k, v in best.items()},
+                peak_GBps=HBM_PEAK_GBS, buffer_GiB=gib, reps=reps, configs=len(results),
+                note="bytes moved / time; copy counts its reads and its writes")
+    print(json.dumps(line), flush=True)
+    return line, results
+
+
 class HipEvents:
     """Raw hipEvent_t handles from the HIP runtime (so the library can attach
     them to its kernel launches)."""
@@ -363,6 +416,9 @@ def main():
                     help="capture one rotation of steps (one step per buffer set) in a HIP "
                          "graph and time its replays (steps rounded up to whole rotations) "
                          "(merged, serial, fused and cached pipelines)")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="measure the achievable read / write / copy bandwidth of plain "
+                         "streaming kernels (libep_probe.so) and exit")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc runs into profiles/ and exit")
     args = ap.parse_args()
@@ -370,6 +426,13 @@ def main():
         args.pipeline = "merged"
     if args.traffic_from:
         traffic_summary(args.traffic_from[0], args.traffic_from[1], args)
+        return
+    if args.ceilings:
+        _, results = ceilings()
+        out = os.environ.get("EP_CEILINGS_OUT")
+        if out:
+            with open(out, "w") as f:
+                json.dump(results, f)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): this path runs on "

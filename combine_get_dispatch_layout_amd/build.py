@@ -1,7 +1,8 @@
-"""Builds libep_amd.so (HIP kernels + C-ABI host runtime) for gfx950 with hipcc.
+"""Builds libep_amd.so (HIP kernels + C-ABI host runtime) for gfx950 with hipcc,
+and libep_probe.so (the streaming bandwidth probes of include/ep_probe.h).
 
-The library is built in-tree, next to this file.  Each source is compiled to
-an object in ``_build/`` and the objects are linked into one shared library.
+The libraries are built in-tree, next to this file.  Each source is compiled
+to an object in ``_build/`` and the objects are linked into shared libraries.
 """
 import os
 import subprocess
@@ -14,10 +15,12 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libep_amd.so")
+PROBE_LIB = os.path.join(PKG, "libep_probe.so")
 ARCH = "gfx950"
 
 SOURCES = ["layout.hip", "dispatch.hip", "fused.hip", "sources.hip", "nonexpand.hip",
            "combine.hip", "overlap.hip", "api.cpp"]
+PROBE_SOURCES = ["probe.hip"]
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 instructions.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -42,19 +45,26 @@ def _compile(src, extra):
     return obj
 
 
-def build(extra_flags=(), out=LIB, verbose=False) -> str:
-    """Compiles every source and links ``out``.  Always rebuilds."""
-    os.makedirs(OBJDIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, list(extra_flags)), SOURCES))
+def _link(objs, out):
     tmp = out + ".tmp%d" % os.getpid()
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, out)
+
+
+def build(extra_flags=(), out=LIB, verbose=False) -> str:
+    """Compiles every source and links ``out`` and the probe library.
+    Always rebuilds."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, list(extra_flags)), srcs))
+    _link(objs[:len(SOURCES)], out)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
-        print(out)
+        print(out, PROBE_LIB)
     return out
 
 

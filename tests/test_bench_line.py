@@ -69,9 +69,10 @@ def test_variant_flags_key_their_own_traffic():
     assert tag == "qwen3_30b_a3b_prefill_q3_qg32" and flags == ["--quant", "mxfp4"]
     _, (w, tag, _) = _variant(num_sources=16, combine_quant="fp8")
     assert tag == "qwen3_30b_a3b_prefill_src16_cq1_cg128" and w.combine_group == 128
-    # the plain workload's record exists; no variant borrows it
-    assert bench.traffic_from_profiles("dispatch", "qwen3_30b_a3b_prefill") is not None
-    assert bench.traffic_from_profiles("dispatch", "qwen3_30b_a3b_prefill_q3_qg32") is None
+    # the plain workload's record exists; a variant without a record of its
+    # own does not borrow it
+    assert bench.traffic_from_profiles("combine", "qwen3_30b_a3b_prefill") is not None
+    assert bench.traffic_from_profiles("combine", "qwen3_30b_a3b_prefill_src2") is None
     # flags that restate the workload's own settings keep its tag
     _, (_, tag, _) = _variant(workload="ll_decode_fp8", quant="fp8")
     assert tag == "ll_decode_fp8"
