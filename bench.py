@@ -218,7 +218,93 @@ def traffic_summary(fetch_csv, write_csv, args):
             write_scale=f_write, source_sha256_16=kernel_source_hash(kern), command=command)
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
+    write_traffic_md(out, tag)
     print(json.dumps(out, indent=1))
+
+
+def write_traffic_md(rec, tag):
+    """profiles/traffic_<tag>.md: the JSON record as a table, with the
+    commands that made each entry."""
+    rows, cmds = [], []
+    for kern, d in rec["kernels"].items():
+        rows.append(f"| {kern} | {d['fetch_kib']:.0f} | {d['write_kib']:.0f} | {d['fetch_scale']:.4f} | "
+                    f"{d['write_scale']:.4f} | {d['hbm_bytes_per_launch']:.4e} | "
+                    f"{d['algorithmic_bytes_per_launch']:.4e} | {d['traffic_over_algorithmic']:.4f} |")
+        for c in d["command"]:
+            if c not in cmds:
+                cmds.append(c)
+    text = [f"# HBM traffic per launch: {tag}", "",
+            "Each kernel's counters come from two rocprofv3 passes (one counter each) over `bench.py`, "
+            "summarised by `bench.py --traffic-from`; FETCH_SIZE and WRITE_SIZE are scaled by what they "
+            "read for the benchmark's own 1 GiB device copy (`__amd_rocclr_copyBuffer`, reads 1 GiB, "
+            "writes 1 GiB).", "",
+            "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | fetch scale | write scale | HBM bytes | "
+            "algorithmic bytes | ratio |", "|---|---|---|---|---|---|---|---|", *rows, "",
+            "Commands (repo root, on one MI355X):", "", "```", *cmds, "```", "",
+            "Medians over the run's launches (warm-up and timed steps).  A ratio near 1 means the kernel "
+            "moves its algorithmic bytes and nothing more (no re-reads; padding rows are never written).  "
+            "`bench.py` reports `roofline.traffic` from the JSON file only while the kernel's sources "
+            "still hash to the recorded value.", ""]
+    with open(os.path.join(ROOT, "profiles", f"traffic_{tag}.md"), "w") as f:
+        f.write("\n".join(text))
+
+
+def trace_summary(trace_dir, args):
+    """profiles/kernels_<tag>[_<pipeline>][_graph].md from a rocprofv3
+    --kernel-trace --stats run of `bench.py --workload <workload> <variant
+    flags> --pipeline <pipeline> [--graph]` whose output went to
+    <trace_dir>/trace_*.csv: per library kernel, calls and average / min /
+    max duration, and its launch shape, LDS and registers."""
+    import csv
+    w, tag, flags = variant_of(args)
+    name = tag + ("" if args.pipeline == "merged" else f"_{args.pipeline}") + \
+        ("_graph" if args.graph else "")
+    stats = list(csv.DictReader(open(os.path.join(trace_dir, "trace_kernel_stats.csv"))))
+    shapes = {}
+    for r in csv.DictReader(open(os.path.join(trace_dir, "trace_kernel_trace.csv"))):
+        wg = int(r["Workgroup_Size_X"]) * int(r["Workgroup_Size_Y"]) * int(r["Workgroup_Size_Z"])
+        grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+        sh = shapes.setdefault(r["Kernel_Name"], dict(shape=set(), lds=set(), vgpr=set()))
+        sh["shape"].add(f"{grid // max(wg, 1)}x{wg}")
+        sh["lds"].add(r.get("LDS_Block_Size", r.get("Lds_Size", "?")))
+        sh["vgpr"].add(r.get("Arch_VGPR_Count", r.get("VGPR_Count", "?")))
+    mine = ("k_", "__amd_rocclr_copyBuffer")
+    rows = []
+    for r in stats:
+        kn = r["Name"]
+        if not kn.startswith(mine):
+            continue
+        sh = shapes.get(kn, dict(shape=set(), lds=set(), vgpr=set()))
+        rows.append(f"| `{kn}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                    f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                    f"{'; '.join(sorted(sh['shape']))} | {'; '.join(sorted(sh['lds']))} | "
+                    f"{'; '.join(sorted(sh['vgpr']))} |")
+    vflags = "".join(" " + f for f in flags)
+    cmd = (f"rocprofv3 --kernel-trace --stats -f csv -d <dir> -o trace -- python3 bench.py "
+           f"--workload {args.workload}{vflags} --pipeline {args.pipeline}"
+           f"{' --graph' if args.graph else ''} --steps {args.steps} --warmup {args.warmup} "
+           "--no-cpu-baseline")
+    text = [f"# Kernel trace: {name}", "", "Command (repo root, on one MI355X):", "", "```", cmd,
+            f"python3 bench.py --trace-from <dir> --workload {args.workload}{vflags} "
+            f"--pipeline {args.pipeline}{' --graph' if args.graph else ''} --steps {args.steps} "
+            f"--warmup {args.warmup}", "```", "",
+            "`<dir>/trace_kernel_stats.csv` and `trace_kernel_trace.csv`; the library's kernels, plus "
+            "the 1 GiB device copy the benchmark times as its achievable-bandwidth reference:", "",
+            "| kernel | calls | avg us | min us | max us | workgroups x threads | LDS B | VGPRs |",
+            "|---|---|---|---|---|---|---|---|", *rows, "",
+            "Workload: " + json.dumps(dict(workload=w.name, num_tokens=w.num_tokens, hidden=w.hidden,
+                                           num_experts=w.num_experts, num_ranks=w.num_ranks,
+                                           num_topk=w.num_topk, expert_alignment=w.expert_alignment,
+                                           rounds=w.rounds, num_sources=w.num_sources, quant=w.quant,
+                                           quant_group=w.quant_group, scale_mode=w.scale_mode,
+                                           combine_quant=w.combine_quant,
+                                           combine_group=w.combine_group)), "",
+            "Kernel averages include the warm-up steps and the eager timing pass.  Other kernels of the "
+            "run (torch's input generation) are left out.", ""]
+    out = os.path.join(ROOT, "profiles", f"kernels_{name}.md")
+    with open(out, "w") as f:
+        f.write("\n".join(text))
+    print(out)
 
 
 def cpu_baseline(w, idx, wts, budget_s=10.0):
@@ -289,24 +375,39 @@ def cpu_baseline(w, idx, wts, budget_s=10.0):
                        f"{time.perf_counter() - t_start:.1f} s")
 
 
-def ceilings(gib=1.0, reps=10):
+def ceilings(w=None, gib=1.0, reps=10):
     """Achievable HBM bandwidth of plain streaming kernels (libep_probe.so):
     for read, write and copy, the best of a sweep over workgroup counts,
     workgroup sizes, 16-byte vectors per lane and the non-temporal hint,
     each timed over `reps` launches on `gib` GiB buffers (torch events on the
-    launch stream).  Prints one JSON line."""
+    launch stream).  With a workload `w`, also the ceilings of its own two
+    row patterns without their arithmetic: the combine's gather and the
+    dispatch's scatter over the workload's slot table (from the library's
+    layout), bf16 rows, four rotating buffer sets.  Prints one JSON line."""
     import ctypes
     import torch
     L = ctypes.CDLL(os.path.join(ROOT, "combine_get_dispatch_layout_amd", "libep_probe.so"))
-    L.ep_probe_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
-                                  ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                  ctypes.c_void_p]
+    P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.ep_probe_stream.argtypes = [I32, P, P, I64, I32, I32, I32, I32, P]
+    L.ep_probe_rows.argtypes = [I32, P, P, P, I64, I32, I64, I32, I32, P]
     dev = torch.device("cuda:0")
     nbytes = int(gib * (1 << 30))
     src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def timed(launch, nrep):
+        launch(0)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for r in range(nrep):
+            launch(r)
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / nrep
+
     names = {0: "read", 1: "write", 2: "copy"}
     results = []
     for mode in (0, 1, 2):
@@ -318,19 +419,15 @@ def ceilings(gib=1.0, reps=10):
                         args = (mode, ctypes.c_void_p(src.data_ptr()),
                                 ctypes.c_void_p(dst.data_ptr()), nbytes, blocks, threads, vpl,
                                 nt, sp)
-                        if L.ep_probe_stream(*args) != 0:
-                            raise RuntimeError("ep_probe_stream failed")
-                        e0 = torch.cuda.Event(enable_timing=True)
-                        e1 = torch.cuda.Event(enable_timing=True)
-                        e0.record(stream)
-                        for _ in range(reps):
-                            L.ep_probe_stream(*args)
-                        e1.record(stream)
-                        e1.synchronize()
-                        gbs = moved * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+                        def go(_r, args=args):
+                            if L.ep_probe_stream(*args) != 0:
+                                raise RuntimeError("ep_probe_stream failed")
+                        t = timed(go, reps)
                         results.append(dict(mode=names[mode], threads=threads, vec_per_lane=vpl,
-                                            nontemporal=nt, blocks=blocks, GBps=gbs))
+                                            nontemporal=nt, blocks=blocks, GBps=moved / t / 1e9))
         print(f"[ceilings] {names[mode]} done", file=sys.stderr, flush=True)
+    del src, dst
     best = {}
     for r in results:
         if r["GBps"] > best.get(r["mode"], {}).get("GBps", 0):
@@ -338,6 +435,43 @@ def ceilings(gib=1.0, reps=10):
     line = dict(ceilings={k: dict(v, frac_of_peak=v["GBps"] / HBM_PEAK_GBS) for k, v in best.items()},
                 peak_GBps=HBM_PEAK_GBS, buffer_GiB=gib, reps=reps, configs=len(results),
                 note="bytes moved / time; copy counts its reads and its writes")
+    if w is not None:
+        import workloads as W
+        from combine_get_dispatch_layout_amd import ep
+        idx, _ = W.routing(w)
+        N, H, K = w.num_tokens, w.hidden, w.num_topk
+        cfg = ep.Config(hidden=H, num_topk=K, num_experts=w.num_experts, num_ranks=w.num_ranks,
+                        expert_alignment=w.expert_alignment, expert_capacity=w.expert_capacity,
+                        non_expand=w.non_expand)
+        h = ep.ep_handle_init(cfg, N, device=dev)
+        S = ep.ep_get_layout(h, torch.from_numpy(idx).to(dev), do_cpu_sync=True)["num_recv_slots"]
+        slot = ep.ep_handle_view(h)["slot_idx"]
+        V = int((slot >= 0).sum().item())
+        rows_b = 2 * H
+        sets = [(torch.empty((max(S, 1), H), dtype=torch.bfloat16, device=dev).fill_(1),
+                 torch.empty((N, H), dtype=torch.bfloat16, device=dev).fill_(1)) for _ in range(4)]
+        pat = []
+        for mode, nm in ((3, "gather"), (4, "scatter")):
+            for threads in (256, 512, 1024):
+                for vpl in (1, 2, 4):
+                    def go(r, mode=mode, threads=threads, vpl=vpl):
+                        big, small = sets[r % 4]
+                        s_, d_ = (big, small) if mode == 3 else (small, big)
+                        if L.ep_probe_rows(mode, ctypes.c_void_p(s_.data_ptr()),
+                                           ctypes.c_void_p(d_.data_ptr()),
+                                           ctypes.c_void_p(slot.data_ptr()), N, K, rows_b, threads,
+                                           vpl, sp) != 0:
+                            raise RuntimeError("ep_probe_rows failed")
+                    t = timed(go, 4 * reps)
+                    moved = (V + N) * rows_b
+                    pat.append(dict(pattern=nm, threads=threads, vec_per_lane=vpl, us=t * 1e6,
+                                    GBps=moved / t / 1e9))
+        for nm in ("gather", "scatter"):
+            b = min((x for x in pat if x["pattern"] == nm), key=lambda x: x["us"])
+            line.setdefault("patterns", {})[nm] = dict(b, frac_of_peak=b["GBps"] / HBM_PEAK_GBS)
+        line["patterns_workload"] = dict(workload=w.name, tokens=N, hidden=H, topk=K, rows=V,
+                                         bytes_moved=(V + N) * rows_b)
+        results += pat
     print(json.dumps(line), flush=True)
     return line, results
 
@@ -419,6 +553,9 @@ def main():
     ap.add_argument("--ceilings", action="store_true",
                     help="measure the achievable read / write / copy bandwidth of plain "
                          "streaming kernels (libep_probe.so) and exit")
+    ap.add_argument("--trace-from", metavar="DIR",
+                    help="summarise a rocprofv3 --kernel-trace --stats run (DIR/trace_*.csv) "
+                         "into profiles/ and exit")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc runs into profiles/ and exit")
     args = ap.parse_args()
@@ -427,8 +564,11 @@ def main():
     if args.traffic_from:
         traffic_summary(args.traffic_from[0], args.traffic_from[1], args)
         return
+    if args.trace_from:
+        trace_summary(args.trace_from, args)
+        return
     if args.ceilings:
-        _, results = ceilings()
+        _, results = ceilings(variant_of(args)[0])
         out = os.environ.get("EP_CEILINGS_OUT")
         if out:
             with open(out, "w") as f:

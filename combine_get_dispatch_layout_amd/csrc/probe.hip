@@ -80,7 +80,103 @@ hipError_t launch_m(int vpl, bool nt, const u32x4* s, u32x4* d, int64_t nvec, in
               : launch_v<MODE, false>(vpl, s, d, nvec, blocks, threads, stream);
 }
 
+// One wave per (token, chunk): KMAX unrolled entries, those past K masked.
+template <int MODE, int VPL, int KMAX>
+__global__ void k_rows(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                       const int32_t* __restrict__ slot, int64_t N, int K, int NV, int NC)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t item = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int64_t t = item / NC;
+    const int c = (int)(item % NC);
+    if (t >= N) return;
+    const int vb = c * 64 * VPL + lane;
+    int s[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k)
+        s[k] = k < K ? __builtin_amdgcn_readfirstlane(slot[t * K + k]) : -1;
+    if constexpr (MODE == EP_PROBE_GATHER) {
+        u32x4 v[KMAX][VPL];
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                const int vi = vb + 64 * i;
+                v[k][i] = (s[k] >= 0 && vi < NV) ? ld<true>(src + (int64_t)s[k] * NV + vi)
+                                                 : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            u32x4 a = v[0][i];
+#pragma unroll
+            for (int k = 1; k < KMAX; ++k) a ^= v[k][i];
+            const int vi = vb + 64 * i;
+            if (vi < NV) st<true>(a, dst + t * NV + vi);
+        }
+    } else {
+        u32x4 v[VPL];
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            const int vi = vb + 64 * i;
+            v[i] = vi < NV ? ld<true>(src + t * NV + vi) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            if (s[k] < 0) continue;
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                const int vi = vb + 64 * i;
+                if (vi < NV) st<true>(v[i], dst + (int64_t)s[k] * NV + vi);
+            }
+        }
+    }
+}
+
+template <int MODE, int VPL>
+hipError_t launch_rows(const u32x4* s, u32x4* d, const int32_t* slot, int64_t N, int K, int NV,
+                       int threads, hipStream_t stream)
+{
+    const int NC = (NV + 64 * VPL - 1) / (64 * VPL);
+    const int64_t waves = N * NC;
+    const int64_t blocks = (waves * 64 + threads - 1) / threads;
+    if (K <= 8)
+        hipLaunchKernelGGL((k_rows<MODE, VPL, 8>), dim3((unsigned)blocks), dim3(threads), 0, stream,
+                           s, d, slot, N, K, NV, NC);
+    else
+        hipLaunchKernelGGL((k_rows<MODE, VPL, 16>), dim3((unsigned)blocks), dim3(threads), 0,
+                           stream, s, d, slot, N, K, NV, NC);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+extern "C" int ep_probe_rows(int mode, const void* d_src, void* d_dst, const int32_t* d_slot,
+                             int64_t num_tokens, int topk, int64_t row_bytes, int threads,
+                             int vec_per_lane, void* stream)
+{
+    const int vpl = vec_per_lane;
+    if ((mode != EP_PROBE_GATHER && mode != EP_PROBE_SCATTER) || num_tokens < 0 || topk < 1 ||
+        topk > 16 || row_bytes <= 0 || row_bytes % 16 != 0 || row_bytes / 16 > (1 << 30) ||
+        threads < 64 || threads > 1024 || threads % 64 != 0 || !(vpl == 1 || vpl == 2 || vpl == 4) ||
+        !d_src || !d_dst || !d_slot)
+        return -1;
+    if (num_tokens == 0) return 0;
+    const int NV = (int)(row_bytes / 16);
+    const u32x4* s = static_cast<const u32x4*>(d_src);
+    u32x4* d = static_cast<u32x4*>(d_dst);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (mode == EP_PROBE_GATHER) {
+        e = vpl == 1 ? launch_rows<EP_PROBE_GATHER, 1>(s, d, d_slot, num_tokens, topk, NV, threads, hs)
+          : vpl == 2 ? launch_rows<EP_PROBE_GATHER, 2>(s, d, d_slot, num_tokens, topk, NV, threads, hs)
+                     : launch_rows<EP_PROBE_GATHER, 4>(s, d, d_slot, num_tokens, topk, NV, threads, hs);
+    } else {
+        e = vpl == 1 ? launch_rows<EP_PROBE_SCATTER, 1>(s, d, d_slot, num_tokens, topk, NV, threads, hs)
+          : vpl == 2 ? launch_rows<EP_PROBE_SCATTER, 2>(s, d, d_slot, num_tokens, topk, NV, threads, hs)
+                     : launch_rows<EP_PROBE_SCATTER, 4>(s, d, d_slot, num_tokens, topk, NV, threads, hs);
+    }
+    return e == hipSuccess ? 0 : (int)e;
+}
 
 extern "C" int ep_probe_stream(int mode, const void* d_src, void* d_dst, int64_t bytes, int blocks,
                                int threads, int vec_per_lane, int nontemporal, void* stream)

@@ -35,6 +35,24 @@ enum { EP_PROBE_READ = 0, EP_PROBE_WRITE = 1, EP_PROBE_COPY = 2 };
 int ep_probe_stream(int mode, const void* d_src, void* d_dst, int64_t bytes, int blocks,
                     int threads, int vec_per_lane, int nontemporal, void* stream);
 
+/* The shuffle's two row access patterns without their arithmetic, one wave
+ * per (token, chunk of 64 * vec_per_lane 16-byte vectors), as the kernels
+ * do them, for the patterns' own ceilings:
+ *   EP_PROBE_GATHER (the combine's): for each token t < num_tokens, row t of
+ *     d_dst = XOR over k < topk with d_slot[t*topk + k] >= 0 of row
+ *     d_slot[t*topk + k] of d_src; all of a chunk's loads are issued first;
+ *   EP_PROBE_SCATTER (the dispatch's): for each token t and k with a slot,
+ *     row d_slot[t*topk + k] of d_dst = row t of d_src.
+ * Rows are row_bytes long (a multiple of 16); d_slot int32 [num_tokens,
+ * topk] with entries < the rows of the indexed buffer (the caller's
+ * guarantee); topk 1..16; threads 64..1024, a multiple of 64;
+ * vec_per_lane 1, 2 or 4; non-temporal loads and stores.  Returns 0, -1 for
+ * invalid arguments, or the HIP error code of the launch. */
+enum { EP_PROBE_GATHER = 3, EP_PROBE_SCATTER = 4 };
+int ep_probe_rows(int mode, const void* d_src, void* d_dst, const int32_t* d_slot,
+                  int64_t num_tokens, int topk, int64_t row_bytes, int threads, int vec_per_lane,
+                  void* stream);
+
 #ifdef __cplusplus
 }
 #endif

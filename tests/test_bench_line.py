@@ -59,9 +59,10 @@ def _variant(**kw):
     return bench, bench.variant_of(argparse.Namespace(**a))
 
 
-def test_variant_flags_key_their_own_traffic():
+def test_variant_flags_key_their_own_traffic(tmp_path, monkeypatch):
     """A run with variant flags is priced and looked up under its own tag:
-    it never reports the plain workload's counted bytes."""
+    it never reports the plain workload's counted bytes, and a record whose
+    kernel sources changed is not used."""
     bench, (w, tag, flags) = _variant()
     assert tag == "qwen3_30b_a3b_prefill" and flags == [] and w.quant == 0
     _, (w, tag, flags) = _variant(quant="mxfp4")
@@ -69,10 +70,16 @@ def test_variant_flags_key_their_own_traffic():
     assert tag == "qwen3_30b_a3b_prefill_q3_qg32" and flags == ["--quant", "mxfp4"]
     _, (w, tag, _) = _variant(num_sources=16, combine_quant="fp8")
     assert tag == "qwen3_30b_a3b_prefill_src16_cq1_cg128" and w.combine_group == 128
-    # the plain workload's record exists; a variant without a record of its
-    # own does not borrow it
-    assert bench.traffic_from_profiles("combine", "qwen3_30b_a3b_prefill") is not None
-    assert bench.traffic_from_profiles("combine", "qwen3_30b_a3b_prefill_src2") is None
     # flags that restate the workload's own settings keep its tag
     _, (_, tag, _) = _variant(workload="ll_decode_fp8", quant="fp8")
     assert tag == "ll_decode_fp8"
+    # lookups: a record for the plain workload only, in a scratch folder
+    monkeypatch.setattr(bench, "traffic_path", lambda t: str(tmp_path / f"traffic_{t}.json"))
+    rec = dict(workload="qwen3_30b_a3b_prefill", kernels=dict(
+        combine=dict(hbm_bytes_per_launch=1.5e8,
+                     source_sha256_16=bench.kernel_source_hash("combine")),
+        dispatch=dict(hbm_bytes_per_launch=1.5e8, source_sha256_16="0000000000000000")))
+    (tmp_path / "traffic_qwen3_30b_a3b_prefill.json").write_text(json.dumps(rec))
+    assert bench.traffic_from_profiles("combine", "qwen3_30b_a3b_prefill") == 1.5e8
+    assert bench.traffic_from_profiles("combine", "qwen3_30b_a3b_prefill_q3_qg32") is None
+    assert bench.traffic_from_profiles("dispatch", "qwen3_30b_a3b_prefill") is None   # stale
