@@ -48,24 +48,28 @@ __global__ __launch_bounds__(BLOCK) void k_combine(CombineArgs a, int NV, int NC
     combine_wave<KMAX, VPL, YQ, YCH, BLOCK / kWave>(a, NV, NC, blockIdx.x);
 }
 
+// Small launches (decode batches) take one vector per lane: twice the waves,
+// each with half the loads in flight (measured on MI355X, decode 128 x 7168:
+// 4.88 -> 4.60 us); large ones EP_COMBINE_VPL.
+template <int KMAX, int VPL, int YQ, bool YCH, int B>
+hipError_t launch_b(const CombineArgs& a, int NV, hipStream_t s, LaunchEvents ev)
+{
+    const int NC = (NV + kWave * VPL - 1) / (kWave * VPL);
+    const int64_t items = (a.t_end - a.t_begin) * NC;
+    const int blocks = (int)((items + B / kWave - 1) / (B / kWave));
+    launch_k(k_combine<KMAX, VPL, YQ, YCH, B>, dim3(blocks), dim3(B), 0, s, ev.start, ev.stop, a, NV,
+             NC);
+    return hipGetLastError();
+}
+
 template <int KMAX, int VPL, int YQ, bool YCH>
 hipError_t launch_kv(const CombineArgs& a, int NV, hipStream_t s, LaunchEvents ev)
 {
     const int NC = (NV + kWave * VPL - 1) / (kWave * VPL);
     const int64_t items = (a.t_end - a.t_begin) * NC;
     if (items <= 0) return hipSuccess;
-    if (items >= EP_COMBINE_BIG_ITEMS) {
-        constexpr int B = EP_COMBINE_BLOCK;
-        const int blocks = (int)((items + B / kWave - 1) / (B / kWave));
-        launch_k(k_combine<KMAX, VPL, YQ, YCH, B>, dim3(blocks), dim3(B), 0, s, ev.start, ev.stop,
-                 a, NV, NC);
-        return hipGetLastError();
-    }
-    constexpr int B = EP_COMBINE_SMALL_BLOCK;
-    const int blocks = (int)((items + B / kWave - 1) / (B / kWave));
-    launch_k(k_combine<KMAX, VPL, YQ, YCH, B>, dim3(blocks), dim3(B), 0, s, ev.start, ev.stop, a,
-             NV, NC);
-    return hipGetLastError();
+    if (items >= EP_COMBINE_BIG_ITEMS) return launch_b<KMAX, VPL, YQ, YCH, EP_COMBINE_BLOCK>(a, NV, s, ev);
+    return launch_b<KMAX, 1, YQ, YCH, EP_COMBINE_SMALL_BLOCK>(a, NV, s, ev);
 }
 
 template <int YQ, bool YCH>

@@ -172,6 +172,7 @@ hipError_t launch_recv_topk(const RecvTopkArgs& a, hipStream_t s, LaunchEvents e
 struct OverlapPlan {
     bool ok = false;          // false: lay the next batch out on its own
     bool fused = false;       // the whole layout in one block of the dispatch launch
+    bool fused_combine = false;   // the whole layout in one block of the combine launch
     bool twin = false;        // non-expand: two layouts (expert level, rank level), C blocks each
     int dispatch_blocks = 0;  // layout blocks in front of the dispatch blocks
     int combine_blocks = 0;   // count blocks whose finish phase the combine launch runs

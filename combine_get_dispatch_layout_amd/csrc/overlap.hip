@@ -17,8 +17,10 @@
 //                    block per 256 tokens;
 //   combine launch:  the second phase (finish_lean, one block per 256
 //                    tokens), which reads the histogram from memory so its
-//                    LDS stays small; the launch's LDS is set to hold the
-//                    combine blocks at four per CU.
+//                    LDS stays small; or, for N <= 256 beside a dispatch of
+//                    4 MiB or more, the whole layout in one block; the
+//                    launch's LDS is set to hold the combine blocks at four
+//                    per CU.
 // Kernel boundaries order the phases: the count phase's histogram and ranks
 // are complete before the combine launch starts, the final slots before the
 // next dispatch.
@@ -115,16 +117,19 @@ void k_dispatch_layout(DispatchArgs da, int NV, int NC, LayoutArgs la, LayoutArg
 // blocks come first -- twice as many with twin (non-expand): those of la,
 // then those of lb -- then, with stacked sources, sblocks blocks of the
 // per-source scan.
+// fused: the one block in front is the whole one-block layout of la
+// (lblocks = 1, C unused) instead of finish blocks.
 template <int KMAX, int VPL, int YQ, bool YCH, int BLOCK>
 __global__ __launch_bounds__(BLOCK) void k_combine_layout(CombineArgs ca, int NV, int NC,
                                                           LayoutArgs la, LayoutArgs lb,
                                                           SourceArgs sa, int lblocks, int C,
-                                                          int twin, int sblocks)
+                                                          int twin, int sblocks, int fused)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     const int all = twin ? 2 * lblocks : lblocks;
     if ((int)blockIdx.x < all) {
-        if ((int)blockIdx.x < lblocks) route::finish_lean<KMAX, BLOCK>(la, C, blockIdx.x, smem);
+        if (fused) route::fused_body<KMAX, BLOCK / kWave>(la, smem);
+        else if ((int)blockIdx.x < lblocks) route::finish_lean<KMAX, BLOCK>(la, C, blockIdx.x, smem);
         else route::finish_lean<KMAX, BLOCK>(lb, C, blockIdx.x - lblocks, smem);
         return;
     }
@@ -157,35 +162,45 @@ hipError_t launch_dl(const DispatchArgs& da, int NV, const LayoutArgs& la, const
     return hipGetLastError();
 }
 
-template <int KMAX, int YQ, bool YCH>
-hipError_t launch_cl(const CombineArgs& ca, const LayoutArgs& la, const LayoutArgs& lb,
-                     const SourceArgs& sa, const OverlapPlan& p, hipStream_t s, LaunchEvents ev)
+template <int KMAX, int VPL, int YQ, bool YCH>
+hipError_t launch_cl_v(const CombineArgs& ca, const LayoutArgs& la, const LayoutArgs& lb,
+                       const SourceArgs& sa, const OverlapPlan& p, hipStream_t s, LaunchEvents ev)
 {
-    constexpr int VPL = 2;
     const int NV = ca.H / 8;
     const int NC = (NV + kWave * VPL - 1) / (kWave * VPL);
     const int64_t items = (ca.t_end - ca.t_begin) * NC;
     const int C = p.combine_blocks;   // count blocks whose finish phase runs here
     auto go = [&](auto block) {
         constexpr int B = decltype(block)::value, WPB = B / kWave, G = B / kLayoutBlock;
-        const int lblocks = (C + G - 1) / G;
+        const int lblocks = p.fused_combine ? 1 : (C + G - 1) / G;
         const int all = p.twin ? 2 * lblocks : lblocks;
         const int sblocks = p.src_combine_blocks;
         const int cblocks = items > 0 ? (int)((items + WPB - 1) / WPB) : 0;
         if (all + sblocks + cblocks == 0) return hipSuccess;
-        size_t lds = C > 0 ? route::finish_lean_lds_bytes(la, B) : 0;
+        size_t lds = p.fused_combine ? p.combine_lds : C > 0 ? route::finish_lean_lds_bytes(la, B) : 0;
         if (p.twin && route::finish_lean_lds_bytes(lb, B) > lds)
             lds = route::finish_lean_lds_bytes(lb, B);
         if (lds < combine_occupancy_lds()) lds = combine_occupancy_lds();
         launch_k(k_combine_layout<KMAX, VPL, YQ, YCH, B>, dim3(all + sblocks + cblocks), dim3(B),
                  lds, s, ev.start, ev.stop, ca, NV, NC, la, lb, sa, lblocks, C, p.twin ? 1 : 0,
-                 sblocks);
+                 sblocks, p.fused_combine ? 1 : 0);
         return hipGetLastError();
     };
     // 256-thread blocks: at the combine's 5 waves per SIMD a CU holds five
     // 4-wave blocks but only two 8-wave ones (measured on MI355X, Qwen3
     // shape: 57.4 us per step with 256, 58.5 with 512-thread blocks)
     return go(std::integral_constant<int, 256>{});
+}
+
+// Two vectors per lane.  (One vector per lane for decode batches, as the
+// plain combine takes, made the launch slower: measured on MI355X, decode
+// 128 x 7168 as a graph, 12.8 -> 14.1 us per step; twice the waves slow the
+// finish block, which is the launch's critical path.)
+template <int KMAX, int YQ, bool YCH>
+hipError_t launch_cl(const CombineArgs& ca, const LayoutArgs& la, const LayoutArgs& lb,
+                     const SourceArgs& sa, const OverlapPlan& p, hipStream_t s, LaunchEvents ev)
+{
+    return launch_cl_v<KMAX, 2, YQ, YCH>(ca, la, lb, sa, p, s, ev);
 }
 
 template <int LK>
@@ -224,17 +239,22 @@ OverlapPlan plan_overlap(const LayoutArgs& la, int64_t dispatch_bytes)
     const size_t finish = route::finish_lean_lds_bytes(la, kBlock);
     const int C = (int)((la.num_tokens + kLayoutBlock - 1) / kLayoutBlock);
     const bool split = C > 0 && count <= kOverlapMaxLds && finish <= kOverlapMaxLds;
-    // A batch of <= 256 tokens is laid out by one block of the dispatch
-    // launch, unless the two launches stream enough to hide a phase each
-    // (the one block then outlasts the dispatch; measured on MI355X, decode
-    // shape 128 x 7168 FP8: 12.5 us per step split, 14.3 in one block; a
-    // 128 x 256 batch: 9.0 in one block, 10.4 split).
-    if (la.num_tokens <= kLayoutBlock && fused <= kOverlapMaxLds &&
-        !(split && dispatch_bytes >= kOverlapSplitMinBytes)) {
+    // A batch of <= 256 tokens is laid out by one block: in the dispatch
+    // launch when that launch moves under 4 MiB (measured on MI355X, a
+    // 128 x 256 batch: 9.0 us per step, against 10.4 split over the two
+    // launches), else in the combine launch, where the CUs are not saturated
+    // by stores (decode shape 128 x 7168 FP8 as a graph: 11.9 us per step,
+    // against 12.4 split into count and finish over the two launches).
+    if (la.num_tokens <= kLayoutBlock && fused <= kOverlapMaxLds) {
         p.ok = true;
-        p.fused = true;
-        p.dispatch_blocks = 1;
-        p.dispatch_lds = fused;
+        if (dispatch_bytes < kOverlapSplitMinBytes || !split) {
+            p.fused = true;
+            p.dispatch_blocks = 1;
+            p.dispatch_lds = fused;
+        } else {
+            p.fused_combine = true;
+            p.combine_lds = fused;
+        }
         return p;
     }
     if (!split) return p;   // LDS too large, or an empty batch whose one block does not fit

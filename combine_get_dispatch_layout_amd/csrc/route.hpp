@@ -23,9 +23,13 @@ __device__ __forceinline__ int count_below(uint64_t m)
 // a per-entry branch is waited for before the next one is issued).
 __device__ __forceinline__ int safe_id(int id) { return id >= 0 ? id : 0; }
 
+// n / d for the host-computed magic of d (div_magic; 0 for d == 1), as
+// arithmetic rather than a branch: umulhi(n, 0) is 0, and n is added back
+// only when the magic is 0.
 __device__ __forceinline__ int div_by(int n, uint32_t magic)
 {
-    return magic == 0u ? n : (int)__umulhi((uint32_t)n, magic);
+    const int keep = -(int)(magic == 0u);
+    return (int)__umulhi((uint32_t)n, magic) + (n & keep);
 }
 
 // LDS of the routing phase for a block of `waves` waves.
@@ -96,14 +100,52 @@ __device__ __forceinline__ void store_row(int32_t* p, int K, bool vec, const int
         if (k < K) p[k] = v[k];
 }
 
+// Inclusive sum over each row of 16 lanes (DPP row shifts; lanes shifted in
+// from outside the row read 0).  Every lane of the wave must be active.
+__device__ __forceinline__ uint32_t row_incl_sum(uint32_t x)
+{
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);   // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);   // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);   // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);   // row_shr:8
+    return x;
+}
+
+// Sum of x over the wave, in every lane (every lane active).
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x)
+{
+    x = row_incl_sum(x);
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, 15) +
+           (uint32_t)__builtin_amdgcn_readlane((int)x, 31) +
+           (uint32_t)__builtin_amdgcn_readlane((int)x, 47) +
+           (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
+// Inclusive prefix sum of x over the wave's lanes (every lane active).
+__device__ __forceinline__ int wave_incl_scan(int x, int lane)
+{
+    const uint32_t r = row_incl_sum((uint32_t)x);
+    const int t0 = __builtin_amdgcn_readlane((int)r, 15);
+    const int t1 = __builtin_amdgcn_readlane((int)r, 31);
+    const int t2 = __builtin_amdgcn_readlane((int)r, 47);
+    const int row = lane >> 4;
+    return (int)r + (row > 0 ? t0 : 0) + (row > 1 ? t1 : 0) + (row > 2 ? t2 : 0);
+}
+
 // Per-wave counts of the set bits of a 64-bit mask held by every lane, for
-// bits [0, n): lane b receives the number of lanes with bit b set.
+// bits [0, n), n <= 64: lane b receives the number of lanes with bit b set.
+// Four bits at a time become four byte counters of one word (a wave has 64
+// lanes, so a byte never overflows), summed over the wave by DPP.  Every
+// lane of the wave must be active.
 __device__ __forceinline__ int wave_bit_counts(uint64_t m, int n, int lane)
 {
     int mine = 0;
-    for (int b = 0; b < n; ++b) {
-        const int c = __popcll(__ballot((m >> b) & 1ull));
-        mine = lane == b ? c : mine;
+    for (int q = 0; 4 * q < n; ++q) {
+        const uint32_t nib = (uint32_t)(m >> (4 * q)) & 15u;
+        const uint32_t spread =
+            (nib & 1u) | ((nib & 2u) << 7) | ((nib & 4u) << 14) | ((nib & 8u) << 21);
+        const uint32_t tot = wave_sum(spread);
+        if ((lane >> 2) == q) mine = (int)((tot >> (8 * (lane & 3))) & 0xFFu);
     }
     return mine;
 }
@@ -149,8 +191,8 @@ __device__ __forceinline__ uint64_t rank_mask(const LayoutArgs& a, const int (&i
     uint64_t m = 0ull;
     if (a.R <= 64) {
 #pragma unroll
-        for (int k = 0; k < KMAX; ++k)
-            if (ids[k] >= 0) m |= 1ull << div_by(ids[k], a.nle_magic);
+        for (int k = 0; k < KMAX; ++k)   // selects, not branches
+            m |= (ids[k] >= 0 ? 1ull : 0ull) << div_by(safe_id(ids[k]), a.nle_magic);
     }
     return m;
 }
@@ -172,7 +214,7 @@ __device__ __forceinline__ void add_rank_counts(const LayoutArgs& a, const int (
             const uint64_t gm = rpn >= 64 ? ~0ull : (1ull << rpn) - 1ull;
             uint64_t nm = 0ull;
             for (int n = 0; n < a.nodes; ++n)
-                if ((m >> (n * rpn)) & gm) nm |= 1ull << n;
+                nm |= (((m >> (n * rpn)) & gm) != 0ull ? 1ull : 0ull) << n;
             const int nc = wave_bit_counts(nm, a.nodes, lane);
             if (lane < a.nodes && nc != 0) atomicAdd(ncnt + lane, nc);
         }
@@ -204,11 +246,19 @@ __device__ __forceinline__ void write_in_rank_row(const LayoutArgs& a, const int
     const int R = a.R;
     if (R <= 64) {
         if (a.in_rank_words) {
+            // 0/1 bytes from 4 bits of the mask per word; 16-byte stores when
+            // the row holds whole, aligned 16-byte pieces
             uint32_t* roww = reinterpret_cast<uint32_t*>(row);
-            for (int q = 0; q < R / 4; ++q) {
-                const uint32_t nib = (uint32_t)(m >> (4 * q));
-                roww[q] =
-                    (nib & 1u) | ((nib & 2u) << 7) | ((nib & 4u) << 14) | ((nib & 8u) << 21);
+            const bool vec = R % 16 == 0 && (reinterpret_cast<uintptr_t>(row) & 15) == 0;
+            for (int q = 0; q < R / 4; q += vec ? 4 : 1) {
+                uint32_t wd[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t nib = (uint32_t)(m >> (4 * (q + i)));
+                    wd[i] = (nib & 1u) | ((nib & 2u) << 7) | ((nib & 4u) << 14) | ((nib & 8u) << 21);
+                }
+                if (vec) *reinterpret_cast<u32x4*>(roww + q) = u32x4{wd[0], wd[1], wd[2], wd[3]};
+                else roww[q] = wd[0];
             }
         } else {
             for (int r = 0; r < R; ++r) row[r] = (uint8_t)((m >> r) & 1ull);
@@ -309,8 +359,7 @@ __device__ __forceinline__ void route_block(const LayoutArgs& a, int64_t t0, con
 #pragma unroll
             for (int k = 0; k < KMAX; ++k) mk[k] = mytab[safe_id(ids[k])];
 #pragma unroll
-            for (int k = 0; k < KMAX; ++k)
-                if (ids[k] >= 0) lr[k] += count_below(mk[k]);
+            for (int k = 0; k < KMAX; ++k) lr[k] += ids[k] >= 0 ? count_below(mk[k]) : 0;
         }
         // the level's per-expert counts, four table words in flight per lane
         for (int e0 = lane; e0 < E; e0 += 4 * kWave) {
@@ -395,12 +444,7 @@ __device__ __forceinline__ void aligned_prefix(const LayoutArgs& a, const int32_
         al[j] = a.A == 1 ? c : ((c + a.A - 1) / a.A) * a.A;
         own += al[j];
     }
-    int incl = own;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const int v = __shfl_up(incl, off);
-        if (lane >= off) incl += v;
-    }
+    const int incl = wave_incl_scan(own, lane);
     if (lane == kWave - 1) scratch[w] = incl;
     __syncthreads();
     int run = incl - own;

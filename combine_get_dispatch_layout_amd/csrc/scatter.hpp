@@ -149,11 +149,35 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(char* row, int bytes)
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+// x from another lane of the same row of 16 (DPP control CTRL).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Maximum over aligned groups of WIDTH lanes (4, 16 or the wave), in every
+// lane of the group, by DPP exchanges: lane ^ 1 and lane ^ 2 inside a quad,
+// then the mirrored lane of the half-row (the other quad) and of the row
+// (the other half-row); across rows by reading the four row maxima.  The
+// whole wave must be active.
 template <int WIDTH>
 __device__ __forceinline__ float group_max(float v)
 {
-#pragma unroll
-    for (int m = 1; m < WIDTH; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, WIDTH));
+    static_assert(WIDTH == 4 || WIDTH == 16 || WIDTH == kWave, "groups of 4, 16 or 64 lanes");
+    v = fmaxf(v, dpp_f<0xB1>(v));       // quad_perm [1,0,3,2]
+    v = fmaxf(v, dpp_f<0x4E>(v));       // quad_perm [2,3,0,1]
+    if constexpr (WIDTH >= 16) {
+        v = fmaxf(v, dpp_f<0x141>(v));  // row_half_mirror
+        v = fmaxf(v, dpp_f<0x140>(v));  // row_mirror
+    }
+    if constexpr (WIDTH == kWave) {
+        const int b = __float_as_int(v);
+        v = fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 0)),
+                        __int_as_float(__builtin_amdgcn_readlane(b, 16))),
+                  fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 32)),
+                        __int_as_float(__builtin_amdgcn_readlane(b, 48))));
+    }
     return v;
 }
 
