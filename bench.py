@@ -268,14 +268,17 @@ def trace_summary(trace_dir, args):
         sh["shape"].add(f"{grid // max(wg, 1)}x{wg}")
         sh["lds"].add(r.get("LDS_Block_Size", r.get("Lds_Size", "?")))
         sh["vgpr"].add(r.get("Arch_VGPR_Count", r.get("VGPR_Count", "?")))
-    mine = ("k_", "__amd_rocclr_copyBuffer")
+    def short(name):
+        # "void epk::(anonymous namespace)::k_x<...>(args)" -> "k_x<...>"
+        name = name.split("(anonymous namespace)::", 1)[-1]
+        return name.split(">(")[0] + ">" if ">(" in name else name.split("(")[0]
     rows = []
     for r in stats:
         kn = r["Name"]
-        if not kn.startswith(mine):
+        if "epk::" not in kn and not kn.startswith("__amd_rocclr_copyBuffer"):
             continue
         sh = shapes.get(kn, dict(shape=set(), lds=set(), vgpr=set()))
-        rows.append(f"| `{kn}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+        rows.append(f"| `{short(kn)}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                     f"{'; '.join(sorted(sh['shape']))} | {'; '.join(sorted(sh['lds']))} | "
                     f"{'; '.join(sorted(sh['vgpr']))} |")
@@ -290,7 +293,7 @@ def trace_summary(trace_dir, args):
             f"--warmup {args.warmup}", "```", "",
             "`<dir>/trace_kernel_stats.csv` and `trace_kernel_trace.csv`; the library's kernels, plus "
             "the 1 GiB device copy the benchmark times as its achievable-bandwidth reference:", "",
-            "| kernel | calls | avg us | min us | max us | workgroups x threads | LDS B | VGPRs |",
+            "| kernel | calls | avg us | min us | max us | workgroups x threads | static LDS B | VGPRs |",
             "|---|---|---|---|---|---|---|---|", *rows, "",
             "Workload: " + json.dumps(dict(workload=w.name, num_tokens=w.num_tokens, hidden=w.hidden,
                                            num_experts=w.num_experts, num_ranks=w.num_ranks,
@@ -300,7 +303,8 @@ def trace_summary(trace_dir, args):
                                            combine_quant=w.combine_quant,
                                            combine_group=w.combine_group)), "",
             "Kernel averages include the warm-up steps and the eager timing pass.  Other kernels of the "
-            "run (torch's input generation) are left out.", ""]
+            "run (torch's input generation) are left out.  The LDS column is the profiler's "
+            "`LDS_Block_Size`, the kernel's static LDS; the dynamic LDS a launch requests is not in it.", ""]
     out = os.path.join(ROOT, "profiles", f"kernels_{name}.md")
     with open(out, "w") as f:
         f.write("\n".join(text))
