@@ -249,6 +249,65 @@ def write_traffic_md(rec, tag):
         f.write("\n".join(text))
 
 
+def ea_summary(rd_csv, wr_csv, args):
+    """profiles/ea_requests_<tag>.md from two rocprofv3 --pmc passes over
+    `bench.py --workload <workload> --pipeline <pipeline>`: the L2's memory
+    requests (TCC_EA0_RDREQ / _32B / _DRAM, then TCC_EA0_WRREQ / _64B /
+    _DRAM, summed over the L2 channels) as bytes per launch, and the share of
+    them sent to the memory controller rather than to other agents."""
+    import csv
+    import numpy as np
+    w, tag, flags = variant_of(args)
+    per = {}
+    for path in (rd_csv, wr_csv):
+        for r in csv.DictReader(open(path)):
+            n = r["Kernel_Name"]
+            if "copyBuffer" in n:
+                n = "__amd_rocclr_copyBuffer"
+            elif "epk::" in n:
+                n = n.split("(anonymous namespace)::", 1)[-1]
+                n = n.split(">(")[0] + ">" if ">(" in n else n.split("(")[0]
+            else:
+                continue
+            per.setdefault(n, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    rows = []
+    for n, c in per.items():
+        # the copy: its largest launch (the 1 GiB one); kernels: the median
+        pick = max if n == "__amd_rocclr_copyBuffer" else (lambda v: float(np.median(v)))
+        v = {k: pick(x) for k, x in c.items()}
+        rd = (v["TCC_EA0_RDREQ_sum"] - v["TCC_EA0_RDREQ_32B_sum"]) * 64 + v["TCC_EA0_RDREQ_32B_sum"] * 32
+        wr = v["TCC_EA0_WRREQ_64B_sum"] * 64 + (v["TCC_EA0_WRREQ_sum"] - v["TCC_EA0_WRREQ_64B_sum"]) * 32
+        rdd = v["TCC_EA0_RDREQ_DRAM_sum"] / max(v["TCC_EA0_RDREQ_sum"], 1.0)
+        wrd = v["TCC_EA0_WRREQ_DRAM_sum"] / max(v["TCC_EA0_WRREQ_sum"], 1.0)
+        rows.append(f"| `{n}` | {len(c['TCC_EA0_RDREQ_sum'])} | {rd / 1e6:.2f} | {rdd:.4f} | "
+                    f"{wr / 1e6:.2f} | {wrd:.4f} |")
+    vflags = "".join(" " + f for f in flags)
+    a = f"--workload {args.workload}{vflags} --pipeline {args.pipeline} --steps 4 --warmup 2 --no-cpu-baseline"
+    text = [f"# L2 memory requests per launch: {tag}", "", "Commands (repo root, on one MI355X):", "",
+            "```",
+            f"rocprofv3 --pmc TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_32B_sum TCC_EA0_RDREQ_DRAM_sum -f csv "
+            f"-d <dir>/rd -o rd -- python3 bench.py {a}",
+            f"rocprofv3 --pmc TCC_EA0_WRREQ_sum TCC_EA0_WRREQ_64B_sum TCC_EA0_WRREQ_DRAM_sum -f csv "
+            f"-d <dir>/wr -o wr -- python3 bench.py {a}",
+            f"python3 bench.py --ea-from <dir>/rd/rd_counter_collection.csv "
+            f"<dir>/wr/wr_counter_collection.csv --workload {args.workload}{vflags} "
+            f"--pipeline {args.pipeline}", "```", "",
+            "| kernel | launches | read MB (64 B and 32 B requests) | read share to DRAM | write MB | "
+            "write share to DRAM |", "|---|---|---|---|---|---|", *rows, "",
+            "Medians over the run's launches; the device copy row is its 1 GiB launch (reads 1 GiB, "
+            "writes 1 GiB).  The read requests seen on this interface are half the bytes read, for the "
+            "copy as for the kernels, which is the factor of 2 applied to FETCH_SIZE in the traffic "
+            "records; writes are counted whole.  Every request is sent to the memory controller (DRAM "
+            "share 1), none to other agents.  The 256 MB Infinity Cache is on the memory side of this "
+            "interface, so these counters cannot tell its hits from HBM accesses; the benchmark rotates "
+            "buffer sets of over 1 GiB per cycle to keep the data out of it, and `--sets 1` measures "
+            "the warm case beside it.", ""]
+    out = os.path.join(ROOT, "profiles", f"ea_requests_{tag}.md")
+    with open(out, "w") as f:
+        f.write("\n".join(text))
+    print(out)
+
+
 def trace_summary(trace_dir, args):
     """profiles/kernels_<tag>[_<pipeline>][_graph].md from a rocprofv3
     --kernel-trace --stats run of `bench.py --workload <workload> <variant
@@ -562,6 +621,9 @@ def main():
                          "into profiles/ and exit")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc runs into profiles/ and exit")
+    ap.add_argument("--ea-from", nargs=2, metavar=("RD_CSV", "WR_CSV"),
+                    help="summarise two rocprofv3 --pmc runs of the L2's memory request counters "
+                         "into profiles/ and exit")
     args = ap.parse_args()
     if args.pipeline is None:
         args.pipeline = "merged"
@@ -570,6 +632,9 @@ def main():
         return
     if args.trace_from:
         trace_summary(args.trace_from, args)
+        return
+    if args.ea_from:
+        ea_summary(args.ea_from[0], args.ea_from[1], args)
         return
     if args.ceilings:
         _, results = ceilings(variant_of(args)[0])
@@ -634,6 +699,12 @@ def main():
         if w.combine_quant:
             s["y"], s["y_scales"] = ep.ep_quantize_rows(cfg, s["y"])
         sets.append(s)
+    data_sets = nsets
+    if nsets == 1 and args.pipeline == "merged":
+        # the merged pipeline lays the next batch out into another handle:
+        # a second handle over the same buffers, so one set of data stays hot
+        sets.append(dict(sets[0], h=ep.ep_handle_init(cfg, N, device=dev)))
+        nsets = 2
     # S from one synced layout (for the byte counts)
     S = ep.ep_get_layout(sets[0]["h"], sets[0]["topk"], do_cpu_sync=True)["num_recv_slots"]
     nbytes = algorithmic_bytes(w, V, S)
@@ -844,7 +915,7 @@ def main():
                    "rounds": len(rounds), "num_sources": w.num_sources, "quant": w.quant,
                    "quant_group": w.quant_group, "scale_mode": w.scale_mode,
                    "combine_quant": w.combine_quant, "combine_group": w.combine_group,
-                   "buffer_sets": nsets},
+                   "buffer_sets": data_sets},
         "roofline": {"bound": "hbm",
                      "kernel": ({"dispatch": "k_dispatch_layout (dispatch + next batch's layout "
                                              "count phase)",
@@ -865,7 +936,7 @@ def main():
         "device_copy_GBps": copy_gbs,
         "pipeline": args.pipeline,
         "cache": ("warm: one buffer set, reused every step (Infinity-Cache-resident where it "
-                  "fits)" if nsets == 1 else
+                  "fits)" if data_sets == 1 else
                   f"cold: {nsets} buffer sets rotate, {nsets * per_set / 2**30:.2f} GiB per "
                   "cycle against a 256 MB Infinity Cache"),
         "timing": {"wall_clock": "host clock around the timed steps, no events inside",
