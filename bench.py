@@ -709,8 +709,6 @@ def main():
     S = ep.ep_get_layout(sets[0]["h"], sets[0]["topk"], do_cpu_sync=True)["num_recv_slots"]
     nbytes = algorithmic_bytes(w, V, S)
     pl = args.pipeline
-    if args.graph and pl == "overlap":
-        sys.exit("--graph captures one stream: use the merged, serial, fused or cached pipeline")
     # a graph is captured on a stream of its own (default priority)
     stream = torch.cuda.Stream() if args.graph else torch.cuda.current_stream()
     # overlap: the layout of batch i+1 runs on a second stream while batch i
@@ -780,15 +778,24 @@ def main():
         else:
             c((hev.ev[base + 2 * j], hev.ev[base + 2 * j + 1]))
 
-    def layout(i, base):
+    fork, join = torch.cuda.Event(), torch.cuda.Event()
+
+    def layout(i, base, capturing=False):
         s = sets[i % nsets]
-        lay_stream.wait_event(s["main_done"])   # the set's previous batch is combined
+        if capturing:
+            # a fork of the captured stream: the layout waits for every earlier
+            # step's work, and the layout stream joins the capture
+            fork.record(stream)
+            lay_stream.wait_event(fork)
+        else:
+            lay_stream.wait_event(s["main_done"])   # the set's previous batch is combined
         issue(i, 0, base)
         s["lay_done"].record(lay_stream)
 
-    def shuffle(i, base):
+    def shuffle(i, base, wait=True):
         s = sets[i % nsets]
-        stream.wait_event(s["lay_done"])
+        if wait:
+            stream.wait_event(s["lay_done"])
         for j in range(1, calls_per_step):
             issue(i, j, base)
         s["main_done"].record(stream)
@@ -799,12 +806,22 @@ def main():
                          sets[0]["per_expert"], sets[0]["in_rank"])
     gstep = [0]   # steps issued so far (the merged pipeline's set rotation)
 
-    def run(n, timed):
+    def run(n, timed, capturing=False):
         """n steps; with overlap the layout of step i+1 is issued before the
         dispatch and combine of step i, otherwise each step's calls in order.
-        timed: every call carries kernel events (the eager timing pass)."""
+        timed: every call carries kernel events (the eager timing pass).
+        capturing (overlap): one rotation inside a graph capture, the first
+        set's layout already done (by the prologue or the previous replay),
+        the last layout for the next replay's first step."""
         def base(i):
             return 2 * calls_per_step * i if timed else None
+        if pl == "overlap" and capturing:
+            for i in range(n):
+                layout(i + 1, None, capturing=True)
+                shuffle(i, None, wait=i > 0)
+            join.record(lay_stream)
+            stream.wait_event(join)
+            return
         if pl == "merged":
             for i in range(n):
                 c = sets[gstep[0] % nsets]["calls"]
@@ -834,8 +851,12 @@ def main():
         # pipeline's host bookkeeping advances by a whole rotation during the
         # capture, the device catches up on each replay
         graph = torch.cuda.CUDAGraph()
+        if pl == "overlap":
+            # the first set's layout, ahead of the captured rotation
+            issue(0, 0, None)
+            torch.cuda.synchronize()
         with torch.cuda.graph(graph, stream=stream):
-            run(nsets, False)
+            run(nsets, False, capturing=True)
         reps = -(-args.steps // nsets)
         args.steps = reps * nsets
         graph.replay()
