@@ -81,10 +81,16 @@ KERNEL_SOURCES = {"dispatch": ("dispatch.hip", "scatter.hpp"),
 
 
 def kernel_source_hash(kernel):
+    """Hash of the kernel's sources without their comments and blank space,
+    so that an edit of the comments alone keeps its counter record valid."""
+    import re
     h = hashlib.sha256()
     for src in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, "combine_get_dispatch_layout_amd", "csrc", src), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "combine_get_dispatch_layout_amd", "csrc", src)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
