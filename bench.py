@@ -376,12 +376,13 @@ def trace_summary(trace_dir, args):
     print(out)
 
 
-def cpu_baseline(w, idx, wts, budget_s=10.0):
+def cpu_baseline(w, idx, wts, budget_s=10.0, nbytes=None):
     """The oracle, as it stands, on the same workload: full passes (layout,
     slots, dispatch, combine) until budget_s is spent (at least 3).  Layout
     and slots run on the serial build; dispatch and combine (the fp32
     reduction) on the OpenMP build, which gives the same bits.  Reports the
-    median pass and per-stage medians."""
+    median pass and per-stage medians, and with nbytes (the algorithmic
+    bytes per stage) the stages' GB/s on the same byte counts as the GPU's."""
     import numpy as np
     import oracle
     import workloads as W
@@ -435,9 +436,14 @@ def cpu_baseline(w, idx, wts, budget_s=10.0):
     total = np.array(times["layout"]) + np.array(times["slots"]) + np.array(times["dispatch"]) \
         + np.array(times["combine"])
     med = {k: float(np.median(v)) for k, v in times.items()}
+    gbps = None
+    if nbytes:
+        gbps = {"layout+slots": nbytes["layout"] / (med["layout"] + med["slots"]) / 1e9,
+                "dispatch": nbytes["dispatch"] / med["dispatch"] / 1e9,
+                "combine": nbytes["combine"] / med["combine"] / 1e9}
     return dict(value=N / float(np.median(total)), unit="tokens/s", cores=threads,
                 host_cpus=os.cpu_count(), kind="oracle",
-                stages_ms={k: v * 1e3 for k, v in med.items()},
+                stages_ms={k: v * 1e3 for k, v in med.items()}, stages_GBps=gbps,
                 sample=f"{passes} full passes of the {w.name} workload ({N} tokens: layout and "
                        f"slots serial, dispatch and fp32 combine over tokens on {threads} "
                        f"OpenMP threads), median pass {np.median(total) * 1e3:.1f} ms, "
@@ -975,7 +981,7 @@ def main():
         "recv_rows": S, "valid_pairs": V,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, idx, wts, budget_s=args.cpu_budget)
+        line["cpu_baseline"] = cpu_baseline(w, idx, wts, budget_s=args.cpu_budget, nbytes=nbytes)
     print(json.dumps(line), flush=True)
 
 

@@ -46,6 +46,7 @@ def test_default_line_has_the_contract_fields():
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1
     assert cb["host_cpus"] >= 1 and set(cb["stages_ms"]) == {"layout", "slots", "dispatch",
                                                              "combine"}
+    assert set(cb["stages_GBps"]) == {"layout+slots", "dispatch", "combine"}
     assert cb["unit"] == line["unit"] and cb["sample"]
 
 
