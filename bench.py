@@ -289,7 +289,7 @@ def ea_summary(rd_csv, wr_csv, args):
                     f"{wr / 1e6:.2f} | {wrd:.4f} |")
     vflags = "".join(" " + f for f in flags)
     a = f"--workload {args.workload}{vflags} --pipeline {args.pipeline} --steps 4 --warmup 2 --no-cpu-baseline"
-    text = [f"# L2 memory requests per launch: {tag}", "", "Commands (repo root, on one MI355X):", "",
+    text = [f"# L2 memory requests per launch: {tag}, {args.pipeline} pipeline", "", "Commands (repo root, on one MI355X):", "",
             "```",
             f"rocprofv3 --pmc TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_32B_sum TCC_EA0_RDREQ_DRAM_sum -f csv "
             f"-d <dir>/rd -o rd -- python3 bench.py {a}",
@@ -308,7 +308,7 @@ def ea_summary(rd_csv, wr_csv, args):
             "interface, so these counters cannot tell its hits from HBM accesses; the benchmark rotates "
             "buffer sets of over 1 GiB per cycle to keep the data out of it, and `--sets 1` measures "
             "the warm case beside it.", ""]
-    out = os.path.join(ROOT, "profiles", f"ea_requests_{tag}.md")
+    out = os.path.join(ROOT, "profiles", f"ea_requests_{tag}_{args.pipeline}.md")
     with open(out, "w") as f:
         f.write("\n".join(text))
     print(out)
