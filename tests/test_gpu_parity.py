@@ -581,7 +581,7 @@ def test_workload_full_size_merged(name):
     (dict(N=1, H=64, E=64, R=8, K=8, A=2), [8500, 9000, 8193]),               # count + finish
     (dict(N=1, H=64, E=64, R=8, K=6, rpn=4), [20000, 17000, 16384]),          # accumulator copies
     (dict(N=1, H=2048, E=128, R=16, K=6, A=4, mask=0.1), [4097, 3000, 4096]),  # odd block count
-    (dict(N=1, H=7168, E=256, R=16, K=8, quant=W.QUANT_FP8, group=128), [128, 200, 256]),  # split: 7+ MiB
+    (dict(N=1, H=7168, E=256, R=16, K=8, quant=W.QUANT_FP8, group=128), [128, 200, 256]),  # in combine: 7+ MiB
     (dict(N=1, H=512, E=256, R=16, K=8, quant=W.QUANT_FP8, group=128), [128, 200, 256]),   # one block
     (dict(N=1, H=520, E=128, R=16, K=6, A=4, mask=0.1), [3000, 257, 777, 1]),  # padding, mixed
     (dict(N=1, H=256, E=64, R=8, K=8, cap=40), [600, 600]),                    # fixed capacity
@@ -673,31 +673,33 @@ def test_overlap_non_expand_group_limited():
     _overlap_sequence(w, [3000, 1000, 2049, 1, 700], [21, 22, 23, 24, 25])
 
 
-@pytest.mark.parametrize("n,two_phase", [(1000, True), (200, False)])
-def test_overlap_states(n, two_phase):
+@pytest.mark.parametrize("n,H,two_phase", [(1000, 64, True), (200, 64, False), (128, 4096, True)])
+def test_overlap_states(n, H, two_phase):
     """Above 256 tokens the next batch's layout is split over the dispatch
     and combine launches and the handle is unusable in between; up to 256
-    (with a dispatch that moves under 4 MiB, as here) it is complete after
-    the dispatch launch."""
-    cfg = ep.Config(64, 8, 64, 8)
+    with a dispatch that moves under 4 MiB it is complete after the dispatch
+    launch; up to 256 beside a larger dispatch (128 x 4096 x 8 bf16 rows) the
+    whole layout runs in the combine launch, so the handle is unusable in
+    between as well."""
+    cfg = ep.Config(H, 8, 64, 8)
     h0, h1 = ep.ep_handle_init(cfg, n), ep.ep_handle_init(cfg, n)
-    other = ep.ep_handle_init(ep.Config(64, 8, 64, 4), n)
-    w = _custom(N=n, H=64, E=64, R=8, K=8)
+    other = ep.ep_handle_init(ep.Config(H, 8, 64, 4), n)
+    w = _custom(N=n, H=H, E=64, R=8, K=8)
     idx, wts = W.routing(w)
     topk = torch.from_numpy(idx).cuda()
-    x = W.activations(n, 64, 5, device="cuda")
-    recv = torch.zeros((ep.ep_recv_capacity(cfg, n), 64), dtype=torch.bfloat16, device="cuda")
+    x = W.activations(n, H, 5, device="cuda")
+    recv = torch.zeros((ep.ep_recv_capacity(cfg, n), H), dtype=torch.bfloat16, device="cuda")
     ep.ep_get_layout(h0, topk)
     for bad in (h0, other):
         with pytest.raises(ep.EpError) as ei:
             ep.ep_dispatch_overlap(h0, x, recv, h_next=bad, topk_next=topk)
         assert ei.value.status == ep.EP_ERR_INVALID_ARG
     ep.ep_dispatch_overlap(h0, x, recv, h_next=h1, topk_next=topk)
-    out = torch.zeros((n, 64), dtype=torch.bfloat16, device="cuda")
-    y = torch.zeros((ep.ep_recv_capacity(cfg, n), 64), dtype=torch.bfloat16, device="cuda")
+    out = torch.zeros((n, H), dtype=torch.bfloat16, device="cuda")
+    y = torch.zeros((ep.ep_recv_capacity(cfg, n), H), dtype=torch.bfloat16, device="cuda")
     wd = torch.from_numpy(wts).cuda()
     if two_phase:
-        # h1 is counted, not finished: only the overlapped combine may use it
+        # h1 is not laid out yet: only the overlapped combine may use it
         with pytest.raises(ep.EpError) as ei:
             ep.ep_dispatch(h1, x, recv)
         assert ei.value.status == ep.EP_ERR_STATE
@@ -711,25 +713,26 @@ def test_overlap_states(n, two_phase):
     assert ep.ep_check_error(h0) == (ep.EP_OK, 0) and ep.ep_check_error(h1) == (ep.EP_OK, 0)
 
 
-@pytest.mark.parametrize("P,non_expand", [(1, False), (4, False), (1, True)])
-def test_overlap_abandoned_layout_starts_over(P, non_expand):
-    """A next-batch layout counted inside a dispatch launch and never
-    finished leaves no trace when the handle is laid out again: through
-    ep_get_layout, and through another ep_dispatch_overlap that names it.
-    Its distinct-token (and per-source) additions must not reach the new
-    layout's counts."""
+@pytest.mark.parametrize("P,non_expand,n,H", [(1, False, 1000, 64), (4, False, 1000, 64),
+                                             (1, True, 1000, 64), (1, False, 128, 4096)])
+def test_overlap_abandoned_layout_starts_over(P, non_expand, n, H):
+    """A next-batch layout started inside a dispatch launch (counted there,
+    or, for 128 tokens beside a 4096-wide dispatch, left whole to the combine
+    launch) and never finished leaves no trace when the handle is laid out
+    again: through ep_get_layout, and through another ep_dispatch_overlap
+    that names it.  Its distinct-token (and per-source) additions must not
+    reach the new layout's counts."""
     from shuffle_check import compare_layout, config_of, oracle_slots
-    n = 1000
-    w = _custom(N=n, H=64, E=64, R=8, K=8, rpn=4).scaled(num_sources=P, non_expand=non_expand)
+    w = _custom(N=n, H=H, E=64, R=8, K=8, rpn=4).scaled(num_sources=P, non_expand=non_expand)
     cfg = config_of(w)
-    _say(f"[parity] abandoned overlap layout P={P} non_expand={non_expand}")
+    _say(f"[parity] abandoned overlap layout P={P} non_expand={non_expand} n={n} H={H}")
     h0, h1 = ep.ep_handle_init(cfg, n), ep.ep_handle_init(cfg, n)
     routes = [W.routing(w.scaled(seed=sd)) for sd in (51, 52, 53)]
     topk = [torch.from_numpy(r[0]).cuda() for r in routes]
-    x = W.activations(n, 64, 5, device="cuda")
-    recv = torch.zeros((ep.ep_recv_capacity(cfg, n), 64), dtype=torch.bfloat16, device="cuda")
-    y = torch.zeros((ep.ep_recv_capacity(cfg, n), 64), dtype=torch.bfloat16, device="cuda")
-    out = torch.zeros((n, 64), dtype=torch.bfloat16, device="cuda")
+    x = W.activations(n, H, 5, device="cuda")
+    recv = torch.zeros((ep.ep_recv_capacity(cfg, n), H), dtype=torch.bfloat16, device="cuda")
+    y = torch.zeros((ep.ep_recv_capacity(cfg, n), H), dtype=torch.bfloat16, device="cuda")
+    out = torch.zeros((n, H), dtype=torch.bfloat16, device="cuda")
     wd = None if non_expand else torch.from_numpy(routes[0][1]).cuda()
 
     class R:
