@@ -244,7 +244,8 @@ OverlapPlan plan_overlap(const LayoutArgs& la, int64_t dispatch_bytes)
     // 128 x 256 batch: 9.0 us per step, against 10.4 split over the two
     // launches), else in the combine launch, where the CUs are not saturated
     // by stores (decode shape 128 x 7168 FP8 as a graph: 11.9 us per step,
-    // against 12.4 split into count and finish over the two launches and
+    // the same as split into count and finish over the two launches, where
+    // each phase outlasts its launch's streaming blocks by about 1 us, and
     // 12.5 with the block in the dispatch launch).
     if (la.num_tokens <= kLayoutBlock && fused <= kOverlapMaxLds) {
         p.ok = true;

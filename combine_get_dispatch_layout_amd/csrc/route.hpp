@@ -471,7 +471,7 @@ __device__ __forceinline__ void write_expert_arrays(const LayoutArgs& a, const i
     for (int e = tid; e < E; e += NT) {
         a.num_unaligned[e] = cnt[e];
         if (a.out_per_expert) a.out_per_expert[e] = cnt[e];
-        const int first = (e / a.nle) * a.nle;
+        const int first = div_by(e, a.nle_magic) * a.nle;   // the rank's first expert
         if (a.cap > 0) {   // rows filled: min(count, cap), prefix within the rank
             int v = 0;
             for (int q = a.counts_as_prefix ? first : e; q <= e; ++q) v += min(cnt[q], a.cap);
@@ -617,10 +617,10 @@ __device__ __forceinline__ void count_body(const LayoutArgs& a, int b, unsigned 
         if (L.ncnt[n] != 0) atomicAdd(a.node_acc + copy + n, L.ncnt[n]);
 }
 
-// Distinct-token totals from the accumulators (the sum of their copies),
-// which are re-zeroed for the next call.  The additions were made by an
-// earlier launch, so plain loads see them; all kAccCopies copies are read
-// at once (the unused ones hold zero).
+// Distinct-token totals from the accumulators (the sum of the acc_copies
+// copies in use), which are re-zeroed for the next call.  The additions were
+// made by an earlier launch, so plain loads see them; the copies are read at
+// once.
 //   RankTotals: when every rank and node has a thread of its own
 //   (R, nodes <= NT) the loads are issued by rank_totals_load at the start
 //   of a block, beside its other loads, so that rank_totals_store at its
@@ -638,8 +638,9 @@ __device__ __forceinline__ void rank_totals_load(const LayoutArgs& a, RankTotals
     if (!rt.early) return;
 #pragma unroll
     for (int c = 0; c < kAccCopies; ++c) {
-        rt.r[c] = tid < a.R ? a.rank_acc[c * a.acc_stride + tid] : 0;
-        rt.n[c] = tid < a.nodes ? a.node_acc[c * a.acc_stride + tid] : 0;
+        const bool used = c < a.acc_copies;
+        rt.r[c] = used && tid < a.R ? a.rank_acc[c * a.acc_stride + tid] : 0;
+        rt.n[c] = used && tid < a.nodes ? a.node_acc[c * a.acc_stride + tid] : 0;
     }
 }
 
@@ -656,12 +657,14 @@ __device__ __forceinline__ void rank_totals_store(const LayoutArgs& a, const Ran
         }
         if (tid < a.R) {
 #pragma unroll
-            for (int c = 0; c < kAccCopies; ++c) a.rank_acc[c * a.acc_stride + tid] = 0;
+            for (int c = 0; c < kAccCopies; ++c)
+                if (c < a.acc_copies) a.rank_acc[c * a.acc_stride + tid] = 0;
             if (a.out_per_rank) a.out_per_rank[tid] = rs;
         }
         if (tid < a.nodes) {
 #pragma unroll
-            for (int c = 0; c < kAccCopies; ++c) a.node_acc[c * a.acc_stride + tid] = 0;
+            for (int c = 0; c < kAccCopies; ++c)
+                if (c < a.acc_copies) a.node_acc[c * a.acc_stride + tid] = 0;
             if (a.out_per_node) a.out_per_node[tid] = ns;
         }
         return;
@@ -669,24 +672,24 @@ __device__ __forceinline__ void rank_totals_store(const LayoutArgs& a, const Ran
     for (int r = threadIdx.x; r < a.R; r += NT) {
         int v[kAccCopies];
 #pragma unroll
-        for (int c = 0; c < kAccCopies; ++c) v[c] = a.rank_acc[c * a.acc_stride + r];
+        for (int c = 0; c < kAccCopies; ++c) v[c] = c < a.acc_copies ? a.rank_acc[c * a.acc_stride + r] : 0;
         int sum = 0;
 #pragma unroll
         for (int c = 0; c < kAccCopies; ++c) {
             sum += v[c];
-            a.rank_acc[c * a.acc_stride + r] = 0;
+            if (c < a.acc_copies) a.rank_acc[c * a.acc_stride + r] = 0;
         }
         if (a.out_per_rank) a.out_per_rank[r] = sum;
     }
     for (int n = threadIdx.x; n < a.nodes; n += NT) {
         int v[kAccCopies];
 #pragma unroll
-        for (int c = 0; c < kAccCopies; ++c) v[c] = a.node_acc[c * a.acc_stride + n];
+        for (int c = 0; c < kAccCopies; ++c) v[c] = c < a.acc_copies ? a.node_acc[c * a.acc_stride + n] : 0;
         int sum = 0;
 #pragma unroll
         for (int c = 0; c < kAccCopies; ++c) {
             sum += v[c];
-            a.node_acc[c * a.acc_stride + n] = 0;
+            if (c < a.acc_copies) a.node_acc[c * a.acc_stride + n] = 0;
         }
         if (a.out_per_node) a.out_per_node[n] = sum;
     }
@@ -731,6 +734,25 @@ __device__ __forceinline__ void finish_lean(const LayoutArgs& a, int C, int b, u
     int32_t* part_pre = scratch + 2 * NT;               // [NT]
     int32_t* part_all = part_pre + NT;                  // [NT]
 
+    // Column e of the histogram is split over P threads (NT / E of them when
+    // E < NT), each summing its rows in batches of kBatch loads.  The first
+    // batch of the first columns is issued before anything else, beside the
+    // token rows and the rank totals, so that a small histogram costs no
+    // round trip of its own.
+    const int EPT = E < NT ? E : NT;
+    int P = NT / EPT;
+    if (P > C) P = C;
+    int v0[kBatch];
+    {
+        const int e = tid % EPT, p = tid / EPT;
+        const bool act = e < E && p < P;
+        const int r0 = act ? p * C / P : 0;
+        const int r1 = act ? (p + 1) * C / P : 0;
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j)
+            v0[j] = r0 + j < r1 ? a.hist[(int64_t)(r0 + j) * E + e] : 0;
+    }
+
     const int64_t t = (int64_t)b * NT + tid;
     const bool tv = t < a.num_tokens && !a.counts_only;
     int ids[KMAX], lr[KMAX];
@@ -741,9 +763,6 @@ __device__ __forceinline__ void finish_lean(const LayoutArgs& a, int C, int b, u
     rt.early = false;
     if (b == 0 && !a.no_rank_counts) rank_totals_load<NT>(a, rt);
 
-    const int EPT = E < NT ? E : NT;
-    int P = NT / EPT;
-    if (P > C) P = C;
     for (int eb = 0; eb < E; eb += EPT) {
         const int e = eb + tid % EPT, p = tid / EPT;
         const bool act = e < E && p < P;
@@ -752,26 +771,37 @@ __device__ __forceinline__ void finish_lean(const LayoutArgs& a, int C, int b, u
         int pre = 0, all = 0;
         for (int r = r0; r < r1; r += kBatch) {
             int v[kBatch];
+            if (eb == 0 && r == r0) {
 #pragma unroll
-            for (int j = 0; j < kBatch; ++j)
-                v[j] = r + j < r1 ? a.hist[(int64_t)(r + j) * E + e] : 0;
+                for (int j = 0; j < kBatch; ++j) v[j] = v0[j];
+            } else {
+#pragma unroll
+                for (int j = 0; j < kBatch; ++j)
+                    v[j] = r + j < r1 ? a.hist[(int64_t)(r + j) * E + e] : 0;
+            }
 #pragma unroll
             for (int j = 0; j < kBatch; ++j) {
                 all += v[j];
                 pre += (r + j < cb0) ? v[j] : 0;
             }
         }
-        if (act) {
-            part_pre[p * EPT + (e - eb)] = pre;
-            part_all[p * EPT + (e - eb)] = all;
-        }
-        __syncthreads();
-        if (act && p == 0) {
-            int sp = 0, sa = 0;
-            for (int q = 0; q < P; ++q) {
-                sp += part_pre[q * EPT + (e - eb)];
-                sa += part_all[q * EPT + (e - eb)];
+        int sp = pre, sa = all;
+        if (P > 1) {   // the column's partial sums meet in LDS
+            if (act) {
+                part_pre[p * EPT + (e - eb)] = pre;
+                part_all[p * EPT + (e - eb)] = all;
             }
+            __syncthreads();
+            if (act && p == 0) {
+                sp = 0;
+                sa = 0;
+                for (int q = 0; q < P; ++q) {
+                    sp += part_pre[q * EPT + (e - eb)];
+                    sa += part_all[q * EPT + (e - eb)];
+                }
+            }
+        }
+        if (act && p == 0) {
             base[e] = sp;
 #pragma unroll
             for (int g = 1; g < G; ++g) {
@@ -781,8 +811,9 @@ __device__ __forceinline__ void finish_lean(const LayoutArgs& a, int C, int b, u
             }
             tot[e] = sa;
         }
-        __syncthreads();
+        if (P > 1) __syncthreads();   // the partials' LDS is reused by the next columns
     }
+    if (P == 1) __syncthreads();      // tot and base complete
     aligned_prefix<NT>(a, tot, psum, scratch);
 
     if (!a.counts_only) {
