@@ -950,11 +950,12 @@ def main():
                    "combine_quant": w.combine_quant, "combine_group": w.combine_group,
                    "buffer_sets": data_sets},
         "roofline": {"bound": "hbm",
-                     "kernel": ({"dispatch": "k_dispatch_layout (dispatch + next batch's layout "
-                                             "count phase)",
-                                 "combine": "k_combine_layout (combine + next batch's layout "
-                                            "finish phase)"}.get(dom, dom)
+                     "kernel": ({"dispatch": "k_dispatch_layout (dispatch, with the next batch's "
+                                             "layout phase it carries)",
+                                 "combine": "k_combine_layout (combine, with the next batch's "
+                                            "layout phase it carries)"}.get(dom, dom)
                                 if merged1 else dom),
+                     "kernel_us_per_launch": t_dom / launches * 1e6,
                      "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": b_dom / launches,
