@@ -603,10 +603,141 @@ void orc_dispatch(const uint16_t* x, int64_t N, int H, const int32_t* slot_idx, 
 /* a4: combine                                                               */
 /* ------------------------------------------------------------------------ */
 
+/* Exact sums of products, rounded once to bf16.
+ *
+ * A term is the product of two or three finite factors (an fp32 weight, a
+ * bf16 value, or a weight, a code and an fp32 scale).  Each factor is an odd
+ * integer significand times a power of two; the term's significand is the
+ * product of those (at most 24 + 24 + 9 bits) and its exponent the sum, never
+ * below -EXACT_LOW.  The terms are added into a two's-complement integer of
+ * EXACT_LIMBS 64-bit limbs in units of 2^-EXACT_LOW, which holds the exact sum
+ * of up to 2^30 terms below 2^270 in magnitude.  The sum is then rounded to
+ * the nearest bf16, ties to the even significand, from its bits.
+ *
+ * The fp64 sum is used instead whenever it is exact: every product is exact
+ * in fp64 (checked with a fused multiply-add) and every addition is exact
+ * (checked with Knuth's two-sum, whose error term is then zero). */
+#define EXACT_LIMBS 10
+#define EXACT_LOW 320
+
+typedef struct {
+    uint64_t l[EXACT_LIMBS];
+} exact_acc;
+
+/* |v| = sig * 2^exp with sig odd (sig = 0 for a zero); v finite, at most 53
+ * significant bits. */
+static void split_finite(double v, uint64_t* sig, int* exp, int* neg)
+{
+    *neg = signbit(v) != 0;
+    v = fabs(v);
+    *sig = 0;
+    *exp = 0;
+    if (v == 0.0) return;
+    int e;
+    double m = frexp(v, &e);                 /* v = m * 2^e, 0.5 <= m < 1 */
+    uint64_t s = (uint64_t)ldexp(m, 53);
+    e -= 53;
+    while ((s & 1u) == 0) {
+        s >>= 1;
+        ++e;
+    }
+    *sig = s;
+    *exp = e;
+}
+
+static void exact_add_product(exact_acc* a, const double* f, int nf)
+{
+    uint64_t sig = 1;
+    int exp = 0, neg = 0;
+    for (int i = 0; i < nf; ++i) {
+        uint64_t s;
+        int e, n;
+        split_finite(f[i], &s, &e, &n);
+        if (s == 0) return;                  /* the product is zero */
+        sig *= s;
+        exp += e;
+        neg ^= n;
+    }
+    const int sh = exp + EXACT_LOW;          /* >= 0: see EXACT_LOW */
+    const int li = sh / 64, bo = sh % 64;
+    uint64_t part[EXACT_LIMBS] = {0};
+    part[li] = sig << bo;
+    if (bo != 0 && li + 1 < EXACT_LIMBS) part[li + 1] = sig >> (64 - bo);
+    if (!neg) {
+        uint64_t carry = 0;
+        for (int i = 0; i < EXACT_LIMBS; ++i) {
+            uint64_t x = a->l[i] + part[i];
+            uint64_t c1 = x < part[i];
+            uint64_t y = x + carry;
+            uint64_t c2 = y < carry;
+            a->l[i] = y;
+            carry = c1 | c2;
+        }
+    } else {
+        uint64_t borrow = 0;
+        for (int i = 0; i < EXACT_LIMBS; ++i) {
+            uint64_t x = a->l[i] - part[i];
+            uint64_t b1 = a->l[i] < part[i];
+            uint64_t y = x - borrow;
+            uint64_t b2 = x < borrow;
+            a->l[i] = y;
+            borrow = b1 | b2;
+        }
+    }
+}
+
+static int exact_bit(const exact_acc* a, int i) { return (int)((a->l[i / 64] >> (i % 64)) & 1u); }
+
+static int exact_any_below(const exact_acc* a, int i)
+{
+    for (int j = 0; j < i; ++j)
+        if (exact_bit(a, j)) return 1;
+    return 0;
+}
+
+static uint16_t exact_to_bf16(const exact_acc* acc)
+{
+    exact_acc m = *acc;
+    const int neg = (int)(m.l[EXACT_LIMBS - 1] >> 63);
+    if (neg) {                               /* magnitude: two's-complement negation */
+        uint64_t carry = 1;
+        for (int i = 0; i < EXACT_LIMBS; ++i) {
+            uint64_t x = ~m.l[i] + carry;
+            carry = (carry && x == 0) ? 1 : 0;
+            m.l[i] = x;
+        }
+    }
+    int p = -1;                              /* highest set bit */
+    for (int i = EXACT_LIMBS - 1; i >= 0 && p < 0; --i)
+        for (int j = 63; j >= 0; --j)
+            if ((m.l[i] >> j) & 1u) {
+                p = 64 * i + j;
+                break;
+            }
+    if (p < 0) return 0;                     /* an exact zero sum is +0 */
+    const int E = p - EXACT_LOW;             /* the sum lies in [2^E, 2^(E+1)) */
+    const int q = E >= -126 ? E - 7 : -133;  /* bf16 spacing there (normal / subnormal) */
+    const int b = q + EXACT_LOW;             /* bit of the spacing unit (>= 187) */
+    uint64_t kept = 0;
+    for (int i = p; i >= b; --i) kept = (kept << 1) | (uint64_t)exact_bit(&m, i);
+    const int half = exact_bit(&m, b - 1), below = exact_any_below(&m, b - 1);
+    if (half && (below || (kept & 1u))) ++kept;   /* nearest, ties to even */
+    const double v = ldexp((double)kept, q);      /* a bf16 value, or 2^128 */
+    return orc_bf16_from_f64(neg ? -v : v);
+}
+
+/* Knuth's two-sum: s = fl(a + b) and whether a + b == s exactly. */
+static double two_sum(double a, double b, int* exact)
+{
+    const double s = a + b;
+    const double bb = s - a;
+    const double err = (a - (s - bb)) + (b - bb);
+    if (err != 0.0) *exact = 0;
+    return s;
+}
+
 /* Combine, the plain definition: the weighted sum of the token's expert
- * outputs is formed exactly enough (fp64: each product of an fp32 weight and
- * a bf16 value is exact, and K <= 16 such terms lose at most a few ulps of
- * fp64) and rounded once to bf16. */
+ * outputs, exact, rounded once to bf16 (see exact_to_bf16 above). */
 void orc_combine(const uint16_t* y, const float* topk_weights, const int32_t* slot_idx,
                  int64_t N, int K, int H, int64_t t_begin, int64_t t_end, uint16_t* out)
 {
@@ -615,12 +746,29 @@ void orc_combine(const uint16_t* y, const float* topk_weights, const int32_t* sl
     for (int64_t t = t_begin; t < t_end; ++t)
         for (int h = 0; h < H; ++h) {
             double acc = 0.0;
+            int exact = 1;
             for (int k = 0; k < K; ++k) {
                 int64_t s = slot_idx[t * K + k];
                 if (s < 0) continue;
-                acc += (double)topk_weights[t * K + k] * (double)orc_f32_from_bf16(y[s * H + h]);
+                /* exact: 24 x 8 significant bits */
+                const double p = (double)topk_weights[t * K + k] * (double)orc_f32_from_bf16(y[s * H + h]);
+                acc = two_sum(acc, p, &exact);
             }
-            out[t * H + h] = orc_bf16_from_f64(acc);
+            if (exact && isfinite(acc)) {
+                out[t * H + h] = orc_bf16_from_f64(acc);
+                continue;
+            }
+            exact_acc e = {{0}};
+            int finite = 1;
+            for (int k = 0; k < K; ++k) {
+                int64_t s = slot_idx[t * K + k];
+                if (s < 0) continue;
+                const double f[2] = {(double)topk_weights[t * K + k],
+                                     (double)orc_f32_from_bf16(y[s * H + h])};
+                if (!isfinite(f[0]) || !isfinite(f[1])) finite = 0;
+                else exact_add_product(&e, f, 2);
+            }
+            out[t * H + h] = finite ? exact_to_bf16(&e) : orc_bf16_from_f64(acc);
         }
 }
 
@@ -647,37 +795,56 @@ void orc_combine_fma(const uint16_t* y, const float* topk_weights, const int32_t
 }
 
 /* Value of element h of a quantised expert-output row: code * scale. */
-static double code_value(const uint8_t* yc, const float* y_scales, int quant, int group, int H,
-                         int64_t s, int h)
+static double code_of(const uint8_t* yc, int quant, int H, int64_t s, int h)
 {
     uint8_t c = yc[s * H + h];
-    double v = quant == 1 ? (double)orc_f32_from_e4m3fn(c) : (double)(int8_t)c;
-    return v * (double)y_scales[s * (H / group) + h / group];
+    return quant == 1 ? (double)orc_f32_from_e4m3fn(c) : (double)(int8_t)c;
 }
 
 /* Combine of quantised expert outputs ("DeepEP 通信库使用指南（v2.1）":
  * from v2.1 combine accepts int8 / fp8 quantisation, with the same
  * quant_size choice as dispatch): y row s holds codes (E4M3FN bytes when
  * quant == 1, int8 when quant == 2) and fp32 scales [*, H/group]; the value
- * of element h is code * scale.  The sum is formed in fp64 and rounded once
- * to bf16, as in orc_combine. */
+ * of element h is code * scale.  The sum is exact and rounded once to bf16,
+ * as in orc_combine. */
 void orc_combine_q(const void* y_codes, const float* y_scales, int quant, int group,
                    const float* topk_weights, const int32_t* slot_idx, int64_t N, int K, int H,
                    int64_t t_begin, int64_t t_end, uint16_t* out)
 {
     (void)N;
     const uint8_t* yc = (const uint8_t*)y_codes;
+    const int G = H / group;
 #pragma omp parallel for schedule(static)
     for (int64_t t = t_begin; t < t_end; ++t)
         for (int h = 0; h < H; ++h) {
             double acc = 0.0;
+            int exact = 1;
             for (int k = 0; k < K; ++k) {
                 int64_t s = slot_idx[t * K + k];
                 if (s < 0) continue;
-                acc += (double)topk_weights[t * K + k] *
-                       code_value(yc, y_scales, quant, group, H, s, h);
+                /* code * scale is exact (at most 9 x 24 bits); the weight's
+                 * product with it may not be: fma recovers its error */
+                const double w = (double)topk_weights[t * K + k];
+                const double v = code_of(yc, quant, H, s, h) * (double)y_scales[s * G + h / group];
+                const double p = w * v;
+                if (fma(w, v, -p) != 0.0) exact = 0;
+                acc = two_sum(acc, p, &exact);
             }
-            out[t * H + h] = orc_bf16_from_f64(acc);
+            if (exact && isfinite(acc)) {
+                out[t * H + h] = orc_bf16_from_f64(acc);
+                continue;
+            }
+            exact_acc e = {{0}};
+            int finite = 1;
+            for (int k = 0; k < K; ++k) {
+                int64_t s = slot_idx[t * K + k];
+                if (s < 0) continue;
+                const double f[3] = {(double)topk_weights[t * K + k], code_of(yc, quant, H, s, h),
+                                     (double)y_scales[s * G + h / group]};
+                if (!isfinite(f[0]) || !isfinite(f[1]) || !isfinite(f[2])) finite = 0;
+                else exact_add_product(&e, f, 3);
+            }
+            out[t * H + h] = finite ? exact_to_bf16(&e) : orc_bf16_from_f64(acc);
         }
 }
 

@@ -169,7 +169,8 @@ void orc_dispatch(const uint16_t* x, int64_t N, int H, const int32_t* slot_idx, 
 
 /* ---- a4: combine ([P2] API table; weighted reduce) ----
  * out[t,:] = bf16( sum over k with slot_idx[t,k] >= 0 of w[t,k] * y[slot,:] ),
- * sum formed in fp64, rounded once.  Rows with every k masked are +0. */
+ * the exact sum rounded once (nearest, ties to even).  Rows with every k
+ * masked, and exact zero sums, are +0. */
 void orc_combine(const uint16_t* y, const float* topk_weights, const int32_t* slot_idx,
                  int64_t N, int K, int H, int64_t t_begin, int64_t t_end, uint16_t* out);
 

@@ -157,6 +157,73 @@ def test_combine_exact_rational_sums():
                 assert got == want, (t, h, q, got, want)
 
 
+def _bf16_of(v):
+    return int(_bf16_bits(torch.tensor([v], dtype=torch.float32).to(torch.bfloat16))[0])
+
+
+def test_combine_exact_beyond_fp64():
+    """Sums whose terms span more than fp64's 53 bits: the exact sum, not
+    its fp64 rounding, decides.  1 + 2^-8 is the midpoint between the bf16
+    neighbours 1 and 1 + 2^-7; a third term of +-2^-120 puts the sum just
+    above or below it (an fp64 sum would land on the midpoint and round to
+    even, 1.0, in both cases)."""
+    S, H = 3, 1
+    y = np.array([[_bf16_of(1.0)], [_bf16_of(2.0 ** -8)], [_bf16_of(2.0 ** -120)]], np.uint16)
+    slot = np.array([[0, 1, 2], [0, 1, 2], [0, 1, -1]], np.int32)
+    w = np.array([[1.0, 1.0, 1.0], [1.0, 1.0, -1.0], [1.0, 1.0, 0.0]], np.float32)
+    out = oracle.combine(y, w, slot)
+    assert out[:, 0].tolist() == [0x3F81, 0x3F80, 0x3F80]     # up, down, tie to even
+    # wide random spans against exact rationals: values down to 2^-133 and
+    # weights from 2^-100 to 2^30
+    rng = np.random.default_rng(23)
+    N, K, H, S = 30, 6, 8, 40
+    # any sign and biased exponent 0..127 (subnormals to just below 2), so
+    # that no sum leaves bf16's range
+    bits = (rng.integers(0, 2 ** 16, size=(S, H)) & 0xBFFF).astype(np.uint16)
+    wv = (rng.standard_normal((N, K)) * 2.0 ** rng.integers(-100, 30, size=(N, K))).astype(np.float32)
+    sl = rng.integers(-1, S, size=(N, K)).astype(np.int32)
+    out = oracle.combine(bits, wv, sl)
+    yv = oracle.f32_from_bf16(bits)
+    for t in range(N):
+        for h in range(H):
+            q = sum((Fraction(float(wv[t, k])) * Fraction(float(yv[sl[t, k], h]))
+                     for k in range(K) if sl[t, k] >= 0), Fraction(0))
+            got = int(out[t, h])
+            if q == 0:
+                assert got == 0x0000, (t, h)
+            else:
+                assert got == _exact_bf16(q), (t, h, got)
+
+
+def test_quantised_combine_exact_beyond_fp64():
+    """A weight times an int8 code times an fp32 scale can need 55 bits: the
+    quantised combine sums the exact products.  The midpoint case as above,
+    and random full-precision weights and scales against exact rationals."""
+    codes = np.array([[1], [1]], np.int8)
+    sc = np.array([[1.0 + 2.0 ** -8], [2.0 ** -100]], np.float32)
+    slot = np.array([[0, 1], [0, -1]], np.int32)
+    w = np.ones((2, 2), np.float32)
+    out = oracle.combine_q(codes, sc, oracle.QUANT_INT8, 1, w, slot)
+    assert out[:, 0].tolist() == [0x3F81, 0x3F80]
+    rng = np.random.default_rng(24)
+    S, H, N, K = 20, 4, 25, 5
+    codes = rng.integers(-127, 128, size=(S, H)).astype(np.int8)
+    sc = (rng.random((S, 1)) * 2.0 ** rng.integers(-60, 20, size=(S, 1))).astype(np.float32)
+    wv = (rng.standard_normal((N, K)) * 2.0 ** rng.integers(-60, 20, size=(N, K))).astype(np.float32)
+    sl = rng.integers(-1, S, size=(N, K)).astype(np.int32)
+    out = oracle.combine_q(codes, sc, oracle.QUANT_INT8, H, wv, sl)
+    for t in range(N):
+        for h in range(H):
+            q = sum((Fraction(float(wv[t, k])) * int(codes[sl[t, k], h])
+                     * Fraction(float(sc[sl[t, k], 0])) for k in range(K) if sl[t, k] >= 0),
+                    Fraction(0))
+            got = int(out[t, h])
+            if q == 0:
+                assert got == 0x0000, (t, h)
+            else:
+                assert got == _exact_bf16(q), (t, h, got)
+
+
 def test_combine_identity_linearity_and_masks():
     rng = np.random.default_rng(4)
     N, K, H, S = 64, 4, 64, 200
