@@ -50,6 +50,25 @@ def test_default_line_has_the_contract_fields():
     assert cb["unit"] == line["unit"] and cb["sample"]
 
 
+@pytest.mark.gpu
+@pytest.mark.parametrize("args,check", [
+    (["--workload", "qwen3_30b_a3b_prefill", "--sets", "1"],
+     lambda l: l["config"]["buffer_sets"] == 1 and l["cache"].startswith("warm")),
+    (["--workload", "tiny", "--pipeline", "overlap", "--graph"],
+     lambda l: l["pipeline"] == "overlap" and l["timing"]["graph"]),
+    (["--workload", "ll_decode_fp8", "--pipeline", "merged", "--graph"],
+     lambda l: l["timing"]["graph"] and l["roofline"]["kernel_us_per_launch"] > 0),
+], ids=["warm", "overlap-graph", "merged-graph"])
+def test_bench_modes(args, check):
+    """The warm mode (one buffer set, two handles for the merged pipeline)
+    and the graph-captured overlap and merged pipelines each print a line."""
+    print("bench.py", *args, flush=True)
+    r = _run([*args, "--steps", "8", "--warmup", "4", "--no-cpu-baseline"], 300)
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-4000:]
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    assert line["value"] > 0 and check(line), line
+
+
 def _variant(**kw):
     import argparse
     sys.path.insert(0, ROOT) if ROOT not in sys.path else None
