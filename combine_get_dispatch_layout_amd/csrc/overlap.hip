@@ -9,9 +9,10 @@
 //
 // Design: a launch whose first blocks do layout work and whose other blocks
 // are the ordinary dispatch (or combine) waves.  The layout blocks have the
-// lowest block ids, so they are scheduled first and finish inside the
-// shadow of the streaming blocks; nothing waits on another stream or an
-// event.
+// lowest block ids, so they are scheduled first; beside a prefill batch's
+// streaming blocks they finish well inside the launch, while a decode
+// batch's one-block layout (about 6 us) outlasts its few-microsecond launch.
+// Nothing waits on another stream or an event.
 //   dispatch launch: the whole layout in one block (N <= 256, when the
 //                    launch moves under 4 MiB), or the count phase, one
 //                    block per 256 tokens;
