@@ -946,7 +946,11 @@ ep_status ep_check_error(ep_handle* h, void* stream, uint32_t* flags)
 
 const char* ep_status_str(ep_status s)
 {
-    switch (s) {
+    // A C caller may pass any int; reading it as the enum would be undefined
+    // for a value outside the enumerators, so its bits are read as an int.
+    int v = 0;
+    memcpy(&v, &s, sizeof(v) < sizeof(s) ? sizeof(v) : sizeof(s));
+    switch (v) {
         case EP_OK: return "EP_OK";
         case EP_ERR_INVALID_ARG: return "EP_ERR_INVALID_ARG";
         case EP_ERR_WORKSPACE: return "EP_ERR_WORKSPACE";
