@@ -20,6 +20,7 @@
 // device address: the address comes from hipGetSymbolAddress, once per
 // device (static_scratch_ptr below).
 constexpr int64_t kStaticScratchBytes = EP_STATIC_SCRATCH_BYTES;
+constexpr int kMaxHidden = EP_MAX_HIDDEN;
 static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 
 namespace {
@@ -83,6 +84,9 @@ ep_status check_config(const ep_config* c)
     if (!c) return EP_FAIL(EP_ERR_INVALID_ARG, "config is NULL");
     if (c->hidden <= 0 || c->hidden % 8 != 0)
         return EP_FAIL(EP_ERR_INVALID_ARG, "hidden=%d must be a positive multiple of 8", c->hidden);
+    // row bytes (2 * hidden) and per-row byte offsets stay far inside 32 bits
+    if (c->hidden > kMaxHidden)
+        return EP_FAIL(EP_ERR_INVALID_ARG, "hidden=%d above %d", c->hidden, kMaxHidden);
     if (c->num_topk < 1 || c->num_topk > epk::kMaxTopk)
         return EP_FAIL(EP_ERR_INVALID_ARG, "num_topk=%d outside [1,%d]", c->num_topk, epk::kMaxTopk);
     if (c->num_experts < 1 || c->num_experts > epk::kMaxExperts)

@@ -84,8 +84,13 @@ enum {
     EP_FLAG_Y_ROWS = 4u          /* combine: slot >= y_rows                    */
 };
 
+/* Largest hidden size: rows of up to 32 MiB of bf16 keep every byte offset
+ * inside a row well within 32 bits. */
+#define EP_MAX_HIDDEN (1 << 24)
+
 typedef struct ep_config {
-    int32_t hidden;            /* H: elements per token row, multiple of 8       */
+    int32_t hidden;            /* H: elements per token row, multiple of 8, at
+                                  most EP_MAX_HIDDEN                              */
     int32_t num_topk;          /* K: experts per token, 1..16                    */
     int32_t num_experts;       /* E: 1..1024, multiple of num_ranks              */
     int32_t num_ranks;         /* R: simulated EP ranks, 1..1024; rank r owns

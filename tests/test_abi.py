@@ -67,7 +67,7 @@ GOOD = dict(hidden=2048, num_topk=8, num_experts=128, num_ranks=16)
 
 
 @pytest.mark.parametrize("bad", [
-    dict(hidden=0), dict(hidden=2047), dict(num_topk=0), dict(num_topk=17),
+    dict(hidden=0), dict(hidden=2047), dict(hidden=(1 << 24) + 8), dict(num_topk=0), dict(num_topk=17),
     dict(num_experts=0), dict(num_experts=1025), dict(num_ranks=0), dict(num_ranks=3),
     dict(num_ranks=2048, num_experts=1024), dict(ranks_per_node=-1), dict(expert_alignment=0),
     dict(quant=3), dict(quant=1, quant_group=64), dict(quant=2, quant_group=128, hidden=2056),

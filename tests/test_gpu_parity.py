@@ -67,6 +67,8 @@ def _custom(N, H, E, R, K, A=1, quant=W.QUANT_NONE, group=0, mask=0.0, seed=7, r
     dict(N=700, H=136, E=8, R=1, K=8, A=5, mask=0.3),     # one rank, odd alignment
     dict(N=64, H=128, E=64, R=8, K=6, A=128),             # heavy padding
     dict(N=999, H=520, E=96, R=12, K=3, rpn=5, mask=0.5),  # ragged R/node, many masked
+    dict(N=40, H=65536, E=16, R=4, K=4),                  # 128 KiB rows
+    dict(N=33, H=32768, E=16, R=4, K=3, quant=W.QUANT_FP8, group=128, mask=0.1),
 ])
 def test_edge_shapes(args):
     w = _custom(**args)
