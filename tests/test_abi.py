@@ -163,3 +163,58 @@ def test_static_handle_rejects_workspace_beyond_its_limit():
     c = ep.Config(**{**GOOD, "num_topk": 0}).c()
     assert ep.lib().ep_handle_init_static(ctypes.byref(c), 16, None, ctypes.byref(out)) == \
         ep.EP_ERR_INVALID_ARG
+
+
+_I32 = (-2 ** 31, 2 ** 31 - 1)
+
+
+def _cfg_strategy():
+    from hypothesis import strategies as st
+
+    def near(vals):
+        return st.one_of(st.sampled_from(vals), st.integers(*_I32))
+    return st.builds(
+        ep.Config,
+        hidden=near([8, 128, 2048, 7168, 8192, 1 << 24]),
+        num_topk=near([1, 8, 16, 17]),
+        num_experts=near([1, 16, 128, 256, 1024]),
+        num_ranks=near([1, 4, 16, 1024]),
+        ranks_per_node=near([0, 1, 8]),
+        expert_alignment=near([1, 128]),
+        quant=near([0, 1, 2, 3]),
+        quant_group=near([0, 32, 128, 2048]),
+        counts_as_prefix=st.booleans(),
+        expert_capacity=near([0, 1, 64]),
+        num_sources=near([0, 1, 16, 1024]),
+        scale_mode=near([0, 1, 2]),
+        combine_quant=near([0, 1, 2]),
+        combine_group=near([0, 128, 2048]),
+        non_expand=st.booleans())
+
+
+def test_sizes_never_misbehave_on_arbitrary_configs():
+    """The host-side size calls, on arbitrary configurations and token counts
+    (any int32 field, any int64 count): a status of EP_OK or
+    EP_ERR_INVALID_ARG, never a crash; an accepted size is positive, a
+    multiple of 256 and holds the receive rows, which stay below 2^31."""
+    from hypothesis import given, settings, strategies as st
+
+    @settings(max_examples=400, deadline=None, derandomize=True)
+    @given(_cfg_strategy(), st.one_of(st.sampled_from([0, 1, 4096, 1 << 20]),
+                                      st.integers(-2 ** 63, 2 ** 63 - 1)))
+    def check(cfg, n):
+        L = ep.lib()
+        c = cfg.c()
+        out = ctypes.c_int64(-7)
+        st_ws = L.ep_workspace_size(ctypes.byref(c), n, ctypes.byref(out))
+        assert st_ws in (ep.EP_OK, ep.EP_ERR_INVALID_ARG)
+        if st_ws == ep.EP_OK:
+            assert out.value > 0 and out.value % 256 == 0
+        cap = ctypes.c_int64(-7)
+        st_cap = L.ep_recv_capacity(ctypes.byref(c), n, ctypes.byref(cap))
+        assert st_cap in (ep.EP_OK, ep.EP_ERR_INVALID_ARG)
+        if st_cap == ep.EP_OK:
+            assert 0 <= cap.value < 2 ** 31
+        if st_ws == ep.EP_OK:
+            assert st_cap == ep.EP_OK and out.value >= 8 * cap.value
+    check()
